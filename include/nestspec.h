@@ -1,0 +1,269 @@
+/*
+ * nestspec.h -- C ABI of the nested-weight self-speculative decoding round.
+ *
+ * The method is BitNest ("BitNest: Bit-Nested Speculative Decoding for
+ * Memory-Efficient LLM Inference Acceleration"). Per its Figure 2, one
+ * quantized weight copy holds a b-bit base and an r-bit refinement of the
+ * base's remaining error. Per its Figure 3, the two codes sit in two
+ * independent 4-bit planes of N/2 bytes each for N weights. The draft reads
+ * only the base plane; verification reads both planes to recover the 8-bit
+ * target. Per its Figure 4, a nested KV cache gives the draft a low-bit
+ * base view and verification the full view of the same cache.
+ *
+ * The round is the one in "How Speculative Decoding Speeds Up Inference",
+ * section "Drafting and checking tokens" (three numbered steps, Table 1).
+ * The draft proposes k tokens and the target checks all positions in one
+ * pass. The matching prefix is kept and the first mismatch is replaced by
+ * the target's token, so a round yields 1..k+1 tokens. With greedy decoding
+ * every kept token is the target's own choice (section "The same output as
+ * the large model alone").
+ *
+ * The pages fix no group size, scale rule, rounding, nibble order or data
+ * layout. This library fixes them as below, and the oracle follows the same
+ * definitions.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every entry point
+ * ---------------------------------------------------------------------------
+ *  - Every buffer pointer is a DEVICE pointer unless the argument says
+ *    "host". The caller allocates and owns every buffer. The library never
+ *    allocates, frees or keeps a buffer.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call enqueues its kernels on that stream and returns without
+ *    synchronising.
+ *  - Arguments are checked on the host before anything is launched. On an
+ *    error nothing is launched, the return value is a nest_status code, and
+ *    nest_last_error() holds a message for the calling thread. A launch
+ *    failure returns NEST_EHIP. A device fault surfaces at the caller's
+ *    next synchronisation.
+ *  - Calls that share a workspace must not overlap in time (same stream, or
+ *    ordered by events).
+ *  - Input floats must be finite.
+ *
+ * ---------------------------------------------------------------------------
+ * Nested weight format (BitNest, Figures 2 and 3)
+ * ---------------------------------------------------------------------------
+ *  W is fp32 [rows][cols], row-major. `rows` are output features; `cols` is
+ *  the reduction dimension K. A group is `group` consecutive elements of one
+ *  row along cols, so a row has G = cols/group groups. Per (row, group):
+ *      m   = max |w| over the group
+ *      s   = fl32(m / 7)                        base scale (0 when m == 0)
+ *      q_b = clamp(rint(w / s), -7, 7)          base code, ties to even
+ *      e   = fma(-s, q_b, w)                    remaining error, one rounding
+ *      s16 = s * 2^-4                           refinement scale
+ *      q_r = clamp(rint(e / s16), -8, 7)        refinement code (0 when s16 == 0)
+ *  Every division is IEEE fp32, correctly rounded. When s == 0 both codes
+ *  are 0.
+ *  Base view of a weight: s * q_b. Full (8-bit) view: s16 * (16*q_b + q_r).
+ *  Planes: base and refine are each uint8 [rows][cols/2]. Byte j of a row
+ *  holds element 2j in bits 0..3 and element 2j+1 in bits 4..7, as 4-bit
+ *  two's complement. Each plane is exactly rows*cols/2 bytes.
+ *  Scales: fp32 [rows][G]. Only s is stored; s16 is derived from it.
+ *
+ * ---------------------------------------------------------------------------
+ * Activations (the "A8" of W4A8 / W8A8 in BitNest's Table 1)
+ * ---------------------------------------------------------------------------
+ *  x is fp32 [M][K]. Per row:
+ *      sa = fl32(max|x| / 127),  qa = clamp(rint(x / sa), -127, 127).
+ *  An all-zero row gives sa = 0 and qa = 0.
+ *
+ * ---------------------------------------------------------------------------
+ * Products and their fp32 fold
+ * ---------------------------------------------------------------------------
+ *  For output row n, activation row m and group g, the group sums are exact
+ *  int32:
+ *      Ab[m][n][g] = sum_{k in g} qa[m][k] * q_b[n][k]
+ *      Av[m][n][g] = sum_{k in g} qa[m][k] * (16*q_b[n][k] + q_r[n][k])
+ *  Reference fold, groups in ascending order, starting from +0:
+ *      draft:  run = fmaf(s[n][g],          (float)Ab[m][n][g], run)
+ *      verify: run = fmaf(s[n][g] * 2^-4,   (float)Av[m][n][g], run)
+ *      y[m][n] = run * sa[m]
+ *  Entry points that return an argmax (draft_gemv with `argmax`, and
+ *  verify_accept) use exactly this fold, so their y and indices are
+ *  bit-identical to it. draft_gemv and verify_gemm without an argmax may
+ *  split a row's groups into contiguous segments. Each segment is folded
+ *  as above, and the segments are then added in ascending order. In that
+ *  case |y - y_ref| <= (G+2) * 2^-24 * sa * sum_g |scale_g * A_g|.
+ *  The debug accumulators (`acc_dbg`) are always exact.
+ *  argmax: the lowest index among the maximal y (-0 counts as +0).
+ *
+ * ---------------------------------------------------------------------------
+ * Nested KV cache (BitNest, Figure 4)
+ * ---------------------------------------------------------------------------
+ *  Each (kv head, block of `block` tokens) of K is one quantization group,
+ *  and likewise for V. It uses the same rule as the weights, over its
+ *  block*d values. Layouts, in elements:
+ *      K planes: [Hkv][capacity][d]                 token-major
+ *      V planes: [Hkv][capacity/block][d][block]    each block dim-major
+ *      scales:   [Hkv][capacity/block] fp32 (one for K, one for V)
+ *  Planes pack element pairs into bytes exactly as for weights.
+ *  Base view (draft): value = s * q_b. Full view (verify): value =
+ *  s16 * (16*q_b + q_r).
+ *  Attention: query i of nq sits at position p_i = ctx_len - nq + i and
+ *  sees tokens 0..p_i. Query head hq reads kv head hq / (Hq/Hkv).
+ *  score = (q . k) / sqrt(d), softmax over the visible tokens, and out is
+ *  the probability-weighted sum of v, in fp32 [nq][Hq][d].
+ *  Truncation after a round is the caller's length update. A round that
+ *  verified k drafts and accepted a of them keeps ctx_len - k + a entries.
+ *  Entries past ctx_len are never read.
+ */
+#ifndef NESTSPEC_H
+#define NESTSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NEST_OK = 0,
+  NEST_EINVAL = 1,       /* null pointer, negative or inconsistent size   */
+  NEST_EALIGN = 2,       /* a pointer is not 16-byte aligned              */
+  NEST_ESHAPE = 3,       /* a size breaks a divisibility rule             */
+  NEST_EWORKSPACE = 4,   /* workspace missing or smaller than required    */
+  NEST_EUNSUPPORTED = 5, /* valid, but not a shape these kernels handle   */
+  NEST_EHIP = 6          /* a HIP call or kernel launch failed            */
+} nest_status;
+
+/* Message describing the last error on the calling thread ("" if none).
+   The pointer stays valid until the thread's next call into the library. */
+const char* nest_last_error(void);
+
+/* nest_pack -- nested quantization of a weight matrix (BitNest, Figures 2
+ * and 3; rule above).
+ *   w       fp32 [rows][cols]
+ *   base    uint8 [rows][cols/2]   (out)
+ *   refine  uint8 [rows][cols/2]   (out)
+ *   scales  fp32 [rows][cols/group] (out)
+ * Requires rows >= 1, cols >= 2, even group >= 2 and cols % group == 0.
+ * Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EHIP. */
+int nest_pack(const float* w, int64_t rows, int64_t cols, int64_t group,
+              uint8_t* base, uint8_t* refine, float* scales, void* stream);
+
+/* nest_act_quant -- per-row symmetric int8 quantization of activations.
+ *   x   fp32 [M][K];  qa int8 [M][K] (out);  sa fp32 [M] (out).
+ * Requires M >= 1 and K >= 1. Errors: NEST_EINVAL, NEST_EHIP. */
+int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
+                   void* stream);
+
+/* draft_gemv -- the draft's W4A8 product over the base plane only (BitNest,
+ * Figure 3: "the draft accesses only the base plane").
+ *   qa       int8 [M][K], 16-byte aligned;  sa fp32 [M]
+ *   base     uint8 [N][K/2], 16-byte aligned;  scales fp32 [N][K/group]
+ *   y        fp32 [M][N] (out, may be NULL when argmax is given)
+ *   argmax   int32 [M] (out, nullable). When given, the fold is exact and
+ *            argmax[m] is the index of the largest y[m][.].
+ *   acc_dbg  int32 [M][N][K/group] (out, nullable): the exact Ab.
+ *   ws       workspace of draft_gemv_workspace_size(M, N) bytes. It is
+ *            needed only when argmax is given (else it may be NULL). It must
+ *            be zero-filled before its first use, and every completed call
+ *            leaves it zero-filled again.
+ * Requires 1 <= M <= 16, group == 128, K % 128 == 0, N >= 1.
+ * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
+ * NEST_EWORKSPACE, NEST_EHIP. */
+int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+               const uint8_t* base, const float* scales, int64_t N, int64_t group,
+               float* y, int32_t* argmax, int32_t* acc_dbg,
+               void* ws, size_t ws_bytes, void* stream);
+size_t draft_gemv_workspace_size(int64_t M, int64_t N);
+
+/* verify_gemm -- the target's W8A8 product over both planes (BitNest,
+ * Figure 3: "the target accesses both planes to recover the full 8-bit
+ * representation"), for the k+1 rows of a round or a batch of rounds.
+ *   qa int8 [M][K] (16-byte aligned); sa fp32 [M]
+ *   base, refine uint8 [N][K/2] (16-byte aligned); scales fp32 [N][K/group]
+ *   y fp32 [M][N] (out); acc_dbg int32 [M][N][K/group] (out, nullable): Av
+ * Requires M >= 1, group == 128, K % 128 == 0, N >= 1. M <= 16 runs the
+ * one-tile kernel. Larger M runs the batched MFMA kernel.
+ * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
+ * NEST_EHIP. */
+int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                const uint8_t* base, const uint8_t* refine, const float* scales,
+                int64_t N, int64_t group, float* y, int32_t* acc_dbg,
+                void* stream);
+
+/* verify_accept -- the verify pass through the nested LM head, with the
+ * greedy accept step ("How Speculative Decoding Speeds Up Inference",
+ * numbered round steps and Table 1).
+ *   qa int8 [B*(k+1)][K]; sa fp32 [B*(k+1)]. Row b*(k+1)+i is sequence b's
+ *        input at slot i. Slot 0 is the last committed token and slot
+ *        i >= 1 is draft token i.
+ *   base, refine uint8 [V][K/2]; scales fp32 [V][K/group]: the LM head
+ *   draft     int32 [B][k]: draft tokens d_1..d_k, each in [0, V)
+ *   target    int32 [B][k+1] (out): t_i = argmax of the exact verify fold
+ *             of row i
+ *   n_emitted int32 [B] (out): a+1, where a is the largest j <= k with
+ *             d_i == t_{i-1} for all 1 <= i <= j
+ *   emitted   int32 [B][k+1] (out): t_0..t_a, then -1 in the unused slots
+ *   y         fp32 [B*(k+1)][V] (out, nullable): the verify logits
+ *   ws        verify_accept_workspace_size(B, k, V) bytes, zero-filled
+ *             before its first use. Every completed call leaves it
+ *             zero-filled.
+ * Requires B >= 1, k >= 0, B*(k+1) <= 16, group == 128, K % 128 == 0.
+ * Draft ids are not read on the host, so an id outside [0, V) simply
+ * never matches. Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE,
+ * NEST_EUNSUPPORTED, NEST_EWORKSPACE, NEST_EHIP. */
+int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64_t k,
+                  int64_t K, const uint8_t* base, const uint8_t* refine,
+                  const float* scales, int64_t V, int64_t group,
+                  const int32_t* draft, int32_t* target, int32_t* n_emitted,
+                  int32_t* emitted, float* y, void* ws, size_t ws_bytes,
+                  void* stream);
+size_t verify_accept_workspace_size(int64_t B, int64_t k, int64_t V);
+
+/* Nested KV cache: a host struct holding device pointers (layouts above). */
+typedef struct nest_kv {
+  const uint8_t* k_base;   /* [Hkv][capacity][d/2] bytes             */
+  const uint8_t* k_refine; /* same shape; may be NULL for view 0     */
+  const float* k_scale;    /* [Hkv][capacity/block]                  */
+  const uint8_t* v_base;   /* [Hkv][capacity/block][d][block/2] bytes */
+  const uint8_t* v_refine; /* same shape; may be NULL for view 0     */
+  const float* v_scale;    /* [Hkv][capacity/block]                  */
+  int64_t n_kv_heads;      /* Hkv                                    */
+  int64_t head_dim;        /* d                                      */
+  int64_t capacity;        /* tokens the planes hold                 */
+  int64_t block;           /* tokens per quantization group          */
+} nest_kv;
+
+/* kv_nest_pack -- build a nested KV cache from fp32 K and V (BitNest,
+ * Figure 4), with the same quantization rule as nest_pack. One group is a
+ * (head, block).
+ *   k, v     fp32 [Hkv][capacity][d], token-major
+ *   k_base, k_refine, v_base, v_refine  (out) planes in the layouts above
+ *   k_scale, v_scale  fp32 [Hkv][capacity/block] (out)
+ * Requires capacity % block == 0, even block, even d.
+ * Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EHIP. */
+int kv_nest_pack(const float* k, const float* v, int64_t n_kv_heads,
+                 int64_t capacity, int64_t head_dim, int64_t block,
+                 uint8_t* k_base, uint8_t* k_refine, float* k_scale,
+                 uint8_t* v_base, uint8_t* v_refine, float* v_scale,
+                 void* stream);
+
+/* kv_nest_attend -- decode attention over the nested cache (BitNest,
+ * Figure 4). view 0 is the base view, which the draft uses and which reads
+ * only the base planes. view 1 is the full view, which verification uses
+ * and which reads both planes.
+ *   q        bf16 bit patterns [nq][Hq][d]
+ *   kv       host pointer to a nest_kv
+ *   ctx_len  host value: visible cache length, nq <= ctx_len <= capacity
+ *   out      fp32 [nq][Hq][d] (out)
+ *   ws       kv_nest_attend_workspace_size(...) bytes (no zero-fill
+ *            needed)
+ * Requires head_dim == 128, block == 128, Hq % Hkv == 0,
+ * 1 <= nq*(Hq/Hkv) <= 64, and 16-byte aligned planes.
+ * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
+ * NEST_EWORKSPACE, NEST_EHIP. */
+int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
+                   const nest_kv* kv, int64_t ctx_len, int view, float* out,
+                   void* ws, size_t ws_bytes, void* stream);
+size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
+                                     int64_t n_kv_heads, int64_t head_dim,
+                                     int64_t ctx_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NESTSPEC_H */

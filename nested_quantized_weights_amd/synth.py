@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the nested-weight speculative round.
+
+Both the HIP path (tests, benchmark) and the CPU oracle take their inputs from
+here. This module holds none of the method's arithmetic. It only draws
+random numbers, converts dtypes and lists workload shapes. Every tensor comes
+from its own numpy stream, ``SeedSequence(0, spawn_key=key)``, so a tensor is
+reproducible on its own, whatever else was drawn before it.
+
+Workloads (names give what they are):
+  * ``linear_4096``: one nested 4096x4096 linear layer. Draft GEMV with 1
+    row, verify with 5 rows (k=4).
+  * ``qwen2.5-7b_layer``: the linears of one Qwen2.5-7B-shaped decoder
+    layer. hidden 3584, QKV 3584->4608 (28 q / 4 kv heads, d=128), O
+    3584->3584, gate and up 3584->18944, down 18944->3584.
+  * ``qwen2.5-7b_lm_head``: the nested 3584x152064 LM head with k=8 verify
+    rows and planted acceptance 0.58 / 0.66 / 0.95. These are the acceptance
+    rates that SpecQuant's Table II and BitNest's abstract report.
+  * ``llama3-8b_batched_verify``: 16 sequences x 9 rows = 144-row verify over
+    the LLaMA-3-8B-shaped linears (hidden 4096, QKV 4096->6144, O
+    4096->4096, gate and up 4096->14336, down 14336->4096), 32 layers.
+  * ``kv_32k``: nested KV cache with 32 q heads / 8 kv heads, d=128 and a
+    32768-token context. bf16 queries; 1 draft query; 9 verify queries.
+
+Distributions: weights ~ N(0, 0.02) (read as standard deviation 0.02).
+Activations, K, V and queries ~ N(0, 1). Queries are rounded to bf16
+(nearest, ties to even).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SEED = 0
+
+WORKLOADS = {
+    "linear_4096": {"K": 4096, "N": 4096, "group": 128, "draft_rows": 1,
+                    "verify_rows": 5, "k": 4},
+    "qwen2.5-7b_layer": {
+        "hidden": 3584, "group": 128, "k": 4,
+        # name -> (N out, K in)
+        "linears": {"qkv": (4608, 3584), "o": (3584, 3584), "gate_up": (2 * 18944, 3584),
+                    "down": (3584, 18944)},
+        "q_heads": 28, "kv_heads": 4, "head_dim": 128,
+    },
+    "qwen2.5-7b_lm_head": {"K": 3584, "V": 152064, "group": 128, "k": 8,
+                           "alphas": (0.58, 0.66, 0.95), "rounds": 10000, "pool": 16},
+    "llama3-8b_batched_verify": {
+        "hidden": 4096, "group": 128, "layers": 32, "sequences": 16, "rows_per_seq": 9,
+        "linears": {"qkv": (6144, 4096), "o": (4096, 4096), "gate": (14336, 4096),
+                    "up": (14336, 4096), "down": (4096, 14336)},
+    },
+    "kv_32k": {"q_heads": 32, "kv_heads": 8, "head_dim": 128, "context": 32768,
+               "block": 128, "draft_queries": 1, "verify_queries": 9},
+}
+
+# Stable small integers for the spawn keys of each workload.
+WORKLOAD_KEY = {name: i + 1 for i, name in enumerate(WORKLOADS)}
+
+
+def rng(*key: int) -> np.random.Generator:
+    """Generator for one tensor: seed 0 and spawn key ``key``."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(SEED, spawn_key=key)))
+
+
+def normal(shape, key, std: float = 1.0) -> np.ndarray:
+    """float32 normal draws, scaled by ``std`` in float32."""
+    a = rng(*key).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
+
+
+def weights(n: int, k: int, key, std: float = 0.02) -> np.ndarray:
+    """fp32 [n][k] weights ~ N(0, std)."""
+    return normal((n, k), key, std)
+
+
+def activations(m: int, k: int, key) -> np.ndarray:
+    """fp32 [m][k] activations ~ N(0, 1)."""
+    return normal((m, k), key)
+
+
+def kv(n_kv_heads: int, capacity: int, head_dim: int, key):
+    """fp32 K and V, each [Hkv][capacity][d], ~ N(0, 1)."""
+    return (normal((n_kv_heads, capacity, head_dim), tuple(key) + (0,)),
+            normal((n_kv_heads, capacity, head_dim), tuple(key) + (1,)))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even) and return the bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_float(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def queries_bf16(nq: int, n_q_heads: int, head_dim: int, key) -> np.ndarray:
+    """bf16 bit patterns [nq][Hq][d] of N(0, 1) draws."""
+    return to_bf16_bits(normal((nq, n_q_heads, head_dim), key))
+
+
+def plant_drafts(target: np.ndarray, alpha: float, vocab: int, key) -> np.ndarray:
+    """Draft tokens planted to match the target's choices at rate ``alpha``.
+
+    ``target`` is int [R][k+1]: the target's choices t_0..t_k of R rounds.
+    Slot i (1..k) holds d_i = t_{i-1} with probability alpha. Otherwise it
+    holds an id drawn uniformly from the other vocab-1 ids. Slots are
+    independent, which is the assumption behind the blog's Eq. (1). The
+    result is int32 [R][k].
+    """
+    target = np.asarray(target, dtype=np.int64)
+    R, k1 = target.shape
+    k = k1 - 1
+    g = rng(*key)
+    u = g.random((R, k))
+    other = g.integers(0, vocab - 1, size=(R, k))
+    prev = target[:, :k]
+    other = np.where(other >= prev, other + 1, other)
+    return np.where(u < alpha, prev, other).astype(np.int32)

@@ -1,0 +1,73 @@
+"""Build libnestspec.so (the HIP library behind include/nestspec.h) for gfx950.
+
+hipcc compiles every .hip/.cpp source under csrc/ into one shared library
+in this package directory. Flags:
+  -ffp-contract=off   no implicit fma: every fused operation is written out,
+                      so the fp32 fold matches its definition bit for bit
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                      no packed fp32 VALU instructions
+IEEE division and denormals stay at HIP's defaults (correctly rounded,
+not flushed).
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(_HERE)
+CSRC = os.path.join(_HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(_HERE, "libnestspec.so")
+ARCH = os.environ.get("NEST_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+         "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source to an object in parallel, then link."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs, objs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = ["hipcc", "-c", src, "-o", obj] + [f for f in FLAGS if f != "-shared"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0), verbose)
+    for p in procs:
+        _wait(p, verbose)
+    cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-o", LIB + ".tmp"] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def _wait(item, verbose):
+    src, p = item
+    out, _ = p.communicate()
+    text = out.decode(errors="replace")
+    # hipcc's host pass does not know the packed-fp32 feature: harmless
+    lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,157 @@
+// Nested quantization (BitNest, Figure 2: a base, then the remaining error
+// as a refinement; Figure 3: two independent 4-bit planes), the nested KV
+// cache builder (Figure 4), and per-token int8 activations.
+//
+// Each quantization group is one wave. Lanes read the group coalesced for
+// the max-abs pass, then each lane codes adjacent element pairs, which are
+// one byte in each plane. Every division is IEEE fp32 (correctly rounded,
+// HIP's default), rintf rounds ties to even, and the residual is one fmaf,
+// so the codes are those of the rule in nestspec.h bit for bit.
+#include "common.h"
+
+namespace {
+
+__device__ __forceinline__ void nest_codes(float w, float s, float s16, int& qb, int& qr) {
+  if (s == 0.0f) {
+    qb = 0;
+    qr = 0;
+    return;
+  }
+  int b = static_cast<int>(rintf(w / s));
+  b = b < -7 ? -7 : (b > 7 ? 7 : b);
+  float e = fmaf(-s, static_cast<float>(b), w);
+  int r = 0;
+  if (s16 != 0.0f) {
+    float u = rintf(e / s16);
+    u = u < -8.0f ? -8.0f : (u > 7.0f ? 7.0f : u);
+    r = static_cast<int>(u);
+  }
+  qb = b;
+  qr = r;
+}
+
+// One wave per group. Group gi covers src[gi*group, (gi+1)*group) in both
+// layouts. VT selects the dim-major plane order that the V cache uses
+// inside a block: plane element e is (dim e/blk, token e%blk), which is
+// the source element (e%blk)*d + e/blk of the token-major block.
+template <bool VT>
+__global__ void __launch_bounds__(256) pack_groups_kernel(const float* __restrict__ src,
+                                                          int64_t num_groups, int64_t group,
+                                                          int64_t d, int64_t blk,
+                                                          uint8_t* __restrict__ base,
+                                                          uint8_t* __restrict__ refine,
+                                                          float* __restrict__ scales) {
+  const int64_t gi = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (gi >= num_groups) return;  // uniform per wave; no block-level sync below
+  const float* g = src + gi * group;
+
+  float m = 0.0f;
+  for (int64_t e = lane; e < group; e += 64) m = fmaxf(m, fabsf(g[e]));
+  m = wave_max(m);
+  const float s = m / 7.0f;
+  const float s16 = s * 0.0625f;
+  if (lane == 0) scales[gi] = s;
+
+  uint8_t* pb = base + gi * (group / 2);
+  uint8_t* pr = refine + gi * (group / 2);
+  for (int64_t p = lane; p < group / 2; p += 64) {
+    float w0, w1;
+    if (VT) {
+      const int64_t e = 2 * p, t = e % blk, j = e / blk;
+      w0 = g[t * d + j];
+      w1 = g[(t + 1) * d + j];
+    } else {
+      w0 = g[2 * p];
+      w1 = g[2 * p + 1];
+    }
+    int b0, r0, b1, r1;
+    nest_codes(w0, s, s16, b0, r0);
+    nest_codes(w1, s, s16, b1, r1);
+    pb[p] = static_cast<uint8_t>((b0 & 15) | ((b1 & 15) << 4));
+    pr[p] = static_cast<uint8_t>((r0 & 15) | ((r1 & 15) << 4));
+  }
+}
+
+// One block of 256 threads per activation row.
+__global__ void __launch_bounds__(256) act_quant_kernel(const float* __restrict__ x, int64_t K,
+                                                        int8_t* __restrict__ qa,
+                                                        float* __restrict__ sa) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * K;
+  float m = 0.0f;
+  for (int64_t k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf(xr[k]));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m / 127.0f;
+  if (threadIdx.x == 0) sa[row] = s;
+  int8_t* q = qa + row * K;
+  for (int64_t k = threadIdx.x; k < K; k += 256) {
+    int v = 0;
+    if (s != 0.0f) {
+      float t = rintf(xr[k] / s);
+      t = t < -127.0f ? -127.0f : (t > 127.0f ? 127.0f : t);
+      v = static_cast<int>(t);
+    }
+    q[k] = static_cast<int8_t>(v);
+  }
+}
+
+int launch_pack(bool vt, const float* src, int64_t num_groups, int64_t group, int64_t d,
+                int64_t blk, uint8_t* base, uint8_t* refine, float* scales, hipStream_t st,
+                const char* what) {
+  const int64_t blocks = (num_groups + 3) / 4;
+  if (blocks > 0x7fffffffLL) return nest::fail(NEST_EUNSUPPORTED, "%s: too many groups", what);
+  if (vt)
+    pack_groups_kernel<true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st>>>(
+        src, num_groups, group, d, blk, base, refine, scales);
+  else
+    pack_groups_kernel<false><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st>>>(
+        src, num_groups, group, d, blk, base, refine, scales);
+  return nest::check_launch(what);
+}
+
+}  // namespace
+
+extern "C" int nest_pack(const float* w, int64_t rows, int64_t cols, int64_t group, uint8_t* base,
+                         uint8_t* refine, float* scales, void* stream) {
+  if (!w || !base || !refine || !scales) return nest::fail(NEST_EINVAL, "nest_pack: null pointer");
+  if (rows < 1 || cols < 2)
+    return nest::fail(NEST_EINVAL, "nest_pack: rows=%lld cols=%lld", (long long)rows, (long long)cols);
+  if (group < 2 || group % 2 || cols % group)
+    return nest::fail(NEST_ESHAPE, "nest_pack: group=%lld must be even and divide cols=%lld",
+                      (long long)group, (long long)cols);
+  return launch_pack(false, w, rows * (cols / group), group, 1, 1, base, refine, scales,
+                     nest::as_stream(stream), "nest_pack");
+}
+
+extern "C" int kv_nest_pack(const float* k, const float* v, int64_t n_kv_heads, int64_t capacity,
+                            int64_t head_dim, int64_t block, uint8_t* k_base, uint8_t* k_refine,
+                            float* k_scale, uint8_t* v_base, uint8_t* v_refine, float* v_scale,
+                            void* stream) {
+  if (!k || !v || !k_base || !k_refine || !k_scale || !v_base || !v_refine || !v_scale)
+    return nest::fail(NEST_EINVAL, "kv_nest_pack: null pointer");
+  if (n_kv_heads < 1 || capacity < 1 || head_dim < 2 || block < 2)
+    return nest::fail(NEST_EINVAL, "kv_nest_pack: bad sizes");
+  if (head_dim % 2 || block % 2 || capacity % block)
+    return nest::fail(NEST_ESHAPE, "kv_nest_pack: need even d and block, capacity %% block == 0");
+  const int64_t groups = n_kv_heads * (capacity / block), gsz = block * head_dim;
+  hipStream_t st = nest::as_stream(stream);
+  int rc = launch_pack(false, k, groups, gsz, head_dim, block, k_base, k_refine, k_scale, st,
+                       "kv_nest_pack(K)");
+  if (rc) return rc;
+  return launch_pack(true, v, groups, gsz, head_dim, block, v_base, v_refine, v_scale, st,
+                     "kv_nest_pack(V)");
+}
+
+extern "C" int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
+                              void* stream) {
+  if (!x || !qa || !sa) return nest::fail(NEST_EINVAL, "nest_act_quant: null pointer");
+  if (M < 1 || K < 1 || M > 0x7fffffffLL)
+    return nest::fail(NEST_EINVAL, "nest_act_quant: M=%lld K=%lld", (long long)M, (long long)K);
+  act_quant_kernel<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, nest::as_stream(stream)>>>(x, K, qa, sa);
+  return nest::check_launch("nest_act_quant");
+}

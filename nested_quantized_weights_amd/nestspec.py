@@ -1,0 +1,286 @@
+"""Python binding of libnestspec.so (include/nestspec.h).
+
+Argument marshalling only. Tensors give device pointers, torch's current
+stream gives the HIP stream, and every computation runs in the library's HIP
+kernels. There is no CPU fallback. If the library is missing or a call
+fails, NestError is raised.
+
+torch is imported before the library is loaded, so the library binds to the
+HIP runtime torch already loaded (same soname) and shares its device memory
+and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnestspec.so")
+
+
+class NestError(RuntimeError):
+    """A nestspec call returned an error status (or the library is missing)."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_lib = None
+_lock = threading.Lock()
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("k_base", _p), ("k_refine", _p), ("k_scale", _p), ("v_base", _p),
+                ("v_refine", _p), ("v_scale", _p), ("n_kv_heads", _i64), ("head_dim", _i64),
+                ("capacity", _i64), ("block", _i64)]
+
+
+_SIGS = {
+    "nest_last_error": (ctypes.c_char_p, []),
+    "nest_pack": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "nest_act_quant": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "draft_gemv": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
+    "draft_gemv_workspace_size": (_sz, [_i64, _i64]),
+    "verify_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p]),
+    "verify_accept": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
+                                     _p, _p, _p, _sz, _p]),
+    "verify_accept_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
+    "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _i64, ctypes.c_int, _p,
+                                      _p, _sz, _p]),
+    "kv_nest_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+}
+
+SYMBOLS = tuple(_SIGS)
+
+
+def lib():
+    """Load libnestspec.so once (raises NestError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise NestError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                                "(hipcc for gfx950) first")
+            handle = ctypes.CDLL(_LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib().nest_last_error().decode(errors="replace")
+        raise NestError(f"{what} failed (status {rc}): {msg}")
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, what: str, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise NestError(f"{what}: {name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise NestError(f"{what}: {name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise NestError(f"{what}: {name} must be contiguous")
+    return t
+
+
+# Zero-filled workspaces for the argmax / accept entry points, cached per
+# (device, stream, kind). The kernels leave them zero-filled after each call.
+_ws_cache: dict = {}
+
+
+def zeroed_workspace(nbytes: int, device: torch.device, key: str) -> torch.Tensor:
+    s = torch.cuda.current_stream(device).cuda_stream
+    k = (device.index, s, key)
+    t = _ws_cache.get(k)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[k] = t
+    return t
+
+
+def nest_pack(w: torch.Tensor, group: int = 128, out=None):
+    """fp32 [rows][cols] -> (base uint8 [rows][cols/2], refine, scales fp32 [rows][cols/group])."""
+    what = "nest_pack"
+    _dev(w, torch.float32, what, "w")
+    rows, cols = w.shape
+    if out is None:
+        out = (torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device),
+               torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device),
+               torch.empty((rows, cols // group), dtype=torch.float32, device=w.device))
+    base, refine, scales = out
+    _check(lib().nest_pack(_ptr(w), rows, cols, group, _ptr(base), _ptr(refine), _ptr(scales),
+                           _stream(w.device)), what)
+    return base, refine, scales
+
+
+def nest_act_quant(x: torch.Tensor, out=None):
+    """fp32 [M][K] -> (qa int8 [M][K], sa fp32 [M])."""
+    what = "nest_act_quant"
+    _dev(x, torch.float32, what, "x")
+    M, K = x.shape
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.int8, device=x.device),
+               torch.empty(M, dtype=torch.float32, device=x.device))
+    qa, sa = out
+    _check(lib().nest_act_quant(_ptr(x), M, K, _ptr(qa), _ptr(sa), _stream(x.device)), what)
+    return qa, sa
+
+
+def draft_gemv(qa, sa, base, scales, group: int = 128, y=None, want_y: bool = True,
+               argmax: bool = False, argmax_out=None, acc_dbg: bool = False, ws=None):
+    """W4A8 over the base plane. Returns y [M][N] (or None), plus argmax [M]
+    when asked, plus the exact int32 group sums [M][N][G] when acc_dbg."""
+    what = "draft_gemv"
+    _dev(qa, torch.int8, what, "qa")
+    _dev(sa, torch.float32, what, "sa")
+    _dev(base, torch.uint8, what, "base")
+    _dev(scales, torch.float32, what, "scales")
+    M, K = qa.shape
+    N = base.shape[0]
+    dev = qa.device
+    if y is None and (want_y or not argmax):
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    am = None
+    wsp, wsn = None, 0
+    if argmax:
+        am = argmax_out if argmax_out is not None else torch.empty(M, dtype=torch.int32, device=dev)
+        wsn = lib().draft_gemv_workspace_size(M, N)
+        if ws is None:
+            ws = zeroed_workspace(wsn, dev, "argmax")
+        wsp = _ptr(ws)
+        wsn = ws.numel()
+    acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
+    _check(lib().draft_gemv(_ptr(qa), _ptr(sa), M, K, _ptr(base), _ptr(scales), N, group, _ptr(y),
+                            _ptr(am), _ptr(acc), wsp, wsn, _stream(dev)), what)
+    out = [y]
+    if argmax:
+        out.append(am)
+    if acc_dbg:
+        out.append(acc)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def verify_gemm(qa, sa, base, refine, scales, group: int = 128, y=None, acc_dbg: bool = False):
+    """W8A8 over both planes. Returns y [M][N] (and the int32 group sums when acc_dbg)."""
+    what = "verify_gemm"
+    _dev(qa, torch.int8, what, "qa")
+    _dev(sa, torch.float32, what, "sa")
+    _dev(base, torch.uint8, what, "base")
+    _dev(refine, torch.uint8, what, "refine")
+    _dev(scales, torch.float32, what, "scales")
+    M, K = qa.shape
+    N = base.shape[0]
+    dev = qa.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
+    _check(lib().verify_gemm(_ptr(qa), _ptr(sa), M, K, _ptr(base), _ptr(refine), _ptr(scales), N,
+                             group, _ptr(y), _ptr(acc), _stream(dev)), what)
+    return (y, acc) if acc_dbg else y
+
+
+def verify_accept(qa, sa, B: int, k: int, base, refine, scales, draft, group: int = 128,
+                  want_y: bool = False, out=None, ws=None):
+    """Verify pass through the nested LM head plus the greedy accept step.
+    Returns a dict of device tensors: target [B][k+1], n_emitted [B],
+    emitted [B][k+1] (and y when want_y)."""
+    what = "verify_accept"
+    _dev(qa, torch.int8, what, "qa")
+    _dev(sa, torch.float32, what, "sa")
+    _dev(base, torch.uint8, what, "base")
+    _dev(refine, torch.uint8, what, "refine")
+    _dev(scales, torch.float32, what, "scales")
+    _dev(draft, torch.int32, what, "draft")
+    K = qa.shape[1]
+    V = base.shape[0]
+    dev = qa.device
+    if out is None:
+        out = {"target": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+               "n_emitted": torch.empty(B, dtype=torch.int32, device=dev),
+               "emitted": torch.empty((B, k + 1), dtype=torch.int32, device=dev)}
+        if want_y:
+            out["y"] = torch.empty((B * (k + 1), V), dtype=torch.float32, device=dev)
+    wsn = lib().verify_accept_workspace_size(B, k, V)
+    if ws is None:
+        ws = zeroed_workspace(wsn, dev, "argmax")
+    _check(lib().verify_accept(_ptr(qa), _ptr(sa), B, k, K, _ptr(base), _ptr(refine), _ptr(scales),
+                               V, group, _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
+                               _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(ws), ws.numel(),
+                               _stream(dev)), what)
+    return out
+
+
+class NestKV:
+    """A nested KV cache in device memory (layouts in include/nestspec.h)."""
+
+    def __init__(self, k_base, k_refine, k_scale, v_base, v_refine, v_scale, n_kv_heads,
+                 capacity, head_dim, block):
+        self.k_base, self.k_refine, self.k_scale = k_base, k_refine, k_scale
+        self.v_base, self.v_refine, self.v_scale = v_base, v_refine, v_scale
+        self.n_kv_heads, self.capacity, self.head_dim, self.block = (
+            int(n_kv_heads), int(capacity), int(head_dim), int(block))
+
+    def struct(self) -> _KV:
+        return _KV(self.k_base.data_ptr(), self.k_refine.data_ptr() if self.k_refine is not None else 0,
+                   self.k_scale.data_ptr(), self.v_base.data_ptr(),
+                   self.v_refine.data_ptr() if self.v_refine is not None else 0,
+                   self.v_scale.data_ptr(), self.n_kv_heads, self.head_dim, self.capacity, self.block)
+
+
+def kv_nest_pack(k: torch.Tensor, v: torch.Tensor, block: int = 128) -> NestKV:
+    """fp32 K and V [Hkv][capacity][d] -> NestKV."""
+    what = "kv_nest_pack"
+    _dev(k, torch.float32, what, "k")
+    _dev(v, torch.float32, what, "v")
+    Hkv, cap, d = k.shape
+    dev = k.device
+    n = Hkv * cap * d // 2
+    planes = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(4)]
+    ks = torch.empty((Hkv, cap // block), dtype=torch.float32, device=dev)
+    vs = torch.empty((Hkv, cap // block), dtype=torch.float32, device=dev)
+    _check(lib().kv_nest_pack(_ptr(k), _ptr(v), Hkv, cap, d, block, _ptr(planes[0]),
+                              _ptr(planes[1]), _ptr(ks), _ptr(planes[2]), _ptr(planes[3]),
+                              _ptr(vs), _stream(dev)), what)
+    return NestKV(planes[0], planes[1], ks, planes[2], planes[3], vs, Hkv, cap, d, block)
+
+
+def kv_nest_attend(q: torch.Tensor, kv: NestKV, ctx_len: int, view: int, out=None, ws=None):
+    """q: bf16 [nq][Hq][d] (torch.bfloat16, or its bit patterns as int16/uint16).
+    Returns fp32 [nq][Hq][d]."""
+    what = "kv_nest_attend"
+    if not isinstance(q, torch.Tensor) or not q.is_cuda or not q.is_contiguous():
+        raise NestError(f"{what}: q must be a contiguous CUDA tensor")
+    if q.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise NestError(f"{what}: q must hold bf16 bit patterns")
+    nq, Hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((nq, Hq, d), dtype=torch.float32, device=dev)
+    wsn = lib().kv_nest_attend_workspace_size(nq, Hq, kv.n_kv_heads, d, int(ctx_len))
+    if ws is None or ws.numel() < wsn:
+        ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=dev)
+    s = kv.struct()
+    _check(lib().kv_nest_attend(_ptr(q), nq, Hq, ctypes.byref(s), int(ctx_len), int(view),
+                                _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), what)
+    return out

@@ -1,0 +1,297 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+The bar:
+  * packed planes, scales, int8 activations, int32 group sums, argmax
+    indices, targets, accepted lengths and emitted tokens are bit-exact;
+  * fp32 outputs on the exact-fold paths (argmax, verify_accept) are
+    bit-identical to the oracle. Elsewhere they are within
+    (G+2) * 2^-24 * sa * sum_g |s_g A_g| of the exact value. That is the
+    rounding bound of any fold order and sits below 1e-5 relative for
+    G <= 165;
+  * attention outputs are within 2e-3 of the fp64 oracle, normwise per
+    (query, head).
+Shapes span several tiles plus a ragged tail. Every input comes from
+nested_quantized_weights_amd.synth, and every expected value from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nested_quantized_weights_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def ns():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nested_quantized_weights_amd import nestspec
+
+    nestspec.lib()  # raises if the HIP library is missing
+    return nestspec
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bound_ok(y, sa, scales, acc, step):
+    s = scales.astype(np.float64) * step
+    terms = s[None] * acc.astype(np.float64)
+    exact = sa.astype(np.float64)[:, None] * terms.sum(axis=2)
+    A = sa.astype(np.float64)[:, None] * np.abs(terms).sum(axis=2)
+    G = scales.shape[1]
+    err = np.abs(y.astype(np.float64) - exact)
+    return np.all(err <= (G + 2) * U32 * A + 1e-45), float(np.max(err / (A + 1e-300)))
+
+
+# ---------------------------------------------------------------------------
+# nest_pack / kv_nest_pack / act_quant: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,group", [(1, 128, 128), (37, 384, 128), (300, 3584, 128),
+                                             (5, 64, 4), (3, 16384, 16384), (2, 8, 8)])
+def test_nest_pack_bit_exact(ns, oracle, rows, cols, group):
+    w = synth.weights(rows, cols, (200, rows, cols))
+    if rows > 3:
+        w[3, :group] = 0.0  # an all-zero group
+    w[0, 1] = 3.0  # a group dominated by one large weight
+    b, r, s = ns.nest_pack(dev(w), group=group)
+    ob, orf, os_ = oracle.nest_pack(w, group=group)
+    assert np.array_equal(host(b), ob)
+    assert np.array_equal(host(r), orf)
+    assert np.array_equal(host(s).view(np.uint32), os_.view(np.uint32))
+
+
+def test_nest_pack_hand_example(ns):
+    import json, os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pack_hand_example.json")))
+    b, r, s = ns.nest_pack(dev(np.array(ex["w"], np.float32)), group=ex["group"])
+    assert host(b).tolist() == ex["base_bytes"]
+    assert host(r).tolist() == ex["refine_bytes"]
+    assert host(s).tolist() == ex["scales"]
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (9, 3584), (144, 4096), (3, 1000)])
+def test_act_quant_bit_exact(ns, oracle, M, K):
+    x = synth.activations(M, K, (201, M, K))
+    x[0, :7] = [127.0, -63.5, 0.5, -0.25, 2.5, -1.5, 0.0]  # ties
+    if M > 1:
+        x[1] = 0.0
+    qa, sa = ns.nest_act_quant(dev(x))
+    oq, osa = oracle.act_quant(x)
+    assert np.array_equal(host(qa), oq)
+    assert np.array_equal(host(sa).view(np.uint32), osa.view(np.uint32))
+
+
+@pytest.mark.parametrize("Hkv,cap,d,block", [(1, 128, 128, 128), (8, 384, 128, 128), (2, 64, 16, 32)])
+def test_kv_nest_pack_bit_exact(ns, oracle, Hkv, cap, d, block):
+    kf, vf = synth.kv(Hkv, cap, d, (202, Hkv, cap))
+    kv = ns.kv_nest_pack(dev(kf), dev(vf), block=block)
+    o = oracle.kv_nest_pack(kf, vf, block=block)
+    for name in ("k_base", "k_refine", "v_base", "v_refine"):
+        assert np.array_equal(host(getattr(kv, name)), o[name]), name
+    for name in ("k_scale", "v_scale"):
+        assert np.array_equal(host(getattr(kv, name)).view(np.uint32), o[name].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# draft_gemv / verify_gemm
+# ---------------------------------------------------------------------------
+
+def _layer(oracle, N, K, M, key):
+    w = synth.weights(N, K, (210,) + key)
+    x = synth.activations(M, K, (211,) + key)
+    base, refine, scales = oracle.nest_pack(w)
+    qa, sa = oracle.act_quant(x)
+    return base, refine, scales, qa, sa
+
+
+GEMV_SHAPES = [(16, 128, 1), (33, 256, 5), (100, 384, 9), (4096, 4096, 1), (4097, 3584, 16),
+               (3584, 18944, 1), (777, 1280, 5)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMV_SHAPES)
+def test_draft_gemv(ns, oracle, N, K, M):
+    base, _, scales, qa, sa = _layer(oracle, N, K, M, (N, K, M))
+    oy, oacc = oracle.draft_gemv(qa, sa, base, scales, want_acc=True)
+    y, acc = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), acc_dbg=True)
+    assert np.array_equal(host(acc), oacc)
+    ok, worst = bound_ok(host(y), sa, scales, oacc, 1.0)
+    assert ok, worst
+    # the argmax path folds exactly: y bit-identical, indices equal
+    y2, am = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), argmax=True)
+    assert np.array_equal(host(y2).view(np.uint32), oy.view(np.uint32))
+    assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMV_SHAPES + [(50, 512, 17), (200, 256, 144), (64, 384, 150)])
+def test_verify_gemm(ns, oracle, N, K, M):
+    base, refine, scales, qa, sa = _layer(oracle, N, K, M, (N, K, M, 1))
+    oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
+    y, acc = ns.verify_gemm(dev(qa), dev(sa), dev(base), dev(refine), dev(scales), acc_dbg=True)
+    assert np.array_equal(host(acc), oacc)
+    ok, worst = bound_ok(host(y), sa, scales, oacc, 1.0 / 16)
+    assert ok, worst
+    y_nodbg = ns.verify_gemm(dev(qa), dev(sa), dev(base), dev(refine), dev(scales))
+    assert np.array_equal(host(y_nodbg).view(np.uint32), host(y).view(np.uint32))
+
+
+def test_gemv_deterministic(ns, oracle):
+    base, refine, scales, qa, sa = _layer(oracle, 3584, 18944, 5, (9,))
+    args = [dev(a) for a in (qa, sa, base, refine, scales)]
+    y1 = host(ns.verify_gemm(*args))
+    y2 = host(ns.verify_gemm(*args))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_draft_reads_only_base_plane(ns, oracle):
+    # BitNest Fig. 3: the draft never touches the refinement plane, and with
+    # the refinement zeroed verify equals draft bit for bit (exact paths).
+    base, refine, scales, qa, sa = _layer(oracle, 300, 512, 1, (10,))
+    yd, _ = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), argmax=True)
+    out = ns.verify_accept(dev(qa), dev(sa), 1, 0, dev(base), dev(np.zeros_like(refine)),
+                           dev(scales), dev(np.zeros(0, np.int32)), want_y=True)
+    assert np.array_equal(host(yd).view(np.uint32), host(out["y"]).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# verify_accept: LM head + argmax + greedy accept
+# ---------------------------------------------------------------------------
+
+def test_table1_worked_round_on_gpu(ns, oracle):
+    import json, os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "table1_round.json")))
+    vocab = ex["vocab"]
+    ids = {t: i for i, t in enumerate(vocab)}
+    k, V, K = ex["k"], len(vocab), 128
+    w = np.zeros((V, K), np.float32)
+    w[np.arange(V), np.arange(V)] = 1.0
+    x = np.zeros((k + 1, K), np.float32)
+    for i, t in enumerate(ex["target_choices"]):
+        x[i, ids[t]] = 1.0
+    b, r, s = ns.nest_pack(dev(w))
+    qa, sa = ns.nest_act_quant(dev(x))
+    draft = dev(np.array([ids[t] for t in ex["draft"]], np.int32))
+    out = ns.verify_accept(qa, sa, 1, k, b, r, s, draft)
+    n = int(host(out["n_emitted"])[0])
+    assert n == ex["expected_n_emitted"]
+    assert [vocab[t] for t in host(out["emitted"])[0][:n]] == ex["expected_emitted"]
+
+
+@pytest.mark.parametrize("V,K,B,k,alpha", [(1000, 256, 1, 8, 0.66), (4099, 512, 1, 4, 0.95),
+                                           (2500, 384, 2, 3, 0.58), (640, 128, 1, 0, 0.5),
+                                           (20000, 3584, 1, 15, 0.9)])
+def test_verify_accept(ns, oracle, V, K, B, k, alpha):
+    w = synth.weights(V, K, (220, V, K))
+    x = synth.activations(B * (k + 1), K, (221, V, K))
+    base, refine, scales = oracle.nest_pack(w)
+    qa, sa = oracle.act_quant(x)
+    t_ref = oracle.verify_gemm(qa, sa, base, refine, scales).argmax(axis=1).reshape(B, k + 1)
+    draft = synth.plant_drafts(t_ref, alpha, V, (222, V))
+    o = oracle.verify_accept(qa, sa, B, k, base, refine, scales, draft, want_y=True)
+    for rep in range(3):  # also checks the workspace is left ready for the next call
+        g = ns.verify_accept(dev(qa), dev(sa), B, k, dev(base), dev(refine), dev(scales),
+                             dev(draft.reshape(-1) if k else np.zeros(0, np.int32)), want_y=True)
+        assert np.array_equal(host(g["target"]), o["target"])
+        assert np.array_equal(host(g["n_emitted"]), o["n_emitted"])
+        assert np.array_equal(host(g["emitted"]), o["emitted"])
+        assert np.array_equal(host(g["y"]).view(np.uint32), o["y"].view(np.uint32))
+
+
+def test_argmax_ties_take_lowest_index(ns, oracle):
+    # Two identical LM-head rows tie on every logit: the lower index wins.
+    V, K = 500, 256
+    w = synth.weights(V, K, (223,))
+    w[300] = w[77]
+    w[77] *= 10.0
+    w[300] = w[77]
+    base, refine, scales = oracle.nest_pack(w)
+    x = w[77:78].copy()
+    qa, sa = oracle.act_quant(x)
+    _, am = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), argmax=True)
+    oy = oracle.draft_gemv(qa, sa, base, scales)
+    assert int(host(am)[0]) == oracle.argmax(oy[0]) == 77
+
+
+# ---------------------------------------------------------------------------
+# kv_nest_attend
+# ---------------------------------------------------------------------------
+
+def _rel_err(o, ref):
+    num = np.linalg.norm(o - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return float(np.max(num / den))
+
+
+@pytest.mark.parametrize("view", [0, 1])
+@pytest.mark.parametrize("Hq,Hkv,cap,ctx,nq", [(32, 8, 256, 256, 1), (32, 8, 384, 300, 9),
+                                               (28, 4, 512, 389, 5), (4, 1, 128, 1, 1),
+                                               (8, 8, 1024, 1000, 8), (16, 2, 2048, 2048, 8)])
+def test_kv_attend(ns, oracle, view, Hq, Hkv, cap, ctx, nq):
+    d = 128
+    kf, vf = synth.kv(Hkv, cap, d, (230, Hq, cap))
+    q = synth.queries_bf16(nq, Hq, d, (231, Hq, nq))
+    okv = oracle.kv_nest_pack(kf, vf)
+    ref = oracle.kv_attend(q, okv, ctx, view)
+    kv = ns.kv_nest_pack(dev(kf), dev(vf))
+    out = host(ns.kv_nest_attend(dev(q.view(np.int16)), kv, ctx, view))
+    assert _rel_err(out, ref) <= 2e-3
+
+
+@pytest.mark.parametrize("view", [0, 1])
+def test_kv_attend_ignores_entries_past_ctx(ns, oracle, view):
+    Hkv, Hq, cap, d, ctx, nq = 2, 8, 512, 128, 300, 5
+    kf, vf = synth.kv(Hkv, cap, d, (232,))
+    q = dev(synth.queries_bf16(nq, Hq, d, (233,)).view(np.int16))
+    kv = ns.kv_nest_pack(dev(kf), dev(vf))
+    ref = host(ns.kv_nest_attend(q, kv, ctx, view))
+    # poison every plane byte past ctx (K token-major, V dim-major per block)
+    g = synth.rng(234)
+    kb = kv.k_base.view(Hkv, cap, d // 2)
+    kr = kv.k_refine.view(Hkv, cap, d // 2)
+    kb[:, ctx:] = dev(g.integers(0, 256, size=(Hkv, cap - ctx, d // 2), dtype=np.uint8))
+    kr[:, ctx:] = dev(g.integers(0, 256, size=(Hkv, cap - ctx, d // 2), dtype=np.uint8))
+    for t in (kv.v_base, kv.v_refine):
+        v = t.view(Hkv, cap // 128, d, 64)
+        b0, t0 = divmod(ctx, 128)
+        v[:, b0, :, t0 // 2:] = dev(g.integers(0, 256, size=(Hkv, d, 64 - t0 // 2), dtype=np.uint8))
+        v[:, b0 + 1:] = dev(g.integers(0, 256, size=(Hkv, cap // 128 - b0 - 1, d, 64), dtype=np.uint8))
+    kv.k_scale[:, (ctx + 127) // 128:] = 1e30
+    kv.v_scale[:, (ctx + 127) // 128:] = 1e30
+    out = host(ns.kv_nest_attend(q, kv, ctx, view))
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_kv_attend_deterministic(ns):
+    kf, vf = synth.kv(8, 4096, 128, (235,))
+    q = dev(synth.queries_bf16(9, 32, 128, (236,)).view(np.int16))
+    kv = ns.kv_nest_pack(dev(kf), dev(vf))
+    a = host(ns.kv_nest_attend(q, kv, 4000, 1))
+    b = host(ns.kv_nest_attend(q, kv, 4000, 1))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# error paths through the C ABI (host-side validation)
+# ---------------------------------------------------------------------------
+
+def test_errors_are_reported(ns):
+    qa = torch.zeros((1, 200), dtype=torch.int8, device="cuda")
+    sa = torch.zeros(1, dtype=torch.float32, device="cuda")
+    base = torch.zeros((16, 100), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((16, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(ns.NestError, match="multiple of 128"):
+        ns.draft_gemv(qa, sa, base, sc)
+    qa = torch.zeros((17, 128), dtype=torch.int8, device="cuda")
+    base = torch.zeros((16, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ns.NestError, match="M=17"):
+        ns.draft_gemv(qa, torch.zeros(17, dtype=torch.float32, device="cuda"), base, sc)

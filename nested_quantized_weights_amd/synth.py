@@ -27,6 +27,8 @@ Activations, K, V and queries ~ N(0, 1). Queries are rounded to bf16
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 SEED = 0
@@ -61,11 +63,38 @@ def rng(*key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(SEED, spawn_key=key)))
 
 
-def normal(shape, key, std: float = 1.0) -> np.ndarray:
-    """float32 normal draws, scaled by ``std`` in float32."""
-    a = rng(*key).standard_normal(size=shape, dtype=np.float32)
+CHUNK = 1 << 22  # elements per independently seeded chunk of a large tensor
+MAX_THREADS = 16  # a one-GPU host share
+
+
+def _fill(out: np.ndarray, key, std: float) -> None:
+    rng(*key).standard_normal(out=out, dtype=np.float32)
     if std != 1.0:
-        a *= np.float32(std)
+        out *= np.float32(std)
+
+
+def normal(shape, key, std: float = 1.0) -> np.ndarray:
+    """float32 normal draws, scaled by ``std`` in float32.
+
+    A tensor of at most CHUNK elements is one stream with spawn key ``key``.
+    A larger one is cut along its first axis into slabs of about CHUNK
+    elements. Slab c draws from spawn key ``key + (c,)``, so the values do
+    not depend on how many threads fill them.
+    """
+    shape = tuple(int(s) for s in np.atleast_1d(shape))
+    a = np.empty(shape, dtype=np.float32)
+    key = tuple(key)
+    if a.size <= CHUNK or len(shape) == 1:
+        _fill(a, key, std)
+        return a
+    row = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    rows_per = max(1, CHUNK // max(row, 1))
+    slabs = [(c, a[r:r + rows_per]) for c, r in enumerate(range(0, shape[0], rows_per))]
+    import concurrent.futures as cf
+
+    workers = min(len(slabs), MAX_THREADS, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda cs: _fill(cs[1], key + (cs[0],), std), slabs))
     return a
 
 

@@ -157,7 +157,7 @@ class Round:
         acc_out = {"target": E(k + 1, dtype=torch.int32, device=cuda),
                    "n": E(1, dtype=torch.int32, device=cuda),
                    "emitted": E(k + 1, dtype=torch.int32, device=cuda)}
-        ws_arg = ns.zeroed_workspace(max(L.draft_gemv_workspace_size(1, V),
+        ws_arg = ns.workspace(max(L.draft_gemv_workspace_size(1, V),
                                          L.verify_accept_workspace_size(1, k, V)),
                                      torch.device(cuda), "argmax")
         ws_att_n = max(L.kv_nest_attend_workspace_size(1, hq, hkv, 128, CAPACITY),

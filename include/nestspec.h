@@ -156,10 +156,9 @@ int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
  *   argmax   int32 [M] (out, nullable). When given, the fold is exact and
  *            argmax[m] is the index of the largest y[m][.].
  *   acc_dbg  int32 [M][N][K/group] (out, nullable): the exact Ab.
- *   ws       workspace of draft_gemv_workspace_size(M, N) bytes. It is
- *            needed only when argmax is given (else it may be NULL). It must
- *            be zero-filled before its first use, and every completed call
- *            leaves it zero-filled again.
+ *   ws       workspace of draft_gemv_workspace_size(M, N) bytes, needed
+ *            only when argmax is given (else it may be NULL). It holds
+ *            per-block partial maxima; no initial contents are required.
  * Requires 1 <= M <= 16, group == 128, K % 128 == 0, N >= 1.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
@@ -198,9 +197,8 @@ int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
  *             d_i == t_{i-1} for all 1 <= i <= j
  *   emitted   int32 [B][k+1] (out): t_0..t_a, then -1 in the unused slots
  *   y         fp32 [B*(k+1)][V] (out, nullable): the verify logits
- *   ws        verify_accept_workspace_size(B, k, V) bytes, zero-filled
- *             before its first use. Every completed call leaves it
- *             zero-filled.
+ *   ws        verify_accept_workspace_size(B, k, V) bytes (per-block
+ *             partial maxima; no initial contents are required).
  * Requires B >= 1, k >= 0, B*(k+1) <= 16, group == 128, K % 128 == 0.
  * Draft ids are not read on the host, so an id outside [0, V) simply
  * never matches. Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE,

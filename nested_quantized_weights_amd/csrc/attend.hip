@@ -289,23 +289,53 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   }
 }
 
-// One block of 128 threads per (row, kv head); thread = dim.
-__global__ void __launch_bounds__(128) combine_kernel(AttArgs a) {
-  const int row = blockIdx.x, h = blockIdx.y, dim = threadIdx.x;
+// One block of 256 threads per (row, kv head). The chunk weights
+// 2^(m_c - M) go to LDS. Then each half-block sums the chunks of one parity
+// for all 128 dims, and the two halves are added (a fixed order).
+constexpr int kCombineChunks = 1024;  // chunks handled per LDS pass
+
+__global__ void __launch_bounds__(256) combine_kernel(AttArgs a) {
+  __shared__ float wts[kCombineChunks];
+  __shared__ float red[8];
+  __shared__ float half_acc[kD];
+  const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const size_t base = static_cast<size_t>(h) * a.nchunk * a.R + row;  // partial of chunk c: base + c*R
   float M = -INFINITY;
-  for (int c = 0; c < a.nchunk; ++c)
-    M = fmaxf(M, a.part_ml[((static_cast<size_t>(h) * a.nchunk + c) * a.R + row) * 2]);
+  for (int c = t; c < a.nchunk; c += 256) M = fmaxf(M, a.part_ml[(base + static_cast<size_t>(c) * a.R) * 2]);
+  M = wave_max(M);
+  if ((t & 63) == 0) red[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float Mu = M == -INFINITY ? 0.0f : M;
+  __syncthreads();
   float L = 0.0f, acc = 0.0f;
-  for (int c = 0; c < a.nchunk; ++c) {
-    const size_t pr = (static_cast<size_t>(h) * a.nchunk + c) * a.R + row;
-    const float mc = a.part_ml[pr * 2];
-    if (mc == -INFINITY) continue;
-    const float w = exp2f(mc - M);
-    L += a.part_ml[pr * 2 + 1] * w;
-    acc += a.part_o[pr * kD + dim] * w;
+  const int dim = t & (kD - 1), par = t >> 7;
+  for (int c0 = 0; c0 < a.nchunk; c0 += kCombineChunks) {
+    const int cn = min(kCombineChunks, a.nchunk - c0);
+    for (int c = t; c < cn; c += 256) {
+      const size_t pr = base + static_cast<size_t>(c0 + c) * a.R;
+      const float mc = a.part_ml[pr * 2];
+      const float w = mc == -INFINITY ? 0.0f : exp2f(mc - Mu);
+      wts[c] = w;
+      L += w * a.part_ml[pr * 2 + 1];
+    }
+    __syncthreads();
+    for (int c = par; c < cn; c += 2) {
+      const float w = wts[c];
+      if (w != 0.0f) acc += a.part_o[(base + static_cast<size_t>(c0 + c) * a.R) * kD + dim] * w;
+    }
+    __syncthreads();
   }
-  const int i = row / a.grp, g = row % a.grp;
-  a.out[(static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + dim] = acc / L;
+  // total denominator: block sum of L
+  L = wave_sum(L);
+  if ((t & 63) == 0) red[4 + (t >> 6)] = L;
+  if (par == 1) half_acc[dim] = acc;
+  __syncthreads();
+  if (par == 0) {
+    const float Lt = (red[4] + red[5]) + (red[6] + red[7]);
+    const int i = row / a.grp, g = row % a.grp;
+    a.out[(static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + dim] = (acc + half_acc[dim]) / Lt;
+  }
 }
 
 struct Plan {
@@ -337,7 +367,7 @@ int launch_att(const AttArgs& a, const Plan& p, int Hkv, hipStream_t st) {
   }
   int rc = nest::check_launch("kv_nest_attend");
   if (rc) return rc;
-  combine_kernel<<<dim3(a.R, Hkv), 128, 0, st>>>(a);
+  combine_kernel<<<dim3(a.R, Hkv), 256, 0, st>>>(a);
   return nest::check_launch("kv_nest_attend(combine)");
 }
 

@@ -48,6 +48,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Wave-wide sum of a float (butterfly order, all lanes end with the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 // Orderable 64-bit argmax key: larger value first, then the lower index.
 // -0 is folded to +0 so that equal values tie on the index.
 __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {

@@ -1,32 +1,42 @@
-// Draft and verify products over the dual-plane nested weights (BitNest,
-// Figure 3: the draft reads the base plane, the target reads both), the
-// fused LM-head argmax, and the greedy accept step of a round ("How
-// Speculative Decoding Speeds Up Inference", numbered round steps, Table 1).
+// Draft and verify products for up to 16 activation rows over the dual-plane
+// nested weights (BitNest, Figure 3: the draft reads the base plane, the
+// target reads both), the fused LM-head argmax, and the greedy accept step
+// of a round ("How Speculative Decoding Speeds Up Inference", numbered round
+// steps, Table 1).
 //
-// Layout on gfx950. One wave owns a tile of 16 weight rows. Per group of
-// 128 weights, lane l loads 16 bytes of each plane: row (l & 15) of the
-// tile, k-quarter (l >> 4). The nibbles become int8 operands of
-// v_mfma_i32_16x16x64_i8 without any cross-lane traffic:
-//   even elements: (w << 4) & 0xF0F0F0F0   (16 * code)
-//   odd  elements:  w       & 0xF0F0F0F0   (16 * code)
-// The activation operand holds the same k-quarter of activation row
-// (l & 15). It is split into even and odd bytes by v_perm_b32 to match. One
-// group is two MFMAs per plane. The D tile gives lane l column m = l & 15
-// and rows 4*(l>>4)+r, so the per-group fp32 fold stays in registers and
-// runs in ascending group order, as the reference fold does.
+// gfx950 mapping. One wave owns a tile of 16 weight rows. Per group of 128
+// weights, v_mfma_i32_16x16x64_i8 takes the activations as the A operand
+// (row m = lane & 15) and the weights as the B operand (column n = tile row
+// lane & 15). Both operands are built from raw bytes (see nibble.h). D then
+// gives lane l the entries m = 4*(l>>4) + r, n = n0 + (l & 15). All M <= 4
+// rows sit in registers r < M of lanes 0..15, so a one-row draft folds a
+// single register, and each lane needs the scale of only one weight row.
+// The fp32 fold runs in registers in ascending group order, as the
+// reference fold does:
 //   draft:  A_b = R_b >> 4,            run = fmaf(s,        A_b, run)
 //   verify: A_v = R_b + (R_r >> 4),    run = fmaf(s * 2^-4, A_v, run)
-// where R_b and R_r are the MFMA sums over 16*q_b and 16*q_r (all exact
-// int32). With one segment per tile the result is bit-identical to the
-// reference fold. With S > 1 segments the waves of a block fold contiguous
-// group ranges, and their partial sums are added in segment order.
-#include "common.h"
+// R_b and R_r are the exact int32 MFMA sums over 16*q_b and 16*q_r. With
+// one segment per tile the result is bit-identical to the reference. With
+// S > 1 segments, the waves of a block fold contiguous group ranges, and
+// the partial sums are added in segment order.
+//
+// When the M x K activation bytes fit, each block stages them once in LDS,
+// already split into even/odd operand order, so the main loop streams
+// only the planes and scales from HBM. Blocks loop over tiles with a grid
+// stride, and the grid is at most what fits on the chip. The argmax path
+// keeps per-lane best (value, index) keys across tiles and writes one key
+// per row and block. A second small kernel reduces the keys and, for
+// verify_accept, applies the accept rule. The kernel boundary makes the
+// keys visible, with no cross-block fence or atomic.
+#include "nibble.h"
 
 namespace {
 
-constexpr int kGroup = 128;
-constexpr unsigned kHiNib = 0xF0F0F0F0u;
-constexpr int kWsHeader = 256;  // bytes: the arrival counter, padded
+using nest::kGroup;
+using nest::ld16;
+
+constexpr int kMaxArgmaxBlocks = 4096;
+constexpr int kLdsActMax = 48 * 1024;  // largest M*K staged in LDS
 
 struct GemvArgs {
   const int8_t* qa;
@@ -35,289 +45,257 @@ struct GemvArgs {
   const uint8_t* base;
   const uint8_t* refine;
   const float* scales;
-  int N, G;
-  int nseg;
+  int N, G, nseg;
   float* y;
   int32_t* acc_dbg;
-  // argmax / accept epilogue
-  unsigned int* counter;
-  unsigned long long* partials;  // [gridDim.x][16]
-  int32_t* argmax_out;           // [M] (draft) or unused (accept)
-  int B, k;                      // accept: B sequences of k+1 rows
+  unsigned long long* partials;  // argmax: [gridDim.x][16]
+};
+
+struct FinishArgs {
+  const unsigned long long* partials;
+  int nparts, M;
+  int32_t* argmax_out;  // draft: [M]
+  int B, k;             // accept: B sequences of k+1 rows
   const int32_t* draft;
   int32_t* target;
   int32_t* n_emitted;
   int32_t* emitted;
 };
 
-__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+// LDS slot of the even (p = 0) or odd (p = 1) operand of activation row m,
+// k-quarter kq, group g.
+__device__ __forceinline__ int lds_slot(int g, int p, int kq, int m, int M) {
+  return ((g * 2 + p) * 4 + kq) * M + m;
 }
 
-// 32 activation bytes (elements 0..31 of a k-quarter) -> even / odd operands.
-__device__ __forceinline__ void split_act(uint4 a0, uint4 a1, v4i& be, v4i& bo) {
-  be[0] = __builtin_amdgcn_perm(a0.y, a0.x, 0x06040200u);
-  be[1] = __builtin_amdgcn_perm(a0.w, a0.z, 0x06040200u);
-  be[2] = __builtin_amdgcn_perm(a1.y, a1.x, 0x06040200u);
-  be[3] = __builtin_amdgcn_perm(a1.w, a1.z, 0x06040200u);
-  bo[0] = __builtin_amdgcn_perm(a0.y, a0.x, 0x07050301u);
-  bo[1] = __builtin_amdgcn_perm(a0.w, a0.z, 0x07050301u);
-  bo[2] = __builtin_amdgcn_perm(a1.y, a1.x, 0x07050301u);
-  bo[3] = __builtin_amdgcn_perm(a1.w, a1.z, 0x07050301u);
-}
-
-// 16 plane bytes (32 nibbles) -> even / odd operands holding 16 * code.
-__device__ __forceinline__ void split_nib(uint4 w, v4i& e, v4i& o) {
-  e[0] = (w.x << 4) & kHiNib;
-  e[1] = (w.y << 4) & kHiNib;
-  e[2] = (w.z << 4) & kHiNib;
-  e[3] = (w.w << 4) & kHiNib;
-  o[0] = w.x & kHiNib;
-  o[1] = w.y & kHiNib;
-  o[2] = w.z & kHiNib;
-  o[3] = w.w & kHiNib;
-}
-
-template <int PLANES, int CT>
-struct GroupData {
-  uint4 wb, wr;
-  float s[4];
-};
-
-// One group of the tile: accumulate into run[CT][4].
-template <int PLANES, int CT, bool DBG>
-__device__ __forceinline__ void do_group(const GemvArgs& a, const GroupData<PLANES, CT>& d,
-                                         const int8_t* pa, int g, int col, int n_out0,
-                                         const uint4* pre_a, float (&run)[CT][4]) {
-  v4i wbe, wbo, wre, wro;  // weight operands: base / refine, even / odd
-  split_nib(d.wb, wbe, wbo);
-  if (PLANES == 2) split_nib(d.wr, wre, wro);
-  float sc[4];
+template <int PLANES, int MR, bool DBG, bool LDSACT>
+__device__ __forceinline__ void gemv_group(const GemvArgs& a, const uint4* lds, const int8_t* pa, int kq,
+                                           int mrow, int n, int g, uint4 wb, uint4 wr, float s,
+                                           float (&run)[MR]) {
+  v4i xe, xo;
+  if (LDSACT) {
+    xe = __builtin_bit_cast(v4i, lds[lds_slot(g, 0, kq, mrow, a.M)]);
+    xo = __builtin_bit_cast(v4i, lds[lds_slot(g, 1, kq, mrow, a.M)]);
+  } else {
+    const int8_t* p = pa + static_cast<size_t>(g) * kGroup;
+    nest::split_act(ld16(p), ld16(p + 16), xe, xo);
+  }
+  v4i wbe, wbo;
+  nest::split_nib(wb, wbe, wbo);
+  const v4i z = {0, 0, 0, 0};
+  v4i rb = nest::mfma_i8(xe, wbe, z);
+  rb = nest::mfma_i8(xo, wbo, rb);
+  v4i acc;
+  if (PLANES == 2) {
+    v4i wre, wro;
+    nest::split_nib(wr, wre, wro);
+    v4i rr = nest::mfma_i8(xe, wre, z);
+    rr = nest::mfma_i8(xo, wro, rr);
+    acc = rb + (rr >> 4);
+  } else {
+    acc = rb >> 4;
+  }
+  const float sc = PLANES == 2 ? s * 0.0625f : s;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sc[r] = PLANES == 2 ? d.s[r] * 0.0625f : d.s[r];
+  for (int r = 0; r < MR; ++r) run[r] = fmaf(sc, static_cast<float>(acc[r]), run[r]);
+  if (DBG && n < a.N) {
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    uint4 a0, a1;
-    if (pre_a) {
-      a0 = pre_a[0];
-      a1 = pre_a[1];
-    } else {
-      const int m = c * 16 + col;
-      if (m < a.M) {
-        const int8_t* p = pa + static_cast<size_t>(c * 16) * a.K + static_cast<size_t>(g) * kGroup;
-        a0 = *reinterpret_cast<const uint4*>(p);
-        a1 = *reinterpret_cast<const uint4*>(p + 16);
+    for (int r = 0; r < MR; ++r) {
+      const int m = 4 * kq + r;
+      if (m < a.M) a.acc_dbg[(static_cast<size_t>(m) * a.N + n) * a.G + g] = acc[r];
+    }
+  }
+}
+
+// Fold groups [g0, g1) of one tile. A4: G % 4 == 0 and the segment is
+// 4-aligned, so the lane's scales load as one float4 per four groups and
+// the plane stream is software-pipelined by four groups.
+template <int PLANES, int MR, bool DBG, bool A4, bool LDSACT>
+__device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds, const uint8_t* pb,
+                                             const uint8_t* pr, const float* ps, const int8_t* pa,
+                                             int kq, int mrow, int n, int g0, int g1, float (&run)[MR]) {
+  if (A4) {
+    uint4 b0, b1, b2, b3, r0, r1, r2, r3;
+    auto load = [&](int g, uint4& x0, uint4& x1, uint4& x2, uint4& x3, uint4& y0, uint4& y1,
+                    uint4& y2, uint4& y3) {
+      x0 = ld16(pb + static_cast<size_t>(g) * 64);
+      x1 = ld16(pb + static_cast<size_t>(g + 1) * 64);
+      x2 = ld16(pb + static_cast<size_t>(g + 2) * 64);
+      x3 = ld16(pb + static_cast<size_t>(g + 3) * 64);
+      if (PLANES == 2) {
+        y0 = ld16(pr + static_cast<size_t>(g) * 64);
+        y1 = ld16(pr + static_cast<size_t>(g + 1) * 64);
+        y2 = ld16(pr + static_cast<size_t>(g + 2) * 64);
+        y3 = ld16(pr + static_cast<size_t>(g + 3) * 64);
       } else {
-        a0 = make_uint4(0, 0, 0, 0);
-        a1 = a0;
+        y0 = y1 = y2 = y3 = make_uint4(0, 0, 0, 0);
       }
+    };
+    if (g0 < g1) load(g0, b0, b1, b2, b3, r0, r1, r2, r3);
+    for (int g = g0; g < g1; g += 4) {
+      uint4 nb0, nb1, nb2, nb3, nr0, nr1, nr2, nr3;
+      if (g + 4 < g1) load(g + 4, nb0, nb1, nb2, nb3, nr0, nr1, nr2, nr3);
+      const float4 s = *reinterpret_cast<const float4*>(ps + g);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, b0, r0, s.x, run);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 1, b1, r1, s.y, run);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 2, b2, r2, s.z, run);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 3, b3, r3, s.w, run);
+      b0 = nb0; b1 = nb1; b2 = nb2; b3 = nb3;
+      r0 = nr0; r1 = nr1; r2 = nr2; r3 = nr3;
     }
-    v4i xe, xo;
-    split_act(a0, a1, xe, xo);
-    const v4i z = {0, 0, 0, 0};
-    v4i rb = mfma_i8(wbe, xe, z);
-    rb = mfma_i8(wbo, xo, rb);
-    v4i acc;
-    if (PLANES == 2) {
-      v4i rr = mfma_i8(wre, xe, z);
-      rr = mfma_i8(wro, xo, rr);
-      acc = rb + (rr >> 4);
-    } else {
-      acc = rb >> 4;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) run[c][r] = fmaf(sc[r], static_cast<float>(acc[r]), run[c][r]);
-    if (DBG) {
-      const int m = c * 16 + col;
-      if (m < a.M) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = n_out0 + r;
-          if (n < a.N) a.acc_dbg[(static_cast<size_t>(m) * a.N + n) * a.G + g] = acc[r];
-        }
-      }
+  } else {
+    for (int g = g0; g < g1; ++g) {
+      const uint4 wb = ld16(pb + static_cast<size_t>(g) * 64);
+      const uint4 wr = PLANES == 2 ? ld16(pr + static_cast<size_t>(g) * 64) : make_uint4(0, 0, 0, 0);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, wb, wr, ps[g], run);
     }
   }
 }
 
 // WAVES waves per block; a tile takes nseg consecutive waves (nseg | WAVES).
-// ARGMAX requires nseg == 1 and CT == 1. ACCEPT implies ARGMAX.
-template <int PLANES, int CT, int WAVES, bool ARGMAX, bool ACCEPT, bool DBG>
+// ARGMAX requires nseg == 1.
+template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT>
 __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
+  extern __shared__ uint4 lds_act[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int S = a.nseg;
-  const int tile = blockIdx.x * (WAVES / S) + wave / S;
-  const int seg = wave % S;
-  const int n0 = tile * 16;
-  const bool tile_ok = n0 < a.N;
-  const int G = a.G;
-  const int g_begin = static_cast<int>(static_cast<long long>(seg) * G / S);
-  const int g_end = static_cast<int>(static_cast<long long>(seg + 1) * G / S);
-
-  const int kq = lane >> 4, col = lane & 15;
-  const int n_out0 = n0 + 4 * kq;  // rows of this lane's D entries: n_out0 + r
+  const int S = a.nseg, per_iter = WAVES / S;
+  const int T = (a.N + 15) / 16, iters = (T + per_iter - 1) / per_iter;
+  const int seg = wave % S, G = a.G;
+  const int unit = A4 ? 4 : 1, units = G / unit;
+  const int g_begin = static_cast<int>(static_cast<long long>(seg) * units / S) * unit;
+  const int g_end = static_cast<int>(static_cast<long long>(seg + 1) * units / S) * unit;
+  const int kq = lane >> 4, c = lane & 15;
+  const int mrow = min(c, a.M - 1);  // A-operand row of this lane (rows past M fill unused D rows)
   const size_t rowb = static_cast<size_t>(a.K / 2);
-  const int arow = min(n0 + col, a.N - 1);
-  const uint8_t* pb = a.base + arow * rowb + kq * 16;
-  const uint8_t* pr = PLANES == 2 ? a.refine + arow * rowb + kq * 16 : nullptr;
-  const int8_t* pa = a.qa + static_cast<size_t>(col) * a.K + kq * 32;  // row c*16+col, added per tile
-  const float* ps[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ps[r] = a.scales + static_cast<size_t>(min(n_out0 + r, a.N - 1)) * G;
+  const int8_t* pa = a.qa + static_cast<size_t>(mrow) * a.K + kq * 32;
 
-  float run[CT][4];
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) run[c][r] = 0.0f;
+  if (LDSACT) {
+    // stage all M x K activation bytes once, split into operand order
+    const int units32 = a.M * G * 4;
+    for (int u = threadIdx.x; u < units32; u += WAVES * 64) {
+      const int m = u % a.M, rest = u / a.M, q = rest & 3, g = rest >> 2;
+      const int8_t* src = a.qa + static_cast<size_t>(m) * a.K + g * kGroup + q * 32;
+      v4i e, o;
+      nest::split_act(ld16(src), ld16(src + 16), e, o);
+      lds_act[lds_slot(g, 0, q, m, a.M)] = __builtin_bit_cast(uint4, e);
+      lds_act[lds_slot(g, 1, q, m, a.M)] = __builtin_bit_cast(uint4, o);
+    }
+    __syncthreads();
+  }
 
-  if (tile_ok) {
-    constexpr int U = CT == 1 ? 4 : 2;
-    int g = g_begin;
-    for (; g + U <= g_end; g += U) {
-      GroupData<PLANES, CT> d[U];
-      uint4 act[U][2];
+  unsigned long long best[MR];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        d[u].wb = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(g + u) * 64);
-        if (PLANES == 2) d[u].wr = *reinterpret_cast<const uint4*>(pr + static_cast<size_t>(g + u) * 64);
+  for (int r = 0; r < MR; ++r) best[r] = 0;
+  float s_a[MR];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[u].s[r] = ps[r][g + u];
-        if (CT == 1) {
-          if (col < a.M) {
-            const int8_t* p = pa + static_cast<size_t>(g + u) * kGroup;
-            act[u][0] = *reinterpret_cast<const uint4*>(p);
-            act[u][1] = *reinterpret_cast<const uint4*>(p + 16);
-          } else {
-            act[u][0] = make_uint4(0, 0, 0, 0);
-            act[u][1] = act[u][0];
+  for (int r = 0; r < MR; ++r) s_a[r] = a.sa[min(4 * kq + r, a.M - 1)];
+
+  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
+    const int n0 = (it * per_iter + wave / S) * 16;
+    const bool tile_ok = n0 < a.N;
+    const int n = n0 + c;  // this lane's output column (weight row)
+    const int wrow = min(n, a.N - 1);
+    const uint8_t* pb = a.base + wrow * rowb + kq * 16;
+    const uint8_t* pr = PLANES == 2 ? a.refine + wrow * rowb + kq * 16 : nullptr;
+    const float* ps = a.scales + static_cast<size_t>(wrow) * G;
+    float run[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) run[r] = 0.0f;
+    if (tile_ok)
+      gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, pb, pr, ps, pa, kq, mrow, n, g_begin,
+                                                g_end, run);
+
+    if (ARGMAX) {
+      if (tile_ok && n < a.N) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          if (4 * kq + r < a.M) {
+            const float v = run[r] * s_a[r];
+            if (a.y) a.y[static_cast<size_t>(4 * kq + r) * a.N + n] = v;
+            best[r] = umax64(best[r], argmax_key(v, static_cast<uint32_t>(n)));
           }
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        do_group<PLANES, CT, DBG>(a, d[u], pa, g + u, col, n_out0, CT == 1 ? act[u] : nullptr, run);
+      continue;
     }
-    for (; g < g_end; ++g) {
-      GroupData<PLANES, CT> d;
-      d.wb = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(g) * 64);
-      if (PLANES == 2) d.wr = *reinterpret_cast<const uint4*>(pr + static_cast<size_t>(g) * 64);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d.s[r] = ps[r][g];
-      do_group<PLANES, CT, DBG>(a, d, pa, g, col, n_out0, nullptr, run);
-    }
-  }
 
-  if (!ARGMAX) {
-    float tot[CT][4];
-    if (WAVES > 1 && S > 1) {
-      __shared__ float part[WAVES][CT][4][64];
+    float tot[MR];
+    if (S > 1) {
+      __shared__ float part[WAVES][MR][64];
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[wave][c][r][lane] = run[c][r];
+      for (int r = 0; r < MR; ++r) part[wave][r][lane] = run[r];
       __syncthreads();
-      if (seg != 0) return;
+      if (seg == 0) {
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float t = part[wave][c][r][lane];
-          for (int s = 1; s < S; ++s) t += part[wave + s][c][r][lane];
-          tot[c][r] = t;
+        for (int r = 0; r < MR; ++r) {
+          float t = part[wave][r][lane];
+          for (int s2 = 1; s2 < S; ++s2) t += part[wave + s2][r][lane];
+          tot[r] = t;
         }
+      }
+      __syncthreads();
     } else {
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tot[c][r] = run[c][r];
+      for (int r = 0; r < MR; ++r) tot[r] = run[r];
     }
-    if (!tile_ok) return;
+    if (seg != 0 || !tile_ok || n >= a.N) continue;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int m = c * 16 + col;
-      if (m >= a.M) continue;
-      const float s_a = a.sa[m];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n_out0 + r;
-        if (n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = tot[c][r] * s_a;
-      }
+    for (int r = 0; r < MR; ++r) {
+      const int m = 4 * kq + r;
+      if (m < a.M) a.y[static_cast<size_t>(m) * a.N + n] = tot[r] * s_a[r];
     }
-    return;
   }
 
-  // ---- argmax epilogue (nseg == 1, CT == 1): exact fold, per-block best ----
-  __shared__ unsigned long long best[WAVES][16];
-  __shared__ unsigned long long red[WAVES * 4][16];
-  __shared__ int32_t tgt[16];
-  __shared__ int last;
-  {
-    unsigned long long key = 0;
-    if (tile_ok && col < a.M) {
-      const float s_a = a.sa[col];
+  if (ARGMAX) {
+    // best over the 16 lanes of each k-quarter group, then over the waves
+    __shared__ unsigned long long bw[WAVES][16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n_out0 + r;
-        if (n < a.N) {
-          const float v = run[0][r] * s_a;
-          if (a.y) a.y[static_cast<size_t>(col) * a.N + n] = v;
-          key = umax64(key, argmax_key(v, static_cast<uint32_t>(n)));
-        }
-      }
+    for (int r = 0; r < 4; ++r) {
+      unsigned long long k = r < MR ? best[r < MR ? r : 0] : 0ull;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) k = umax64(k, shfl_xor_u64(k, o));
+      if (c == 0) bw[wave][4 * kq + r] = k;
     }
-    key = umax64(key, shfl_xor_u64(key, 16));
-    key = umax64(key, shfl_xor_u64(key, 32));
-    if (lane < 16) best[wave][lane] = key;
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    unsigned long long k = 0;
-    for (int w = 0; w < WAVES; ++w) k = umax64(k, best[w][threadIdx.x]);
-    a.partials[static_cast<size_t>(blockIdx.x) * 16 + threadIdx.x] = k;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = (prev == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  {
-    // Thread t reduces column t & 15 over blocks p, p + P, p + 2P, ...
-    // (p = t >> 4, P = WAVES * 4), then one thread per column folds the P
-    // strands. The maximum of u64 keys does not depend on the order.
-    constexpr int P = WAVES * 4;
-    const int m = threadIdx.x & 15, p = threadIdx.x >> 4;
-    unsigned long long k = 0;
-    for (unsigned b = p; b < gridDim.x; b += P)
-      k = umax64(k, a.partials[static_cast<size_t>(b) * 16 + m]);
-    red[p][m] = k;
     __syncthreads();
     if (threadIdx.x < 16) {
-      unsigned long long f = 0;
-      for (int q = 0; q < P; ++q) f = umax64(f, red[q][threadIdx.x]);
-      tgt[threadIdx.x] = static_cast<int32_t>(argmax_key_index(f));
-      if (!ACCEPT && threadIdx.x < a.M) a.argmax_out[threadIdx.x] = tgt[threadIdx.x];
+      unsigned long long k = 0;
+      for (int w = 0; w < WAVES; ++w) k = umax64(k, bw[w][threadIdx.x]);
+      a.partials[static_cast<size_t>(blockIdx.x) * 16 + threadIdx.x] = k;
     }
-    __syncthreads();
   }
-  if (ACCEPT && threadIdx.x < a.B) {
+}
+
+// Reduce the per-block argmax keys; ACCEPT also applies the accept rule.
+// One block of 1024 threads: 64 strands per row.
+template <bool ACCEPT>
+__global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
+  __shared__ unsigned long long red[64][16];
+  __shared__ int32_t tgt[16];
+  const int m = threadIdx.x & 15, p = threadIdx.x >> 4;
+  unsigned long long k = 0;
+#pragma unroll 8
+  for (int b = p; b < f.nparts; b += 64) k = umax64(k, f.partials[static_cast<size_t>(b) * 16 + m]);
+  red[p][m] = k;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    unsigned long long t = 0;
+    for (int q = 0; q < 64; ++q) t = umax64(t, red[q][threadIdx.x]);
+    tgt[threadIdx.x] = static_cast<int32_t>(argmax_key_index(t));
+    if (!ACCEPT && threadIdx.x < f.M) f.argmax_out[threadIdx.x] = tgt[threadIdx.x];
+  }
+  __syncthreads();
+  if (ACCEPT && threadIdx.x < f.B) {
     // One thread per sequence: slot i's draft d_i is checked against
     // t_{i-1}; the first mismatch ends the round.
-    const int b = threadIdx.x, k1 = a.k + 1;
+    const int b = threadIdx.x, k1 = f.k + 1;
     int acc = 0;
-    while (acc < a.k && a.draft[b * a.k + acc] == tgt[b * k1 + acc]) ++acc;
-    a.n_emitted[b] = acc + 1;
+    while (acc < f.k && f.draft[b * f.k + acc] == tgt[b * k1 + acc]) ++acc;
+    f.n_emitted[b] = acc + 1;
     for (int j = 0; j < k1; ++j) {
-      a.target[b * k1 + j] = tgt[b * k1 + j];
-      a.emitted[b * k1 + j] = j <= acc ? tgt[b * k1 + j] : -1;
+      f.target[b * k1 + j] = tgt[b * k1 + j];
+      f.emitted[b * k1 + j] = j <= acc ? tgt[b * k1 + j] : -1;
     }
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,51 +309,65 @@ int pick_split(int tiles, int G) {
   return s;
 }
 
-template <int PLANES, int CT, int WAVES, bool ARGMAX, bool ACCEPT, bool DBG>
-int launch_one(const GemvArgs& a, int blocks, hipStream_t st, const char* what) {
-  gemv_kernel<PLANES, CT, WAVES, ARGMAX, ACCEPT, DBG><<<dim3(blocks), dim3(WAVES * 64), 0, st>>>(a);
+template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT>
+int launch_one(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
+  auto kern = gemv_kernel<PLANES, MR, WAVES, ARGMAX, DBG, A4, LDSACT>;
+  const size_t lds = LDSACT ? static_cast<size_t>(a.M) * a.K : 0;
+  const int per_iter = WAVES / a.nseg;
+  const int iters = ((a.N + 15) / 16 + per_iter - 1) / per_iter;
+  int blocks = min(iters, nest::resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, lds));
+  blocks = min(blocks, max_blocks);
+  if (used) *used = blocks;
+  kern<<<dim3(blocks), dim3(WAVES * 64), lds, st>>>(a);
   return nest::check_launch(what);
 }
 
-template <int PLANES, int CT, bool DBG>
-int launch_split(GemvArgs a, hipStream_t st, const char* what) {
-  const int tiles = (a.N + 15) / 16;
-  const int S = CT == 1 ? a.nseg : min(a.nseg, 4);
-  a.nseg = S;
-  const int waves = S <= 4 ? 4 : S;
-  const int blocks = (tiles + waves / S - 1) / (waves / S);
-  if constexpr (CT == 1) {
-    switch (waves) {
-      case 4: return launch_one<PLANES, CT, 4, false, false, DBG>(a, blocks, st, what);
-      case 8: return launch_one<PLANES, CT, 8, false, false, DBG>(a, blocks, st, what);
-      default: return launch_one<PLANES, CT, 16, false, false, DBG>(a, blocks, st, what);
-    }
-  } else {
-    return launch_one<PLANES, CT, 4, false, false, DBG>(a, blocks, st, what);
+template <int PLANES, int MR, bool ARGMAX, bool DBG, bool A4, bool LDSACT>
+int launch_waves(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
+  if (ARGMAX || a.nseg <= 4)
+    return launch_one<PLANES, MR, 4, ARGMAX, DBG, A4, LDSACT>(a, st, what, max_blocks, used);
+  if constexpr (!ARGMAX) {
+    if (a.nseg == 8) return launch_one<PLANES, MR, 8, false, DBG, A4, LDSACT>(a, st, what, max_blocks, used);
+    return launch_one<PLANES, MR, 16, false, DBG, A4, LDSACT>(a, st, what, max_blocks, used);
   }
+  return NEST_EHIP;
 }
 
-template <int PLANES, bool DBG>
-int launch_ct(GemvArgs a, int CT, hipStream_t st, const char* what) {
-  switch (CT) {
-    case 1: return launch_split<PLANES, 1, DBG>(a, st, what);
-    case 2: return launch_split<PLANES, 2, DBG>(a, st, what);
-    case 3: return launch_split<PLANES, 3, DBG>(a, st, what);
-    case 4: return launch_split<PLANES, 4, DBG>(a, st, what);
-    case 5: return launch_split<PLANES, 5, DBG>(a, st, what);
-    case 6: return launch_split<PLANES, 6, DBG>(a, st, what);
-    case 7: return launch_split<PLANES, 7, DBG>(a, st, what);
-    case 8: return launch_split<PLANES, 8, DBG>(a, st, what);
-    default: return launch_split<PLANES, 9, DBG>(a, st, what);
+template <int PLANES, bool ARGMAX, bool DBG>
+int launch_gemv(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
+  const bool a4 = a.G % 4 == 0 && nest::aligned16(a.scales);
+  const bool ldsact = a4 && static_cast<long long>(a.M) * a.K <= kLdsActMax;
+  if (a.M == 1) {
+    if (ldsact) return launch_waves<PLANES, 1, ARGMAX, DBG, true, true>(a, st, what, max_blocks, used);
+    if (a4) return launch_waves<PLANES, 1, ARGMAX, DBG, true, false>(a, st, what, max_blocks, used);
+    return launch_waves<PLANES, 1, ARGMAX, DBG, false, false>(a, st, what, max_blocks, used);
   }
+  if (ldsact) return launch_waves<PLANES, 4, ARGMAX, DBG, true, true>(a, st, what, max_blocks, used);
+  if (a4) return launch_waves<PLANES, 4, ARGMAX, DBG, true, false>(a, st, what, max_blocks, used);
+  return launch_waves<PLANES, 4, ARGMAX, DBG, false, false>(a, st, what, max_blocks, used);
 }
-
-constexpr int kArgmaxWaves = 4;
-
-int argmax_blocks(int N) { return ((N + 15) / 16 + kArgmaxWaves - 1) / kArgmaxWaves; }
 
 size_t argmax_ws_bytes(int N) {
-  return kWsHeader + static_cast<size_t>(argmax_blocks(N)) * 16 * sizeof(unsigned long long);
+  const int iters = ((N + 15) / 16 + 3) / 4;
+  return static_cast<size_t>(min(iters, kMaxArgmaxBlocks)) * 16 * sizeof(unsigned long long);
+}
+
+// The exact-fold argmax GEMV and its finishing kernel.
+template <int PLANES, bool DBG>
+int launch_argmax(GemvArgs a, const FinishArgs& f0, bool accept, hipStream_t st, const char* what) {
+  a.nseg = 1;
+  int used = 0;
+  int rc = launch_gemv<PLANES, true, DBG>(a, st, what, kMaxArgmaxBlocks, &used);
+  if (rc) return rc;
+  FinishArgs f = f0;
+  f.partials = a.partials;
+  f.nparts = used;
+  f.M = a.M;
+  if (accept)
+    argmax_finish_kernel<true><<<1, 1024, 0, st>>>(f);
+  else
+    argmax_finish_kernel<false><<<1, 1024, 0, st>>>(f);
+  return nest::check_launch(what);
 }
 
 int check_common(const char* what, const int8_t* qa, const float* sa, int64_t M, int64_t K,
@@ -423,16 +415,15 @@ extern "C" int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t 
   if (argmax) {
     if (!ws || ws_bytes < argmax_ws_bytes(a.N))
       return nest::fail(NEST_EWORKSPACE, "draft_gemv: workspace needs %zu bytes", argmax_ws_bytes(a.N));
-    a.nseg = 1;
-    a.counter = static_cast<unsigned int*>(ws);
-    a.partials = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + kWsHeader);
-    a.argmax_out = argmax;
-    const int blocks = argmax_blocks(a.N);
-    return acc_dbg ? launch_one<1, 1, kArgmaxWaves, true, false, true>(a, blocks, st, what)
-                   : launch_one<1, 1, kArgmaxWaves, true, false, false>(a, blocks, st, what);
+    a.partials = static_cast<unsigned long long*>(ws);
+    FinishArgs f{};
+    f.argmax_out = argmax;
+    return acc_dbg ? launch_argmax<1, true>(a, f, false, st, what)
+                   : launch_argmax<1, false>(a, f, false, st, what);
   }
   a.nseg = pick_split((a.N + 15) / 16, a.G);
-  return acc_dbg ? launch_ct<1, true>(a, 1, st, what) : launch_ct<1, false>(a, 1, st, what);
+  return acc_dbg ? launch_gemv<1, false, true>(a, st, what, 1 << 30, nullptr)
+                 : launch_gemv<1, false, false>(a, st, what, 1 << 30, nullptr);
 }
 
 extern "C" int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
@@ -444,17 +435,20 @@ extern "C" int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t
   if (!refine || !y) return nest::fail(NEST_EINVAL, "verify_gemm: null pointer");
   if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "verify_gemm: refine not 16-byte aligned");
   hipStream_t st = nest::as_stream(stream);
-  // Row chunks of up to 144 (nine 16-row column tiles) per launch.
+  if (M <= 16) {
+    GemvArgs a{};
+    a.qa = qa; a.sa = sa; a.M = (int)M; a.K = (int)K; a.base = base; a.refine = refine;
+    a.scales = scales; a.N = (int)N; a.G = (int)(K / kGroup); a.y = y; a.acc_dbg = acc_dbg;
+    a.nseg = pick_split((a.N + 15) / 16, a.G);
+    return acc_dbg ? launch_gemv<2, false, true>(a, st, what, 1 << 30, nullptr)
+                   : launch_gemv<2, false, false>(a, st, what, 1 << 30, nullptr);
+  }
+  // More rows: the batched kernel, in chunks of up to 144 rows.
   for (int64_t m0 = 0; m0 < M; m0 += 144) {
     const int64_t mc = M - m0 < 144 ? M - m0 : 144;
-    GemvArgs a{};
-    a.qa = qa + m0 * K; a.sa = sa + m0; a.M = (int)mc; a.K = (int)K; a.base = base;
-    a.refine = refine; a.scales = scales; a.N = (int)N; a.G = (int)(K / kGroup);
-    a.y = y + m0 * N;
-    a.acc_dbg = acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr;
-    const int CT = (int)((mc + 15) / 16);
-    a.nseg = pick_split((a.N + 15) / 16, a.G);
-    rc = acc_dbg ? launch_ct<2, true>(a, CT, st, what) : launch_ct<2, false>(a, CT, st, what);
+    rc = nest::launch_verify_batched(qa + m0 * K, sa + m0, (int)mc, (int)K, base, refine, scales,
+                                     (int)N, y + m0 * N,
+                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, st);
     if (rc) return rc;
   }
   return NEST_OK;
@@ -479,10 +473,10 @@ extern "C" int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64
     return nest::fail(NEST_EWORKSPACE, "verify_accept: workspace needs %zu bytes", argmax_ws_bytes((int)V));
   GemvArgs a{};
   a.qa = qa; a.sa = sa; a.M = (int)(B * (k + 1)); a.K = (int)K; a.base = base; a.refine = refine;
-  a.scales = scales; a.N = (int)V; a.G = (int)(K / kGroup); a.nseg = 1; a.y = y;
-  a.counter = static_cast<unsigned int*>(ws);
-  a.partials = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + kWsHeader);
-  a.B = (int)B; a.k = (int)k; a.draft = draft; a.target = target; a.n_emitted = n_emitted;
-  a.emitted = emitted;
-  return launch_one<2, 1, kArgmaxWaves, true, true, false>(a, argmax_blocks(a.N), nest::as_stream(stream), what);
+  a.scales = scales; a.N = (int)V; a.G = (int)(K / kGroup); a.y = y;
+  a.partials = static_cast<unsigned long long*>(ws);
+  FinishArgs f{};
+  f.B = (int)B; f.k = (int)k; f.draft = draft; f.target = target; f.n_emitted = n_emitted;
+  f.emitted = emitted;
+  return launch_argmax<2, false>(a, f, true, nest::as_stream(stream), what);
 }

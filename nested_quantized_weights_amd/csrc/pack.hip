@@ -73,30 +73,65 @@ __global__ void __launch_bounds__(256) pack_groups_kernel(const float* __restric
   }
 }
 
-// One block of 256 threads per activation row.
-__global__ void __launch_bounds__(256) act_quant_kernel(const float* __restrict__ x, int64_t K,
-                                                        int8_t* __restrict__ qa,
-                                                        float* __restrict__ sa) {
-  __shared__ float red[4];
-  const int64_t row = blockIdx.x;
-  const float* xr = x + row * K;
-  float m = 0.0f;
-  for (int64_t k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf(xr[k]));
+__device__ __forceinline__ int8_t quant_act(float x, float s) {
+  if (s == 0.0f) return 0;
+  float t = rintf(x / s);
+  t = t < -127.0f ? -127.0f : (t > 127.0f ? 127.0f : t);
+  return static_cast<int8_t>(static_cast<int>(t));
+}
+
+// Block-wide maximum for blocks of 1024 threads (16 waves).
+__device__ __forceinline__ float block_max_1024(float m, float* red) {
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = m / 127.0f;
-  if (threadIdx.x == 0) sa[row] = s;
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// One block of 1024 threads per activation row. When K % 4 == 0 and the
+// row fits in PER float4 per thread, the row is read once into registers.
+template <int PER>
+__global__ void __launch_bounds__(1024) act_quant_kernel(const float* __restrict__ x, int64_t K,
+                                                         int8_t* __restrict__ qa,
+                                                         float* __restrict__ sa) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * K;
   int8_t* q = qa + row * K;
-  for (int64_t k = threadIdx.x; k < K; k += 256) {
-    int v = 0;
-    if (s != 0.0f) {
-      float t = rintf(xr[k] / s);
-      t = t < -127.0f ? -127.0f : (t > 127.0f ? 127.0f : t);
-      v = static_cast<int>(t);
+  if (PER > 0) {
+    float4 v[PER > 0 ? PER : 1];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t e = (static_cast<int64_t>(i) * 1024 + threadIdx.x) * 4;
+      v[i] = e < K ? *reinterpret_cast<const float4*>(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     }
-    q[k] = static_cast<int8_t>(v);
+    m = block_max_1024(m, red);
+    const float s = m / 127.0f;
+    if (threadIdx.x == 0) sa[row] = s;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t e = (static_cast<int64_t>(i) * 1024 + threadIdx.x) * 4;
+      if (e < K) {
+        char4 c;
+        c.x = quant_act(v[i].x, s);
+        c.y = quant_act(v[i].y, s);
+        c.z = quant_act(v[i].z, s);
+        c.w = quant_act(v[i].w, s);
+        *reinterpret_cast<char4*>(q + e) = c;
+      }
+    }
+  } else {
+    float m = 0.0f;
+    for (int64_t k = threadIdx.x; k < K; k += 1024) m = fmaxf(m, fabsf(xr[k]));
+    m = block_max_1024(m, red);
+    const float s = m / 127.0f;
+    if (threadIdx.x == 0) sa[row] = s;
+    for (int64_t k = threadIdx.x; k < K; k += 1024) q[k] = quant_act(xr[k], s);
   }
 }
 
@@ -152,6 +187,20 @@ extern "C" int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, 
   if (!x || !qa || !sa) return nest::fail(NEST_EINVAL, "nest_act_quant: null pointer");
   if (M < 1 || K < 1 || M > 0x7fffffffLL)
     return nest::fail(NEST_EINVAL, "nest_act_quant: M=%lld K=%lld", (long long)M, (long long)K);
-  act_quant_kernel<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, nest::as_stream(stream)>>>(x, K, qa, sa);
+  const dim3 grid(static_cast<unsigned>(M)), block(1024);
+  hipStream_t st = nest::as_stream(stream);
+  const bool vec = K % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(qa) & 3) == 0;
+  const int64_t per = (K / 4 + 1023) / 1024;
+  if (vec && per <= 1)
+    act_quant_kernel<1><<<grid, block, 0, st>>>(x, K, qa, sa);
+  else if (vec && per <= 2)
+    act_quant_kernel<2><<<grid, block, 0, st>>>(x, K, qa, sa);
+  else if (vec && per <= 5)
+    act_quant_kernel<5><<<grid, block, 0, st>>>(x, K, qa, sa);
+  else if (vec && per <= 8)
+    act_quant_kernel<8><<<grid, block, 0, st>>>(x, K, qa, sa);
+  else
+    act_quant_kernel<0><<<grid, block, 0, st>>>(x, K, qa, sa);
   return nest::check_launch("nest_act_quant");
 }

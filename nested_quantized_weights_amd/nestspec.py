@@ -104,17 +104,17 @@ def _dev(t: torch.Tensor, dtype, what: str, name: str) -> torch.Tensor:
     return t
 
 
-# Zero-filled workspaces for the argmax / accept entry points, cached per
-# (device, stream, kind). The kernels leave them zero-filled after each call.
+# Workspaces for the argmax / accept entry points, cached per (device,
+# stream, kind): calls on one stream run in order, so they can share one.
 _ws_cache: dict = {}
 
 
-def zeroed_workspace(nbytes: int, device: torch.device, key: str) -> torch.Tensor:
+def workspace(nbytes: int, device: torch.device, key: str) -> torch.Tensor:
     s = torch.cuda.current_stream(device).cuda_stream
     k = (device.index, s, key)
     t = _ws_cache.get(k)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[k] = t
     return t
 
@@ -167,7 +167,7 @@ def draft_gemv(qa, sa, base, scales, group: int = 128, y=None, want_y: bool = Tr
         am = argmax_out if argmax_out is not None else torch.empty(M, dtype=torch.int32, device=dev)
         wsn = lib().draft_gemv_workspace_size(M, N)
         if ws is None:
-            ws = zeroed_workspace(wsn, dev, "argmax")
+            ws = workspace(wsn, dev, "argmax")
         wsp = _ptr(ws)
         wsn = ws.numel()
     acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
@@ -223,7 +223,7 @@ def verify_accept(qa, sa, B: int, k: int, base, refine, scales, draft, group: in
             out["y"] = torch.empty((B * (k + 1), V), dtype=torch.float32, device=dev)
     wsn = lib().verify_accept_workspace_size(B, k, V)
     if ws is None:
-        ws = zeroed_workspace(wsn, dev, "argmax")
+        ws = workspace(wsn, dev, "argmax")
     _check(lib().verify_accept(_ptr(qa), _ptr(sa), B, k, K, _ptr(base), _ptr(refine), _ptr(scales),
                                V, group, _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
                                _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(ws), ws.numel(),

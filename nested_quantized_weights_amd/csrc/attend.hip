@@ -4,23 +4,27 @@
 // past ctx_len are never read, and the caller's length update discards a
 // rejected suffix.
 //
-// gfx950 design (flash-decoding). Work unit = (kv head, 128-token block).
-// A block of 4 waves takes 4*bpw consecutive blocks of one head, and each
-// wave keeps an online softmax over its blocks. The waves merge in LDS in a
-// fixed order. A second kernel merges the blocks' partial (max, sum, O)
-// with log-sum-exp weights, also in a fixed order. Both products use
-// v_mfma_f32_16x16x32_f16:
-//   S^T = K Q^T : A = 16 tokens x 32 dims of K codes, B = Q^T (16 query rows)
-//   O^T += V^T P^T : A = 16 dims x 32 tokens of V codes, B = P^T
-// Cache codes become exact f16 integers without converts. v_perm_b32 puts
-// a nibble-or-byte u under the exponent byte 0x64 (the f16 1024 + u). One
-// v_pk_add_f16 then removes the offset exactly (1032 for a 4-bit base code,
-// 1160 for the 8-bit code 16*q_b + q_r biased by 136). Inside a block, token
-// tile 2j+e row 4q+i holds token 32q + 8j + 4e + i. Then the S^T tile that
-// a lane holds is exactly the P^T operand it needs, and each lane's V codes
-// for a dim tile are 16 contiguous bytes of the dim-major V block.
-// Query values enter as f16 (bf16 -> f16 is exact in the normal range).
-// Softmax runs in the log2 domain with exp2f.
+// gfx950 design (flash-decoding). A workgroup of 4 waves walks a chunk of
+// 128-token blocks of one kv head. Per block:
+//   phase A  all 256 threads read the block's codes once (K token-major, V
+//            dim-major) and convert them to f16 MFMA operands in LDS
+//            (32 KB K + 32 KB V). A nibble (or the 8-bit code biased by
+//            136) is put under the f16 exponent byte 0x64 by v_perm_b32,
+//            giving 1024 + u. One v_pk_add_f16 then removes the offset
+//            exactly, so every code becomes an exact f16 integer.
+//   phase B  waves split the query rows into 16-row tiles and, when rows
+//            are few, the block's four 32-token k-steps. Each keeps an
+//            online softmax (log2 domain, exp2f) and multiplies with
+//            v_mfma_f32_16x16x32_f16:
+//              S^T = K Q^T    (A = 16 tokens x 32 dims from LDS, B = Q^T)
+//              O^T += V^T P^T (A = 16 dims x 32 tokens from LDS, B = P^T)
+// Inside a block, token tile 2j+e row 4q+i holds token 32q + 8j + 4e + i.
+// Then the S^T values a lane holds are exactly the P^T operand it needs.
+// Waves that share a row tile merge in LDS in a fixed order, and each
+// workgroup writes one partial (max, sum, O) per row. A second kernel
+// merges the partials over chunks with log-sum-exp weights, also in a
+// fixed order. P enters the PV product as f16 scaled by the block's V
+// scale. Queries enter as f16 (bf16 -> f16 is exact in the normal range).
 #include "common.h"
 
 namespace {
@@ -30,6 +34,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;
 constexpr int kBlk = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTargetBlocks = 512;  // workgroups to aim for (two resident per CU)
 
 struct AttArgs {
   const uint16_t* q;
@@ -38,7 +43,7 @@ struct AttArgs {
   const uint8_t *kb, *kr, *vb, *vr;
   const float *ks, *vs;
   int cap, nb;         // capacity and blocks per head in the planes
-  int bpw, nchunk;     // blocks per wave, chunks (workgroups) per head
+  int bpw, nchunk;     // blocks per workgroup, chunks (workgroups) per head
   float* part_ml;      // [Hkv][nchunk][R][2]  (max in log2 domain, sum)
   float* part_o;       // [Hkv][nchunk][R][128]
   float* out;          // [nq][Hq][128]
@@ -51,8 +56,8 @@ __device__ __forceinline__ uint32_t sub_h2(uint32_t v, uint32_t off) {
   return __builtin_bit_cast(uint32_t, a - b);
 }
 
-// Four bytes u (each < 256) -> two VGPRs of f16 pairs 1024+u in the order
-// (byte0, byte1) and (byte2, byte3).
+// Four bytes u (each < 256) -> two VGPRs of f16 pairs (1024+u) - off, in the
+// order (byte0, byte1) and (byte2, byte3).
 __device__ __forceinline__ void bytes_to_h(uint32_t bytes, uint32_t off, uint32_t& p01, uint32_t& p23) {
   const uint32_t c64 = 0x64646464u;
   p01 = sub_h2(__builtin_amdgcn_perm(c64, bytes, 0x04010400u), off);
@@ -62,7 +67,7 @@ __device__ __forceinline__ void bytes_to_h(uint32_t bytes, uint32_t off, uint32_
 // One 32-bit word of codes (8 elements e0..e7, e_{2b} in the low nibble of
 // byte b) -> 8 f16 code values in the order [e0 e2 e4 e6 e1 e3 e5 e7].
 template <int VIEW>
-__device__ __forceinline__ v8h codes_to_h8(uint32_t wb, uint32_t wr) {
+__device__ __forceinline__ uint4 codes_to_h8(uint32_t wb, uint32_t wr) {
   uint32_t ev, od, off;
   const uint32_t xb = wb ^ 0x88888888u;
   if (VIEW == 0) {
@@ -75,37 +80,53 @@ __device__ __forceinline__ v8h codes_to_h8(uint32_t wb, uint32_t wr) {
     od = bfi(0xF0F0F0F0u, xb, xr >> 4);
     off = 0x64886488u;                   // f16 1160 = 1024 + 136, twice
   }
-  uint32_t r[4];
-  bytes_to_h(ev, off, r[0], r[1]);
-  bytes_to_h(od, off, r[2], r[3]);
-  v4i t = {(int)r[0], (int)r[1], (int)r[2], (int)r[3]};
-  return __builtin_bit_cast(v8h, t);
+  uint4 r;
+  bytes_to_h(ev, off, r.x, r.y);
+  bytes_to_h(od, off, r.z, r.w);
+  return r;
 }
 
-__device__ __forceinline__ v4f mfma_h(v8h a, v8h b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ v4f mfma_h(uint4 a, v8h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ _Float16 bf16_to_h(uint16_t b) {
   return static_cast<_Float16>(__uint_as_float(static_cast<uint32_t>(b) << 16));
 }
 
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint32_t word(uint4 v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// LDS operand tables (uint4 = 8 f16):
+//   K: slot ((tt*4 + s)*4 + q)*16 + r: token tau(tt, r), dims 32q + 8s + [0 2 4 6 1 3 5 7]
+//   V: slot ((dt*4 + j)*4 + q)*16 + r: dim dt*16 + r, tokens 32q + 8j + [0 2 4 6 1 3 5 7]
+// with tau(tt, r) = 32*(r>>2) + 8*(tt>>1) + 4*(tt&1) + (r&3).
+__device__ __forceinline__ int op_slot(int a, int b, int q, int r) { return ((a * 4 + b) * 4 + q) * 16 + r; }
+
 template <int RT, int VIEW>
 __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
+  __shared__ uint4 kf[2048];
+  __shared__ uint4 vf[2048];
+  // waves per row tile (TS) and 32-token k-steps per wave (JS)
+  constexpr int TS = RT == 1 ? 4 : (RT == 2 ? 2 : 1);
+  constexpr int JS = 4 / TS;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int h = blockIdx.y, chunk = blockIdx.x;
+  const int rt = wave / TS, tp = wave % TS, j0 = tp * JS;
+  const bool active = rt < RT;
 
-  // Query operands: row rt*16 + c16, k-step s holds dims 32*q4 + 8*s + [0 2 4 6 1 3 5 7].
-  v8h qop[RT][4];
-  int pos[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  // Query operand of row rt*16 + c16, k-step s: dims 32*q4 + 8*s + [0 2 4 6 1 3 5 7].
+  v8h qop[4];
+  int pos = -1;
+  {
     const int rho = rt * 16 + c16;
-    pos[rt] = -1;
-    if (rho < a.R) {
+    if (active && rho < a.R) {
       const int i = rho / a.grp, g = rho % a.grp;
-      pos[rt] = a.ctx - a.nq + i;
+      pos = a.ctx - a.nq + i;
       const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -113,185 +134,196 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
         v8h v;
         v[0] = bf16_to_h(p[0]); v[1] = bf16_to_h(p[2]); v[2] = bf16_to_h(p[4]); v[3] = bf16_to_h(p[6]);
         v[4] = bf16_to_h(p[1]); v[5] = bf16_to_h(p[3]); v[6] = bf16_to_h(p[5]); v[7] = bf16_to_h(p[7]);
-        qop[rt][s] = v;
+        qop[s] = v;
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qop[rt][s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int s = 0; s < 4; ++s) qop[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
 
-  float m[RT], l[RT];
-  v4f O[RT][8];
+  float m = -INFINITY, l = 0.0f;
+  v4f O[8];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
-    l[rt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) O[rt][dt] = v4f{0, 0, 0, 0};
-  }
+  for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
 
   const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
-  const int first = chunk * 4 * a.bpw;
-  for (int t = 0; t < a.bpw; ++t) {
-    const int blk = first + wave + 4 * t;
-    if (blk >= a.nbv) break;  // uniform per wave
+  const int b_first = chunk * a.bpw;
+  const int b_last = min(b_first + a.bpw, a.nbv);
+
+  // Phase A items of this thread: it = threadIdx.x + 256*rep is (t, q, r) with
+  // t = it >> 6 (K token tile / V dim tile), q = (it >> 4) & 3, r = it & 15.
+  // The next block's codes are loaded into registers while the current block
+  // is multiplied (software pipelining across blocks).
+  uint4 ck_b[2], ck_r[2], cv_b[2], cv_r[2];
+  auto load_codes = [&](int blk) {
+    const int t0 = blk * kBlk;
+    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int it = threadIdx.x + rep * 256;
+      const int t = it >> 6, q = (it >> 4) & 3, r = it & 15;
+      const int tok = 32 * (r >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (r & 3);
+      const size_t koff = (static_cast<size_t>(h) * a.cap + t0 + tok) * (kD / 2) + 16 * q;
+      const size_t voff = (hb * kD + t * 16 + r) * (kBlk / 2) + 16 * q;
+      ck_b[rep] = ld16(a.kb + koff);
+      cv_b[rep] = ld16(a.vb + voff);
+      if (VIEW) {
+        ck_r[rep] = ld16(a.kr + koff);
+        cv_r[rep] = ld16(a.vr + voff);
+      } else {
+        ck_r[rep] = cv_r[rep] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  if (b_first < b_last) load_codes(b_first);
+
+  for (int blk = b_first; blk < b_last; ++blk) {
     const int t0 = blk * kBlk;
     const size_t hb = static_cast<size_t>(h) * a.nb + blk;
 
-    // K: token tile tt = 2j+e, row c16 = 4*qq+i -> token 32*qq + 8*j + 4*e + i.
-    uint4 kw[8], kwr[8], vw[8], vwr[8];
+    // ---- phase A: codes -> f16 operands in LDS, then prefetch the next block ----
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
-      const size_t off = (static_cast<size_t>(h) * a.cap + t0 + tok) * (kD / 2) + 16 * q4;
-      kw[tt] = *reinterpret_cast<const uint4*>(a.kb + off);
-      if (VIEW) kwr[tt] = *reinterpret_cast<const uint4*>(a.kr + off);
-    }
-    // V: dim tile dt, dim row dt*16 + c16, tokens 32*q4 .. 32*q4+31.
+    for (int rep = 0; rep < 2; ++rep) {
+      const int it = threadIdx.x + rep * 256;
+      const int t = it >> 6, q = (it >> 4) & 3, r = it & 15;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const size_t off = (hb * kD + dt * 16 + c16) * (kBlk / 2) + 16 * q4;
-      vw[dt] = *reinterpret_cast<const uint4*>(a.vb + off);
-      if (VIEW) vwr[dt] = *reinterpret_cast<const uint4*>(a.vr + off);
+      for (int s = 0; s < 4; ++s)
+        kf[op_slot(t, s, q, r)] = codes_to_h8<VIEW>(word(ck_b[rep], s), word(ck_r[rep], s));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vf[op_slot(t, j, q, r)] = codes_to_h8<VIEW>(word(cv_b[rep], j), word(cv_r[rep], j));
     }
-    const float ck = a.ks[hb] * sm_scale;
-    const float sv = VIEW ? a.vs[hb] * 0.0625f : a.vs[hb];
+    if (blk + 1 < b_last) load_codes(blk + 1);
+    __syncthreads();
 
-    // S^T tiles
-    v4f S[RT][8];
+    // ---- phase B: this wave's row tile over its k-steps ----
+    if (active) {
+      const float ck = a.ks[hb] * sm_scale;
+      const float sv = VIEW ? a.vs[hb] * 0.0625f : a.vs[hb];
+      v4f S[2 * JS];
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t w0[4] = {kw[tt].x, kw[tt].y, kw[tt].z, kw[tt].w};
-      uint32_t w1[4] = {0, 0, 0, 0};
-      if (VIEW) { w1[0] = kwr[tt].x; w1[1] = kwr[tt].y; w1[2] = kwr[tt].z; w1[3] = kwr[tt].w; }
+      for (int jj = 0; jj < JS; ++jj)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) S[rt][tt] = v4f{0, 0, 0, 0};
+        for (int e = 0; e < 2; ++e) {
+          const int tt = 2 * (j0 + jj) + e;
+          v4f acc = v4f{0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8h av = codes_to_h8<VIEW>(w0[s], w1[s]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) S[rt][tt] = mfma_h(av, qop[rt][s], S[rt][tt]);
-      }
-    }
-
-    // online softmax (log2 domain) for the row this lane carries
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+          for (int s = 0; s < 4; ++s) acc = mfma_h(kf[op_slot(tt, s, q4, c16)], qop[s], acc);
+          S[2 * jj + e] = acc;
+        }
       float mb = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+      for (int jj = 0; jj < JS; ++jj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = t0 + 32 * q4 + 8 * (tt >> 1) + 4 * (tt & 1) + i;
-          const float v = tok <= pos[rt] ? S[rt][tt][i] * ck : -INFINITY;
-          S[rt][tt][i] = v;
-          mb = fmaxf(mb, v);
-        }
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + 32 * q4 + 8 * (j0 + jj) + 4 * e + i;
+            const float v = tok <= pos ? S[2 * jj + e][i] * ck : -INFINITY;
+            S[2 * jj + e][i] = v;
+            mb = fmaxf(mb, v);
+          }
       mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
       mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float mn = fmaxf(m[rt], mb);
+      const float mn = fmaxf(m, mb);
       const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float alpha = exp2f(m[rt] - mu);
+      const float alpha = exp2f(m - mu);
       float ls = 0.0f;
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+      for (int k = 0; k < 2 * JS; ++k)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(S[rt][tt][i] - mu);
-          S[rt][tt][i] = p;
+          const float p = exp2f(S[k][i] - mu);
+          S[k][i] = p;
           ls += p;
         }
       ls += __shfl_xor(ls, 16, 64);
       ls += __shfl_xor(ls, 32, 64);
-      l[rt] = l[rt] * alpha + ls;
-      m[rt] = mn;
+      l = l * alpha + ls;
+      m = mn;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[rt][dt] *= alpha;
-    }
-
-    // O^T += V^T P^T ; P pre-scaled by the block's V scale
+      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v8h pb[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const v4f e0 = S[rt][2 * j], e1 = S[rt][2 * j + 1];
+      for (int jj = 0; jj < JS; ++jj) {
+        const v4f e0 = S[2 * jj], e1 = S[2 * jj + 1];
         v8h p;
         p[0] = (_Float16)(e0[0] * sv); p[1] = (_Float16)(e0[2] * sv);
         p[2] = (_Float16)(e1[0] * sv); p[3] = (_Float16)(e1[2] * sv);
         p[4] = (_Float16)(e0[1] * sv); p[5] = (_Float16)(e0[3] * sv);
         p[6] = (_Float16)(e1[1] * sv); p[7] = (_Float16)(e1[3] * sv);
-        pb[rt] = p;
-      }
+        const int j = j0 + jj;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint32_t wb = j == 0 ? vw[dt].x : j == 1 ? vw[dt].y : j == 2 ? vw[dt].z : vw[dt].w;
-        uint32_t wr = 0;
-        if (VIEW) wr = j == 0 ? vwr[dt].x : j == 1 ? vwr[dt].y : j == 2 ? vwr[dt].z : vwr[dt].w;
-        const v8h av = codes_to_h8<VIEW>(wb, wr);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) O[rt][dt] = mfma_h(av, pb[rt], O[rt][dt]);
+        for (int dt = 0; dt < 8; ++dt) O[dt] = mfma_h(vf[op_slot(dt, j, q4, c16)], p, O[dt]);
       }
     }
+    __syncthreads();  // the next block's phase A overwrites the tables
   }
 
-  // ---- merge the 4 waves in LDS, in the fixed order 3, 2, 1, 0 ----
-  __shared__ float ml[4][RT * 16][2];
-  __shared__ float buf[RT * 16][kD + 4];
-  if (q4 == 0) {
+  // ---- write this workgroup's partial per row ----
+  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;
+  if (TS == 1) {
+    const int rho = rt * 16 + c16;
+    if (active && rho < a.R) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      ml[wave][rt * 16 + c16][0] = m[rt];
-      ml[wave][rt * 16 + c16][1] = l[rt];
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(&a.part_o[(pbase + rho) * kD + dt * 16 + 4 * q4]) =
+            make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
+      if (q4 == 0) {
+        a.part_ml[(pbase + rho) * 2 + 0] = m;
+        a.part_ml[(pbase + rho) * 2 + 1] = l;
+      }
     }
+    return;
+  }
+  // TS waves share a row tile: merge them in LDS, in the fixed order tp = TS-1 .. 0
+  float* ml = reinterpret_cast<float*>(kf);      // [4 waves][16 rows][2]
+  float* buf = reinterpret_cast<float*>(vf);     // [RT][16 rows][132]
+  if (q4 == 0) {
+    ml[(wave * 16 + c16) * 2 + 0] = m;
+    ml[(wave * 16 + c16) * 2 + 1] = l;
   }
   __syncthreads();
-  float f[RT];
+  float M = -INFINITY;
+  for (int t = 0; t < TS; ++t) M = fmaxf(M, ml[((rt * TS + t) * 16 + c16) * 2]);
+  const float Mu = M == -INFINITY ? 0.0f : M;
+  const float f = exp2f(m - Mu);
+  for (int step = TS - 1; step >= 0; --step) {
+    if (active && tp == step) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = rt * 16 + c16;
-    float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w][row][0]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-    f[rt] = exp2f(m[rt] - Mu);
-  }
-  for (int w = 3; w >= 0; --w) {
-    if (wave == w) {
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* p = &buf[rt * 16 + c16][dt * 16 + 4 * q4 + i];
-            const float v = O[rt][dt][i] * f[rt];
-            *p = (w == 3) ? v : *p + v;
-          }
+        for (int i = 0; i < 4; ++i) {
+          float* p = &buf[(rt * 16 + c16) * (kD + 4) + dt * 16 + 4 * q4 + i];
+          const float v = O[dt][i] * f;
+          *p = (step == TS - 1) ? v : *p + v;
+        }
     }
     __syncthreads();
   }
-  // write this workgroup's partial: rows < R
-  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;
   for (int idx = threadIdx.x; idx < a.R * kD; idx += 256) {
     const int row = idx / kD, dim = idx % kD;
-    a.part_o[(pbase + row) * kD + dim] = buf[row][dim];
+    if (row < RT * 16) a.part_o[(pbase + row) * kD + dim] = buf[row * (kD + 4) + dim];
   }
-  if (threadIdx.x < a.R) {
-    const int row = threadIdx.x;
-    float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w][row][0]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
+  if (threadIdx.x < a.R && static_cast<int>(threadIdx.x) < RT * 16) {
+    const int row = threadIdx.x, r16 = row & 15, t_rt = row >> 4;
+    float Mr = -INFINITY;
+    for (int t = 0; t < TS; ++t) Mr = fmaxf(Mr, ml[((t_rt * TS + t) * 16 + r16) * 2]);
+    const float Mru = Mr == -INFINITY ? 0.0f : Mr;
     float L = 0.0f;
-    for (int w = 0; w < 4; ++w) L += ml[w][row][1] * exp2f(ml[w][row][0] - Mu);
-    a.part_ml[(pbase + row) * 2 + 0] = M;
+    for (int t = 0; t < TS; ++t) {
+      const int w = t_rt * TS + t;
+      L += ml[(w * 16 + r16) * 2 + 1] * exp2f(ml[(w * 16 + r16) * 2] - Mru);
+    }
+    a.part_ml[(pbase + row) * 2 + 0] = Mr;
     a.part_ml[(pbase + row) * 2 + 1] = L;
   }
 }
 
 // One block of 256 threads per (row, kv head). The chunk weights
 // 2^(m_c - M) go to LDS. Then each half-block sums the chunks of one parity
-// for all 128 dims, and the two halves are added (a fixed order).
+// for all 128 dims, unrolled so that the loads overlap, and the two halves
+// are added (a fixed order).
 constexpr int kCombineChunks = 1024;  // chunks handled per LDS pass
 
 __global__ void __launch_bounds__(256) combine_kernel(AttArgs a) {
@@ -310,6 +342,8 @@ __global__ void __launch_bounds__(256) combine_kernel(AttArgs a) {
   __syncthreads();
   float L = 0.0f, acc = 0.0f;
   const int dim = t & (kD - 1), par = t >> 7;
+  const float* po = a.part_o + base * kD + dim;
+  const size_t cstride = static_cast<size_t>(a.R) * kD;
   for (int c0 = 0; c0 < a.nchunk; c0 += kCombineChunks) {
     const int cn = min(kCombineChunks, a.nchunk - c0);
     for (int c = t; c < cn; c += 256) {
@@ -320,10 +354,16 @@ __global__ void __launch_bounds__(256) combine_kernel(AttArgs a) {
       L += w * a.part_ml[pr * 2 + 1];
     }
     __syncthreads();
-    for (int c = par; c < cn; c += 2) {
-      const float w = wts[c];
-      if (w != 0.0f) acc += a.part_o[(base + static_cast<size_t>(c0 + c) * a.R) * kD + dim] * w;
+    // chunks with no visible token have O = 0 and weight 0
+    int c = par;
+    for (; c + 14 < cn; c += 16) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = po[static_cast<size_t>(c0 + c + 2 * u) * cstride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(v[u], wts[c + 2 * u], acc);
     }
+    for (; c < cn; c += 2) acc = fmaf(po[static_cast<size_t>(c0 + c) * cstride], wts[c], acc);
     __syncthreads();
   }
   // total denominator: block sum of L
@@ -347,12 +387,13 @@ Plan make_plan(int64_t nq, int64_t Hq, int64_t Hkv, int64_t ctx) {
   Plan p{};
   const int64_t R = nq * (Hq / Hkv);
   p.nbv = static_cast<int>((ctx + kBlk - 1) / kBlk);
-  p.bpw = 1;
-  // keep at least ~2 workgroups per CU, then grow the per-wave work
-  while (Hkv * ((p.nbv + 8 * p.bpw - 1) / (8 * p.bpw)) >= 512) p.bpw *= 2;
-  p.nchunk = (p.nbv + 4 * p.bpw - 1) / (4 * p.bpw);
+  const int64_t blocks = Hkv * p.nbv;
+  p.bpw = static_cast<int>((blocks + kTargetBlocks - 1) / kTargetBlocks);
+  if (p.bpw < 1) p.bpw = 1;
+  p.nchunk = (p.nbv + p.bpw - 1) / p.bpw;
   p.RT = static_cast<int>((R + 15) / 16);
-  p.ws = static_cast<size_t>(Hkv) * p.nchunk * R * (kD + 2) * sizeof(float);
+  const size_t rows = static_cast<size_t>(Hkv) * p.nchunk * R;
+  p.ws = (((rows * 2 + 3) & ~static_cast<size_t>(3)) + rows * kD) * sizeof(float);
   return p;
 }
 
@@ -408,6 +449,7 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
     return nest::fail(NEST_EALIGN, "%s: planes must be 16-byte aligned", what);
   const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_len);
   if (!ws || ws_bytes < p.ws) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, p.ws);
+  if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
   AttArgs a{};
   a.q = q; a.nq = (int)nq; a.Hq = (int)n_q_heads; a.grp = (int)(n_q_heads / Hkv); a.R = (int)R;
   a.ctx = (int)ctx_len; a.nbv = p.nbv;
@@ -416,7 +458,9 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
   a.cap = (int)kv->capacity; a.nb = (int)(kv->capacity / kBlk);
   a.bpw = p.bpw; a.nchunk = p.nchunk;
   a.part_ml = static_cast<float*>(ws);
-  a.part_o = a.part_ml + static_cast<size_t>(Hkv) * p.nchunk * R * 2;
+  // part_o starts 16-byte aligned after the (max, sum) pairs
+  const size_t ml_floats = (static_cast<size_t>(Hkv) * p.nchunk * R * 2 + 3) & ~static_cast<size_t>(3);
+  a.part_o = a.part_ml + ml_floats;
   a.out = out;
   hipStream_t st = nest::as_stream(stream);
   return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);

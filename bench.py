@@ -300,11 +300,12 @@ def cpu_baseline(inp, k):
 
 # ---------------------------------------------------------------------------
 
-def traffic_from_profile():
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, or None if missing or taken on a different kernel source."""
+def profile_summary():
+    """Figures of the dominant kernel from the committed rocprofv3 summary:
+    (HBM bytes per launch, kernel-trace averages in us), or (None, None) if
+    the summary is missing or was taken on a different kernel source."""
     if not os.path.exists(PROFILE_SUMMARY):
-        return None
+        return None, None
     src_hash = hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()[:16]
     vals = {}
     for ln in open(PROFILE_SUMMARY):
@@ -312,11 +313,13 @@ def traffic_from_profile():
             key, _, v = ln.partition(":")
             vals[key.strip()] = v.strip()
     if vals.get("gemv_source_sha256_16") != src_hash:
-        return None
+        return None, None
     try:
-        return int(float(vals["hbm_bytes_per_launch"]))
+        trace = {"gemv_kernel": round(float(vals["kernel_trace_avg_ns"]) / 1e3, 2),
+                 "argmax_finish_kernel": round(float(vals["finish_kernel_trace_avg_ns"]) / 1e3, 2)}
+        return int(float(vals["hbm_bytes_per_launch"])), trace
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 def main():
@@ -370,7 +373,7 @@ def main():
     dom_ms = float(np.mean(res[4]["dom"]))
     dom_bytes = gemv_bytes(QWEN["vocab"], QWEN["hidden"], 1, 1, y=False, argmax=True)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile()
+    traffic, trace_us = profile_summary()
     line = {
         "metric": "draft/verify weight-stream HBM GB/s (% of peak) + spec rounds/s at k=4,8",
         "value": round(value, 2),
@@ -400,7 +403,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
-                     "avg_launch_us": round(dom_ms * 1e3, 3), "launches": len(res[4]["dom"])},
+                     "avg_launch_us": round(dom_ms * 1e3, 3), "launches": len(res[4]["dom"]),
+                     "timed": "HIP events around each draft_gemv(argmax) call in the timed "
+                              "region: the GEMV kernel plus its finishing kernel",
+                     "kernel_trace_avg_us": trace_us},
     }
     if not args.no_cpu_baseline:
         print("# bench: timing the oracle on one k=4 round", file=sys.stderr, flush=True)

@@ -1,0 +1,74 @@
+"""The C-ABI library loads and exports every function include/nestspec.h declares (CPU only).
+
+No compute call is made. Only host-side argument checks run: they return an
+error status before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nestspec.h")
+LIB = os.path.join(ROOT, "nested_quantized_weights_amd", "libnestspec.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libnestspec.so not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("nest_pack", "nest_act_quant", "draft_gemv", "verify_gemm", "verify_accept",
+                     "kv_nest_pack", "kv_nest_attend", "nest_last_error",
+                     "draft_gemv_workspace_size", "verify_accept_workspace_size",
+                     "kv_nest_attend_workspace_size"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_symbol():
+    from nested_quantized_weights_amd import nestspec
+
+    assert sorted(nestspec.SYMBOLS) == declared_functions()
+
+
+def test_host_validation_reports_errors_without_a_gpu(lib):
+    lib.nest_last_error.restype = ctypes.c_char_p
+    f = lib.nest_pack
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 4, 8, 4, None, None, None, None) == 1  # NEST_EINVAL: null pointer
+    assert b"null" in lib.nest_last_error()
+    dummy = ctypes.c_void_p(16)
+    assert f(dummy, 4, 10, 4, dummy, dummy, dummy, None) == 3  # NEST_ESHAPE: 4 does not divide 10
+    g = lib.draft_gemv
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 2 + \
+        [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert g(dummy, dummy, 1, 256, dummy, dummy, 16, 64, dummy, None, None, None, 0, None) == 5
+    assert g(dummy, dummy, 1, 200, dummy, dummy, 16, 128, dummy, None, None, None, 0, None) == 3
+    assert g(ctypes.c_void_p(17), dummy, 1, 256, dummy, dummy, 16, 128, dummy, None, None, None, 0,
+             None) == 2  # NEST_EALIGN
+    assert g(dummy, dummy, 1, 256, dummy, dummy, 16, 128, None, dummy, None, None, 0, None) == 4
+    ws = lib.verify_accept_workspace_size
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int64] * 3
+    assert ws(1, 8, 152064) > 0

@@ -59,6 +59,20 @@
  *  holds element 2j in bits 0..3 and element 2j+1 in bits 4..7, as 4-bit
  *  two's complement. Each plane is exactly rows*cols/2 bytes.
  *  Scales: fp32 [rows][G]. Only s is stored; s16 is derived from it.
+ *  This row-major form is the storage format nest_pack writes.
+ *
+ *  Tile layout (what draft_gemv, verify_gemm and verify_accept read; made
+ *  from the storage format by nest_tile; group == 128). Rows go in tiles of
+ *  16, T = ceil(rows/16); the last tile is padded with zero rows.
+ *    plane: byte ((t*G + g)*4 + q)*256 + r*16 + j holds storage byte
+ *           (row 16t + r, byte 64g + 16q + j), i.e. per (tile, group) one
+ *           kilobyte of [k-quarter q][row r][16 bytes]. T*16*cols/2 bytes.
+ *    scales: float ((t*Gq + u)*16 + r)*4 + i, Gq = ceil(G/4), holds the
+ *           scale of (row 16t + r, group 4u + i); padding holds 0.
+ *           T*64*Gq floats.
+ *  Each 16-byte piece a GEMV lane needs, and the four scales of its quad,
+ *  are then contiguous across a wave, so the weight stream reads whole
+ *  kilobytes instead of 64-byte pieces of 16 rows.
  *
  * ---------------------------------------------------------------------------
  * Activations (the "A8" of W4A8 / W8A8 in BitNest's Table 1)
@@ -142,6 +156,21 @@ const char* nest_last_error(void);
 int nest_pack(const float* w, int64_t rows, int64_t cols, int64_t group,
               uint8_t* base, uint8_t* refine, float* scales, void* stream);
 
+/* nest_tile -- storage format (nest_pack) -> tile layout (above), for the
+ * planes and the scales of one weight matrix. Pure data movement.
+ *   base, refine  uint8 [rows][cols/2] (refine may be NULL, with refine_t)
+ *   scales        fp32 [rows][cols/128]
+ *   base_t, refine_t  uint8, nest_tile_plane_bytes(rows, cols) each (out)
+ *   scales_t      fp32, nest_tile_scale_count(rows, cols, group) (out)
+ * Requires group == 128, cols % 128 == 0, 16-byte aligned planes. The
+ * outputs must not overlap the inputs.
+ * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED, NEST_EHIP. */
+int nest_tile(const uint8_t* base, const uint8_t* refine, const float* scales,
+              int64_t rows, int64_t cols, int64_t group, uint8_t* base_t,
+              uint8_t* refine_t, float* scales_t, void* stream);
+size_t nest_tile_plane_bytes(int64_t rows, int64_t cols);            /* 0 if invalid */
+size_t nest_tile_scale_count(int64_t rows, int64_t cols, int64_t group); /* 0 if invalid */
+
 /* nest_act_quant -- per-row symmetric int8 quantization of activations.
  *   x   fp32 [M][K];  qa int8 [M][K] (out);  sa fp32 [M] (out).
  * Requires M >= 1 and K >= 1. Errors: NEST_EINVAL, NEST_EHIP. */
@@ -151,14 +180,16 @@ int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
 /* draft_gemv -- the draft's W4A8 product over the base plane only (BitNest,
  * Figure 3: "the draft accesses only the base plane").
  *   qa       int8 [M][K], 16-byte aligned;  sa fp32 [M]
- *   base     uint8 [N][K/2], 16-byte aligned;  scales fp32 [N][K/group]
+ *   base     base plane in the tile layout (nest_tile), 16-byte aligned
+ *   scales   scales in the tile layout, 16-byte aligned
  *   y        fp32 [M][N] (out, may be NULL when argmax is given)
  *   argmax   int32 [M] (out, nullable). When given, the fold is exact and
  *            argmax[m] is the index of the largest y[m][.].
  *   acc_dbg  int32 [M][N][K/group] (out, nullable): the exact Ab.
- *   ws       workspace of draft_gemv_workspace_size(M, N) bytes, needed
- *            only when argmax is given (else it may be NULL). It holds
- *            per-block partial maxima; no initial contents are required.
+ *   ws       workspace of draft_gemv_workspace_size(M, N) bytes, 16-byte
+ *            aligned, needed only when argmax is given (else it may be
+ *            NULL). It holds per-block partial maxima; no initial contents
+ *            are required.
  * Requires 1 <= M <= 16, group == 128, K % 128 == 0, N >= 1.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
@@ -168,11 +199,24 @@ int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                void* ws, size_t ws_bytes, void* stream);
 size_t draft_gemv_workspace_size(int64_t M, int64_t N);
 
+/* draft_gemv_x -- draft_gemv on fp32 activations. Each block quantizes x
+ * itself while staging it (the nest_act_quant rule above), so the result is
+ * bit-identical to nest_act_quant followed by draft_gemv, with one launch
+ * fewer.
+ *   x        fp32 [M][K], 16-byte aligned
+ *   the rest as for draft_gemv (no debug accumulators)
+ * Requires 1 <= M <= 16 and M*K <= 131072 (the activation codes are held in
+ * LDS); larger activations go through nest_act_quant and draft_gemv.
+ * Errors: as draft_gemv. */
+int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
+                 const float* scales, int64_t N, int64_t group, float* y,
+                 int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
+
 /* verify_gemm -- the target's W8A8 product over both planes (BitNest,
  * Figure 3: "the target accesses both planes to recover the full 8-bit
  * representation"), for the k+1 rows of a round or a batch of rounds.
  *   qa int8 [M][K] (16-byte aligned); sa fp32 [M]
- *   base, refine uint8 [N][K/2] (16-byte aligned); scales fp32 [N][K/group]
+ *   base, refine, scales: the tile layout (nest_tile), 16-byte aligned
  *   y fp32 [M][N] (out); acc_dbg int32 [M][N][K/group] (out, nullable): Av
  * Requires M >= 1, group == 128, K % 128 == 0, N >= 1. M <= 16 runs the
  * one-tile kernel. Larger M runs the batched MFMA kernel.
@@ -183,13 +227,20 @@ int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                 int64_t N, int64_t group, float* y, int32_t* acc_dbg,
                 void* stream);
 
+/* verify_gemm_x -- verify_gemm on fp32 activations, quantized in the kernel
+ * as for draft_gemv_x (bit-identical to nest_act_quant + verify_gemm).
+ * Requires 1 <= M <= 16 and M*K <= 131072. Errors: as verify_gemm. */
+int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
+                  const uint8_t* refine, const float* scales, int64_t N,
+                  int64_t group, float* y, void* stream);
+
 /* verify_accept -- the verify pass through the nested LM head, with the
  * greedy accept step ("How Speculative Decoding Speeds Up Inference",
  * numbered round steps and Table 1).
  *   qa int8 [B*(k+1)][K]; sa fp32 [B*(k+1)]. Row b*(k+1)+i is sequence b's
  *        input at slot i. Slot 0 is the last committed token and slot
  *        i >= 1 is draft token i.
- *   base, refine uint8 [V][K/2]; scales fp32 [V][K/group]: the LM head
+ *   base, refine, scales: the LM head in the tile layout (nest_tile)
  *   draft     int32 [B][k]: draft tokens d_1..d_k, each in [0, V)
  *   target    int32 [B][k+1] (out): t_i = argmax of the exact verify fold
  *             of row i
@@ -197,8 +248,8 @@ int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
  *             d_i == t_{i-1} for all 1 <= i <= j
  *   emitted   int32 [B][k+1] (out): t_0..t_a, then -1 in the unused slots
  *   y         fp32 [B*(k+1)][V] (out, nullable): the verify logits
- *   ws        verify_accept_workspace_size(B, k, V) bytes (per-block
- *             partial maxima; no initial contents are required).
+ *   ws        verify_accept_workspace_size(B, k, V) bytes, 16-byte aligned
+ *             (per-block partial maxima; no initial contents are required).
  * Requires B >= 1, k >= 0, B*(k+1) <= 16, group == 128, K % 128 == 0.
  * Draft ids are not read on the host, so an id outside [0, V) simply
  * never matches. Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE,
@@ -210,6 +261,17 @@ int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64_t k,
                   int32_t* emitted, float* y, void* ws, size_t ws_bytes,
                   void* stream);
 size_t verify_accept_workspace_size(int64_t B, int64_t k, int64_t V);
+
+/* verify_accept_x -- verify_accept on fp32 activations x [B*(k+1)][K]
+ * (16-byte aligned), quantized in the kernel as for draft_gemv_x
+ * (bit-identical to nest_act_quant + verify_accept). Requires
+ * B*(k+1)*K <= 131072. Errors: as verify_accept. */
+int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K,
+                    const uint8_t* base, const uint8_t* refine,
+                    const float* scales, int64_t V, int64_t group,
+                    const int32_t* draft, int32_t* target, int32_t* n_emitted,
+                    int32_t* emitted, float* y, void* ws, size_t ws_bytes,
+                    void* stream);
 
 /* Nested KV cache: a host struct holding device pointers (layouts above). */
 typedef struct nest_kv {

@@ -4,8 +4,11 @@
 // past ctx_len are never read, and the caller's length update discards a
 // rejected suffix.
 //
-// gfx950 design (flash-decoding). A workgroup of 4 waves walks a chunk of
-// 128-token blocks of one kv head. Per block:
+// gfx950 design (flash-decoding). Up to 16 query rows per kv head (the
+// draft's one query over a GQA group): attend_wave_kernel, where each wave
+// owns whole 128-token blocks and converts codes in registers. More rows
+// (verification's k+1 queries): a workgroup of 4 waves walks a chunk of
+// 128-token blocks of one kv head and shares converted operands. Per block:
 //   phase A  all 256 threads read the block's codes once (K token-major, V
 //            dim-major) and convert them to f16 MFMA operands in LDS
 //            (32 KB K + 32 KB V). A nibble (or the 8-bit code biased by
@@ -34,7 +37,8 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;
 constexpr int kBlk = 128;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTargetBlocks = 512;  // workgroups to aim for (two resident per CU)
+constexpr int kTargetBlocks = 512;  // LDS-table kernel: workgroups to aim for (two resident per CU)
+constexpr int kTargetWaves = 2048;  // wave kernel: waves to aim for (eight per CU)
 
 struct AttArgs {
   const uint16_t* q;
@@ -320,61 +324,246 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   }
 }
 
-// One block of 256 threads per (row, kv head). The chunk weights
-// 2^(m_c - M) go to LDS. Then each half-block sums the chunks of one parity
-// for all 128 dims, unrolled so that the loads overlap, and the two halves
-// are added (a fixed order).
-constexpr int kCombineChunks = 1024;  // chunks handled per LDS pass
+// Few query rows (R <= 16, e.g. one draft query over a GQA group): every
+// wave owns whole 128-token blocks. Lane (q4, c16) loads exactly the 16-byte
+// code slices its MFMA operands need (K: token tau(tt, c16), dims
+// 32*q4..32*q4+31, for the 8 token tiles; V: dim 16*dt + c16, tokens
+// 32*q4..32*q4+31, for the 8 dim tiles) and converts them in registers, so
+// the loop has no LDS tables and no barrier. Several resident waves per
+// SIMD overlap one wave's loads with another's arithmetic. The 4 waves of a workgroup
+// take interleaved blocks of its chunk and merge once at the end, in LDS,
+// in the fixed order w = 3 .. 0.
+template <int VIEW>
+__global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
+  __shared__ float ml[4][16][2];
+  __shared__ float buf[16][kD + 4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q4 = lane >> 4, c16 = lane & 15;
+  const int h = blockIdx.y, chunk = blockIdx.x;
 
-__global__ void __launch_bounds__(256) combine_kernel(AttArgs a) {
-  __shared__ float wts[kCombineChunks];
-  __shared__ float red[8];
-  __shared__ float half_acc[kD];
-  const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const size_t base = static_cast<size_t>(h) * a.nchunk * a.R + row;  // partial of chunk c: base + c*R
+  v8h qop[4];
+  int pos = -1;
+  if (c16 < a.R) {
+    const int i = c16 / a.grp, g = c16 % a.grp;
+    pos = a.ctx - a.nq + i;
+    const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint16_t* p = qr + 8 * s;
+      v8h v;
+      v[0] = bf16_to_h(p[0]); v[1] = bf16_to_h(p[2]); v[2] = bf16_to_h(p[4]); v[3] = bf16_to_h(p[6]);
+      v[4] = bf16_to_h(p[1]); v[5] = bf16_to_h(p[3]); v[6] = bf16_to_h(p[5]); v[7] = bf16_to_h(p[7]);
+      qop[s] = v;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qop[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  float m = -INFINITY, l = 0.0f;
+  v4f O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
+  const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
+
+  const int b_first = chunk * a.bpw;
+  const int b_last = min(b_first + a.bpw, a.nbv);
+  uint4 kb[8], kr[8], vb[8], vr[8];
+  auto load = [&](int blk) {
+    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
+      const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
+      const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
+      kb[tt] = ld16(a.kb + koff);
+      vb[tt] = ld16(a.vb + voff);
+      if (VIEW) {
+        kr[tt] = ld16(a.kr + koff);
+        vr[tt] = ld16(a.vr + voff);
+      } else {
+        kr[tt] = vr[tt] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  for (int blk = b_first + wave; blk < b_last; blk += 4) {
+    load(blk);
+    const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
+    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+    const int t0 = blk * kBlk;
+    const float sk = a.ks[hb] * sm_scale;
+    const float sv = VIEW ? a.vs[hb] * 0.0625f : a.vs[hb];
+    v4f S[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      v4f acc = v4f{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = mfma_h(codes_to_h8<VIEW>(word(ck[tt], s), word(cr[tt], s)), qop[s], acc);
+      S[tt] = acc;
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 32 * q4 + 8 * (tt >> 1) + 4 * (tt & 1) + i;
+        const float v = tok <= pos ? S[tt][i] * sk : -INFINITY;
+        S[tt][i] = v;
+        mb = fmaxf(mb, v);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);
+    const float mu = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = exp2f(m - mu);
+    float ls = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(S[tt][i] - mu);
+        S[tt][i] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l = l * alpha + ls;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4f e0 = S[2 * j], e1 = S[2 * j + 1];
+      v8h p;
+      p[0] = (_Float16)(e0[0] * sv); p[1] = (_Float16)(e0[2] * sv);
+      p[2] = (_Float16)(e1[0] * sv); p[3] = (_Float16)(e1[2] * sv);
+      p[4] = (_Float16)(e0[1] * sv); p[5] = (_Float16)(e0[3] * sv);
+      p[6] = (_Float16)(e1[1] * sv); p[7] = (_Float16)(e1[3] * sv);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        O[dt] = mfma_h(codes_to_h8<VIEW>(word(dk[dt], j), word(dr[dt], j)), p, O[dt]);
+    }
+  }
+
+  // merge the 4 waves (fixed order w = 3 .. 0) and write the chunk's partial
+  if (q4 == 0) {
+    ml[wave][c16][0] = m;
+    ml[wave][c16][1] = l;
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int c = t; c < a.nchunk; c += 256) M = fmaxf(M, a.part_ml[(base + static_cast<size_t>(c) * a.R) * 2]);
-  M = wave_max(M);
-  if ((t & 63) == 0) red[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w][c16][0]);
   const float Mu = M == -INFINITY ? 0.0f : M;
-  __syncthreads();
-  float L = 0.0f, acc = 0.0f;
-  const int dim = t & (kD - 1), par = t >> 7;
-  const float* po = a.part_o + base * kD + dim;
-  const size_t cstride = static_cast<size_t>(a.R) * kD;
-  for (int c0 = 0; c0 < a.nchunk; c0 += kCombineChunks) {
-    const int cn = min(kCombineChunks, a.nchunk - c0);
-    for (int c = t; c < cn; c += 256) {
-      const size_t pr = base + static_cast<size_t>(c0 + c) * a.R;
-      const float mc = a.part_ml[pr * 2];
-      const float w = mc == -INFINITY ? 0.0f : exp2f(mc - Mu);
-      wts[c] = w;
-      L += w * a.part_ml[pr * 2 + 1];
-    }
-    __syncthreads();
-    // chunks with no visible token have O = 0 and weight 0
-    int c = par;
-    for (; c + 14 < cn; c += 16) {
-      float v[8];
+  const float f = exp2f(m - Mu);
+  for (int step = 3; step >= 0; --step) {
+    if (wave == step) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = po[static_cast<size_t>(c0 + c + 2 * u) * cstride];
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(v[u], wts[c + 2 * u], acc);
+        for (int i = 0; i < 4; ++i) {
+          float* p = &buf[c16][dt * 16 + 4 * q4 + i];
+          const float v = O[dt][i] * f;
+          *p = step == 3 ? v : *p + v;
+        }
     }
-    for (; c < cn; c += 2) acc = fmaf(po[static_cast<size_t>(c0 + c) * cstride], wts[c], acc);
     __syncthreads();
   }
-  // total denominator: block sum of L
-  L = wave_sum(L);
-  if ((t & 63) == 0) red[4 + (t >> 6)] = L;
-  if (par == 1) half_acc[dim] = acc;
+  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;
+  for (int idx = threadIdx.x; idx < a.R * (kD / 4); idx += 256) {
+    const int row = idx / (kD / 4), d4 = idx % (kD / 4);
+    *reinterpret_cast<float4*>(&a.part_o[(pbase + row) * kD + 4 * d4]) =
+        *reinterpret_cast<const float4*>(&buf[row][4 * d4]);
+  }
+  if (threadIdx.x < a.R) {
+    const int row = threadIdx.x;
+    float Mr = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, ml[w][row][0]);
+    const float Mru = Mr == -INFINITY ? 0.0f : Mr;
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += ml[w][row][1] * exp2f(ml[w][row][0] - Mru);
+    a.part_ml[(pbase + row) * 2 + 0] = Mr;
+    a.part_ml[(pbase + row) * 2 + 1] = L;
+  }
+}
+
+// Merge of the chunk partials: one block of 1024 threads per (row, kv head).
+// Thread t sums the chunks c = t/128 (mod 8) of dim t % 128. Its first 16
+// partial outputs are loaded before the chunk weights 2^(m_c - M) are
+// known, so the kernel needs one round trip to memory for up to 128
+// chunks. Each strand adds its chunks in ascending order, and the 8
+// strands are then added in order (a fixed order overall).
+constexpr int kStrands = 8;
+constexpr int kBatch = 16;
+constexpr int kMaxChunks = 4096;
+
+__global__ void __launch_bounds__(1024) combine_kernel(AttArgs a) {
+  __shared__ float wts[kMaxChunks];
+  __shared__ float red_m[16], red_l[16];
+  __shared__ float accs[kStrands][kD];
+  const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int dim = t & (kD - 1), strand = t >> 7, wave = t >> 6;
+  const size_t base = static_cast<size_t>(h) * a.nchunk * a.R + row;  // partial of chunk c: base + c*R
+  const size_t cstride = static_cast<size_t>(a.R) * kD;
+  const float* po = a.part_o + base * kD + dim;
+  float v[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const int c = strand + i * kStrands;
+    v[i] = c < a.nchunk ? po[static_cast<size_t>(c) * cstride] : 0.0f;
+  }
+  float M = -INFINITY;
+  for (int c = t; c < a.nchunk; c += 1024) M = fmaxf(M, a.part_ml[(base + static_cast<size_t>(c) * a.R) * 2]);
+  M = wave_max(M);
+  if ((t & 63) == 0) red_m[wave] = M;
   __syncthreads();
-  if (par == 0) {
-    const float Lt = (red[4] + red[5]) + (red[6] + red[7]);
+  M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) M = fmaxf(M, red_m[w]);
+  const float Mu = M == -INFINITY ? 0.0f : M;
+  float L = 0.0f;
+  for (int c = t; c < a.nchunk; c += 1024) {
+    const size_t pr = base + static_cast<size_t>(c) * a.R;
+    const float mc = a.part_ml[pr * 2];
+    const float w = mc == -INFINITY ? 0.0f : exp2f(mc - Mu);  // chunks with no visible token: O = 0
+    wts[c] = w;
+    L += w * a.part_ml[pr * 2 + 1];
+  }
+  L = wave_sum(L);
+  if ((t & 63) == 0) red_l[wave] = L;
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const int c = strand + i * kStrands;
+    if (c < a.nchunk) acc = fmaf(v[i], wts[c], acc);
+  }
+  for (int c0 = kBatch * kStrands; c0 < a.nchunk; c0 += kBatch * kStrands) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + strand + i * kStrands;
+      v[i] = c < a.nchunk ? po[static_cast<size_t>(c) * cstride] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + strand + i * kStrands;
+      if (c < a.nchunk) acc = fmaf(v[i], wts[c], acc);
+    }
+  }
+  accs[strand][dim] = acc;
+  __syncthreads();
+  if (strand == 0) {
+    float o = accs[0][dim];
+#pragma unroll
+    for (int s2 = 1; s2 < kStrands; ++s2) o += accs[s2][dim];
+    float Lt = red_l[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) Lt += red_l[w];
     const int i = row / a.grp, g = row % a.grp;
-    a.out[(static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + dim] = (acc + half_acc[dim]) / Lt;
+    a.out[(static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + dim] = o / Lt;
   }
 }
 
@@ -383,15 +572,23 @@ struct Plan {
   size_t ws;
 };
 
+// Work split. Up to 16 query rows: one 128-token block per wave while the
+// chip has wave slots to spare (about kTargetWaves), 4 waves per workgroup.
+// More rows: the LDS-table kernel with about kTargetBlocks workgroups.
 Plan make_plan(int64_t nq, int64_t Hq, int64_t Hkv, int64_t ctx) {
   Plan p{};
   const int64_t R = nq * (Hq / Hkv);
   p.nbv = static_cast<int>((ctx + kBlk - 1) / kBlk);
-  const int64_t blocks = Hkv * p.nbv;
-  p.bpw = static_cast<int>((blocks + kTargetBlocks - 1) / kTargetBlocks);
-  if (p.bpw < 1) p.bpw = 1;
-  p.nchunk = (p.nbv + p.bpw - 1) / p.bpw;
   p.RT = static_cast<int>((R + 15) / 16);
+  const int64_t blocks = Hkv * p.nbv;
+  if (p.RT == 1) {
+    const int64_t per_wave = (blocks + kTargetWaves - 1) / kTargetWaves;
+    p.bpw = static_cast<int>(4 * per_wave);
+  } else {
+    p.bpw = static_cast<int>((blocks + kTargetBlocks - 1) / kTargetBlocks);
+  }
+  if (p.bpw < 1) p.bpw = 1;
+  p.nchunk = (p.nbv + p.bpw - 1) / p.bpw;  // at most about max(kTargetWaves/4, kTargetBlocks)/Hkv + 1
   const size_t rows = static_cast<size_t>(Hkv) * p.nchunk * R;
   p.ws = (((rows * 2 + 3) & ~static_cast<size_t>(3)) + rows * kD) * sizeof(float);
   return p;
@@ -401,14 +598,14 @@ template <int VIEW>
 int launch_att(const AttArgs& a, const Plan& p, int Hkv, hipStream_t st) {
   dim3 grid(p.nchunk, Hkv);
   switch (p.RT) {
-    case 1: attend_kernel<1, VIEW><<<grid, 256, 0, st>>>(a); break;
+    case 1: attend_wave_kernel<VIEW><<<grid, 256, 0, st>>>(a); break;
     case 2: attend_kernel<2, VIEW><<<grid, 256, 0, st>>>(a); break;
     case 3: attend_kernel<3, VIEW><<<grid, 256, 0, st>>>(a); break;
     default: attend_kernel<4, VIEW><<<grid, 256, 0, st>>>(a); break;
   }
   int rc = nest::check_launch("kv_nest_attend");
   if (rc) return rc;
-  combine_kernel<<<dim3(a.R, Hkv), 256, 0, st>>>(a);
+  combine_kernel<<<dim3(a.R, Hkv), 1024, 0, st>>>(a);
   return nest::check_launch("kv_nest_attend(combine)");
 }
 
@@ -448,6 +645,7 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
       (view == 1 && (!nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))))
     return nest::fail(NEST_EALIGN, "%s: planes must be 16-byte aligned", what);
   const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_len);
+  if (p.nchunk > kMaxChunks) return nest::fail(NEST_EUNSUPPORTED, "%s: too many chunks", what);
   if (!ws || ws_bytes < p.ws) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, p.ws);
   if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
   AttArgs a{};

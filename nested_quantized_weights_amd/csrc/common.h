@@ -78,3 +78,21 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   hi = __shfl_xor(hi, o, 64);
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
+
+// clamp(rint(x / s), -127, 127) with x / s the IEEE quotient, computed as
+// t = x * r with r = 1/s (itself correctly rounded). |x / s| <= 127(1 + 2^-23),
+// so |t - x/s| and |fl(x/s) - x/s| are both below 1.6e-5. When t is more
+// than 3e-5 away from the nearest half-integer, t, x/s and fl(x/s) lie on
+// the same side of it and round alike. Only near a tie is the quotient
+// formed exactly. s == 0 gives 0; an r that overflows takes the exact path.
+__device__ __forceinline__ int quant_act(float x, float s, float r) {
+  if (s == 0.0f) return 0;
+  const float t = x * r;
+  float q;
+  if (fabsf(t - floorf(t) - 0.5f) > 3.0e-5f && r < INFINITY)
+    q = rintf(t);
+  else
+    q = rintf(x / s);
+  q = q < -127.0f ? -127.0f : (q > 127.0f ? 127.0f : q);
+  return static_cast<int>(q);
+}

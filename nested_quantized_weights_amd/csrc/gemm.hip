@@ -2,8 +2,9 @@
 // base and the refinement plane) for more than 16 activation rows, e.g. 16
 // sequences x (k+1) = 144 rows.
 //
-// One wave owns 16 weight rows (the MFMA A operand: row lane & 15,
-// k-quarter lane >> 4) and all CT 16-row column tiles of activations. Per
+// One wave owns a 16-row weight tile in the tile layout (the MFMA A operand:
+// row lane & 15, k-quarter lane >> 4; one contiguous kilobyte per group) and
+// all CT 16-row column tiles of activations. Per
 // group, the plane bytes are unpacked once and reused for every column
 // tile: two v_mfma_i32_16x16x64_i8 per plane and tile. The fp32 fold stays
 // in registers, one run per (column tile, row) entry, in ascending group
@@ -68,7 +69,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
   const int g_begin = static_cast<int>(static_cast<long long>(seg) * G / S);
   const int g_end = static_cast<int>(static_cast<long long>(seg + 1) * G / S);
   const int kq = lane >> 4, col = lane & 15;
-  const size_t rowb = static_cast<size_t>(a.K / 2);
+  const int Gq = (G + 3) / 4;
   const int8_t* pa = a.qa + kq * 32;
   __shared__ float part[4][CT][4][64];
 
@@ -76,13 +77,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
     const int n0 = (it * per_iter + wave / S) * 16;
     const bool tile_ok = n0 < a.N;
     const int n_out0 = n0 + 4 * kq;
-    const int arow = min(n0 + col, a.N - 1);
-    const uint8_t* pb = a.base + arow * rowb + kq * 16;
-    const uint8_t* pr = a.refine + arow * rowb + kq * 16;
-    const float* ps0 = a.scales + static_cast<size_t>(min(n_out0 + 0, a.N - 1)) * G;
-    const float* ps1 = a.scales + static_cast<size_t>(min(n_out0 + 1, a.N - 1)) * G;
-    const float* ps2 = a.scales + static_cast<size_t>(min(n_out0 + 2, a.N - 1)) * G;
-    const float* ps3 = a.scales + static_cast<size_t>(min(n_out0 + 3, a.N - 1)) * G;
+    // tile layout: lane (kq, col) reads 16 bytes of row n0 + col at
+    // ((t*G + g)*4 + kq)*256 + col*16; the scales of rows n0 + 4kq + r sit at
+    // ((t*Gq + g/4)*16 + 4kq + r)*4 + g%4 (padded rows and groups hold 0)
+    const size_t t = static_cast<size_t>(n0 / 16);
+    const uint8_t* pb = a.base + (t * G * 4 + kq) * 256 + col * 16;
+    const uint8_t* pr = a.refine + (t * G * 4 + kq) * 256 + col * 16;
+    const float* ps = a.scales + (t * Gq * 16 + 4 * kq) * 4;
     float run[CT][4];
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -90,9 +91,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 4; ++r) run[c][r] = 0.0f;
     if (tile_ok) {
       for (int g = g_begin; g < g_end; ++g) {
-        const uint4 wb = nest::ld16(pb + static_cast<size_t>(g) * 64);
-        const uint4 wr = nest::ld16(pr + static_cast<size_t>(g) * 64);
-        const float4 s = make_float4(ps0[g], ps1[g], ps2[g], ps3[g]);
+        const uint4 wb = nest::ld16(pb + static_cast<size_t>(g) * 1024);
+        const uint4 wr = nest::ld16(pr + static_cast<size_t>(g) * 1024);
+        const float* pq = ps + static_cast<size_t>(g / 4) * 64 + (g & 3);
+        const float4 s = make_float4(pq[0], pq[4], pq[8], pq[12]);
         gemm_group<CT, DBG>(a, pa, col, n_out0, g, wb, wr, s, run);
       }
     }

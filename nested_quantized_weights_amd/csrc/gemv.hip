@@ -22,7 +22,11 @@
 //
 // When the M x K activation bytes fit, each block stages them once in LDS,
 // already split into even/odd operand order, so the main loop streams
-// only the planes and scales from HBM. Blocks loop over tiles with a grid
+// only the planes and scales from HBM. The *_x entry points take fp32
+// activations instead: every block quantizes them itself while staging
+// (s_a = max|x|/127 per row, q = clamp(rint(x/s_a), +-127), the rule of
+// nest_act_quant), so the round needs no separate quantization launch.
+// Blocks loop over tiles with a grid
 // stride, and the grid is at most what fits on the chip. The argmax path
 // keeps per-lane best (value, index) keys across tiles and writes one key
 // per row and block. A second small kernel reduces the keys and, for
@@ -36,11 +40,13 @@ using nest::kGroup;
 using nest::ld16;
 
 constexpr int kMaxArgmaxBlocks = 4096;
-constexpr int kLdsActMax = 48 * 1024;  // largest M*K staged in LDS
+constexpr int kLdsActMax = 48 * 1024;     // largest M*K staged in LDS from int8 activations
+constexpr int kLdsActMaxX = 128 * 1024;   // largest M*K the fp32-activation path stages
 
 struct GemvArgs {
   const int8_t* qa;
   const float* sa;
+  const float* x;  // fp32 activations (the *_x entry points), else null
   int M, K;
   const uint8_t* base;
   const uint8_t* refine;
@@ -66,6 +72,92 @@ struct FinishArgs {
 // k-quarter kq, group g.
 __device__ __forceinline__ int lds_slot(int g, int p, int kq, int m, int M) {
   return ((g * 2 + p) * 4 + kq) * M + m;
+}
+
+__device__ __forceinline__ uint32_t quant4(float4 v, float s, float r) {
+  return (static_cast<uint32_t>(quant_act(v.x, s, r)) & 0xFFu) |
+         ((static_cast<uint32_t>(quant_act(v.y, s, r)) & 0xFFu) << 8) |
+         ((static_cast<uint32_t>(quant_act(v.z, s, r)) & 0xFFu) << 16) |
+         ((static_cast<uint32_t>(quant_act(v.w, s, r)) & 0xFFu) << 24);
+}
+
+__device__ __forceinline__ float absmax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// Code 16 elements (an "item") with the row's (s, 1/s) and store their even
+// and odd bytes into the two operand slots of their k-quarter. Item idx of
+// a row covers elements [16*idx, 16*idx + 16): group idx >> 3, k-quarter
+// (idx >> 1) & 3, half idx & 1 of that quarter.
+__device__ __forceinline__ void store_item(uint2* lds2, int M, int m, int idx, const float4 (&v)[4],
+                                           float s, float r) {
+  const int half = idx & 1, q = (idx >> 1) & 3, g = idx >> 3;
+  const uint32_t w0 = quant4(v[0], s, r), w1 = quant4(v[1], s, r), w2 = quant4(v[2], s, r),
+                 w3 = quant4(v[3], s, r);
+  lds2[lds_slot(g, 0, q, m, M) * 2 + half] =
+      make_uint2(__builtin_amdgcn_perm(w1, w0, 0x06040200u), __builtin_amdgcn_perm(w3, w2, 0x06040200u));
+  lds2[lds_slot(g, 1, q, m, M) * 2 + half] =
+      make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07050301u), __builtin_amdgcn_perm(w3, w2, 0x07050301u));
+}
+
+// Per-token int8 quantization of fp32 activations x [M][K], written straight
+// into the LDS operand layout. Thread t owns items t, t + NT, ... of the
+// flattened rows. Its first ITEMS items are loaded at once and kept in
+// registers, so a block that fits (M*K <= 16*ITEMS*NT) reads x in one round
+// trip. Row maxima of |x| merge through an LDS max on the float bits (they
+// order like the values for x >= 0); items past the first ITEMS*NT are read
+// once for the maximum and again for coding.
+template <int NT, int ITEMS>
+__device__ __forceinline__ void stage_quantized(const float* __restrict__ x, int M, int K, int G,
+                                                uint4* lds, float* sa_sh, unsigned* amax_sh) {
+  const int t = threadIdx.x;
+  const int ipr = G * 8, total = M * ipr;
+  float4 v[ITEMS][4];
+  int row[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int h = t + j * NT;
+    row[j] = h < total ? h / ipr : -1;
+    if (row[j] >= 0) {
+      const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(row[j]) * K) +
+                          4 * (h - row[j] * ipr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = src[e];
+    }
+  }
+  if (t < 16) amax_sh[t] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (row[j] >= 0)
+      atomicMax(&amax_sh[row[j]],
+                __float_as_uint(fmaxf(fmaxf(absmax4(v[j][0]), absmax4(v[j][1])),
+                                      fmaxf(absmax4(v[j][2]), absmax4(v[j][3])))));
+  for (int h = t + ITEMS * NT; h < total; h += NT) {
+    const int m = h / ipr;
+    const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(m) * K) + 4 * (h - m * ipr);
+    atomicMax(&amax_sh[m], __float_as_uint(fmaxf(fmaxf(absmax4(src[0]), absmax4(src[1])),
+                                                 fmaxf(absmax4(src[2]), absmax4(src[3])))));
+  }
+  __syncthreads();
+  if (t < M) {
+    const float s = __uint_as_float(amax_sh[t]) / 127.0f;
+    sa_sh[t] = s;
+    sa_sh[16 + t] = 1.0f / s;
+  }
+  __syncthreads();
+  uint2* lds2 = reinterpret_cast<uint2*>(lds);
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (row[j] >= 0)
+      store_item(lds2, M, row[j], t + j * NT - row[j] * ipr, v[j], sa_sh[row[j]], sa_sh[16 + row[j]]);
+  for (int h = t + ITEMS * NT; h < total; h += NT) {
+    const int m = h / ipr;
+    const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(m) * K) + 4 * (h - m * ipr);
+    const float4 w[4] = {src[0], src[1], src[2], src[3]};
+    store_item(lds2, M, m, h - m * ipr, w, sa_sh[m], sa_sh[16 + m]);
+  }
+  __syncthreads();
 }
 
 template <int PLANES, int MR, bool DBG, bool LDSACT>
@@ -107,55 +199,96 @@ __device__ __forceinline__ void gemv_group(const GemvArgs& a, const uint4* lds, 
   }
 }
 
-// Fold groups [g0, g1) of one tile. A4: G % 4 == 0 and the segment is
-// 4-aligned, so the lane's scales load as one float4 per four groups and
-// the plane stream is software-pipelined by four groups.
+// Four consecutive groups of one lane's weight row: 16 plane bytes per
+// group and plane, and the four scales.
+struct Quad {
+  uint4 b0, b1, b2, b3, r0, r1, r2, r3;
+  float4 s;
+};
+
+// A lane's place in the tile layout (nestspec.h, nest_tile): for tile t and
+// group g, the planes hold 1 KB = [k-quarter][16 rows][16 bytes], so lane
+// (kq, c) reads 16 bytes at ((t*G + g)*4 + kq)*256 + c*16 and a wave's load
+// covers the whole kilobyte; the scales hold [quad][16 rows][4], so lane c
+// reads the float4 of groups 4u..4u+3 at ((t*Gq + u)*16 + c)*4.
+struct TilePtr {
+  const uint8_t* pb;  // group 0 of the lane's 16 bytes; group g adds g * 1024
+  const uint8_t* pr;
+  const float* ps;    // quad 0 of the lane's scales; quad u adds u * 64
+};
+
+template <int PLANES>
+__device__ __forceinline__ TilePtr tile_ptr(const GemvArgs& a, int t, int kq, int c) {
+  const size_t pl = (static_cast<size_t>(t) * a.G * 4 + kq) * 256 + c * 16;
+  TilePtr p;
+  p.pb = a.base + pl;
+  p.pr = PLANES == 2 ? a.refine + pl : nullptr;
+  p.ps = a.scales + (static_cast<size_t>(t) * ((a.G + 3) / 4) * 16 + c) * 4;
+  return p;
+}
+
+template <int PLANES>
+__device__ __forceinline__ void load_quad(const TilePtr& p, int g, Quad& q) {
+  q.b0 = ld16(p.pb + static_cast<size_t>(g) * 1024);
+  q.b1 = ld16(p.pb + static_cast<size_t>(g + 1) * 1024);
+  q.b2 = ld16(p.pb + static_cast<size_t>(g + 2) * 1024);
+  q.b3 = ld16(p.pb + static_cast<size_t>(g + 3) * 1024);
+  if (PLANES == 2) {
+    q.r0 = ld16(p.pr + static_cast<size_t>(g) * 1024);
+    q.r1 = ld16(p.pr + static_cast<size_t>(g + 1) * 1024);
+    q.r2 = ld16(p.pr + static_cast<size_t>(g + 2) * 1024);
+    q.r3 = ld16(p.pr + static_cast<size_t>(g + 3) * 1024);
+  } else {
+    q.r0 = q.r1 = q.r2 = q.r3 = make_uint4(0, 0, 0, 0);
+  }
+  q.s = *reinterpret_cast<const float4*>(p.ps + static_cast<size_t>(g / 4) * 64);
+}
+
+// Fold groups [g0, g1) of one tile (A4: 4-aligned bounds; cur holds the
+// quad at g0, already loaded). The next quad is loaded while the current one
+// is multiplied. Without A4 the groups are loaded one at a time.
 template <int PLANES, int MR, bool DBG, bool A4, bool LDSACT>
-__device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds, const uint8_t* pb,
-                                             const uint8_t* pr, const float* ps, const int8_t* pa,
-                                             int kq, int mrow, int n, int g0, int g1, float (&run)[MR]) {
+__device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds, const TilePtr& tp,
+                                             const int8_t* pa, int kq, int mrow, int n, int g0, int g1,
+                                             float (&run)[MR], Quad& cur) {
   if (A4) {
-    uint4 b0, b1, b2, b3, r0, r1, r2, r3;
-    auto load = [&](int g, uint4& x0, uint4& x1, uint4& x2, uint4& x3, uint4& y0, uint4& y1,
-                    uint4& y2, uint4& y3) {
-      x0 = ld16(pb + static_cast<size_t>(g) * 64);
-      x1 = ld16(pb + static_cast<size_t>(g + 1) * 64);
-      x2 = ld16(pb + static_cast<size_t>(g + 2) * 64);
-      x3 = ld16(pb + static_cast<size_t>(g + 3) * 64);
-      if (PLANES == 2) {
-        y0 = ld16(pr + static_cast<size_t>(g) * 64);
-        y1 = ld16(pr + static_cast<size_t>(g + 1) * 64);
-        y2 = ld16(pr + static_cast<size_t>(g + 2) * 64);
-        y3 = ld16(pr + static_cast<size_t>(g + 3) * 64);
-      } else {
-        y0 = y1 = y2 = y3 = make_uint4(0, 0, 0, 0);
-      }
-    };
-    if (g0 < g1) load(g0, b0, b1, b2, b3, r0, r1, r2, r3);
     for (int g = g0; g < g1; g += 4) {
-      uint4 nb0, nb1, nb2, nb3, nr0, nr1, nr2, nr3;
-      if (g + 4 < g1) load(g + 4, nb0, nb1, nb2, nb3, nr0, nr1, nr2, nr3);
-      const float4 s = *reinterpret_cast<const float4*>(ps + g);
-      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, b0, r0, s.x, run);
-      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 1, b1, r1, s.y, run);
-      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 2, b2, r2, s.z, run);
-      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 3, b3, r3, s.w, run);
-      b0 = nb0; b1 = nb1; b2 = nb2; b3 = nb3;
-      r0 = nr0; r1 = nr1; r2 = nr2; r3 = nr3;
+      Quad q;
+      const bool more = g + 4 < g1;
+      if (more) load_quad<PLANES>(tp, g + 4, q);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, cur.b0, cur.r0, cur.s.x, run);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 1, cur.b1, cur.r1, cur.s.y, run);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 2, cur.b2, cur.r2, cur.s.z, run);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 3, cur.b3, cur.r3, cur.s.w, run);
+      if (more) cur = q;
     }
   } else {
     for (int g = g0; g < g1; ++g) {
-      const uint4 wb = ld16(pb + static_cast<size_t>(g) * 64);
-      const uint4 wr = PLANES == 2 ? ld16(pr + static_cast<size_t>(g) * 64) : make_uint4(0, 0, 0, 0);
-      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, wb, wr, ps[g], run);
+      const uint4 wb = ld16(tp.pb + static_cast<size_t>(g) * 1024);
+      const uint4 wr = PLANES == 2 ? ld16(tp.pr + static_cast<size_t>(g) * 1024) : make_uint4(0, 0, 0, 0);
+      gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, wb, wr,
+                                          tp.ps[static_cast<size_t>(g / 4) * 64 + (g & 3)], run);
     }
   }
 }
 
 // WAVES waves per block; a tile takes nseg consecutive waves (nseg | WAVES).
-// ARGMAX requires nseg == 1.
-template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT>
-__global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
+// ARGMAX requires nseg == 1. XQ: fp32 activations, quantized while staging
+// (requires LDSACT). The first quad of each wave's first tile is requested
+// before the activations are staged, so staging overlaps the first HBM
+// round trip of the weights.
+// Waves per SIMD the register allocation must allow. The streams need
+// enough waves in flight; the targets are the largest that compile without
+// spills for each fold (the debug build is left unconstrained).
+constexpr int occupancy_target(int planes, int mr, bool lds, bool dbg) {
+  return dbg ? 1 : planes == 2 ? 3 : mr == 4 ? 4 : lds ? 5 : 4;
+}
+
+template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
+__global__ void __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(occupancy_target(PLANES, MR, LDSACT, DBG))))
+gemv_kernel(GemvArgs a) {
+  static_assert(!XQ || LDSACT, "fp32 activations are quantized into LDS");
   extern __shared__ uint4 lds_act[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int S = a.nseg, per_iter = WAVES / S;
@@ -166,10 +299,23 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   const int g_end = static_cast<int>(static_cast<long long>(seg + 1) * units / S) * unit;
   const int kq = lane >> 4, c = lane & 15;
   const int mrow = min(c, a.M - 1);  // A-operand row of this lane (rows past M fill unused D rows)
-  const size_t rowb = static_cast<size_t>(a.K / 2);
-  const int8_t* pa = a.qa + static_cast<size_t>(mrow) * a.K + kq * 32;
+  const int8_t* pa = LDSACT ? nullptr : a.qa + static_cast<size_t>(mrow) * a.K + kq * 32;
+  auto tile_n0 = [&](int it) { return (it * per_iter + wave / S) * 16; };
 
-  if (LDSACT) {
+  Quad cur;
+  int it = blockIdx.x;
+  if (A4 && it < iters && tile_n0(it) < a.N && g_begin < g_end)
+    load_quad<PLANES>(tile_ptr<PLANES>(a, tile_n0(it) / 16, kq, c), g_begin, cur);
+
+  __shared__ float sa_sh[32];  // [0, 16): s_a per row; [16, 32): 1 / s_a
+  __shared__ unsigned amax_sh[16];
+  if (XQ) {
+    // items held in registers: one round trip for the draft's single row
+    // (K <= 16 * NT with 4 waves, 32 * NT with more) and, for several rows,
+    // as many as the fold's own register budget leaves room for
+    stage_quantized<WAVES * 64, (MR == 1 ? (WAVES == 4 ? 1 : 2) : (WAVES >= 16 ? 1 : 4))>(
+        a.x, a.M, a.K, G, lds_act, sa_sh, amax_sh);
+  } else if (LDSACT) {
     // stage all M x K activation bytes once, split into operand order
     const int units32 = a.M * G * 4;
     for (int u = threadIdx.x; u < units32; u += WAVES * 64) {
@@ -188,22 +334,20 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   for (int r = 0; r < MR; ++r) best[r] = 0;
   float s_a[MR];
 #pragma unroll
-  for (int r = 0; r < MR; ++r) s_a[r] = a.sa[min(4 * kq + r, a.M - 1)];
+  for (int r = 0; r < MR; ++r) s_a[r] = XQ ? sa_sh[min(4 * kq + r, a.M - 1)] : a.sa[min(4 * kq + r, a.M - 1)];
 
-  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
-    const int n0 = (it * per_iter + wave / S) * 16;
+  for (; it < iters; it += gridDim.x) {
+    const int n0 = tile_n0(it);
     const bool tile_ok = n0 < a.N;
     const int n = n0 + c;  // this lane's output column (weight row)
-    const int wrow = min(n, a.N - 1);
-    const uint8_t* pb = a.base + wrow * rowb + kq * 16;
-    const uint8_t* pr = PLANES == 2 ? a.refine + wrow * rowb + kq * 16 : nullptr;
-    const float* ps = a.scales + static_cast<size_t>(wrow) * G;
+    const TilePtr tp = tile_ptr<PLANES>(a, n0 / 16, kq, c);
     float run[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) run[r] = 0.0f;
+    // the first tile's first quad was requested before staging
+    if (A4 && tile_ok && it != static_cast<int>(blockIdx.x) && g_begin < g_end) load_quad<PLANES>(tp, g_begin, cur);
     if (tile_ok)
-      gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, pb, pr, ps, pa, kq, mrow, n, g_begin,
-                                                g_end, run);
+      gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur);
 
     if (ARGMAX) {
       if (tile_ok && n < a.N) {
@@ -266,22 +410,50 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
 }
 
 // Reduce the per-block argmax keys; ACCEPT also applies the accept rule.
-// One block of 1024 threads: 64 strands per row.
+// One block of 1024 threads. Thread t reads the keys of blocks t, t + 1024,
+// ... for the M live rows, all loads issued before any is used, so the
+// kernel waits for one round trip to memory. Rows are then reduced per
+// wave (shuffles) and across the 16 waves (LDS).
 template <bool ACCEPT>
 __global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
-  __shared__ unsigned long long red[64][16];
+  constexpr int kPer = kMaxArgmaxBlocks / 1024;
+  __shared__ unsigned long long red[16][16];
   __shared__ int32_t tgt[16];
-  const int m = threadIdx.x & 15, p = threadIdx.x >> 4;
-  unsigned long long k = 0;
-#pragma unroll 8
-  for (int b = p; b < f.nparts; b += 64) k = umax64(k, f.partials[static_cast<size_t>(b) * 16 + m]);
-  red[p][m] = k;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int nv = (f.M + 1) >> 1;  // 16-byte pairs of keys per block
+  unsigned long long best[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) best[r] = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int b = t + j * 1024;
+    if (b < f.nparts) {
+      const uint4* p = reinterpret_cast<const uint4*>(f.partials + static_cast<size_t>(b) * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < nv) {
+          const uint4 w = p[i];
+          best[2 * i] = umax64(best[2 * i], (static_cast<unsigned long long>(w.y) << 32) | w.x);
+          best[2 * i + 1] = umax64(best[2 * i + 1], (static_cast<unsigned long long>(w.w) << 32) | w.z);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < f.M) {
+      unsigned long long k = best[r];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) k = umax64(k, shfl_xor_u64(k, o));
+      if (lane == 0) red[r][wave] = k;
+    }
+  }
   __syncthreads();
-  if (threadIdx.x < 16) {
-    unsigned long long t = 0;
-    for (int q = 0; q < 64; ++q) t = umax64(t, red[q][threadIdx.x]);
-    tgt[threadIdx.x] = static_cast<int32_t>(argmax_key_index(t));
-    if (!ACCEPT && threadIdx.x < f.M) f.argmax_out[threadIdx.x] = tgt[threadIdx.x];
+  if (t < f.M) {
+    unsigned long long k = 0;
+    for (int w = 0; w < 16; ++w) k = umax64(k, red[t][w]);
+    tgt[t] = static_cast<int32_t>(argmax_key_index(k));
+    if (!ACCEPT) f.argmax_out[t] = tgt[t];
   }
   __syncthreads();
   if (ACCEPT && threadIdx.x < f.B) {
@@ -302,49 +474,79 @@ __global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
 // host side
 // ---------------------------------------------------------------------------
 
-int pick_split(int tiles, int G) {
+int pick_split(int tiles, int G, int max_split) {
   // Enough waves to keep HBM busy (~8 per CU), at least two groups each.
   int s = 1;
-  while (s < 16 && static_cast<long long>(tiles) * s < 2048 && G / (2 * s) >= 2) s *= 2;
+  while (s < max_split && static_cast<long long>(tiles) * s < 2048 && G / (2 * s) >= 2) s *= 2;
   return s;
 }
 
-template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT>
+// The two-plane fold needs more than the 128 VGPRs a wave of a 1024-thread
+// block may hold, so it uses at most 8 waves per block.
+int max_split(int planes) { return planes == 2 ? 8 : 16; }
+
+template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
 int launch_one(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
-  auto kern = gemv_kernel<PLANES, MR, WAVES, ARGMAX, DBG, A4, LDSACT>;
+  auto kern = gemv_kernel<PLANES, MR, WAVES, ARGMAX, DBG, A4, LDSACT, XQ>;
   const size_t lds = LDSACT ? static_cast<size_t>(a.M) * a.K : 0;
+  if (lds > 64 * 1024) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       kLdsActMaxX);
+    if (attr != hipSuccess)
+      return nest::fail(NEST_EHIP, "%s: cannot raise the LDS limit: %s", what, hipGetErrorString(attr));
+  }
   const int per_iter = WAVES / a.nseg;
   const int iters = ((a.N + 15) / 16 + per_iter - 1) / per_iter;
-  int blocks = min(iters, nest::resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, lds));
-  blocks = min(blocks, max_blocks);
+  // As many blocks as fit, then evened out so that every block runs the
+  // same number of tile iterations (a last, partly filled round would run
+  // at a fraction of the chip's bandwidth).
+  const int fit = min(max_blocks, nest::resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, lds));
+  const int rounds = (iters + fit - 1) / fit;
+  const int blocks = (iters + rounds - 1) / rounds;
   if (used) *used = blocks;
   kern<<<dim3(blocks), dim3(WAVES * 64), lds, st>>>(a);
   return nest::check_launch(what);
 }
 
-template <int PLANES, int MR, bool ARGMAX, bool DBG, bool A4, bool LDSACT>
+template <int PLANES, int MR, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
 int launch_waves(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
   if (ARGMAX || a.nseg <= 4)
-    return launch_one<PLANES, MR, 4, ARGMAX, DBG, A4, LDSACT>(a, st, what, max_blocks, used);
+    return launch_one<PLANES, MR, 4, ARGMAX, DBG, A4, LDSACT, XQ>(a, st, what, max_blocks, used);
   if constexpr (!ARGMAX) {
-    if (a.nseg == 8) return launch_one<PLANES, MR, 8, false, DBG, A4, LDSACT>(a, st, what, max_blocks, used);
-    return launch_one<PLANES, MR, 16, false, DBG, A4, LDSACT>(a, st, what, max_blocks, used);
+    if (PLANES == 2 || a.nseg == 8)
+      return launch_one<PLANES, MR, 8, false, DBG, A4, LDSACT, XQ>(a, st, what, max_blocks, used);
+    if constexpr (PLANES == 1)
+      return launch_one<PLANES, MR, 16, false, DBG, A4, LDSACT, XQ>(a, st, what, max_blocks, used);
   }
   return NEST_EHIP;
 }
 
+// Kernel choice: one-row (MR = 1) or up-to-16-row (MR = 4) fold; A4 (groups
+// in quads) when G % 4 == 0; LDS-staged activations when M*K fits; the fp32
+// activation path (a.x set) always stages, quantizing on the way.
 template <int PLANES, bool ARGMAX, bool DBG>
 int launch_gemv(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
-  const bool a4 = a.G % 4 == 0 && nest::aligned16(a.scales);
-  const bool ldsact = a4 && static_cast<long long>(a.M) * a.K <= kLdsActMax;
-  if (a.M == 1) {
-    if (ldsact) return launch_waves<PLANES, 1, ARGMAX, DBG, true, true>(a, st, what, max_blocks, used);
-    if (a4) return launch_waves<PLANES, 1, ARGMAX, DBG, true, false>(a, st, what, max_blocks, used);
-    return launch_waves<PLANES, 1, ARGMAX, DBG, false, false>(a, st, what, max_blocks, used);
+  const bool a4 = a.G % 4 == 0;
+  const bool stage = a.x || (a4 && static_cast<long long>(a.M) * a.K <= kLdsActMax);
+  if constexpr (!DBG) {
+    if (a.x) {
+      if (a.M == 1)
+        return a4 ? launch_waves<PLANES, 1, ARGMAX, false, true, true, true>(a, st, what, max_blocks, used)
+                  : launch_waves<PLANES, 1, ARGMAX, false, false, true, true>(a, st, what, max_blocks, used);
+      return a4 ? launch_waves<PLANES, 4, ARGMAX, false, true, true, true>(a, st, what, max_blocks, used)
+                : launch_waves<PLANES, 4, ARGMAX, false, false, true, true>(a, st, what, max_blocks, used);
+    }
   }
-  if (ldsact) return launch_waves<PLANES, 4, ARGMAX, DBG, true, true>(a, st, what, max_blocks, used);
-  if (a4) return launch_waves<PLANES, 4, ARGMAX, DBG, true, false>(a, st, what, max_blocks, used);
-  return launch_waves<PLANES, 4, ARGMAX, DBG, false, false>(a, st, what, max_blocks, used);
+  const bool ldsact = stage;
+  if (a.M == 1) {
+    if (ldsact) return launch_waves<PLANES, 1, ARGMAX, DBG, true, true, false>(a, st, what, max_blocks, used);
+    if (a4) return launch_waves<PLANES, 1, ARGMAX, DBG, true, false, false>(a, st, what, max_blocks, used);
+    return launch_waves<PLANES, 1, ARGMAX, DBG, false, false, false>(a, st, what, max_blocks, used);
+  }
+  if (ldsact) return launch_waves<PLANES, 4, ARGMAX, DBG, true, true, false>(a, st, what, max_blocks, used);
+  if (a4) return launch_waves<PLANES, 4, ARGMAX, DBG, true, false, false>(a, st, what, max_blocks, used);
+  return launch_waves<PLANES, 4, ARGMAX, DBG, false, false, false>(a, st, what, max_blocks, used);
 }
 
 size_t argmax_ws_bytes(int N) {
@@ -370,18 +572,124 @@ int launch_argmax(GemvArgs a, const FinishArgs& f0, bool accept, hipStream_t st,
   return nest::check_launch(what);
 }
 
-int check_common(const char* what, const int8_t* qa, const float* sa, int64_t M, int64_t K,
-                 const uint8_t* base, const float* scales, int64_t N, int64_t group) {
-  if (!qa || !sa || !base || !scales) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+// Activations of a call: int8 codes with their row scales, or fp32 values
+// that the kernel quantizes itself.
+struct Act {
+  const int8_t* qa;
+  const float* sa;
+  const float* x;
+};
+
+int check_common(const char* what, const Act& act, int64_t M, int64_t K, const uint8_t* base,
+                 const float* scales, int64_t N, int64_t group) {
+  if (!base || !scales) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (act.x ? false : (!act.qa || !act.sa)) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (M < 1 || K < 1 || N < 1) return nest::fail(NEST_EINVAL, "%s: empty shape", what);
   if (group != kGroup)
     return nest::fail(NEST_EUNSUPPORTED, "%s: group=%lld (kernels handle 128)", what, (long long)group);
   if (K % kGroup) return nest::fail(NEST_ESHAPE, "%s: K=%lld is not a multiple of 128", what, (long long)K);
   if (K > (1LL << 24) || N > (1LL << 30) || M > (1LL << 20))
     return nest::fail(NEST_EUNSUPPORTED, "%s: shape too large", what);
-  if (!nest::aligned16(qa) || !nest::aligned16(base))
-    return nest::fail(NEST_EALIGN, "%s: qa and planes must be 16-byte aligned", what);
+  if (!nest::aligned16(base) || !nest::aligned16(scales))
+    return nest::fail(NEST_EALIGN, "%s: planes and scales must be 16-byte aligned", what);
+  if (act.x) {
+    if (!nest::aligned16(act.x)) return nest::fail(NEST_EALIGN, "%s: x must be 16-byte aligned", what);
+    if (M > 16 || M * K > kLdsActMaxX)
+      return nest::fail(NEST_EUNSUPPORTED,
+                        "%s: M=%lld K=%lld exceeds the in-kernel quantization limit (M <= 16, "
+                        "M*K <= %d); use nest_act_quant and the int8 entry point",
+                        what, (long long)M, (long long)K, kLdsActMaxX);
+  } else if (!nest::aligned16(act.qa)) {
+    return nest::fail(NEST_EALIGN, "%s: qa must be 16-byte aligned", what);
+  }
   return NEST_OK;
+}
+
+int check_ws(const char* what, const void* ws, size_t ws_bytes, int N) {
+  if (!ws || ws_bytes < argmax_ws_bytes(N))
+    return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, argmax_ws_bytes(N));
+  if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
+  return NEST_OK;
+}
+
+GemvArgs make_args(const Act& act, int64_t M, int64_t K, const uint8_t* base, const uint8_t* refine,
+                   const float* scales, int64_t N, float* y, int32_t* acc_dbg) {
+  GemvArgs a{};
+  a.qa = act.qa; a.sa = act.sa; a.x = act.x;
+  a.M = (int)M; a.K = (int)K; a.base = base; a.refine = refine; a.scales = scales;
+  a.N = (int)N; a.G = (int)(K / kGroup); a.y = y; a.acc_dbg = acc_dbg;
+  return a;
+}
+
+int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uint8_t* base,
+               const float* scales, int64_t N, int64_t group, float* y, int32_t* argmax,
+               int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(what, act, M, K, base, scales, N, group);
+  if (rc) return rc;
+  if (M > 16) return nest::fail(NEST_EUNSUPPORTED, "%s: M=%lld > 16", what, (long long)M);
+  if (!y && !argmax) return nest::fail(NEST_EINVAL, "%s: need y or argmax", what);
+  GemvArgs a = make_args(act, M, K, base, nullptr, scales, N, y, acc_dbg);
+  hipStream_t st = nest::as_stream(stream);
+  if (argmax) {
+    rc = check_ws(what, ws, ws_bytes, a.N);
+    if (rc) return rc;
+    a.partials = static_cast<unsigned long long*>(ws);
+    FinishArgs f{};
+    f.argmax_out = argmax;
+    return acc_dbg ? launch_argmax<1, true>(a, f, false, st, what)
+                   : launch_argmax<1, false>(a, f, false, st, what);
+  }
+  a.nseg = pick_split((a.N + 15) / 16, a.G, max_split(1));
+  return acc_dbg ? launch_gemv<1, false, true>(a, st, what, 1 << 30, nullptr)
+                 : launch_gemv<1, false, false>(a, st, what, 1 << 30, nullptr);
+}
+
+int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const uint8_t* base,
+                const uint8_t* refine, const float* scales, int64_t N, int64_t group, float* y,
+                int32_t* acc_dbg, void* stream) {
+  int rc = check_common(what, act, M, K, base, scales, N, group);
+  if (rc) return rc;
+  if (!refine || !y) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "%s: refine not 16-byte aligned", what);
+  hipStream_t st = nest::as_stream(stream);
+  if (M <= 16) {
+    GemvArgs a = make_args(act, M, K, base, refine, scales, N, y, acc_dbg);
+    a.nseg = pick_split((a.N + 15) / 16, a.G, max_split(2));
+    return acc_dbg ? launch_gemv<2, false, true>(a, st, what, 1 << 30, nullptr)
+                   : launch_gemv<2, false, false>(a, st, what, 1 << 30, nullptr);
+  }
+  // More rows (int8 activations only): the batched kernel, in chunks of up to 144 rows.
+  for (int64_t m0 = 0; m0 < M; m0 += 144) {
+    const int64_t mc = M - m0 < 144 ? M - m0 : 144;
+    rc = nest::launch_verify_batched(act.qa + m0 * K, act.sa + m0, (int)mc, (int)K, base, refine, scales,
+                                     (int)N, y + m0 * N,
+                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, st);
+    if (rc) return rc;
+  }
+  return NEST_OK;
+}
+
+int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t K, const uint8_t* base,
+                const uint8_t* refine, const float* scales, int64_t V, int64_t group,
+                const int32_t* draft, int32_t* target, int32_t* n_emitted, int32_t* emitted, float* y,
+                void* ws, size_t ws_bytes, void* stream) {
+  if (B < 1 || k < 0) return nest::fail(NEST_EINVAL, "%s: B=%lld k=%lld", what, (long long)B, (long long)k);
+  if (B * (k + 1) > 16)
+    return nest::fail(NEST_EUNSUPPORTED, "%s: B*(k+1)=%lld > 16", what, (long long)(B * (k + 1)));
+  int rc = check_common(what, act, B * (k + 1), K, base, scales, V, group);
+  if (rc) return rc;
+  if (!refine || !target || !n_emitted || !emitted || (k > 0 && !draft))
+    return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "%s: refine not 16-byte aligned", what);
+  if (V > 0x7fffffffLL) return nest::fail(NEST_EUNSUPPORTED, "%s: V too large", what);
+  rc = check_ws(what, ws, ws_bytes, (int)V);
+  if (rc) return rc;
+  GemvArgs a = make_args(act, B * (k + 1), K, base, refine, scales, V, y, nullptr);
+  a.partials = static_cast<unsigned long long*>(ws);
+  FinishArgs f{};
+  f.B = (int)B; f.k = (int)k; f.draft = draft; f.target = target; f.n_emitted = n_emitted;
+  f.emitted = emitted;
+  return launch_argmax<2, false>(a, f, true, nest::as_stream(stream), what);
 }
 
 }  // namespace
@@ -403,55 +711,31 @@ extern "C" int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t 
                           const uint8_t* base, const float* scales, int64_t N, int64_t group,
                           float* y, int32_t* argmax, int32_t* acc_dbg, void* ws, size_t ws_bytes,
                           void* stream) {
-  const char* what = "draft_gemv";
-  int rc = check_common(what, qa, sa, M, K, base, scales, N, group);
-  if (rc) return rc;
-  if (M > 16) return nest::fail(NEST_EUNSUPPORTED, "draft_gemv: M=%lld > 16", (long long)M);
-  if (!y && !argmax) return nest::fail(NEST_EINVAL, "draft_gemv: need y or argmax");
-  GemvArgs a{};
-  a.qa = qa; a.sa = sa; a.M = (int)M; a.K = (int)K; a.base = base; a.scales = scales;
-  a.N = (int)N; a.G = (int)(K / kGroup); a.y = y; a.acc_dbg = acc_dbg;
-  hipStream_t st = nest::as_stream(stream);
-  if (argmax) {
-    if (!ws || ws_bytes < argmax_ws_bytes(a.N))
-      return nest::fail(NEST_EWORKSPACE, "draft_gemv: workspace needs %zu bytes", argmax_ws_bytes(a.N));
-    a.partials = static_cast<unsigned long long*>(ws);
-    FinishArgs f{};
-    f.argmax_out = argmax;
-    return acc_dbg ? launch_argmax<1, true>(a, f, false, st, what)
-                   : launch_argmax<1, false>(a, f, false, st, what);
-  }
-  a.nseg = pick_split((a.N + 15) / 16, a.G);
-  return acc_dbg ? launch_gemv<1, false, true>(a, st, what, 1 << 30, nullptr)
-                 : launch_gemv<1, false, false>(a, st, what, 1 << 30, nullptr);
+  return draft_impl("draft_gemv", Act{qa, sa, nullptr}, M, K, base, scales, N, group, y, argmax,
+                    acc_dbg, ws, ws_bytes, stream);
+}
+
+extern "C" int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
+                            const float* scales, int64_t N, int64_t group, float* y,
+                            int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+  if (!x) return nest::fail(NEST_EINVAL, "draft_gemv_x: null pointer");
+  return draft_impl("draft_gemv_x", Act{nullptr, nullptr, x}, M, K, base, scales, N, group, y, argmax,
+                    nullptr, ws, ws_bytes, stream);
 }
 
 extern "C" int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                            const uint8_t* base, const uint8_t* refine, const float* scales,
                            int64_t N, int64_t group, float* y, int32_t* acc_dbg, void* stream) {
-  const char* what = "verify_gemm";
-  int rc = check_common(what, qa, sa, M, K, base, scales, N, group);
-  if (rc) return rc;
-  if (!refine || !y) return nest::fail(NEST_EINVAL, "verify_gemm: null pointer");
-  if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "verify_gemm: refine not 16-byte aligned");
-  hipStream_t st = nest::as_stream(stream);
-  if (M <= 16) {
-    GemvArgs a{};
-    a.qa = qa; a.sa = sa; a.M = (int)M; a.K = (int)K; a.base = base; a.refine = refine;
-    a.scales = scales; a.N = (int)N; a.G = (int)(K / kGroup); a.y = y; a.acc_dbg = acc_dbg;
-    a.nseg = pick_split((a.N + 15) / 16, a.G);
-    return acc_dbg ? launch_gemv<2, false, true>(a, st, what, 1 << 30, nullptr)
-                   : launch_gemv<2, false, false>(a, st, what, 1 << 30, nullptr);
-  }
-  // More rows: the batched kernel, in chunks of up to 144 rows.
-  for (int64_t m0 = 0; m0 < M; m0 += 144) {
-    const int64_t mc = M - m0 < 144 ? M - m0 : 144;
-    rc = nest::launch_verify_batched(qa + m0 * K, sa + m0, (int)mc, (int)K, base, refine, scales,
-                                     (int)N, y + m0 * N,
-                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, st);
-    if (rc) return rc;
-  }
-  return NEST_OK;
+  return verify_impl("verify_gemm", Act{qa, sa, nullptr}, M, K, base, refine, scales, N, group, y,
+                     acc_dbg, stream);
+}
+
+extern "C" int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
+                             const uint8_t* refine, const float* scales, int64_t N, int64_t group,
+                             float* y, void* stream) {
+  if (!x) return nest::fail(NEST_EINVAL, "verify_gemm_x: null pointer");
+  return verify_impl("verify_gemm_x", Act{nullptr, nullptr, x}, M, K, base, refine, scales, N, group,
+                     y, nullptr, stream);
 }
 
 extern "C" int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64_t k, int64_t K,
@@ -459,24 +743,15 @@ extern "C" int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64
                              int64_t V, int64_t group, const int32_t* draft, int32_t* target,
                              int32_t* n_emitted, int32_t* emitted, float* y, void* ws,
                              size_t ws_bytes, void* stream) {
-  const char* what = "verify_accept";
-  if (B < 1 || k < 0) return nest::fail(NEST_EINVAL, "verify_accept: B=%lld k=%lld", (long long)B, (long long)k);
-  if (B * (k + 1) > 16)
-    return nest::fail(NEST_EUNSUPPORTED, "verify_accept: B*(k+1)=%lld > 16", (long long)(B * (k + 1)));
-  int rc = check_common(what, qa, sa, B * (k + 1), K, base, scales, V, group);
-  if (rc) return rc;
-  if (!refine || !target || !n_emitted || !emitted || (k > 0 && !draft))
-    return nest::fail(NEST_EINVAL, "verify_accept: null pointer");
-  if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "verify_accept: refine not 16-byte aligned");
-  if (V > 0x7fffffffLL) return nest::fail(NEST_EUNSUPPORTED, "verify_accept: V too large");
-  if (!ws || ws_bytes < argmax_ws_bytes((int)V))
-    return nest::fail(NEST_EWORKSPACE, "verify_accept: workspace needs %zu bytes", argmax_ws_bytes((int)V));
-  GemvArgs a{};
-  a.qa = qa; a.sa = sa; a.M = (int)(B * (k + 1)); a.K = (int)K; a.base = base; a.refine = refine;
-  a.scales = scales; a.N = (int)V; a.G = (int)(K / kGroup); a.y = y;
-  a.partials = static_cast<unsigned long long*>(ws);
-  FinishArgs f{};
-  f.B = (int)B; f.k = (int)k; f.draft = draft; f.target = target; f.n_emitted = n_emitted;
-  f.emitted = emitted;
-  return launch_argmax<2, false>(a, f, true, nest::as_stream(stream), what);
+  return accept_impl("verify_accept", Act{qa, sa, nullptr}, B, k, K, base, refine, scales, V, group,
+                     draft, target, n_emitted, emitted, y, ws, ws_bytes, stream);
+}
+
+extern "C" int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K, const uint8_t* base,
+                               const uint8_t* refine, const float* scales, int64_t V, int64_t group,
+                               const int32_t* draft, int32_t* target, int32_t* n_emitted,
+                               int32_t* emitted, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x) return nest::fail(NEST_EINVAL, "verify_accept_x: null pointer");
+  return accept_impl("verify_accept_x", Act{nullptr, nullptr, x}, B, k, K, base, refine, scales, V,
+                     group, draft, target, n_emitted, emitted, y, ws, ws_bytes, stream);
 }

@@ -73,13 +73,6 @@ __global__ void __launch_bounds__(256) pack_groups_kernel(const float* __restric
   }
 }
 
-__device__ __forceinline__ int8_t quant_act(float x, float s) {
-  if (s == 0.0f) return 0;
-  float t = rintf(x / s);
-  t = t < -127.0f ? -127.0f : (t > 127.0f ? 127.0f : t);
-  return static_cast<int8_t>(static_cast<int>(t));
-}
-
 // Block-wide maximum for blocks of 1024 threads (16 waves).
 __device__ __forceinline__ float block_max_1024(float m, float* red) {
   m = wave_max(m);
@@ -111,17 +104,17 @@ __global__ void __launch_bounds__(1024) act_quant_kernel(const float* __restrict
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     }
     m = block_max_1024(m, red);
-    const float s = m / 127.0f;
+    const float s = m / 127.0f, r = 1.0f / s;
     if (threadIdx.x == 0) sa[row] = s;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int64_t e = (static_cast<int64_t>(i) * 1024 + threadIdx.x) * 4;
       if (e < K) {
         char4 c;
-        c.x = quant_act(v[i].x, s);
-        c.y = quant_act(v[i].y, s);
-        c.z = quant_act(v[i].z, s);
-        c.w = quant_act(v[i].w, s);
+        c.x = static_cast<signed char>(quant_act(v[i].x, s, r));
+        c.y = static_cast<signed char>(quant_act(v[i].y, s, r));
+        c.z = static_cast<signed char>(quant_act(v[i].z, s, r));
+        c.w = static_cast<signed char>(quant_act(v[i].w, s, r));
         *reinterpret_cast<char4*>(q + e) = c;
       }
     }
@@ -129,10 +122,37 @@ __global__ void __launch_bounds__(1024) act_quant_kernel(const float* __restrict
     float m = 0.0f;
     for (int64_t k = threadIdx.x; k < K; k += 1024) m = fmaxf(m, fabsf(xr[k]));
     m = block_max_1024(m, red);
-    const float s = m / 127.0f;
+    const float s = m / 127.0f, r = 1.0f / s;
     if (threadIdx.x == 0) sa[row] = s;
-    for (int64_t k = threadIdx.x; k < K; k += 1024) q[k] = quant_act(xr[k], s);
+    for (int64_t k = threadIdx.x; k < K; k += 1024) q[k] = static_cast<int8_t>(quant_act(xr[k], s, r));
   }
+}
+
+// Row-major planes and scales -> the tile layout the GEMV/GEMM kernels read
+// (nestspec.h, nest_tile). One thread writes one 16-byte piece of a plane:
+// piece o is (tile t, group g, k-quarter q, row r) with r = o % 16,
+// q = (o / 16) % 4, g = (o / 64) % G, t = o / (64 G), copied from row
+// 16t + r, bytes 64g + 16q .. +15 (zero past the last row). Scales: float f
+// is (tile t, quad u, row r, i) with i = f % 4, r = (f / 4) % 16,
+// u = (f / 64) % Gq, t = f / (64 Gq): scale (16t + r, 4u + i), zero when the
+// row or group is padding.
+__global__ void __launch_bounds__(256) tile_planes_kernel(const uint4* __restrict__ src, int64_t rows,
+                                                          int64_t G, int64_t pieces, uint4* __restrict__ dst) {
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (o >= pieces) return;
+  const int64_t r = o & 15, q = (o >> 4) & 3, tg = o >> 6, g = tg % G, t = tg / G;
+  const int64_t n = 16 * t + r;
+  dst[o] = n < rows ? src[n * (G * 4) + g * 4 + q] : make_uint4(0, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(256) tile_scales_kernel(const float* __restrict__ src, int64_t rows, int64_t G,
+                                                          int64_t count, float* __restrict__ dst) {
+  const int64_t f = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (f >= count) return;
+  const int64_t Gq = (G + 3) / 4;
+  const int64_t i = f & 3, r = (f >> 2) & 15, uq = f >> 6, u = uq % Gq, t = uq / Gq;
+  const int64_t n = 16 * t + r, g = 4 * u + i;
+  dst[f] = (n < rows && g < G) ? src[n * G + g] : 0.0f;
 }
 
 int launch_pack(bool vt, const float* src, int64_t num_groups, int64_t group, int64_t d,
@@ -203,4 +223,44 @@ extern "C" int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, 
   else
     act_quant_kernel<0><<<grid, block, 0, st>>>(x, K, qa, sa);
   return nest::check_launch("nest_act_quant");
+}
+
+extern "C" size_t nest_tile_plane_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 128 || cols % 128 || rows > (1LL << 34) || cols > (1LL << 30)) return 0;
+  return static_cast<size_t>((rows + 15) / 16) * 16 * static_cast<size_t>(cols / 2);
+}
+
+extern "C" size_t nest_tile_scale_count(int64_t rows, int64_t cols, int64_t group) {
+  if (group != 128 || nest_tile_plane_bytes(rows, cols) == 0) return 0;
+  return static_cast<size_t>((rows + 15) / 16) * 64 * static_cast<size_t>((cols / 128 + 3) / 4);
+}
+
+extern "C" int nest_tile(const uint8_t* base, const uint8_t* refine, const float* scales, int64_t rows,
+                         int64_t cols, int64_t group, uint8_t* base_t, uint8_t* refine_t, float* scales_t,
+                         void* stream) {
+  const char* what = "nest_tile";
+  if (!base || !scales || !base_t || !scales_t) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (!refine != !refine_t) return nest::fail(NEST_EINVAL, "%s: refine and refine_t go together", what);
+  if (group != 128) return nest::fail(NEST_EUNSUPPORTED, "%s: group=%lld (the tile layout uses 128)", what,
+                                      (long long)group);
+  if (rows < 1 || cols < 128 || cols % 128)
+    return nest::fail(NEST_ESHAPE, "%s: rows=%lld cols=%lld (cols must be a multiple of 128)", what,
+                      (long long)rows, (long long)cols);
+  if (nest_tile_plane_bytes(rows, cols) == 0) return nest::fail(NEST_EUNSUPPORTED, "%s: shape too large", what);
+  if (!nest::aligned16(base) || !nest::aligned16(base_t) || (refine && (!nest::aligned16(refine) ||
+                                                                        !nest::aligned16(refine_t))))
+    return nest::fail(NEST_EALIGN, "%s: planes must be 16-byte aligned", what);
+  const int64_t G = cols / 128;
+  const int64_t pieces = static_cast<int64_t>(nest_tile_plane_bytes(rows, cols) / 16);
+  const int64_t count = static_cast<int64_t>(nest_tile_scale_count(rows, cols, group));
+  hipStream_t st = nest::as_stream(stream);
+  const dim3 b(256);
+  tile_planes_kernel<<<dim3(static_cast<unsigned>((pieces + 255) / 256)), b, 0, st>>>(
+      reinterpret_cast<const uint4*>(base), rows, G, pieces, reinterpret_cast<uint4*>(base_t));
+  if (refine)
+    tile_planes_kernel<<<dim3(static_cast<unsigned>((pieces + 255) / 256)), b, 0, st>>>(
+        reinterpret_cast<const uint4*>(refine), rows, G, pieces, reinterpret_cast<uint4*>(refine_t));
+  tile_scales_kernel<<<dim3(static_cast<unsigned>((count + 255) / 256)), b, 0, st>>>(scales, rows, G, count,
+                                                                                       scales_t);
+  return nest::check_launch(what);
 }

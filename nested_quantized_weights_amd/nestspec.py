@@ -52,6 +52,13 @@ _SIGS = {
     "verify_accept": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
                                      _p, _p, _p, _sz, _p]),
     "verify_accept_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nest_tile": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "nest_tile_plane_bytes": (_sz, [_i64, _i64]),
+    "nest_tile_scale_count": (_sz, [_i64, _i64, _i64]),
+    "draft_gemv_x": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "verify_gemm_x": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p]),
+    "verify_accept_x": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
+                                       _p, _p, _p, _sz, _p]),
     "kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
     "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _i64, ctypes.c_int, _p,
                                       _p, _sz, _p]),
@@ -134,6 +141,48 @@ def nest_pack(w: torch.Tensor, group: int = 128, out=None):
     return base, refine, scales
 
 
+class Tiled:
+    """A weight matrix in the tile layout (include/nestspec.h): what the
+    draft / verify entry points read. rows and cols are the logical shape."""
+
+    def __init__(self, base, refine, scales, rows, cols):
+        self.base, self.refine, self.scales = base, refine, scales
+        self.rows, self.cols = int(rows), int(cols)
+        self.shape = (self.rows, self.cols)
+
+
+def nest_tile(base, refine, scales, group: int = 128) -> Tiled:
+    """Storage format (nest_pack's planes and scales) -> tile layout."""
+    what = "nest_tile"
+    _dev(base, torch.uint8, what, "base")
+    if refine is not None:
+        _dev(refine, torch.uint8, what, "refine")
+    _dev(scales, torch.float32, what, "scales")
+    rows, half = base.shape
+    cols = 2 * half
+    L = lib()
+    nb = L.nest_tile_plane_bytes(rows, cols)
+    ns = L.nest_tile_scale_count(rows, cols, group)
+    if nb == 0 or ns == 0:
+        raise NestError(f"{what}: unsupported shape rows={rows} cols={cols} group={group} "
+                        "(the tile layout needs group 128 and cols a multiple of 128)")
+    dev = base.device
+    bt = torch.empty(nb, dtype=torch.uint8, device=dev)
+    rt = torch.empty(nb, dtype=torch.uint8, device=dev) if refine is not None else None
+    st = torch.empty(ns, dtype=torch.float32, device=dev)
+    _check(L.nest_tile(_ptr(base), _ptr(refine), _ptr(scales), rows, cols, group, _ptr(bt), _ptr(rt),
+                       _ptr(st), _stream(dev)), what)
+    return Tiled(bt, rt, st, rows, cols)
+
+
+def nest_pack_tiled(w: torch.Tensor, group: int = 128) -> Tiled:
+    """nest_pack then nest_tile: a weight matrix ready for the draft / verify calls."""
+    b, r, s = nest_pack(w, group)
+    t = nest_tile(b, r, s, group)
+    del b, r, s
+    return t
+
+
 def nest_act_quant(x: torch.Tensor, out=None):
     """fp32 [M][K] -> (qa int8 [M][K], sa fp32 [M])."""
     what = "nest_act_quant"
@@ -147,17 +196,25 @@ def nest_act_quant(x: torch.Tensor, out=None):
     return qa, sa
 
 
-def draft_gemv(qa, sa, base, scales, group: int = 128, y=None, want_y: bool = True,
-               argmax: bool = False, argmax_out=None, acc_dbg: bool = False, ws=None):
-    """W4A8 over the base plane. Returns y [M][N] (or None), plus argmax [M]
-    when asked, plus the exact int32 group sums [M][N][G] when acc_dbg."""
+def _tiled(W, what, planes):
+    if not isinstance(W, Tiled):
+        raise NestError(f"{what}: weights must be a Tiled matrix (nest_tile / nest_pack_tiled)")
+    if planes == 2 and W.refine is None:
+        raise NestError(f"{what}: the refinement plane is missing")
+    return W
+
+
+def draft_gemv(qa, sa, W, group: int = 128, y=None, want_y: bool = True, argmax: bool = False,
+               argmax_out=None, acc_dbg: bool = False, ws=None):
+    """W4A8 over the base plane of W (Tiled). Returns y [M][N] (or None),
+    plus argmax [M] when asked, plus the exact int32 group sums [M][N][G]
+    when acc_dbg."""
     what = "draft_gemv"
     _dev(qa, torch.int8, what, "qa")
     _dev(sa, torch.float32, what, "sa")
-    _dev(base, torch.uint8, what, "base")
-    _dev(scales, torch.float32, what, "scales")
+    W = _tiled(W, what, 1)
     M, K = qa.shape
-    N = base.shape[0]
+    N = W.rows
     dev = qa.device
     if y is None and (want_y or not argmax):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -165,13 +222,11 @@ def draft_gemv(qa, sa, base, scales, group: int = 128, y=None, want_y: bool = Tr
     wsp, wsn = None, 0
     if argmax:
         am = argmax_out if argmax_out is not None else torch.empty(M, dtype=torch.int32, device=dev)
-        wsn = lib().draft_gemv_workspace_size(M, N)
         if ws is None:
-            ws = workspace(wsn, dev, "argmax")
-        wsp = _ptr(ws)
-        wsn = ws.numel()
+            ws = workspace(lib().draft_gemv_workspace_size(M, N), dev, "argmax")
+        wsp, wsn = _ptr(ws), ws.numel()
     acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
-    _check(lib().draft_gemv(_ptr(qa), _ptr(sa), M, K, _ptr(base), _ptr(scales), N, group, _ptr(y),
+    _check(lib().draft_gemv(_ptr(qa), _ptr(sa), M, K, _ptr(W.base), _ptr(W.scales), N, group, _ptr(y),
                             _ptr(am), _ptr(acc), wsp, wsn, _stream(dev)), what)
     out = [y]
     if argmax:
@@ -181,53 +236,114 @@ def draft_gemv(qa, sa, base, scales, group: int = 128, y=None, want_y: bool = Tr
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def verify_gemm(qa, sa, base, refine, scales, group: int = 128, y=None, acc_dbg: bool = False):
-    """W8A8 over both planes. Returns y [M][N] (and the int32 group sums when acc_dbg)."""
+def verify_gemm(qa, sa, W, group: int = 128, y=None, acc_dbg: bool = False):
+    """W8A8 over both planes of W (Tiled). Returns y [M][N] (and the int32
+    group sums when acc_dbg)."""
     what = "verify_gemm"
     _dev(qa, torch.int8, what, "qa")
     _dev(sa, torch.float32, what, "sa")
-    _dev(base, torch.uint8, what, "base")
-    _dev(refine, torch.uint8, what, "refine")
-    _dev(scales, torch.float32, what, "scales")
+    W = _tiled(W, what, 2)
     M, K = qa.shape
-    N = base.shape[0]
+    N = W.rows
     dev = qa.device
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
-    _check(lib().verify_gemm(_ptr(qa), _ptr(sa), M, K, _ptr(base), _ptr(refine), _ptr(scales), N,
+    _check(lib().verify_gemm(_ptr(qa), _ptr(sa), M, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), N,
                              group, _ptr(y), _ptr(acc), _stream(dev)), what)
     return (y, acc) if acc_dbg else y
 
 
-def verify_accept(qa, sa, B: int, k: int, base, refine, scales, draft, group: int = 128,
-                  want_y: bool = False, out=None, ws=None):
-    """Verify pass through the nested LM head plus the greedy accept step.
-    Returns a dict of device tensors: target [B][k+1], n_emitted [B],
-    emitted [B][k+1] (and y when want_y)."""
+def _accept_out(B, k, V, dev, want_y):
+    out = {"target": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+           "n_emitted": torch.empty(B, dtype=torch.int32, device=dev),
+           "emitted": torch.empty((B, k + 1), dtype=torch.int32, device=dev)}
+    if want_y:
+        out["y"] = torch.empty((B * (k + 1), V), dtype=torch.float32, device=dev)
+    return out
+
+
+def verify_accept(qa, sa, B: int, k: int, W, draft, group: int = 128, want_y: bool = False, out=None,
+                  ws=None):
+    """Verify pass through the nested LM head W (Tiled) plus the greedy
+    accept step. Returns a dict of device tensors: target [B][k+1],
+    n_emitted [B], emitted [B][k+1] (and y when want_y)."""
     what = "verify_accept"
     _dev(qa, torch.int8, what, "qa")
     _dev(sa, torch.float32, what, "sa")
-    _dev(base, torch.uint8, what, "base")
-    _dev(refine, torch.uint8, what, "refine")
-    _dev(scales, torch.float32, what, "scales")
     _dev(draft, torch.int32, what, "draft")
+    W = _tiled(W, what, 2)
     K = qa.shape[1]
-    V = base.shape[0]
+    V = W.rows
     dev = qa.device
     if out is None:
-        out = {"target": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
-               "n_emitted": torch.empty(B, dtype=torch.int32, device=dev),
-               "emitted": torch.empty((B, k + 1), dtype=torch.int32, device=dev)}
-        if want_y:
-            out["y"] = torch.empty((B * (k + 1), V), dtype=torch.float32, device=dev)
-    wsn = lib().verify_accept_workspace_size(B, k, V)
+        out = _accept_out(B, k, V, dev, want_y)
     if ws is None:
-        ws = workspace(wsn, dev, "argmax")
-    _check(lib().verify_accept(_ptr(qa), _ptr(sa), B, k, K, _ptr(base), _ptr(refine), _ptr(scales),
+        ws = workspace(lib().verify_accept_workspace_size(B, k, V), dev, "argmax")
+    _check(lib().verify_accept(_ptr(qa), _ptr(sa), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales),
                                V, group, _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
                                _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(ws), ws.numel(),
                                _stream(dev)), what)
+    return out
+
+
+def draft_gemv_x(x, W, group: int = 128, y=None, want_y: bool = True, argmax: bool = False,
+                 argmax_out=None, ws=None):
+    """draft_gemv on fp32 activations x [M][K], quantized inside the kernel.
+    Returns y (or None), plus argmax [M] when asked."""
+    what = "draft_gemv_x"
+    _dev(x, torch.float32, what, "x")
+    W = _tiled(W, what, 1)
+    M, K = x.shape
+    N = W.rows
+    dev = x.device
+    if y is None and (want_y or not argmax):
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    am, wsp, wsn = None, None, 0
+    if argmax:
+        am = argmax_out if argmax_out is not None else torch.empty(M, dtype=torch.int32, device=dev)
+        if ws is None:
+            ws = workspace(lib().draft_gemv_workspace_size(M, N), dev, "argmax")
+        wsp, wsn = _ptr(ws), ws.numel()
+    _check(lib().draft_gemv_x(_ptr(x), M, K, _ptr(W.base), _ptr(W.scales), N, group, _ptr(y), _ptr(am),
+                              wsp, wsn, _stream(dev)), what)
+    if argmax:
+        return (y, am) if y is not None else am
+    return y
+
+
+def verify_gemm_x(x, W, group: int = 128, y=None):
+    """verify_gemm on fp32 activations x [M][K] (M <= 16), quantized inside the kernel."""
+    what = "verify_gemm_x"
+    _dev(x, torch.float32, what, "x")
+    W = _tiled(W, what, 2)
+    M, K = x.shape
+    N = W.rows
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().verify_gemm_x(_ptr(x), M, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), N, group,
+                               _ptr(y), _stream(x.device)), what)
+    return y
+
+
+def verify_accept_x(x, B: int, k: int, W, draft, group: int = 128, want_y: bool = False, out=None,
+                    ws=None):
+    """verify_accept on fp32 activations x [B*(k+1)][K], quantized inside the kernel."""
+    what = "verify_accept_x"
+    _dev(x, torch.float32, what, "x")
+    _dev(draft, torch.int32, what, "draft")
+    W = _tiled(W, what, 2)
+    K = x.shape[1]
+    V = W.rows
+    dev = x.device
+    if out is None:
+        out = _accept_out(B, k, V, dev, want_y)
+    if ws is None:
+        ws = workspace(lib().verify_accept_workspace_size(B, k, V), dev, "argmax")
+    _check(lib().verify_accept_x(_ptr(x), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), V, group,
+                                 _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
+                                 _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(ws), ws.numel(),
+                                 _stream(dev)), what)
     return out
 
 

@@ -41,3 +41,22 @@ def decode_v_cache(plane, n_kv_heads, capacity, head_dim, block) -> np.ndarray:
 def block_scales_per_token(scales, capacity, block) -> np.ndarray:
     """[Hkv][capacity/block] -> [Hkv][capacity] (each token's block scale)."""
     return np.repeat(np.asarray(scales, dtype=np.float64), block, axis=1)[:, :capacity]
+
+
+def tile_plane(plane: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Storage plane uint8 [rows][cols/2] -> the tile layout of nestspec.h:
+    rows padded with zeros to T*16, then per (tile t, group g) the kilobyte
+    [k-quarter q][row r][16 bytes] = bytes 64g + 16q .. +15 of row 16t + r."""
+    T, G = -(-rows // 16), cols // 128
+    p = np.zeros((T * 16, cols // 2), np.uint8)
+    p[:rows] = np.asarray(plane, np.uint8).reshape(rows, cols // 2)
+    return p.reshape(T, 16, G, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+def tile_scales(scales: np.ndarray, rows: int, G: int) -> np.ndarray:
+    """Storage scales fp32 [rows][G] -> the tile layout: rows padded to
+    T*16 and groups to Gq*4 with zeros, then [t][quad u][row r][i]."""
+    T, Gq = -(-rows // 16), -(-G // 4)
+    s = np.zeros((T * 16, Gq * 4), np.float32)
+    s[:rows, :G] = np.asarray(scales, np.float32).reshape(rows, G)
+    return s.reshape(T, 16, Gq, 4).transpose(0, 2, 1, 3).reshape(-1)

@@ -64,16 +64,18 @@ def check_linear(ns, oracle, w, x_draft, x_verify, rows):
     assert np.array_equal(host(b[dev(rows)]), ob)
     assert np.array_equal(host(r[dev(rows)]), orf)
     assert np.array_equal(host(s[dev(rows)]).view(np.uint32), osc.view(np.uint32))
+    W = ns.nest_tile(b, r, s)
+    del b, r, s
     for x, verify in ((x_draft, False), (x_verify, True)):
         qa, sa = ns.nest_act_quant(dev(x))
         oqa, osa = oracle.act_quant(x)
         assert np.array_equal(host(qa), oqa)
         if verify:
-            y, acc = ns.verify_gemm(qa, sa, b, r, s, acc_dbg=True)
+            y, acc = ns.verify_gemm(qa, sa, W, acc_dbg=True)
             oy, oacc = oracle.verify_gemm(oqa, osa, ob, orf, osc, want_acc=True)
             step = 1.0 / 16
         else:
-            y, acc = ns.draft_gemv(qa, sa, b, s, acc_dbg=True)
+            y, acc = ns.draft_gemv(qa, sa, W, acc_dbg=True)
             oy, oacc = oracle.draft_gemv(oqa, osa, ob, osc, want_acc=True)
             step = 1.0
         acc_h = host(acc)[:, rows]
@@ -112,18 +114,16 @@ def test_llama_batched_verify_144(ns, oracle, name):
     w = synth.weights(N, K, (key, 0, 0, li))
     x = synth.activations(M, K, (key, 1, 0, li))
     rows = np.sort(synth.rng(key, 7, li).choice(N, size=256, replace=False))
-    wd = dev(w)
-    b, r, s = ns.nest_pack(wd)
-    del wd
+    W = ns.nest_pack_tiled(dev(w))
     ob, orf, osc = oracle.nest_pack(w[rows])
     qa, sa = ns.nest_act_quant(dev(x))
     oqa, osa = oracle.act_quant(x)
     assert np.array_equal(host(qa), oqa)
-    y, acc = ns.verify_gemm(qa, sa, b, r, s, acc_dbg=True)
+    y, acc = ns.verify_gemm(qa, sa, W, acc_dbg=True)
     oy, oacc = oracle.verify_gemm(oqa, osa, ob, orf, osc, want_acc=True)
     assert np.array_equal(host(acc)[:, rows], oacc)
     assert bound_ok(host(y)[:, rows], osa, osc, oacc, 1.0 / 16)
-    y2 = ns.verify_gemm(qa, sa, b, r, s)  # the bench's launch (no debug output)
+    y2 = ns.verify_gemm(qa, sa, W)  # the bench's launch (no debug output)
     assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
 
 
@@ -139,31 +139,33 @@ def lm_head(ns, oracle):
     del wd, w
     assert np.array_equal(host(b), ob) and np.array_equal(host(r), orf)
     assert np.array_equal(host(s).view(np.uint32), osc.view(np.uint32))
+    W = ns.nest_tile(b, r, s)
+    del b, r, s
     pool, targets = [], []
     for p in range(4):  # activation sets whose full-vocabulary targets the oracle computes
         x = synth.activations(k + 1, K, (key, 1, p))
         oqa, osa = oracle.act_quant(x)
         pool.append((oqa, osa))
         targets.append(oracle.verify_gemm(oqa, osa, ob, orf, osc).argmax(axis=1))
-    return {"o": (ob, orf, osc), "g": (b, r, s), "pool": pool, "targets": np.stack(targets),
+    return {"o": (ob, orf, osc), "g": W, "pool": pool, "targets": np.stack(targets),
             "V": V, "k": k, "key": key}
 
 
 def test_lm_head_verify_accept_full(ns, oracle, lm_head):
     ob, orf, osc = lm_head["o"]
-    b, r, s = lm_head["g"]
+    W = lm_head["g"]
     k, V = lm_head["k"], lm_head["V"]
     for p, (oqa, osa) in enumerate(lm_head["pool"][:2]):
         t = lm_head["targets"][p].reshape(1, k + 1)
         draft = synth.plant_drafts(t, 0.95, V, (lm_head["key"], 2, p))
         o = oracle.verify_accept(oqa, osa, 1, k, ob, orf, osc, draft, want_y=True)
-        g = ns.verify_accept(dev(oqa), dev(osa), 1, k, b, r, s, dev(draft.ravel()), want_y=True)
+        g = ns.verify_accept(dev(oqa), dev(osa), 1, k, W, dev(draft.ravel()), want_y=True)
         assert np.array_equal(host(g["target"]), o["target"])
         assert np.array_equal(host(g["n_emitted"]), o["n_emitted"])
         assert np.array_equal(host(g["emitted"]), o["emitted"])
         assert np.array_equal(host(g["y"]).view(np.uint32), o["y"].view(np.uint32))
         # the draft's own choice: base plane only, exact fold, same tie rule
-        yd, am = ns.draft_gemv(dev(oqa[:1]), dev(osa[:1]), b, s, argmax=True)
+        yd, am = ns.draft_gemv(dev(oqa[:1]), dev(osa[:1]), W, argmax=True)
         oyd = oracle.draft_gemv(oqa[:1], osa[:1], ob, osc)
         assert np.array_equal(host(yd).view(np.uint32), oyd.view(np.uint32))
         assert int(host(am)[0]) == oracle.argmax(oyd[0])
@@ -172,7 +174,7 @@ def test_lm_head_verify_accept_full(ns, oracle, lm_head):
 @pytest.mark.parametrize("alpha", [0.58, 0.66, 0.95])
 def test_lm_head_planted_rounds_eq1(ns, oracle, lm_head, alpha):
     ob, orf, osc = lm_head["o"]
-    b, r, s = lm_head["g"]
+    W = lm_head["g"]
     k, V, key = lm_head["k"], lm_head["V"], lm_head["key"]
     R = synth.WORKLOADS["qwen2.5-7b_lm_head"]["rounds"]
     pool, targets = lm_head["pool"], lm_head["targets"]
@@ -187,7 +189,7 @@ def test_lm_head_planted_rounds_eq1(ns, oracle, lm_head, alpha):
            "emitted": torch.empty((1, k + 1), dtype=torch.int32, device="cuda")}
     for i in range(R):
         out["n_emitted"] = n_d[i:i + 1]
-        ns.verify_accept(qa_d[which[i]], sa_d[which[i]], 1, k, b, r, s, d_d[i], out=out)
+        ns.verify_accept(qa_d[which[i]], sa_d[which[i]], 1, k, W, d_d[i], out=out)
     got = host(n_d)
     assert np.array_equal(got, expect)
     assert got.min() >= 1 and got.max() <= k + 1

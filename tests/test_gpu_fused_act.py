@@ -1,0 +1,176 @@
+"""GPU parity of the fp32-activation entry points (draft_gemv_x, verify_gemm_x,
+verify_accept_x) against the oracle.
+
+These kernels quantize x per token inside each block. The oracle quantizes
+the same x with its own act_quant, then runs its own draft / verify /
+accept, so the bar is the one of test_gpu_parity.py:
+  * argmax indices, targets, accepted lengths, emitted tokens: bit-exact;
+  * y on the exact-fold paths (argmax, verify_accept): bit-identical;
+  * y elsewhere: within (G+2) * 2^-24 * sa * sum_g |s_g A_g| of the exact
+    value, with A_g the oracle's exact group sums.
+Edge rows: quantization ties (x/sa at k + 1/2), an all-zero row (sa = 0),
+-0.0, one dominant element. Shapes cover M = 1..16, several tiles plus a
+ragged tail, group counts not divisible by 4, and the M*K limit itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nested_quantized_weights_amd import synth
+
+pytestmark = pytest.mark.gpu
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def ns():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nested_quantized_weights_amd import nestspec
+
+    nestspec.lib()
+    return nestspec
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def tiled(ns, base, refine, scales):
+    """The oracle's storage-format planes, moved to the GPU's tile layout by nest_tile."""
+    return ns.nest_tile(dev(base), None if refine is None else dev(refine), dev(scales))
+
+
+def bound_ok(y, sa, scales, acc, step):
+    s = scales.astype(np.float64) * step
+    terms = s[None] * acc.astype(np.float64)
+    exact = sa.astype(np.float64)[:, None] * terms.sum(axis=2)
+    A = sa.astype(np.float64)[:, None] * np.abs(terms).sum(axis=2)
+    err = np.abs(y.astype(np.float64) - exact)
+    return bool(np.all(err <= (scales.shape[1] + 2) * U32 * A + 1e-45))
+
+
+def edge_rows(x):
+    """Plant quantization ties, an all-zero row, -0.0 and a dominant element."""
+    x[0, :8] = [127.0, -63.5, 0.5, -0.25, 2.5, -1.5, -0.0, 126.5]  # sa = 1: ties to even
+    if x.shape[0] > 1:
+        x[1] = 0.0
+    if x.shape[0] > 2:
+        x[2, 5] = 1e4
+    return x
+
+
+SHAPES = [(16, 128, 1), (33, 256, 5), (100, 384, 9), (4096, 4096, 1), (4097, 3584, 16),
+          (3584, 18944, 1), (777, 1280, 5), (3584, 18944, 5), (300, 8192, 16)]
+
+
+@pytest.mark.parametrize("N,K,M", SHAPES)
+def test_draft_gemv_x(ns, oracle, N, K, M):
+    w = synth.weights(N, K, (300, N, K))
+    x = edge_rows(synth.activations(M, K, (301, N, K, M)))
+    base, _, scales = oracle.nest_pack(w)
+    qa, sa = oracle.act_quant(x)
+    oy, oacc = oracle.draft_gemv(qa, sa, base, scales, want_acc=True)
+    W = tiled(ns, base, None, scales)
+    y = ns.draft_gemv_x(dev(x), W)
+    assert bound_ok(host(y), sa, scales, oacc, 1.0)
+    y2, am = ns.draft_gemv_x(dev(x), W, argmax=True)
+    assert np.array_equal(host(y2).view(np.uint32), oy.view(np.uint32))
+    assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
+
+
+@pytest.mark.parametrize("N,K,M", SHAPES)
+def test_verify_gemm_x(ns, oracle, N, K, M):
+    w = synth.weights(N, K, (302, N, K))
+    x = edge_rows(synth.activations(M, K, (303, N, K, M)))
+    base, refine, scales = oracle.nest_pack(w)
+    qa, sa = oracle.act_quant(x)
+    oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
+    W = tiled(ns, base, refine, scales)
+    y = ns.verify_gemm_x(dev(x), W)
+    assert bound_ok(host(y), sa, scales, oacc, 1.0 / 16)
+    # same codes and the same fold as the int8 entry point on the oracle's codes
+    y8 = ns.verify_gemm(dev(qa), dev(sa), W)
+    assert np.array_equal(host(y).view(np.uint32), host(y8).view(np.uint32))
+
+
+@pytest.mark.parametrize("V,K,B,k,alpha", [(1000, 256, 1, 8, 0.66), (4099, 512, 1, 4, 0.95),
+                                           (2500, 384, 2, 3, 0.58), (640, 128, 1, 0, 0.5),
+                                           (20000, 3584, 1, 15, 0.9)])
+def test_verify_accept_x(ns, oracle, V, K, B, k, alpha):
+    w = synth.weights(V, K, (304, V, K))
+    x = edge_rows(synth.activations(B * (k + 1), K, (305, V, K)))
+    base, refine, scales = oracle.nest_pack(w)
+    qa, sa = oracle.act_quant(x)
+    t_ref = oracle.verify_gemm(qa, sa, base, refine, scales).argmax(axis=1).reshape(B, k + 1)
+    draft = synth.plant_drafts(t_ref, alpha, V, (306, V))
+    o = oracle.verify_accept(qa, sa, B, k, base, refine, scales, draft, want_y=True)
+    xd = dev(x)
+    args = (tiled(ns, base, refine, scales), dev(draft.reshape(-1) if k else np.zeros(0, np.int32)))
+    for rep in range(2):
+        g = ns.verify_accept_x(xd, B, k, *args, want_y=True)
+        assert np.array_equal(host(g["target"]), o["target"])
+        assert np.array_equal(host(g["n_emitted"]), o["n_emitted"])
+        assert np.array_equal(host(g["emitted"]), o["emitted"])
+        assert np.array_equal(host(g["y"]).view(np.uint32), o["y"].view(np.uint32))
+
+
+def test_fused_limit_is_an_error(ns):
+    x = torch.zeros((16, 8320), dtype=torch.float32, device="cuda")  # 16 * 8320 > 131072
+    W = ns.nest_tile(torch.zeros((16, 4160), dtype=torch.uint8, device="cuda"), None,
+                     torch.zeros((16, 65), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ns.NestError, match="in-kernel quantization limit"):
+        ns.draft_gemv_x(x, W)
+    x1 = torch.zeros(132, dtype=torch.float32, device="cuda")[1:129].view(1, 128)  # 4-byte offset
+    W1 = ns.nest_tile(torch.zeros((16, 64), dtype=torch.uint8, device="cuda"), None,
+                      torch.zeros((16, 1), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ns.NestError, match="16-byte aligned"):
+        ns.draft_gemv_x(x1, W1)
+
+
+def near_tie_rows(M, K, seed):
+    """Rows whose x / s_a sit on and within a few ulps of half-integers, for
+    several s_a, so that the rounding decision of every kernel is stressed.
+    Row m has max |x| = 100 + 7m; elements are (n + 1/2) * s_a nudged by
+    -4..4 ulps."""
+    g = synth.rng(seed)
+    x = np.zeros((M, K), np.float32)
+    for m in range(M):
+        mx = np.float32(100.0 + 7.0 * m)
+        s = np.float32(mx / np.float32(127.0))
+        n = g.integers(-127, 127, size=K).astype(np.float32)
+        base = ((n + np.float32(0.5)) * s).astype(np.float32)
+        nudge = g.integers(-4, 5, size=K)
+        v = base.copy()
+        for k in range(1, 5):
+            v = np.where(nudge >= k, np.nextafter(v, np.float32(np.inf)), v)
+            v = np.where(nudge <= -k, np.nextafter(v, np.float32(-np.inf)), v)
+        v = np.clip(v, -mx, mx).astype(np.float32)
+        v[0] = mx  # the row maximum fixes s_a
+        x[m] = v
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(1, 3584), (5, 1024), (16, 4096), (9, 18944)])
+def test_quantization_near_ties(ns, oracle, M, K):
+    x = near_tie_rows(M, K, (307, M, K))
+    qa, sa = oracle.act_quant(x)
+    gq, gs = ns.nest_act_quant(dev(x))
+    assert np.array_equal(host(gq), qa)
+    assert np.array_equal(host(gs).view(np.uint32), sa.view(np.uint32))
+    if M * K <= 131072:
+        N = 64
+        w = synth.weights(N, K, (308, M, K))
+        base, _, scales = oracle.nest_pack(w)
+        oy, oacc = oracle.draft_gemv(qa, sa, base, scales, want_acc=True)
+        W = tiled(ns, base, None, scales)
+        y, am = ns.draft_gemv_x(dev(x), W, argmax=True)
+        assert np.array_equal(host(y).view(np.uint32), oy.view(np.uint32))
+        # and the codes the kernel used are the oracle's: the int8 path agrees bit for bit
+        y8, _ = ns.draft_gemv(dev(qa), dev(sa), W, argmax=True)
+        assert np.array_equal(host(y).view(np.uint32), host(y8).view(np.uint32))

@@ -43,6 +43,11 @@ def host(t):
     return t.cpu().numpy()
 
 
+def tiled(ns, base, refine, scales):
+    """The oracle's storage-format planes, moved to the GPU's tile layout by nest_tile."""
+    return ns.nest_tile(dev(base), None if refine is None else dev(refine), dev(scales))
+
+
 def bound_ok(y, sa, scales, acc, step):
     s = scales.astype(np.float64) * step
     terms = s[None] * acc.astype(np.float64)
@@ -92,6 +97,21 @@ def test_act_quant_bit_exact(ns, oracle, M, K):
     assert np.array_equal(host(sa).view(np.uint32), osa.view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols", [(16, 128), (37, 384), (300, 3584), (5, 1280), (4097, 512)])
+def test_nest_tile_bit_exact(ns, oracle, rows, cols):
+    # nest_tile against the independent numpy permutation of the documented layout
+    from formats import tile_plane, tile_scales
+
+    w = synth.weights(rows, cols, (203, rows, cols))
+    ob, orf, osc = oracle.nest_pack(w)
+    t = tiled(ns, ob, orf, osc)
+    assert np.array_equal(host(t.base), tile_plane(ob, rows, cols))
+    assert np.array_equal(host(t.refine), tile_plane(orf, rows, cols))
+    assert np.array_equal(host(t.scales).view(np.uint32), tile_scales(osc, rows, cols // 128).view(np.uint32))
+    t1 = ns.nest_tile(dev(ob), None, dev(osc))  # base only
+    assert t1.refine is None and np.array_equal(host(t1.base), host(t.base))
+
+
 @pytest.mark.parametrize("Hkv,cap,d,block", [(1, 128, 128, 128), (8, 384, 128, 128), (2, 64, 16, 32)])
 def test_kv_nest_pack_bit_exact(ns, oracle, Hkv, cap, d, block):
     kf, vf = synth.kv(Hkv, cap, d, (202, Hkv, cap))
@@ -123,12 +143,13 @@ GEMV_SHAPES = [(16, 128, 1), (33, 256, 5), (100, 384, 9), (4096, 4096, 1), (4097
 def test_draft_gemv(ns, oracle, N, K, M):
     base, _, scales, qa, sa = _layer(oracle, N, K, M, (N, K, M))
     oy, oacc = oracle.draft_gemv(qa, sa, base, scales, want_acc=True)
-    y, acc = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), acc_dbg=True)
+    W = tiled(ns, base, None, scales)
+    y, acc = ns.draft_gemv(dev(qa), dev(sa), W, acc_dbg=True)
     assert np.array_equal(host(acc), oacc)
     ok, worst = bound_ok(host(y), sa, scales, oacc, 1.0)
     assert ok, worst
     # the argmax path folds exactly: y bit-identical, indices equal
-    y2, am = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), argmax=True)
+    y2, am = ns.draft_gemv(dev(qa), dev(sa), W, argmax=True)
     assert np.array_equal(host(y2).view(np.uint32), oy.view(np.uint32))
     assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
 
@@ -137,17 +158,18 @@ def test_draft_gemv(ns, oracle, N, K, M):
 def test_verify_gemm(ns, oracle, N, K, M):
     base, refine, scales, qa, sa = _layer(oracle, N, K, M, (N, K, M, 1))
     oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
-    y, acc = ns.verify_gemm(dev(qa), dev(sa), dev(base), dev(refine), dev(scales), acc_dbg=True)
+    W = tiled(ns, base, refine, scales)
+    y, acc = ns.verify_gemm(dev(qa), dev(sa), W, acc_dbg=True)
     assert np.array_equal(host(acc), oacc)
     ok, worst = bound_ok(host(y), sa, scales, oacc, 1.0 / 16)
     assert ok, worst
-    y_nodbg = ns.verify_gemm(dev(qa), dev(sa), dev(base), dev(refine), dev(scales))
+    y_nodbg = ns.verify_gemm(dev(qa), dev(sa), W)
     assert np.array_equal(host(y_nodbg).view(np.uint32), host(y).view(np.uint32))
 
 
 def test_gemv_deterministic(ns, oracle):
     base, refine, scales, qa, sa = _layer(oracle, 3584, 18944, 5, (9,))
-    args = [dev(a) for a in (qa, sa, base, refine, scales)]
+    args = [dev(qa), dev(sa), tiled(ns, base, refine, scales)]
     y1 = host(ns.verify_gemm(*args))
     y2 = host(ns.verify_gemm(*args))
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
@@ -157,9 +179,9 @@ def test_draft_reads_only_base_plane(ns, oracle):
     # BitNest Fig. 3: the draft never touches the refinement plane, and with
     # the refinement zeroed verify equals draft bit for bit (exact paths).
     base, refine, scales, qa, sa = _layer(oracle, 300, 512, 1, (10,))
-    yd, _ = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), argmax=True)
-    out = ns.verify_accept(dev(qa), dev(sa), 1, 0, dev(base), dev(np.zeros_like(refine)),
-                           dev(scales), dev(np.zeros(0, np.int32)), want_y=True)
+    yd, _ = ns.draft_gemv(dev(qa), dev(sa), tiled(ns, base, None, scales), argmax=True)
+    out = ns.verify_accept(dev(qa), dev(sa), 1, 0, tiled(ns, base, np.zeros_like(refine), scales),
+                           dev(np.zeros(0, np.int32)), want_y=True)
     assert np.array_equal(host(yd).view(np.uint32), host(out["y"]).view(np.uint32))
 
 
@@ -178,10 +200,10 @@ def test_table1_worked_round_on_gpu(ns, oracle):
     x = np.zeros((k + 1, K), np.float32)
     for i, t in enumerate(ex["target_choices"]):
         x[i, ids[t]] = 1.0
-    b, r, s = ns.nest_pack(dev(w))
+    W = ns.nest_pack_tiled(dev(w))
     qa, sa = ns.nest_act_quant(dev(x))
     draft = dev(np.array([ids[t] for t in ex["draft"]], np.int32))
-    out = ns.verify_accept(qa, sa, 1, k, b, r, s, draft)
+    out = ns.verify_accept(qa, sa, 1, k, W, draft)
     n = int(host(out["n_emitted"])[0])
     assert n == ex["expected_n_emitted"]
     assert [vocab[t] for t in host(out["emitted"])[0][:n]] == ex["expected_emitted"]
@@ -198,8 +220,9 @@ def test_verify_accept(ns, oracle, V, K, B, k, alpha):
     t_ref = oracle.verify_gemm(qa, sa, base, refine, scales).argmax(axis=1).reshape(B, k + 1)
     draft = synth.plant_drafts(t_ref, alpha, V, (222, V))
     o = oracle.verify_accept(qa, sa, B, k, base, refine, scales, draft, want_y=True)
+    W = tiled(ns, base, refine, scales)
     for rep in range(3):  # also checks the workspace is left ready for the next call
-        g = ns.verify_accept(dev(qa), dev(sa), B, k, dev(base), dev(refine), dev(scales),
+        g = ns.verify_accept(dev(qa), dev(sa), B, k, W,
                              dev(draft.reshape(-1) if k else np.zeros(0, np.int32)), want_y=True)
         assert np.array_equal(host(g["target"]), o["target"])
         assert np.array_equal(host(g["n_emitted"]), o["n_emitted"])
@@ -217,7 +240,7 @@ def test_argmax_ties_take_lowest_index(ns, oracle):
     base, refine, scales = oracle.nest_pack(w)
     x = w[77:78].copy()
     qa, sa = oracle.act_quant(x)
-    _, am = ns.draft_gemv(dev(qa), dev(sa), dev(base), dev(scales), argmax=True)
+    _, am = ns.draft_gemv(dev(qa), dev(sa), tiled(ns, base, None, scales), argmax=True)
     oy = oracle.draft_gemv(qa, sa, base, scales)
     assert int(host(am)[0]) == oracle.argmax(oy[0]) == 77
 
@@ -248,8 +271,9 @@ def test_kv_attend(ns, oracle, view, Hq, Hkv, cap, ctx, nq):
 
 
 @pytest.mark.parametrize("view", [0, 1])
-def test_kv_attend_ignores_entries_past_ctx(ns, oracle, view):
-    Hkv, Hq, cap, d, ctx, nq = 2, 8, 512, 128, 300, 5
+@pytest.mark.parametrize("nq", [5, 1])  # 20 query rows per kv head (LDS tables) and 4 (wave kernel)
+def test_kv_attend_ignores_entries_past_ctx(ns, oracle, view, nq):
+    Hkv, Hq, cap, d, ctx = 2, 8, 512, 128, 300
     kf, vf = synth.kv(Hkv, cap, d, (232,))
     q = dev(synth.queries_bf16(nq, Hq, d, (233,)).view(np.int16))
     kv = ns.kv_nest_pack(dev(kf), dev(vf))
@@ -287,11 +311,17 @@ def test_kv_attend_deterministic(ns):
 def test_errors_are_reported(ns):
     qa = torch.zeros((1, 200), dtype=torch.int8, device="cuda")
     sa = torch.zeros(1, dtype=torch.float32, device="cuda")
-    base = torch.zeros((16, 100), dtype=torch.uint8, device="cuda")
-    sc = torch.zeros((16, 1), dtype=torch.float32, device="cuda")
+    W = ns.Tiled(torch.zeros(1600, dtype=torch.uint8, device="cuda"), None,
+                 torch.zeros(64, dtype=torch.float32, device="cuda"), 16, 200)
     with pytest.raises(ns.NestError, match="multiple of 128"):
-        ns.draft_gemv(qa, sa, base, sc)
+        ns.draft_gemv(qa, sa, W)
     qa = torch.zeros((17, 128), dtype=torch.int8, device="cuda")
-    base = torch.zeros((16, 64), dtype=torch.uint8, device="cuda")
+    W = ns.nest_tile(torch.zeros((16, 64), dtype=torch.uint8, device="cuda"), None,
+                     torch.zeros((16, 1), dtype=torch.float32, device="cuda"))
     with pytest.raises(ns.NestError, match="M=17"):
-        ns.draft_gemv(qa, torch.zeros(17, dtype=torch.float32, device="cuda"), base, sc)
+        ns.draft_gemv(qa, torch.zeros(17, dtype=torch.float32, device="cuda"), W)
+    with pytest.raises(ns.NestError, match="Tiled"):
+        ns.draft_gemv(qa[:1], sa, torch.zeros((16, 64), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ns.NestError, match="multiple of 128"):
+        ns.nest_tile(torch.zeros((16, 100), dtype=torch.uint8, device="cuda"), None,
+                     torch.zeros((16, 1), dtype=torch.float32, device="cuda"))

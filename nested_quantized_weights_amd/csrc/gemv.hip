@@ -89,11 +89,35 @@ __device__ __forceinline__ float absmax4(float4 v) {
 // and odd bytes into the two operand slots of their k-quarter. Item idx of
 // a row covers elements [16*idx, 16*idx + 16): group idx >> 3, k-quarter
 // (idx >> 1) & 3, half idx & 1 of that quarter.
+// The fast half of quant_act without its branch: the code of rint(x * r),
+// and `near` set when x * r is within 3e-5 of a half-integer or r is not
+// finite (then the caller recomputes with the exact quotient).
+__device__ __forceinline__ uint32_t code_fast(float x, float r, bool& near) {
+  const float t = x * r;
+  near |= !(fabsf(t - floorf(t) - 0.5f) > 3.0e-5f);
+  const float q = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int>(q)) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t quant4_fast(float4 v, float r, bool& near) {
+  return code_fast(v.x, r, near) | (code_fast(v.y, r, near) << 8) | (code_fast(v.z, r, near) << 16) |
+         (code_fast(v.w, r, near) << 24);
+}
+
 __device__ __forceinline__ void store_item(uint2* lds2, int M, int m, int idx, const float4 (&v)[4],
                                            float s, float r) {
   const int half = idx & 1, q = (idx >> 1) & 3, g = idx >> 3;
-  const uint32_t w0 = quant4(v[0], s, r), w1 = quant4(v[1], s, r), w2 = quant4(v[2], s, r),
-                 w3 = quant4(v[3], s, r);
+  // 16 codes without branches; one exact pass for the rare item that holds
+  // a near-tie (or a zero / tiny row scale)
+  bool near = !(r < INFINITY);
+  uint32_t w0 = quant4_fast(v[0], r, near), w1 = quant4_fast(v[1], r, near), w2 = quant4_fast(v[2], r, near),
+           w3 = quant4_fast(v[3], r, near);
+  if (near) {
+    w0 = quant4(v[0], s, r);
+    w1 = quant4(v[1], s, r);
+    w2 = quant4(v[2], s, r);
+    w3 = quant4(v[3], s, r);
+  }
   lds2[lds_slot(g, 0, q, m, M) * 2 + half] =
       make_uint2(__builtin_amdgcn_perm(w1, w0, 0x06040200u), __builtin_amdgcn_perm(w3, w2, 0x06040200u));
   lds2[lds_slot(g, 1, q, m, M) * 2 + half] =
@@ -101,38 +125,55 @@ __device__ __forceinline__ void store_item(uint2* lds2, int M, int m, int idx, c
 }
 
 // Per-token int8 quantization of fp32 activations x [M][K], written straight
-// into the LDS operand layout. Thread t owns items t, t + NT, ... of the
-// flattened rows. Its first ITEMS items are loaded at once and kept in
-// registers, so a block that fits (M*K <= 16*ITEMS*NT) reads x in one round
-// trip. Row maxima of |x| merge through an LDS max on the float bits (they
-// order like the values for x >= 0); items past the first ITEMS*NT are read
-// once for the maximum and again for coding.
-template <int NT, int ITEMS>
-__device__ __forceinline__ void stage_quantized(const float* __restrict__ x, int M, int K, int G,
-                                                uint4* lds, float* sa_sh, unsigned* amax_sh) {
-  const int t = threadIdx.x;
-  const int ipr = G * 8, total = M * ipr;
+// into the LDS operand layout, in two steps so that the kernel can request
+// its first weights in between: vector loads return in issue order, so x
+// must be requested before the weights for staging to wait on x alone.
+// Thread t owns items t, t + NT, ... of the flattened rows; its first ITEMS
+// items are loaded at once and kept in registers (one round trip when
+// M*K <= 16*ITEMS*NT). Row maxima of |x| merge through an LDS max on the
+// float bits (they order like the values for x >= 0); items past the first
+// ITEMS*NT are read once for the maximum and again for coding.
+template <int ITEMS>
+struct XItems {
   float4 v[ITEMS][4];
   int row[ITEMS];
+};
+
+// Items base + t + j*NT (j < ITEMS) of the flattened rows. Branch-free: a
+// clamped (in-bounds) load for every item, used only if its index is below
+// total, so that a wait for these loads can leave later ones outstanding.
+template <int NT, int ITEMS>
+__device__ __forceinline__ void stage_x_batch(const float* __restrict__ x, int K, int ipr, int total, int base,
+                                              XItems<ITEMS>& it) {
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    const int h = t + j * NT;
-    row[j] = h < total ? h / ipr : -1;
-    if (row[j] >= 0) {
-      const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(row[j]) * K) +
-                          4 * (h - row[j] * ipr);
+    const int h = base + static_cast<int>(threadIdx.x) + j * NT, hc = min(h, total - 1), m = hc / ipr;
+    it.row[j] = h < total ? m : -1;
+    const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(m) * K) + 4 * (hc - m * ipr);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[j][e] = src[e];
-    }
+    for (int e = 0; e < 4; ++e) it.v[j][e] = src[e];
   }
+}
+
+template <int NT, int ITEMS>
+__device__ __forceinline__ void stage_x_issue(const float* __restrict__ x, int M, int K, int G,
+                                              XItems<ITEMS>& it) {
+  stage_x_batch<NT, ITEMS>(x, K, G * 8, M * G * 8, 0, it);
+}
+
+template <int NT, int ITEMS>
+__device__ __forceinline__ void stage_x_finish(const float* __restrict__ x, int M, int K, int G, uint4* lds,
+                                               float* sa_sh, unsigned* amax_sh, const XItems<ITEMS>& it) {
+  const int t = threadIdx.x;
+  const int ipr = G * 8, total = M * ipr;
   if (t < 16) amax_sh[t] = 0u;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j)
-    if (row[j] >= 0)
-      atomicMax(&amax_sh[row[j]],
-                __float_as_uint(fmaxf(fmaxf(absmax4(v[j][0]), absmax4(v[j][1])),
-                                      fmaxf(absmax4(v[j][2]), absmax4(v[j][3])))));
+    if (it.row[j] >= 0)
+      atomicMax(&amax_sh[it.row[j]],
+                __float_as_uint(fmaxf(fmaxf(absmax4(it.v[j][0]), absmax4(it.v[j][1])),
+                                      fmaxf(absmax4(it.v[j][2]), absmax4(it.v[j][3])))));
   for (int h = t + ITEMS * NT; h < total; h += NT) {
     const int m = h / ipr;
     const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(m) * K) + 4 * (h - m * ipr);
@@ -149,13 +190,60 @@ __device__ __forceinline__ void stage_quantized(const float* __restrict__ x, int
   uint2* lds2 = reinterpret_cast<uint2*>(lds);
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j)
-    if (row[j] >= 0)
-      store_item(lds2, M, row[j], t + j * NT - row[j] * ipr, v[j], sa_sh[row[j]], sa_sh[16 + row[j]]);
+    if (it.row[j] >= 0)
+      store_item(lds2, M, it.row[j], t + j * NT - it.row[j] * ipr, it.v[j], sa_sh[it.row[j]],
+                 sa_sh[16 + it.row[j]]);
   for (int h = t + ITEMS * NT; h < total; h += NT) {
     const int m = h / ipr;
     const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(m) * K) + 4 * (h - m * ipr);
     const float4 w[4] = {src[0], src[1], src[2], src[3]};
     store_item(lds2, M, m, h - m * ipr, w, sa_sh[m], sa_sh[16 + m]);
+  }
+  __syncthreads();
+}
+
+// int8 activations qa [M][K] -> the LDS operand layout, in the same two
+// steps: unit u (32 bytes: row u % M, k-quarter (u / M) & 3, group u / 4M)
+// of the first UNITS per thread is loaded before the weights are requested.
+template <int UNITS>
+struct QItems {
+  uint4 a[UNITS], b[UNITS];
+};
+
+template <int NT, int UNITS>
+__device__ __forceinline__ void stage_q_issue(const int8_t* __restrict__ qa, int M, int K, int G,
+                                              QItems<UNITS>& it) {
+  const int total = M * G * 4;
+#pragma unroll
+  for (int j = 0; j < UNITS; ++j) {
+    const int u = min(static_cast<int>(threadIdx.x) + j * NT, total - 1);  // clamped, branch-free
+    const int m = u % M, rest = u / M, q = rest & 3, g = rest >> 2;
+    const int8_t* src = qa + static_cast<size_t>(m) * K + g * kGroup + q * 32;
+    it.a[j] = ld16(src);
+    it.b[j] = ld16(src + 16);
+  }
+}
+
+template <int NT, int UNITS>
+__device__ __forceinline__ void stage_q_finish(const int8_t* __restrict__ qa, int M, int K, int G, uint4* lds,
+                                               const QItems<UNITS>& it) {
+  const int total = M * G * 4;
+  auto put = [&](int u, uint4 a0, uint4 a1) {
+    const int m = u % M, rest = u / M, q = rest & 3, g = rest >> 2;
+    v4i e, o;
+    nest::split_act(a0, a1, e, o);
+    lds[lds_slot(g, 0, q, m, M)] = __builtin_bit_cast(uint4, e);
+    lds[lds_slot(g, 1, q, m, M)] = __builtin_bit_cast(uint4, o);
+  };
+#pragma unroll
+  for (int j = 0; j < UNITS; ++j) {
+    const int u = threadIdx.x + j * NT;
+    if (u < total) put(u, it.a[j], it.b[j]);
+  }
+  for (int u = threadIdx.x + UNITS * NT; u < total; u += NT) {
+    const int m = u % M, rest = u / M, q = rest & 3, g = rest >> 2;
+    const int8_t* src = qa + static_cast<size_t>(m) * K + g * kGroup + q * 32;
+    put(u, ld16(src), ld16(src + 16));
   }
   __syncthreads();
 }
@@ -280,13 +368,13 @@ __device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds
 // Waves per SIMD the register allocation must allow. The streams need
 // enough waves in flight; the targets are the largest that compile without
 // spills for each fold (the debug build is left unconstrained).
-constexpr int occupancy_target(int planes, int mr, bool lds, bool dbg) {
-  return dbg ? 1 : planes == 2 ? 3 : mr == 4 ? 4 : lds ? 5 : 4;
+constexpr int occupancy_target(int planes, int mr, bool dbg) {
+  return dbg ? 1 : planes == 2 ? 3 : 4;
 }
 
 template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
 __global__ void __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(occupancy_target(PLANES, MR, LDSACT, DBG))))
+__attribute__((amdgpu_waves_per_eu(occupancy_target(PLANES, MR, DBG))))
 gemv_kernel(GemvArgs a) {
   static_assert(!XQ || LDSACT, "fp32 activations are quantized into LDS");
   extern __shared__ uint4 lds_act[];
@@ -302,32 +390,27 @@ gemv_kernel(GemvArgs a) {
   const int8_t* pa = LDSACT ? nullptr : a.qa + static_cast<size_t>(mrow) * a.K + kq * 32;
   auto tile_n0 = [&](int it) { return (it * per_iter + wave / S) * 16; };
 
+  // activations first (returns come back in issue order), then the first
+  // weight quad, then the rest of staging
+  constexpr int kXItems = MR == 1 ? (WAVES == 4 ? 1 : 2)
+                                  : (WAVES >= 16 || PLANES == 1) ? (WAVES >= 16 ? 1 : 2) : (WAVES == 8 ? 3 : 4);
+  constexpr int kQUnits = MR == 1 ? 1 : (WAVES >= 16 ? 1 : 3);
+  XItems<XQ ? kXItems : 1> xi;
+  QItems<(LDSACT && !XQ) ? kQUnits : 1> qi;
+  if (XQ) stage_x_issue<WAVES * 64>(a.x, a.M, a.K, G, xi);
+  else if (LDSACT) stage_q_issue<WAVES * 64>(a.qa, a.M, a.K, G, qi);
+
+  // branch-free first quad: tile and group clamped into range; it is only
+  // used when this wave's first tile exists and its segment is not empty
   Quad cur;
   int it = blockIdx.x;
-  if (A4 && it < iters && tile_n0(it) < a.N && g_begin < g_end)
-    load_quad<PLANES>(tile_ptr<PLANES>(a, tile_n0(it) / 16, kq, c), g_begin, cur);
+  if (A4) load_quad<PLANES>(tile_ptr<PLANES>(a, min(tile_n0(it), (T - 1) * 16) / 16, kq, c),
+                            min(g_begin, G - 4), cur);
 
   __shared__ float sa_sh[32];  // [0, 16): s_a per row; [16, 32): 1 / s_a
   __shared__ unsigned amax_sh[16];
-  if (XQ) {
-    // items held in registers: one round trip for the draft's single row
-    // (K <= 16 * NT with 4 waves, 32 * NT with more) and, for several rows,
-    // as many as the fold's own register budget leaves room for
-    stage_quantized<WAVES * 64, (MR == 1 ? (WAVES == 4 ? 1 : 2) : (WAVES >= 16 ? 1 : 4))>(
-        a.x, a.M, a.K, G, lds_act, sa_sh, amax_sh);
-  } else if (LDSACT) {
-    // stage all M x K activation bytes once, split into operand order
-    const int units32 = a.M * G * 4;
-    for (int u = threadIdx.x; u < units32; u += WAVES * 64) {
-      const int m = u % a.M, rest = u / a.M, q = rest & 3, g = rest >> 2;
-      const int8_t* src = a.qa + static_cast<size_t>(m) * a.K + g * kGroup + q * 32;
-      v4i e, o;
-      nest::split_act(ld16(src), ld16(src + 16), e, o);
-      lds_act[lds_slot(g, 0, q, m, a.M)] = __builtin_bit_cast(uint4, e);
-      lds_act[lds_slot(g, 1, q, m, a.M)] = __builtin_bit_cast(uint4, o);
-    }
-    __syncthreads();
-  }
+  if (XQ) stage_x_finish<WAVES * 64>(a.x, a.M, a.K, G, lds_act, sa_sh, amax_sh, xi);
+  else if (LDSACT) stage_q_finish<WAVES * 64>(a.qa, a.M, a.K, G, lds_act, qi);
 
   unsigned long long best[MR];
 #pragma unroll

@@ -31,6 +31,10 @@
  *   runs over groups in ascending order; the argmax takes the lowest index
  *   of the maxima; the V cache is stored dim-major inside each block.
  *
+ * KV append (the write path after verification) is a reading of its own:
+ * new tokens' fp32 values are kept, and each block they touch is quantized
+ * again over its valid tokens with the rest taken as 0.
+ *
  * Parity status: every exported function is pinned by the CPU tests
  * against page values, closed forms, library routines or brute force.
  * The worked round of [Blog] Table 1 and Eq. (1) pin the accept rule.
@@ -306,9 +310,41 @@ static int64_t v_index(int64_t h, int64_t t, int64_t j, int64_t cap, int64_t d,
   return h * cap * d + (b * d + j) * block + (t % block);
 }
 
-/* One group per (head, block), for K and for V. The values are gathered in
- * the plane's element order, quantized by the same rule as the weights,
- * and packed. */
+/* Quantize block b of head h, for K and for V, with tokens at or past
+ * `valid` (counted from the block start) taken as 0. The values are
+ * gathered in the plane's element order, quantized by the same rule as the
+ * weights, and packed. With valid == block this is the plain block group of
+ * kv_nest_pack. A zero never raises max|v|, so the scale of a partial block
+ * covers exactly its valid tokens. */
+static void kv_pack_block(const float* kf, const float* vf, int64_t h, int64_t b,
+                          int64_t valid, int64_t cap, int64_t d, int64_t block,
+                          uint8_t* kb, uint8_t* kr, float* ks, uint8_t* vb,
+                          uint8_t* vr, float* vs) {
+  int64_t nb = cap / block, n = block * d, hb = h * nb + b;
+  float* gk = (float*)malloc((size_t)n * sizeof(float));
+  float* gv = (float*)malloc((size_t)n * sizeof(float));
+  int8_t* q1 = (int8_t*)malloc((size_t)n);
+  int8_t* q2 = (int8_t*)malloc((size_t)n);
+  for (int64_t t = b * block; t < (b + 1) * block; t++)
+    for (int64_t j = 0; j < d; j++) {
+      int live = t - b * block < valid;
+      gk[k_index(h, t, j, cap, d) - h * cap * d - b * n] = live ? kf[(h * cap + t) * d + j] : 0.0f;
+      gv[v_index(h, t, j, cap, d, block) - h * cap * d - b * n] = live ? vf[(h * cap + t) * d + j] : 0.0f;
+    }
+  int64_t off = (h * cap * d + b * n) / 2;
+  oracle_quantize_group(gk, n, q1, q2, &ks[hb]);
+  oracle_pack_nibbles(q1, n, kb + off);
+  oracle_pack_nibbles(q2, n, kr + off);
+  oracle_quantize_group(gv, n, q1, q2, &vs[hb]);
+  oracle_pack_nibbles(q1, n, vb + off);
+  oracle_pack_nibbles(q2, n, vr + off);
+  free(gk);
+  free(gv);
+  free(q1);
+  free(q2);
+}
+
+/* One group per (head, block), for K and for V [BitNest Fig. 4]. */
 int oracle_kv_nest_pack(const float* kf, const float* vf, int64_t Hkv,
                         int64_t cap, int64_t d, int64_t block, uint8_t* kb,
                         uint8_t* kr, float* ks, uint8_t* vb, uint8_t* vr,
@@ -316,31 +352,39 @@ int oracle_kv_nest_pack(const float* kf, const float* vf, int64_t Hkv,
   if (Hkv < 1 || cap < 1 || block < 2 || block % 2 || d < 2 || d % 2 ||
       cap % block)
     return -1;
-  int64_t nb = cap / block, n = block * d;
+  int64_t nb = cap / block;
 #pragma omp parallel for schedule(static)
-  for (int64_t hb = 0; hb < Hkv * nb; hb++) {
-    int64_t h = hb / nb, b = hb % nb;
-    float* gk = (float*)malloc((size_t)n * sizeof(float));
-    float* gv = (float*)malloc((size_t)n * sizeof(float));
-    int8_t* q1 = (int8_t*)malloc((size_t)n);
-    int8_t* q2 = (int8_t*)malloc((size_t)n);
-    for (int64_t t = b * block; t < (b + 1) * block; t++)
+  for (int64_t hb = 0; hb < Hkv * nb; hb++)
+    kv_pack_block(kf, vf, hb / nb, hb % nb, block, cap, d, block, kb, kr, ks, vb, vr, vs);
+  return 0;
+}
+
+/* Append n tokens at positions pos .. pos+n-1 [BitNest Fig. 4: accepted
+ * entries are retained; a rejected suffix is discarded by the caller's
+ * length update and later overwritten by the next append]. kf and vf hold
+ * every token's fp32 value [Hkv][cap][d]; the new values are written there,
+ * then every block the new tokens touch is quantized again over its valid
+ * tokens (those before pos + n), the rest taken as 0. A block that fills
+ * thereby equals the kv_nest_pack block of its values. */
+int oracle_kv_append(float* kf, float* vf, const float* k_new, const float* v_new,
+                     int64_t Hkv, int64_t cap, int64_t d, int64_t block, int64_t pos,
+                     int64_t n, uint8_t* kb, uint8_t* kr, float* ks, uint8_t* vb,
+                     uint8_t* vr, float* vs) {
+  if (Hkv < 1 || block < 2 || block % 2 || d < 2 || d % 2 || cap % block || pos < 0 ||
+      n < 1 || pos + n > cap)
+    return -1;
+  for (int64_t h = 0; h < Hkv; h++)
+    for (int64_t t = pos; t < pos + n; t++)
       for (int64_t j = 0; j < d; j++) {
-        gk[k_index(h, t, j, cap, d) - h * cap * d - b * n] = kf[(h * cap + t) * d + j];
-        gv[v_index(h, t, j, cap, d, block) - h * cap * d - b * n] = vf[(h * cap + t) * d + j];
+        kf[(h * cap + t) * d + j] = k_new[(h * n + t - pos) * d + j];
+        vf[(h * cap + t) * d + j] = v_new[(h * n + t - pos) * d + j];
       }
-    int64_t off = (h * cap * d + b * n) / 2;
-    oracle_quantize_group(gk, n, q1, q2, &ks[hb]);
-    oracle_pack_nibbles(q1, n, kb + off);
-    oracle_pack_nibbles(q2, n, kr + off);
-    oracle_quantize_group(gv, n, q1, q2, &vs[hb]);
-    oracle_pack_nibbles(q1, n, vb + off);
-    oracle_pack_nibbles(q2, n, vr + off);
-    free(gk);
-    free(gv);
-    free(q1);
-    free(q2);
-  }
+  int64_t end = pos + n;
+  for (int64_t h = 0; h < Hkv; h++)
+    for (int64_t b = pos / block; b <= (end - 1) / block; b++) {
+      int64_t valid = end - b * block < block ? end - b * block : block;
+      kv_pack_block(kf, vf, h, b, valid, cap, d, block, kb, kr, ks, vb, vr, vs);
+    }
   return 0;
 }
 

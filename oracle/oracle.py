@@ -48,6 +48,8 @@ def _load():
                                         _p, _p, _p, _p, _p]),
         "oracle_kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64,
                                                _p, _p, _p, _p, _p, _p]),
+        "oracle_kv_append": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                            _p, _p, _p, _p, _p, _p]),
         "oracle_kv_attend": (None, [_p, _i64, _i64, _i64, _i64, _i64, _i64,
                                     _p, _p, _p, _p, _p, _p, _i64, ctypes.c_int, _p]),
     }
@@ -206,6 +208,23 @@ def kv_nest_pack(kf, vf, block=128):
     return {"k_base": kb, "k_refine": kr, "k_scale": ks, "v_base": vb, "v_refine": vr,
             "v_scale": vs, "n_kv_heads": Hkv, "capacity": cap, "head_dim": d,
             "block": block}
+
+
+def kv_append(kv, kf, vf, k_new, v_new, pos):
+    """Append k_new / v_new [Hkv][n][d] at positions pos..pos+n-1 of the cache
+    dict `kv` (planes and scales updated in place). kf / vf [Hkv][cap][d] are
+    the oracle's fp32 values of every token and are updated too."""
+    assert kf.dtype == np.float32 and kf.flags.c_contiguous and vf.dtype == np.float32
+    kn = _c(k_new, np.float32)
+    vn = _c(v_new, np.float32)
+    Hkv, n, d = kn.shape
+    rc = _load().oracle_kv_append(_ptr(kf), _ptr(vf), _ptr(kn), _ptr(vn), Hkv, kv["capacity"], d,
+                                  kv["block"], int(pos), n, _ptr(kv["k_base"]), _ptr(kv["k_refine"]),
+                                  _ptr(kv["k_scale"]), _ptr(kv["v_base"]), _ptr(kv["v_refine"]),
+                                  _ptr(kv["v_scale"]))
+    if rc != 0:
+        raise ValueError("oracle_kv_append: bad sizes")
+    return kv
 
 
 def kv_attend(q_bf16, kv, ctx_len, view):

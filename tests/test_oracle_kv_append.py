@@ -1,0 +1,170 @@
+"""Pins of the oracle's KV append (the cache write path after verification).
+
+BitNest, Figure 4: verification reads the full view of the same nested cache,
+accepted entries are retained and the rejected suffix is discarded. The
+append rule (a reading: each touched block is quantized again over its valid
+tokens, the rest taken as 0) is pinned by:
+  * sealing: a block that fills equals the kv_nest_pack block of its values
+    (kv_nest_pack is pinned on its own in test_oracle_pack / test_oracle_attend);
+  * the closed form of an open block's scale, fl32(max |valid values| / 7);
+  * padding: codes of tokens past the valid end decode to 0 in both planes
+    (decoded with tests/formats.py, written from the documented layouts);
+  * history independence: a rejected suffix overwritten by a later append
+    leaves the same cache as writing the final values directly;
+  * boundaries: appends that cross a block boundary touch both blocks only.
+"""
+import numpy as np
+import pytest
+
+from formats import decode_k_cache, decode_v_cache
+from nested_quantized_weights_amd import synth
+
+BLOCK = 128
+
+
+def empty_cache(oracle, Hkv, cap, d):
+    kf = np.zeros((Hkv, cap, d), np.float32)
+    vf = np.zeros((Hkv, cap, d), np.float32)
+    return kf, vf, oracle.kv_nest_pack(kf, vf, block=BLOCK)
+
+
+def fields(kv):
+    return [kv[n] for n in ("k_base", "k_refine", "k_scale", "v_base", "v_refine", "v_scale")]
+
+
+def append_chunks(oracle, kv, kf, vf, values_k, values_v, start, sizes):
+    pos = start
+    for n in sizes:
+        oracle.kv_append(kv, kf, vf, values_k[:, pos - start:pos - start + n], values_v[:, pos - start:pos - start + n],
+                         pos)
+        pos += n
+    return pos
+
+
+@pytest.mark.parametrize("Hkv,d", [(2, 128), (1, 16)])
+def test_sealed_blocks_equal_pack(oracle, Hkv, d):
+    cap = 4 * BLOCK
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    nk, nv = synth.kv(Hkv, 300, d, (500, Hkv, d))
+    g = synth.rng(501, Hkv, d)
+    sizes = []
+    while sum(sizes) < 300:
+        sizes.append(int(min(g.integers(1, 18), 300 - sum(sizes))))
+    end = append_chunks(oracle, kv, kf, vf, nk, nv, 0, sizes)
+    assert end == 300
+    # reference: kv_nest_pack of the final values, with tokens >= 300 zero
+    fk = np.zeros((Hkv, cap, d), np.float32)
+    fv = np.zeros((Hkv, cap, d), np.float32)
+    fk[:, :300], fv[:, :300] = nk, nv
+    ref = oracle.kv_nest_pack(fk, fv, block=BLOCK)
+    for a, b in zip(fields(kv), fields(ref)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_open_block_scale_closed_form(oracle):
+    Hkv, cap, d = 2, 2 * BLOCK, 128
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    nk, nv = synth.kv(Hkv, 37, d, (502,))
+    nk[1, 5, 7] = 40.0  # dominant element in head 1
+    oracle.kv_append(kv, kf, vf, nk, nv, 0)
+    for h in range(Hkv):
+        want_k = np.float32(np.float32(np.abs(nk[h]).max()) / np.float32(7.0))
+        want_v = np.float32(np.float32(np.abs(nv[h]).max()) / np.float32(7.0))
+        assert kv["k_scale"][h, 0] == want_k and kv["v_scale"][h, 0] == want_v
+        assert kv["k_scale"][h, 1] == 0.0  # an untouched, empty block
+
+
+def test_padding_decodes_to_zero(oracle):
+    Hkv, cap, d = 2, 2 * BLOCK, 128
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    nk, nv = synth.kv(Hkv, 150, d, (503,))
+    oracle.kv_append(kv, kf, vf, nk, nv, 0)
+    for name in ("k_base", "k_refine"):
+        c = decode_k_cache(kv[name], Hkv, cap, d)
+        assert not c[:, 150:].any()
+        assert c[:, :150].any()
+    for name in ("v_base", "v_refine"):
+        c = decode_v_cache(kv[name], Hkv, cap, d, BLOCK)
+        assert not c[:, 150:].any()
+
+
+@pytest.mark.parametrize("pos,k,a", [(0, 8, 3), (120, 8, 2), (125, 8, 8), (127, 4, 0), (300, 16, 15)])
+def test_rejected_suffix_is_overwritten(oracle, pos, k, a):
+    # a round: append k+1 speculative tokens, keep a+1, then the next append
+    # writes over the rejected positions
+    Hkv, cap, d = 2, 4 * BLOCK, 64
+    base_k, base_v = synth.kv(Hkv, pos, d, (504, pos))
+    spec_k, spec_v = synth.kv(Hkv, k + 1, d, (505, pos))
+    spec_k *= 30.0  # rejected values that would dominate a scale
+    next_k, next_v = synth.kv(Hkv, k + 1, d, (506, pos))
+
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    if pos:
+        oracle.kv_append(kv, kf, vf, base_k, base_v, 0)
+    oracle.kv_append(kv, kf, vf, spec_k, spec_v, pos)
+    keep = pos + a + 1  # truncation: a length update only
+    oracle.kv_append(kv, kf, vf, next_k, next_v, keep)
+
+    kf2, vf2, kv2 = empty_cache(oracle, Hkv, cap, d)
+    direct_k = np.concatenate([base_k, spec_k[:, :a + 1], next_k], axis=1)
+    direct_v = np.concatenate([base_v, spec_v[:, :a + 1], next_v], axis=1)
+    oracle.kv_append(kv2, kf2, vf2, direct_k, direct_v, 0)
+    # every block up to the final length matches; positions past it are beyond ctx
+    end = keep + k + 1
+    for name in ("k_scale", "v_scale"):
+        assert np.array_equal(kv[name][:, :(end + BLOCK - 1) // BLOCK],
+                              kv2[name][:, :(end + BLOCK - 1) // BLOCK])
+    kc = decode_k_cache(kv["k_base"], Hkv, cap, d)[:, :end]
+    kc2 = decode_k_cache(kv2["k_base"], Hkv, cap, d)[:, :end]
+    assert np.array_equal(kc, kc2)
+    vc = decode_v_cache(kv["v_refine"], Hkv, cap, d, BLOCK)[:, :end]
+    vc2 = decode_v_cache(kv2["v_refine"], Hkv, cap, d, BLOCK)[:, :end]
+    assert np.array_equal(vc, vc2)
+
+
+def test_append_touches_only_its_blocks(oracle):
+    Hkv, cap, d = 1, 4 * BLOCK, 32
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    nk, nv = synth.kv(Hkv, 3 * BLOCK, d, (507,))
+    oracle.kv_append(kv, kf, vf, nk, nv, 0)
+    before = {n: kv[n].copy() for n in ("k_base", "k_scale", "v_refine", "v_scale")}
+    ak, av = synth.kv(Hkv, 9, d, (508,))
+    oracle.kv_append(kv, kf, vf, ak, av, 2 * BLOCK - 4)  # crosses into block 2
+    assert np.array_equal(kv["k_scale"][:, :1], before["k_scale"][:, :1])
+    assert not np.array_equal(kv["k_scale"][:, 1:3], before["k_scale"][:, 1:3])
+    half = BLOCK * d // 2
+    assert np.array_equal(kv["k_base"][:half], before["k_base"][:half])
+    assert np.array_equal(kv["v_refine"][:half], before["v_refine"][:half])
+    # block 2 now holds only its first 5 tokens: the scale is over those alone
+    want = np.float32(np.float32(np.abs(ak[0, 4:]).max()) / np.float32(7.0))
+    assert kv["k_scale"][0, 2] == want
+
+
+def test_bad_arguments_are_rejected(oracle):
+    Hkv, cap, d = 1, BLOCK, 16
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    nk, nv = synth.kv(Hkv, 4, d, (509,))
+    with pytest.raises(ValueError):
+        oracle.kv_append(kv, kf, vf, nk, nv, cap - 2)  # past the capacity
+
+
+def test_stale_values_past_the_end_are_ignored(oracle):
+    # 9 speculative tokens, 3 kept, then a shorter append of 2: positions
+    # pos+5 .. pos+8 still hold large rejected values, which must not enter
+    # the block's scale or codes
+    Hkv, cap, d, pos = 1, 2 * BLOCK, 64, 40
+    kf, vf, kv = empty_cache(oracle, Hkv, cap, d)
+    bk, bv = synth.kv(Hkv, pos, d, (510,))
+    oracle.kv_append(kv, kf, vf, bk, bv, 0)
+    sk, sv = synth.kv(Hkv, 9, d, (511,))
+    sk *= 50.0
+    sv *= 50.0
+    oracle.kv_append(kv, kf, vf, sk, sv, pos)
+    nk, nv = synth.kv(Hkv, 2, d, (512,))
+    oracle.kv_append(kv, kf, vf, nk, nv, pos + 3)
+    valid_k = np.concatenate([bk[0], sk[0, :3], nk[0]])
+    valid_v = np.concatenate([bv[0], sv[0, :3], nv[0]])
+    assert kv["k_scale"][0, 0] == np.float32(np.float32(np.abs(valid_k).max()) / np.float32(7.0))
+    assert kv["v_scale"][0, 0] == np.float32(np.float32(np.abs(valid_v).max()) / np.float32(7.0))
+    c = decode_k_cache(kv["k_base"], Hkv, cap, d)
+    assert not c[:, pos + 5:].any()

@@ -5,21 +5,25 @@ Workload (one GPU): one Qwen2.5-7B-shaped decoder layer with its nested LM
 head and nested KV cache. A step is one full round at k = 4:
   k draft steps, each:  draft_gemv over the base planes of QKV
                         (4608x3584), O (3584x3584), gate|up (37888x3584) and
-                        down (3584x18944); kv_nest_attend over the base view
+                        down (3584x18944); kv_nest_append of the step's
+                        own token, then kv_nest_attend over the base view
                         (28 q / 4 kv heads, d=128, ~32K context); the nested
                         LM head (152064x3584) with the fused argmax that
                         gives the draft token;
-  one verify pass:      verify_gemm over both planes for the
-                        k+1 rows; kv_nest_attend over the full view with k+1
-                        queries; verify_accept on the LM head (exact fold,
-                        fused argmax, greedy accept of the draft tokens).
+  one verify pass:      verify_gemm over both planes for the k+1 rows;
+                        kv_nest_append of the target's K/V for the k+1
+                        positions (over the draft's); kv_nest_attend over
+                        the full view with k+1 queries; verify_accept on the
+                        LM head (exact fold, fused argmax, greedy accept of
+                        the draft tokens).
 The per-token int8 quantization of each linear's fp32 input runs inside
 the consuming kernel (the *_x entry points); only activations larger than
 that kernel's LDS budget (the k = 8 verify of down) take a separate
 nest_act_quant launch. Every launch goes to the library's HIP kernels on
-torch's current stream,
-and inputs are resident in HBM before the timed region. The same round at
-k = 8 (9 verify rows) is timed as well.
+torch's current stream, and inputs are resident in HBM before the timed
+region. Every round writes the same cache positions (the committed context
+stays at 32768), so each step does the same work. The same round at k = 8
+(9 verify rows) is timed as well.
 
 Output: one JSON line. `value` is the round's algorithmic bytes (the planes
 and scales each kernel must read, plus activations and outputs) divided by
@@ -85,6 +89,16 @@ def attend_bytes(view, Hkv, Hq, nq, ctx, d=128):
             + nq * Hq * d * 2 + nq * Hq * d * 4)
 
 
+def append_bytes(Hkv, pos, n, d=128, blk=128):
+    """New K/V values in, the touched blocks' valid fp32 values read back from
+    the shadow, both planes of every touched K and V block written, scales."""
+    b = n * d * 4 * 2 * Hkv
+    for blkno in range(pos // blk, (pos + n - 1) // blk + 1):
+        valid = min(pos + n, (blkno + 1) * blk) - blkno * blk
+        b += Hkv * 2 * (valid * d * 4 + 2 * blk * d // 2 + 4)
+    return b
+
+
 def accept_bytes(V, K, k, x_fp32=False):
     return gemv_bytes(V, K, k + 1, 2, y=False, x_fp32=x_fp32) + k * 4 + 3 * (k + 1) * 4 + 4
 
@@ -108,11 +122,11 @@ def round_bytes(k):
     for j in range(k):
         for _, N, K in LINEARS:
             tot += linear_bytes(N, K, 1, 1)
-        tot += attend_bytes(0, hkv, hq, 1, CONTEXT + j)
+        tot += append_bytes(hkv, CONTEXT + j, 1) + attend_bytes(0, hkv, hq, 1, CONTEXT + j + 1)
         tot += linear_bytes(V, H, 1, 1, y=False, argmax=True)
     for _, N, K in LINEARS:
         tot += linear_bytes(N, K, k + 1, 2)
-    tot += attend_bytes(1, hkv, hq, k + 1, CONTEXT + k)
+    tot += append_bytes(hkv, CONTEXT, k + 1) + attend_bytes(1, hkv, hq, k + 1, CONTEXT + k + 1)
     tot += accept_bytes(V, H, k, x_fp32=True)
     return tot
 
@@ -140,6 +154,11 @@ def make_inputs(kmax):
     inp["x"]["head"] = synth.activations(kmax, H, (wk, 1, 9))
     inp["xv"]["head"] = synth.activations(kmax + 1, H, (wk, 2, 9))
     inp["kf"], inp["vf"] = synth.kv(QWEN["kv_heads"], CAPACITY, QWEN["head_dim"], (wk, 3))
+    inp["kf"][:, CONTEXT:] = 0.0  # the prefill covers the context; later entries come by append
+    inp["vf"][:, CONTEXT:] = 0.0
+    # new tokens' K/V: one per draft step [kmax][Hkv][1][d], and the verify pass's k+1
+    inp["dk"], inp["dv"] = synth.kv(kmax, QWEN["kv_heads"], QWEN["head_dim"], (wk, 6))
+    inp["vk"], inp["vv"] = synth.kv(QWEN["kv_heads"], kmax + 1, QWEN["head_dim"], (wk, 7))
     inp["qd"] = synth.queries_bf16(kmax, QWEN["q_heads"], QWEN["head_dim"], (wk, 4))
     inp["qv"] = synth.queries_bf16(kmax + 1, QWEN["q_heads"], QWEN["head_dim"], (wk, 5))
     return inp
@@ -184,6 +203,7 @@ class Round:
         ws_att = E(ws_att_n, dtype=torch.uint8, device=cuda)
         keep += [qa, sa, y, att_out, draft_tok, acc_out, ws_arg, ws_att]
         self.kvs = d["kv"].struct()
+        sh = d["shadow"]
         self.draft_tok, self.acc_out = draft_tok, acc_out
 
         calls = []  # (fn, args, tag)
@@ -193,9 +213,14 @@ class Round:
                 calls.append((L.draft_gemv_x, (p(x), 1, K, p(d["base"][n]), p(d["scales"][n]), N,
                                                128, p(y[n]), None, None, 0, st), "draft_" + n))
                 if n == "qkv":
+                    # the step's own token enters the cache, then the draft attends (base view)
+                    dk, dvv = d["dk"][j].unsqueeze(1).contiguous(), d["dv"][j].unsqueeze(1).contiguous()
+                    keep += [dk, dvv]
+                    calls.append((L.kv_nest_append, (ctypes.byref(self.kvs), p(sh[0]), p(sh[1]), p(dk),
+                                                     p(dvv), CONTEXT + j, 1, st), "append_draft"))
                     q = d["qd"][j:j + 1]
                     calls.append((L.kv_nest_attend, (p(q), 1, hq, ctypes.byref(self.kvs),
-                                                     CONTEXT + j, 0, p(att_out), p(ws_att),
+                                                     CONTEXT + j + 1, 0, p(att_out), p(ws_att),
                                                      ws_att_n, st), "attend_draft"))
             xh = d["x"]["head"][j:j + 1]
             calls.append((L.draft_gemv_x, (p(xh), 1, H, p(d["base"]["head"]), p(d["scales"]["head"]),
@@ -213,9 +238,14 @@ class Round:
                                               p(d["refine"][n]), p(d["scales"][n]), N, 128,
                                               p(y[n]), None, st), "verify_" + n))
             if n == "qkv":
+                # the target's K/V for all k+1 positions overwrite the draft's, then attend (full view)
+                vk, vvv = d["vk"][:, :k + 1].contiguous(), d["vv"][:, :k + 1].contiguous()
+                keep += [vk, vvv]
+                calls.append((L.kv_nest_append, (ctypes.byref(self.kvs), p(sh[0]), p(sh[1]), p(vk),
+                                                 p(vvv), CONTEXT, k + 1, st), "append_verify"))
                 q = d["qv"][:k + 1]
                 calls.append((L.kv_nest_attend, (p(q), k + 1, hq, ctypes.byref(self.kvs),
-                                                 CONTEXT + k, 1, p(att_out), p(ws_att), ws_att_n,
+                                                 CONTEXT + k + 1, 1, p(att_out), p(ws_att), ws_att_n,
                                                  st), "attend_verify"))
         xh = d["xv"]["head"][:k + 1]
         calls.append((L.verify_accept_x, (p(xh), 1, k, H, p(d["base"]["head"]),
@@ -253,7 +283,13 @@ def upload(ns, torch, inp):
     for key in ("x", "xv"):
         for name, x in inp[key].items():
             dv[key][name] = torch.from_numpy(x).cuda()
-    dv["kv"] = ns.kv_nest_pack(torch.from_numpy(inp["kf"]).cuda(), torch.from_numpy(inp["vf"]).cuda())
+    kf, vf = torch.from_numpy(inp["kf"]).cuda(), torch.from_numpy(inp["vf"]).cuda()
+    dv["kv"] = ns.kv_nest_pack(kf, vf)
+    dv["shadow"] = ns.kv_shadow(dv["kv"])
+    ns.kv_nest_shadow_fill(dv["kv"], kf, vf, CONTEXT, dv["shadow"])
+    del kf, vf
+    for key in ("dk", "dv", "vk", "vv"):
+        dv[key] = torch.from_numpy(inp[key]).cuda()
     dv["qd"] = torch.from_numpy(inp["qd"].view(np.int16)).cuda()
     dv["qv"] = torch.from_numpy(inp["qv"].view(np.int16)).cuda()
     torch.cuda.synchronize()
@@ -290,6 +326,7 @@ def cpu_baseline(inp, k):
     hq = QWEN["q_heads"]
     packed = {n: O.nest_pack(w) for n, w in inp["w"].items()}
     okv = O.kv_nest_pack(inp["kf"], inp["vf"])
+    kf, vf = inp["kf"].copy(), inp["vf"].copy()
     threads = O.get_threads()
     t0 = time.perf_counter()
     drafts = []
@@ -298,14 +335,16 @@ def cpu_baseline(inp, k):
             qa, sa = O.act_quant(inp["x"][n][j:j + 1])
             O.draft_gemv(qa, sa, packed[n][0], packed[n][2])
             if n == "qkv":
-                O.kv_attend(inp["qd"][j:j + 1], okv, CONTEXT + j, 0)
+                O.kv_append(okv, kf, vf, inp["dk"][j][:, None], inp["dv"][j][:, None], CONTEXT + j)
+                O.kv_attend(inp["qd"][j:j + 1], okv, CONTEXT + j + 1, 0)
         qa, sa = O.act_quant(inp["x"]["head"][j:j + 1])
         drafts.append(O.argmax(O.draft_gemv(qa, sa, packed["head"][0], packed["head"][2])[0]))
     for n, _, _ in LINEARS:
         qa, sa = O.act_quant(inp["xv"][n][:k + 1])
         O.verify_gemm(qa, sa, *packed[n])
         if n == "qkv":
-            O.kv_attend(inp["qv"][:k + 1], okv, CONTEXT + k, 1)
+            O.kv_append(okv, kf, vf, inp["vk"][:, :k + 1], inp["vv"][:, :k + 1], CONTEXT)
+            O.kv_attend(inp["qv"][:k + 1], okv, CONTEXT + k + 1, 1)
     qa, sa = O.act_quant(inp["xv"]["head"][:k + 1])
     O.verify_accept(qa, sa, 1, k, *packed["head"], np.array(drafts, np.int32))
     dt = time.perf_counter() - t0
@@ -409,7 +448,7 @@ def main():
             "workload": "qwen2.5-7b_layer speculative round: k=4 draft steps (1 row) + one 5-row "
                         "verify over the nested QKV 4608x3584, O 3584x3584, gate|up 37888x3584, "
                         "down 3584x18944; nested LM head 152064x3584 with fused argmax and greedy "
-                        "accept; nested KV cache 28 q / 4 kv heads, d=128, context 32768",
+                        "accept; nested KV cache 28 q / 4 kv heads, d=128, context 32768 with per-step append",
             "k": 4, "group": 128, "context": CONTEXT, "round_bytes": round_bytes(4),
         },
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),

@@ -119,7 +119,9 @@
  *  the probability-weighted sum of v, in fp32 [nq][Hq][d].
  *  Truncation after a round is the caller's length update. A round that
  *  verified k drafts and accepted a of them keeps ctx_len - k + a entries.
- *  Entries past ctx_len are never read.
+ *  Entries past ctx_len are never read. New entries go in through
+ *  kv_nest_append, which quantizes each touched block again over its valid
+ *  tokens (the open block's scale covers the tokens written so far).
  */
 #ifndef NESTSPEC_H
 #define NESTSPEC_H
@@ -300,6 +302,41 @@ int kv_nest_pack(const float* k, const float* v, int64_t n_kv_heads,
                  uint8_t* k_base, uint8_t* k_refine, float* k_scale,
                  uint8_t* v_base, uint8_t* v_refine, float* v_scale,
                  void* stream);
+
+/* kv_nest_append -- write n new tokens' fp32 K and V at positions
+ * pos .. pos+n-1 of the nested cache and quantize again every block they
+ * touch (BitNest, Figure 4: accepted entries are retained; the rejected
+ * suffix is discarded by the caller's length update and overwritten by the
+ * next append at the same positions).
+ *   kv        the cache; the planes and scales of the touched blocks are
+ *             written (through the pointers in *kv)
+ *   shadow_k, shadow_v  fp32 [Hkv][2][block][d] each: the values of the two
+ *             most recent blocks, block b in slot b % 2. On entry, slot
+ *             (pos/block) % 2 must hold tokens block*floor(pos/block) .. pos-1
+ *             (kv_nest_shadow_fill sets this up after a prefill); the call
+ *             keeps it so for the next append at any pos' in
+ *             (floor(pos/block)*block, pos+n].
+ *   k_new, v_new  fp32 [Hkv][n][d]
+ *   pos, n    host values: pos >= 0, 1 <= n <= block, pos + n <= capacity
+ * A touched block with L valid tokens (those before pos + n) is quantized as
+ * kv_nest_pack quantizes a block whose tokens from L on are 0: its scale
+ * covers the valid tokens only and the padding codes are 0; a block that
+ * fills equals kv_nest_pack of its tokens. Blocks outside the touched range
+ * are not written.
+ * Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EUNSUPPORTED, NEST_EHIP. */
+int kv_nest_append(const nest_kv* kv, float* shadow_k, float* shadow_v,
+                   const float* k_new, const float* v_new, int64_t pos,
+                   int64_t n, void* stream);
+size_t kv_nest_shadow_floats(int64_t n_kv_heads, int64_t head_dim,
+                             int64_t block); /* per shadow (K or V); 0 if invalid */
+
+/* kv_nest_shadow_fill -- after a prefill: copy the open block's tokens
+ * block*floor(ctx_len/block) .. ctx_len-1 of each head from fp32 K and V
+ * [Hkv][src_len][d] into their shadow slot (nothing when ctx_len is a
+ * multiple of block). Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EHIP. */
+int kv_nest_shadow_fill(const nest_kv* kv, const float* k, const float* v,
+                        int64_t src_len, int64_t ctx_len, float* shadow_k,
+                        float* shadow_v, void* stream);
 
 /* kv_nest_attend -- decode attention over the nested cache (BitNest,
  * Figure 4). view 0 is the base view, which the draft uses and which reads

@@ -155,6 +155,121 @@ __global__ void __launch_bounds__(256) tile_scales_kernel(const float* __restric
   dst[f] = (n < rows && g < G) ? src[n * G + g] : 0.0f;
 }
 
+// Round to the nearest integer of x / s by x * r (r = 1/s), taking the IEEE
+// quotient only when x * r is within 1e-5 of a half-integer. For |x/s| <= 8
+// both x * r and fl(x/s) are within 1e-6 of x/s, so away from a tie all
+// three round alike.
+__device__ __forceinline__ float rint_div(float x, float s, float r) {
+  const float t = x * r;
+  return (fabsf(t - floorf(t) - 0.5f) > 1.0e-5f && r < INFINITY) ? rintf(t) : rintf(x / s);
+}
+
+// nest_codes with the two quotients formed by rint_div; |w/s| <= 7 and
+// |e/s16| <= 8 + 2^-20 hold by construction of s, so the codes are those of
+// nest_codes bit for bit.
+__device__ __forceinline__ void nest_codes_fast(float w, float s, float s16, float rs, float rs16, int& qb,
+                                                int& qr) {
+  if (s == 0.0f) {
+    qb = 0;
+    qr = 0;
+    return;
+  }
+  int b = static_cast<int>(rint_div(w, s, rs));
+  b = b < -7 ? -7 : (b > 7 ? 7 : b);
+  const float e = fmaf(-s, static_cast<float>(b), w);
+  int r = 0;
+  if (s16 != 0.0f) {
+    float u = rint_div(e, s16, rs16);
+    u = u < -8.0f ? -8.0f : (u > 7.0f ? 7.0f : u);
+    r = static_cast<int>(u);
+  }
+  qb = b;
+  qr = r;
+}
+
+// KV append. Block b of kv head h, K or V, is coded by kAppendSplit
+// workgroups, each over its own share of the element pairs. Every one of
+// them takes the block's max |v| itself (tokens before pos from the shadow
+// slot b % 2, later ones straight from the new values, tokens past the valid
+// end as 0), so the workgroups never wait on one another; part 0 also
+// writes the block's new tokens into the shadow and the scale. Codes follow
+// nest_codes: K token-major (element t*d + j), V dim-major (element
+// j*blk + t).
+constexpr int kAppendSplit = 16;
+
+struct AppendArgs {
+  uint8_t *kb, *kr, *vb, *vr;
+  float *ks, *vs;
+  float *shk, *shv;              // [Hkv][2][blk][d]
+  const float *knew, *vnew;      // [Hkv][n][d]
+  int64_t cap, d, blk, pos, n;
+};
+
+__global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
+  __shared__ float red[4];
+  const int64_t b = a.pos / a.blk + blockIdx.x, h = blockIdx.y;
+  const bool is_v = (blockIdx.z & 1) == 1;
+  const int part = static_cast<int>(blockIdx.z >> 1);
+  const int64_t t0 = b * a.blk, nb = a.cap / a.blk;
+  float* sh = (is_v ? a.shv : a.shk) + (h * 2 + (b & 1)) * a.blk * a.d;
+  const float* nw = (is_v ? a.vnew : a.knew) + h * a.n * a.d;  // token pos + i at nw[i*d]
+  const int64_t hi = a.pos + a.n < t0 + a.blk ? a.pos + a.n : t0 + a.blk;
+  const int64_t valid = hi - t0;
+  const int64_t old_end = a.pos > t0 ? a.pos - t0 : 0;  // tokens [0, old_end) come from the shadow
+  auto value = [&](int64_t t, int64_t j) -> float {
+    if (t >= valid) return 0.0f;
+    return t < old_end ? sh[t * a.d + j] : nw[(t0 + t - a.pos) * a.d + j];
+  };
+  // 1. the block's max |v| over its valid tokens
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < valid * a.d; i += 256) m = fmaxf(m, fabsf(value(i / a.d, i % a.d)));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m / 7.0f, s16 = s * 0.0625f, rs = 1.0f / s, rs16 = 1.0f / s16;
+  if (part == 0) {
+    if (threadIdx.x == 0) (is_v ? a.vs : a.ks)[h * nb + b] = s;
+    for (int64_t i = threadIdx.x; i < (valid - old_end) * a.d; i += 256)
+      sh[old_end * a.d + i] = nw[(t0 + old_end - a.pos) * a.d + i];
+  }
+  // 2. this part's element pairs (element e, e+1 share a byte)
+  uint8_t* pb = (is_v ? a.vb : a.kb) + (h * a.cap + t0) * a.d / 2;
+  uint8_t* pr = (is_v ? a.vr : a.kr) + (h * a.cap + t0) * a.d / 2;
+  const int64_t pairs = a.blk * a.d / 2;
+  const int64_t p0 = pairs * part / kAppendSplit, p1 = pairs * (part + 1) / kAppendSplit;
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
+    const int64_t e = 2 * p;
+    float w0, w1;
+    if (is_v) {  // tokens t, t+1 of dim j
+      const int64_t j = e / a.blk, t = e % a.blk;
+      w0 = value(t, j);
+      w1 = value(t + 1, j);
+    } else {     // dims j, j+1 of token t
+      const int64_t t = e / a.d, j = e % a.d;
+      w0 = value(t, j);
+      w1 = value(t, j + 1);
+    }
+    int b0, r0, b1, r1;
+    nest_codes_fast(w0, s, s16, rs, rs16, b0, r0);
+    nest_codes_fast(w1, s, s16, rs, rs16, b1, r1);
+    pb[p] = static_cast<uint8_t>((b0 & 15) | ((b1 & 15) << 4));
+    pr[p] = static_cast<uint8_t>((r0 & 15) | ((r1 & 15) << 4));
+  }
+}
+
+// Copy tokens [blk * floor(ctx/blk), ctx) of every head from full fp32 K/V
+// [Hkv][src_len][d] into their shadow slot.
+__global__ void __launch_bounds__(256) kv_shadow_fill_kernel(const float* __restrict__ src, int64_t src_len,
+                                                             int64_t d, int64_t blk, int64_t ctx,
+                                                             float* __restrict__ sh) {
+  const int64_t h = blockIdx.y, b = ctx / blk, t0 = b * blk, n = (ctx - t0) * d;
+  float* dst = sh + (h * 2 + (b & 1)) * blk * d;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    dst[i] = src[(h * src_len + t0) * d + i];
+}
+
 int launch_pack(bool vt, const float* src, int64_t num_groups, int64_t group, int64_t d,
                 int64_t blk, uint8_t* base, uint8_t* refine, float* scales, hipStream_t st,
                 const char* what) {
@@ -262,5 +377,61 @@ extern "C" int nest_tile(const uint8_t* base, const uint8_t* refine, const float
         reinterpret_cast<const uint4*>(refine), rows, G, pieces, reinterpret_cast<uint4*>(refine_t));
   tile_scales_kernel<<<dim3(static_cast<unsigned>((count + 255) / 256)), b, 0, st>>>(scales, rows, G, count,
                                                                                        scales_t);
+  return nest::check_launch(what);
+}
+
+namespace {
+int check_kv(const char* what, const nest_kv* kv) {
+  if (!kv || !kv->k_base || !kv->k_refine || !kv->v_base || !kv->v_refine || !kv->k_scale || !kv->v_scale)
+    return nest::fail(NEST_EINVAL, "%s: null cache pointer", what);
+  if (kv->n_kv_heads < 1 || kv->head_dim < 2 || kv->head_dim % 2 || kv->block < 2 || kv->block % 2 ||
+      kv->capacity < kv->block || kv->capacity % kv->block)
+    return nest::fail(NEST_ESHAPE, "%s: bad cache shape", what);
+  if (kv->n_kv_heads > 65535) return nest::fail(NEST_EUNSUPPORTED, "%s: too many kv heads", what);
+  return NEST_OK;
+}
+}  // namespace
+
+extern "C" size_t kv_nest_shadow_floats(int64_t n_kv_heads, int64_t head_dim, int64_t block) {
+  if (n_kv_heads < 1 || head_dim < 2 || block < 2) return 0;
+  return static_cast<size_t>(n_kv_heads) * 2 * static_cast<size_t>(block) * static_cast<size_t>(head_dim);
+}
+
+extern "C" int kv_nest_shadow_fill(const nest_kv* kv, const float* k, const float* v, int64_t src_len,
+                                   int64_t ctx_len, float* shadow_k, float* shadow_v, void* stream) {
+  const char* what = "kv_nest_shadow_fill";
+  int rc = check_kv(what, kv);
+  if (rc) return rc;
+  if (!k || !v || !shadow_k || !shadow_v) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (ctx_len < 0 || ctx_len > src_len || ctx_len > kv->capacity)
+    return nest::fail(NEST_EINVAL, "%s: need 0 <= ctx_len <= src_len, capacity", what);
+  if (ctx_len % kv->block == 0) return nest::ok();  // no open block to carry
+  const dim3 grid(static_cast<unsigned>((kv->block * kv->head_dim + 255) / 256),
+                  static_cast<unsigned>(kv->n_kv_heads));
+  hipStream_t st = nest::as_stream(stream);
+  kv_shadow_fill_kernel<<<grid, 256, 0, st>>>(k, src_len, kv->head_dim, kv->block, ctx_len, shadow_k);
+  kv_shadow_fill_kernel<<<grid, 256, 0, st>>>(v, src_len, kv->head_dim, kv->block, ctx_len, shadow_v);
+  return nest::check_launch(what);
+}
+
+extern "C" int kv_nest_append(const nest_kv* kv, float* shadow_k, float* shadow_v, const float* k_new,
+                              const float* v_new, int64_t pos, int64_t n, void* stream) {
+  const char* what = "kv_nest_append";
+  int rc = check_kv(what, kv);
+  if (rc) return rc;
+  if (!shadow_k || !shadow_v || !k_new || !v_new) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (pos < 0 || n < 1 || n > kv->block || pos + n > kv->capacity)
+    return nest::fail(NEST_EINVAL, "%s: need pos >= 0, 1 <= n <= block, pos + n <= capacity (pos=%lld n=%lld)",
+                      what, (long long)pos, (long long)n);
+  AppendArgs a{};
+  a.kb = const_cast<uint8_t*>(kv->k_base); a.kr = const_cast<uint8_t*>(kv->k_refine);
+  a.vb = const_cast<uint8_t*>(kv->v_base); a.vr = const_cast<uint8_t*>(kv->v_refine);
+  a.ks = const_cast<float*>(kv->k_scale); a.vs = const_cast<float*>(kv->v_scale);
+  a.shk = shadow_k; a.shv = shadow_v; a.knew = k_new; a.vnew = v_new;
+  a.cap = kv->capacity; a.d = kv->head_dim; a.blk = kv->block; a.pos = pos; a.n = n;
+  const int64_t touched = (pos + n - 1) / kv->block - pos / kv->block + 1;
+  kv_append_kernel<<<dim3(static_cast<unsigned>(touched), static_cast<unsigned>(kv->n_kv_heads),
+                          2 * kAppendSplit),
+                     256, 0, nest::as_stream(stream)>>>(a);
   return nest::check_launch(what);
 }

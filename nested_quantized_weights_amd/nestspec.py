@@ -60,6 +60,9 @@ _SIGS = {
     "verify_accept_x": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
                                        _p, _p, _p, _sz, _p]),
     "kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
+    "kv_nest_append": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _p, _p, _i64, _i64, _p]),
+    "kv_nest_shadow_floats": (_sz, [_i64, _i64, _i64]),
+    "kv_nest_shadow_fill": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _i64, _i64, _p, _p, _p]),
     "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _i64, ctypes.c_int, _p,
                                       _p, _sz, _p]),
     "kv_nest_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
@@ -379,6 +382,33 @@ def kv_nest_pack(k: torch.Tensor, v: torch.Tensor, block: int = 128) -> NestKV:
                               _ptr(planes[1]), _ptr(ks), _ptr(planes[2]), _ptr(planes[3]),
                               _ptr(vs), _stream(dev)), what)
     return NestKV(planes[0], planes[1], ks, planes[2], planes[3], vs, Hkv, cap, d, block)
+
+
+def kv_shadow(kv: NestKV):
+    """fp32 shadows (K, V) of the two most recent blocks, for kv_nest_append."""
+    n = lib().kv_nest_shadow_floats(kv.n_kv_heads, kv.head_dim, kv.block)
+    dev = kv.k_base.device
+    return (torch.zeros(n, dtype=torch.float32, device=dev), torch.zeros(n, dtype=torch.float32, device=dev))
+
+
+def kv_nest_shadow_fill(kv: NestKV, k: torch.Tensor, v: torch.Tensor, ctx_len: int, shadow):
+    """Carry the open block's fp32 tokens of k, v [Hkv][src_len][d] into the shadows."""
+    what = "kv_nest_shadow_fill"
+    _dev(k, torch.float32, what, "k")
+    _dev(v, torch.float32, what, "v")
+    s = kv.struct()
+    _check(lib().kv_nest_shadow_fill(ctypes.byref(s), _ptr(k), _ptr(v), k.shape[1], int(ctx_len),
+                                     _ptr(shadow[0]), _ptr(shadow[1]), _stream(k.device)), what)
+
+
+def kv_nest_append(kv: NestKV, shadow, k_new: torch.Tensor, v_new: torch.Tensor, pos: int):
+    """Write fp32 k_new, v_new [Hkv][n][d] at positions pos.. and quantize the touched blocks again."""
+    what = "kv_nest_append"
+    _dev(k_new, torch.float32, what, "k_new")
+    _dev(v_new, torch.float32, what, "v_new")
+    s = kv.struct()
+    _check(lib().kv_nest_append(ctypes.byref(s), _ptr(shadow[0]), _ptr(shadow[1]), _ptr(k_new), _ptr(v_new),
+                                int(pos), k_new.shape[1], _stream(k_new.device)), what)
 
 
 def kv_nest_attend(q: torch.Tensor, kv: NestKV, ctx_len: int, view: int, out=None, ws=None):

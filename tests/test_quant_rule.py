@@ -50,3 +50,52 @@ def test_fast_rule_equals_division_rule(oracle, seed):
     qa, sa = oracle.act_quant(x)
     for m in range(x.shape[0]):
         assert np.array_equal(fast_rule(x[m], sa[m]), qa[m]), m
+
+
+def fast_codes(w, s):
+    """The KV-append kernel's weight-code rule: rint(w * (1/s)) and
+    rint(e * (1/s16)), each taking the IEEE quotient within 1e-5 of a
+    half-integer; e = fma(-s, q_b, w) formed exactly in float64 and rounded
+    once to float32, which is what fmaf does."""
+    w = w.astype(np.float32)
+    s = np.float32(s)
+    if s == 0:
+        return np.zeros(w.shape, np.int8), np.zeros(w.shape, np.int8)
+    s16 = np.float32(s * np.float32(0.0625))
+
+    def rint_div(x, d):
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            r = np.float32(1.0) / d
+            t = (x * r).astype(np.float32)
+            far = (np.abs((t - np.floor(t) - np.float32(0.5)).astype(np.float32)) > np.float32(1e-5)) & (r < np.inf)
+            return np.where(far, np.rint(t), np.rint((x / d).astype(np.float32)))
+
+    qb = np.clip(rint_div(w, s), -7, 7)
+    e = (w.astype(np.float64) - np.float64(s) * qb).astype(np.float32)
+    qr = np.clip(rint_div(e, s16), -8, 7) if s16 != 0 else np.zeros_like(qb)
+    return qb.astype(np.int8), qr.astype(np.int8)
+
+
+def tie_groups(seed):
+    g = synth.rng(seed)
+    out = [synth.weights(8, 128, (seed, 0)).reshape(-1, 128)]
+    for mx in (1.0, 0.37, 7.0, 100.0, 3e-30):
+        s = np.float32(np.float32(mx) / np.float32(7.0))
+        for half in (0.5, 0.03125):  # ties of q_b, and of q_r at s/16 steps
+            n = g.integers(-7, 8, size=128).astype(np.float32)
+            v = ((n + np.float32(half) * g.choice([-1, 1], size=128)) * s).astype(np.float32)
+            for _ in range(3):
+                v = np.where(g.random(128) < 0.3, np.nextafter(v, np.float32(np.inf)), v)
+                v = np.where(g.random(128) < 0.3, np.nextafter(v, np.float32(-np.inf)), v)
+            v = np.clip(v, -np.float32(mx), np.float32(mx)).astype(np.float32)
+            v[0] = np.float32(mx)
+            out.append(v[None])
+    return np.concatenate(out).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fast_weight_codes_equal_division_rule(oracle, seed):
+    for grp in tie_groups(410 + seed):
+        qb, qr, s = oracle.quantize_group(grp)
+        fb, fr = fast_codes(grp, s)
+        assert np.array_equal(fb, qb) and np.array_equal(fr, qr)

@@ -443,3 +443,49 @@ void oracle_kv_attend(const uint16_t* q, int64_t nq, int64_t Hq, int64_t Hkv,
     free(score);
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* choosing k: Eq. (1) and Eq. (2) of [Blog], section "Tokens per pass  */
+/* and time per token"                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Eq. (1): E = (1 - a^(k+1)) / (1 - a), with its limit k + 1 at a = 1. */
+double oracle_expected_tokens(double alpha, int64_t k) {
+  if (alpha == 1.0) return (double)(k + 1);
+  return (1.0 - pow(alpha, (double)(k + 1))) / (1.0 - alpha);
+}
+
+/* Eq. (2): t_token = (t_pass + k t_draft) / E. */
+double oracle_token_time(double alpha, int64_t k, double t_draft, double t_pass) {
+  return (t_pass + (double)k * t_draft) / oracle_expected_tokens(alpha, k);
+}
+
+/* The k in [0, kmax] with the least time per token, t_pass[k] being the
+ * pass time with k draft tokens; the smallest k among equal times. */
+int64_t oracle_choose_k(double alpha, double t_draft, const double* t_pass, int64_t kmax) {
+  int64_t best = 0;
+  double tb = oracle_token_time(alpha, 0, t_draft, t_pass[0]);
+  for (int64_t k = 1; k <= kmax; k++) {
+    double t = oracle_token_time(alpha, k, t_draft, t_pass[k]);
+    if (t < tb) {
+      tb = t;
+      best = k;
+    }
+  }
+  return best;
+}
+
+/* Running acceptance rate from rounds: round r kept a_r of k_r drafts.
+ * Under the independence of Eq. (1), a_r counts accepted slots and a round
+ * with a_r < k_r ends in one rejected slot, so the estimate is accepted
+ * slots over judged slots. Older rounds weigh decay^(age); the prior counts
+ * weigh as a round before the first. */
+double oracle_alpha_estimate(const int64_t* accepted, const int64_t* k, int64_t rounds, double decay,
+                             double prior_accepted, double prior_rejected) {
+  double acc = prior_accepted, rej = prior_rejected;
+  for (int64_t r = 0; r < rounds; r++) {
+    acc = decay * acc + (double)accepted[r];
+    rej = decay * rej + (accepted[r] < k[r] ? 1.0 : 0.0);
+  }
+  return acc + rej > 0.0 ? acc / (acc + rej) : 0.0;
+}

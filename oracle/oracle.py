@@ -48,6 +48,11 @@ def _load():
                                         _p, _p, _p, _p, _p]),
         "oracle_kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64,
                                                _p, _p, _p, _p, _p, _p]),
+        "oracle_expected_tokens": (ctypes.c_double, [ctypes.c_double, _i64]),
+        "oracle_token_time": (ctypes.c_double, [ctypes.c_double, _i64, ctypes.c_double, ctypes.c_double]),
+        "oracle_choose_k": (_i64, [ctypes.c_double, ctypes.c_double, _p, _i64]),
+        "oracle_alpha_estimate": (ctypes.c_double, [_p, _p, _i64, ctypes.c_double, ctypes.c_double,
+                                                    ctypes.c_double]),
         "oracle_kv_append": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                             _p, _p, _p, _p, _p, _p]),
         "oracle_kv_attend": (None, [_p, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -237,3 +242,26 @@ def kv_attend(q_bf16, kv, ctx_len, view):
                              _ptr(kv["k_scale"]), _ptr(kv["v_base"]), _ptr(kv["v_refine"]),
                              _ptr(kv["v_scale"]), int(ctx_len), int(view), _ptr(out))
     return out
+
+
+def expected_tokens(alpha, k):
+    """Eq. (1)."""
+    return _load().oracle_expected_tokens(float(alpha), int(k))
+
+
+def token_time(alpha, k, t_draft, t_pass):
+    """Eq. (2)."""
+    return _load().oracle_token_time(float(alpha), int(k), float(t_draft), float(t_pass))
+
+
+def choose_k(alpha, t_draft, t_pass):
+    """argmin_k Eq. (2) over k = 0 .. len(t_pass)-1 (t_pass[k]: pass time with k drafts)."""
+    tp = _c(t_pass, np.float64)
+    return int(_load().oracle_choose_k(float(alpha), float(t_draft), _ptr(tp), tp.size - 1))
+
+
+def alpha_estimate(accepted, k, decay=1.0, prior_accepted=1.0, prior_rejected=1.0):
+    a = _c(accepted, np.int64)
+    kk = _c(np.broadcast_to(np.asarray(k, np.int64), a.shape), np.int64)
+    return _load().oracle_alpha_estimate(_ptr(a), _ptr(kk), a.size, float(decay), float(prior_accepted),
+                                         float(prior_rejected))

@@ -31,6 +31,9 @@ the measured time per round. `rounds_per_s` gives the k=4 and k=8 rates.
 `roofline` covers the dominant kernel, the draft GEMV over the LM head's
 base plane, timed with HIP events around every launch in the timed region.
 `cpu_baseline` times the oracle on one full k=4 round on the host's cores.
+`k_choice_eq2` gives, for each planted acceptance rate, the draft length
+that Eq. (1)/(2) choose from the measured time of one draft step and of
+the verify pass at each k (nest_choose_k), with the derived tokens/s.
 """
 from __future__ import annotations
 
@@ -207,6 +210,7 @@ class Round:
         self.draft_tok, self.acc_out = draft_tok, acc_out
 
         calls = []  # (fn, args, tag)
+        phases = []  # draft step j, or "verify", per call
         for j in range(k):
             for n, N, K in LINEARS:
                 x = d["x"][n][j:j + 1]
@@ -226,6 +230,7 @@ class Round:
             calls.append((L.draft_gemv_x, (p(xh), 1, H, p(d["base"]["head"]), p(d["scales"]["head"]),
                                            V, 128, None, P(draft_tok.data_ptr() + 4 * j),
                                            p(ws_arg), ws_arg.numel(), st), "DOMINANT"))
+            phases += [j] * (len(calls) - len(phases))
         for n, N, K in LINEARS:
             xv = d["xv"][n][:k + 1]
             if fused(k + 1, K):
@@ -253,7 +258,9 @@ class Round:
                                           p(draft_tok), p(acc_out["target"]), p(acc_out["n"]),
                                           p(acc_out["emitted"]), None, p(ws_arg), ws_arg.numel(),
                                           st), "verify_accept"))
+        phases += ["verify"] * (len(calls) - len(phases))
         self.calls = calls
+        self.phases = phases
         self.keep = keep
 
     def run(self, events=None):
@@ -271,6 +278,45 @@ class Round:
                 rc = fn(*args)
             if rc:
                 raise RuntimeError(f"{tag}: status {rc}: {self.ns.lib().nest_last_error().decode()}")
+
+
+    def run_phase(self, phase):
+        """Issue only the calls of one draft step (j) or of the verify pass."""
+        for (fn, args, tag), ph in zip(self.calls, self.phases):
+            if ph == phase:
+                rc = fn(*args)
+                if rc:
+                    raise RuntimeError(f"{tag}: status {rc}: {self.ns.lib().nest_last_error().decode()}")
+
+
+def time_phase(torch, rnd, phase, reps=30, warmup=3):
+    """Average time in seconds of one draft step or one verify pass (HIP events)."""
+    for _ in range(warmup):
+        rnd.run_phase(phase)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        rnd.run_phase(phase)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e-3
+
+
+def k_choice(ns, torch, dv, kmax=8):
+    """Eq. (1)/(2) with measured times: t_draft = one draft step, t_pass[k] =
+    the verify pass over k+1 positions; the k with the least time per token
+    for each planted acceptance rate, next to the fixed k = 4."""
+    t_draft = time_phase(torch, Round(ns, torch, dv, 4), 0)
+    t_pass = [time_phase(torch, Round(ns, torch, dv, k), "verify") for k in range(kmax + 1)]
+    out = {"t_draft_us": round(t_draft * 1e6, 2), "t_pass_us": [round(t * 1e6, 2) for t in t_pass],
+           "chosen": {}}
+    for name, a in ALPHAS.items():
+        k, t = ns.choose_k(a, t_draft, t_pass)
+        t4 = ns.token_time(a, 4, t_draft, t_pass[4])
+        out["chosen"][name] = {"alpha": a, "k": k, "tokens_per_s": round(1.0 / t, 1),
+                               "fixed_k4_tokens_per_s": round(1.0 / t4, 1)}
+    return out
 
 
 def upload(ns, torch, inp):
@@ -425,6 +471,8 @@ def main():
         res[k] = {"ms": ms, "wall": wall, "dom": dom, "n": int(rnd.acc_out["n"].item())}
         print(f"# bench: k={k} {ms:.4f} ms/round", file=sys.stderr, flush=True)
 
+    print("# bench: timing draft steps and verify passes for the choice of k", file=sys.stderr, flush=True)
+    kc = k_choice(ns, torch, dv)
     ms4 = res[4]["ms"]
     value = round_bytes(4) / (ms4 * 1e-3) / 1e9
     dom_ms = float(np.mean(res[4]["dom"]))
@@ -457,6 +505,7 @@ def main():
         "tokens_per_s_eq1_derived": {name: {"k4": round(1e3 / ms4 * eq1(a, 4), 1),
                                             "k8": round(1e3 / res[8]["ms"] * eq1(a, 8), 1)}
                                      for name, a in ALPHAS.items()},
+        "k_choice_eq2": kc,
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,

@@ -359,6 +359,42 @@ size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
                                      int64_t n_kv_heads, int64_t head_dim,
                                      int64_t ctx_len);
 
+/* ---------------------------------------------------------------------------
+ * Choosing the draft length ("How Speculative Decoding Speeds Up Inference",
+ * section "Tokens per pass and time per token"). Host functions: every
+ * pointer is a host pointer and nothing runs on the GPU.
+ * --------------------------------------------------------------------------- */
+
+/* Eq. (1): expected tokens per pass, E = (1 - alpha^(k+1)) / (1 - alpha)
+ * (k + 1 at alpha = 1). NaN for alpha outside [0, 1] or k < 0. */
+double nest_expected_tokens(double alpha, int64_t k);
+
+/* Eq. (2): time per token, (t_pass + k * t_draft) / E(alpha, k). */
+double nest_token_time(double alpha, int64_t k, double t_draft, double t_pass);
+
+/* The k in [0, kmax] with the least time per token, given the time of one
+ * draft step t_draft and the pass times t_pass[0..kmax] (host array; the
+ * pass with k draft tokens checks k+1 positions). Ties keep the smaller k.
+ * Writes that time to *t_token when non-NULL. Returns -1 on bad arguments
+ * (message in nest_last_error). */
+int64_t nest_choose_k(double alpha, double t_draft, const double* t_pass,
+                      int64_t kmax, double* t_token);
+
+/* Running acceptance rate. A round that kept a of k drafts judged a + 1
+ * slots when a < k (a accepted, one rejected) and k slots when a == k (all
+ * accepted), independently per slot as Eq. (1) assumes; the estimate is
+ * accepted over judged slots, older rounds weighted by decay^(age) and the
+ * prior counting as judged slots before the first round. */
+typedef struct nest_alpha {
+  double accepted; /* weighted accepted slots */
+  double rejected; /* weighted rejected slots */
+  double decay;    /* weight kept per round, in [0, 1] */
+} nest_alpha;
+void nest_alpha_init(nest_alpha* st, double decay, double prior_accepted,
+                     double prior_rejected);
+void nest_alpha_update(nest_alpha* st, int64_t accepted, int64_t k);
+double nest_alpha_value(const nest_alpha* st);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,12 @@ class _KV(ctypes.Structure):
                 ("capacity", _i64), ("block", _i64)]
 
 
+class _Alpha(ctypes.Structure):
+    _fields_ = [("accepted", ctypes.c_double), ("rejected", ctypes.c_double), ("decay", ctypes.c_double)]
+
+
+_d = ctypes.c_double
+
 _SIGS = {
     "nest_last_error": (ctypes.c_char_p, []),
     "nest_pack": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
@@ -60,6 +66,12 @@ _SIGS = {
     "verify_accept_x": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
                                        _p, _p, _p, _sz, _p]),
     "kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
+    "nest_expected_tokens": (_d, [_d, _i64]),
+    "nest_token_time": (_d, [_d, _i64, _d, _d]),
+    "nest_choose_k": (_i64, [_d, _d, _p, _i64, ctypes.POINTER(_d)]),
+    "nest_alpha_init": (None, [ctypes.POINTER(_Alpha), _d, _d, _d]),
+    "nest_alpha_update": (None, [ctypes.POINTER(_Alpha), _i64, _i64]),
+    "nest_alpha_value": (_d, [ctypes.POINTER(_Alpha)]),
     "kv_nest_append": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _p, _p, _i64, _i64, _p]),
     "kv_nest_shadow_floats": (_sz, [_i64, _i64, _i64]),
     "kv_nest_shadow_fill": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _i64, _i64, _p, _p, _p]),
@@ -430,3 +442,47 @@ def kv_nest_attend(q: torch.Tensor, kv: NestKV, ctx_len: int, view: int, out=Non
     _check(lib().kv_nest_attend(_ptr(q), nq, Hq, ctypes.byref(s), int(ctx_len), int(view),
                                 _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), what)
     return out
+
+
+# ---------------------------------------------------------------------------
+# choosing k (host functions of the library; no GPU involved)
+# ---------------------------------------------------------------------------
+
+def expected_tokens(alpha: float, k: int) -> float:
+    """Eq. (1)."""
+    return lib().nest_expected_tokens(float(alpha), int(k))
+
+
+def token_time(alpha: float, k: int, t_draft: float, t_pass: float) -> float:
+    """Eq. (2)."""
+    return lib().nest_token_time(float(alpha), int(k), float(t_draft), float(t_pass))
+
+
+def choose_k(alpha: float, t_draft: float, t_pass):
+    """(k, time per token) minimising Eq. (2) over k = 0 .. len(t_pass)-1."""
+    import numpy as np
+
+    tp = np.ascontiguousarray(t_pass, dtype=np.float64)
+    out = ctypes.c_double(0.0)
+    k = lib().nest_choose_k(float(alpha), float(t_draft), tp.ctypes.data_as(ctypes.c_void_p), tp.size - 1,
+                            ctypes.byref(out))
+    if k < 0:
+        _check(1, "nest_choose_k")
+    return int(k), out.value
+
+
+class AlphaEstimate:
+    """Running acceptance rate (nest_alpha)."""
+
+    def __init__(self, decay: float = 1.0, prior_accepted: float = 1.0, prior_rejected: float = 1.0):
+        self._st = _Alpha()
+        lib().nest_alpha_init(ctypes.byref(self._st), float(decay), float(prior_accepted),
+                              float(prior_rejected))
+
+    def update(self, accepted: int, k: int) -> float:
+        lib().nest_alpha_update(ctypes.byref(self._st), int(accepted), int(k))
+        return self.value
+
+    @property
+    def value(self) -> float:
+        return lib().nest_alpha_value(ctypes.byref(self._st))

@@ -148,3 +148,30 @@ def plant_drafts(target: np.ndarray, alpha: float, vocab: int, key) -> np.ndarra
     prev = target[:, :k]
     other = np.where(other >= prev, other + 1, other)
     return np.where(u < alpha, prev, other).astype(np.int32)
+
+
+def logits(rows: int, vocab: int, key, spread: float = 2.0, peaks: int = 3, lift: float = 9.0) -> np.ndarray:
+    """float32 [rows][vocab] language-model-like logits.
+
+    N(0, spread) for every id, plus ``lift`` * U(0.6, 1) on ``peaks`` random ids
+    of each row, so that a few ids hold most of the probability and a long
+    tail holds the rest, as in a trained model's next-token scores.
+    """
+    g = rng(*key)
+    y = g.standard_normal((rows, vocab), dtype=np.float32) * np.float32(spread)
+    for r in range(rows):
+        ids = g.choice(vocab, size=min(peaks, vocab), replace=False)
+        y[r, ids] += (lift * g.uniform(0.6, 1.0, size=ids.size)).astype(np.float32)
+    return y
+
+
+def logits_near(y: np.ndarray, key, noise: float = 0.3) -> np.ndarray:
+    """``y`` plus N(0, noise) per element: a second model's logits that
+    mostly agree with ``y`` (a draft close to its target)."""
+    g = rng(*key)
+    return (y + g.standard_normal(y.shape, dtype=np.float32) * np.float32(noise)).astype(np.float32)
+
+
+def uniforms(shape, key) -> np.ndarray:
+    """float32 uniforms in [0, 1): the random numbers a sampling step consumes."""
+    return rng(*key).random(shape, dtype=np.float32)

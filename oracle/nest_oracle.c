@@ -35,6 +35,11 @@
  * new tokens' fp32 values are kept, and each block they touch is quantized
  * again over its valid tokens with the rest taken as 0.
  *
+ * Speculative sampling is read as the published method the [Blog] page
+ * names: keep d with probability min(1, p(d)/q(d)), else draw from
+ * max(0, p - q) normalized; the bonus from the last position; scores are
+ * softmax(logits / T); draws by inverse CDF with uniforms passed in.
+ *
  * Parity status: every exported function is pinned by the CPU tests
  * against page values, closed forms, library routines or brute force.
  * The worked round of [Blog] Table 1 and Eq. (1) pin the accept rule.
@@ -488,4 +493,163 @@ double oracle_alpha_estimate(const int64_t* accepted, const int64_t* k, int64_t 
     rej = decay * rej + (accepted[r] < k[r] ? 1.0 : 0.0);
   }
   return acc + rej > 0.0 ? acc / (acc + rej) : 0.0;
+}
+
+/* ------------------------------------------------------------------ */
+/* speculative sampling ([Blog], section "The same output as the large  */
+/* model alone": each draft token is kept with a probability set by the */
+/* scores of both models, and after a rejection a replacement is drawn  */
+/* from a corrected distribution; the method of Leviathan et al. and    */
+/* Chen et al. that the page names, whose result follows the target's   */
+/* distribution exactly). Readings: the scores are softmax(logits / T); */
+/* a slot keeps d when u * q(d) < p(d) (probability min(1, p/q)); the   */
+/* corrected distribution is max(0, p - q) normalized; a token is drawn */
+/* by inverse CDF: the smallest t whose running weight exceeds u times  */
+/* the total. Computed in fp64.                                         */
+/* ------------------------------------------------------------------ */
+
+/* softmax(y / T) in fp64. */
+static void softmax_row(const float* y, int64_t V, double T, double* p) {
+  double m = -INFINITY, s = 0.0;
+  for (int64_t t = 0; t < V; t++)
+    if ((double)y[t] > m) m = (double)y[t];
+  for (int64_t t = 0; t < V; t++) {
+    p[t] = exp(((double)y[t] - m) / T);
+    s += p[t];
+  }
+  for (int64_t t = 0; t < V; t++) p[t] /= s;
+}
+
+/* Inverse CDF over the weights w: the smallest t whose running sum exceeds
+ * u * sum(w); if rounding leaves none, the last t of positive weight.
+ * Reports t's interval [lo, hi) of the running sum and the target u*sum. */
+static int64_t inverse_cdf(const double* w, int64_t V, double u, double* lo, double* hi,
+                           double* target) {
+  double total = 0.0;
+  for (int64_t t = 0; t < V; t++) total += w[t];
+  const double tg = u * total;
+  double run = 0.0;
+  int64_t pick = -1;
+  double at = 0.0;
+  for (int64_t t = 0; t < V; t++) {
+    if (run + w[t] > tg) {
+      pick = t;
+      at = run;
+      break;
+    }
+    run += w[t];
+  }
+  if (pick < 0) {
+    double r2 = 0.0;
+    for (int64_t t = 0; t < V; t++) {
+      if (w[t] > 0.0) {
+        pick = t;
+        at = r2;
+      }
+      r2 += w[t];
+    }
+  }
+  *lo = at;
+  *hi = at + w[pick];
+  *target = tg;
+  return pick;
+}
+
+/* Distance of the target from the nearer edge of [lo, hi). */
+static double edge_margin(double lo, double hi, double tg) { return fmin(tg - lo, hi - tg); }
+
+/* One token from softmax(y / T) with the uniform u; *margin (if non-NULL)
+ * is the target's distance, in probability, from the drawn token's
+ * interval edges. */
+int64_t oracle_sample(const float* y, int64_t V, float T, float u, double* margin) {
+  double* p = (double*)malloc((size_t)V * sizeof(double));
+  softmax_row(y, V, (double)T, p);
+  double lo, hi, tg;
+  int64_t t = inverse_cdf(p, V, (double)u, &lo, &hi, &tg);
+  if (margin) *margin = edge_margin(lo, hi, tg);
+  free(p);
+  return t;
+}
+
+/* The interval [lo, hi) of token t in the running sum of softmax(y / T),
+ * and the target u * 1: lets a caller check a token drawn elsewhere. */
+void oracle_sample_interval(const float* y, int64_t V, float T, float u, int64_t t, double* lo,
+                            double* hi, double* target) {
+  double* p = (double*)malloc((size_t)V * sizeof(double));
+  softmax_row(y, V, (double)T, p);
+  double run = 0.0, tot = 0.0;
+  for (int64_t j = 0; j < V; j++) tot += p[j];
+  for (int64_t j = 0; j < t; j++) run += p[j];
+  *lo = run;
+  *hi = run + p[t];
+  *target = (double)u * tot;
+  free(p);
+}
+
+/* The distribution a round draws its last token from, after a kept
+ * drafts: max(0, p_{a+1} - q_{a+1}) when slot a+1 was rejected (a < k),
+ * else p_{k+1} (the bonus). w gets V weights in probability units. */
+static void final_weights(const float* yt, const float* yd, int64_t k, int64_t V, double T, int64_t a,
+                          double* w, double* q) {
+  softmax_row(yt + a * V, V, T, w);
+  if (a < k) {
+    softmax_row(yd + a * V, V, T, q);
+    for (int64_t t = 0; t < V; t++) w[t] = fmax(0.0, w[t] - q[t]);
+  }
+}
+
+/* One speculative-sampling round of one sequence. yt [k+1][V]: the
+ * target's logits at the k+1 positions (row i-1 scores draft slot i, row k
+ * the bonus); yd [k][V]: the draft's logits draft token i was drawn from
+ * (row i-1). Slot i keeps d_i when u_acc[i-1] * q_i(d_i) < p_i(d_i). At
+ * the first slot that fails, the last token is drawn with u_fin from
+ * max(0, p_i - q_i); when every slot is kept, from p_{k+1}. emitted gets
+ * the kept drafts and the drawn token (-1 after); returns their number
+ * a + 1. ratio (k values, if non-NULL) gets p_i(d_i) / q_i(d_i) of every
+ * slot; *margin the drawn token's edge margin in probability units. */
+int64_t oracle_verify_sample(const float* yt, const float* yd, int64_t k, int64_t V, float T,
+                             const int32_t* draft, const float* u_acc, float u_fin,
+                             int32_t* emitted, double* ratio, double* margin) {
+  double* p = (double*)malloc((size_t)V * sizeof(double));
+  double* q = (double*)malloc((size_t)V * sizeof(double));
+  int64_t a = 0;
+  int rejected = 0;
+  for (int64_t i = 1; i <= k; i++) {
+    softmax_row(yt + (i - 1) * V, V, (double)T, p);
+    softmax_row(yd + (i - 1) * V, V, (double)T, q);
+    const int32_t d = draft[i - 1];
+    const double r = p[d] / q[d];
+    if (ratio) ratio[i - 1] = r;
+    if (!rejected) {
+      if ((double)u_acc[i - 1] * q[d] < p[d])
+        emitted[a++] = d;
+      else
+        rejected = 1;
+    }
+  }
+  final_weights(yt, yd, k, V, (double)T, a, p, q);
+  double lo, hi, tg;
+  emitted[a] = (int32_t)inverse_cdf(p, V, (double)u_fin, &lo, &hi, &tg);
+  if (margin) *margin = edge_margin(lo, hi, tg);
+  for (int64_t j = a + 1; j <= k; j++) emitted[j] = -1;
+  free(p);
+  free(q);
+  return a + 1;
+}
+
+/* The interval [lo, hi) of token t in the running sum of the last token's
+ * distribution after a kept drafts, and the target u_fin * total. */
+void oracle_final_interval(const float* yt, const float* yd, int64_t k, int64_t V, float T, int64_t a,
+                           float u_fin, int64_t t, double* lo, double* hi, double* target) {
+  double* w = (double*)malloc((size_t)V * sizeof(double));
+  double* q = (double*)malloc((size_t)V * sizeof(double));
+  final_weights(yt, yd, k, V, (double)T, a, w, q);
+  double run = 0.0, tot = 0.0;
+  for (int64_t j = 0; j < V; j++) tot += w[j];
+  for (int64_t j = 0; j < t; j++) run += w[j];
+  *lo = run;
+  *hi = run + w[t];
+  *target = (double)u_fin * tot;
+  free(w);
+  free(q);
 }

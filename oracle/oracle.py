@@ -53,6 +53,12 @@ def _load():
         "oracle_choose_k": (_i64, [ctypes.c_double, ctypes.c_double, _p, _i64]),
         "oracle_alpha_estimate": (ctypes.c_double, [_p, _p, _i64, ctypes.c_double, ctypes.c_double,
                                                     ctypes.c_double]),
+        "oracle_sample": (_i64, [_p, _i64, ctypes.c_float, ctypes.c_float, _p]),
+        "oracle_sample_interval": (None, [_p, _i64, ctypes.c_float, ctypes.c_float, _i64, _p, _p, _p]),
+        "oracle_verify_sample": (_i64, [_p, _p, _i64, _i64, ctypes.c_float, _p, _p, ctypes.c_float,
+                                        _p, _p, _p]),
+        "oracle_final_interval": (None, [_p, _p, _i64, _i64, ctypes.c_float, _i64, ctypes.c_float, _i64,
+                                         _p, _p, _p]),
         "oracle_kv_append": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                             _p, _p, _p, _p, _p, _p]),
         "oracle_kv_attend": (None, [_p, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -265,3 +271,54 @@ def alpha_estimate(accepted, k, decay=1.0, prior_accepted=1.0, prior_rejected=1.
     kk = _c(np.broadcast_to(np.asarray(k, np.int64), a.shape), np.int64)
     return _load().oracle_alpha_estimate(_ptr(a), _ptr(kk), a.size, float(decay), float(prior_accepted),
                                          float(prior_rejected))
+
+
+def sample(y, T, u):
+    """One token from softmax(y / T) by inverse CDF with the uniform u:
+    (token, margin of the decision from its interval's edges)."""
+    yy = _c(y, np.float32).ravel()
+    m = np.zeros(1, np.float64)
+    t = _load().oracle_sample(_ptr(yy), yy.size, float(T), float(u), _ptr(m))
+    return int(t), float(m[0])
+
+
+def sample_interval(y, T, u, t):
+    """Interval [lo, hi) of token t in the running sum of softmax(y / T), and the target u."""
+    yy = _c(y, np.float32).ravel()
+    out = np.zeros(3, np.float64)
+    _load().oracle_sample_interval(_ptr(yy), yy.size, float(T), float(u), int(t), _ptr(out[0:]),
+                                   _ptr(out[1:]), _ptr(out[2:]))
+    return float(out[0]), float(out[1]), float(out[2])
+
+
+def _spec_inputs(yt, yd, draft, u_acc):
+    yt = _c(yt, np.float32)
+    k1, V = yt.shape
+    k = k1 - 1
+    yd = _c(yd if k else np.zeros((1, V), np.float32), np.float32)
+    dr = _c(np.asarray(draft, np.int32).reshape(-1) if k else np.zeros(1, np.int32), np.int32)
+    ua = _c(np.asarray(u_acc, np.float32).reshape(-1) if k else np.zeros(1, np.float32), np.float32)
+    return yt, yd, dr, ua, k, V
+
+
+def verify_sample(yt, yd, draft, T, u_acc, u_fin):
+    """Speculative-sampling round of one sequence: (n_emitted, emitted [k+1],
+    ratio p/q of every slot [k], edge margin of the drawn token)."""
+    yt, yd, dr, ua, k, V = _spec_inputs(yt, yd, draft, u_acc)
+    em = np.empty(k + 1, np.int32)
+    ratio = np.zeros(max(k, 1), np.float64)
+    m = np.zeros(1, np.float64)
+    n = _load().oracle_verify_sample(_ptr(yt), _ptr(yd), k, V, float(T), _ptr(dr), _ptr(ua), float(u_fin),
+                                     _ptr(em), _ptr(ratio), _ptr(m))
+    return int(n), em, ratio[:k], float(m[0])
+
+
+def final_interval(yt, yd, T, a, u_fin, t):
+    """Interval [lo, hi) of token t in the last token's distribution after a
+    kept drafts (residual of slot a+1, or the bonus when a = k), and the target."""
+    yt, yd, _, _, k, V = _spec_inputs(yt, yd, np.zeros(max(yt.shape[0] - 1, 1), np.int32),
+                                      np.zeros(max(yt.shape[0] - 1, 1), np.float32))
+    out = np.zeros(3, np.float64)
+    _load().oracle_final_interval(_ptr(yt), _ptr(yd), k, V, float(T), int(a), float(u_fin), int(t),
+                                  _ptr(out[0:]), _ptr(out[1:]), _ptr(out[2:]))
+    return float(out[0]), float(out[1]), float(out[2])

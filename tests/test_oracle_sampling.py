@@ -1,0 +1,206 @@
+"""Pins of the oracle's speculative sampling ("How Speculative Decoding Speeds
+Up Inference", section "The same output as the large model alone": a draft
+token is kept with a probability set by both models' scores and a rejection
+is followed by a draw from a corrected distribution, so that the output
+follows the target model's distribution exactly).
+
+What fixes the expected values:
+  * the inverse-CDF draw against numpy's searchsorted over scipy's softmax,
+    and its frequencies on a uniform grid against the probabilities;
+  * the page's claim itself: over the draft token and the uniforms, the
+    first emitted token is distributed as the target's softmax (checked by
+    quadrature over the uniforms, and by Monte Carlo over whole rounds,
+    where the second token follows the second position's softmax);
+  * special cases: identical models keep every draft and draw the bonus from
+    the last row; a draft with no target mass is always rejected and the
+    replacement follows the target; the near-zero-temperature limit is the
+    greedy rule of the page's Table 1.
+A plausible mistake (the ratio upside down, the replacement drawn from p
+instead of max(0, p - q), the bonus from the wrong row, an unnormalized
+residual, a wrong temperature) fails one of these.
+"""
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from nested_quantized_weights_amd import synth
+
+
+def cdf_pick(p, u):
+    return int(np.searchsorted(np.cumsum(p), u * p.sum(), side="right"))
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
+def test_sample_is_inverse_cdf(oracle, T):
+    y = synth.logits(8, 1000, (700, int(T * 10)))
+    u = synth.uniforms((8, 25), (701, int(T * 10)))
+    checked = 0
+    for r in range(8):
+        p = softmax(y[r].astype(np.float64) / T)
+        for uu in u[r]:
+            t, margin = oracle.sample(y[r], T, uu)
+            lo, hi, tg = oracle.sample_interval(y[r], T, uu, t)
+            assert lo <= tg < hi and abs(min(tg - lo, hi - tg) - margin) < 1e-15
+            if margin > 1e-12:
+                assert t == cdf_pick(p, float(uu))
+                checked += 1
+    assert checked > 150
+
+
+def test_sample_frequencies_on_a_grid(oracle):
+    y = np.array([0.3, -1.0, 2.5, 0.0, 1.2, -3.0], np.float32)
+    for T in (1.0, 0.7):
+        p = softmax(y.astype(np.float64) / T)
+        N = 4000
+        counts = np.zeros(y.size)
+        for i in range(N):
+            counts[oracle.sample(y, T, (i + 0.5) / N)[0]] += 1
+        assert np.all(np.abs(counts / N - p) <= 1.0 / N + 1e-12)
+
+
+def test_sample_temperature_scales_logits(oracle):
+    y = synth.logits(1, 500, (702,))[0]
+    for u in synth.uniforms(40, (703,)):
+        assert oracle.sample(y, 0.5, u)[0] == oracle.sample(2.0 * y, 1.0, u)[0]
+        assert oracle.sample(y, 0.25, u)[0] == oracle.sample(4.0 * y, 1.0, u)[0]
+
+
+def test_sample_greedy_limit(oracle):
+    y = synth.logits(6, 300, (704,))
+    for r in range(6):
+        for u in (0.0, 0.3, 0.999):
+            assert oracle.sample(y[r], 1e-4, u)[0] == int(np.argmax(y[r]))
+
+
+def first_token_law(oracle, yt, yd, T, N):
+    """Probability of each first emitted token, over d ~ q_1 and uniforms on
+    midpoint grids (the accept test depends on u_acc, the draw on u_fin)."""
+    V = yt.shape[1]
+    q = softmax(yd[0].astype(np.float64) / T)
+    law = np.zeros(V)
+    grid = (np.arange(N) + 0.5) / N
+    for d in range(V):
+        kept = 0
+        for u in grid:
+            n, em, ratio, _ = oracle.verify_sample(yt, yd, [d], T, [u], 0.5)
+            kept += n == 2
+            assert (n == 2) == (u < ratio[0])  # the accept test in the oracle's own ratio
+        law[d] += q[d] * kept / N
+        rej = np.zeros(V)
+        for u in grid:
+            n, em, _, _ = oracle.verify_sample(yt, yd, [d], T, [np.float32(0.99999994)], u)
+            if n == 1:
+                rej[em[0]] += 1.0 / N
+        if rej.sum() > 0:
+            law += q[d] * (1.0 - kept / N) * rej
+    return law
+
+
+@pytest.mark.parametrize("T", [1.0, 0.8])
+def test_first_token_follows_the_target(oracle, T):
+    V = 6
+    yt = synth.logits(2, V, (705,), spread=1.0, peaks=1, lift=2.0)
+    yd = synth.logits_near(yt[:1], (706,), noise=2.0)
+    N = 1500
+    law = first_token_law(oracle, yt, yd, T, N)
+    p = softmax(yt[0].astype(np.float64) / T)
+    assert np.all(np.abs(law - p) <= 3.0 / N), (law, p)
+    # the law differs from the draft's own: the check has power
+    q = softmax(yd[0].astype(np.float64) / T)
+    assert np.abs(q - p).max() > 20.0 / N
+
+
+def test_whole_rounds_follow_the_target(oracle):
+    # Monte Carlo over rounds: drafts drawn from q with the oracle's sampler,
+    # then the round. Emitted token j (when the round reaches it) ~ p_{j+1}.
+    V, k, R = 5, 2, 12000
+    yt = synth.logits(k + 1, V, (707,), spread=1.0, peaks=1, lift=2.0)
+    yd = synth.logits_near(yt[:k], (708,), noise=1.0)
+    u = synth.uniforms((R, 2 * k + 1), (709,))
+    hits = [np.zeros(V) for _ in range(k + 1)]
+    reached = np.zeros(k + 1)
+    lengths = np.zeros(k + 2)
+    for r in range(R):
+        draft = [oracle.sample(yd[i], 1.0, u[r, i])[0] for i in range(k)]
+        n, em, _, _ = oracle.verify_sample(yt, yd, draft, 1.0, u[r, k:2 * k], u[r, 2 * k])
+        lengths[n] += 1
+        for j in range(n):
+            hits[j][em[j]] += 1
+            reached[j] += 1
+    for j in range(k + 1):
+        p = softmax(yt[j].astype(np.float64))
+        f = hits[j] / reached[j]
+        sd = np.sqrt(p * (1 - p) / reached[j])
+        assert np.all(np.abs(f - p) < 5 * sd + 1e-9), (j, f, p)
+    # expected emitted tokens per round: sum over slots of P(reach slot)
+    beta = [np.minimum(softmax(yt[i].astype(np.float64)), softmax(yd[i].astype(np.float64))).sum()
+            for i in range(k)]
+    e = 1.0 + beta[0] + beta[0] * beta[1]
+    mean = (lengths * np.arange(k + 2)).sum() / R
+    assert abs(mean - e) < 0.03
+
+
+def test_identical_models_keep_every_draft(oracle):
+    V, k = 400, 4
+    yt = synth.logits(k + 1, V, (710,))
+    u = synth.uniforms(2 * k + 1, (711,))
+    draft = [oracle.sample(yt[i], 1.0, u[i])[0] for i in range(k)]
+    n, em, ratio, margin = oracle.verify_sample(yt, yt[:k], draft, 1.0, u[k:2 * k], u[2 * k])
+    assert n == k + 1 and np.all(ratio == 1.0)
+    assert list(em[:k]) == draft
+    if margin > 1e-12:
+        assert em[k] == cdf_pick(softmax(yt[k].astype(np.float64)), float(u[2 * k]))
+
+
+def test_draft_without_target_mass_is_replaced_from_the_target(oracle):
+    V, k = 64, 3
+    yt = synth.logits(k + 1, V, (712,))
+    yd = yt[:k].copy()
+    d = 17
+    yt[0, d] = -1.0e4  # the target gives d no mass
+    yd[0, :] = -1.0e4
+    yd[0, d] = 0.0  # the draft is sure of d
+    for uf in synth.uniforms(20, (713,)):
+        n, em, ratio, margin = oracle.verify_sample(yt, yd, [d, 0, 0], 1.0, [0.0, 0.0, 0.0], uf)
+        assert n == 1 and ratio[0] == 0.0
+        if margin > 1e-12:
+            assert em[0] == cdf_pick(softmax(yt[0].astype(np.float64)), float(uf))
+        assert list(em[1:]) == [-1] * k
+
+
+def test_near_zero_temperature_is_the_greedy_rule(oracle):
+    # page Table 1's rule: keep drafts while they equal the target's top
+    # choice, then emit the target's top choice at the first mismatch
+    V, k = 200, 6
+    g = synth.rng(714)
+    for trial in range(20):
+        yt = synth.logits(k + 1, V, (715, trial))
+        yd = synth.logits_near(yt[:k], (716, trial), noise=2.0)
+        tgt = yt.argmax(axis=1)
+        draft = yd.argmax(axis=1).astype(np.int32)
+        u = g.random(k + 1)
+        n, em, _, _ = oracle.verify_sample(yt, yd, draft, 1e-4, u[:k], u[k])
+        a = 0
+        while a < k and draft[a] == tgt[a]:
+            a += 1
+        assert n == a + 1
+        assert list(em[:a]) == list(draft[:a]) and em[a] == tgt[a]
+
+
+def test_final_interval_agrees_with_the_round(oracle):
+    V, k = 300, 3
+    yt = synth.logits(k + 1, V, (717,))
+    yd = synth.logits_near(yt[:k], (718,), noise=0.5)
+    u = synth.uniforms((30, 2 * k + 1), (719,))
+    for r in range(30):
+        draft = [oracle.sample(yd[i], 1.0, u[r, i])[0] for i in range(k)]
+        n, em, _, margin = oracle.verify_sample(yt, yd, draft, 1.0, u[r, k:2 * k], u[r, 2 * k])
+        lo, hi, tg = oracle.final_interval(yt, yd, 1.0, n - 1, u[r, 2 * k], em[n - 1])
+        assert lo <= tg < hi and abs(min(tg - lo, hi - tg) - margin) < 1e-15
+
+
+def test_k_zero_is_a_plain_draw(oracle):
+    yt = synth.logits(1, 100, (720,))
+    for uf in synth.uniforms(10, (721,)):
+        n, em, _, _ = oracle.verify_sample(yt, np.zeros((0, 100), np.float32), [], 1.0, [], uf)
+        assert n == 1 and em[0] == oracle.sample(yt[0], 1.0, uf)[0]

@@ -31,6 +31,9 @@ the measured time per round. `rounds_per_s` gives the k=4 and k=8 rates.
 `roofline` covers the dominant kernel, the draft GEMV over the LM head's
 base plane, timed with HIP events around every launch in the timed region.
 `cpu_baseline` times the oracle on one full k=4 round on the host's cores.
+`sampled_round_k4` times the same k=4 round with speculative sampling at
+T = 1 (draft tokens drawn by nest_sample from the draft head's logits; the
+verify head's logits through verify_sample) next to the greedy round.
 `k_choice_eq2` gives, for each planted acceptance rate, the draft length
 that Eq. (1)/(2) choose from the measured time of one draft step and of
 the verify pass at each k (nest_choose_k), with the derived tokens/s.
@@ -164,6 +167,8 @@ def make_inputs(kmax):
     inp["vk"], inp["vv"] = synth.kv(QWEN["kv_heads"], kmax + 1, QWEN["head_dim"], (wk, 7))
     inp["qd"] = synth.queries_bf16(kmax, QWEN["q_heads"], QWEN["head_dim"], (wk, 4))
     inp["qv"] = synth.queries_bf16(kmax + 1, QWEN["q_heads"], QWEN["head_dim"], (wk, 5))
+    # uniforms of the sampled round: k draft draws, k accept tests, one last draw
+    inp["u"] = synth.uniforms(2 * kmax + 1, (wk, 8))
     return inp
 
 
@@ -172,8 +177,14 @@ def make_inputs(kmax):
 # ---------------------------------------------------------------------------
 
 class Round:
-    def __init__(self, ns, torch, dev_inp, k):
+    def __init__(self, ns, torch, dev_inp, k, temperature=None):
+        """temperature None: greedy round (fused argmax, greedy accept);
+        otherwise the sampled round: the draft head writes its logits and
+        nest_sample draws the draft token, the verify head writes the k+1
+        target rows and verify_sample applies the min(1, p/q) accept test and
+        the last draw."""
         self.ns, self.torch, self.k = ns, torch, k
+        sampled = temperature is not None
         L = ns.lib()
         P = ctypes.c_void_p
         st = P(torch.cuda.current_stream().cuda_stream)
@@ -205,6 +216,13 @@ class Round:
                        L.kv_nest_attend_workspace_size(k + 1, hq, hkv, 128, CAPACITY))
         ws_att = E(ws_att_n, dtype=torch.uint8, device=cuda)
         keep += [qa, sa, y, att_out, draft_tok, acc_out, ws_arg, ws_att]
+        if sampled:
+            yd_head = E((max(k, 1), V), dtype=torch.float32, device=cuda)
+            yt_head = E((k + 1, V), dtype=torch.float32, device=cuda)
+            u = d["u"]  # uniforms [k] draft draws, [k] accept tests, [1] last draw
+            ws_s_n = max(L.nest_sample_workspace_size(1, V), L.verify_sample_workspace_size(1, k, V))
+            ws_s = E(ws_s_n, dtype=torch.uint8, device=cuda)
+            keep += [yd_head, yt_head, ws_s]
         self.kvs = d["kv"].struct()
         sh = d["shadow"]
         self.draft_tok, self.acc_out = draft_tok, acc_out
@@ -227,9 +245,17 @@ class Round:
                                                      CONTEXT + j + 1, 0, p(att_out), p(ws_att),
                                                      ws_att_n, st), "attend_draft"))
             xh = d["x"]["head"][j:j + 1]
-            calls.append((L.draft_gemv_x, (p(xh), 1, H, p(d["base"]["head"]), p(d["scales"]["head"]),
-                                           V, 128, None, P(draft_tok.data_ptr() + 4 * j),
-                                           p(ws_arg), ws_arg.numel(), st), "DOMINANT"))
+            if sampled:
+                yj = P(yd_head.data_ptr() + 4 * V * j)
+                calls.append((L.draft_gemv_x, (p(xh), 1, H, p(d["base"]["head"]), p(d["scales"]["head"]),
+                                               V, 128, yj, None, None, 0, st), "draft_head_y"))
+                calls.append((L.nest_sample, (yj, 1, V, ctypes.c_float(temperature), P(u.data_ptr() + 4 * j),
+                                              P(draft_tok.data_ptr() + 4 * j), p(ws_s), ws_s_n, st),
+                              "sample"))
+            else:
+                calls.append((L.draft_gemv_x, (p(xh), 1, H, p(d["base"]["head"]), p(d["scales"]["head"]),
+                                               V, 128, None, P(draft_tok.data_ptr() + 4 * j),
+                                               p(ws_arg), ws_arg.numel(), st), "DOMINANT"))
             phases += [j] * (len(calls) - len(phases))
         for n, N, K in LINEARS:
             xv = d["xv"][n][:k + 1]
@@ -253,11 +279,19 @@ class Round:
                                                  CONTEXT + k + 1, 1, p(att_out), p(ws_att), ws_att_n,
                                                  st), "attend_verify"))
         xh = d["xv"]["head"][:k + 1]
-        calls.append((L.verify_accept_x, (p(xh), 1, k, H, p(d["base"]["head"]),
-                                          p(d["refine"]["head"]), p(d["scales"]["head"]), V, 128,
-                                          p(draft_tok), p(acc_out["target"]), p(acc_out["n"]),
-                                          p(acc_out["emitted"]), None, p(ws_arg), ws_arg.numel(),
-                                          st), "verify_accept"))
+        if sampled:
+            calls.append((L.verify_gemm_x, (p(xh), k + 1, H, p(d["base"]["head"]), p(d["refine"]["head"]),
+                                            p(d["scales"]["head"]), V, 128, p(yt_head), st), "verify_head_y"))
+            calls.append((L.verify_sample, (p(yt_head), p(yd_head), 1, k, V, ctypes.c_float(temperature),
+                                            p(draft_tok), P(u.data_ptr() + 4 * k), P(u.data_ptr() + 8 * k),
+                                            p(acc_out["n"]), p(acc_out["emitted"]), p(ws_s), ws_s_n, st),
+                          "verify_sample"))
+        else:
+            calls.append((L.verify_accept_x, (p(xh), 1, k, H, p(d["base"]["head"]),
+                                              p(d["refine"]["head"]), p(d["scales"]["head"]), V, 128,
+                                              p(draft_tok), p(acc_out["target"]), p(acc_out["n"]),
+                                              p(acc_out["emitted"]), None, p(ws_arg), ws_arg.numel(),
+                                              st), "verify_accept"))
         phases += ["verify"] * (len(calls) - len(phases))
         self.calls = calls
         self.phases = phases
@@ -334,7 +368,7 @@ def upload(ns, torch, inp):
     dv["shadow"] = ns.kv_shadow(dv["kv"])
     ns.kv_nest_shadow_fill(dv["kv"], kf, vf, CONTEXT, dv["shadow"])
     del kf, vf
-    for key in ("dk", "dv", "vk", "vv"):
+    for key in ("dk", "dv", "vk", "vv", "u"):
         dv[key] = torch.from_numpy(inp[key]).cuda()
     dv["qd"] = torch.from_numpy(inp["qd"].view(np.int16)).cuda()
     dv["qv"] = torch.from_numpy(inp["qv"].view(np.int16)).cuda()
@@ -471,6 +505,14 @@ def main():
         res[k] = {"ms": ms, "wall": wall, "dom": dom, "n": int(rnd.acc_out["n"].item())}
         print(f"# bench: k={k} {ms:.4f} ms/round", file=sys.stderr, flush=True)
 
+    T_SAMPLE = 1.0
+    rnd = Round(ns, torch, dv, 4, temperature=T_SAMPLE)
+    ms_s, _, _ = time_rounds(torch, rnd, args.steps, args.warmup, with_events=False)
+    sampled = {"temperature": T_SAMPLE, "ms": round(ms_s, 5), "rounds_per_s": round(1e3 / ms_s, 2),
+               "vs_greedy_round": round(ms_s / res[4]["ms"], 4), "n_emitted": int(rnd.acc_out["n"].item())}
+    print(f"# bench: sampled k=4 {ms_s:.4f} ms/round", file=sys.stderr, flush=True)
+    del rnd
+
     print("# bench: timing draft steps and verify passes for the choice of k", file=sys.stderr, flush=True)
     kc = k_choice(ns, torch, dv)
     ms4 = res[4]["ms"]
@@ -506,6 +548,7 @@ def main():
                                             "k8": round(1e3 / res[8]["ms"] * eq1(a, 8), 1)}
                                      for name, a in ALPHAS.items()},
         "k_choice_eq2": kc,
+        "sampled_round_k4": sampled,
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,

@@ -360,6 +360,60 @@ size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
                                      int64_t ctx_len);
 
 /* ---------------------------------------------------------------------------
+ * Speculative sampling ("How Speculative Decoding Speeds Up Inference",
+ * section "The same output as the large model alone", and the method of
+ * Leviathan et al. and Chen et al. it names). Scores are softmax(y / T) of
+ * fp32 logits y; a draw with uniform u takes the smallest id whose running
+ * weight exceeds u times the total weight (inverse CDF). The uniforms are
+ * inputs, so a caller owns the random stream. Arithmetic is fp32; a draw
+ * whose target lies within rounding of an id boundary may take either id.
+ * Logits must be finite or -inf (a masked id), with at least one finite
+ * value per row. Device pointers unless stated; the calls are asynchronous
+ * on `stream`, and the workspace needs no zero-fill.
+ * --------------------------------------------------------------------------- */
+
+/* nest_sample -- one id per row from softmax(y / T).
+ *   y            fp32 [M][V] logits
+ *   M, V         host values: rows (1..65535) and vocabulary (<= 8388608)
+ *   temperature  host value, > 0
+ *   u            fp32 [M] uniforms in [0, 1)
+ *   tokens       int32 [M] (out)
+ *   ws           nest_sample_workspace_size(M, V) bytes, 16-byte aligned
+ * Errors: NEST_EINVAL, NEST_EUNSUPPORTED, NEST_EWORKSPACE, NEST_EALIGN,
+ * NEST_EHIP. */
+int nest_sample(const float* y, int64_t M, int64_t V, float temperature,
+                const float* u, int32_t* tokens, void* ws, size_t ws_bytes,
+                void* stream);
+size_t nest_sample_workspace_size(int64_t M, int64_t V);
+
+/* verify_sample -- the accept test and last draw of B speculative rounds.
+ * Slot i (1..k) of sequence b keeps its draft d_i while
+ * u_acc * q_i(d_i) < p_i(d_i), i.e. with probability min(1, p/q); at the
+ * first slot that fails, the last id is drawn with u_fin from
+ * max(0, p_i - q_i) normalized (from p_i itself if rounding leaves that
+ * without mass); when all k are kept, from p_{k+1} (the bonus).
+ *   yt       fp32 [B][k+1][V]: the target's logits; row i-1 scores slot i,
+ *            row k the bonus position
+ *   yd       fp32 [B][k][V]: the draft logits each d_i was drawn from
+ *            (may be NULL when k == 0)
+ *   B, k, V  host values: 1 <= B, 0 <= k <= 32, B*(2k+1) <= 65535,
+ *            V <= 8388608
+ *   temperature  host value, > 0: the same T for both models
+ *   draft    int32 [B][k]; an id outside [0, V) is never kept
+ *   u_acc    fp32 [B][k] uniforms of the accept tests
+ *   u_fin    fp32 [B] uniforms of the last draws
+ *   n_emitted  int32 [B] (out): kept drafts + 1
+ *   emitted    int32 [B][k+1] (out): the kept drafts, the drawn id, then -1
+ *   ws       verify_sample_workspace_size(B, k, V) bytes, 16-byte aligned
+ * Errors: NEST_EINVAL, NEST_EUNSUPPORTED, NEST_EWORKSPACE, NEST_EALIGN,
+ * NEST_EHIP. */
+int verify_sample(const float* yt, const float* yd, int64_t B, int64_t k,
+                  int64_t V, float temperature, const int32_t* draft,
+                  const float* u_acc, const float* u_fin, int32_t* n_emitted,
+                  int32_t* emitted, void* ws, size_t ws_bytes, void* stream);
+size_t verify_sample_workspace_size(int64_t B, int64_t k, int64_t V);
+
+/* ---------------------------------------------------------------------------
  * Choosing the draft length ("How Speculative Decoding Speeds Up Inference",
  * section "Tokens per pass and time per token"). Host functions: every
  * pointer is a host pointer and nothing runs on the GPU.

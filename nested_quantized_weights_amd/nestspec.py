@@ -78,6 +78,11 @@ _SIGS = {
     "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _i64, ctypes.c_int, _p,
                                       _p, _sz, _p]),
     "kv_nest_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "nest_sample": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_float, _p, _p, _p, _sz, _p]),
+    "nest_sample_workspace_size": (_sz, [_i64, _i64]),
+    "verify_sample": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p, _p,
+                                     _sz, _p]),
+    "verify_sample_workspace_size": (_sz, [_i64, _i64, _i64]),
 }
 
 SYMBOLS = tuple(_SIGS)
@@ -456,6 +461,56 @@ def expected_tokens(alpha: float, k: int) -> float:
 def token_time(alpha: float, k: int, t_draft: float, t_pass: float) -> float:
     """Eq. (2)."""
     return lib().nest_token_time(float(alpha), int(k), float(t_draft), float(t_pass))
+
+
+def sample(y, temperature: float, u, tokens=None, ws=None):
+    """One id per row of the fp32 logits y [M][V] from softmax(y / T), drawn
+    by inverse CDF with the fp32 uniforms u [M]. Returns int32 [M]."""
+    what = "nest_sample"
+    _dev(y, torch.float32, what, "y")
+    _dev(u, torch.float32, what, "u")
+    M, V = y.shape
+    if u.numel() != M:
+        raise NestError(f"{what}: u needs {M} values")
+    dev = y.device
+    if tokens is None:
+        tokens = torch.empty(M, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(lib().nest_sample_workspace_size(M, V), dev, "sample")
+    _check(lib().nest_sample(_ptr(y), M, V, float(temperature), _ptr(u), _ptr(tokens), _ptr(ws), ws.numel(),
+                             _stream(dev)), what)
+    return tokens
+
+
+def verify_sample(yt, yd, draft, temperature: float, u_acc, u_fin, out=None, ws=None):
+    """Accept test and last draw of B speculative-sampling rounds.
+    yt fp32 [B][k+1][V], yd fp32 [B][k][V] (or None when k == 0), draft
+    int32 [B][k], u_acc fp32 [B][k], u_fin fp32 [B]. Returns a dict of device
+    tensors n_emitted [B] and emitted [B][k+1]."""
+    what = "verify_sample"
+    _dev(yt, torch.float32, what, "yt")
+    B, k1, V = yt.shape
+    k = k1 - 1
+    if k > 0:
+        _dev(yd, torch.float32, what, "yd")
+        _dev(draft, torch.int32, what, "draft")
+        _dev(u_acc, torch.float32, what, "u_acc")
+        if tuple(yd.shape) != (B, k, V) or draft.numel() != B * k or u_acc.numel() != B * k:
+            raise NestError(f"{what}: yd, draft and u_acc must hold [B][k] rows")
+    _dev(u_fin, torch.float32, what, "u_fin")
+    if u_fin.numel() != B:
+        raise NestError(f"{what}: u_fin needs {B} values")
+    dev = yt.device
+    if out is None:
+        out = {"n_emitted": torch.empty(B, dtype=torch.int32, device=dev),
+               "emitted": torch.empty((B, k1), dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = workspace(lib().verify_sample_workspace_size(B, k, V), dev, "verify_sample")
+    _check(lib().verify_sample(_ptr(yt), _ptr(yd) if k else None, B, k, V, float(temperature),
+                               _ptr(draft) if k else None, _ptr(u_acc) if k else None, _ptr(u_fin),
+                               _ptr(out["n_emitted"]), _ptr(out["emitted"]), _ptr(ws), ws.numel(),
+                               _stream(dev)), what)
+    return out
 
 
 def choose_k(alpha: float, t_draft: float, t_pass):

@@ -594,7 +594,12 @@ static void final_weights(const float* yt, const float* yd, int64_t k, int64_t V
   softmax_row(yt + a * V, V, T, w);
   if (a < k) {
     softmax_row(yd + a * V, V, T, q);
-    for (int64_t t = 0; t < V; t++) w[t] = fmax(0.0, w[t] - q[t]);
+    double tot = 0.0;
+    for (int64_t t = 0; t < V; t++) tot += fmax(0.0, w[t] - q[t]);
+    /* a rejection leaves mass in max(0, p - q) (p(d) < q(d)); only if
+     * rounding took all of it is the draw made from p itself */
+    if (tot > 0.0)
+      for (int64_t t = 0; t < V; t++) w[t] = fmax(0.0, w[t] - q[t]);
   }
 }
 
@@ -618,10 +623,12 @@ int64_t oracle_verify_sample(const float* yt, const float* yd, int64_t k, int64_
     softmax_row(yt + (i - 1) * V, V, (double)T, p);
     softmax_row(yd + (i - 1) * V, V, (double)T, q);
     const int32_t d = draft[i - 1];
-    const double r = p[d] / q[d];
+    /* an id outside the vocabulary has no probability under either model
+     * and is never kept */
+    const double r = (d >= 0 && d < V) ? p[d] / q[d] : 0.0;
     if (ratio) ratio[i - 1] = r;
     if (!rejected) {
-      if ((double)u_acc[i - 1] * q[d] < p[d])
+      if (d >= 0 && d < V && (double)u_acc[i - 1] * q[d] < p[d])
         emitted[a++] = d;
       else
         rejected = 1;

@@ -204,3 +204,24 @@ def test_k_zero_is_a_plain_draw(oracle):
     for uf in synth.uniforms(10, (721,)):
         n, em, _, _ = oracle.verify_sample(yt, np.zeros((0, 100), np.float32), [], 1.0, [], uf)
         assert n == 1 and em[0] == oracle.sample(yt[0], 1.0, uf)[0]
+
+
+def test_out_of_range_draft_is_never_kept(oracle):
+    V, k = 50, 2
+    yt = synth.logits(k + 1, V, (722,))
+    for d in (-1, V, 10 ** 6):
+        n, em, ratio, _ = oracle.verify_sample(yt, yt[:k], [d, 3], 1.0, [0.0, 0.0], 0.4)
+        assert n == 1 and ratio[0] == 0.0
+        assert em[0] == oracle.sample(yt[0], 1.0, 0.4)[0]  # max(0, p - q) = p when q = p: fallback to p
+
+
+def test_rejection_without_residual_mass_draws_from_the_target(oracle):
+    # identical models and u_acc = 1: the test u * q < p fails with p = q,
+    # and max(0, p - q) has no mass; the draw then follows p itself
+    V, k = 300, 3
+    yt = synth.logits(k + 1, V, (723,))
+    for uf in synth.uniforms(20, (724,)):
+        n, em, ratio, margin = oracle.verify_sample(yt, yt[:k], [5, 6, 7], 1.0, [1.0, 0.0, 0.0], uf)
+        assert n == 1 and ratio[0] == 1.0
+        if margin > 1e-12:
+            assert em[0] == cdf_pick(softmax(yt[0].astype(np.float64)), float(uf))

@@ -53,7 +53,7 @@ def within(lo, hi, tg):
 
 
 @pytest.mark.parametrize("M,V,T", [(1, 1000, 1.0), (5, 2049, 0.7), (16, 4096, 1.5), (3, 152064, 1.0),
-                                   (2, 152064, 0.6), (4, 33, 1.0), (1, 1, 1.0)])
+                                   (2, 152064, 0.6), (4, 33, 1.0), (1, 1, 1.0), (2, 600000, 1.0)])
 def test_sample_matches_oracle(ns, oracle, M, V, T):
     y = synth.logits(M, V, (730, M, V))
     yd = dev(y)
@@ -125,7 +125,8 @@ def check_round(oracle, yt, yd, draft, T, u_acc, u_fin, n_got, em_got):
 
 @pytest.mark.parametrize("B,k,V,T,noise", [(1, 4, 1000, 1.0, 0.3), (3, 1, 2049, 0.8, 1.0), (2, 8, 4096, 1.0, 0.3),
                                            (1, 8, 152064, 1.0, 0.3), (2, 4, 152064, 0.7, 0.1),
-                                           (4, 0, 5000, 1.0, 0.3), (1, 32, 700, 1.2, 0.5)])
+                                           (4, 0, 5000, 1.0, 0.3), (1, 32, 700, 1.2, 0.5),
+                                           (1, 2, 600000, 1.0, 0.3), (2, 9, 3000, 1.0, 0.3)])
 def test_verify_sample_matches_oracle(ns, oracle, B, k, V, T, noise):
     exact = total = 0
     for rep in range(3):

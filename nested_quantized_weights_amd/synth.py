@@ -175,3 +175,41 @@ def logits_near(y: np.ndarray, key, noise: float = 0.3) -> np.ndarray:
 def uniforms(shape, key) -> np.ndarray:
     """float32 uniforms in [0, 1): the random numbers a sampling step consumes."""
     return rng(*key).random(shape, dtype=np.float32)
+
+
+# A small synthetic pre-norm decoder (Llama / Qwen style) for running rounds
+# end to end: 2 layers, hidden 512 (4 q heads / 2 kv heads of 128), SwiGLU
+# width 1024, vocabulary 4096, nested KV cache of 1024 tokens.
+TINY_DECODER = {"vocab": 4096, "hidden": 512, "layers": 2, "q_heads": 4, "kv_heads": 2, "head_dim": 128,
+                "inter": 1024, "theta": 10000.0, "eps": 1e-6, "capacity": 1024}
+
+
+def decoder_weights(cfg: dict, key) -> dict:
+    """fp32 weights of the decoder in ``cfg``: linears ~ N(0, 1/fan_in)
+    (std 1/sqrt(fan_in)), the LM head at twice that, embeddings N(0, 1), norm
+    gains 1 + N(0, 0.1). Linears are [out][in]; gate and up are stored
+    concatenated as gate_up [2 * inter][hidden]."""
+    H, I, V = cfg["hidden"], cfg["inter"], cfg["vocab"]
+    qd = cfg["q_heads"] * cfg["head_dim"]
+    kvd = cfg["kv_heads"] * cfg["head_dim"]
+    key = tuple(key)
+    w = {"embed": normal((V, H), key + (0,)),
+         "lm_head": normal((V, H), key + (1,), std=2.0 / np.sqrt(H)),
+         "norm_final": (1.0 + normal(H, key + (2,), std=0.1)).astype(np.float32),
+         "layers": []}
+    for li in range(cfg["layers"]):
+        k2 = key + (10 + li,)
+        w["layers"].append({
+            "norm_attn": (1.0 + normal(H, k2 + (0,), std=0.1)).astype(np.float32),
+            "norm_mlp": (1.0 + normal(H, k2 + (1,), std=0.1)).astype(np.float32),
+            "qkv": normal((qd + 2 * kvd, H), k2 + (2,), std=1.0 / np.sqrt(H)),
+            "o": normal((H, qd), k2 + (3,), std=1.0 / np.sqrt(qd)),
+            "gate_up": normal((2 * I, H), k2 + (4,), std=1.0 / np.sqrt(H)),
+            "down": normal((H, I), k2 + (5,), std=1.0 / np.sqrt(I)),
+        })
+    return w
+
+
+def tokens(n: int, vocab: int, key) -> np.ndarray:
+    """int32 token ids, uniform over the vocabulary (a synthetic prompt)."""
+    return rng(*key).integers(0, vocab, size=n).astype(np.int32)

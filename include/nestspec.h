@@ -414,6 +414,48 @@ int verify_sample(const float* yt, const float* yd, int64_t B, int64_t k,
 size_t verify_sample_workspace_size(int64_t B, int64_t k, int64_t V);
 
 /* ---------------------------------------------------------------------------
+ * Decoder glue for running rounds end to end through a small synthetic
+ * pre-norm decoder ("How Speculative Decoding Speeds Up Inference", section
+ * "The same output as the large model alone": greedy speculation keeps only
+ * the target's own top choices). The pages define none of these layers;
+ * they are the plain Llama/Qwen-style ones. Every output row depends only
+ * on its own input row and is computed in a fixed order, so a position is
+ * bit-identical whether it runs alone or inside a batch. fp32, device
+ * pointers, asynchronous on `stream`.
+ * --------------------------------------------------------------------------- */
+
+/* out [M][H] = table [V][H] rows at tokens [M] (int32); an id outside
+ * [0, V) gives a zero row. Errors: NEST_EINVAL, NEST_EUNSUPPORTED, NEST_EHIP. */
+int nest_embed(const float* table, int64_t V, int64_t H, const int32_t* tokens,
+               int64_t M, float* out, void* stream);
+
+/* Residual add and RMSNorm: when y is non-NULL, x += y (x is written);
+ * then out = x / sqrt(mean(x^2) + eps) * gamma, per row of x [M][H].
+ * out may not alias x. Errors: NEST_EINVAL, NEST_EUNSUPPORTED, NEST_EHIP. */
+int nest_add_rmsnorm(float* x, const float* y, const float* gamma, int64_t M,
+                     int64_t H, float eps, float* out, void* stream);
+
+/* Rotary embedding and q/k/v split of a QKV projection qkv
+ * [M][(Hq + 2 Hkv) * d] (q heads, then k heads, then v heads). Row m is at
+ * position pos0 + m; pair (i, i + d/2) of a q or k head is rotated by
+ * (pos0 + m) * theta^(-2i/d) (rotate-half convention). Outputs: q as bf16
+ * bit patterns [M][Hq][d] (nearest, ties to even), ready for
+ * kv_nest_attend; k and v fp32, laid out [Hkv][M][d] (token_major = 0, the
+ * kv_nest_append layout for M tokens) or [M][Hkv][d] (token_major = 1, so
+ * that each token's slice is a [Hkv][1][d] append). d even, theta > 1.
+ * Errors: NEST_EINVAL, NEST_EUNSUPPORTED, NEST_EHIP. */
+int nest_rope_split(const float* qkv, int64_t M, int64_t pos0,
+                    int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim,
+                    float theta, int token_major, uint16_t* q, float* k,
+                    float* v, void* stream);
+
+/* SwiGLU: out [M][I] = silu(g) * u with gate_up [M][2I] = [g | u] per row
+ * and silu(g) = g / (1 + exp(-g)). Errors: NEST_EINVAL, NEST_EUNSUPPORTED,
+ * NEST_EHIP. */
+int nest_swiglu(const float* gate_up, int64_t M, int64_t I, float* out,
+                void* stream);
+
+/* ---------------------------------------------------------------------------
  * Choosing the draft length ("How Speculative Decoding Speeds Up Inference",
  * section "Tokens per pass and time per token"). Host functions: every
  * pointer is a host pointer and nothing runs on the GPU.

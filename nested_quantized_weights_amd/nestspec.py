@@ -83,6 +83,11 @@ _SIGS = {
     "verify_sample": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p, _p,
                                      _sz, _p]),
     "verify_sample_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nest_embed": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _p]),
+    "nest_add_rmsnorm": (ctypes.c_int, [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p]),
+    "nest_rope_split": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _p, _p,
+                                       _p, _p]),
+    "nest_swiglu": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
 }
 
 SYMBOLS = tuple(_SIGS)
@@ -510,6 +515,64 @@ def verify_sample(yt, yd, draft, temperature: float, u_acc, u_fin, out=None, ws=
                                _ptr(draft) if k else None, _ptr(u_acc) if k else None, _ptr(u_fin),
                                _ptr(out["n_emitted"]), _ptr(out["emitted"]), _ptr(ws), ws.numel(),
                                _stream(dev)), what)
+    return out
+
+
+def embed(table, tokens, out=None):
+    """out [M][H] = table[tokens] (fp32 table [V][H], int32 tokens [M])."""
+    what = "nest_embed"
+    _dev(table, torch.float32, what, "table")
+    _dev(tokens, torch.int32, what, "tokens")
+    V, H = table.shape
+    M = tokens.numel()
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32, device=table.device)
+    _check(lib().nest_embed(_ptr(table), V, H, _ptr(tokens), M, _ptr(out), _stream(table.device)), what)
+    return out
+
+
+def add_rmsnorm(x, y, gamma, eps: float, out=None):
+    """x += y (when y is given, in place), then RMSNorm of x with gamma."""
+    what = "nest_add_rmsnorm"
+    _dev(x, torch.float32, what, "x")
+    _dev(gamma, torch.float32, what, "gamma")
+    if y is not None:
+        _dev(y, torch.float32, what, "y")
+    M, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().nest_add_rmsnorm(_ptr(x), _ptr(y), _ptr(gamma), M, H, float(eps), _ptr(out),
+                                  _stream(x.device)), what)
+    return out
+
+
+def rope_split(qkv, pos0: int, n_q_heads: int, n_kv_heads: int, head_dim: int, theta: float,
+               token_major: bool = False, out=None):
+    """Rotary embedding + q/k/v split of qkv [M][(Hq+2Hkv)d]: (q bf16 bits
+    [M][Hq][d] as int16, k, v fp32 [Hkv][M][d] or [M][Hkv][d])."""
+    what = "nest_rope_split"
+    _dev(qkv, torch.float32, what, "qkv")
+    M = qkv.shape[0]
+    dev = qkv.device
+    if out is None:
+        kv_shape = (M, n_kv_heads, head_dim) if token_major else (n_kv_heads, M, head_dim)
+        out = (torch.empty((M, n_q_heads, head_dim), dtype=torch.int16, device=dev),
+               torch.empty(kv_shape, dtype=torch.float32, device=dev),
+               torch.empty(kv_shape, dtype=torch.float32, device=dev))
+    q, k, v = out
+    _check(lib().nest_rope_split(_ptr(qkv), M, int(pos0), n_q_heads, n_kv_heads, head_dim, float(theta),
+                                 1 if token_major else 0, _ptr(q), _ptr(k), _ptr(v), _stream(dev)), what)
+    return q, k, v
+
+
+def swiglu(gate_up, out=None):
+    """silu(gate) * up for gate_up [M][2I]."""
+    what = "nest_swiglu"
+    _dev(gate_up, torch.float32, what, "gate_up")
+    M, I2 = gate_up.shape
+    if out is None:
+        out = torch.empty((M, I2 // 2), dtype=torch.float32, device=gate_up.device)
+    _check(lib().nest_swiglu(_ptr(gate_up), M, I2 // 2, _ptr(out), _stream(gate_up.device)), what)
     return out
 
 

@@ -1,0 +1,174 @@
+"""A small synthetic decoder run through greedy speculative rounds on the GPU
+("How Speculative Decoding Speeds Up Inference", section "The same output as
+the large model alone").
+
+  * Glue kernels against the oracle's layers: embedding exact; RMSNorm and
+    SwiGLU within fp32 rounding (fp64 on the oracle side); the rotary
+    embedding within the error of an fp32 angle (pos * inv_freq rounds to
+    2^-24 relative, so up to ~6e-5 rad at position 1000) and q within one
+    bf16 step.
+  * Row independence: every glue kernel and linear gives a row the same bits
+    alone as inside a batch of 5 (what makes the claim below exact).
+  * The claim: speculative rounds with position-by-position attention in the
+    target pass emit exactly the tokens of target-only decoding, and the
+    target logits of every emitted position are bit-identical.
+  * Against the oracle's own decode: the token sequences agree; a
+    divergence is allowed only where the oracle's top two logits are within
+    the envelope of the GPU-oracle logit differences seen up to that point.
+    Stage by stage the two decoders agree closely (linears bit-identical,
+    attention within the KV tolerance, glue within fp32 rounding), but the
+    per-token int8 activations are a step function: a 1e-4 difference in a
+    layer's input moves about 2 % of its codes by one step (1/127 of the
+    row's max), and the layers after it carry that, so the logits differ by
+    about 2 % of their largest value. The envelope is checked against 5 %.
+  * The batched target pass (one append + one k+1-query attention) is run
+    and its first divergence from target-only decoding reported: there the
+    open block is quantized with later positions, so agreement is measured,
+    not guaranteed.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nested_quantized_weights_amd import synth
+
+pytestmark = pytest.mark.gpu
+CFG = synth.TINY_DECODER
+
+
+@pytest.fixture(scope="module")
+def ns():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nested_quantized_weights_amd import nestspec
+
+    nestspec.lib()
+    return nestspec
+
+
+@pytest.fixture(scope="module")
+def D(oracle):
+    from oracle import decoder
+
+    return decoder
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.decoder_weights(CFG, (800,))
+
+
+@pytest.fixture(scope="module")
+def gpu_dec(ns, weights):
+    from nested_quantized_weights_amd.decoder import Decoder
+
+    return Decoder(CFG, weights)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def test_glue_against_oracle(ns, D):
+    M, H = 7, 512
+    table = synth.normal((300, H), (820,))
+    tok = np.array([0, 299, 5, 17, 5, 100, 42], np.int32)
+    assert np.array_equal(host(ns.embed(dev(table), dev(tok))), table[tok])
+    x, y = synth.normal((M, H), (821,)), synth.normal((M, H), (822,))
+    g = (1.0 + synth.normal(H, (823,), std=0.1)).astype(np.float32)
+    xd = dev(x)
+    out = host(ns.add_rmsnorm(xd, dev(y), dev(g), 1e-6))
+    assert np.array_equal(host(xd), (x + y).astype(np.float32))
+    ref = D.rmsnorm((x + y).astype(np.float32), g, 1e-6)
+    assert np.allclose(out, ref, rtol=4e-6, atol=1e-6)
+    gu = synth.normal((M, 2048), (824,), std=3.0)
+    assert np.allclose(host(ns.swiglu(dev(gu))), D.swiglu(gu), rtol=2e-6, atol=1e-6)
+    Hq, Hkv, d = 4, 2, 128
+    qkv = synth.normal((M, (Hq + 2 * Hkv) * d), (825,))
+    for pos0 in (0, 993):
+        q, k, v = (host(t) for t in ns.rope_split(dev(qkv), pos0, Hq, Hkv, d, 1e4))
+        r = qkv.reshape(M, Hq + 2 * Hkv, d)
+        pos = np.arange(pos0, pos0 + M)
+        kr = D.rope(r[:, Hq:Hq + Hkv], pos, 1e4).transpose(1, 0, 2)
+        tol = 1e-6 + (pos0 + M) * 2.0 ** -24 * 4
+        assert np.allclose(k, kr, atol=tol * np.abs(r).max())
+        assert np.array_equal(v, r[:, Hq + Hkv:].transpose(1, 0, 2))
+        qf = (q.astype(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        qr = D.rope(r[:, :Hq], pos, 1e4)
+        assert np.all(np.abs(qf - qr) <= 2.0 ** -8 * np.abs(qr) + tol * np.abs(r).max())
+        qt, kt, vt = (host(t) for t in ns.rope_split(dev(qkv), pos0, Hq, Hkv, d, 1e4, token_major=True))
+        assert np.array_equal(qt, q) and np.array_equal(kt, k.transpose(1, 0, 2))
+
+
+def test_rows_do_not_depend_on_the_batch(ns, gpu_dec):
+    H = CFG["hidden"]
+    x = dev(synth.normal((5, H), (826,)))
+    g = gpu_dec.layers[0]["norm_attn"]
+    full = host(ns.add_rmsnorm(x.clone(), None, g, 1e-6))
+    for i in range(5):
+        assert np.array_equal(host(ns.add_rmsnorm(x[i:i + 1].clone(), None, g, 1e-6))[0], full[i])
+    for name, K in (("qkv", H), ("gate_up", H), ("down", CFG["inter"])):
+        W = gpu_dec.layers[1][name]
+        xs = dev(synth.normal((5, K), (827, K)))
+        for fn in (ns.verify_gemm_x, ns.draft_gemv_x):
+            full = host(fn(xs, W))
+            for i in range(5):
+                assert np.array_equal(host(fn(xs[i:i + 1].contiguous(), W))[0].view(np.uint32),
+                                      full[i].view(np.uint32)), (name, fn)
+    qkv = dev(synth.normal((5, 8 * 128), (828,)))
+    q, k, v = (host(t) for t in ns.rope_split(qkv, 30, 4, 2, 128, 1e4, token_major=True))
+    for i in range(5):
+        qi, ki, _ = (host(t) for t in ns.rope_split(qkv[i:i + 1].contiguous(), 30 + i, 4, 2, 128, 1e4,
+                                                    token_major=True))
+        assert np.array_equal(qi[0], q[i]) and np.array_equal(ki[0], k[i])
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_speculative_rounds_emit_the_target_only_tokens(gpu_dec, k):
+    prompt = synth.tokens(40, CFG["vocab"], (801,))
+    ar, r_ar = gpu_dec.generate(prompt, 48, 0)
+    sp, r_sp = gpu_dec.generate(prompt, 48, k, exact=True)
+    assert sp == ar
+    y_ar = torch.cat([y for _, y in r_ar]).cpu().numpy()
+    y_sp = torch.cat([y for _, y in r_sp]).cpu().numpy()[:len(y_ar)]
+    assert np.array_equal(y_sp.view(np.uint32), y_ar[:len(y_sp)].view(np.uint32))
+    tpr = np.mean([n for n, _ in r_sp])
+    print(f"k={k}: {tpr:.3f} tokens per round over {len(r_sp)} rounds")
+    assert tpr > 1.5
+
+
+def test_decode_matches_the_oracle(gpu_dec, weights, D):
+    prompt = synth.tokens(40, CFG["vocab"], (801,))
+    ar, r_ar = gpu_dec.generate(prompt, 48, 0)
+    odec = D.Decoder(CFG, weights)
+    oar, r_oar = odec.generate(prompt, 48, 0)
+    envelope = 0.0
+    for j, (a, b) in enumerate(zip(ar, oar)):
+        yg = r_ar[j][1][0].cpu().numpy().astype(np.float64)
+        yo = r_oar[j][1][0].astype(np.float64)
+        if a != b:
+            # a divergence only where the oracle's choice and the GPU's are
+            # within the logit differences seen so far
+            assert yo[b] - yo[a] <= 4.0 * envelope, (j, yo[b] - yo[a], envelope)
+            assert j >= 8  # the first tokens must agree
+            print(f"diverged at token {j} (oracle gap {yo[b] - yo[a]:.3g}, envelope {envelope:.3g})")
+            return
+        envelope = max(envelope, float(np.abs(yg - yo).max()))
+    scale = max(float(np.abs(y[0].cpu().numpy()).max()) for _, y in r_ar)
+    print(f"all {len(ar)} tokens agree; max logit difference {envelope:.3g} (largest logit {scale:.3g})")
+    assert envelope < 0.05 * scale
+
+
+def test_batched_target_pass_is_measured(gpu_dec):
+    prompt = synth.tokens(40, CFG["vocab"], (801,))
+    ar, _ = gpu_dec.generate(prompt, 48, 0)
+    for k in (1, 4):
+        sp, r = gpu_dec.generate(prompt, 48, k, exact=False)
+        first = next((i for i, (a, b) in enumerate(zip(sp, ar)) if a != b), None)
+        print(f"batched k={k}: {np.mean([n for n, _ in r]):.3f} tokens/round, first divergence {first}")
+        assert all(0 <= t < CFG["vocab"] for t in sp)

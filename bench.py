@@ -34,6 +34,11 @@ base plane, timed with HIP events around every launch in the timed region.
 `sampled_round_k4` times the same k=4 round with speculative sampling at
 T = 1 (draft tokens drawn by nest_sample from the draft head's logits; the
 verify head's logits through verify_sample) next to the greedy round.
+`tiny_decoder_greedy` runs greedy rounds end to end through a small synthetic
+decoder (the library's glue kernels around the nested linears and KV cache):
+real tokens per round at k = 1 and 4, whether the emitted tokens equal
+target-only decoding (position-by-position attention in the target pass),
+and where the batched target pass first diverges.
 `k_choice_eq2` gives, for each planted acceptance rate, the draft length
 that Eq. (1)/(2) choose from the measured time of one draft step and of
 the verify pass at each k (nest_choose_k), with the derived tokens/s.
@@ -353,6 +358,45 @@ def k_choice(ns, torch, dv, kmax=8):
     return out
 
 
+def tiny_decoder(torch, n_new=48, prompt_len=40):
+    """Greedy rounds end to end through the small synthetic decoder: emitted
+    tokens per round, equality with target-only decoding, and wall-clock
+    tokens/s of the host-driven loop (one host sync per round)."""
+    from nested_quantized_weights_amd import synth
+    from nested_quantized_weights_amd.decoder import Decoder
+
+    cfg = synth.TINY_DECODER
+    dec = Decoder(cfg, synth.decoder_weights(cfg, (800,)))
+    prompt = synth.tokens(prompt_len, cfg["vocab"], (801,))
+
+    def run(k, exact):
+        dec.generate(prompt, 8, k, exact)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, rounds = dec.generate(prompt, n_new, k, exact)
+        torch.cuda.synchronize()
+        return toks, rounds, time.perf_counter() - t0
+
+    ar, _, t_ar = run(0, True)
+    out = {"workload": f"{cfg['layers']}-layer synthetic pre-norm decoder, hidden {cfg['hidden']}, "
+                       f"{cfg['q_heads']}/{cfg['kv_heads']} heads of {cfg['head_dim']}, SwiGLU {cfg['inter']}, "
+                       f"vocab {cfg['vocab']}; {prompt_len}-token prompt, {n_new} new tokens",
+           "tokens_per_round": {}, "equal_to_target_only": {}, "batched_first_divergence": {},
+           "host_loop_tokens_per_s": {"target_only": round(n_new / t_ar, 1)}}
+    for k in (1, 4):
+        for exact in (True, False):
+            toks, rounds, t = run(k, exact)
+            tag = f"k{k}_{'exact' if exact else 'batched'}"
+            out["tokens_per_round"][tag] = round(float(np.mean([n for n, _ in rounds])), 3)
+            out["host_loop_tokens_per_s"][tag] = round(n_new / t, 1)
+            if exact:
+                out["equal_to_target_only"][tag] = toks == ar
+            else:
+                out["batched_first_divergence"][tag] = next(
+                    (i for i, (a, b) in enumerate(zip(toks, ar)) if a != b), None)
+    return out
+
+
 def upload(ns, torch, inp):
     dv = {"base": {}, "refine": {}, "scales": {}, "x": {}, "xv": {}}
     for name, w in inp["w"].items():
@@ -513,6 +557,9 @@ def main():
     print(f"# bench: sampled k=4 {ms_s:.4f} ms/round", file=sys.stderr, flush=True)
     del rnd
 
+    print("# bench: greedy rounds through the small decoder", file=sys.stderr, flush=True)
+    tiny = tiny_decoder(torch)
+
     print("# bench: timing draft steps and verify passes for the choice of k", file=sys.stderr, flush=True)
     kc = k_choice(ns, torch, dv)
     ms4 = res[4]["ms"]
@@ -549,6 +596,7 @@ def main():
                                      for name, a in ALPHAS.items()},
         "k_choice_eq2": kc,
         "sampled_round_k4": sampled,
+        "tiny_decoder_greedy": tiny,
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,

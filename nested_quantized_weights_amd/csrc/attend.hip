@@ -170,11 +170,11 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
       const int tok = 32 * (r >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (r & 3);
       const size_t koff = (static_cast<size_t>(h) * a.cap + t0 + tok) * (kD / 2) + 16 * q;
       const size_t voff = (hb * kD + t * 16 + r) * (kBlk / 2) + 16 * q;
-      ck_b[rep] = ld16(a.kb + koff);
-      cv_b[rep] = ld16(a.vb + voff);
+      ck_b[rep] = nest::ldnt16(a.kb + koff);
+      cv_b[rep] = nest::ldnt16(a.vb + voff);
       if (VIEW) {
-        ck_r[rep] = ld16(a.kr + koff);
-        cv_r[rep] = ld16(a.vr + voff);
+        ck_r[rep] = nest::ldnt16(a.kr + koff);
+        cv_r[rep] = nest::ldnt16(a.vr + voff);
       } else {
         ck_r[rep] = cv_r[rep] = make_uint4(0, 0, 0, 0);
       }
@@ -376,11 +376,11 @@ __global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
       const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
       const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
       const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
-      kb[tt] = ld16(a.kb + koff);
-      vb[tt] = ld16(a.vb + voff);
+      kb[tt] = nest::ldnt16(a.kb + koff);
+      vb[tt] = nest::ldnt16(a.vb + voff);
       if (VIEW) {
-        kr[tt] = ld16(a.kr + koff);
-        vr[tt] = ld16(a.vr + voff);
+        kr[tt] = nest::ldnt16(a.kr + koff);
+        vr[tt] = nest::ldnt16(a.vr + voff);
       } else {
         kr[tt] = vr[tt] = make_uint4(0, 0, 0, 0);
       }

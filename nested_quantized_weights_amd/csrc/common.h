@@ -55,6 +55,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+namespace nest {
+// 16-byte load with the nontemporal hint, for data that one call streams
+// through once (weight planes and scales, KV planes): on MI355X a streaming
+// read with the hint sustains ~7.0 TB/s against ~6.3 TB/s without it.
+typedef unsigned nt_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldnt16(const void* p) {
+  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ldnt_f4(const void* p) {
+  const uint4 v = ldnt16(p);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+}  // namespace nest
+
 // Orderable 64-bit argmax key: larger value first, then the lower index.
 // -0 is folded to +0 so that equal values tie on the index.
 __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {

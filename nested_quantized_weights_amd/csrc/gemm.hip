@@ -91,8 +91,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 4; ++r) run[c][r] = 0.0f;
     if (tile_ok) {
       for (int g = g_begin; g < g_end; ++g) {
-        const uint4 wb = nest::ld16(pb + static_cast<size_t>(g) * 1024);
-        const uint4 wr = nest::ld16(pr + static_cast<size_t>(g) * 1024);
+        const uint4 wb = nest::ldnt16(pb + static_cast<size_t>(g) * 1024);
+        const uint4 wr = nest::ldnt16(pr + static_cast<size_t>(g) * 1024);
         const float* pq = ps + static_cast<size_t>(g / 4) * 64 + (g & 3);
         const float4 s = make_float4(pq[0], pq[4], pq[8], pq[12]);
         gemm_group<CT, DBG>(a, pa, col, n_out0, g, wb, wr, s, run);

@@ -317,19 +317,19 @@ __device__ __forceinline__ TilePtr tile_ptr(const GemvArgs& a, int t, int kq, in
 
 template <int PLANES>
 __device__ __forceinline__ void load_quad(const TilePtr& p, int g, Quad& q) {
-  q.b0 = ld16(p.pb + static_cast<size_t>(g) * 1024);
-  q.b1 = ld16(p.pb + static_cast<size_t>(g + 1) * 1024);
-  q.b2 = ld16(p.pb + static_cast<size_t>(g + 2) * 1024);
-  q.b3 = ld16(p.pb + static_cast<size_t>(g + 3) * 1024);
+  q.b0 = nest::ldnt16(p.pb + static_cast<size_t>(g) * 1024);
+  q.b1 = nest::ldnt16(p.pb + static_cast<size_t>(g + 1) * 1024);
+  q.b2 = nest::ldnt16(p.pb + static_cast<size_t>(g + 2) * 1024);
+  q.b3 = nest::ldnt16(p.pb + static_cast<size_t>(g + 3) * 1024);
   if (PLANES == 2) {
-    q.r0 = ld16(p.pr + static_cast<size_t>(g) * 1024);
-    q.r1 = ld16(p.pr + static_cast<size_t>(g + 1) * 1024);
-    q.r2 = ld16(p.pr + static_cast<size_t>(g + 2) * 1024);
-    q.r3 = ld16(p.pr + static_cast<size_t>(g + 3) * 1024);
+    q.r0 = nest::ldnt16(p.pr + static_cast<size_t>(g) * 1024);
+    q.r1 = nest::ldnt16(p.pr + static_cast<size_t>(g + 1) * 1024);
+    q.r2 = nest::ldnt16(p.pr + static_cast<size_t>(g + 2) * 1024);
+    q.r3 = nest::ldnt16(p.pr + static_cast<size_t>(g + 3) * 1024);
   } else {
     q.r0 = q.r1 = q.r2 = q.r3 = make_uint4(0, 0, 0, 0);
   }
-  q.s = *reinterpret_cast<const float4*>(p.ps + static_cast<size_t>(g / 4) * 64);
+  q.s = nest::ldnt_f4(p.ps + static_cast<size_t>(g / 4) * 64);
 }
 
 // Fold groups [g0, g1) of one tile (A4: 4-aligned bounds; cur holds the
@@ -352,8 +352,8 @@ __device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds
     }
   } else {
     for (int g = g0; g < g1; ++g) {
-      const uint4 wb = ld16(tp.pb + static_cast<size_t>(g) * 1024);
-      const uint4 wr = PLANES == 2 ? ld16(tp.pr + static_cast<size_t>(g) * 1024) : make_uint4(0, 0, 0, 0);
+      const uint4 wb = nest::ldnt16(tp.pb + static_cast<size_t>(g) * 1024);
+      const uint4 wr = PLANES == 2 ? nest::ldnt16(tp.pr + static_cast<size_t>(g) * 1024) : make_uint4(0, 0, 0, 0);
       gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, wb, wr,
                                           tp.ps[static_cast<size_t>(g / 4) * 64 + (g & 3)], run);
     }

@@ -378,9 +378,20 @@ __attribute__((amdgpu_waves_per_eu(occupancy_target(PLANES, MR, DBG))))
 gemv_kernel(GemvArgs a) {
   static_assert(!XQ || LDSACT, "fp32 activations are quantized into LDS");
   extern __shared__ uint4 lds_act[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is the same in every lane: values derived from it stay
+  // in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int S = a.nseg, per_iter = WAVES / S;
-  const int T = (a.N + 15) / 16, iters = (T + per_iter - 1) / per_iter;
+  const int T = (a.N + 15) / 16;
+  // Tiles: the block's per_iter wave groups (S waves each) are numbered
+  // across the grid, and group gg takes the contiguous tiles
+  // [gg T / NG, (gg+1) T / NG): every group gets within one tile of the
+  // same share, so the CUs' shares are even too.
+  const int NG = static_cast<int>(gridDim.x) * per_iter;
+  const int gg = static_cast<int>(blockIdx.x) * per_iter + wave / S;
+  const int t_lo = static_cast<int>(static_cast<long long>(gg) * T / NG);
+  const int t_hi = static_cast<int>(static_cast<long long>(gg + 1) * T / NG);
+  const int J = (T + NG - 1) / NG;  // the most tiles a group takes
   const int seg = wave % S, G = a.G;
   const int unit = A4 ? 4 : 1, units = G / unit;
   const int g_begin = static_cast<int>(static_cast<long long>(seg) * units / S) * unit;
@@ -388,7 +399,6 @@ gemv_kernel(GemvArgs a) {
   const int kq = lane >> 4, c = lane & 15;
   const int mrow = min(c, a.M - 1);  // A-operand row of this lane (rows past M fill unused D rows)
   const int8_t* pa = LDSACT ? nullptr : a.qa + static_cast<size_t>(mrow) * a.K + kq * 32;
-  auto tile_n0 = [&](int it) { return (it * per_iter + wave / S) * 16; };
 
   // activations first (returns come back in issue order), then the first
   // weight quad, then the rest of staging
@@ -403,9 +413,7 @@ gemv_kernel(GemvArgs a) {
   // branch-free first quad: tile and group clamped into range; it is only
   // used when this wave's first tile exists and its segment is not empty
   Quad cur;
-  int it = blockIdx.x;
-  if (A4) load_quad<PLANES>(tile_ptr<PLANES>(a, min(tile_n0(it), (T - 1) * 16) / 16, kq, c),
-                            min(g_begin, G - 4), cur);
+  if (A4) load_quad<PLANES>(tile_ptr<PLANES>(a, min(t_lo, T - 1), kq, c), min(g_begin, G - 4), cur);
 
   __shared__ float sa_sh[32];  // [0, 16): s_a per row; [16, 32): 1 / s_a
   __shared__ unsigned amax_sh[16];
@@ -419,16 +427,16 @@ gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int r = 0; r < MR; ++r) s_a[r] = XQ ? sa_sh[min(4 * kq + r, a.M - 1)] : a.sa[min(4 * kq + r, a.M - 1)];
 
-  for (; it < iters; it += gridDim.x) {
-    const int n0 = tile_n0(it);
-    const bool tile_ok = n0 < a.N;
+  for (int j = 0; j < J; ++j) {
+    const int n0 = (t_lo + j) * 16;
+    const bool tile_ok = t_lo + j < t_hi;
     const int n = n0 + c;  // this lane's output column (weight row)
     const TilePtr tp = tile_ptr<PLANES>(a, n0 / 16, kq, c);
     float run[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) run[r] = 0.0f;
     // the first tile's first quad was requested before staging
-    if (A4 && tile_ok && it != static_cast<int>(blockIdx.x) && g_begin < g_end) load_quad<PLANES>(tp, g_begin, cur);
+    if (A4 && tile_ok && j != 0 && g_begin < g_end) load_quad<PLANES>(tp, g_begin, cur);
     if (tile_ok)
       gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur);
 
@@ -581,12 +589,10 @@ int launch_one(const GemvArgs& a, hipStream_t st, const char* what, int max_bloc
   }
   const int per_iter = WAVES / a.nseg;
   const int iters = ((a.N + 15) / 16 + per_iter - 1) / per_iter;
-  // As many blocks as fit, then evened out so that every block runs the
-  // same number of tile iterations (a last, partly filled round would run
-  // at a fraction of the chip's bandwidth).
+  // As many blocks as fit at once (a whole number per CU, so no CU carries
+  // a larger share of blocks than another), at most one tile per wave group.
   const int fit = min(max_blocks, nest::resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, lds));
-  const int rounds = (iters + fit - 1) / fit;
-  const int blocks = (iters + rounds - 1) / rounds;
+  const int blocks = min(fit, iters);
   if (used) *used = blocks;
   kern<<<dim3(blocks), dim3(WAVES * 64), lds, st>>>(a);
   return nest::check_launch(what);
@@ -594,7 +600,10 @@ int launch_one(const GemvArgs& a, hipStream_t st, const char* what, int max_bloc
 
 template <int PLANES, int MR, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
 int launch_waves(const GemvArgs& a, hipStream_t st, const char* what, int max_blocks, int* used) {
-  if (ARGMAX || a.nseg <= 4)
+  // the exact-fold argmax GEMVs (one tile per wave) run 8 waves per block:
+  // fewer blocks to dispatch and to stage activations for
+  if constexpr (ARGMAX) return launch_one<PLANES, MR, 8, ARGMAX, DBG, A4, LDSACT, XQ>(a, st, what, max_blocks, used);
+  if (a.nseg <= 4)
     return launch_one<PLANES, MR, 4, ARGMAX, DBG, A4, LDSACT, XQ>(a, st, what, max_blocks, used);
   if constexpr (!ARGMAX) {
     if (PLANES == 2 || a.nseg == 8)

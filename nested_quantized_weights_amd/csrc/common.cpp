@@ -66,3 +66,32 @@ int resident_blocks(const void* kernel, int threads, size_t dyn_lds) {
 }
 
 }  // namespace nest
+
+namespace nest {
+
+namespace {
+std::mutex g_counter_mu;
+}
+
+unsigned* stream_counter(hipStream_t stream) {
+  // One zeroed word per (device, stream). Kernels on one stream run one
+  // after another, and a kernel that counts its blocks with it leaves it at
+  // zero when it ends, so two running kernels never share one.
+  static std::map<std::pair<int, hipStream_t>, unsigned*> slots;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_counter_mu);
+  const auto key = std::make_pair(dev, stream);
+  auto it = slots.find(key);
+  if (it != slots.end()) return it->second;
+  void* p = nullptr;
+  if (hipMalloc(&p, 256) != hipSuccess) return nullptr;
+  if (hipMemset(p, 0, 256) != hipSuccess) {
+    (void)hipFree(p);
+    return nullptr;
+  }
+  slots[key] = static_cast<unsigned*>(p);
+  return static_cast<unsigned*>(p);
+}
+
+}  // namespace nest

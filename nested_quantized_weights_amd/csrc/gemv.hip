@@ -43,6 +43,18 @@ constexpr int kMaxArgmaxBlocks = 4096;
 constexpr int kLdsActMax = 48 * 1024;     // largest M*K staged in LDS from int8 activations
 constexpr int kLdsActMaxX = 128 * 1024;   // largest M*K the fp32-activation path stages
 
+struct FinishArgs {
+  const unsigned long long* partials;
+  int nparts, M;
+  int32_t* argmax_out;  // draft: [M]
+  int B, k;             // accept: B sequences of k+1 rows
+  const int32_t* draft;
+  int32_t* target;
+  int32_t* n_emitted;
+  int32_t* emitted;
+  bool accept;  // apply the greedy accept rule (else write argmax_out)
+};
+
 struct GemvArgs {
   const int8_t* qa;
   const float* sa;
@@ -55,18 +67,10 @@ struct GemvArgs {
   float* y;
   int32_t* acc_dbg;
   unsigned long long* partials;  // argmax: [gridDim.x][16]
+  unsigned* done;                // argmax: finished-block counter (zero at launch), or null
+  FinishArgs fin;                // argmax with done: what the last block writes
 };
 
-struct FinishArgs {
-  const unsigned long long* partials;
-  int nparts, M;
-  int32_t* argmax_out;  // draft: [M]
-  int B, k;             // accept: B sequences of k+1 rows
-  const int32_t* draft;
-  int32_t* target;
-  int32_t* n_emitted;
-  int32_t* emitted;
-};
 
 // LDS slot of the even (p = 0) or odd (p = 1) operand of activation row m,
 // k-quarter kq, group g.
@@ -495,20 +499,47 @@ gemv_kernel(GemvArgs a) {
     if (threadIdx.x < 16) {
       unsigned long long k = 0;
       for (int w = 0; w < WAVES; ++w) k = umax64(k, bw[w][threadIdx.x]);
-      a.partials[static_cast<size_t>(blockIdx.x) * 16 + threadIdx.x] = k;
+      unsigned long long* slot = a.partials + static_cast<size_t>(blockIdx.x) * 16 + threadIdx.x;
+      if (a.done)
+        __hip_atomic_store(slot, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *slot = k;
+    }
+    if (a.done) {
+      // The last block to finish reduces every block's keys. Keys go out
+      // with device-scope stores, and each block waits for its stores to
+      // complete before it counts itself done, so the last block (which
+      // reads them with device-scope loads) sees all of them; it then
+      // leaves the counter at zero for the next launch on the stream.
+      __shared__ int last_sh;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) last_sh = atomicAdd(a.done, 1u) == gridDim.x - 1;
+      __syncthreads();
+      if (last_sh) {
+        FinishArgs f = a.fin;
+        f.partials = a.partials;
+        f.nparts = gridDim.x;
+        f.M = a.M;
+        finish_reduce<WAVES * 64, true>(f);
+        if (threadIdx.x == 0) atomicExch(a.done, 0u);
+      }
     }
   }
 }
 
-// Reduce the per-block argmax keys; ACCEPT also applies the accept rule.
-// One block of 1024 threads. Thread t reads the keys of blocks t, t + 1024,
-// ... for the M live rows, all loads issued before any is used, so the
-// kernel waits for one round trip to memory. Rows are then reduced per
-// wave (shuffles) and across the 16 waves (LDS).
-template <bool ACCEPT>
-__global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
-  constexpr int kPer = kMaxArgmaxBlocks / 1024;
-  __shared__ unsigned long long red[16][16];
+// Reduce the per-block argmax keys of f.partials (f.nparts blocks, f.M live
+// rows) and write the argmaxes, or apply the greedy accept rule (f.accept).
+// NT threads; thread t reads the keys of blocks t, t + NT, ..., all loads
+// issued before any is used, so the reduction waits for one round trip to
+// memory. Rows are then reduced per wave (shuffles) and across the waves
+// (LDS). COHERENT: the keys were written by other blocks of the running
+// kernel with device-scope stores and are read with device-scope loads
+// (past the non-coherent per-XCD caches).
+template <int NT, bool COHERENT>
+__device__ void finish_reduce(const FinishArgs& f) {
+  constexpr int kPer = kMaxArgmaxBlocks / NT, kW = NT / 64;
+  __shared__ unsigned long long red[16][kW];
   __shared__ int32_t tgt[16];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int nv = (f.M + 1) >> 1;  // 16-byte pairs of keys per block
@@ -517,15 +548,23 @@ __global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
   for (int r = 0; r < 16; ++r) best[r] = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int b = t + j * 1024;
+    const int b = t + j * NT;
     if (b < f.nparts) {
-      const uint4* p = reinterpret_cast<const uint4*>(f.partials + static_cast<size_t>(b) * 16);
+      const unsigned long long* p = f.partials + static_cast<size_t>(b) * 16;
+      if (COHERENT) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < nv) {
-          const uint4 w = p[i];
-          best[2 * i] = umax64(best[2 * i], (static_cast<unsigned long long>(w.y) << 32) | w.x);
-          best[2 * i + 1] = umax64(best[2 * i + 1], (static_cast<unsigned long long>(w.w) << 32) | w.z);
+        for (int i = 0; i < 16; ++i)
+          if (i < f.M)
+            best[i] = umax64(best[i], __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      } else {
+        const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < nv) {
+            const uint4 w = p4[i];
+            best[2 * i] = umax64(best[2 * i], (static_cast<unsigned long long>(w.y) << 32) | w.x);
+            best[2 * i + 1] = umax64(best[2 * i + 1], (static_cast<unsigned long long>(w.w) << 32) | w.z);
+          }
         }
       }
     }
@@ -542,15 +581,15 @@ __global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
   __syncthreads();
   if (t < f.M) {
     unsigned long long k = 0;
-    for (int w = 0; w < 16; ++w) k = umax64(k, red[t][w]);
+    for (int w = 0; w < kW; ++w) k = umax64(k, red[t][w]);
     tgt[t] = static_cast<int32_t>(argmax_key_index(k));
-    if (!ACCEPT) f.argmax_out[t] = tgt[t];
+    if (!f.accept) f.argmax_out[t] = tgt[t];
   }
   __syncthreads();
-  if (ACCEPT && threadIdx.x < f.B) {
+  if (f.accept && t < f.B) {
     // One thread per sequence: slot i's draft d_i is checked against
     // t_{i-1}; the first mismatch ends the round.
-    const int b = threadIdx.x, k1 = f.k + 1;
+    const int b = t, k1 = f.k + 1;
     int acc = 0;
     while (acc < f.k && f.draft[b * f.k + acc] == tgt[b * k1 + acc]) ++acc;
     f.n_emitted[b] = acc + 1;
@@ -560,6 +599,10 @@ __global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) {
     }
   }
 }
+
+// The finishing step as its own launch (one block of 1024 threads), for
+// when no block counter is available.
+__global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) { finish_reduce<1024, false>(f); }
 
 // ---------------------------------------------------------------------------
 // host side
@@ -650,17 +693,22 @@ size_t argmax_ws_bytes(int N) {
 template <int PLANES, bool DBG>
 int launch_argmax(GemvArgs a, const FinishArgs& f0, bool accept, hipStream_t st, const char* what) {
   a.nseg = 1;
+  FinishArgs f = f0;
+  f.accept = accept;
+  // with a block counter the GEMV's last block finishes the reduction;
+  // otherwise a second launch does
+  a.done = nest::stream_counter(st);
+  if (a.done) {
+    a.fin = f;
+    return launch_gemv<PLANES, true, DBG>(a, st, what, kMaxArgmaxBlocks, nullptr);
+  }
   int used = 0;
   int rc = launch_gemv<PLANES, true, DBG>(a, st, what, kMaxArgmaxBlocks, &used);
   if (rc) return rc;
-  FinishArgs f = f0;
   f.partials = a.partials;
   f.nparts = used;
   f.M = a.M;
-  if (accept)
-    argmax_finish_kernel<true><<<1, 1024, 0, st>>>(f);
-  else
-    argmax_finish_kernel<false><<<1, 1024, 0, st>>>(f);
+  argmax_finish_kernel<<<1, 1024, 0, st>>>(f);
   return nest::check_launch(what);
 }
 

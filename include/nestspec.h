@@ -207,8 +207,11 @@ size_t draft_gemv_workspace_size(int64_t M, int64_t N);
  * fewer.
  *   x        fp32 [M][K], 16-byte aligned
  *   the rest as for draft_gemv (no debug accumulators)
- * Requires 1 <= M <= 16 and M*K <= 131072 (the activation codes are held in
- * LDS); larger activations go through nest_act_quant and draft_gemv.
+ * Requires 1 <= M <= 16. Activations with M*K > 131072 (beyond the LDS
+ * budget for codes), and several rows that many blocks would each quantize
+ * again (N*M*K >= 1.2e8, M >= 2), are quantized once by a nest_act_quant
+ * launch into a buffer the library keeps per stream (allocated on first
+ * use, grown on demand); the codes are the same either way.
  * Errors: as draft_gemv. */
 int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
                  const float* scales, int64_t N, int64_t group, float* y,
@@ -230,8 +233,10 @@ int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                 void* stream);
 
 /* verify_gemm_x -- verify_gemm on fp32 activations, quantized in the kernel
- * as for draft_gemv_x (bit-identical to nest_act_quant + verify_gemm).
- * Requires 1 <= M <= 16 and M*K <= 131072. Errors: as verify_gemm. */
+ * as for draft_gemv_x (bit-identical to nest_act_quant + verify_gemm), or
+ * first quantized into the library's per-stream buffer under the same rule
+ * (always when M > 16, which then runs the batched kernel).
+ * Requires M >= 1. Errors: as verify_gemm. */
 int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
                   const uint8_t* refine, const float* scales, int64_t N,
                   int64_t group, float* y, void* stream);
@@ -266,8 +271,9 @@ size_t verify_accept_workspace_size(int64_t B, int64_t k, int64_t V);
 
 /* verify_accept_x -- verify_accept on fp32 activations x [B*(k+1)][K]
  * (16-byte aligned), quantized in the kernel as for draft_gemv_x
- * (bit-identical to nest_act_quant + verify_accept). Requires
- * B*(k+1)*K <= 131072. Errors: as verify_accept. */
+ * (bit-identical to nest_act_quant + verify_accept); when
+ * B*(k+1)*K > 131072 the activations are first quantized into the
+ * library's per-stream buffer. Errors: as verify_accept. */
 int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K,
                     const uint8_t* base, const uint8_t* refine,
                     const float* scales, int64_t V, int64_t group,

@@ -95,3 +95,34 @@ unsigned* stream_counter(hipStream_t stream) {
 }
 
 }  // namespace nest
+
+namespace nest {
+
+namespace {
+std::mutex g_scratch_mu;
+}
+
+void* stream_scratch(hipStream_t stream, size_t bytes) {
+  // One buffer per (device, stream), grown on demand and kept until the
+  // process ends. Calls on one stream run in order, so each call's use of
+  // it ends before the next call's begins; before a smaller buffer is
+  // replaced, the stream is drained (work queued on it may still read it).
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> bufs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto& e = bufs[std::make_pair(dev, stream)];
+  if (e.first && e.second >= bytes) return e.first;
+  if (e.first) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return nullptr;
+    (void)hipFree(e.first);
+    e = {nullptr, 0};
+  }
+  size_t n = bytes < (size_t{1} << 20) ? (size_t{1} << 20) : bytes;
+  void* p = nullptr;
+  if (hipMalloc(&p, n) != hipSuccess) return nullptr;
+  e = {p, n};
+  return p;
+}
+
+}  // namespace nest

@@ -734,14 +734,39 @@ int check_common(const char* what, const Act& act, int64_t M, int64_t K, const u
     return nest::fail(NEST_EALIGN, "%s: planes and scales must be 16-byte aligned", what);
   if (act.x) {
     if (!nest::aligned16(act.x)) return nest::fail(NEST_EALIGN, "%s: x must be 16-byte aligned", what);
-    if (M > 16 || M * K > kLdsActMaxX)
-      return nest::fail(NEST_EUNSUPPORTED,
-                        "%s: M=%lld K=%lld exceeds the in-kernel quantization limit (M <= 16, "
-                        "M*K <= %d); use nest_act_quant and the int8 entry point",
-                        what, (long long)M, (long long)K, kLdsActMaxX);
   } else if (!nest::aligned16(act.qa)) {
     return nest::fail(NEST_EALIGN, "%s: qa must be 16-byte aligned", what);
   }
+  return NEST_OK;
+}
+
+// fp32 activations are quantized inside the GEMV when they fit its LDS
+// budget. A separate nest_act_quant launch into library scratch (per
+// stream) comes first when they do not fit, or when several rows would be
+// quantized again by each of many blocks (N*M*K at least kQuantFirst:
+// there one launch is cheaper than the blocks' staging; measured on the
+// 5- and 9-row verify of 3584x37888 and 18944x3584 linears). The codes
+// are the same either way.
+constexpr double kQuantFirst = 1.2e8;
+
+int quantize_first(const char* what, Act& act, int64_t M, int64_t K, int64_t N, hipStream_t st,
+                   bool by_size) {
+  if (!act.x) return NEST_OK;
+  const bool fits = M <= 16 && M * K <= kLdsActMaxX;
+  const bool heavy = by_size && M >= 2 && static_cast<double>(N) * M * K >= kQuantFirst;
+  if (fits && !heavy) return NEST_OK;
+  const size_t qbytes = (static_cast<size_t>(M) * K + 255) & ~static_cast<size_t>(255);
+  void* p = nest::stream_scratch(st, qbytes + static_cast<size_t>(M) * sizeof(float));
+  if (!p) {
+    if (fits) return NEST_OK;  // stay with the in-kernel path
+    return nest::fail(NEST_EHIP, "%s: cannot allocate %lld x %lld activation codes", what, (long long)M,
+                      (long long)K);
+  }
+  int8_t* qa = static_cast<int8_t*>(p);
+  float* sa = reinterpret_cast<float*>(static_cast<char*>(p) + qbytes);
+  const int rc = nest_act_quant(act.x, M, K, qa, sa, st);
+  if (rc) return rc;
+  act = Act{qa, sa, nullptr};
   return NEST_OK;
 }
 
@@ -768,8 +793,11 @@ int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uin
   if (rc) return rc;
   if (M > 16) return nest::fail(NEST_EUNSUPPORTED, "%s: M=%lld > 16", what, (long long)M);
   if (!y && !argmax) return nest::fail(NEST_EINVAL, "%s: need y or argmax", what);
-  GemvArgs a = make_args(act, M, K, base, nullptr, scales, N, y, acc_dbg);
   hipStream_t st = nest::as_stream(stream);
+  Act act2 = act;
+  rc = quantize_first(what, act2, M, K, N, st, true);
+  if (rc) return rc;
+  GemvArgs a = make_args(act2, M, K, base, nullptr, scales, N, y, acc_dbg);
   if (argmax) {
     rc = check_ws(what, ws, ws_bytes, a.N);
     if (rc) return rc;
@@ -792,8 +820,11 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
   if (!refine || !y) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "%s: refine not 16-byte aligned", what);
   hipStream_t st = nest::as_stream(stream);
+  Act act2 = act;
+  rc = quantize_first(what, act2, M, K, N, st, true);
+  if (rc) return rc;
   if (M <= 16) {
-    GemvArgs a = make_args(act, M, K, base, refine, scales, N, y, acc_dbg);
+    GemvArgs a = make_args(act2, M, K, base, refine, scales, N, y, acc_dbg);
     a.nseg = pick_split((a.N + 15) / 16, a.G, max_split(2));
     return acc_dbg ? launch_gemv<2, false, true>(a, st, what, 1 << 30, nullptr)
                    : launch_gemv<2, false, false>(a, st, what, 1 << 30, nullptr);
@@ -801,7 +832,7 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
   // More rows (int8 activations only): the batched kernel, in chunks of up to 144 rows.
   for (int64_t m0 = 0; m0 < M; m0 += 144) {
     const int64_t mc = M - m0 < 144 ? M - m0 : 144;
-    rc = nest::launch_verify_batched(act.qa + m0 * K, act.sa + m0, (int)mc, (int)K, base, refine, scales,
+    rc = nest::launch_verify_batched(act2.qa + m0 * K, act2.sa + m0, (int)mc, (int)K, base, refine, scales,
                                      (int)N, y + m0 * N,
                                      acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, st);
     if (rc) return rc;
@@ -824,12 +855,16 @@ int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t 
   if (V > 0x7fffffffLL) return nest::fail(NEST_EUNSUPPORTED, "%s: V too large", what);
   rc = check_ws(what, ws, ws_bytes, (int)V);
   if (rc) return rc;
-  GemvArgs a = make_args(act, B * (k + 1), K, base, refine, scales, V, y, nullptr);
+  hipStream_t st = nest::as_stream(stream);
+  Act act2 = act;  // the LM head stays with in-kernel quantization whenever it fits
+  rc = quantize_first(what, act2, B * (k + 1), K, V, st, false);
+  if (rc) return rc;
+  GemvArgs a = make_args(act2, B * (k + 1), K, base, refine, scales, V, y, nullptr);
   a.partials = static_cast<unsigned long long*>(ws);
   FinishArgs f{};
   f.B = (int)B; f.k = (int)k; f.draft = draft; f.target = target; f.n_emitted = n_emitted;
   f.emitted = emitted;
-  return launch_argmax<2, false>(a, f, true, nest::as_stream(stream), what);
+  return launch_argmax<2, false>(a, f, true, st, what);
 }
 
 }  // namespace

@@ -120,12 +120,23 @@ def test_verify_accept_x(ns, oracle, V, K, B, k, alpha):
         assert np.array_equal(host(g["y"]).view(np.uint32), o["y"].view(np.uint32))
 
 
-def test_fused_limit_is_an_error(ns):
-    x = torch.zeros((16, 8320), dtype=torch.float32, device="cuda")  # 16 * 8320 > 131072
-    W = ns.nest_tile(torch.zeros((16, 4160), dtype=torch.uint8, device="cuda"), None,
-                     torch.zeros((16, 65), dtype=torch.float32, device="cuda"))
-    with pytest.raises(ns.NestError, match="in-kernel quantization limit"):
-        ns.draft_gemv_x(x, W)
+def test_large_activations_are_quantized_first(ns, oracle):
+    # beyond the in-kernel limit (M*K > 131072), or M > 16 for the verify, the
+    # call quantizes once into library scratch; the result is the int8 path's
+    # bit for bit
+    for M, K, N, planes in ((16, 8320, 40, 1), (16, 8320, 40, 2), (20, 1024, 300, 2), (9, 18944, 64, 2)):
+        w = synth.weights(N, K, (309, M, K))
+        x = synth.activations(M, K, (310, M, K))
+        base, refine, scales = oracle.nest_pack(w)
+        qa, sa = oracle.act_quant(x)
+        W = tiled(ns, base, refine if planes == 2 else None, scales)
+        if planes == 1:
+            y = host(ns.draft_gemv_x(dev(x), W))
+            y8 = host(ns.draft_gemv(dev(qa), dev(sa), W))
+        else:
+            y = host(ns.verify_gemm_x(dev(x), W))
+            y8 = host(ns.verify_gemm(dev(qa), dev(sa), W))
+        assert np.array_equal(y.view(np.uint32), y8.view(np.uint32)), (M, K, N, planes)
     x1 = torch.zeros(132, dtype=torch.float32, device="cuda")[1:129].view(1, 128)  # 4-byte offset
     W1 = ns.nest_tile(torch.zeros((16, 64), dtype=torch.uint8, device="cuda"), None,
                       torch.zeros((16, 1), dtype=torch.float32, device="cuda"))

@@ -185,23 +185,28 @@ __device__ __forceinline__ void stage_x_finish(const float* __restrict__ x, int 
                                                  fmaxf(absmax4(src[2]), absmax4(src[3])))));
   }
   __syncthreads();
+  // every thread derives the scales it needs from the row maxima itself
+  // (the same IEEE operations, so the same values everywhere); thread m
+  // also records row m's for the fold
+  auto scale = [&](int m) { return __uint_as_float(amax_sh[m]) / 127.0f; };
   if (t < M) {
-    const float s = __uint_as_float(amax_sh[t]) / 127.0f;
+    const float s = scale(t);
     sa_sh[t] = s;
     sa_sh[16 + t] = 1.0f / s;
   }
-  __syncthreads();
   uint2* lds2 = reinterpret_cast<uint2*>(lds);
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j)
-    if (it.row[j] >= 0)
-      store_item(lds2, M, it.row[j], t + j * NT - it.row[j] * ipr, it.v[j], sa_sh[it.row[j]],
-                 sa_sh[16 + it.row[j]]);
+    if (it.row[j] >= 0) {
+      const float s = scale(it.row[j]);
+      store_item(lds2, M, it.row[j], t + j * NT - it.row[j] * ipr, it.v[j], s, 1.0f / s);
+    }
   for (int h = t + ITEMS * NT; h < total; h += NT) {
     const int m = h / ipr;
     const float4* src = reinterpret_cast<const float4*>(x + static_cast<size_t>(m) * K) + 4 * (h - m * ipr);
     const float4 w[4] = {src[0], src[1], src[2], src[3]};
-    store_item(lds2, M, m, h - m * ipr, w, sa_sh[m], sa_sh[16 + m]);
+    const float s = scale(m);
+    store_item(lds2, M, m, h - m * ipr, w, s, 1.0f / s);
   }
   __syncthreads();
 }

@@ -369,16 +369,41 @@ __device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds
   }
 }
 
+// The same with two quads in flight: cur holds the quad at g0 and nxt the
+// one at g0 + 4 (when it exists), both already requested; the quad two
+// ahead is requested while cur is multiplied. Used by the one-plane argmax
+// GEMV, whose waves take two or three whole tiles each: in the last third
+// of a launch only the three-tile waves still stream, and the deeper queue
+// keeps enough bytes in flight per CU for them.
+template <int PLANES, int MR, bool DBG, bool LDSACT>
+__device__ __forceinline__ void gemv_segment2(const GemvArgs& a, const uint4* lds, const TilePtr& tp,
+                                              const int8_t* pa, int kq, int mrow, int n, int g0, int g1,
+                                              float (&run)[MR], Quad& cur, Quad& nxt) {
+  for (int g = g0; g < g1; g += 4) {
+    Quad q;
+    const bool more = g + 8 < g1;
+    if (more) load_quad<PLANES>(tp, g + 8, q);
+    gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, cur.b0, cur.r0, cur.s.x, run);
+    gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 1, cur.b1, cur.r1, cur.s.y, run);
+    gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 2, cur.b2, cur.r2, cur.s.z, run);
+    gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 3, cur.b3, cur.r3, cur.s.w, run);
+    cur = nxt;
+    if (more) nxt = q;
+  }
+}
+
 // WAVES waves per block; a tile takes nseg consecutive waves (nseg | WAVES).
 // ARGMAX requires nseg == 1. XQ: fp32 activations, quantized while staging
 // (requires LDSACT). The first quad of each wave's first tile is requested
 // before the activations are staged, so staging overlaps the first HBM
 // round trip of the weights.
 // Waves per SIMD the register allocation must allow. The streams need
-// enough waves in flight; the targets are the largest that compile without
-// spills for each fold (the debug build is left unconstrained).
+// enough bytes in flight; the targets are the largest that compile without
+// spills for each fold (the one-row, one-plane fold trades a fourth wave
+// for a second quad in flight, measured faster; the debug build is left
+// unconstrained).
 constexpr int occupancy_target(int planes, int mr, bool dbg) {
-  return dbg ? 1 : planes == 2 ? 3 : 4;
+  return dbg ? 1 : (planes == 2 || mr == 1) ? 3 : 4;
 }
 
 template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
@@ -421,8 +446,13 @@ gemv_kernel(GemvArgs a) {
 
   // branch-free first quad: tile and group clamped into range; it is only
   // used when this wave's first tile exists and its segment is not empty
-  Quad cur;
-  if (A4) load_quad<PLANES>(tile_ptr<PLANES>(a, min(t_lo, T - 1), kq, c), min(g_begin, G - 4), cur);
+  constexpr bool kDeep = ARGMAX && PLANES == 1 && A4 && !DBG;
+  Quad cur, nxt;
+  if (A4) {
+    const TilePtr tp0 = tile_ptr<PLANES>(a, min(t_lo, T - 1), kq, c);
+    load_quad<PLANES>(tp0, min(g_begin, G - 4), cur);
+    if (kDeep) load_quad<PLANES>(tp0, min(g_begin + 4, G - 4), nxt);
+  }
 
   __shared__ float sa_sh[32];  // [0, 16): s_a per row; [16, 32): 1 / s_a
   __shared__ unsigned amax_sh[16];
@@ -445,9 +475,16 @@ gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < MR; ++r) run[r] = 0.0f;
     // the first tile's first quad was requested before staging
-    if (A4 && tile_ok && j != 0 && g_begin < g_end) load_quad<PLANES>(tp, g_begin, cur);
-    if (tile_ok)
-      gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur);
+    if (A4 && tile_ok && j != 0 && g_begin < g_end) {
+      load_quad<PLANES>(tp, g_begin, cur);
+      if (kDeep && g_begin + 4 < g_end) load_quad<PLANES>(tp, g_begin + 4, nxt);
+    }
+    if (tile_ok) {
+      if constexpr (kDeep)
+        gemv_segment2<PLANES, MR, DBG, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur, nxt);
+      else
+        gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur);
+    }
 
     if (ARGMAX) {
       if (tile_ok && n < a.N) {

@@ -369,26 +369,27 @@ __device__ __forceinline__ void gemv_segment(const GemvArgs& a, const uint4* lds
   }
 }
 
-// The same with two quads in flight: cur holds the quad at g0 and nxt the
-// one at g0 + 4 (when it exists), both already requested; the quad two
-// ahead is requested while cur is multiplied. Used by the one-plane argmax
-// GEMV, whose waves take two or three whole tiles each: in the last third
-// of a launch only the three-tile waves still stream, and the deeper queue
-// keeps enough bytes in flight per CU for them.
-template <int PLANES, int MR, bool DBG, bool LDSACT>
-__device__ __forceinline__ void gemv_segment2(const GemvArgs& a, const uint4* lds, const TilePtr& tp,
-                                              const int8_t* pa, int kq, int mrow, int n, int g0, int g1,
-                                              float (&run)[MR], Quad& cur, Quad& nxt) {
+// The same with D quads in flight: q[i] holds the quad at g0 + 4i (when it
+// exists), all already requested; the quad D ahead is requested while q[0]
+// is multiplied. Used by the argmax GEMVs, whose waves take two or three
+// whole tiles each: in the last third of a launch only the three-tile waves
+// still stream, and the deeper queue keeps enough bytes in flight per CU.
+template <int PLANES, int MR, bool DBG, bool LDSACT, int D>
+__device__ __forceinline__ void gemv_segment_d(const GemvArgs& a, const uint4* lds, const TilePtr& tp,
+                                               const int8_t* pa, int kq, int mrow, int n, int g0, int g1,
+                                               float (&run)[MR], Quad (&qs)[D]) {
   for (int g = g0; g < g1; g += 4) {
     Quad q;
-    const bool more = g + 8 < g1;
-    if (more) load_quad<PLANES>(tp, g + 8, q);
+    const bool more = g + 4 * D < g1;
+    if (more) load_quad<PLANES>(tp, g + 4 * D, q);
+    const Quad& cur = qs[0];
     gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g, cur.b0, cur.r0, cur.s.x, run);
     gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 1, cur.b1, cur.r1, cur.s.y, run);
     gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 2, cur.b2, cur.r2, cur.s.z, run);
     gemv_group<PLANES, MR, DBG, LDSACT>(a, lds, pa, kq, mrow, n, g + 3, cur.b3, cur.r3, cur.s.w, run);
-    cur = nxt;
-    if (more) nxt = q;
+#pragma unroll
+    for (int i = 0; i + 1 < D; ++i) qs[i] = qs[i + 1];
+    if (more) qs[D - 1] = q;
   }
 }
 
@@ -402,8 +403,13 @@ __device__ __forceinline__ void gemv_segment2(const GemvArgs& a, const uint4* ld
 // spills for each fold (the one-row, one-plane fold trades a fourth wave
 // for a second quad in flight, measured faster; the debug build is left
 // unconstrained).
+// Quads in flight per wave for the argmax GEMVs (see gemv_segment_d): two
+// for one plane; the two-plane fold keeps one (a second, at two waves per
+// SIMD, measured no faster), and three for one plane was slower.
+constexpr int prefetch_depth(int planes) { return planes == 1 ? 2 : 1; }
+
 constexpr int occupancy_target(int planes, int mr, bool dbg) {
-  return dbg ? 1 : (planes == 2 || mr == 1) ? 3 : 4;
+  return dbg ? 1 : planes == 2 ? 3 : mr == 1 ? 3 : 4;
 }
 
 template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
@@ -446,12 +452,13 @@ gemv_kernel(GemvArgs a) {
 
   // branch-free first quad: tile and group clamped into range; it is only
   // used when this wave's first tile exists and its segment is not empty
-  constexpr bool kDeep = ARGMAX && PLANES == 1 && A4 && !DBG;
-  Quad cur, nxt;
+  constexpr int kDepth = (ARGMAX && A4 && !DBG) ? prefetch_depth(PLANES) : 1;
+  Quad qs[kDepth];
+  Quad& cur = qs[0];
   if (A4) {
     const TilePtr tp0 = tile_ptr<PLANES>(a, min(t_lo, T - 1), kq, c);
-    load_quad<PLANES>(tp0, min(g_begin, G - 4), cur);
-    if (kDeep) load_quad<PLANES>(tp0, min(g_begin + 4, G - 4), nxt);
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) load_quad<PLANES>(tp0, min(g_begin + 4 * i, G - 4), qs[i]);
   }
 
   __shared__ float sa_sh[32];  // [0, 16): s_a per row; [16, 32): 1 / s_a
@@ -476,12 +483,13 @@ gemv_kernel(GemvArgs a) {
     for (int r = 0; r < MR; ++r) run[r] = 0.0f;
     // the first tile's first quad was requested before staging
     if (A4 && tile_ok && j != 0 && g_begin < g_end) {
-      load_quad<PLANES>(tp, g_begin, cur);
-      if (kDeep && g_begin + 4 < g_end) load_quad<PLANES>(tp, g_begin + 4, nxt);
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i)
+        if (g_begin + 4 * i < g_end) load_quad<PLANES>(tp, g_begin + 4 * i, qs[i]);
     }
     if (tile_ok) {
-      if constexpr (kDeep)
-        gemv_segment2<PLANES, MR, DBG, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur, nxt);
+      if constexpr (kDepth > 1)
+        gemv_segment_d<PLANES, MR, DBG, LDSACT, kDepth>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, qs);
       else
         gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur);
     }

@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
 template <int VIEW>
 __global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
   __shared__ float ml[4][16][2];
-  __shared__ float buf[16][kD + 4];
+  __shared__ float buf[4][16][kD + 4];  // each wave's rescaled O
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int h = blockIdx.y, chunk = blockIdx.x;
@@ -457,24 +457,22 @@ __global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
   for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w][c16][0]);
   const float Mu = M == -INFINITY ? 0.0f : M;
   const float f = exp2f(m - Mu);
-  for (int step = 3; step >= 0; --step) {
-    if (wave == step) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float* p = &buf[c16][dt * 16 + 4 * q4 + i];
-          const float v = O[dt][i] * f;
-          *p = step == 3 ? v : *p + v;
-        }
-    }
-    __syncthreads();
-  }
+    for (int i = 0; i < 4; ++i) buf[wave][c16][dt * 16 + 4 * q4 + i] = O[dt][i] * f;
+  __syncthreads();
+  // the four waves' parts added in the fixed order w = 3 .. 0
   const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;
   for (int idx = threadIdx.x; idx < a.R * (kD / 4); idx += 256) {
     const int row = idx / (kD / 4), d4 = idx % (kD / 4);
-    *reinterpret_cast<float4*>(&a.part_o[(pbase + row) * kD + 4 * d4]) =
-        *reinterpret_cast<const float4*>(&buf[row][4 * d4]);
+    float4 v = *reinterpret_cast<const float4*>(&buf[3][row][4 * d4]);
+#pragma unroll
+    for (int w = 2; w >= 0; --w) {
+      const float4 u = *reinterpret_cast<const float4*>(&buf[w][row][4 * d4]);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    *reinterpret_cast<float4*>(&a.part_o[(pbase + row) * kD + 4 * d4]) = v;
   }
   if (threadIdx.x < a.R) {
     const int row = threadIdx.x;

@@ -26,11 +26,17 @@
  * Conventions for every entry point
  * ---------------------------------------------------------------------------
  *  - Every buffer pointer is a DEVICE pointer unless the argument says
- *    "host". The caller allocates and owns every buffer. The library never
- *    allocates, frees or keeps a buffer.
+ *    "host". The caller allocates and owns every buffer it passes.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call enqueues its kernels on that stream and returns without
  *    synchronising.
+ *  - The library keeps two pieces of device memory of its own per (device,
+ *    stream), allocated on first use and held until the process ends: a
+ *    256-byte block counter for the argmax GEMVs (left at zero by every
+ *    launch) and the buffer of the fp32 entry points that quantize first
+ *    (grown on demand; growing it synchronises that stream). Calls on one
+ *    stream run in order and so share them safely; hipStreamPerThread is
+ *    told apart by the calling host thread.
  *  - Arguments are checked on the host before anything is launched. On an
  *    error nothing is launched, the return value is a nest_status code, and
  *    nest_last_error() holds a message for the calling thread. A launch

@@ -97,10 +97,16 @@ __global__ void __launch_bounds__(1024) act_quant_kernel(const float* __restrict
   if (PER > 0) {
     float4 v[PER > 0 ? PER : 1];
     float m = 0.0f;
+    // clamped, branch-free loads: all PER of them are in flight together
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int64_t e = (static_cast<int64_t>(i) * 1024 + threadIdx.x) * 4;
-      v[i] = e < K ? *reinterpret_cast<const float4*>(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[i] = *reinterpret_cast<const float4*>(xr + (e < K ? e : K - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t e = (static_cast<int64_t>(i) * 1024 + threadIdx.x) * 4;
+      if (e >= K) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     }
     m = block_max_1024(m, red);

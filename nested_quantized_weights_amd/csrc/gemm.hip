@@ -1,168 +1,365 @@
 // Batched verify over both planes (BitNest, Figure 3: the target reads the
 // base and the refinement plane) for more than 16 activation rows, e.g. 16
-// sequences x (k+1) = 144 rows.
+// sequences x (k+1) = 144 rows: y = sa * fold_g s/16 * (sum q_a (16 q_b + q_r)).
 //
-// One wave owns a 16-row weight tile in the tile layout (the MFMA A operand:
-// row lane & 15, k-quarter lane >> 4; one contiguous kilobyte per group) and
-// all CT 16-row column tiles of activations. Per
-// group, the plane bytes are unpacked once and reused for every column
-// tile: two v_mfma_i32_16x16x64_i8 per plane and tile. The fp32 fold stays
-// in registers, one run per (column tile, row) entry, in ascending group
-// order. A block of four waves may split a tile's groups into S <= 4
-// contiguous segments, whose partial sums are added in segment order.
+// A block owns 64 weight rows (four 16-row tiles), a range of the
+// activation rows (CTP column tiles of 16) and all groups. Its ninth wave
+// only copies int8 activation rows from HBM/L2 into an LDS ring (direct
+// 16-byte loads to LDS, whole 128-byte rows of a group, two groups ahead).
+// The eight compute waves (two per SIMD, which hide each other's MFMA and
+// LDS latencies) each own one weight tile and one half of the groups (four
+// waves per half) and stream their plane bytes with two groups of loads in
+// flight beyond the current one. Per group the planes are merged into the
+// 8-bit verify code of each weight,
+//   c = 16 q_b + q_r = 16 (q_b - h) + (q_r mod 16),   h = [q_r < 0],
+// an exact int8 (|c| <= 120): the base nibble less the refine sign goes to
+// the high half of a byte (nibble arithmetic without borrows), the refine
+// nibble to the low half, and the bytes are put back in element order. One
+// v_mfma_i32_16x16x64_i8 pair per tile pair then gives the exact group sum
+// of q_a c; the activation operand is 16 contiguous bytes of one row. The
+// fp32 fold runs in registers in ascending group order within each half,
+// and the halves are added in group order. Matrices with few rows split
+// the activation rows over several blocks (each reads the same weights, on
+// the same XCD, so the repeats come from its L2).
+#include <algorithm>
+
 #include "nibble.h"
 
 namespace {
 
 using nest::kGroup;
 
+constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
+constexpr int kCW = 8;                   // compute waves per block (two per SIMD)
+constexpr int kWK = 2;                   // halves of the groups
+constexpr int kWR = kCW / kWK;           // compute waves per half
+constexpr int kBlockTiles = kWR * kRT;   // 16-row weight tiles per block (64 rows)
+constexpr int kThreads = (kCW + 1) * 64; // + the copy wave
+constexpr int kNBuf = 3;                 // LDS ring slots per half
+constexpr int kAhead = kNBuf - 1;        // groups the copy wave runs ahead
+constexpr int kSlots = 3;                // weight groups in flight per compute wave
+constexpr int kMaxCT = 9;                // 144 activation rows per launch
+constexpr int kXcds = 8;                 // blocks are dealt to the XCDs in turn
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 struct GemmArgs {
-  const int8_t* qa;
-  const float* sa;
-  int M, K;
+  const int8_t* qa;   // [M][K]
+  const float* sa;    // [M]
   const uint8_t* base;
   const uint8_t* refine;
   const float* scales;
-  int N, G, nseg;
-  float* y;
-  int32_t* acc_dbg;
+  float* y;           // [M][N]
+  int32_t* acc_dbg;   // [M][N][G] (DBG)
+  int M, K, N, G, T;
+  int row_blocks, parts;
 };
 
-template <int CT, bool DBG>
-__device__ __forceinline__ void gemm_group(const GemmArgs& a, const int8_t* pa, int col, int n_out0, int g,
-                                           uint4 wb, uint4 wr, float4 s, float (&run)[CT][4]) {
-  v4i wbe, wbo, wre, wro;
-  nest::split_nib(wb, wbe, wbo);
-  nest::split_nib(wr, wre, wro);
-  const float sc[4] = {s.x * 0.0625f, s.y * 0.0625f, s.z * 0.0625f, s.w * 0.0625f};
+struct WLoad {
+  uint4 b, r;
+  float s;
+};
+
+__device__ __forceinline__ void load_w(const GemmArgs& a, int t, int g, int kq, int idx, WLoad& w) {
+  // tile layout: 16 bytes of row 16t + idx, k-quarter kq of group g at
+  // ((t G + g) 4 + kq) 256 + 16 idx; the scale of that row and group at
+  // ((t Gq + g/4) 16 + idx) 4 + g%4
+  const size_t off = (static_cast<size_t>(t * a.G + g) * 4 + kq) * 256 + idx * 16;
+  w.b = nest::ldnt16(a.base + off);
+  w.r = nest::ldnt16(a.refine + off);
+  const int Gq = (a.G + 3) >> 2;
+  w.s = __builtin_nontemporal_load(a.scales + (static_cast<size_t>(t * Gq + (g >> 2)) * 16 + idx) * 4 + (g & 3));
+}
+
+// Eight elements (one word of each plane: nibble j is element 8t + j) ->
+// their verify codes c = 16 q_b + q_r as eight bytes in element order.
+__device__ __forceinline__ void merge_word(unsigned x, unsigned y, unsigned& lo, unsigned& hi) {
+  constexpr unsigned H = 0x88888888u;
+  const unsigned hv = (y >> 3) & 0x11111111u;    // refine sign -> bit 0 of its nibble
+  const unsigned d = ((x | H) - hv) ^ (~x & H);  // per nibble (q_b - sign) mod 16, no borrows
+  const unsigned e = ((d << 4) & 0xF0F0F0F0u) | (y & 0x0F0F0F0Fu);  // codes of elements 8t + 0, 2, 4, 6
+  const unsigned o = (d & 0xF0F0F0F0u) | ((y >> 4) & 0x0F0F0F0Fu);  // and of 8t + 1, 3, 5, 7
+  lo = __builtin_amdgcn_perm(o, e, 0x05010400u);  // elements 8t + 0..3
+  hi = __builtin_amdgcn_perm(o, e, 0x07030602u);  // elements 8t + 4..7
+}
+
+// A weight slot's operands for one group: the codes of elements 0..15 and
+// 16..31 of the lane's k-quarter for each tile, and the scales s/16.
+struct WOps {
+  v4i c0[kRT], c1[kRT];
+  float sc[kRT];
+};
+
+__device__ __forceinline__ void build_ops(const WLoad (&w)[kRT], WOps& o) {
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    // activation row c*16 + col (clamped; rows past M only fill unused columns)
-    const int m = min(c * 16 + col, a.M - 1);
-    const int8_t* p = pa + static_cast<size_t>(m) * a.K + static_cast<size_t>(g) * kGroup;
-    v4i xe, xo;
-    nest::split_act(nest::ld16(p), nest::ld16(p + 16), xe, xo);
-    const v4i z = {0, 0, 0, 0};
-    v4i rb = nest::mfma_i8(wbe, xe, z);
-    rb = nest::mfma_i8(wbo, xo, rb);
-    v4i rr = nest::mfma_i8(wre, xe, z);
-    rr = nest::mfma_i8(wro, xo, rr);
-    const v4i acc = rb + (rr >> 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) run[c][r] = fmaf(sc[r], static_cast<float>(acc[r]), run[c][r]);
-    if (DBG && c * 16 + col < a.M) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n_out0 + r;
-        if (n < a.N) a.acc_dbg[(static_cast<size_t>(c * 16 + col) * a.N + n) * a.G + g] = acc[r];
-      }
-    }
+  for (int rt = 0; rt < kRT; ++rt) {
+    unsigned l, h;
+    merge_word(w[rt].b.x, w[rt].r.x, l, h);
+    o.c0[rt][0] = static_cast<int>(l);
+    o.c0[rt][1] = static_cast<int>(h);
+    merge_word(w[rt].b.y, w[rt].r.y, l, h);
+    o.c0[rt][2] = static_cast<int>(l);
+    o.c0[rt][3] = static_cast<int>(h);
+    merge_word(w[rt].b.z, w[rt].r.z, l, h);
+    o.c1[rt][0] = static_cast<int>(l);
+    o.c1[rt][1] = static_cast<int>(h);
+    merge_word(w[rt].b.w, w[rt].r.w, l, h);
+    o.c1[rt][2] = static_cast<int>(l);
+    o.c1[rt][3] = static_cast<int>(h);
+    o.sc[rt] = w[rt].s * 0.0625f;
   }
 }
 
-template <int CT, bool DBG>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int S = a.nseg, per_iter = 4 / S;
-  const int T = (a.N + 15) / 16, iters = (T + per_iter - 1) / per_iter;
-  const int seg = wave % S, G = a.G;
-  const int g_begin = static_cast<int>(static_cast<long long>(seg) * G / S);
-  const int g_end = static_cast<int>(static_cast<long long>(seg + 1) * G / S);
-  const int kq = lane >> 4, col = lane & 15;
-  const int Gq = (G + 3) / 4;
-  const int8_t* pa = a.qa + kq * 32;
-  __shared__ float part[4][CT][4][64];
+// LDS slot of one group: per column tile ct, 16 rows of 128 bytes, the
+// 16-byte piece q of row r stored at position q ^ (r & 7) of that row. A
+// copy instruction then reads eight whole rows (full cache lines) and a
+// 16-lane read of one piece from 16 rows touches every bank evenly.
+__device__ __forceinline__ int act_lds_off(int ct, int r, int q) { return ct * 2048 + r * 128 + ((q ^ (r & 7)) << 4); }
 
-  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
-    const int n0 = (it * per_iter + wave / S) * 16;
-    const bool tile_ok = n0 < a.N;
-    const int n_out0 = n0 + 4 * kq;
-    // tile layout: lane (kq, col) reads 16 bytes of row n0 + col at
-    // ((t*G + g)*4 + kq)*256 + col*16; the scales of rows n0 + 4kq + r sit at
-    // ((t*Gq + g/4)*16 + 4kq + r)*4 + g%4 (padded rows and groups hold 0)
-    const size_t t = static_cast<size_t>(n0 / 16);
-    const uint8_t* pb = a.base + (t * G * 4 + kq) * 256 + col * 16;
-    const uint8_t* pr = a.refine + (t * G * 4 + kq) * 256 + col * 16;
-    const float* ps = a.scales + (t * Gq * 16 + 4 * kq) * 4;
-    float run[CT][4];
+// One group for the wave's weight tile(s) and the block's CTP column tiles:
+// lane (kq, idx) takes pieces 2kq and 2kq + 1 (elements 32 kq .. +31) of
+// row 16 ct + idx as its two A operands, and ends up with D[m][n] for
+// m = 16 ct + 4 kq + i, n = 16 t + idx. Software-pipelined over the column
+// tiles: operands are read two tiles ahead, products issued one tile ahead
+// of their fold.
+template <int CTP, bool DBG>
+__device__ __forceinline__ void gemm_group(const GemmArgs& a, const uint8_t* slot, int lane, int kq, int idx,
+                                           const int (&t)[kRT], int g, int ct0, const WOps& o,
+                                           float (&run)[kRT][CTP][4]) {
+  v4i la[3][2];
+  v4i d[2][kRT];
+  const v4i z = {0, 0, 0, 0};
+  const int off0 = act_lds_off(0, idx, 2 * kq), off1 = act_lds_off(0, idx, 2 * kq + 1);
+  auto lds = [&](int ct, int buf) {
+    la[buf][0] = *reinterpret_cast<const v4i*>(slot + ct * 2048 + off0);
+    la[buf][1] = *reinterpret_cast<const v4i*>(slot + ct * 2048 + off1);
+  };
+  auto mma = [&](int buf, int db) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+    for (int rt = 0; rt < kRT; ++rt) {
+      d[db][rt] = nest::mfma_i8(la[buf][0], o.c0[rt], z);
+      d[db][rt] = nest::mfma_i8(la[buf][1], o.c1[rt], d[db][rt]);
+    }
+  };
+  lds(0, 0);
+  if (CTP > 1) lds(1, 1);
+  mma(0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) run[c][r] = 0.0f;
-    if (tile_ok) {
-      for (int g = g_begin; g < g_end; ++g) {
-        const uint4 wb = nest::ldnt16(pb + static_cast<size_t>(g) * 1024);
-        const uint4 wr = nest::ldnt16(pr + static_cast<size_t>(g) * 1024);
-        const float* pq = ps + static_cast<size_t>(g / 4) * 64 + (g & 3);
-        const float4 s = make_float4(pq[0], pq[4], pq[8], pq[12]);
-        gemm_group<CT, DBG>(a, pa, col, n_out0, g, wb, wr, s, run);
+  for (int ct = 0; ct < CTP; ++ct) {
+    if (ct + 2 < CTP) lds(ct + 2, (ct + 2) % 3);
+    if (ct + 1 < CTP) mma((ct + 1) % 3, (ct + 1) % 2);
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        run[rt][ct][i] = fmaf(o.sc[rt], static_cast<float>(d[ct % 2][rt][i]), run[rt][ct][i]);
+      if (DBG) {
+        const int n = t[rt] * 16 + idx;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = (ct0 + ct) * 16 + 4 * kq + i;
+          if (m < a.M && n < a.N) a.acc_dbg[(static_cast<size_t>(m) * a.N + n) * a.G + g] = d[ct % 2][rt][i];
+        }
       }
     }
-    float tot[CT][4];
-    if (S > 1) {
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// LDS-only barrier for the compute waves (their weight loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The copy wave's barrier: it waits for its copies itself (vmcnt), so the
+// compiler must neither add a wait nor move memory operations across.
+__device__ __forceinline__ void copy_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int CTP, bool DBG>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
+  constexpr int SB = CTP * 2048;               // LDS bytes of one group's activations
+  constexpr int kCopies = kWK * 2 * CTP;       // copy instructions per step
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kNBuf * kWK * SB];
+
+  // blocks of one row block sit kXcds apart, i.e. on one XCD
+  const int b = static_cast<int>(blockIdx.x), P = a.parts;
+  const int rb = (b / (kXcds * P)) * kXcds + b % kXcds;
+  const int part = (b / kXcds) % P;
+  if (rb >= a.row_blocks) return;
+  const int ct0 = part * CTP;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int kq = lane >> 4, idx = lane & 15;
+  const int G = a.G;
+  const int steps = (G + kWK - 1) / kWK;
+  auto h0 = [&](int wk) { return wk * G / kWK; };  // half wk: groups [h0(wk), h0(wk + 1))
+
+  if (wave == kCW) {
+    // copy wave: group j of each half into slot j % kNBuf. Copy (ct, e)
+    // fills rows 8e .. 8e + 7 of column tile ct: lane l writes position
+    // l & 7 of row r = 8e + (l >> 3), i.e. piece (l & 7) ^ (r & 7) of
+    // activation row 16 ct + r (clamped to the last row). The group index is
+    // clamped into the half (to group 0 for an empty half), so every step
+    // issues kCopies copies.
+    const int8_t* src_l[CTP][2];
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
+    for (int c = 0; c < CTP; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[wave][c][r][lane] = run[c][r];
-      __syncthreads();
-      if (seg == 0) {
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float t = part[wave][c][r][lane];
-            for (int s2 = 1; s2 < S; ++s2) t += part[wave + s2][c][r][lane];
-            tot[c][r] = t;
-          }
+      for (int e = 0; e < 2; ++e) {
+        const int r = 8 * e + (lane >> 3);
+        src_l[c][e] = a.qa + static_cast<size_t>(min((ct0 + c) * 16 + r, a.M - 1)) * a.K +
+                      (((lane & 7) ^ (r & 7)) << 4);
       }
-      __syncthreads();
-    } else {
+    auto copy_step = [&](int j) {
+      uint8_t* slot0 = ring + (j % kNBuf) * kWK * SB;
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
+      for (int wk = 0; wk < kWK; ++wk) {
+        const int g = max(min(h0(wk) + j, h0(wk + 1) - 1), 0);
+        uint8_t* dst = slot0 + wk * SB;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tot[c][r] = run[c][r];
+        for (int c = 0; c < CTP; ++c)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            __builtin_amdgcn_global_load_lds((glb_void*)(src_l[c][e] + static_cast<size_t>(g) * kGroup),
+                                             (lds_void*)(dst + c * 2048 + e * 1024), 16, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (j < steps) copy_step(j);
+    for (int j = 0; j < steps; ++j) {
+      // step j's copies are done once at most the later step's are pending
+      if (j + kAhead - 1 < steps) wait_vm<(kAhead - 1) * kCopies>();
+      else wait_vm<0>();
+      copy_barrier();
+      if (j + kAhead < steps) copy_step(j + kAhead);
     }
-    if (seg != 0 || !tile_ok) continue;
+    wait_vm<0>();
+    copy_barrier();  // the ring is free: the halves' sums go through it
+    copy_barrier();
+    return;
+  }
+
+  const int wr = wave % kWR, wk = wave / kWR;
+  const int t_first = (rb * kWR + wr) * kRT;
+  int t[kRT];
+  bool t_ok[kRT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int m = c * 16 + col;
+  for (int rt = 0; rt < kRT; ++rt) {
+    t_ok[rt] = t_first + rt < a.T;
+    t[rt] = min(t_first + rt, a.T - 1);
+  }
+  const int ga = h0(wk), gb = h0(wk + 1);
+  float run[kRT][CTP][4];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTP; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) run[rt][ct][i] = 0.0f;
+
+  // weight loads: kSlots groups in flight, one register slot each; the
+  // loop is unrolled by kSlots so that a slot's registers are only ever
+  // refilled, never copied while their loads are in flight (group indices
+  // clamped into the half, to group 0 for an empty half: branch-free and
+  // in bounds), and every path through the loop issues the same loads
+  auto gclamp = [&](int g) { return max(min(g, gb - 1), 0); };
+  WLoad w0[kRT], w1[kRT], w2[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga), kq, idx, w0[rt]);
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + 1), kq, idx, w1[rt]);
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + 2), kq, idx, w2[rt]);
+  auto step = [&](int j, WLoad (&w)[kRT]) {
+    lds_barrier();  // step j's activations are in the ring
+    WOps o;
+    build_ops(w, o);
+    // the slot's registers are free again: request the group it serves next
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + j + kSlots), kq, idx, w[rt]);
+    if (ga + j < gb)
+      gemm_group<CTP, DBG>(a, ring + ((j % kNBuf) * kWK + wk) * SB, lane, kq, idx, t, ga + j, ct0, o, run);
+  };
+  const int full = steps - steps % kSlots;
+  for (int j = 0; j < full; j += kSlots) {
+    step(j, w0);
+    step(j + 1, w1);
+    step(j + 2, w2);
+  }
+  if (full < steps) step(full, w0);
+  if (full + 1 < steps) step(full + 1, w1);
+  lds_barrier();  // all copies landed and every wave is past the ring
+
+  // halves: wk = 1 hands its sums to wk = 0 through LDS (ring reused)
+  float* comb = reinterpret_cast<float*>(ring);
+  auto cidx = [&](int rt, int ct, int i) { return (((wr * kRT + rt) * CTP + ct) * 4 + i) * 64 + lane; };
+  if (wk == 1) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTP; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) comb[cidx(rt, ct, i)] = run[rt][ct][i];
+  }
+  lds_barrier();
+  if (wk == 1) return;
+#pragma unroll
+  for (int ct = 0; ct < CTP; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = (ct0 + ct) * 16 + 4 * kq + i;
       if (m >= a.M) continue;
       const float sm = a.sa[m];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n_out0 + r;
-        if (n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = tot[c][r] * sm;
+      for (int rt = 0; rt < kRT; ++rt) {
+        const int n = t[rt] * 16 + idx;
+        if (t_ok[rt] && n < a.N)
+          a.y[static_cast<size_t>(m) * a.N + n] = (run[rt][ct][i] + comb[cidx(rt, ct, i)]) * sm;
       }
     }
-  }
 }
 
-template <int CT, bool DBG>
-int launch(const GemmArgs& a0, hipStream_t st) {
-  GemmArgs a = a0;
-  const int tiles = (a.N + 15) / 16;
-  a.nseg = 1;
-  while (a.nseg < 4 && tiles * a.nseg < 1024 && a.G / (2 * a.nseg) >= 2) a.nseg *= 2;
-  auto kern = gemm_kernel<CT, DBG>;
-  const int per_iter = 4 / a.nseg;
-  const int iters = (tiles + per_iter - 1) / per_iter;
-  const int blocks = min(iters, nest::resident_blocks(reinterpret_cast<const void*>(kern), 256, 0));
-  kern<<<dim3(blocks), dim3(256), 0, st>>>(a);
+template <int CTP, bool DBG>
+int launch_gemm(const GemmArgs& a, int blocks, hipStream_t st) {
+  gemm_kernel<CTP, DBG><<<dim3(blocks), dim3(kThreads), 0, st>>>(a);
   return nest::check_launch("verify_gemm(batched)");
 }
 
 template <bool DBG>
-int launch_ct(const GemmArgs& a, int CT, hipStream_t st) {
-  switch (CT) {
-    case 2: return launch<2, DBG>(a, st);
-    case 3: return launch<3, DBG>(a, st);
-    case 4: return launch<4, DBG>(a, st);
-    case 5: return launch<5, DBG>(a, st);
-    case 6: return launch<6, DBG>(a, st);
-    case 7: return launch<7, DBG>(a, st);
-    case 8: return launch<8, DBG>(a, st);
-    default: return launch<9, DBG>(a, st);
+int launch_ctp(const GemmArgs& a, int ctp, int blocks, hipStream_t st) {
+  switch (ctp) {
+    case 1: return launch_gemm<1, DBG>(a, blocks, st);
+    case 2: return launch_gemm<2, DBG>(a, blocks, st);
+    case 3: return launch_gemm<3, DBG>(a, blocks, st);
+    case 4: return launch_gemm<4, DBG>(a, blocks, st);
+    case 5: return launch_gemm<5, DBG>(a, blocks, st);
+    case 6: return launch_gemm<6, DBG>(a, blocks, st);
+    case 7: return launch_gemm<7, DBG>(a, blocks, st);
+    case 8: return launch_gemm<8, DBG>(a, blocks, st);
+    default: return launch_gemm<9, DBG>(a, blocks, st);
   }
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
 }
 
 }  // namespace
@@ -170,13 +367,27 @@ int launch_ct(const GemmArgs& a, int CT, hipStream_t st) {
 namespace nest {
 
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
-                          const uint8_t* refine, const float* scales, int N, float* y,
-                          int32_t* acc_dbg, hipStream_t st) {
+                          const uint8_t* refine, const float* scales, int N, float* y, int32_t* acc_dbg,
+                          hipStream_t st) {
+  if (M < 1 || M > 16 * kMaxCT)
+    return fail(NEST_EINVAL, "verify_gemm(batched): %d rows per launch (1..%d)", M, 16 * kMaxCT);
   GemmArgs a{};
-  a.qa = qa; a.sa = sa; a.M = M; a.K = K; a.base = base; a.refine = refine; a.scales = scales;
-  a.N = N; a.G = K / kGroup; a.y = y; a.acc_dbg = acc_dbg;
+  a.qa = qa; a.sa = sa; a.base = base; a.refine = refine; a.scales = scales;
+  a.y = y; a.acc_dbg = acc_dbg;
+  a.M = M; a.K = K; a.N = N; a.G = K / kGroup; a.T = (N + 15) / 16;
+  a.row_blocks = (a.T + kBlockTiles - 1) / kBlockTiles;
+  // Activation rows split evenly over P blocks per row block when the
+  // matrix alone would leave CUs idle (P divides the column tiles).
   const int CT = (M + 15) / 16;
-  return acc_dbg ? launch_ct<true>(a, CT, st) : launch_ct<false>(a, CT, st);
+  int P = 1;
+  for (int p = 1; p <= CT; ++p) {
+    if (CT % p) continue;
+    P = p;
+    if (4 * a.row_blocks * p >= 3 * device_cus()) break;
+  }
+  a.parts = P;
+  const int blocks = ((a.row_blocks + kXcds - 1) / kXcds) * kXcds * P;
+  return acc_dbg ? launch_ctp<true>(a, CT / P, blocks, st) : launch_ctp<false>(a, CT / P, blocks, st);
 }
 
 }  // namespace nest

@@ -187,6 +187,21 @@ def test_quantization_near_ties(ns, oracle, M, K):
         assert np.array_equal(host(y).view(np.uint32), host(y8).view(np.uint32))
 
 
+@pytest.mark.parametrize("M,K", [(40, 1024), (144, 4096)])
+def test_batched_verify_quantizes_near_ties(ns, oracle, M, K):
+    # M > 16: the batched kernel's staging pass quantizes fp32 rows; on rows
+    # built on and around ties its result equals the int8 path fed with the
+    # oracle's codes and scales, bit for bit
+    x = near_tie_rows(M, K, (313, M, K))
+    qa, sa = oracle.act_quant(x)
+    w = synth.weights(200, K, (314, M, K))
+    base, refine, scales = oracle.nest_pack(w)
+    W = tiled(ns, base, refine, scales)
+    y = host(ns.verify_gemm_x(dev(x), W))
+    y8 = host(ns.verify_gemm(dev(qa), dev(sa), W))
+    assert np.array_equal(y.view(np.uint32), y8.view(np.uint32))
+
+
 def test_two_streams_keep_their_own_counters_and_scratch(ns, oracle):
     # the argmax GEMV's block counter and the quantize-first scratch are per
     # stream: calls interleaved on two streams must each match the oracle

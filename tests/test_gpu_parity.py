@@ -154,7 +154,15 @@ def test_draft_gemv(ns, oracle, N, K, M):
     assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
 
 
-@pytest.mark.parametrize("N,K,M", GEMV_SHAPES + [(50, 512, 17), (200, 256, 144), (64, 384, 150)])
+# M > 16 runs the batched kernel: (200, 2048, 144) splits each row block's
+# groups over 8 blocks, (1000, 1024, 144) over 4; K = 128 leaves one half of
+# a block's groups empty; (130, 384, 100) has an odd group count and ragged
+# row and activation tiles.
+BATCHED_SHAPES = [(50, 512, 17), (200, 256, 144), (64, 384, 150), (200, 2048, 144), (1000, 1024, 144),
+                  (64, 128, 33), (130, 384, 100)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMV_SHAPES + BATCHED_SHAPES)
 def test_verify_gemm(ns, oracle, N, K, M):
     base, refine, scales, qa, sa = _layer(oracle, N, K, M, (N, K, M, 1))
     oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
@@ -165,6 +173,23 @@ def test_verify_gemm(ns, oracle, N, K, M):
     assert ok, worst
     y_nodbg = ns.verify_gemm(dev(qa), dev(sa), W)
     assert np.array_equal(host(y_nodbg).view(np.uint32), host(y).view(np.uint32))
+
+
+def test_batched_verify_repeats(ns, oracle):
+    # blocks that split a row block's groups count themselves done on
+    # per-stream counters and leave them at zero: calls in a row agree bit
+    # for bit, also after a call with other shapes on the same stream
+    base, refine, scales, qa, sa = _layer(oracle, 300, 4096, 144, (11,))
+    W = tiled(ns, base, refine, scales)
+    y1 = host(ns.verify_gemm(dev(qa), dev(sa), W))
+    b2, r2, s2, qa2, sa2 = _layer(oracle, 70, 1024, 40, (12,))
+    ns.verify_gemm(dev(qa2), dev(sa2), tiled(ns, b2, r2, s2))
+    for _ in range(3):
+        y2 = host(ns.verify_gemm(dev(qa), dev(sa), W))
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
+    ok, worst = bound_ok(y1, sa, scales, oacc, 1.0 / 16)
+    assert ok, worst
 
 
 def test_gemv_deterministic(ns, oracle):

@@ -43,6 +43,14 @@ and where the batched target pass first diverges.
 `k_choice_eq2` gives, for each planted acceptance rate, the draft length
 that Eq. (1)/(2) choose from the measured time of one draft step and of
 the verify pass at each k (nest_choose_k), with the derived tokens/s.
+`workloads` measures each configured workload on its own, cache-cold
+(rotating over copies when one copy would fit the 256 MB last-level cache):
+the 4096x4096 linear (draft 1 row, verify 5 rows); the nested LM head at
+k = 8 (draft step with argmax, verify_accept over 9 rows, and 10k rounds
+with drafts planted at 0.58 / 0.66 / 0.95, mean tokens per round next to
+Eq. (1)); the 144-row batched verify over the LLaMA-3-8B linears x 32 layers
+(GB/s, int8 TOPS and the fraction of the 5.0 POPS MFMA peak); the nested KV
+cache at 32K (32 q / 8 kv heads), draft and verify views.
 """
 from __future__ import annotations
 
@@ -419,6 +427,215 @@ def time_rounds(torch, rnd, steps, warmup, with_events):
 
 
 # ---------------------------------------------------------------------------
+# the configured workloads, each on its own (kernel-level figures)
+# ---------------------------------------------------------------------------
+
+def _copies(torch, W, n):
+    """n device copies of a tiled matrix (distinct addresses, so a rotation
+    over them reads HBM rather than the 256 MB last-level cache)."""
+    return [W] + [type(W)(W.base.clone(), None if W.refine is None else W.refine.clone(), W.scales.clone(),
+                          W.rows, W.cols) for _ in range(n - 1)]
+
+
+def _timed_us(torch, fn, reps, warmup=3):
+    """Average microseconds per call of fn (HIP events on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def _rate(nbytes, us, ops=None):
+    r = {"us": round(us, 2), "GB_per_s": round(nbytes / us / 1e3, 1),
+         "frac_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "bytes": int(nbytes)}
+    if ops is not None:
+        r["int8_TOPS"] = round(ops / us / 1e6, 1)
+        r["frac_int8_mfma_peak"] = round(ops / us / 1e6 / PEAK_INT8_TOPS, 4)
+    return r
+
+
+def _check_rc(ns, rc, what):
+    if rc:
+        raise RuntimeError(f"{what}: status {rc}: {ns.lib().nest_last_error().decode()}")
+
+
+def workloads(ns, torch, dv):
+    """Each configured workload measured on its own, cache-cold (rotating over
+    copies well past the 256 MB last-level cache where one copy fits in it).
+    Weights are seeded synthetic (synth.py); the LLaMA-shaped pass uses one
+    packed layer copied to 32 distinct layer buffers."""
+    from nested_quantized_weights_amd import synth
+
+    L = ns.lib()
+    P = ctypes.c_void_p
+    st = P(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: P(t.data_ptr())
+    cuda = "cuda"
+    out = {}
+
+    # -- single nested 4096 x 4096 linear: draft 1 row, verify 5 rows (k = 4)
+    wl = synth.WORKLOADS["linear_4096"]
+    key = synth.WORKLOAD_KEY["linear_4096"]
+    N, K = wl["N"], wl["K"]
+    Ws = _copies(torch, ns.nest_pack_tiled(torch.from_numpy(synth.weights(N, K, (key, 0))).cuda()), 24)
+    x = torch.from_numpy(synth.activations(wl["verify_rows"], K, (key, 1))).cuda()
+    y = torch.empty((wl["verify_rows"], N), dtype=torch.float32, device=cuda)
+    it = [0]
+
+    def draft():
+        W = Ws[it[0] % len(Ws)]
+        it[0] += 1
+        _check_rc(ns, L.draft_gemv_x(ptr(x), 1, K, ptr(W.base), ptr(W.scales), N, 128, ptr(y), None, None, 0,
+                                     st), "draft_gemv_x")
+
+    def verify():
+        W = Ws[it[0] % len(Ws)]
+        it[0] += 1
+        _check_rc(ns, L.verify_gemm_x(ptr(x), wl["verify_rows"], K, ptr(W.base), ptr(W.refine), ptr(W.scales),
+                                      N, 128, ptr(y), st), "verify_gemm_x")
+
+    out["linear_4096"] = {
+        "draft_gemv_x_1row": _rate(gemv_bytes(N, K, 1, 1, x_fp32=True), _timed_us(torch, draft, 200)),
+        "verify_gemm_x_5rows": _rate(gemv_bytes(N, K, 5, 2, x_fp32=True), _timed_us(torch, verify, 200))}
+    del Ws, x, y
+
+    # -- nested LM head, k = 8: draft step (1 row, argmax) and verify_accept
+    # (9 rows); then 10k rounds with drafts planted at each alpha: mean
+    # tokens per round next to Eq. (1)
+    wl = synth.WORKLOADS["qwen2.5-7b_lm_head"]
+    key = synth.WORKLOAD_KEY["qwen2.5-7b_lm_head"]
+    V, H, k = wl["V"], wl["K"], wl["k"]
+    base, refine, scales = dv["base"]["head"], dv["refine"]["head"], dv["scales"]["head"]
+    pool = [torch.from_numpy(synth.activations(k + 1, H, (key, 1, p))).cuda() for p in range(wl["pool"])]
+    ws = ns.workspace(max(L.draft_gemv_workspace_size(1, V), L.verify_accept_workspace_size(1, k, V)),
+                      torch.device(cuda), "argmax")
+    am = torch.empty(1, dtype=torch.int32, device=cuda)
+    R = wl["rounds"]
+    tgt = torch.empty((R, k + 1), dtype=torch.int32, device=cuda)
+    n_em = torch.empty(R, dtype=torch.int32, device=cuda)
+    emit = torch.empty((R, k + 1), dtype=torch.int32, device=cuda)
+    zero_draft = torch.zeros(k, dtype=torch.int32, device=cuda)
+
+    def head_draft():
+        _check_rc(ns, L.draft_gemv_x(ptr(pool[0][:1]), 1, H, ptr(base), ptr(scales), V, 128, None, ptr(am),
+                                     ptr(ws), ws.numel(), st), "draft_gemv_x")
+
+    def accept(r, drafts):
+        x9 = pool[r % len(pool)]
+        _check_rc(ns, L.verify_accept_x(ptr(x9), 1, k, H, ptr(base), ptr(refine), ptr(scales), V, 128,
+                                        P(drafts.data_ptr() + 4 * k * r), P(tgt.data_ptr() + 4 * (k + 1) * r),
+                                        P(n_em.data_ptr() + 4 * r), P(emit.data_ptr() + 4 * (k + 1) * r), None,
+                                        ptr(ws), ws.numel(), st), "verify_accept_x")
+
+    head = {"draft_gemv_x_argmax_1row": _rate(gemv_bytes(V, H, 1, 1, y=False, argmax=True, x_fp32=True),
+                                               _timed_us(torch, head_draft, 100))}
+    zd = zero_draft.repeat(len(pool), 1).contiguous()
+    for r in range(len(pool)):
+        accept(r, zd)
+    torch.cuda.synchronize()
+    targets = tgt[:len(pool)].cpu().numpy()
+    cnt = [0]
+
+    def accept_one():
+        accept(cnt[0] % len(pool), zd)
+        cnt[0] += 1
+
+    head["verify_accept_x_9rows"] = _rate(accept_bytes(V, H, k, x_fp32=True), _timed_us(torch, accept_one, 100))
+    head["planted_rounds"] = {}
+    for a in wl["alphas"]:
+        t_r = targets[np.arange(R) % len(pool)]
+        drafts = torch.from_numpy(synth.plant_drafts(t_r, a, V, (key, 3, int(a * 100)))).cuda()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(R):
+            accept(r, drafts)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        n = n_em.cpu().numpy()
+        head["planted_rounds"][str(a)] = {
+            "rounds": R, "mean_tokens_per_round": round(float(n.mean()), 4),
+            "eq1_expected": round(eq1(a, k), 4), "min": int(n.min()), "max": int(n.max()),
+            "verify_accept_rounds_per_s": round(R / (ms * 1e-3), 1)}
+    out["qwen2.5-7b_lm_head"] = head
+    del pool, tgt, n_em, emit
+
+    # -- 144-row batched verify over the LLaMA-3-8B linears x 32 layers
+    wl = synth.WORKLOADS["llama3-8b_batched_verify"]
+    key = synth.WORKLOAD_KEY["llama3-8b_batched_verify"]
+    M = wl["sequences"] * wl["rows_per_seq"]
+    layer0 = {}
+    for li, (name, (N, K)) in enumerate(wl["linears"].items()):
+        layer0[name] = ns.nest_pack_tiled(torch.from_numpy(synth.weights(N, K, (key, 0, 0, li))).cuda())
+    layers = [layer0] + [{n: _copies(torch, W, 2)[1] for n, W in layer0.items()} for _ in range(wl["layers"] - 1)]
+    xs = {K: torch.from_numpy(synth.activations(M, K, (key, 1, 0, K))).cuda() for _, (_, K) in wl["linears"].items()}
+    ys = {n: torch.empty((M, N), dtype=torch.float32, device=cuda) for n, (N, _) in wl["linears"].items()}
+    calls = []
+    for lay in layers:
+        for name, (N, K) in wl["linears"].items():
+            W = lay[name]
+            calls.append((N, K, ptr(xs[K]), ptr(W.base), ptr(W.refine), ptr(W.scales), ptr(ys[name])))
+
+    def verify_pass():
+        for N, K, px, pb, pr, ps, py in calls:
+            _check_rc(ns, L.verify_gemm_x(px, M, K, pb, pr, ps, N, 128, py, st), "verify_gemm_x")
+
+    per_layer = {n: _timed_us(torch, lambda n=n, N=N, K=K: _check_rc(
+        ns, L.verify_gemm_x(ptr(xs[K]), M, K, ptr(layers[1][n].base), ptr(layers[1][n].refine),
+                            ptr(layers[1][n].scales), N, 128, ptr(ys[n]), st), "verify_gemm_x"), 20)
+                 for n, (N, K) in wl["linears"].items()}
+    us = _timed_us(torch, verify_pass, 5, warmup=1)
+    nbytes = wl["layers"] * sum(gemv_bytes(N, K, M, 2, x_fp32=True) for N, K in wl["linears"].values())
+    ops = wl["layers"] * sum(2 * M * N * K for N, K in wl["linears"].values())
+    out["llama3-8b_batched_verify"] = dict(_rate(nbytes, us, ops), rows=M, layers=wl["layers"],
+                                           ms_per_pass=round(us / 1e3, 4),
+                                           per_linear_us={n: round(v, 2) for n, v in per_layer.items()})
+    del layers, layer0, xs, ys, calls
+
+    # -- nested KV attention at 32K: draft (1 query, base view), verify (9
+    # queries, full view), rotating over 8 caches
+    wl = synth.WORKLOADS["kv_32k"]
+    key = synth.WORKLOAD_KEY["kv_32k"]
+    Hq, Hkv, d, ctx = wl["q_heads"], wl["kv_heads"], wl["head_dim"], wl["context"]
+    cap = ctx + wl["block"]
+    kf, vf = synth.kv(Hkv, cap, d, (key, 0))
+    kt, vt = torch.from_numpy(kf).cuda(), torch.from_numpy(vf).cuda()
+    del kf, vf
+    caches = [ns.kv_nest_pack(kt, vt) for _ in range(8)]
+    del kt, vt
+    kvs = [c.struct() for c in caches]
+    att = {}
+    for view, nq in ((0, wl["draft_queries"]), (1, wl["verify_queries"])):
+        q = torch.from_numpy(synth.queries_bf16(nq, Hq, d, (key, 1, view)).view(np.int16)).cuda()
+        o = torch.empty((nq, Hq, d), dtype=torch.float32, device=cuda)
+        wsn = L.kv_nest_attend_workspace_size(nq, Hq, Hkv, d, ctx)
+        wsa = torch.empty(max(wsn, 256), dtype=torch.uint8, device=cuda)
+        it = [0]
+
+        def attend(view=view, nq=nq, q=q, o=o, wsa=wsa, wsn=wsn):
+            s_ = kvs[it[0] % len(kvs)]
+            it[0] += 1
+            _check_rc(ns, L.kv_nest_attend(ptr(q), nq, Hq, ctypes.byref(s_), ctx, view, ptr(o), ptr(wsa), wsn, st),
+                      "kv_nest_attend")
+
+        tag = "draft_base_view_1q" if view == 0 else f"verify_full_view_{nq}q"
+        att[tag] = _rate(attend_bytes(view, Hkv, Hq, nq, ctx), _timed_us(torch, attend, 200))
+    out["kv_32k"] = att
+    del caches, kvs
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on one full k=4 round
 # ---------------------------------------------------------------------------
 
@@ -540,6 +757,8 @@ def main():
 
     print("# bench: timing draft steps and verify passes for the choice of k", file=sys.stderr, flush=True)
     kc = k_choice(ns, torch, dv)
+    print("# bench: each configured workload on its own", file=sys.stderr, flush=True)
+    wls = workloads(ns, torch, dv)
     ms4 = res[4]["ms"]
     value = round_bytes(4) / (ms4 * 1e-3) / 1e9
     dom_ms = float(np.mean(res[4]["dom"]))
@@ -575,6 +794,7 @@ def main():
         "k_choice_eq2": kc,
         "sampled_round_k4": sampled,
         "tiny_decoder_greedy": tiny,
+        "workloads": wls,
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,

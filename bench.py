@@ -49,7 +49,8 @@ the 4096x4096 linear (draft 1 row, verify 5 rows); the nested LM head at
 k = 8 (draft step with argmax, verify_accept over 9 rows, and 10k rounds
 with drafts planted at 0.58 / 0.66 / 0.95, mean tokens per round next to
 Eq. (1)); the 144-row batched verify over the LLaMA-3-8B linears x 32 layers
-(GB/s, int8 TOPS and the fraction of the 5.0 POPS MFMA peak); the nested KV
+on int8 activations (GB/s, int8 TOPS and the fraction of the 5.0 POPS MFMA
+peak); the nested KV
 cache at 32K (32 q / 8 kv heads), draft and verify views.
 """
 from __future__ import annotations
@@ -577,24 +578,27 @@ def workloads(ns, torch, dv):
     for li, (name, (N, K)) in enumerate(wl["linears"].items()):
         layer0[name] = ns.nest_pack_tiled(torch.from_numpy(synth.weights(N, K, (key, 0, 0, li))).cuda())
     layers = [layer0] + [{n: _copies(torch, W, 2)[1] for n, W in layer0.items()} for _ in range(wl["layers"] - 1)]
-    xs = {K: torch.from_numpy(synth.activations(M, K, (key, 1, 0, K))).cuda() for _, (_, K) in wl["linears"].items()}
+    # the workload's activations are int8 (per-token codes and scales, quantized once up front)
+    xs = {K: ns.nest_act_quant(torch.from_numpy(synth.activations(M, K, (key, 1, 0, K))).cuda())
+          for _, (_, K) in wl["linears"].items()}
     ys = {n: torch.empty((M, N), dtype=torch.float32, device=cuda) for n, (N, _) in wl["linears"].items()}
     calls = []
     for lay in layers:
         for name, (N, K) in wl["linears"].items():
             W = lay[name]
-            calls.append((N, K, ptr(xs[K]), ptr(W.base), ptr(W.refine), ptr(W.scales), ptr(ys[name])))
+            calls.append((N, K, ptr(xs[K][0]), ptr(xs[K][1]), ptr(W.base), ptr(W.refine), ptr(W.scales),
+                          ptr(ys[name])))
 
     def verify_pass():
-        for N, K, px, pb, pr, ps, py in calls:
-            _check_rc(ns, L.verify_gemm_x(px, M, K, pb, pr, ps, N, 128, py, st), "verify_gemm_x")
+        for N, K, pq, psa, pb, pr, ps, py in calls:
+            _check_rc(ns, L.verify_gemm(pq, psa, M, K, pb, pr, ps, N, 128, py, None, st), "verify_gemm")
 
     per_layer = {n: _timed_us(torch, lambda n=n, N=N, K=K: _check_rc(
-        ns, L.verify_gemm_x(ptr(xs[K]), M, K, ptr(layers[1][n].base), ptr(layers[1][n].refine),
-                            ptr(layers[1][n].scales), N, 128, ptr(ys[n]), st), "verify_gemm_x"), 20)
+        ns, L.verify_gemm(ptr(xs[K][0]), ptr(xs[K][1]), M, K, ptr(layers[1][n].base), ptr(layers[1][n].refine),
+                          ptr(layers[1][n].scales), N, 128, ptr(ys[n]), None, st), "verify_gemm"), 20)
                  for n, (N, K) in wl["linears"].items()}
     us = _timed_us(torch, verify_pass, 5, warmup=1)
-    nbytes = wl["layers"] * sum(gemv_bytes(N, K, M, 2, x_fp32=True) for N, K in wl["linears"].values())
+    nbytes = wl["layers"] * sum(gemv_bytes(N, K, M, 2) for N, K in wl["linears"].values())
     ops = wl["layers"] * sum(2 * M * N * K for N, K in wl["linears"].values())
     out["llama3-8b_batched_verify"] = dict(_rate(nbytes, us, ops), rows=M, layers=wl["layers"],
                                            ms_per_pass=round(us / 1e3, 4),
@@ -704,6 +708,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--round-only", action="store_true",
+                    help="time the k=4 and k=8 rounds only (no sampled round, small decoder, "
+                         "choice of k or per-workload figures): for counter runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -743,6 +750,13 @@ def main():
         ms, wall, dom = time_rounds(torch, rnd, args.steps, args.warmup, with_events=(k == 4))
         res[k] = {"ms": ms, "wall": wall, "dom": dom, "n": int(rnd.acc_out["n"].item())}
         print(f"# bench: k={k} {ms:.4f} ms/round", file=sys.stderr, flush=True)
+
+    if args.round_only:
+        ms4 = res[4]["ms"]
+        print(json.dumps({"round_only": True, "ms_per_step_k4": round(ms4, 5),
+                          "ms_per_step_k8": round(res[8]["ms"], 5),
+                          "dominant_avg_us": round(float(np.mean(res[4]["dom"])) * 1e3, 3)}), flush=True)
+        return 0
 
     T_SAMPLE = 1.0
     rnd = Round(ns, torch, dv, 4, temperature=T_SAMPLE)

@@ -31,12 +31,14 @@ using nest::kGroup;
 
 constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
 constexpr int kCW = 8;                   // compute waves per block (two per SIMD)
-constexpr int kWK = 2;                   // halves of the groups
-constexpr int kWR = kCW / kWK;           // compute waves per half
+constexpr int kWK = 2;                   // parts of the groups (one per compute wave row)
+constexpr int kWR = kCW / kWK;           // compute waves per part
 constexpr int kBlockTiles = kWR * kRT;   // 16-row weight tiles per block (64 rows)
 constexpr int kThreads = (kCW + 1) * 64; // + the copy wave
-constexpr int kNBuf = 3;                 // LDS ring slots per half
-constexpr int kAhead = kNBuf - 1;        // groups the copy wave runs ahead
+constexpr int kLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
+// LDS ring slots per part of the groups: three (the copy wave runs two
+// groups ahead) when they fit, else two
+constexpr int ring_slots(int ctp) { return 3 * kWK * ctp * 2048 <= kLdsBytes ? 3 : 2; }
 constexpr int kSlots = 3;                // weight groups in flight per compute wave
 constexpr int kMaxCT = 9;                // 144 activation rows per launch
 constexpr int kXcds = 8;                 // blocks are dealt to the XCDs in turn
@@ -112,10 +114,13 @@ __device__ __forceinline__ void build_ops(const WLoad (&w)[kRT], WOps& o) {
 }
 
 // LDS slot of one group: per column tile ct, 16 rows of 128 bytes, the
-// 16-byte piece q of row r stored at position q ^ (r & 7) of that row. A
-// copy instruction then reads eight whole rows (full cache lines) and a
-// 16-lane read of one piece from 16 rows touches every bank evenly.
-__device__ __forceinline__ int act_lds_off(int ct, int r, int q) { return ct * 2048 + r * 128 + ((q ^ (r & 7)) << 4); }
+// 16-byte piece q of row r stored at position q ^ ((r >> 1) & 7) of that
+// row. A copy instruction then reads eight whole rows (full cache lines),
+// and a 16-lane read of one piece from rows 0..15 covers each of the 64
+// four-byte banks once (rows of one parity share half the banks; the
+// swizzle spreads the eight of each parity over that half).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int act_lds_off(int ct, int r, int q) { return ct * 2048 + r * 128 + ((q ^ swz(r)) << 4); }
 
 // One group for the wave's weight tile(s) and the block's CTP column tiles:
 // lane (kq, idx) takes pieces 2kq and 2kq + 1 (elements 32 kq .. +31) of
@@ -187,6 +192,10 @@ template <int CTP, bool DBG>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
   constexpr int SB = CTP * 2048;               // LDS bytes of one group's activations
   constexpr int kCopies = kWK * 2 * CTP;       // copy instructions per step
+  constexpr int kNBuf = ring_slots(CTP);       // ring slots per part
+  constexpr int kAhead = kNBuf - 1;            // steps the copy wave runs ahead
+  static_assert(kNBuf * kWK * SB <= kLdsBytes, "ring exceeds LDS");
+  static_assert((kAhead - 1) * kCopies <= 63, "copies in flight exceed the vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kNBuf * kWK * SB];
 
   // blocks of one row block sit kXcds apart, i.e. on one XCD
@@ -205,7 +214,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
   if (wave == kCW) {
     // copy wave: group j of each half into slot j % kNBuf. Copy (ct, e)
     // fills rows 8e .. 8e + 7 of column tile ct: lane l writes position
-    // l & 7 of row r = 8e + (l >> 3), i.e. piece (l & 7) ^ (r & 7) of
+    // l & 7 of row r = 8e + (l >> 3), i.e. piece (l & 7) ^ swz(r) of
     // activation row 16 ct + r (clamped to the last row). The group index is
     // clamped into the half (to group 0 for an empty half), so every step
     // issues kCopies copies.
@@ -216,7 +225,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
       for (int e = 0; e < 2; ++e) {
         const int r = 8 * e + (lane >> 3);
         src_l[c][e] = a.qa + static_cast<size_t>(min((ct0 + c) * 16 + r, a.M - 1)) * a.K +
-                      (((lane & 7) ^ (r & 7)) << 4);
+                      (((lane & 7) ^ swz(r)) << 4);
       }
     auto copy_step = [&](int j) {
       uint8_t* slot0 = ring + (j % kNBuf) * kWK * SB;
@@ -243,7 +252,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
       if (j + kAhead < steps) copy_step(j + kAhead);
     }
     wait_vm<0>();
-    copy_barrier();  // the ring is free: the halves' sums go through it
+    copy_barrier();  // the ring is free: the parts' sums go through it
     copy_barrier();
     return;
   }
@@ -299,19 +308,23 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
   if (full + 1 < steps) step(full + 1, w1);
   lds_barrier();  // all copies landed and every wave is past the ring
 
-  // halves: wk = 1 hands its sums to wk = 0 through LDS (ring reused)
+  // parts wk > 0 hand their sums to wk = 0 through LDS (ring reused), which
+  // adds them in group order
+  static_assert((kWK - 1) * kWR * kRT * CTP * 4 * 64 * 4 <= kNBuf * kWK * SB, "partial sums exceed the ring");
   float* comb = reinterpret_cast<float*>(ring);
-  auto cidx = [&](int rt, int ct, int i) { return (((wr * kRT + rt) * CTP + ct) * 4 + i) * 64 + lane; };
-  if (wk == 1) {
+  auto cidx = [&](int w, int rt, int ct, int i) {
+    return ((((w - 1) * kWR + wr) * kRT + rt) * CTP * 4 + ct * 4 + i) * 64 + lane;
+  };
+  if (wk > 0) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < CTP; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) comb[cidx(rt, ct, i)] = run[rt][ct][i];
+        for (int i = 0; i < 4; ++i) comb[cidx(wk, rt, ct, i)] = run[rt][ct][i];
   }
   lds_barrier();
-  if (wk == 1) return;
+  if (wk > 0) return;
 #pragma unroll
   for (int ct = 0; ct < CTP; ++ct)
 #pragma unroll
@@ -322,8 +335,10 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         const int n = t[rt] * 16 + idx;
-        if (t_ok[rt] && n < a.N)
-          a.y[static_cast<size_t>(m) * a.N + n] = (run[rt][ct][i] + comb[cidx(rt, ct, i)]) * sm;
+        float v = run[rt][ct][i];
+#pragma unroll
+        for (int w = 1; w < kWK; ++w) v += comb[cidx(w, rt, ct, i)];
+        if (t_ok[rt] && n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = v * sm;
       }
     }
 }

@@ -90,6 +90,42 @@ __device__ __forceinline__ uint4 codes_to_h8(uint32_t wb, uint32_t wr) {
   return r;
 }
 
+// The same 8 codes left biased: f16 (1024 + u) with u the byte under the
+// exponent, i.e. base + (code or 16 code) with one v_perm_b32 per two values
+// and no subtraction. View 0: positions 0..3 (even elements) hold 1032 + c,
+// positions 4..7 (odd elements) hold 1152 + 16 c, so their partner operand
+// carries a factor 1/16. View 1: every position holds 1160 + c. The bias
+// is removed afterwards from whole sums (kernels below).
+template <int VIEW>
+__device__ __forceinline__ uint4 codes_to_h8b(uint32_t wb, uint32_t wr) {
+  const uint32_t xb = wb ^ 0x88888888u;
+  uint32_t ev, od;
+  if (VIEW == 0) {
+    ev = xb & 0x0F0F0F0Fu;  // q_b + 8 of even elements
+    od = xb & 0xF0F0F0F0u;  // 16 (q_b + 8) of odd elements
+  } else {
+    const uint32_t xr = wr ^ 0x88888888u;
+    ev = bfi(0xF0F0F0F0u, xb << 4, xr);  // c + 136
+    od = bfi(0xF0F0F0F0u, xb, xr >> 4);
+  }
+  const uint32_t c64 = 0x64646464u;
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(c64, ev, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(c64, ev, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(c64, od, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(c64, od, 0x04030402u);
+  return r;
+}
+
+// The bias of each position of codes_to_h8b as an f16 operand (1032 / 1152
+// for view 0, 1160 for view 1): its product with a partner operand is the
+// amount to take off the biased product.
+template <int VIEW>
+__device__ __forceinline__ uint4 bias_h8() {
+  return VIEW == 0 ? make_uint4(0x64086408u, 0x64086408u, 0x64806480u, 0x64806480u)
+                   : make_uint4(0x64886488u, 0x64886488u, 0x64886488u, 0x64886488u);
+}
+
 __device__ __forceinline__ v4f mfma_h(uint4 a, v8h b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), b, c, 0, 0, 0);
 }
@@ -360,8 +396,26 @@ __global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
     for (int s = 0; s < 4; ++s) qop[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
+  // Biased codes (codes_to_h8b): in view 0 the odd dims of q carry 1/16
+  // (exact), and the row's bias sum(q * base) is one product with the bias
+  // operand, taken off every score of the row.
+  if (VIEW == 0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 4; e < 8; ++e) qop[s][e] = qop[s][e] * static_cast<_Float16>(0.0625f);
+  }
+  float kbias;
+  {
+    v4f acc = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_h(bias_h8<VIEW>(), qop[s], acc);
+    kbias = acc[0];  // every row of the product is the same
+  }
+
   float m = -INFINITY, l = 0.0f;
   v4f O[8];
+  v4f Ob = v4f{0, 0, 0, 0};  // the bias part of O (the same for every dim)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
   const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
@@ -369,24 +423,28 @@ __global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
   const int b_first = chunk * a.bpw;
   const int b_last = min(b_first + a.bpw, a.nbv);
   uint4 kb[8], kr[8], vb[8], vr[8];
+  // K codes first, then V: loads return in issue order, so the scores and
+  // the softmax of a block start while its V codes are still on the way
   auto load = [&](int blk) {
     const size_t hb = static_cast<size_t>(h) * a.nb + blk;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
       const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
-      const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
       kb[tt] = nest::ldnt16(a.kb + koff);
+      kr[tt] = VIEW ? nest::ldnt16(a.kr + koff) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
       vb[tt] = nest::ldnt16(a.vb + voff);
-      if (VIEW) {
-        kr[tt] = nest::ldnt16(a.kr + koff);
-        vr[tt] = nest::ldnt16(a.vr + voff);
-      } else {
-        kr[tt] = vr[tt] = make_uint4(0, 0, 0, 0);
-      }
+      vr[tt] = VIEW ? nest::ldnt16(a.vr + voff) : make_uint4(0, 0, 0, 0);
     }
   };
-  for (int blk = b_first + wave; blk < b_last; blk += 4) {
+  // Rows whose position is at least pos_min see every token of a block that
+  // ends at or before pos_min; only later blocks need the causal mask.
+  const int pos_min = a.ctx - a.nq;
+  auto block = [&](int blk, bool first) {
     load(blk);
     const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
     const size_t hb = static_cast<size_t>(h) * a.nb + blk;
@@ -399,52 +457,82 @@ __global__ void __launch_bounds__(256) attend_wave_kernel(AttArgs a) {
       v4f acc = v4f{0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc = mfma_h(codes_to_h8<VIEW>(word(ck[tt], s), word(cr[tt], s)), qop[s], acc);
-      S[tt] = acc;
+        acc = mfma_h(codes_to_h8b<VIEW>(word(ck[tt], s), word(cr[tt], s)), qop[s], acc);
+      S[tt] = acc;  // kbias + q . k
     }
+    // block maximum of the biased scores (the bias and the scale sk >= 0
+    // are applied after)
+    const bool masked = t0 + kBlk - 1 > pos_min;
     float mb = -INFINITY;
+    if (masked) {
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
+      for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 32 * q4 + 8 * (tt >> 1) + 4 * (tt & 1) + i;
-        const float v = tok <= pos ? S[tt][i] * sk : -INFINITY;
-        S[tt][i] = v;
-        mb = fmaxf(mb, v);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int tok = t0 + 32 * q4 + 8 * (tt >> 1) + 4 * (tt & 1) + i;
+          if (tok > pos) S[tt][i] = -INFINITY;
+          mb = fmaxf(mb, S[tt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mb = fmaxf(mb, S[tt][i]);
+    }
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mn = fmaxf(m, mb);
+    const float mbs = mb == -INFINITY ? -INFINITY : (mb - kbias) * sk;
+    const float mn = fmaxf(m, mbs);
     const float mu = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = exp2f(m - mu);
+    const float c2 = fmaf(kbias, sk, mu);
+    // p = 2^((S - kbias) sk - mu) <= 1 (up to rounding): the hardware exp2
+    // (flushing results below 2^-126 to zero, which no sum here can
+    // notice); masked tokens give 0
     float ls = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(S[tt][i] - mu);
+        float p = __builtin_amdgcn_exp2f(fmaf(S[tt][i], sk, -c2));
+        if (masked) p = S[tt][i] == -INFINITY ? 0.0f : p;
         S[tt][i] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
-    l = l * alpha + ls;
-    m = mn;
+    if (first) {
+      l = ls;  // O is still zero: nothing to rescale
+    } else {
+      const float alpha = __builtin_amdgcn_exp2f(m - mu);
+      l = l * alpha + ls;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+      Ob *= alpha;
+    }
+    m = mn;
+    // odd tokens' weights carry 1/16 in view 0 (biased V codes)
+    const float svo = VIEW ? sv : sv * 0.0625f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const v4f e0 = S[2 * j], e1 = S[2 * j + 1];
       v8h p;
       p[0] = (_Float16)(e0[0] * sv); p[1] = (_Float16)(e0[2] * sv);
       p[2] = (_Float16)(e1[0] * sv); p[3] = (_Float16)(e1[2] * sv);
-      p[4] = (_Float16)(e0[1] * sv); p[5] = (_Float16)(e0[3] * sv);
-      p[6] = (_Float16)(e1[1] * sv); p[7] = (_Float16)(e1[3] * sv);
+      p[4] = (_Float16)(e0[1] * svo); p[5] = (_Float16)(e0[3] * svo);
+      p[6] = (_Float16)(e1[1] * svo); p[7] = (_Float16)(e1[3] * svo);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        O[dt] = mfma_h(codes_to_h8<VIEW>(word(dk[dt], j), word(dr[dt], j)), p, O[dt]);
+        O[dt] = mfma_h(codes_to_h8b<VIEW>(word(dk[dt], j), word(dr[dt], j)), p, O[dt]);
+      Ob = mfma_h(bias_h8<VIEW>(), p, Ob);
     }
-  }
+  };
+  // the first block of the wave is peeled: the running max and sum start
+  // there, so O needs no rescaling (most waves own a single block)
+  if (b_first + wave < b_last) block(b_first + wave, true);
+  for (int blk = b_first + wave + 4; blk < b_last; blk += 4) block(blk, false);
+  // take the V bias off (every dim of a row has the same bias sum)
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob[0];
 
   // merge the 4 waves (fixed order w = 3 .. 0) and write the chunk's partial
   if (q4 == 0) {

@@ -13,8 +13,10 @@
 //            dim-major) and convert them to f16 MFMA operands in LDS
 //            (32 KB K + 32 KB V). A nibble (or the 8-bit code biased by
 //            136) is put under the f16 exponent byte 0x64 by v_perm_b32,
-//            giving 1024 + u. One v_pk_add_f16 then removes the offset
-//            exactly, so every code becomes an exact f16 integer.
+//            giving the exact f16 1024 + u. The bias is not subtracted per
+//            value: its contribution to a row's scores is one MFMA with a
+//            constant operand (taken off inside the exp2), and to O one
+//            more MFMA per 32 tokens (taken off at the end).
 //   phase B  waves split the query rows into 16-row tiles and, when rows
 //            are few, the block's four 32-token k-steps. Each keeps an
 //            online softmax (log2 domain, exp2f) and multiplies with
@@ -32,7 +34,6 @@
 
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kBlk = 128;
@@ -55,44 +56,10 @@ struct AttArgs {
 
 __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); }
 
-__device__ __forceinline__ uint32_t sub_h2(uint32_t v, uint32_t off) {
-  h2 a = __builtin_bit_cast(h2, v), b = __builtin_bit_cast(h2, off);
-  return __builtin_bit_cast(uint32_t, a - b);
-}
-
-// Four bytes u (each < 256) -> two VGPRs of f16 pairs (1024+u) - off, in the
-// order (byte0, byte1) and (byte2, byte3).
-__device__ __forceinline__ void bytes_to_h(uint32_t bytes, uint32_t off, uint32_t& p01, uint32_t& p23) {
-  const uint32_t c64 = 0x64646464u;
-  p01 = sub_h2(__builtin_amdgcn_perm(c64, bytes, 0x04010400u), off);
-  p23 = sub_h2(__builtin_amdgcn_perm(c64, bytes, 0x04030402u), off);
-}
-
 // One 32-bit word of codes (8 elements e0..e7, e_{2b} in the low nibble of
-// byte b) -> 8 f16 code values in the order [e0 e2 e4 e6 e1 e3 e5 e7].
-template <int VIEW>
-__device__ __forceinline__ uint4 codes_to_h8(uint32_t wb, uint32_t wr) {
-  uint32_t ev, od, off;
-  const uint32_t xb = wb ^ 0x88888888u;
-  if (VIEW == 0) {
-    ev = xb & 0x0F0F0F0Fu;          // q_b + 8 of even elements
-    od = (xb >> 4) & 0x0F0F0F0Fu;   // of odd elements
-    off = 0x64086408u;              // f16 1032 = 1024 + 8, twice
-  } else {
-    const uint32_t xr = wr ^ 0x88888888u;
-    ev = bfi(0xF0F0F0F0u, xb << 4, xr);  // 16*(q_b+8) + (q_r+8) = c + 136
-    od = bfi(0xF0F0F0F0u, xb, xr >> 4);
-    off = 0x64886488u;                   // f16 1160 = 1024 + 136, twice
-  }
-  uint4 r;
-  bytes_to_h(ev, off, r.x, r.y);
-  bytes_to_h(od, off, r.z, r.w);
-  return r;
-}
-
-// The same 8 codes left biased: f16 (1024 + u) with u the byte under the
-// exponent, i.e. base + (code or 16 code) with one v_perm_b32 per two values
-// and no subtraction. View 0: positions 0..3 (even elements) hold 1032 + c,
+// byte b) -> 8 biased f16 code values in the order [e0 e2 e4 e6 e1 e3 e5 e7]:
+// f16 (1024 + u) with u the byte put under the exponent byte 0x64 by
+// v_perm_b32, i.e. base + (code or 16 code), one permute per two values. View 0: positions 0..3 (even elements) hold 1032 + c,
 // positions 4..7 (odd elements) hold 1152 + 16 c, so their partner operand
 // carries a factor 1/16. View 1: every position holds 1160 + c. The bias
 // is removed afterwards from whole sums (kernels below).
@@ -182,14 +149,34 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
     }
   }
 
+  // Biased codes in the tables (codes_to_h8b): in view 0 the odd dims of q
+  // carry 1/16 (exact), and the row's bias sum(q * base) is one product with
+  // the bias operand, taken off every score of the row.
+  if (VIEW == 0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 4; e < 8; ++e) qop[s][e] = qop[s][e] * static_cast<_Float16>(0.0625f);
+  }
+  float kbias;
+  {
+    v4f acc = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_h(bias_h8<VIEW>(), qop[s], acc);
+    kbias = acc[0];  // every row of the product is the same
+  }
+
   float m = -INFINITY, l = 0.0f;
   v4f O[8];
+  v4f Ob = v4f{0, 0, 0, 0};  // the bias part of O (the same for every dim)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
 
   const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
   const int b_first = chunk * a.bpw;
   const int b_last = min(b_first + a.bpw, a.nbv);
+  // blocks ending at or before the first query's position need no mask
+  const int pos_min = a.ctx - a.nq;
 
   // Phase A items of this thread: it = threadIdx.x + 256*rep is (t, q, r) with
   // t = it >> 6 (K token tile / V dim tile), q = (it >> 4) & 3, r = it & 15.
@@ -229,10 +216,10 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
       const int t = it >> 6, q = (it >> 4) & 3, r = it & 15;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        kf[op_slot(t, s, q, r)] = codes_to_h8<VIEW>(word(ck_b[rep], s), word(ck_r[rep], s));
+        kf[op_slot(t, s, q, r)] = codes_to_h8b<VIEW>(word(ck_b[rep], s), word(ck_r[rep], s));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        vf[op_slot(t, j, q, r)] = codes_to_h8<VIEW>(word(cv_b[rep], j), word(cv_r[rep], j));
+        vf[op_slot(t, j, q, r)] = codes_to_h8b<VIEW>(word(cv_b[rep], j), word(cv_r[rep], j));
     }
     if (blk + 1 < b_last) load_codes(blk + 1);
     __syncthreads();
@@ -252,6 +239,9 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
           for (int s = 0; s < 4; ++s) acc = mfma_h(kf[op_slot(tt, s, q4, c16)], qop[s], acc);
           S[2 * jj + e] = acc;
         }
+      // maximum of the biased scores of this wave's tokens (the bias and
+      // the scale ck >= 0 are applied after); the mask only near the end
+      const bool masked = t0 + kBlk - 1 > pos_min;
       float mb = -INFINITY;
 #pragma unroll
       for (int jj = 0; jj < JS; ++jj)
@@ -259,22 +249,26 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = t0 + 32 * q4 + 8 * (j0 + jj) + 4 * e + i;
-            const float v = tok <= pos ? S[2 * jj + e][i] * ck : -INFINITY;
-            S[2 * jj + e][i] = v;
-            mb = fmaxf(mb, v);
+            if (masked) {
+              const int tok = t0 + 32 * q4 + 8 * (j0 + jj) + 4 * e + i;
+              if (tok > pos) S[2 * jj + e][i] = -INFINITY;
+            }
+            mb = fmaxf(mb, S[2 * jj + e][i]);
           }
       mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
       mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float mn = fmaxf(m, mb);
+      const float mbs = mb == -INFINITY ? -INFINITY : (mb - kbias) * ck;
+      const float mn = fmaxf(m, mbs);
       const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float alpha = exp2f(m - mu);
+      const float c2 = fmaf(kbias, ck, mu);
+      const float alpha = __builtin_amdgcn_exp2f(m - mu);
       float ls = 0.0f;
 #pragma unroll
       for (int k = 0; k < 2 * JS; ++k)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(S[k][i] - mu);
+          float p = __builtin_amdgcn_exp2f(fmaf(S[k][i], ck, -c2));
+          if (masked) p = S[k][i] == -INFINITY ? 0.0f : p;
           S[k][i] = p;
           ls += p;
         }
@@ -284,21 +278,29 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
       m = mn;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+      Ob *= alpha;
+      // odd tokens' weights carry 1/16 in view 0 (biased V codes)
+      const float svo = VIEW ? sv : sv * 0.0625f;
 #pragma unroll
       for (int jj = 0; jj < JS; ++jj) {
         const v4f e0 = S[2 * jj], e1 = S[2 * jj + 1];
         v8h p;
         p[0] = (_Float16)(e0[0] * sv); p[1] = (_Float16)(e0[2] * sv);
         p[2] = (_Float16)(e1[0] * sv); p[3] = (_Float16)(e1[2] * sv);
-        p[4] = (_Float16)(e0[1] * sv); p[5] = (_Float16)(e0[3] * sv);
-        p[6] = (_Float16)(e1[1] * sv); p[7] = (_Float16)(e1[3] * sv);
+        p[4] = (_Float16)(e0[1] * svo); p[5] = (_Float16)(e0[3] * svo);
+        p[6] = (_Float16)(e1[1] * svo); p[7] = (_Float16)(e1[3] * svo);
         const int j = j0 + jj;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) O[dt] = mfma_h(vf[op_slot(dt, j, q4, c16)], p, O[dt]);
+        Ob = mfma_h(bias_h8<VIEW>(), p, Ob);
       }
     }
     __syncthreads();  // the next block's phase A overwrites the tables
   }
+
+  // take the V bias off (every dim of a row has the same bias sum)
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob[0];
 
   // ---- write this workgroup's partial per row ----
   const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;

@@ -696,8 +696,8 @@ def profile_summary():
     if vals.get("gemv_source_sha256_16") != src_hash:
         return None, None
     try:
-        trace = {"gemv_kernel": round(float(vals["kernel_trace_avg_ns"]) / 1e3, 2)}
-        return int(float(vals["hbm_bytes_per_launch"])), trace
+        trace = {"gemv_kernel": round(float(vals["kernel_trace_avg_ns"].split()[0]) / 1e3, 2)}
+        return int(float(vals["hbm_bytes_per_launch"].split()[0])), trace
     except (KeyError, ValueError):
         return None, None
 

@@ -711,6 +711,8 @@ def main():
     ap.add_argument("--round-only", action="store_true",
                     help="time the k=4 and k=8 rounds only (no sampled round, small decoder, "
                          "choice of k or per-workload figures): for counter runs")
+    ap.add_argument("--workloads-only", action="store_true",
+                    help="only the per-workload figures (one JSON line of them): for counter runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -743,6 +745,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.workloads_only:
+        print(json.dumps({"workloads": workloads(ns, torch, dv)}), flush=True)
+        return 0
 
     res = {}
     for k in (4, 8):

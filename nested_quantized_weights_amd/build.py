@@ -27,6 +27,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
          "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC]
 
+# Per-source additions. The attention kernels keep their MFMA accumulators
+# in VGPRs (the default places them in AGPRs and copies them back and forth
+# around the softmax of every 128-token block); measured 2-4 % faster.
+FILE_FLAGS = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
@@ -40,7 +45,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = ["hipcc", "-c", src, "-o", obj] + [f for f in FLAGS if f != "-shared"]
+        cmd = (["hipcc", "-c", src, "-o", obj] + [f for f in FLAGS if f != "-shared"]
+               + FILE_FLAGS.get(os.path.basename(src), []))
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

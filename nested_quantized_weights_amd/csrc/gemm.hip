@@ -3,13 +3,13 @@
 // sequences x (k+1) = 144 rows: y = sa * fold_g s/16 * (sum q_a (16 q_b + q_r)).
 //
 // A block owns 64 weight rows (four 16-row tiles), a range of the
-// activation rows (CTP column tiles of 16) and all groups. Its ninth wave
+// activation rows (CTP column tiles of 16) and all groups. Its last wave
 // only copies int8 activation rows from HBM/L2 into an LDS ring (direct
 // 16-byte loads to LDS, whole 128-byte rows of a group, two groups ahead).
-// The eight compute waves (two per SIMD, which hide each other's MFMA and
-// LDS latencies) each own one weight tile and one half of the groups (four
-// waves per half) and stream their plane bytes with two groups of loads in
-// flight beyond the current one. Per group the planes are merged into the
+// The 4 WK compute waves (two or three per SIMD, which hide each other's
+// MFMA and LDS latencies) each own one weight tile and one of WK parts of
+// the groups (four waves per part) and stream their plane bytes with two
+// groups of loads in flight beyond the current one. Per group the planes are merged into the
 // 8-bit verify code of each weight,
 //   c = 16 q_b + q_r = 16 (q_b - h) + (q_r mod 16),   h = [q_r < 0],
 // an exact int8 (|c| <= 120): the base nibble less the refine sign goes to
@@ -30,15 +30,15 @@ namespace {
 using nest::kGroup;
 
 constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
-constexpr int kCW = 8;                   // compute waves per block (two per SIMD)
-constexpr int kWK = 2;                   // parts of the groups (one per compute wave row)
-constexpr int kWR = kCW / kWK;           // compute waves per part
+constexpr int kWR = 4;                   // compute waves per part of the groups (one per tile)
 constexpr int kBlockTiles = kWR * kRT;   // 16-row weight tiles per block (64 rows)
-constexpr int kThreads = (kCW + 1) * 64; // + the copy wave
+// WK parts of the groups (a template parameter): 4 WK compute waves, two or
+// three per SIMD, plus the copy wave
+constexpr int threads_for(int wk) { return (kWR * wk + 1) * 64; }
 constexpr int kLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
 // LDS ring slots per part of the groups: three (the copy wave runs two
 // groups ahead) when they fit, else two
-constexpr int ring_slots(int ctp) { return 3 * kWK * ctp * 2048 <= kLdsBytes ? 3 : 2; }
+constexpr int ring_slots(int ctp, int wk) { return 3 * wk * ctp * 2048 <= kLdsBytes ? 3 : 2; }
 constexpr int kSlots = 3;                // weight groups in flight per compute wave
 constexpr int kMaxCT = 9;                // 144 activation rows per launch
 constexpr int kXcds = 8;                 // blocks are dealt to the XCDs in turn
@@ -188,11 +188,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int CTP, bool DBG>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
+template <int CTP, int WK, bool DBG>
+__global__ void __launch_bounds__(threads_for(WK)) gemm_kernel(GemmArgs a) {
+  constexpr int kWK = WK, kCW = kWR * WK;
   constexpr int SB = CTP * 2048;               // LDS bytes of one group's activations
   constexpr int kCopies = kWK * 2 * CTP;       // copy instructions per step
-  constexpr int kNBuf = ring_slots(CTP);       // ring slots per part
+  constexpr int kNBuf = ring_slots(CTP, WK);   // ring slots per part
   constexpr int kAhead = kNBuf - 1;            // steps the copy wave runs ahead
   static_assert(kNBuf * kWK * SB <= kLdsBytes, "ring exceeds LDS");
   static_assert((kAhead - 1) * kCopies <= 63, "copies in flight exceed the vmcnt range");
@@ -343,24 +344,27 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int CTP, bool DBG>
+template <int CTP, int WK, bool DBG>
 int launch_gemm(const GemmArgs& a, int blocks, hipStream_t st) {
-  gemm_kernel<CTP, DBG><<<dim3(blocks), dim3(kThreads), 0, st>>>(a);
+  gemm_kernel<CTP, WK, DBG><<<dim3(blocks), dim3(threads_for(WK)), 0, st>>>(a);
   return nest::check_launch("verify_gemm(batched)");
 }
 
+// Blocks carrying few column tiles have little work per group: their
+// groups go to three parts (three compute waves per SIMD), which measured
+// faster there (4096 x 14336: 43 -> 39 us); more column tiles keep two.
 template <bool DBG>
 int launch_ctp(const GemmArgs& a, int ctp, int blocks, hipStream_t st) {
   switch (ctp) {
-    case 1: return launch_gemm<1, DBG>(a, blocks, st);
-    case 2: return launch_gemm<2, DBG>(a, blocks, st);
-    case 3: return launch_gemm<3, DBG>(a, blocks, st);
-    case 4: return launch_gemm<4, DBG>(a, blocks, st);
-    case 5: return launch_gemm<5, DBG>(a, blocks, st);
-    case 6: return launch_gemm<6, DBG>(a, blocks, st);
-    case 7: return launch_gemm<7, DBG>(a, blocks, st);
-    case 8: return launch_gemm<8, DBG>(a, blocks, st);
-    default: return launch_gemm<9, DBG>(a, blocks, st);
+    case 1: return launch_gemm<1, 3, DBG>(a, blocks, st);
+    case 2: return launch_gemm<2, 3, DBG>(a, blocks, st);
+    case 3: return launch_gemm<3, 3, DBG>(a, blocks, st);
+    case 4: return launch_gemm<4, 2, DBG>(a, blocks, st);
+    case 5: return launch_gemm<5, 2, DBG>(a, blocks, st);
+    case 6: return launch_gemm<6, 2, DBG>(a, blocks, st);
+    case 7: return launch_gemm<7, 2, DBG>(a, blocks, st);
+    case 8: return launch_gemm<8, 2, DBG>(a, blocks, st);
+    default: return launch_gemm<9, 2, DBG>(a, blocks, st);
   }
 }
 

@@ -361,7 +361,7 @@ int kv_nest_shadow_fill(const nest_kv* kv, const float* k, const float* v,
  *   ws       kv_nest_attend_workspace_size(...) bytes (no zero-fill
  *            needed)
  * Requires head_dim == 128, block == 128, Hq % Hkv == 0,
- * 1 <= nq*(Hq/Hkv) <= 64, and 16-byte aligned planes.
+ * 1 <= nq*(Hq/Hkv) <= 64, and 16-byte aligned planes and q.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
 int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,

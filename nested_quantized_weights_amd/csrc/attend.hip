@@ -103,6 +103,21 @@ __device__ __forceinline__ _Float16 bf16_to_h(uint16_t b) {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 8 bf16 query values (dims 8s .. 8s+7, two per word, even dim in the low
+// half) -> the f16 operand order [e0 e2 e4 e6 e1 e3 e5 e7] of codes_to_h8b
+__device__ __forceinline__ v8h bf16x8_to_op(uint4 w) {
+  v8h v;
+  v[0] = static_cast<_Float16>(__uint_as_float(w.x << 16));
+  v[1] = static_cast<_Float16>(__uint_as_float(w.y << 16));
+  v[2] = static_cast<_Float16>(__uint_as_float(w.z << 16));
+  v[3] = static_cast<_Float16>(__uint_as_float(w.w << 16));
+  v[4] = static_cast<_Float16>(__uint_as_float(w.x & 0xFFFF0000u));
+  v[5] = static_cast<_Float16>(__uint_as_float(w.y & 0xFFFF0000u));
+  v[6] = static_cast<_Float16>(__uint_as_float(w.z & 0xFFFF0000u));
+  v[7] = static_cast<_Float16>(__uint_as_float(w.w & 0xFFFF0000u));
+  return v;
+}
+
 __device__ __forceinline__ uint32_t word(uint4 v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -127,7 +142,9 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   const bool active = rt < RT;
 
   // Query operand of row rt*16 + c16, k-step s: dims 32*q4 + 8*s + [0 2 4 6 1 3 5 7].
-  v8h qop[4];
+  // Its raw bytes (four 16-byte loads) are requested with the first block's
+  // codes, and converted while those are on the way.
+  uint4 qraw[4];
   int pos = -1;
   {
     const int rho = rt * 16 + c16;
@@ -136,18 +153,45 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
       pos = a.ctx - a.nq + i;
       const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint16_t* p = qr + 8 * s;
-        v8h v;
-        v[0] = bf16_to_h(p[0]); v[1] = bf16_to_h(p[2]); v[2] = bf16_to_h(p[4]); v[3] = bf16_to_h(p[6]);
-        v[4] = bf16_to_h(p[1]); v[5] = bf16_to_h(p[3]); v[6] = bf16_to_h(p[5]); v[7] = bf16_to_h(p[7]);
-        qop[s] = v;
-      }
+      for (int s = 0; s < 4; ++s) qraw[s] = ld16(qr + 8 * s);
     } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qop[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int s = 0; s < 4; ++s) qraw[s] = make_uint4(0, 0, 0, 0);
     }
   }
+  const int b_first = chunk * a.bpw;
+  const int b_last = min(b_first + a.bpw, a.nbv);
+
+  // Phase A items of this thread: it = threadIdx.x + 256*rep is (t, q, r) with
+  // t = it >> 6 (K token tile / V dim tile), q = (it >> 4) & 3, r = it & 15.
+  // The next block's codes are loaded into registers while the current block
+  // is multiplied (software pipelining across blocks).
+  uint4 ck_b[2], ck_r[2], cv_b[2], cv_r[2];
+  auto load_codes = [&](int blk) {
+    const int t0 = blk * kBlk;
+    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int it = threadIdx.x + rep * 256;
+      const int t = it >> 6, q = (it >> 4) & 3, r = it & 15;
+      const int tok = 32 * (r >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (r & 3);
+      const size_t koff = (static_cast<size_t>(h) * a.cap + t0 + tok) * (kD / 2) + 16 * q;
+      const size_t voff = (hb * kD + t * 16 + r) * (kBlk / 2) + 16 * q;
+      ck_b[rep] = nest::ldnt16(a.kb + koff);
+      cv_b[rep] = nest::ldnt16(a.vb + voff);
+      if (VIEW) {
+        ck_r[rep] = nest::ldnt16(a.kr + koff);
+        cv_r[rep] = nest::ldnt16(a.vr + voff);
+      } else {
+        ck_r[rep] = make_uint4(0, 0, 0, 0);
+        cv_r[rep] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  if (b_first < b_last) load_codes(b_first);
+  v8h qop[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qop[s] = bf16x8_to_op(qraw[s]);
 
   // Biased codes in the tables (codes_to_h8b): in view 0 the odd dims of q
   // carry 1/16 (exact), and the row's bias sum(q * base) is one product with
@@ -173,37 +217,8 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
 
   const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
-  const int b_first = chunk * a.bpw;
-  const int b_last = min(b_first + a.bpw, a.nbv);
   // blocks ending at or before the first query's position need no mask
   const int pos_min = a.ctx - a.nq;
-
-  // Phase A items of this thread: it = threadIdx.x + 256*rep is (t, q, r) with
-  // t = it >> 6 (K token tile / V dim tile), q = (it >> 4) & 3, r = it & 15.
-  // The next block's codes are loaded into registers while the current block
-  // is multiplied (software pipelining across blocks).
-  uint4 ck_b[2], ck_r[2], cv_b[2], cv_r[2];
-  auto load_codes = [&](int blk) {
-    const int t0 = blk * kBlk;
-    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int it = threadIdx.x + rep * 256;
-      const int t = it >> 6, q = (it >> 4) & 3, r = it & 15;
-      const int tok = 32 * (r >> 2) + 8 * (t >> 1) + 4 * (t & 1) + (r & 3);
-      const size_t koff = (static_cast<size_t>(h) * a.cap + t0 + tok) * (kD / 2) + 16 * q;
-      const size_t voff = (hb * kD + t * 16 + r) * (kBlk / 2) + 16 * q;
-      ck_b[rep] = nest::ldnt16(a.kb + koff);
-      cv_b[rep] = nest::ldnt16(a.vb + voff);
-      if (VIEW) {
-        ck_r[rep] = nest::ldnt16(a.kr + koff);
-        cv_r[rep] = nest::ldnt16(a.vr + voff);
-      } else {
-        ck_r[rep] = cv_r[rep] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  if (b_first < b_last) load_codes(b_first);
 
   for (int blk = b_first; blk < b_last; ++blk) {
     const int t0 = blk * kBlk;
@@ -378,28 +393,62 @@ template <int VIEW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) attend_wave_kernel(AttArgs a) {
   __shared__ float ml[4][16][2];
   __shared__ float buf[4][16][kD + 4];  // each wave's rescaled O
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: block numbers, scale loads and branches on
+  // them stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int h = blockIdx.y, chunk = blockIdx.x;
 
-  v8h qop[4];
+  const int b_first = chunk * a.bpw;
+  const int b_last = min(b_first + a.bpw, a.nbv);
+  const int b0 = b_first + wave;  // the wave's blocks are b0, b0 + 4, ...
+
+  uint4 kb[8], kr[8], vb[8], vr[8];
+  float ks, vs;
+  // K codes first, then V: loads return in issue order, so the scores and
+  // the softmax of a block start while its V codes are still on the way
+  auto load = [&](int blk) {
+    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+    ks = a.ks[hb];
+    vs = a.vs[hb];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
+      const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
+      kb[tt] = nest::ldnt16(a.kb + koff);
+      kr[tt] = VIEW ? nest::ldnt16(a.kr + koff) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
+      vb[tt] = nest::ldnt16(a.vb + voff);
+      vr[tt] = VIEW ? nest::ldnt16(a.vr + voff) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // The query (dims 32*q4 .. 32*q4 + 31 of row c16: four 16-byte loads) and
+  // the first block's codes are requested together; the query operand and
+  // the bias product are formed while the codes are on the way.
+  uint4 qraw[4];
   int pos = -1;
   if (c16 < a.R) {
     const int i = c16 / a.grp, g = c16 % a.grp;
     pos = a.ctx - a.nq + i;
     const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint16_t* p = qr + 8 * s;
-      v8h v;
-      v[0] = bf16_to_h(p[0]); v[1] = bf16_to_h(p[2]); v[2] = bf16_to_h(p[4]); v[3] = bf16_to_h(p[6]);
-      v[4] = bf16_to_h(p[1]); v[5] = bf16_to_h(p[3]); v[6] = bf16_to_h(p[5]); v[7] = bf16_to_h(p[7]);
-      qop[s] = v;
-    }
+    for (int s = 0; s < 4; ++s) qraw[s] = ld16(qr + 8 * s);
   } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qop[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < 4; ++s) qraw[s] = make_uint4(0, 0, 0, 0);
   }
+  // unconditional (a wave without a block of its own reads the chunk's first
+  // block and discards it): a load under a branch makes the compiler copy
+  // the codes at the join, which waits for all of them
+  load(b0 < b_last ? b0 : b_first);
+  __builtin_amdgcn_sched_barrier(0);
+  v8h qop[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qop[s] = bf16x8_to_op(qraw[s]);
 
   // Biased codes (codes_to_h8b): in view 0 the odd dims of q carry 1/16
   // (exact), and the row's bias sum(q * base) is one product with the bias
@@ -425,37 +474,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
   const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
 
-  const int b_first = chunk * a.bpw;
-  const int b_last = min(b_first + a.bpw, a.nbv);
-  uint4 kb[8], kr[8], vb[8], vr[8];
-  // K codes first, then V: loads return in issue order, so the scores and
-  // the softmax of a block start while its V codes are still on the way
-  auto load = [&](int blk) {
-    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
-      const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
-      kb[tt] = nest::ldnt16(a.kb + koff);
-      kr[tt] = VIEW ? nest::ldnt16(a.kr + koff) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
-      vb[tt] = nest::ldnt16(a.vb + voff);
-      vr[tt] = VIEW ? nest::ldnt16(a.vr + voff) : make_uint4(0, 0, 0, 0);
-    }
-  };
   // Rows whose position is at least pos_min see every token of a block that
   // ends at or before pos_min; only later blocks need the causal mask.
   const int pos_min = a.ctx - a.nq;
   auto block = [&](int blk, bool first) {
-    load(blk);
     const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
-    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
     const int t0 = blk * kBlk;
-    const float sk = a.ks[hb] * sm_scale;
-    const float sv = VIEW ? a.vs[hb] * 0.0625f : a.vs[hb];
+    const float sk = ks * sm_scale;
+    const float sv = VIEW ? vs * 0.0625f : vs;
     v4f S[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -515,6 +541,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
       Ob *= alpha;
     }
     m = mn;
+    // a scheduling fence: the V codes are converted only here, after the
+    // softmax, so the scores never wait for them
+    __builtin_amdgcn_sched_barrier(0);
     // odd tokens' weights carry 1/16 in view 0 (biased V codes)
     const float svo = VIEW ? sv : sv * 0.0625f;
 #pragma unroll
@@ -531,10 +560,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
       Ob = mfma_h(bias_h8<VIEW>(), p, Ob);
     }
   };
-  // the first block of the wave is peeled: the running max and sum start
-  // there, so O needs no rescaling (most waves own a single block)
-  if (b_first + wave < b_last) block(b_first + wave, true);
-  for (int blk = b_first + wave + 4; blk < b_last; blk += 4) block(blk, false);
+  // the first block (already requested) starts the running max and sum, so
+  // O needs no rescaling there; most waves own a single block
+  if (b0 < b_last) {
+    block(b0, true);
+    for (int blk = b0 + 4; blk < b_last; blk += 4) {
+      load(blk);
+      __builtin_amdgcn_sched_barrier(0);
+      block(blk, false);
+    }
+  }
   // take the V bias off (every dim of a row has the same bias sum)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob[0];
@@ -735,6 +770,7 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
   if (!nest::aligned16(kv->k_base) || !nest::aligned16(kv->v_base) ||
       (view == 1 && (!nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))))
     return nest::fail(NEST_EALIGN, "%s: planes must be 16-byte aligned", what);
+  if (!nest::aligned16(q)) return nest::fail(NEST_EALIGN, "%s: q must be 16-byte aligned", what);
   const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_len);
   if (p.nchunk > kMaxChunks) return nest::fail(NEST_EUNSUPPORTED, "%s: too many chunks", what);
   if (!ws || ws_bytes < p.ws) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, p.ws);

@@ -2,14 +2,14 @@
 // base and the refinement plane) for more than 16 activation rows, e.g. 16
 // sequences x (k+1) = 144 rows: y = sa * fold_g s/16 * (sum q_a (16 q_b + q_r)).
 //
-// A block owns 64 weight rows (four 16-row tiles), a range of the
-// activation rows (CTP column tiles of 16) and all groups. Its last wave
-// only copies int8 activation rows from HBM/L2 into an LDS ring (direct
-// 16-byte loads to LDS, whole 128-byte rows of a group, two groups ahead).
-// The 4 WK compute waves (two or three per SIMD, which hide each other's
-// MFMA and LDS latencies) each own one weight tile and one of WK parts of
-// the groups (four waves per part) and stream their plane bytes with two
-// groups of loads in flight beyond the current one. Per group the planes are merged into the
+// A block owns WR 16-row weight tiles (four, i.e. 64 rows; two for some
+// shapes), a range of the activation rows (CTP column tiles of 16) and all
+// groups. Its last wave only copies int8 activation rows from HBM/L2 into an
+// LDS ring (direct 16-byte loads to LDS, whole 128-byte rows of a group, two
+// groups ahead). The WR WK compute waves (which hide each other's MFMA and
+// LDS latencies) each own one weight tile and one of WK parts of the groups
+// (WR waves per part) and stream their plane bytes with two groups of loads
+// in flight beyond the current one. Per group the planes are merged into the
 // 8-bit verify code of each weight,
 //   c = 16 q_b + q_r = 16 (q_b - h) + (q_r mod 16),   h = [q_r < 0],
 // an exact int8 (|c| <= 120): the base nibble less the refine sign goes to
@@ -30,11 +30,10 @@ namespace {
 using nest::kGroup;
 
 constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
-constexpr int kWR = 4;                   // compute waves per part of the groups (one per tile)
-constexpr int kBlockTiles = kWR * kRT;   // 16-row weight tiles per block (64 rows)
-// WK parts of the groups (a template parameter): 4 WK compute waves, two or
-// three per SIMD, plus the copy wave
-constexpr int threads_for(int wk) { return (kWR * wk + 1) * 64; }
+// WR 16-row weight tiles per block (a template parameter, 4 or 2) and WK
+// parts of the groups: WR WK compute waves, one per (tile, part), plus the
+// copy wave
+constexpr int threads_for(int wk, int wr) { return (wr * wk + 1) * 64; }
 constexpr int kLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
 // LDS ring slots per part of the groups: three (the copy wave runs two
 // groups ahead) when they fit, else two
@@ -188,9 +187,9 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int CTP, int WK, bool DBG>
-__global__ void __launch_bounds__(threads_for(WK)) gemm_kernel(GemmArgs a) {
-  constexpr int kWK = WK, kCW = kWR * WK;
+template <int CTP, int WK, int WR, bool DBG>
+__global__ void __launch_bounds__(threads_for(WK, WR)) gemm_kernel(GemmArgs a) {
+  constexpr int kWK = WK, kWR = WR, kCW = kWR * WK;
   constexpr int SB = CTP * 2048;               // LDS bytes of one group's activations
   constexpr int kCopies = kWK * 2 * CTP;       // copy instructions per step
   constexpr int kNBuf = ring_slots(CTP, WK);   // ring slots per part
@@ -344,28 +343,33 @@ __global__ void __launch_bounds__(threads_for(WK)) gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int CTP, int WK, bool DBG>
+template <int CTP, int WK, int WR, bool DBG>
 int launch_gemm(const GemmArgs& a, int blocks, hipStream_t st) {
-  gemm_kernel<CTP, WK, DBG><<<dim3(blocks), dim3(threads_for(WK)), 0, st>>>(a);
+  gemm_kernel<CTP, WK, WR, DBG><<<dim3(blocks), dim3(threads_for(WK, WR)), 0, st>>>(a);
   return nest::check_launch("verify_gemm(batched)");
 }
 
 // Blocks carrying few column tiles have little work per group: their
 // groups go to three parts (three compute waves per SIMD), which measured
 // faster there (4096 x 14336: 43 -> 39 us); more column tiles keep two.
-template <bool DBG>
+template <int WR, bool DBG>
 int launch_ctp(const GemmArgs& a, int ctp, int blocks, hipStream_t st) {
   switch (ctp) {
-    case 1: return launch_gemm<1, 3, DBG>(a, blocks, st);
-    case 2: return launch_gemm<2, 3, DBG>(a, blocks, st);
-    case 3: return launch_gemm<3, 3, DBG>(a, blocks, st);
-    case 4: return launch_gemm<4, 2, DBG>(a, blocks, st);
-    case 5: return launch_gemm<5, 2, DBG>(a, blocks, st);
-    case 6: return launch_gemm<6, 2, DBG>(a, blocks, st);
-    case 7: return launch_gemm<7, 2, DBG>(a, blocks, st);
-    case 8: return launch_gemm<8, 2, DBG>(a, blocks, st);
-    default: return launch_gemm<9, 2, DBG>(a, blocks, st);
+    case 1: return launch_gemm<1, 3, WR, DBG>(a, blocks, st);
+    case 2: return launch_gemm<2, 3, WR, DBG>(a, blocks, st);
+    case 3: return launch_gemm<3, 3, WR, DBG>(a, blocks, st);
+    case 4: return launch_gemm<4, 2, WR, DBG>(a, blocks, st);
+    case 5: return launch_gemm<5, 2, WR, DBG>(a, blocks, st);
+    case 6: return launch_gemm<6, 2, WR, DBG>(a, blocks, st);
+    case 7: return launch_gemm<7, 2, WR, DBG>(a, blocks, st);
+    case 8: return launch_gemm<8, 2, WR, DBG>(a, blocks, st);
+    default: return launch_gemm<9, 2, WR, DBG>(a, blocks, st);
   }
+}
+
+template <bool DBG>
+int launch_wr(const GemmArgs& a, int wr, int ctp, int blocks, hipStream_t st) {
+  return wr == 2 ? launch_ctp<2, DBG>(a, ctp, blocks, st) : launch_ctp<4, DBG>(a, ctp, blocks, st);
 }
 
 int device_cus() {
@@ -381,6 +385,28 @@ int device_cus() {
   return cus;
 }
 
+// Work split: four weight tiles per block, the activation rows split evenly
+// over P blocks per row block when the matrix alone would leave CUs idle
+// (P divides the column tiles). When that needs more blocks than CUs (a
+// partial second round of blocks on some CUs) and two-tile blocks over all
+// activation rows fit in one round, those are taken: LLaMA-3-8B qkv
+// (6144 x 4096, 144 rows) 23.9 -> 19.4 us, with the other linears' splits
+// measured best as they were.
+void plan_batched(int T, int CT, int cus, int& WR, int& P) {
+  WR = 4;
+  const int row_blocks = (T + 3) / 4;
+  P = 1;
+  for (int p = 1; p <= CT; ++p) {
+    if (CT % p) continue;
+    P = p;
+    if (4 * row_blocks * p >= 3 * cus) break;
+  }
+  if (row_blocks * P > cus && (T + 1) / 2 <= cus) {
+    WR = 2;
+    P = 1;
+  }
+}
+
 }  // namespace
 
 namespace nest {
@@ -394,19 +420,13 @@ int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const
   a.qa = qa; a.sa = sa; a.base = base; a.refine = refine; a.scales = scales;
   a.y = y; a.acc_dbg = acc_dbg;
   a.M = M; a.K = K; a.N = N; a.G = K / kGroup; a.T = (N + 15) / 16;
-  a.row_blocks = (a.T + kBlockTiles - 1) / kBlockTiles;
-  // Activation rows split evenly over P blocks per row block when the
-  // matrix alone would leave CUs idle (P divides the column tiles).
   const int CT = (M + 15) / 16;
-  int P = 1;
-  for (int p = 1; p <= CT; ++p) {
-    if (CT % p) continue;
-    P = p;
-    if (4 * a.row_blocks * p >= 3 * device_cus()) break;
-  }
+  int WR = 4, P = 1;
+  plan_batched(a.T, CT, device_cus(), WR, P);
+  a.row_blocks = (a.T + WR - 1) / WR;
   a.parts = P;
   const int blocks = ((a.row_blocks + kXcds - 1) / kXcds) * kXcds * P;
-  return acc_dbg ? launch_ctp<true>(a, CT / P, blocks, st) : launch_ctp<false>(a, CT / P, blocks, st);
+  return acc_dbg ? launch_wr<true>(a, WR, CT / P, blocks, st) : launch_wr<false>(a, WR, CT / P, blocks, st);
 }
 
 }  // namespace nest

@@ -154,12 +154,14 @@ def test_draft_gemv(ns, oracle, N, K, M):
     assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
 
 
-# M > 16 runs the batched kernel: (200, 2048, 144) splits each row block's
-# groups over 8 blocks, (1000, 1024, 144) over 4; K = 128 leaves one half of
-# a block's groups empty; (130, 384, 100) has an odd group count and ragged
-# row and activation tiles.
+# M > 16 runs the batched kernel: (200, 2048, 144) and (1000, 1024, 144)
+# split each row block's activation rows over 9 blocks (one column tile
+# each); K = 128 leaves one part of a block's groups empty; (130, 384, 100)
+# has an odd group count and ragged row and activation tiles; (5511, 256,
+# 144) has more row blocks than three parts of them fit in one round, so it
+# takes two-tile blocks (345 tiles, the last one partial).
 BATCHED_SHAPES = [(50, 512, 17), (200, 256, 144), (64, 384, 150), (200, 2048, 144), (1000, 1024, 144),
-                  (64, 128, 33), (130, 384, 100)]
+                  (64, 128, 33), (130, 384, 100), (5511, 256, 144)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMV_SHAPES + BATCHED_SHAPES)

@@ -281,31 +281,29 @@ __global__ void __launch_bounds__(threads_for(WK, WR)) gemm_kernel(GemmArgs a) {
   // clamped into the half, to group 0 for an empty half: branch-free and
   // in bounds), and every path through the loop issues the same loads
   auto gclamp = [&](int g) { return max(min(g, gb - 1), 0); };
-  WLoad w0[kRT], w1[kRT], w2[kRT];
+  WLoad w[kSlots][kRT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga), kq, idx, w0[rt]);
+  for (int sl = 0; sl < kSlots; ++sl)
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + 1), kq, idx, w1[rt]);
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + 2), kq, idx, w2[rt]);
-  auto step = [&](int j, WLoad (&w)[kRT]) {
+    for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + sl), kq, idx, w[sl][rt]);
+  auto step = [&](int j, WLoad (&ws)[kRT]) {
     lds_barrier();  // step j's activations are in the ring
     WOps o;
-    build_ops(w, o);
+    build_ops(ws, o);
     // the slot's registers are free again: request the group it serves next
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + j + kSlots), kq, idx, w[rt]);
+    for (int rt = 0; rt < kRT; ++rt) load_w(a, t[rt], gclamp(ga + j + kSlots), kq, idx, ws[rt]);
     if (ga + j < gb)
       gemm_group<CTP, DBG>(a, ring + ((j % kNBuf) * kWK + wk) * SB, lane, kq, idx, t, ga + j, ct0, o, run);
   };
   const int full = steps - steps % kSlots;
   for (int j = 0; j < full; j += kSlots) {
-    step(j, w0);
-    step(j + 1, w1);
-    step(j + 2, w2);
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) step(j + sl, w[sl]);
   }
-  if (full < steps) step(full, w0);
-  if (full + 1 < steps) step(full + 1, w1);
+#pragma unroll
+  for (int sl = 0; sl + 1 < kSlots; ++sl)
+    if (full + sl < steps) step(full + sl, w[sl]);
   lds_barrier();  // all copies landed and every wave is past the ring
 
   // parts wk > 0 hand their sums to wk = 0 through LDS (ring reused), which

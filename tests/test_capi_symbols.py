@@ -72,3 +72,30 @@ def test_host_validation_reports_errors_without_a_gpu(lib):
     ws.restype = ctypes.c_size_t
     ws.argtypes = [ctypes.c_int64] * 3
     assert ws(1, 8, 152064) > 0
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("k_base", ctypes.c_void_p), ("k_refine", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_base", ctypes.c_void_p), ("v_refine", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("capacity", ctypes.c_int64),
+                ("block", ctypes.c_int64)]
+
+
+def test_attend_host_validation_without_a_gpu(lib):
+    # kv_nest_attend checks its arguments (including a 16-byte aligned
+    # query: the kernels read it in 16-byte pieces) before any HIP call
+    lib.nest_last_error.restype = ctypes.c_char_p
+    f = lib.kv_nest_attend
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_KV), ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    p = ctypes.c_void_p(256)
+    kv = _KV(256, 256, 256, 256, 256, 256, 8, 128, 32768, 128)
+    ws = 1 << 24
+    assert f(ctypes.c_void_p(258), 1, 32, ctypes.byref(kv), 4096, 0, p, p, ws, None) == 2  # NEST_EALIGN
+    assert b"q must be 16-byte aligned" in lib.nest_last_error()
+    assert f(p, 1, 30, ctypes.byref(kv), 4096, 0, p, p, ws, None) == 3  # NEST_ESHAPE: 8 does not divide 30
+    assert f(p, 1, 32, ctypes.byref(kv), 4096, 2, p, p, ws, None) == 1  # NEST_EINVAL: view
+    assert f(p, 1, 32, ctypes.byref(kv), 40000, 0, p, p, ws, None) == 1  # ctx_len > capacity
+    assert f(p, 17, 32, ctypes.byref(kv), 4096, 1, p, p, ws, None) == 5  # NEST_EUNSUPPORTED: 68 rows
+    assert f(p, 1, 32, ctypes.byref(kv), 4096, 0, p, p, 16, None) == 4  # NEST_EWORKSPACE

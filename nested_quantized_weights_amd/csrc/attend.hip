@@ -385,11 +385,11 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
 // the loop has no LDS tables and no barrier. Several resident waves per
 // SIMD overlap one wave's loads with another's arithmetic. The 4 waves of a workgroup
 // take interleaved blocks of its chunk and merge once at the end, in LDS,
-// in the fixed order w = 3 .. 0.
+// in the fixed order w = 3 .. 0. The grid holds about two waves per SIMD
+// (one block per wave, kTargetWaves), so the register budget of two waves
+// per SIMD is free: the MFMA accumulators then stay in VGPRs (no AGPR round
+// trips per block).
 template <int VIEW>
-// The grid holds about two waves per SIMD (one block per wave, kTargetWaves),
-// so the register budget of two waves per SIMD is free: the MFMA
-// accumulators then stay in VGPRs (no AGPR round trips per block).
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) attend_wave_kernel(AttArgs a) {
   __shared__ float ml[4][16][2];
   __shared__ float buf[4][16][kD + 4];  // each wave's rescaled O

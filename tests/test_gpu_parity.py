@@ -282,10 +282,14 @@ def _rel_err(o, ref):
     return float(np.max(num / den))
 
 
+# Up to 16 query rows per kv head run the wave kernel: one 128-token block
+# per wave up to 2048 blocks in all (32/8 heads at ctx 20000: 1256), several
+# past that (8/8 heads at ctx 40000: 2504 blocks, two per wave).
 @pytest.mark.parametrize("view", [0, 1])
 @pytest.mark.parametrize("Hq,Hkv,cap,ctx,nq", [(32, 8, 256, 256, 1), (32, 8, 384, 300, 9),
                                                (28, 4, 512, 389, 5), (4, 1, 128, 1, 1),
-                                               (8, 8, 1024, 1000, 8), (16, 2, 2048, 2048, 8)])
+                                               (8, 8, 1024, 1000, 8), (16, 2, 2048, 2048, 8),
+                                               (32, 8, 20096, 20000, 1), (8, 8, 40960, 40000, 1)])
 def test_kv_attend(ns, oracle, view, Hq, Hkv, cap, ctx, nq):
     d = 128
     kf, vf = synth.kv(Hkv, cap, d, (230, Hq, cap))

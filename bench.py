@@ -410,8 +410,8 @@ def upload(ns, torch, inp):
 
 # Rounds of the timed region whose dominant launches carry HIP events: every
 # EVENT_STRIDE-th. An event record between two launches adds a gap of a few
-# microseconds to the stream (about 11 us per k=4 round with events around
-# all four LM-head launches), so the other rounds carry none.
+# microseconds to the stream (a k=4 round with events around all four
+# LM-head launches took about 22 us longer), so the other rounds carry none.
 EVENT_STRIDE = 10
 
 

@@ -186,7 +186,7 @@ int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
                    void* stream);
 
 /* draft_gemv -- the draft's W4A8 product over the base plane only (BitNest,
- * Figure 3: "the draft accesses only the base plane").
+ * Figure 3: the draft touches the base plane alone).
  *   qa       int8 [M][K], 16-byte aligned;  sa fp32 [M]
  *   base     base plane in the tile layout (nest_tile), 16-byte aligned
  *   scales   scales in the tile layout, 16-byte aligned

@@ -364,9 +364,9 @@ int oracle_kv_nest_pack(const float* kf, const float* vf, int64_t Hkv,
   return 0;
 }
 
-/* Append n tokens at positions pos .. pos+n-1 [BitNest Fig. 4: accepted
- * entries are retained; a rejected suffix is discarded by the caller's
- * length update and later overwritten by the next append]. kf and vf hold
+/* Append n tokens at positions pos .. pos+n-1 [BitNest Fig. 4: kept
+ * entries stay; a rejected suffix is dropped by the caller's length
+ * update and later overwritten by the next append]. kf and vf hold
  * every token's fp32 value [Hkv][cap][d]; the new values are written there,
  * then every block the new tokens touch is quantized again over its valid
  * tokens (those before pos + n), the rest taken as 0. A block that fills

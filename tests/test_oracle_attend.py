@@ -5,7 +5,7 @@ What fixes the expected values:
     dequantized through tests/formats.py (written from the documented K and V
     layouts), with the causal window given as an explicit mask;
   * BitNest, Figure 4: the draft's base view equals the full view of a cache
-    whose refinement planes are zero; "the rejected suffix is discarded":
+    whose refinement planes are zero; a rejected suffix is dropped:
     entries past ctx_len never change the output;
   * special cases: ctx = 1 gives o = v_0; identical keys give the mean of the
     visible values; one constant value per kv head exposes the GQA map;

@@ -1,7 +1,7 @@
 """Pins of the oracle's KV append (the cache write path after verification).
 
-BitNest, Figure 4: verification reads the full view of the same nested cache,
-accepted entries are retained and the rejected suffix is discarded. The
+BitNest, Figure 4: verification reads the full view of the same nested cache;
+kept entries stay and a rejected suffix is dropped. The
 append rule (a reading: each touched block is quantized again over its valid
 tokens, the rest taken as 0) is pinned by:
   * sealing: a block that fills equals the kv_nest_pack block of its values

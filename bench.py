@@ -79,7 +79,7 @@ DOMINANT = "draft_gemv_x(LM head, base plane, in-kernel act quant, fused argmax)
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "draft_gemv_lm_head.pmc.txt")
 GEMV_SRC = os.path.join(ROOT, "nested_quantized_weights_amd", "csrc", "gemv.hip")
 # ---------------------------------------------------------------------------
-# algorithmic bytes (what the method must move; stated in the design doc)
+# algorithmic bytes (what the method must move per call)
 # ---------------------------------------------------------------------------
 
 def gemv_bytes(N, K, M, planes, y=True, argmax=False, x_fp32=False):
@@ -724,7 +724,7 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: the benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "no multi-GPU path exists", file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:

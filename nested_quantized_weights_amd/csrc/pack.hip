@@ -226,9 +226,23 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
     if (t >= valid) return 0.0f;
     return t < old_end ? sh[t * a.d + j] : nw[(t0 + t - a.pos) * a.d + j];
   };
-  // 1. the block's max |v| over its valid tokens
+  // 1. the block's max |v| over its valid tokens: the shadow's tokens
+  // [0, old_end) and the new ones [old_end, valid) are two contiguous runs
+  // (read as float4 when aligned, so that a block takes one round trip)
   float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < valid * a.d; i += 256) m = fmaxf(m, fabsf(value(i / a.d, i % a.d)));
+  auto absmax_run = [&](const float* src, int64_t n) {
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (n & 3) == 0) {
+#pragma unroll 16
+      for (int64_t i = 4 * static_cast<int64_t>(threadIdx.x); i < n; i += 1024) {
+        const float4 v = *reinterpret_cast<const float4*>(src + i);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(src[i]));
+    }
+  };
+  absmax_run(sh, old_end * a.d);
+  absmax_run(nw + (t0 + old_end - a.pos) * a.d, (valid - old_end) * a.d);
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();

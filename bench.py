@@ -730,6 +730,9 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: one process per run; multi-rank launch is not supported", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: need --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
     import torch
 

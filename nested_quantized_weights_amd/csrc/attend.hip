@@ -11,12 +11,15 @@
 // 128-token blocks of one kv head and shares converted operands. Per block:
 //   phase A  all 256 threads read the block's codes once (K token-major, V
 //            dim-major) and convert them to f16 MFMA operands in LDS
-//            (32 KB K + 32 KB V). A nibble (or the 8-bit code biased by
-//            136) is put under the f16 exponent byte 0x64 by v_perm_b32,
-//            giving the exact f16 1024 + u. The bias is not subtracted per
-//            value: its contribution to a row's scores is one MFMA with a
-//            constant operand (taken off inside the exp2), and to O one
-//            more MFMA per 32 tokens (taken off at the end).
+//            (32 KB K + 32 KB V). An 8-bit code u (16*q_b + 8 biased by 128
+//            in the base view, 16*q_b + q_r biased by 136 in the full view)
+//            is put under the f16 exponent byte 0x64 by v_perm_b32, giving
+//            the exact f16 1024 + u. Both views thus carry codes at s/16
+//            with a bias of about 18 times their typical size. The bias is
+//            not subtracted per value: its contribution to a row's scores
+//            is one MFMA with a constant operand (taken off inside the
+//            exp2), and to O one more MFMA per 32 tokens (taken off at the
+//            end).
 //   phase B  waves split the query rows into 16-row tiles and, when rows
 //            are few, the block's four 32-token k-steps. Each keeps an
 //            online softmax (log2 domain, exp2f) and multiplies with
@@ -28,8 +31,18 @@
 // Waves that share a row tile merge in LDS in a fixed order, and each
 // workgroup writes one partial (max, sum, O) per row. A second kernel
 // merges the partials over chunks with log-sum-exp weights, also in a
-// fixed order. P enters the PV product as f16 scaled by the block's V
-// scale. Queries enter as f16 (bf16 -> f16 is exact in the normal range).
+// fixed order.
+//
+// Range. Only exact integers and values in [0, 1] pass through f16:
+//   - each query row is multiplied by a power of two 2^e chosen from its
+//     largest |value| (bf16 has fp32's exponent range, f16 does not), and
+//     2^-e goes into the fp32 score scale;
+//   - a block's softmax weights enter the PV product relative to the
+//     block's own largest score (so the largest is 1), and the V block
+//     scale together with the factor from the block's maximum to the
+//     running maximum multiply the block's fp32 product.
+// The result then does not depend on the magnitude of q, K or V beyond
+// fp32's range.
 #include "common.h"
 
 namespace {
@@ -59,17 +72,17 @@ __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t x, uint32_t y) { re
 // One 32-bit word of codes (8 elements e0..e7, e_{2b} in the low nibble of
 // byte b) -> 8 biased f16 code values in the order [e0 e2 e4 e6 e1 e3 e5 e7]:
 // f16 (1024 + u) with u the byte put under the exponent byte 0x64 by
-// v_perm_b32, i.e. base + (code or 16 code), one permute per two values. View 0: positions 0..3 (even elements) hold 1032 + c,
-// positions 4..7 (odd elements) hold 1152 + 16 c, so their partner operand
-// carries a factor 1/16. View 1: every position holds 1160 + c. The bias
-// is removed afterwards from whole sums (kernels below).
+// v_perm_b32, one permute per two values. View 0: u = 16*q_b + 128, i.e.
+// the value 1152 + 16*q_b. View 1: u = c + 136 with c = 16*q_b + q_r, i.e.
+// 1160 + c. Both are codes at s/16 plus a bias, removed afterwards from
+// whole sums (kernels below).
 template <int VIEW>
 __device__ __forceinline__ uint4 codes_to_h8b(uint32_t wb, uint32_t wr) {
   const uint32_t xb = wb ^ 0x88888888u;
   uint32_t ev, od;
   if (VIEW == 0) {
-    ev = xb & 0x0F0F0F0Fu;  // q_b + 8 of even elements
-    od = xb & 0xF0F0F0F0u;  // 16 (q_b + 8) of odd elements
+    ev = (xb << 4) & 0xF0F0F0F0u;  // 16 (q_b + 8) of even elements
+    od = xb & 0xF0F0F0F0u;         // 16 (q_b + 8) of odd elements
   } else {
     const uint32_t xr = wr ^ 0x88888888u;
     ev = bfi(0xF0F0F0F0u, xb << 4, xr);  // c + 136
@@ -84,12 +97,12 @@ __device__ __forceinline__ uint4 codes_to_h8b(uint32_t wb, uint32_t wr) {
   return r;
 }
 
-// The bias of each position of codes_to_h8b as an f16 operand (1032 / 1152
-// for view 0, 1160 for view 1): its product with a partner operand is the
-// amount to take off the biased product.
+// The bias of codes_to_h8b as an f16 operand (1152 for view 0, 1160 for
+// view 1): its product with a partner operand is the amount to take off
+// the biased product.
 template <int VIEW>
 __device__ __forceinline__ uint4 bias_h8() {
-  return VIEW == 0 ? make_uint4(0x64086408u, 0x64086408u, 0x64806480u, 0x64806480u)
+  return VIEW == 0 ? make_uint4(0x64806480u, 0x64806480u, 0x64806480u, 0x64806480u)
                    : make_uint4(0x64886488u, 0x64886488u, 0x64886488u, 0x64886488u);
 }
 
@@ -97,24 +110,44 @@ __device__ __forceinline__ v4f mfma_h(uint4 a, v8h b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ _Float16 bf16_to_h(uint16_t b) {
-  return static_cast<_Float16>(__uint_as_float(static_cast<uint32_t>(b) << 16));
-}
-
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Exponent e of a query row's power-of-two factor: the largest |value| of
+// the row (its 128 bf16 values are spread over the four lanes c16 + 16*q4,
+// 32 each in qraw) times 2^e lies in [2^14, 2^15), well inside f16's
+// normal range, and every bf16 value of the row times 2^e is then exactly
+// an f16 (8 significant bits) unless it is below 2^-28 of the largest.
+// An all-zero row gives 0.
+__device__ __forceinline__ int q_row_exp(const uint4 (&qraw)[4]) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+  mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 16, 64)));
+  mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 32, 64)));
+  if (mx == 0) return 0;
+  return 15 - __builtin_amdgcn_frexp_expf(__uint_as_float(mx << 16));
+}
+
 // 8 bf16 query values (dims 8s .. 8s+7, two per word, even dim in the low
-// half) -> the f16 operand order [e0 e2 e4 e6 e1 e3 e5 e7] of codes_to_h8b
-__device__ __forceinline__ v8h bf16x8_to_op(uint4 w) {
+// half) times 2^e -> the f16 operand order [e0 e2 e4 e6 e1 e3 e5 e7] of
+// codes_to_h8b
+__device__ __forceinline__ v8h bf16x8_to_op(uint4 w, int e) {
+  auto cv = [e](uint32_t bits) {
+    return static_cast<_Float16>(__builtin_amdgcn_ldexpf(__uint_as_float(bits), e));
+  };
   v8h v;
-  v[0] = static_cast<_Float16>(__uint_as_float(w.x << 16));
-  v[1] = static_cast<_Float16>(__uint_as_float(w.y << 16));
-  v[2] = static_cast<_Float16>(__uint_as_float(w.z << 16));
-  v[3] = static_cast<_Float16>(__uint_as_float(w.w << 16));
-  v[4] = static_cast<_Float16>(__uint_as_float(w.x & 0xFFFF0000u));
-  v[5] = static_cast<_Float16>(__uint_as_float(w.y & 0xFFFF0000u));
-  v[6] = static_cast<_Float16>(__uint_as_float(w.z & 0xFFFF0000u));
-  v[7] = static_cast<_Float16>(__uint_as_float(w.w & 0xFFFF0000u));
+  v[0] = cv(w.x << 16);
+  v[1] = cv(w.y << 16);
+  v[2] = cv(w.z << 16);
+  v[3] = cv(w.w << 16);
+  v[4] = cv(w.x & 0xFFFF0000u);
+  v[5] = cv(w.y & 0xFFFF0000u);
+  v[6] = cv(w.z & 0xFFFF0000u);
+  v[7] = cv(w.w & 0xFFFF0000u);
   return v;
 }
 
@@ -189,19 +222,15 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
     }
   };
   if (b_first < b_last) load_codes(b_first);
+  // the query operand of this lane's row, times the row's power of two
+  const int qe = q_row_exp(qraw);
   v8h qop[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qop[s] = bf16x8_to_op(qraw[s]);
+  for (int s = 0; s < 4; ++s) qop[s] = bf16x8_to_op(qraw[s], qe);
 
-  // Biased codes in the tables (codes_to_h8b): in view 0 the odd dims of q
-  // carry 1/16 (exact), and the row's bias sum(q * base) is one product with
-  // the bias operand, taken off every score of the row.
-  if (VIEW == 0) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 4; e < 8; ++e) qop[s][e] = qop[s][e] * static_cast<_Float16>(0.0625f);
-  }
+  // Biased codes in the tables (codes_to_h8b): the row's bias
+  // sum(q * bias) is one product with the bias operand, taken off every
+  // score of the row.
   float kbias;
   {
     v4f acc = v4f{0, 0, 0, 0};
@@ -211,12 +240,14 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   }
 
   float m = -INFINITY, l = 0.0f;
+  float Ob = 0.0f;  // the bias part of O (the same for every dim)
   v4f O[8];
-  v4f Ob = v4f{0, 0, 0, 0};  // the bias part of O (the same for every dim)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
 
-  const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
+  // score scale in log2 units: codes at s/16, 1/sqrt(128), and the
+  // query row's 2^-qe
+  const float sm_scale = __builtin_amdgcn_ldexpf(0.0625f * 0.08838834764831845f * kLog2e, -qe);
   // blocks ending at or before the first query's position need no mask
   const int pos_min = a.ctx - a.nq;
 
@@ -242,7 +273,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
     // ---- phase B: this wave's row tile over its k-steps ----
     if (active) {
       const float ck = a.ks[hb] * sm_scale;
-      const float sv = VIEW ? a.vs[hb] * 0.0625f : a.vs[hb];
+      const float sv = a.vs[hb] * 0.0625f;
       v4f S[2 * JS];
 #pragma unroll
       for (int jj = 0; jj < JS; ++jj)
@@ -272,11 +303,15 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
           }
       mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
       mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float mbs = mb == -INFINITY ? -INFINITY : (mb - kbias) * ck;
+      // weights relative to this block's largest score (largest weight 1),
+      // then beta = 2^(block max - running max) in fp32
+      const bool live = mb != -INFINITY;
+      const float mbs = live ? (mb - kbias) * ck : -INFINITY;
+      const float c2 = live ? fmaf(kbias, ck, mbs) : 0.0f;
       const float mn = fmaxf(m, mbs);
       const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float c2 = fmaf(kbias, ck, mu);
       const float alpha = __builtin_amdgcn_exp2f(m - mu);
+      const float beta = live ? __builtin_amdgcn_exp2f(mbs - mu) : 0.0f;
       float ls = 0.0f;
 #pragma unroll
       for (int k = 0; k < 2 * JS; ++k)
@@ -289,33 +324,40 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
         }
       ls += __shfl_xor(ls, 16, 64);
       ls += __shfl_xor(ls, 32, 64);
-      l = l * alpha + ls;
+      l = fmaf(ls, beta, l * alpha);
       m = mn;
+      // the block's product with weights in [0, 1], then the V scale and
+      // beta applied to it in fp32
+      v4f Ot[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
-      Ob *= alpha;
-      // odd tokens' weights carry 1/16 in view 0 (biased V codes)
-      const float svo = VIEW ? sv : sv * 0.0625f;
+      for (int dt = 0; dt < 8; ++dt) Ot[dt] = v4f{0, 0, 0, 0};
+      v4f Obt = v4f{0, 0, 0, 0};
 #pragma unroll
       for (int jj = 0; jj < JS; ++jj) {
         const v4f e0 = S[2 * jj], e1 = S[2 * jj + 1];
         v8h p;
-        p[0] = (_Float16)(e0[0] * sv); p[1] = (_Float16)(e0[2] * sv);
-        p[2] = (_Float16)(e1[0] * sv); p[3] = (_Float16)(e1[2] * sv);
-        p[4] = (_Float16)(e0[1] * svo); p[5] = (_Float16)(e0[3] * svo);
-        p[6] = (_Float16)(e1[1] * svo); p[7] = (_Float16)(e1[3] * svo);
+        p[0] = (_Float16)e0[0]; p[1] = (_Float16)e0[2];
+        p[2] = (_Float16)e1[0]; p[3] = (_Float16)e1[2];
+        p[4] = (_Float16)e0[1]; p[5] = (_Float16)e0[3];
+        p[6] = (_Float16)e1[1]; p[7] = (_Float16)e1[3];
         const int j = j0 + jj;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) O[dt] = mfma_h(vf[op_slot(dt, j, q4, c16)], p, O[dt]);
-        Ob = mfma_h(bias_h8<VIEW>(), p, Ob);
+        for (int dt = 0; dt < 8; ++dt) Ot[dt] = mfma_h(vf[op_slot(dt, j, q4, c16)], p, Ot[dt]);
+        Obt = mfma_h(bias_h8<VIEW>(), p, Obt);
       }
+      const float w = sv * beta;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[dt][i] = fmaf(w, Ot[dt][i], O[dt][i] * alpha);
+      Ob = fmaf(w, Obt[0], Ob * alpha);
     }
     __syncthreads();  // the next block's phase A overwrites the tables
   }
 
   // take the V bias off (every dim of a row has the same bias sum)
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob[0];
+  for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob;
 
   // ---- write this workgroup's partial per row ----
   const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;
@@ -446,19 +488,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   // the codes at the join, which waits for all of them
   load(b0 < b_last ? b0 : b_first);
   __builtin_amdgcn_sched_barrier(0);
+  // the query operand of this lane's row, times the row's power of two
+  const int qe = q_row_exp(qraw);
   v8h qop[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qop[s] = bf16x8_to_op(qraw[s]);
+  for (int s = 0; s < 4; ++s) qop[s] = bf16x8_to_op(qraw[s], qe);
 
-  // Biased codes (codes_to_h8b): in view 0 the odd dims of q carry 1/16
-  // (exact), and the row's bias sum(q * base) is one product with the bias
-  // operand, taken off every score of the row.
-  if (VIEW == 0) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 4; e < 8; ++e) qop[s][e] = qop[s][e] * static_cast<_Float16>(0.0625f);
-  }
+  // Biased codes (codes_to_h8b): the row's bias sum(q * bias) is one
+  // product with the bias operand, taken off every score of the row.
   float kbias;
   {
     v4f acc = v4f{0, 0, 0, 0};
@@ -468,11 +505,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   }
 
   float m = -INFINITY, l = 0.0f;
+  float Ob = 0.0f;  // the bias part of O (the same for every dim)
   v4f O[8];
-  v4f Ob = v4f{0, 0, 0, 0};  // the bias part of O (the same for every dim)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = v4f{0, 0, 0, 0};
-  const float sm_scale = (VIEW ? 0.0625f : 1.0f) * 0.08838834764831845f * kLog2e;  // 1/sqrt(128)
+  // score scale in log2 units: codes at s/16, 1/sqrt(128), and the query
+  // row's 2^-qe
+  const float sm_scale = __builtin_amdgcn_ldexpf(0.0625f * 0.08838834764831845f * kLog2e, -qe);
 
   // Rows whose position is at least pos_min see every token of a block that
   // ends at or before pos_min; only later blocks need the causal mask.
@@ -481,7 +520,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
     const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
     const int t0 = blk * kBlk;
     const float sk = ks * sm_scale;
-    const float sv = VIEW ? vs * 0.0625f : vs;
+    const float sv = vs * 0.0625f;
     v4f S[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -512,13 +551,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mbs = mb == -INFINITY ? -INFINITY : (mb - kbias) * sk;
+    // p = 2^(score - block max) in [0, 1] (up to rounding), the largest 1:
+    // the hardware exp2 (flushing results below 2^-126 to zero, which no
+    // sum here can notice); masked tokens give 0. beta = 2^(block max -
+    // running max) carries the block to the running maximum in fp32.
+    const bool live = mb != -INFINITY;
+    const float mbs = live ? (mb - kbias) * sk : -INFINITY;
+    const float c2 = live ? fmaf(kbias, sk, mbs) : 0.0f;
     const float mn = fmaxf(m, mbs);
     const float mu = mn == -INFINITY ? 0.0f : mn;
-    const float c2 = fmaf(kbias, sk, mu);
-    // p = 2^((S - kbias) sk - mu) <= 1 (up to rounding): the hardware exp2
-    // (flushing results below 2^-126 to zero, which no sum here can
-    // notice); masked tokens give 0
+    const float beta = live ? __builtin_amdgcn_exp2f(mbs - mu) : 0.0f;
     float ls = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
@@ -531,33 +573,48 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
       }
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
-    if (first) {
-      l = ls;  // O is still zero: nothing to rescale
-    } else {
-      const float alpha = __builtin_amdgcn_exp2f(m - mu);
-      l = l * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
-      Ob *= alpha;
-    }
+    const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(m - mu);
+    l = first ? ls * beta : fmaf(ls, beta, l * alpha);
     m = mn;
     // a scheduling fence: the V codes are converted only here, after the
     // softmax, so the scores never wait for them
     __builtin_amdgcn_sched_barrier(0);
-    // odd tokens' weights carry 1/16 in view 0 (biased V codes)
-    const float svo = VIEW ? sv : sv * 0.0625f;
+    // the block's product with the weights in [0, 1]; the V scale and
+    // beta are applied to it in fp32 (the first block accumulates straight
+    // into O, which is still zero)
+    v4f Ot[8];
+    v4f Obt = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) Ot[dt] = v4f{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const v4f e0 = S[2 * j], e1 = S[2 * j + 1];
       v8h p;
-      p[0] = (_Float16)(e0[0] * sv); p[1] = (_Float16)(e0[2] * sv);
-      p[2] = (_Float16)(e1[0] * sv); p[3] = (_Float16)(e1[2] * sv);
-      p[4] = (_Float16)(e0[1] * svo); p[5] = (_Float16)(e0[3] * svo);
-      p[6] = (_Float16)(e1[1] * svo); p[7] = (_Float16)(e1[3] * svo);
+      p[0] = (_Float16)e0[0]; p[1] = (_Float16)e0[2];
+      p[2] = (_Float16)e1[0]; p[3] = (_Float16)e1[2];
+      p[4] = (_Float16)e0[1]; p[5] = (_Float16)e0[3];
+      p[6] = (_Float16)e1[1]; p[7] = (_Float16)e1[3];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint4 vop = codes_to_h8b<VIEW>(word(dk[dt], j), word(dr[dt], j));
+        if (first)
+          O[dt] = mfma_h(vop, p, O[dt]);
+        else
+          Ot[dt] = mfma_h(vop, p, Ot[dt]);
+      }
+      Obt = mfma_h(bias_h8<VIEW>(), p, Obt);
+    }
+    const float w = sv * beta;
+    if (first) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt] *= w;
+      Ob = w * Obt[0];
+    } else {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        O[dt] = mfma_h(codes_to_h8b<VIEW>(word(dk[dt], j), word(dr[dt], j)), p, O[dt]);
-      Ob = mfma_h(bias_h8<VIEW>(), p, Ob);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[dt][i] = fmaf(w, Ot[dt][i], O[dt][i] * alpha);
+      Ob = fmaf(w, Obt[0], Ob * alpha);
     }
   };
   // the first block (already requested) starts the running max and sum, so
@@ -572,7 +629,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   }
   // take the V bias off (every dim of a row has the same bias sum)
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob[0];
+  for (int dt = 0; dt < 8; ++dt) O[dt] -= Ob;
 
   // merge the 4 waves (fixed order w = 3 .. 0) and write the chunk's partial
   if (q4 == 0) {

@@ -108,10 +108,10 @@ def activations(m: int, k: int, key) -> np.ndarray:
     return normal((m, k), key)
 
 
-def kv(n_kv_heads: int, capacity: int, head_dim: int, key):
-    """fp32 K and V, each [Hkv][capacity][d], ~ N(0, 1)."""
-    return (normal((n_kv_heads, capacity, head_dim), tuple(key) + (0,)),
-            normal((n_kv_heads, capacity, head_dim), tuple(key) + (1,)))
+def kv(n_kv_heads: int, capacity: int, head_dim: int, key, k_std: float = 1.0, v_std: float = 1.0):
+    """fp32 K and V, each [Hkv][capacity][d], ~ N(0, k_std) and N(0, v_std)."""
+    return (normal((n_kv_heads, capacity, head_dim), tuple(key) + (0,), k_std),
+            normal((n_kv_heads, capacity, head_dim), tuple(key) + (1,), v_std))
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -125,9 +125,9 @@ def bf16_bits_to_float(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def queries_bf16(nq: int, n_q_heads: int, head_dim: int, key) -> np.ndarray:
-    """bf16 bit patterns [nq][Hq][d] of N(0, 1) draws."""
-    return to_bf16_bits(normal((nq, n_q_heads, head_dim), key))
+def queries_bf16(nq: int, n_q_heads: int, head_dim: int, key, std: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns [nq][Hq][d] of N(0, std) draws."""
+    return to_bf16_bits(normal((nq, n_q_heads, head_dim), key, std))
 
 
 def plant_drafts(target: np.ndarray, alpha: float, vocab: int, key) -> np.ndarray:

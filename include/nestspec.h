@@ -26,24 +26,29 @@
  * Conventions for every entry point
  * ---------------------------------------------------------------------------
  *  - Every buffer pointer is a DEVICE pointer unless the argument says
- *    "host". The caller allocates and owns every buffer it passes.
+ *    "host". The caller allocates and owns every buffer it passes,
+ *    workspaces included; the library allocates, frees and keeps no device
+ *    memory of its own and never synchronises.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call enqueues its kernels on that stream and returns without
  *    synchronising.
- *  - The library keeps two pieces of device memory of its own per (device,
- *    stream), allocated on first use and held until the process ends: a
- *    256-byte block counter for the argmax GEMVs (left at zero by every
- *    launch) and the buffer of the fp32 entry points that quantize first
- *    (grown on demand; growing it synchronises that stream). Calls on one
- *    stream run in order and so share them safely; hipStreamPerThread is
- *    told apart by the calling host thread.
+ *  - Workspaces: sizes come from the *_workspace_size functions. The GEMV
+ *    workspaces (draft_gemv, draft_gemv_x, verify_gemm_x, verify_accept,
+ *    verify_accept_x) are 256-byte aligned and must be all zero before
+ *    their first use; every call leaves the part that must stay zero (a
+ *    block counter in the first 256 bytes) at zero, so one workspace serves
+ *    any number of calls. Calls that share a workspace must not overlap in
+ *    time (same stream, or ordered by events).
+ *  - Lengths that change from round to round can live on the device: the
+ *    calls that take a position or a context length also take an optional
+ *    device int32 pointer whose value is added to the host value, so a
+ *    loop of rounds can advance them (verify_accept does) without the host
+ *    reading anything back.
  *  - Arguments are checked on the host before anything is launched. On an
  *    error nothing is launched, the return value is a nest_status code, and
  *    nest_last_error() holds a message for the calling thread. A launch
  *    failure returns NEST_EHIP. A device fault surfaces at the caller's
  *    next synchronisation.
- *  - Calls that share a workspace must not overlap in time (same stream, or
- *    ordered by events).
  *  - Input floats must be finite.
  *
  * ---------------------------------------------------------------------------
@@ -142,7 +147,7 @@ extern "C" {
 typedef enum {
   NEST_OK = 0,
   NEST_EINVAL = 1,       /* null pointer, negative or inconsistent size   */
-  NEST_EALIGN = 2,       /* a pointer is not 16-byte aligned              */
+  NEST_EALIGN = 2,       /* a pointer is not 16- (or 256-) byte aligned   */
   NEST_ESHAPE = 3,       /* a size breaks a divisibility rule             */
   NEST_EWORKSPACE = 4,   /* workspace missing or smaller than required    */
   NEST_EUNSUPPORTED = 5, /* valid, but not a shape these kernels handle   */
@@ -194,10 +199,10 @@ int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
  *   argmax   int32 [M] (out, nullable). When given, the fold is exact and
  *            argmax[m] is the index of the largest y[m][.].
  *   acc_dbg  int32 [M][N][K/group] (out, nullable): the exact Ab.
- *   ws       workspace of draft_gemv_workspace_size(M, N) bytes, 16-byte
- *            aligned, needed only when argmax is given (else it may be
- *            NULL). It holds per-block partial maxima; no initial contents
- *            are required.
+ *   ws       workspace of draft_gemv_workspace_size(M, N) bytes (zeroed
+ *            before first use, see the conventions), needed only when
+ *            argmax is given (else it may be NULL). It holds the per-block
+ *            partial maxima and the counter that finds the last block.
  * Requires 1 <= M <= 16, group == 128, K % 128 == 0, N >= 1.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
@@ -207,25 +212,31 @@ int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                void* ws, size_t ws_bytes, void* stream);
 size_t draft_gemv_workspace_size(int64_t M, int64_t N);
 
+/* Workspace of the fp32-activation GEMV calls: draft_gemv_x, verify_gemm_x
+ * (M rows) and verify_accept_x (M = B*(k+1)) over N output rows (V for the
+ * LM head) and reduction length K. 0 if the sizes are invalid. */
+size_t nest_gemv_x_workspace_size(int64_t M, int64_t K, int64_t N);
+
 /* draft_gemv_x -- draft_gemv on fp32 activations. Each block quantizes x
  * itself while staging it (the nest_act_quant rule above), so the result is
  * bit-identical to nest_act_quant followed by draft_gemv, with one launch
  * fewer.
  *   x        fp32 [M][K], 16-byte aligned
  *   the rest as for draft_gemv (no debug accumulators)
+ *   ws       nest_gemv_x_workspace_size(M, K, N) bytes, zeroed before first
+ *            use (always required)
  * Requires 1 <= M <= 16. Activations with M*K > 131072 (beyond the LDS
  * budget for codes), and several rows that many blocks would each quantize
  * again (N*M*K >= 1.2e8, M >= 2), are quantized once by a nest_act_quant
- * launch into a buffer the library keeps per stream (allocated on first
- * use, grown on demand); the codes are the same either way.
+ * launch into the workspace; the codes are the same either way.
  * Errors: as draft_gemv. */
 int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
                  const float* scales, int64_t N, int64_t group, float* y,
                  int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
 
 /* verify_gemm -- the target's W8A8 product over both planes (BitNest,
- * Figure 3: "the target accesses both planes to recover the full 8-bit
- * representation"), for the k+1 rows of a round or a batch of rounds.
+ * Figure 3: the target reads the refinement plane as well and so works with
+ * the whole 8-bit code), for the k+1 rows of a round or a batch of rounds.
  *   qa int8 [M][K] (16-byte aligned); sa fp32 [M]
  *   base, refine, scales: the tile layout (nest_tile), 16-byte aligned
  *   y fp32 [M][N] (out); acc_dbg int32 [M][N][K/group] (out, nullable): Av
@@ -240,12 +251,14 @@ int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
 
 /* verify_gemm_x -- verify_gemm on fp32 activations, quantized in the kernel
  * as for draft_gemv_x (bit-identical to nest_act_quant + verify_gemm), or
- * first quantized into the library's per-stream buffer under the same rule
- * (always when M > 16, which then runs the batched kernel).
- * Requires M >= 1. Errors: as verify_gemm. */
+ * first quantized into the workspace under the same rule (always when
+ * M > 16, which then runs the batched kernel).
+ *   ws  nest_gemv_x_workspace_size(M, K, N) bytes, zeroed before first use
+ * Requires M >= 1. Errors: as verify_gemm, and NEST_EWORKSPACE. */
 int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
                   const uint8_t* refine, const float* scales, int64_t N,
-                  int64_t group, float* y, void* stream);
+                  int64_t group, float* y, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* verify_accept -- the verify pass through the nested LM head, with the
  * greedy accept step ("How Speculative Decoding Speeds Up Inference",
@@ -261,8 +274,17 @@ int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
  *             d_i == t_{i-1} for all 1 <= i <= j
  *   emitted   int32 [B][k+1] (out): t_0..t_a, then -1 in the unused slots
  *   y         fp32 [B*(k+1)][V] (out, nullable): the verify logits
- *   ws        verify_accept_workspace_size(B, k, V) bytes, 16-byte aligned
- *             (per-block partial maxima; no initial contents are required).
+ *   len       int32 [B] (in/out, nullable): each sequence's committed
+ *             length, advanced by n_emitted (BitNest, Figure 4: the
+ *             accepted entries stay; the blog's round step 3: the next pass
+ *             starts after the kept tokens). A loop that keeps its cache
+ *             length here passes the same pointer to kv_nest_append,
+ *             kv_nest_attend and nest_rope_split.
+ *   next      int32 [B] (out, nullable): t_a, the last emitted token, which
+ *             is the next round's slot-0 input
+ *   ws        verify_accept_workspace_size(B, k, V) bytes, zeroed before
+ *             first use (per-block partial maxima and the last-block
+ *             counter).
  * Requires B >= 1, k >= 0, B*(k+1) <= 16, group == 128, K % 128 == 0.
  * Draft ids are not read on the host, so an id outside [0, V) simply
  * never matches. Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE,
@@ -271,21 +293,22 @@ int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64_t k,
                   int64_t K, const uint8_t* base, const uint8_t* refine,
                   const float* scales, int64_t V, int64_t group,
                   const int32_t* draft, int32_t* target, int32_t* n_emitted,
-                  int32_t* emitted, float* y, void* ws, size_t ws_bytes,
-                  void* stream);
+                  int32_t* emitted, float* y, int32_t* len, int32_t* next,
+                  void* ws, size_t ws_bytes, void* stream);
 size_t verify_accept_workspace_size(int64_t B, int64_t k, int64_t V);
 
 /* verify_accept_x -- verify_accept on fp32 activations x [B*(k+1)][K]
  * (16-byte aligned), quantized in the kernel as for draft_gemv_x
  * (bit-identical to nest_act_quant + verify_accept); when
  * B*(k+1)*K > 131072 the activations are first quantized into the
- * library's per-stream buffer. Errors: as verify_accept. */
+ * workspace, of nest_gemv_x_workspace_size(B*(k+1), K, V) bytes (zeroed
+ * before first use). Errors: as verify_accept. */
 int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K,
                     const uint8_t* base, const uint8_t* refine,
                     const float* scales, int64_t V, int64_t group,
                     const int32_t* draft, int32_t* target, int32_t* n_emitted,
-                    int32_t* emitted, float* y, void* ws, size_t ws_bytes,
-                    void* stream);
+                    int32_t* emitted, float* y, int32_t* len, int32_t* next,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* Nested KV cache: a host struct holding device pointers (layouts above). */
 typedef struct nest_kv {
@@ -329,7 +352,12 @@ int kv_nest_pack(const float* k, const float* v, int64_t n_kv_heads,
  *             keeps it so for the next append at any pos' in
  *             (floor(pos/block)*block, pos+n].
  *   k_new, v_new  fp32 [Hkv][n][d]
- *   pos, n    host values: pos >= 0, 1 <= n <= block, pos + n <= capacity
+ *   pos_dev   int32 (device, nullable): when given, the first position is
+ *             *pos_dev + pos, read by the kernel; an append that would then
+ *             start below 0 or end past capacity writes nothing
+ *   pos, n    host values: the first position (or its offset from
+ *             *pos_dev) and the token count; 1 <= n <= block, and without
+ *             pos_dev pos >= 0, pos + n <= capacity
  * A touched block with L valid tokens (those before pos + n) is quantized as
  * kv_nest_pack quantizes a block whose tokens from L on are 0: its scale
  * covers the valid tokens only and the padding codes are 0; a block that
@@ -337,8 +365,8 @@ int kv_nest_pack(const float* k, const float* v, int64_t n_kv_heads,
  * are not written.
  * Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EUNSUPPORTED, NEST_EHIP. */
 int kv_nest_append(const nest_kv* kv, float* shadow_k, float* shadow_v,
-                   const float* k_new, const float* v_new, int64_t pos,
-                   int64_t n, void* stream);
+                   const float* k_new, const float* v_new, const int32_t* pos_dev,
+                   int64_t pos, int64_t n, void* stream);
 size_t kv_nest_shadow_floats(int64_t n_kv_heads, int64_t head_dim,
                              int64_t block); /* per shadow (K or V); 0 if invalid */
 
@@ -356,17 +384,24 @@ int kv_nest_shadow_fill(const nest_kv* kv, const float* k, const float* v,
  * and which reads both planes.
  *   q        bf16 bit patterns [nq][Hq][d]
  *   kv       host pointer to a nest_kv
- *   ctx_len  host value: visible cache length, nq <= ctx_len <= capacity
+ *   ctx_dev  int32 (device, nullable): when given, the visible length is
+ *            *ctx_dev + ctx_len, read by the kernels and clamped into
+ *            [nq, capacity]; the grid then covers the whole capacity
+ *   ctx_len  host value: the visible cache length, nq <= ctx_len <=
+ *            capacity (or, with ctx_dev, the offset added to it,
+ *            0 <= ctx_len <= capacity)
  *   out      fp32 [nq][Hq][d] (out)
- *   ws       kv_nest_attend_workspace_size(...) bytes (no zero-fill
- *            needed)
+ *   ws       kv_nest_attend_workspace_size(nq, Hq, Hkv, d, L) bytes with
+ *            L = ctx_len, or L = capacity when ctx_dev is given (no
+ *            zero-fill needed)
  * Requires head_dim == 128, block == 128, Hq % Hkv == 0,
  * 1 <= nq*(Hq/Hkv) <= 64, and 16-byte aligned planes and q.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
 int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
-                   const nest_kv* kv, int64_t ctx_len, int view, float* out,
-                   void* ws, size_t ws_bytes, void* stream);
+                   const nest_kv* kv, const int32_t* ctx_dev, int64_t ctx_len,
+                   int view, float* out, void* ws, size_t ws_bytes,
+                   void* stream);
 size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
                                      int64_t n_kv_heads, int64_t head_dim,
                                      int64_t ctx_len);
@@ -449,14 +484,15 @@ int nest_add_rmsnorm(float* x, const float* y, const float* gamma, int64_t M,
 
 /* Rotary embedding and q/k/v split of a QKV projection qkv
  * [M][(Hq + 2 Hkv) * d] (q heads, then k heads, then v heads). Row m is at
- * position pos0 + m; pair (i, i + d/2) of a q or k head is rotated by
- * (pos0 + m) * theta^(-2i/d) (rotate-half convention). Outputs: q as bf16
+ * position p_m = pos0 + m, plus *pos_dev when pos_dev (device int32,
+ * nullable) is given; pair (i, i + d/2) of a q or k head is rotated by
+ * p_m * theta^(-2i/d) (rotate-half convention). Outputs: q as bf16
  * bit patterns [M][Hq][d] (nearest, ties to even), ready for
  * kv_nest_attend; k and v fp32, laid out [Hkv][M][d] (token_major = 0, the
  * kv_nest_append layout for M tokens) or [M][Hkv][d] (token_major = 1, so
  * that each token's slice is a [Hkv][1][d] append). d even, theta > 1.
  * Errors: NEST_EINVAL, NEST_EUNSUPPORTED, NEST_EHIP. */
-int nest_rope_split(const float* qkv, int64_t M, int64_t pos0,
+int nest_rope_split(const float* qkv, int64_t M, const int32_t* pos_dev, int64_t pos0,
                     int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim,
                     float theta, int token_major, uint16_t* q, float* k,
                     float* v, void* stream);
@@ -502,6 +538,20 @@ void nest_alpha_init(nest_alpha* st, double decay, double prior_accepted,
                      double prior_rejected);
 void nest_alpha_update(nest_alpha* st, int64_t accepted, int64_t k);
 double nest_alpha_value(const nest_alpha* st);
+
+/* ---------------------------------------------------------------------------
+ * Calibration
+ * --------------------------------------------------------------------------- */
+
+/* nest_read_stream -- read `bytes` of device memory once as a plain stream
+ * (16-byte nontemporal loads, as the weight and cache streams use), folding
+ * them into one word xored into *sink. Its rate is what a kernel that reads
+ * each byte once can reach on the device: the "achievable" bandwidth the
+ * kernels' roofline fractions are also quoted against.
+ *   src   device, 16-byte aligned;  bytes  a positive multiple of 16
+ *   sink  uint32 (device)
+ * Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EALIGN, NEST_EHIP. */
+int nest_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

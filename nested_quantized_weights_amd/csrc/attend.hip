@@ -57,7 +57,8 @@ constexpr int kTargetWaves = 2048;  // wave kernel: waves to aim for (eight per 
 struct AttArgs {
   const uint16_t* q;
   int nq, Hq, grp, R;  // R = nq * grp query rows per kv head
-  int ctx, nbv;        // visible length and visible blocks
+  int ctx;             // visible length (an offset added to *ctx_dev when that is given)
+  const int32_t* ctx_dev;  // device word holding the rest of the length, or null
   const uint8_t *kb, *kr, *vb, *vr;
   const float *ks, *vs;
   int cap, nb;         // capacity and blocks per head in the planes
@@ -155,6 +156,15 @@ __device__ __forceinline__ uint32_t word(uint4 v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// The visible length of a call: the host value, plus the device word when
+// one is given. A device length outside [nq, capacity] is clamped into it,
+// so no read leaves the planes.
+__device__ __forceinline__ int live_ctx(const AttArgs& a) {
+  if (!a.ctx_dev) return a.ctx;
+  const long long c = static_cast<long long>(a.ctx) + *a.ctx_dev;
+  return static_cast<int>(c < a.nq ? a.nq : (c > a.cap ? a.cap : c));
+}
+
 // LDS operand tables (uint4 = 8 f16):
 //   K: slot ((tt*4 + s)*4 + q)*16 + r: token tau(tt, r), dims 32q + 8s + [0 2 4 6 1 3 5 7]
 //   V: slot ((dt*4 + j)*4 + q)*16 + r: dim dt*16 + r, tokens 32q + 8j + [0 2 4 6 1 3 5 7]
@@ -171,6 +181,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int h = blockIdx.y, chunk = blockIdx.x;
+  const int ctx = live_ctx(a), nbv = (ctx + kBlk - 1) / kBlk;
   const int rt = wave / TS, tp = wave % TS, j0 = tp * JS;
   const bool active = rt < RT;
 
@@ -183,7 +194,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
     const int rho = rt * 16 + c16;
     if (active && rho < a.R) {
       const int i = rho / a.grp, g = rho % a.grp;
-      pos = a.ctx - a.nq + i;
+      pos = ctx - a.nq + i;
       const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
       for (int s = 0; s < 4; ++s) qraw[s] = ld16(qr + 8 * s);
@@ -193,7 +204,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
     }
   }
   const int b_first = chunk * a.bpw;
-  const int b_last = min(b_first + a.bpw, a.nbv);
+  const int b_last = min(b_first + a.bpw, nbv);
 
   // Phase A items of this thread: it = threadIdx.x + 256*rep is (t, q, r) with
   // t = it >> 6 (K token tile / V dim tile), q = (it >> 4) & 3, r = it & 15.
@@ -249,7 +260,7 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   // query row's 2^-qe
   const float sm_scale = __builtin_amdgcn_ldexpf(0.0625f * 0.08838834764831845f * kLog2e, -qe);
   // blocks ending at or before the first query's position need no mask
-  const int pos_min = a.ctx - a.nq;
+  const int pos_min = ctx - a.nq;
 
   for (int blk = b_first; blk < b_last; ++blk) {
     const int t0 = blk * kBlk;
@@ -440,9 +451,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int h = blockIdx.y, chunk = blockIdx.x;
+  const int ctx = live_ctx(a), nbv = (ctx + kBlk - 1) / kBlk;
 
   const int b_first = chunk * a.bpw;
-  const int b_last = min(b_first + a.bpw, a.nbv);
+  const int b_last = min(b_first + a.bpw, nbv);
   const int b0 = b_first + wave;  // the wave's blocks are b0, b0 + 4, ...
 
   uint4 kb[8], kr[8], vb[8], vr[8];
@@ -475,7 +487,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   int pos = -1;
   if (c16 < a.R) {
     const int i = c16 / a.grp, g = c16 % a.grp;
-    pos = a.ctx - a.nq + i;
+    pos = ctx - a.nq + i;
     const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qraw[s] = ld16(qr + 8 * s);
@@ -515,7 +527,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   // Rows whose position is at least pos_min see every token of a block that
   // ends at or before pos_min; only later blocks need the causal mask.
-  const int pos_min = a.ctx - a.nq;
+  const int pos_min = ctx - a.nq;
   auto block = [&](int blk, bool first) {
     const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
     const int t0 = blk * kBlk;
@@ -801,8 +813,8 @@ extern "C" size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads, i
 }
 
 extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
-                              int64_t ctx_len, int view, float* out, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
   const char* what = "kv_nest_attend";
   if (!q || !kv || !out) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (!kv->k_base || !kv->v_base || !kv->k_scale || !kv->v_scale)
@@ -817,7 +829,8 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
     return nest::fail(NEST_EUNSUPPORTED, "%s: head_dim and block must be 128", what);
   if (n_q_heads % Hkv) return nest::fail(NEST_ESHAPE, "%s: Hq %% Hkv != 0", what);
   if (kv->capacity % kBlk) return nest::fail(NEST_ESHAPE, "%s: capacity %% block != 0", what);
-  if (ctx_len < nq || ctx_len > kv->capacity)
+  if (ctx_dev ? (ctx_len < 0 || ctx_len > kv->capacity || nq > kv->capacity)
+              : (ctx_len < nq || ctx_len > kv->capacity))
     return nest::fail(NEST_EINVAL, "%s: need nq <= ctx_len <= capacity (ctx_len=%lld)", what,
                       (long long)ctx_len);
   const int64_t R = nq * (n_q_heads / Hkv);
@@ -828,13 +841,15 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
       (view == 1 && (!nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))))
     return nest::fail(NEST_EALIGN, "%s: planes must be 16-byte aligned", what);
   if (!nest::aligned16(q)) return nest::fail(NEST_EALIGN, "%s: q must be 16-byte aligned", what);
-  const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_len);
+  // with the length on the device, the grid covers the whole capacity and
+  // the workgroups past the live length write empty partials
+  const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
   if (p.nchunk > kMaxChunks) return nest::fail(NEST_EUNSUPPORTED, "%s: too many chunks", what);
   if (!ws || ws_bytes < p.ws) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, p.ws);
   if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
   AttArgs a{};
   a.q = q; a.nq = (int)nq; a.Hq = (int)n_q_heads; a.grp = (int)(n_q_heads / Hkv); a.R = (int)R;
-  a.ctx = (int)ctx_len; a.nbv = p.nbv;
+  a.ctx = (int)ctx_len; a.ctx_dev = ctx_dev;
   a.kb = kv->k_base; a.kr = kv->k_refine; a.vb = kv->v_base; a.vr = kv->v_refine;
   a.ks = kv->k_scale; a.vs = kv->v_scale;
   a.cap = (int)kv->capacity; a.nb = (int)(kv->capacity / kBlk);

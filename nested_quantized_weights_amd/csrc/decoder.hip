@@ -64,7 +64,8 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 struct RopeArgs {
   const float* qkv;  // [M][(Hq + 2 Hkv) d]
   int M, Hq, Hkv, d;
-  int64_t pos0;
+  int64_t pos0;            // position of row 0, or an offset added to *pos_dev
+  const int32_t* pos_dev;  // device word holding the rest of the position, or null
   float log2_theta;
   int token_major;  // K/V out as [M][Hkv][d] (1) or [Hkv][M][d] (0)
   uint16_t* q;      // bf16 [M][Hq][d]
@@ -77,12 +78,13 @@ struct RopeArgs {
 // (i, i + d/2); q rounded to bf16, v copied.
 __global__ void __launch_bounds__(64) rope_split_kernel(RopeArgs a) {
   const int m = blockIdx.x, h = blockIdx.y, i = threadIdx.x, half = a.d / 2;
+  const int64_t pos = a.pos0 + (a.pos_dev ? *a.pos_dev : 0) + m;
   const float* src = a.qkv + static_cast<size_t>(m) * (a.Hq + 2 * a.Hkv) * a.d + static_cast<size_t>(h) * a.d;
   for (int j = i; j < half; j += 64) {
     const float x1 = src[j], x2 = src[j + half];
     if (h < a.Hq + a.Hkv) {
       const float inv_freq = exp2f(-(2.0f * static_cast<float>(j) / static_cast<float>(a.d)) * a.log2_theta);
-      const float ang = static_cast<float>(a.pos0 + m) * inv_freq;
+      const float ang = static_cast<float>(pos) * inv_freq;
       float s, c;
       sincosf(ang, &s, &c);
       const float o1 = x1 * c - x2 * s, o2 = x2 * c + x1 * s;
@@ -151,20 +153,21 @@ extern "C" int nest_add_rmsnorm(float* x, const float* y, const float* gamma, in
   return nest::check_launch(what);
 }
 
-extern "C" int nest_rope_split(const float* qkv, int64_t M, int64_t pos0, int64_t n_q_heads, int64_t n_kv_heads,
+extern "C" int nest_rope_split(const float* qkv, int64_t M, const int32_t* pos_dev, int64_t pos0,
+                               int64_t n_q_heads, int64_t n_kv_heads,
                                int64_t head_dim, float theta, int token_major, uint16_t* q, float* k, float* v,
                                void* stream) {
   const char* what = "nest_rope_split";
   if (!qkv || !q || !k || !v) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   int rc = check_rows(what, M, head_dim);
   if (rc) return rc;
-  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads + 2 * n_kv_heads > 65535 || head_dim % 2 || pos0 < 0 ||
-      pos0 > (1LL << 24))
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads + 2 * n_kv_heads > 65535 || head_dim % 2 ||
+      (!pos_dev && pos0 < 0) || pos0 > (1LL << 24) || pos0 < -(1LL << 24))
     return nest::fail(NEST_EINVAL, "%s: heads=%lld/%lld head_dim=%lld pos0=%lld", what, (long long)n_q_heads,
                       (long long)n_kv_heads, (long long)head_dim, (long long)pos0);
   if (!(theta > 1.0f)) return nest::fail(NEST_EINVAL, "%s: theta must be > 1", what);
   RopeArgs a{qkv, static_cast<int>(M), static_cast<int>(n_q_heads), static_cast<int>(n_kv_heads),
-             static_cast<int>(head_dim), pos0, log2f(theta), token_major ? 1 : 0, q, k, v};
+             static_cast<int>(head_dim), pos0, pos_dev, log2f(theta), token_major ? 1 : 0, q, k, v};
   rope_split_kernel<<<dim3(static_cast<unsigned>(M), static_cast<unsigned>(n_q_heads + 2 * n_kv_heads)), 64, 0,
                       nest::as_stream(stream)>>>(a);
   return nest::check_launch(what);

@@ -26,12 +26,24 @@
 // activations instead: every block quantizes them itself while staging
 // (s_a = max|x|/127 per row, q = clamp(rint(x/s_a), +-127), the rule of
 // nest_act_quant), so the round needs no separate quantization launch.
-// Blocks loop over tiles with a grid
-// stride, and the grid is at most what fits on the chip. The argmax path
-// keeps per-lane best (value, index) keys across tiles and writes one key
-// per row and block. A second small kernel reduces the keys and, for
-// verify_accept, applies the accept rule. The kernel boundary makes the
-// keys visible, with no cross-block fence or atomic.
+// Blocks loop over tiles with a grid stride, and the grid is at most what
+// fits on the chip.
+//
+// The argmax path keeps per-lane best (value, index) keys across tiles and
+// writes one key per row and block into the caller's workspace; the last
+// block to finish (a counter in the workspace, zero between calls) reduces
+// every block's keys and writes the argmax or, for verify_accept, applies
+// the accept rule. Why the last block sees every key: each block writes
+// its keys with agent-scope atomic stores (on gfx950 these carry sc1 and
+// are written through to the agent's coherence point rather than left in
+// one XCD's L2), waits until those stores are acknowledged (s_waitcnt 0
+// covers stores on this architecture), and only then increments the
+// counter with an agent-scope atomic. The block whose increment returns
+// gridDim - 1 therefore runs after every other block's keys have reached
+// the coherence point, and it reads them with agent-scope atomic loads
+// (sc1, served from that point). This is the ordering a release/acquire
+// pair would give, without the release's write-back of the whole L2, which
+// nothing here needs because no plain store carries data between blocks.
 #include "nibble.h"
 
 namespace {
@@ -52,7 +64,9 @@ struct FinishArgs {
   int32_t* target;
   int32_t* n_emitted;
   int32_t* emitted;
-  bool accept;  // apply the greedy accept rule (else write argmax_out)
+  int32_t* len;   // accept: [B] committed lengths advanced by n_emitted (nullable)
+  int32_t* next;  // accept: [B] the last emitted token, the next round's input (nullable)
+  bool accept;    // apply the greedy accept rule (else write argmax_out)
 };
 
 struct GemvArgs {
@@ -67,8 +81,8 @@ struct GemvArgs {
   float* y;
   int32_t* acc_dbg;
   unsigned long long* partials;  // argmax: [gridDim.x][16]
-  unsigned* done;                // argmax: finished-block counter (zero at launch), or null
-  FinishArgs fin;                // argmax with done: what the last block writes
+  unsigned* done;                // argmax: finished-block counter (zero at launch)
+  FinishArgs fin;                // argmax: what the last block writes
 };
 
 
@@ -550,30 +564,23 @@ gemv_kernel(GemvArgs a) {
       unsigned long long k = 0;
       for (int w = 0; w < WAVES; ++w) k = umax64(k, bw[w][threadIdx.x]);
       unsigned long long* slot = a.partials + static_cast<size_t>(blockIdx.x) * 16 + threadIdx.x;
-      if (a.done)
-        __hip_atomic_store(slot, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        *slot = k;
+      __hip_atomic_store(slot, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (a.done) {
-      // The last block to finish reduces every block's keys. Keys go out
-      // with device-scope stores, and each block waits for its stores to
-      // complete before it counts itself done, so the last block (which
-      // reads them with device-scope loads) sees all of them; it then
-      // leaves the counter at zero for the next launch on the stream.
-      __shared__ int last_sh;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0) last_sh = atomicAdd(a.done, 1u) == gridDim.x - 1;
-      __syncthreads();
-      if (last_sh) {
-        FinishArgs f = a.fin;
-        f.partials = a.partials;
-        f.nparts = gridDim.x;
-        f.M = a.M;
-        finish_reduce<WAVES * 64, true>(f);
-        if (threadIdx.x == 0) atomicExch(a.done, 0u);
-      }
+    // The last block to finish reduces every block's keys (the ordering
+    // argument is in the file header), then leaves the counter at zero for
+    // the next launch that uses this workspace.
+    __shared__ int last_sh;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) last_sh = atomicAdd(a.done, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (last_sh) {
+      FinishArgs f = a.fin;
+      f.partials = a.partials;
+      f.nparts = gridDim.x;
+      f.M = a.M;
+      finish_reduce<WAVES * 64>(f);
+      if (threadIdx.x == 0) atomicExch(a.done, 0u);
     }
   }
 }
@@ -583,16 +590,14 @@ gemv_kernel(GemvArgs a) {
 // NT threads; thread t reads the keys of blocks t, t + NT, ..., all loads
 // issued before any is used, so the reduction waits for one round trip to
 // memory. Rows are then reduced per wave (shuffles) and across the waves
-// (LDS). COHERENT: the keys were written by other blocks of the running
-// kernel with device-scope stores and are read with device-scope loads
-// (past the non-coherent per-XCD caches).
-template <int NT, bool COHERENT>
+// (LDS). The keys were written by other blocks of the running kernel with
+// agent-scope stores and are read with agent-scope loads.
+template <int NT>
 __device__ void finish_reduce(const FinishArgs& f) {
   constexpr int kPer = kMaxArgmaxBlocks / NT, kW = NT / 64;
   __shared__ unsigned long long red[16][kW];
   __shared__ int32_t tgt[16];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int nv = (f.M + 1) >> 1;  // 16-byte pairs of keys per block
   unsigned long long best[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) best[r] = 0;
@@ -601,22 +606,10 @@ __device__ void finish_reduce(const FinishArgs& f) {
     const int b = t + j * NT;
     if (b < f.nparts) {
       const unsigned long long* p = f.partials + static_cast<size_t>(b) * 16;
-      if (COHERENT) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < f.M)
-            best[i] = umax64(best[i], __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      } else {
-        const uint4* p4 = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i < nv) {
-            const uint4 w = p4[i];
-            best[2 * i] = umax64(best[2 * i], (static_cast<unsigned long long>(w.y) << 32) | w.x);
-            best[2 * i + 1] = umax64(best[2 * i + 1], (static_cast<unsigned long long>(w.w) << 32) | w.z);
-          }
-        }
-      }
+      for (int i = 0; i < 16; ++i)
+        if (i < f.M)
+          best[i] = umax64(best[i], __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
   }
 #pragma unroll
@@ -647,12 +640,10 @@ __device__ void finish_reduce(const FinishArgs& f) {
       f.target[b * k1 + j] = tgt[b * k1 + j];
       f.emitted[b * k1 + j] = j <= acc ? tgt[b * k1 + j] : -1;
     }
+    if (f.len) f.len[b] += acc + 1;
+    if (f.next) f.next[b] = tgt[b * k1 + acc];
   }
 }
-
-// The finishing step as its own launch (one block of 1024 threads), for
-// when no block counter is available.
-__global__ void __launch_bounds__(1024) argmax_finish_kernel(FinishArgs f) { finish_reduce<1024, false>(f); }
 
 // ---------------------------------------------------------------------------
 // host side
@@ -739,27 +730,50 @@ size_t argmax_ws_bytes(int N) {
   return static_cast<size_t>(min(iters, kMaxArgmaxBlocks)) * 16 * sizeof(unsigned long long);
 }
 
-// The exact-fold argmax GEMV and its finishing kernel.
+// Workspace of the GEMV entry points (all offsets 256-byte aligned):
+//   [0, 256)             the argmax kernels' finished-block counter; zero
+//                        before the first call, and every call leaves it zero
+//   [256, 256 + P)       per-block argmax keys, P = argmax_ws_bytes(N)
+//   then, for fp32 activations (the *_x entry points), M*K int8 codes and M
+//   fp32 row scales, used when the codes are made by a separate
+//   nest_act_quant launch rather than inside the GEMV.
+constexpr size_t kCounterBytes = 256;
+constexpr size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N, bool x) {
+  size_t n = kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
+  if (x) n += round256(static_cast<size_t>(M) * K) + round256(static_cast<size_t>(M) * sizeof(float));
+  return n;
+}
+
+struct Workspace {
+  unsigned* counter;
+  unsigned long long* partials;
+  int8_t* codes;  // fp32-activation paths only
+  float* code_scales;
+};
+
+Workspace carve(void* ws, int64_t M, int64_t K, int64_t N) {
+  char* p = static_cast<char*>(ws);
+  Workspace w{};
+  w.counter = reinterpret_cast<unsigned*>(p);
+  w.partials = reinterpret_cast<unsigned long long*>(p + kCounterBytes);
+  char* c = p + kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
+  w.codes = reinterpret_cast<int8_t*>(c);
+  w.code_scales = reinterpret_cast<float*>(c + round256(static_cast<size_t>(M) * K));
+  return w;
+}
+
+// The exact-fold argmax GEMV; its last block reduces the keys.
 template <int PLANES, bool DBG>
-int launch_argmax(GemvArgs a, const FinishArgs& f0, bool accept, hipStream_t st, const char* what) {
+int launch_argmax(GemvArgs a, const FinishArgs& f0, bool accept, const Workspace& w, hipStream_t st,
+                  const char* what) {
   a.nseg = 1;
-  FinishArgs f = f0;
-  f.accept = accept;
-  // with a block counter the GEMV's last block finishes the reduction;
-  // otherwise a second launch does
-  a.done = nest::stream_counter(st);
-  if (a.done) {
-    a.fin = f;
-    return launch_gemv<PLANES, true, DBG>(a, st, what, kMaxArgmaxBlocks, nullptr);
-  }
-  int used = 0;
-  int rc = launch_gemv<PLANES, true, DBG>(a, st, what, kMaxArgmaxBlocks, &used);
-  if (rc) return rc;
-  f.partials = a.partials;
-  f.nparts = used;
-  f.M = a.M;
-  argmax_finish_kernel<<<1, 1024, 0, st>>>(f);
-  return nest::check_launch(what);
+  a.done = w.counter;
+  a.partials = w.partials;
+  a.fin = f0;
+  a.fin.accept = accept;
+  return launch_gemv<PLANES, true, DBG>(a, st, what, kMaxArgmaxBlocks, nullptr);
 }
 
 // Activations of a call: int8 codes with their row scales, or fp32 values
@@ -790,40 +804,33 @@ int check_common(const char* what, const Act& act, int64_t M, int64_t K, const u
   return NEST_OK;
 }
 
-// fp32 activations are quantized inside the GEMV when they fit its LDS
-// budget. A separate nest_act_quant launch into library scratch (per
-// stream) comes first when they do not fit, or when several rows would be
-// quantized again by each of many blocks (N*M*K at least kQuantFirst:
-// there one launch is cheaper than the blocks' staging; measured on the
-// 5- and 9-row verify of 3584x37888 and 18944x3584 linears). The codes
-// are the same either way.
-constexpr double kQuantFirst = 1.2e8;
-
-int quantize_first(const char* what, Act& act, int64_t M, int64_t K, int64_t N, hipStream_t st,
-                   bool by_size) {
-  if (!act.x) return NEST_OK;
-  const bool fits = M <= 16 && M * K <= kLdsActMaxX;
-  const bool heavy = by_size && M >= 2 && static_cast<double>(N) * M * K >= kQuantFirst;
-  if (fits && !heavy) return NEST_OK;
-  const size_t qbytes = (static_cast<size_t>(M) * K + 255) & ~static_cast<size_t>(255);
-  void* p = nest::stream_scratch(st, qbytes + static_cast<size_t>(M) * sizeof(float));
-  if (!p) {
-    if (fits) return NEST_OK;  // stay with the in-kernel path
-    return nest::fail(NEST_EHIP, "%s: cannot allocate %lld x %lld activation codes", what, (long long)M,
-                      (long long)K);
-  }
-  int8_t* qa = static_cast<int8_t*>(p);
-  float* sa = reinterpret_cast<float*>(static_cast<char*>(p) + qbytes);
-  const int rc = nest_act_quant(act.x, M, K, qa, sa, st);
-  if (rc) return rc;
-  act = Act{qa, sa, nullptr};
+int check_ws(const char* what, const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || ws_bytes < need) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return nest::fail(NEST_EALIGN, "%s: workspace must be 256-byte aligned", what);
   return NEST_OK;
 }
 
-int check_ws(const char* what, const void* ws, size_t ws_bytes, int N) {
-  if (!ws || ws_bytes < argmax_ws_bytes(N))
-    return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, argmax_ws_bytes(N));
-  if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
+// fp32 activations are quantized inside the GEMV when they fit its LDS
+// budget. A separate nest_act_quant launch into the workspace comes first
+// when they do not fit, or when several rows would be quantized again by
+// each of many blocks (N*M*K at least kQuantFirst: there one launch is
+// cheaper than the blocks' staging; measured on the 5- and 9-row verify of
+// 3584x37888 and 18944x3584 linears). The codes are the same either way.
+constexpr double kQuantFirst = 1.2e8;
+
+bool needs_quantize_first(int64_t M, int64_t K, int64_t N, bool by_size) {
+  const bool fits = M <= 16 && M * K <= kLdsActMaxX;
+  const bool heavy = by_size && M >= 2 && static_cast<double>(N) * M * K >= kQuantFirst;
+  return !fits || heavy;
+}
+
+int quantize_first(Act& act, int64_t M, int64_t K, int64_t N, const Workspace& w, hipStream_t st,
+                   bool by_size) {
+  if (!act.x || !needs_quantize_first(M, K, N, by_size)) return NEST_OK;
+  const int rc = nest_act_quant(act.x, M, K, w.codes, w.code_scales, st);
+  if (rc) return rc;
+  act = Act{w.codes, w.code_scales, nullptr};
   return NEST_OK;
 }
 
@@ -843,19 +850,21 @@ int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uin
   if (rc) return rc;
   if (M > 16) return nest::fail(NEST_EUNSUPPORTED, "%s: M=%lld > 16", what, (long long)M);
   if (!y && !argmax) return nest::fail(NEST_EINVAL, "%s: need y or argmax", what);
+  if (act.x || argmax) {
+    rc = check_ws(what, ws, ws_bytes, gemv_ws_bytes(M, K, N, act.x != nullptr));
+    if (rc) return rc;
+  }
   hipStream_t st = nest::as_stream(stream);
+  const Workspace w = ws ? carve(ws, M, K, N) : Workspace{};
   Act act2 = act;
-  rc = quantize_first(what, act2, M, K, N, st, true);
+  rc = quantize_first(act2, M, K, N, w, st, true);
   if (rc) return rc;
   GemvArgs a = make_args(act2, M, K, base, nullptr, scales, N, y, acc_dbg);
   if (argmax) {
-    rc = check_ws(what, ws, ws_bytes, a.N);
-    if (rc) return rc;
-    a.partials = static_cast<unsigned long long*>(ws);
     FinishArgs f{};
     f.argmax_out = argmax;
-    return acc_dbg ? launch_argmax<1, true>(a, f, false, st, what)
-                   : launch_argmax<1, false>(a, f, false, st, what);
+    return acc_dbg ? launch_argmax<1, true>(a, f, false, w, st, what)
+                   : launch_argmax<1, false>(a, f, false, w, st, what);
   }
   a.nseg = pick_split((a.N + 15) / 16, a.G, max_split(1));
   return acc_dbg ? launch_gemv<1, false, true>(a, st, what, 1 << 30, nullptr)
@@ -864,15 +873,21 @@ int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uin
 
 int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const uint8_t* base,
                 const uint8_t* refine, const float* scales, int64_t N, int64_t group, float* y,
-                int32_t* acc_dbg, void* stream) {
+                int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(what, act, M, K, base, scales, N, group);
   if (rc) return rc;
   if (!refine || !y) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "%s: refine not 16-byte aligned", what);
+  if (act.x) {
+    rc = check_ws(what, ws, ws_bytes, gemv_ws_bytes(M, K, N, true));
+    if (rc) return rc;
+  }
   hipStream_t st = nest::as_stream(stream);
   Act act2 = act;
-  rc = quantize_first(what, act2, M, K, N, st, true);
-  if (rc) return rc;
+  if (act.x) {
+    rc = quantize_first(act2, M, K, N, carve(ws, M, K, N), st, true);
+    if (rc) return rc;
+  }
   if (M <= 16) {
     GemvArgs a = make_args(act2, M, K, base, refine, scales, N, y, acc_dbg);
     a.nseg = pick_split((a.N + 15) / 16, a.G, max_split(2));
@@ -893,43 +908,46 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
 int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t K, const uint8_t* base,
                 const uint8_t* refine, const float* scales, int64_t V, int64_t group,
                 const int32_t* draft, int32_t* target, int32_t* n_emitted, int32_t* emitted, float* y,
-                void* ws, size_t ws_bytes, void* stream) {
+                int32_t* len, int32_t* next, void* ws, size_t ws_bytes, void* stream) {
   if (B < 1 || k < 0) return nest::fail(NEST_EINVAL, "%s: B=%lld k=%lld", what, (long long)B, (long long)k);
   if (B * (k + 1) > 16)
     return nest::fail(NEST_EUNSUPPORTED, "%s: B*(k+1)=%lld > 16", what, (long long)(B * (k + 1)));
-  int rc = check_common(what, act, B * (k + 1), K, base, scales, V, group);
+  const int64_t M = B * (k + 1);
+  int rc = check_common(what, act, M, K, base, scales, V, group);
   if (rc) return rc;
   if (!refine || !target || !n_emitted || !emitted || (k > 0 && !draft))
     return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (!nest::aligned16(refine)) return nest::fail(NEST_EALIGN, "%s: refine not 16-byte aligned", what);
   if (V > 0x7fffffffLL) return nest::fail(NEST_EUNSUPPORTED, "%s: V too large", what);
-  rc = check_ws(what, ws, ws_bytes, (int)V);
+  rc = check_ws(what, ws, ws_bytes, gemv_ws_bytes(M, K, V, act.x != nullptr));
   if (rc) return rc;
   hipStream_t st = nest::as_stream(stream);
+  const Workspace w = carve(ws, M, K, V);
   Act act2 = act;  // the LM head stays with in-kernel quantization whenever it fits
-  rc = quantize_first(what, act2, B * (k + 1), K, V, st, false);
+  rc = quantize_first(act2, M, K, V, w, st, false);
   if (rc) return rc;
-  GemvArgs a = make_args(act2, B * (k + 1), K, base, refine, scales, V, y, nullptr);
-  a.partials = static_cast<unsigned long long*>(ws);
+  GemvArgs a = make_args(act2, M, K, base, refine, scales, V, y, nullptr);
   FinishArgs f{};
   f.B = (int)B; f.k = (int)k; f.draft = draft; f.target = target; f.n_emitted = n_emitted;
-  f.emitted = emitted;
-  return launch_argmax<2, false>(a, f, true, st, what);
+  f.emitted = emitted; f.len = len; f.next = next;
+  return launch_argmax<2, false>(a, f, true, w, st, what);
 }
 
 }  // namespace
 
 extern "C" size_t draft_gemv_workspace_size(int64_t M, int64_t N) {
-  (void)M;
-  if (N < 1 || N > (1LL << 30)) return 0;
-  return argmax_ws_bytes(static_cast<int>(N));
+  if (M < 1 || N < 1 || N > (1LL << 30)) return 0;
+  return gemv_ws_bytes(M, 0, N, false);
 }
 
 extern "C" size_t verify_accept_workspace_size(int64_t B, int64_t k, int64_t V) {
-  (void)B;
-  (void)k;
-  if (V < 1 || V > (1LL << 30)) return 0;
-  return argmax_ws_bytes(static_cast<int>(V));
+  if (B < 1 || k < 0 || V < 1 || V > (1LL << 30)) return 0;
+  return gemv_ws_bytes(B * (k + 1), 0, V, false);
+}
+
+extern "C" size_t nest_gemv_x_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M < 1 || K < 1 || N < 1 || N > (1LL << 30) || K > (1LL << 24) || M > (1LL << 20)) return 0;
+  return gemv_ws_bytes(M, K, N, true);
 }
 
 extern "C" int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t K,
@@ -952,31 +970,32 @@ extern "C" int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t
                            const uint8_t* base, const uint8_t* refine, const float* scales,
                            int64_t N, int64_t group, float* y, int32_t* acc_dbg, void* stream) {
   return verify_impl("verify_gemm", Act{qa, sa, nullptr}, M, K, base, refine, scales, N, group, y,
-                     acc_dbg, stream);
+                     acc_dbg, nullptr, 0, stream);
 }
 
 extern "C" int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
                              const uint8_t* refine, const float* scales, int64_t N, int64_t group,
-                             float* y, void* stream) {
+                             float* y, void* ws, size_t ws_bytes, void* stream) {
   if (!x) return nest::fail(NEST_EINVAL, "verify_gemm_x: null pointer");
   return verify_impl("verify_gemm_x", Act{nullptr, nullptr, x}, M, K, base, refine, scales, N, group,
-                     y, nullptr, stream);
+                     y, nullptr, ws, ws_bytes, stream);
 }
 
 extern "C" int verify_accept(const int8_t* qa, const float* sa, int64_t B, int64_t k, int64_t K,
                              const uint8_t* base, const uint8_t* refine, const float* scales,
                              int64_t V, int64_t group, const int32_t* draft, int32_t* target,
-                             int32_t* n_emitted, int32_t* emitted, float* y, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             int32_t* n_emitted, int32_t* emitted, float* y, int32_t* len,
+                             int32_t* next, void* ws, size_t ws_bytes, void* stream) {
   return accept_impl("verify_accept", Act{qa, sa, nullptr}, B, k, K, base, refine, scales, V, group,
-                     draft, target, n_emitted, emitted, y, ws, ws_bytes, stream);
+                     draft, target, n_emitted, emitted, y, len, next, ws, ws_bytes, stream);
 }
 
 extern "C" int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K, const uint8_t* base,
                                const uint8_t* refine, const float* scales, int64_t V, int64_t group,
                                const int32_t* draft, int32_t* target, int32_t* n_emitted,
-                               int32_t* emitted, float* y, void* ws, size_t ws_bytes, void* stream) {
+                               int32_t* emitted, float* y, int32_t* len, int32_t* next, void* ws,
+                               size_t ws_bytes, void* stream) {
   if (!x) return nest::fail(NEST_EINVAL, "verify_accept_x: null pointer");
   return accept_impl("verify_accept_x", Act{nullptr, nullptr, x}, B, k, K, base, refine, scales, V,
-                     group, draft, target, n_emitted, emitted, y, ws, ws_bytes, stream);
+                     group, draft, target, n_emitted, emitted, y, len, next, ws, ws_bytes, stream);
 }

@@ -56,15 +56,6 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 // dynamic LDS size).
 int resident_blocks(const void* kernel, int threads, size_t dyn_lds);
 
-// A device word for counting a kernel's finished blocks on `stream`: zero
-// before each launch (the last block resets it); null if it cannot be
-// allocated.
-unsigned* stream_counter(hipStream_t stream);
-
-// At least `bytes` of device scratch owned by the library for calls on
-// `stream` (256-byte aligned); null if it cannot be allocated.
-void* stream_scratch(hipStream_t stream, size_t bytes);
-
 // Batched verify (M > 16 rows): one launch for up to 144 rows.
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
                           const uint8_t* refine, const float* scales, int N, float* y,

@@ -208,12 +208,20 @@ struct AppendArgs {
   float *ks, *vs;
   float *shk, *shv;              // [Hkv][2][blk][d]
   const float *knew, *vnew;      // [Hkv][n][d]
-  int64_t cap, d, blk, pos, n;
+  int64_t cap, d, blk, pos, n;   // pos: the first position, or an offset added to *pos_dev
+  const int32_t* pos_dev;        // device word holding the rest of the position, or null
 };
 
 __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
   __shared__ float red[4];
+  // the first position: host value, plus the device word when given; an
+  // append that would not fit in the cache writes nothing
+  if (a.pos_dev) {
+    a.pos += *a.pos_dev;
+    if (a.pos < 0 || a.pos + a.n > a.cap) return;
+  }
   const int64_t b = a.pos / a.blk + blockIdx.x, h = blockIdx.y;
+  if (b > (a.pos + a.n - 1) / a.blk) return;  // a block the append does not touch
   const bool is_v = (blockIdx.z & 1) == 1;
   const int part = static_cast<int>(blockIdx.z >> 1);
   const int64_t t0 = b * a.blk, nb = a.cap / a.blk;
@@ -435,12 +443,14 @@ extern "C" int kv_nest_shadow_fill(const nest_kv* kv, const float* k, const floa
 }
 
 extern "C" int kv_nest_append(const nest_kv* kv, float* shadow_k, float* shadow_v, const float* k_new,
-                              const float* v_new, int64_t pos, int64_t n, void* stream) {
+                              const float* v_new, const int32_t* pos_dev, int64_t pos, int64_t n,
+                              void* stream) {
   const char* what = "kv_nest_append";
   int rc = check_kv(what, kv);
   if (rc) return rc;
   if (!shadow_k || !shadow_v || !k_new || !v_new) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
-  if (pos < 0 || n < 1 || n > kv->block || pos + n > kv->capacity)
+  if (n < 1 || n > kv->block || (!pos_dev && (pos < 0 || pos + n > kv->capacity)) ||
+      (pos_dev && (pos < -kv->capacity || pos > kv->capacity)))
     return nest::fail(NEST_EINVAL, "%s: need pos >= 0, 1 <= n <= block, pos + n <= capacity (pos=%lld n=%lld)",
                       what, (long long)pos, (long long)n);
   AppendArgs a{};
@@ -448,8 +458,10 @@ extern "C" int kv_nest_append(const nest_kv* kv, float* shadow_k, float* shadow_
   a.vb = const_cast<uint8_t*>(kv->v_base); a.vr = const_cast<uint8_t*>(kv->v_refine);
   a.ks = const_cast<float*>(kv->k_scale); a.vs = const_cast<float*>(kv->v_scale);
   a.shk = shadow_k; a.shv = shadow_v; a.knew = k_new; a.vnew = v_new;
-  a.cap = kv->capacity; a.d = kv->head_dim; a.blk = kv->block; a.pos = pos; a.n = n;
-  const int64_t touched = (pos + n - 1) / kv->block - pos / kv->block + 1;
+  a.cap = kv->capacity; a.d = kv->head_dim; a.blk = kv->block; a.pos = pos; a.n = n; a.pos_dev = pos_dev;
+  // n <= block tokens touch at most two blocks; with the position on the
+  // device both are launched and the kernel skips one the append misses
+  const int64_t touched = pos_dev ? 2 : (pos + n - 1) / kv->block - pos / kv->block + 1;
   kv_append_kernel<<<dim3(static_cast<unsigned>(touched), static_cast<unsigned>(kv->n_kv_heads),
                           2 * kAppendSplit),
                      256, 0, nest::as_stream(stream)>>>(a);

@@ -6,8 +6,14 @@ nested linears (draft_gemv_x over the base planes, verify_gemm_x over both),
 kv_nest_append / kv_nest_attend on one nested KV cache per layer (base view
 for the draft, full view for the target), and draft_gemv_x / verify_accept_x
 with the fused argmax on the nested LM head. This module only sequences the
-calls and keeps positions (the round of "How Speculative Decoding Speeds Up
-Inference", Table 1).
+calls (the round of "How Speculative Decoding Speeds Up Inference", Table 1).
+
+Round state lives on the device: the committed cache length (one int32,
+advanced by verify_accept by the tokens it emits) and each round's token
+buffer, whose slot 0 verify_accept fills with the next round's input. Every
+position and context length is that device length plus a host offset, so
+rounds can be issued back to back without the host reading anything
+(run_rounds); generate() reads each round's count only to know when to stop.
 
 A target pass over the k+1 positions of a round attends either
   exact    position by position (append one token, attend with its query),
@@ -16,8 +22,8 @@ A target pass over the k+1 positions of a round attends either
            and logits of target-only decoding ("The same output as the
            large model alone"), or
   batched  with one append of all k+1 tokens and one attention of all k+1
-           queries (what the benchmark's round does), where the open block
-           is quantized with the later positions of the pass included.
+           queries, where the open block is quantized with the later
+           positions of the pass included.
 """
 from __future__ import annotations
 
@@ -43,6 +49,7 @@ class Decoder:
             self.layers.append({"norm_attn": t(lw["norm_attn"]), "norm_mlp": t(lw["norm_mlp"]),
                                 **{n: ns.nest_pack_tiled(t(lw[n])) for n in ("qkv", "o", "gate_up", "down")}})
         self.no_draft = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        self.length = torch.zeros(1, dtype=torch.int32, device=self.dev)  # committed cache length
         self.reset()
 
     def reset(self):
@@ -55,67 +62,107 @@ class Decoder:
             sh = ns.kv_shadow(kv)
             ns.kv_nest_shadow_fill(kv, z, z, 0, sh)
             self.kv.append((kv, sh))
+        self.length.zero_()
 
     def _linear(self, x, W, draft):
         return ns.draft_gemv_x(x, W) if draft else ns.verify_gemm_x(x, W)
 
-    def forward(self, tokens: torch.Tensor, pos0: int, draft: bool, exact: bool = True) -> torch.Tensor:
+    def forward(self, tokens: torch.Tensor, off: int, draft: bool, exact: bool = True) -> torch.Tensor:
         """Hidden states after the final norm for int32 tokens [M] at
-        positions pos0.., with their K/V appended to every layer's cache."""
+        positions length + off.. (length on the device), with their K/V
+        appended to every layer's cache."""
         c = self.cfg
         M = tokens.numel()
         Hq, Hkv, d, eps = c["q_heads"], c["kv_heads"], c["head_dim"], c["eps"]
         view = 0 if draft else 1
+        L = self.length
         x = ns.embed(self.embed, tokens)
         h = torch.empty_like(x)
         dn = None
         for lw, (kv, sh) in zip(self.layers, self.kv):
             ns.add_rmsnorm(x, dn, lw["norm_attn"], eps, out=h)
             qkv = self._linear(h, lw["qkv"], draft)
-            q, k, v = ns.rope_split(qkv, pos0, Hq, Hkv, d, c["theta"], token_major=exact)
+            q, k, v = ns.rope_split(qkv, off, Hq, Hkv, d, c["theta"], token_major=exact, pos_dev=L)
             if exact:
                 att = torch.empty((M, Hq, d), dtype=torch.float32, device=self.dev)
                 for i in range(M):
-                    ns.kv_nest_append(kv, sh, k[i].unsqueeze(1), v[i].unsqueeze(1), pos0 + i)
-                    ns.kv_nest_attend(q[i:i + 1], kv, pos0 + i + 1, view, out=att[i:i + 1])
+                    ns.kv_nest_append(kv, sh, k[i].unsqueeze(1), v[i].unsqueeze(1), off + i, pos_dev=L)
+                    ns.kv_nest_attend(q[i:i + 1], kv, off + i + 1, view, out=att[i:i + 1], ctx_dev=L)
             else:
-                ns.kv_nest_append(kv, sh, k, v, pos0)
-                att = ns.kv_nest_attend(q, kv, pos0 + M, view)
+                ns.kv_nest_append(kv, sh, k, v, off, pos_dev=L)
+                att = ns.kv_nest_attend(q, kv, off + M, view, ctx_dev=L)
             o = self._linear(att.view(M, Hq * d), lw["o"], draft)
             ns.add_rmsnorm(x, o, lw["norm_mlp"], eps, out=h)
             dn = self._linear(ns.swiglu(self._linear(h, lw["gate_up"], draft)), lw["down"], draft)
         ns.add_rmsnorm(x, dn, self.norm_final, eps, out=h)
         return h
 
-    def prefill(self, prompt) -> tuple:
+    def prefill(self, prompt) -> torch.Tensor:
         """Target passes over prompt[:-1], 16 positions at a time with
-        position-by-position attention; returns the round input (the last
-        prompt token on the device, its position)."""
+        position-by-position attention; leaves the committed length at
+        len(prompt) - 1 and returns the last prompt token on the device."""
+        self.reset()
         p = torch.from_numpy(np.ascontiguousarray(prompt, np.int32)).to(self.dev)
         n = p.numel() - 1
         for s in range(0, n, 16):
             self.forward(p[s:min(n, s + 16)], s, draft=False, exact=True)
-        return p[n:n + 1].clone(), n
+        self.length.fill_(n)
+        return p[n:n + 1]
+
+    def _buffers(self, rounds: int, k: int, want_y: bool):
+        V = self.head.rows
+        E = torch.empty
+        return {"toks": E((rounds + 1, k + 1), dtype=torch.int32, device=self.dev),
+                "target": E((rounds, k + 1), dtype=torch.int32, device=self.dev),
+                "n_emitted": E((rounds, 1), dtype=torch.int32, device=self.dev),
+                "emitted": E((rounds, k + 1), dtype=torch.int32, device=self.dev),
+                "y": E((rounds, k + 1, V), dtype=torch.float32, device=self.dev) if want_y else None}
+
+    def _round(self, r: int, k: int, exact: bool, b: dict):
+        """Issue round r: k draft steps and one target pass. Slot 0 of
+        b["toks"][r] holds the round's input; verify_accept advances the
+        committed length and writes the next round's input."""
+        toks = b["toks"][r]
+        for j in range(k):
+            h = self.forward(toks[j:j + 1], j, draft=True, exact=True)
+            ns.draft_gemv_x(h, self.head, want_y=False, argmax=True, argmax_out=toks[j + 1:j + 2])
+        h = self.forward(toks, 0, draft=False, exact=exact)
+        out = {"target": b["target"][r], "n_emitted": b["n_emitted"][r], "emitted": b["emitted"][r]}
+        if b["y"] is not None:
+            out["y"] = b["y"][r]
+        ns.verify_accept_x(h, 1, k, self.head, toks[1:] if k else self.no_draft, out=out,
+                           length=self.length, next_token=b["toks"][r + 1][0:1])
+
+    def run_rounds(self, prompt, rounds: int, k: int, exact: bool = True, want_y: bool = True):
+        """A fixed number of rounds issued back to back with no host read
+        between them (positions, lengths and inputs advance on the device).
+        Returns (tokens, per round (emitted count, logits of the emitted
+        positions [n][V] or None)) after one synchronisation at the end."""
+        b = self._buffers(rounds, k, want_y)
+        b["toks"][0, 0:1].copy_(self.prefill(prompt))
+        for r in range(rounds):
+            self._round(r, k, exact, b)
+        n = b["n_emitted"][:, 0].cpu().numpy()
+        em = b["emitted"].cpu().numpy()
+        toks, per = [], []
+        for r in range(rounds):
+            toks += em[r, :n[r]].tolist()
+            per.append((int(n[r]), b["y"][r, :n[r]] if want_y else None))
+        return toks, per
 
     def generate(self, prompt, n_new: int, k: int, exact: bool = True):
         """Greedy decoding of n_new tokens after the prompt: one target pass
         per token when k = 0, else rounds of k draft steps and one target
-        pass. Returns (tokens, rounds): rounds lists (emitted count, target
-        logits of the emitted positions [n][V] on the device)."""
-        self.reset()
-        t, pos = self.prefill(prompt)
-        out, rounds = [], []
+        pass; each round's emitted count is read back to know when to stop.
+        Returns (tokens, rounds): rounds lists (emitted count, target logits
+        of the emitted positions [n][V] on the device)."""
+        b = self._buffers(n_new, k, True)
+        b["toks"][0, 0:1].copy_(self.prefill(prompt))
+        out, rounds, r = [], [], 0
         while len(out) < n_new:
-            toks = torch.empty(k + 1, dtype=torch.int32, device=self.dev)
-            toks[0:1] = t
-            for j in range(k):
-                h = self.forward(toks[j:j + 1], pos + j, draft=True, exact=True)
-                ns.draft_gemv_x(h, self.head, want_y=False, argmax=True, argmax_out=toks[j + 1:j + 2])
-            h = self.forward(toks, pos, draft=False, exact=exact)
-            res = ns.verify_accept_x(h, 1, k, self.head, toks[1:] if k else self.no_draft, want_y=True)
-            n = int(res["n_emitted"][0].item())
-            out += res["emitted"][0, :n].tolist()
-            rounds.append((n, res["y"][:n]))
-            pos += n
-            t = res["emitted"][0, n - 1:n].clone()
+            self._round(r, k, exact, b)
+            n = int(b["n_emitted"][r, 0].item())
+            out += b["emitted"][r, :n].tolist()
+            rounds.append((n, b["y"][r, :n]))
+            r += 1
         return out[:n_new], rounds

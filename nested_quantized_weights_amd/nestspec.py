@@ -56,15 +56,16 @@ _SIGS = {
     "draft_gemv_workspace_size": (_sz, [_i64, _i64]),
     "verify_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p]),
     "verify_accept": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
-                                     _p, _p, _p, _sz, _p]),
+                                     _p, _p, _p, _p, _p, _sz, _p]),
     "verify_accept_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nest_tile": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "nest_tile_plane_bytes": (_sz, [_i64, _i64]),
     "nest_tile_scale_count": (_sz, [_i64, _i64, _i64]),
     "draft_gemv_x": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _p, _sz, _p]),
-    "verify_gemm_x": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p]),
+    "verify_gemm_x": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _sz, _p]),
     "verify_accept_x": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
-                                       _p, _p, _p, _sz, _p]),
+                                       _p, _p, _p, _p, _p, _sz, _p]),
+    "nest_gemv_x_workspace_size": (_sz, [_i64, _i64, _i64]),
     "kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
     "nest_expected_tokens": (_d, [_d, _i64]),
     "nest_token_time": (_d, [_d, _i64, _d, _d]),
@@ -72,10 +73,10 @@ _SIGS = {
     "nest_alpha_init": (None, [ctypes.POINTER(_Alpha), _d, _d, _d]),
     "nest_alpha_update": (None, [ctypes.POINTER(_Alpha), _i64, _i64]),
     "nest_alpha_value": (_d, [ctypes.POINTER(_Alpha)]),
-    "kv_nest_append": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _p, _p, _i64, _i64, _p]),
+    "kv_nest_append": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _p, _p, _p, _i64, _i64, _p]),
     "kv_nest_shadow_floats": (_sz, [_i64, _i64, _i64]),
     "kv_nest_shadow_fill": (ctypes.c_int, [ctypes.POINTER(_KV), _p, _p, _i64, _i64, _p, _p, _p]),
-    "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _i64, ctypes.c_int, _p,
+    "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _i64, ctypes.c_int, _p,
                                       _p, _sz, _p]),
     "kv_nest_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "nest_sample": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_float, _p, _p, _p, _sz, _p]),
@@ -85,9 +86,10 @@ _SIGS = {
     "verify_sample_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nest_embed": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _p]),
     "nest_add_rmsnorm": (ctypes.c_int, [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p]),
-    "nest_rope_split": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _p, _p,
-                                       _p, _p]),
+    "nest_rope_split": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                       _p, _p, _p, _p]),
     "nest_swiglu": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
+    "nest_read_stream": (ctypes.c_int, [_p, _sz, _p, _p]),
 }
 
 SYMBOLS = tuple(_SIGS)
@@ -136,8 +138,9 @@ def _dev(t: torch.Tensor, dtype, what: str, name: str) -> torch.Tensor:
     return t
 
 
-# Workspaces for the argmax / accept entry points, cached per (device,
-# stream, kind): calls on one stream run in order, so they can share one.
+# Workspaces, cached per (device, stream, kind): calls on one stream run
+# in order, so they can share one. They start all zero, as the GEMV
+# workspaces must (each call leaves its block counter at zero again).
 _ws_cache: dict = {}
 
 
@@ -146,9 +149,14 @@ def workspace(nbytes: int, device: torch.device, key: str) -> torch.Tensor:
     k = (device.index, s, key)
     t = _ws_cache.get(k)
     if t is None or t.numel() < nbytes:
-        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[k] = t
     return t
+
+
+def gemv_x_workspace(M: int, K: int, N: int, device: torch.device) -> torch.Tensor:
+    """The zeroed workspace of the fp32-activation GEMV calls."""
+    return workspace(lib().nest_gemv_x_workspace_size(M, K, N), device, "gemv")
 
 
 def nest_pack(w: torch.Tensor, group: int = 128, out=None):
@@ -248,7 +256,7 @@ def draft_gemv(qa, sa, W, group: int = 128, y=None, want_y: bool = True, argmax:
     if argmax:
         am = argmax_out if argmax_out is not None else torch.empty(M, dtype=torch.int32, device=dev)
         if ws is None:
-            ws = workspace(lib().draft_gemv_workspace_size(M, N), dev, "argmax")
+            ws = workspace(lib().draft_gemv_workspace_size(M, N), dev, "gemv")
         wsp, wsn = _ptr(ws), ws.numel()
     acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
     _check(lib().draft_gemv(_ptr(qa), _ptr(sa), M, K, _ptr(W.base), _ptr(W.scales), N, group, _ptr(y),
@@ -289,10 +297,12 @@ def _accept_out(B, k, V, dev, want_y):
 
 
 def verify_accept(qa, sa, B: int, k: int, W, draft, group: int = 128, want_y: bool = False, out=None,
-                  ws=None):
+                  ws=None, length=None, next_token=None):
     """Verify pass through the nested LM head W (Tiled) plus the greedy
     accept step. Returns a dict of device tensors: target [B][k+1],
-    n_emitted [B], emitted [B][k+1] (and y when want_y)."""
+    n_emitted [B], emitted [B][k+1] (and y when want_y). length (int32 [B],
+    device) is advanced by n_emitted when given; next_token (int32 [B])
+    receives the last emitted token."""
     what = "verify_accept"
     _dev(qa, torch.int8, what, "qa")
     _dev(sa, torch.float32, what, "sa")
@@ -304,11 +314,11 @@ def verify_accept(qa, sa, B: int, k: int, W, draft, group: int = 128, want_y: bo
     if out is None:
         out = _accept_out(B, k, V, dev, want_y)
     if ws is None:
-        ws = workspace(lib().verify_accept_workspace_size(B, k, V), dev, "argmax")
+        ws = workspace(lib().verify_accept_workspace_size(B, k, V), dev, "gemv")
     _check(lib().verify_accept(_ptr(qa), _ptr(sa), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales),
                                V, group, _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
-                               _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(ws), ws.numel(),
-                               _stream(dev)), what)
+                               _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(length), _ptr(next_token),
+                               _ptr(ws), ws.numel(), _stream(dev)), what)
     return out
 
 
@@ -324,21 +334,21 @@ def draft_gemv_x(x, W, group: int = 128, y=None, want_y: bool = True, argmax: bo
     dev = x.device
     if y is None and (want_y or not argmax):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    am, wsp, wsn = None, None, 0
+    am = None
     if argmax:
         am = argmax_out if argmax_out is not None else torch.empty(M, dtype=torch.int32, device=dev)
-        if ws is None:
-            ws = workspace(lib().draft_gemv_workspace_size(M, N), dev, "argmax")
-        wsp, wsn = _ptr(ws), ws.numel()
+    if ws is None:
+        ws = gemv_x_workspace(M, K, N, dev)
     _check(lib().draft_gemv_x(_ptr(x), M, K, _ptr(W.base), _ptr(W.scales), N, group, _ptr(y), _ptr(am),
-                              wsp, wsn, _stream(dev)), what)
+                              _ptr(ws), ws.numel(), _stream(dev)), what)
     if argmax:
         return (y, am) if y is not None else am
     return y
 
 
-def verify_gemm_x(x, W, group: int = 128, y=None):
-    """verify_gemm on fp32 activations x [M][K] (M <= 16), quantized inside the kernel."""
+def verify_gemm_x(x, W, group: int = 128, y=None, ws=None):
+    """verify_gemm on fp32 activations x [M][K], quantized inside the kernel
+    (or first into the workspace)."""
     what = "verify_gemm_x"
     _dev(x, torch.float32, what, "x")
     W = _tiled(W, what, 2)
@@ -346,13 +356,15 @@ def verify_gemm_x(x, W, group: int = 128, y=None):
     N = W.rows
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = gemv_x_workspace(M, K, N, x.device)
     _check(lib().verify_gemm_x(_ptr(x), M, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), N, group,
-                               _ptr(y), _stream(x.device)), what)
+                               _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)), what)
     return y
 
 
 def verify_accept_x(x, B: int, k: int, W, draft, group: int = 128, want_y: bool = False, out=None,
-                    ws=None):
+                    ws=None, length=None, next_token=None):
     """verify_accept on fp32 activations x [B*(k+1)][K], quantized inside the kernel."""
     what = "verify_accept_x"
     _dev(x, torch.float32, what, "x")
@@ -364,11 +376,11 @@ def verify_accept_x(x, B: int, k: int, W, draft, group: int = 128, want_y: bool 
     if out is None:
         out = _accept_out(B, k, V, dev, want_y)
     if ws is None:
-        ws = workspace(lib().verify_accept_workspace_size(B, k, V), dev, "argmax")
+        ws = gemv_x_workspace(B * (k + 1), K, V, dev)
     _check(lib().verify_accept_x(_ptr(x), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), V, group,
                                  _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
-                                 _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(ws), ws.numel(),
-                                 _stream(dev)), what)
+                                 _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(length), _ptr(next_token),
+                                 _ptr(ws), ws.numel(), _stream(dev)), what)
     return out
 
 
@@ -423,33 +435,40 @@ def kv_nest_shadow_fill(kv: NestKV, k: torch.Tensor, v: torch.Tensor, ctx_len: i
                                      _ptr(shadow[0]), _ptr(shadow[1]), _stream(k.device)), what)
 
 
-def kv_nest_append(kv: NestKV, shadow, k_new: torch.Tensor, v_new: torch.Tensor, pos: int):
-    """Write fp32 k_new, v_new [Hkv][n][d] at positions pos.. and quantize the touched blocks again."""
+def kv_nest_append(kv: NestKV, shadow, k_new: torch.Tensor, v_new: torch.Tensor, pos: int, pos_dev=None):
+    """Write fp32 k_new, v_new [Hkv][n][d] at positions pos.. (pos plus the
+    device int32 pos_dev when given) and quantize the touched blocks again."""
     what = "kv_nest_append"
     _dev(k_new, torch.float32, what, "k_new")
     _dev(v_new, torch.float32, what, "v_new")
+    if pos_dev is not None:
+        _dev(pos_dev, torch.int32, what, "pos_dev")
     s = kv.struct()
     _check(lib().kv_nest_append(ctypes.byref(s), _ptr(shadow[0]), _ptr(shadow[1]), _ptr(k_new), _ptr(v_new),
-                                int(pos), k_new.shape[1], _stream(k_new.device)), what)
+                                _ptr(pos_dev), int(pos), k_new.shape[1], _stream(k_new.device)), what)
 
 
-def kv_nest_attend(q: torch.Tensor, kv: NestKV, ctx_len: int, view: int, out=None, ws=None):
+def kv_nest_attend(q: torch.Tensor, kv: NestKV, ctx_len: int, view: int, out=None, ws=None, ctx_dev=None):
     """q: bf16 [nq][Hq][d] (torch.bfloat16, or its bit patterns as int16/uint16).
+    The visible length is ctx_len, plus the device int32 ctx_dev when given.
     Returns fp32 [nq][Hq][d]."""
     what = "kv_nest_attend"
     if not isinstance(q, torch.Tensor) or not q.is_cuda or not q.is_contiguous():
         raise NestError(f"{what}: q must be a contiguous CUDA tensor")
     if q.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise NestError(f"{what}: q must hold bf16 bit patterns")
+    if ctx_dev is not None:
+        _dev(ctx_dev, torch.int32, what, "ctx_dev")
     nq, Hq, d = q.shape
     dev = q.device
     if out is None:
         out = torch.empty((nq, Hq, d), dtype=torch.float32, device=dev)
-    wsn = lib().kv_nest_attend_workspace_size(nq, Hq, kv.n_kv_heads, d, int(ctx_len))
+    plan_len = kv.capacity if ctx_dev is not None else int(ctx_len)
+    wsn = lib().kv_nest_attend_workspace_size(nq, Hq, kv.n_kv_heads, d, plan_len)
     if ws is None or ws.numel() < wsn:
-        ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=dev)
+        ws = workspace(max(wsn, 256), dev, "attend")
     s = kv.struct()
-    _check(lib().kv_nest_attend(_ptr(q), nq, Hq, ctypes.byref(s), int(ctx_len), int(view),
+    _check(lib().kv_nest_attend(_ptr(q), nq, Hq, ctypes.byref(s), _ptr(ctx_dev), int(ctx_len), int(view),
                                 _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), what)
     return out
 
@@ -547,8 +566,9 @@ def add_rmsnorm(x, y, gamma, eps: float, out=None):
 
 
 def rope_split(qkv, pos0: int, n_q_heads: int, n_kv_heads: int, head_dim: int, theta: float,
-               token_major: bool = False, out=None):
-    """Rotary embedding + q/k/v split of qkv [M][(Hq+2Hkv)d]: (q bf16 bits
+               token_major: bool = False, out=None, pos_dev=None):
+    """Rotary embedding + q/k/v split of qkv [M][(Hq+2Hkv)d] at positions
+    pos0 + m (plus the device int32 pos_dev when given): (q bf16 bits
     [M][Hq][d] as int16, k, v fp32 [Hkv][M][d] or [M][Hkv][d])."""
     what = "nest_rope_split"
     _dev(qkv, torch.float32, what, "qkv")
@@ -560,8 +580,9 @@ def rope_split(qkv, pos0: int, n_q_heads: int, n_kv_heads: int, head_dim: int, t
                torch.empty(kv_shape, dtype=torch.float32, device=dev),
                torch.empty(kv_shape, dtype=torch.float32, device=dev))
     q, k, v = out
-    _check(lib().nest_rope_split(_ptr(qkv), M, int(pos0), n_q_heads, n_kv_heads, head_dim, float(theta),
-                                 1 if token_major else 0, _ptr(q), _ptr(k), _ptr(v), _stream(dev)), what)
+    _check(lib().nest_rope_split(_ptr(qkv), M, _ptr(pos_dev), int(pos0), n_q_heads, n_kv_heads, head_dim,
+                                 float(theta), 1 if token_major else 0, _ptr(q), _ptr(k), _ptr(v),
+                                 _stream(dev)), what)
     return q, k, v
 
 

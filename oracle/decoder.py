@@ -78,8 +78,14 @@ def bf16_bits(x):
 class Decoder:
     """The decoder with nested weights and one nested KV cache per layer."""
 
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, att_noise=0.0, noise_seed=0):
+        """att_noise > 0 adds to every attention output vector (per position
+        and head) a random vector of att_noise times its norm: a test of how
+        far the logits move when attention is off by a given normwise
+        tolerance. 0 (the default) leaves the computation untouched."""
         self.cfg = cfg
+        self.att_noise = float(att_noise)
+        self.noise_rng = np.random.default_rng(noise_seed)
         self.embed = np.asarray(weights["embed"], np.float32)
         self.norm_final = weights["norm_final"]
         self.head = O.nest_pack(weights["lm_head"])
@@ -131,6 +137,11 @@ class Decoder:
             else:
                 O.kv_append(kv, kf, vf, k_new, v_new, pos0)
                 att = O.kv_attend(q, kv, pos0 + M, view).astype(np.float32)
+            if self.att_noise > 0.0:
+                u = self.noise_rng.standard_normal(att.shape)
+                u *= (self.att_noise * np.linalg.norm(att, axis=-1, keepdims=True)
+                      / np.linalg.norm(u, axis=-1, keepdims=True))
+                att = (att + u).astype(np.float32)
             x = (x + self.linear(att.reshape(M, Hq * d), lw["o"], draft)).astype(np.float32)
             h = rmsnorm(x, lw["norm_mlp"], c["eps"])
             x = (x + self.linear(swiglu(self.linear(h, lw["gate_up"], draft)), lw["down"], draft)).astype(np.float32)
@@ -146,6 +157,21 @@ class Decoder:
         for s in range(0, n, 16):
             self.forward(prompt[s:min(n, s + 16)], s, draft=False, exact=True)
         return int(prompt[-1]), n
+
+    def teacher_forced_logits(self, tokens, start):
+        """Target logits of every position from start on, each computed from
+        the sequence's own prefix: one exact target pass over tokens[:-1],
+        16 positions at a time, so row j holds what target-only decoding
+        would score after tokens[start + j]. [len(tokens) - 1 - start][V]."""
+        self.reset()
+        n = len(tokens) - 1
+        rows = []
+        for s in range(0, n, 16):
+            h = self.forward(list(tokens[s:min(n, s + 16)]), s, draft=False, exact=True)
+            if s + h.shape[0] > start:
+                y = self.logits(h, draft=False)
+                rows.append(y[max(0, start - s):])
+        return np.concatenate(rows)
 
     def generate(self, prompt, n_new, k, exact=True):
         """Greedy decoding of n_new tokens after the prompt. k = 0: one target

@@ -87,15 +87,50 @@ def test_attend_host_validation_without_a_gpu(lib):
     lib.nest_last_error.restype = ctypes.c_char_p
     f = lib.kv_nest_attend
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_KV), ctypes.c_int64,
-                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_KV), ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     p = ctypes.c_void_p(256)
     kv = _KV(256, 256, 256, 256, 256, 256, 8, 128, 32768, 128)
     ws = 1 << 24
-    assert f(ctypes.c_void_p(258), 1, 32, ctypes.byref(kv), 4096, 0, p, p, ws, None) == 2  # NEST_EALIGN
+    assert f(ctypes.c_void_p(258), 1, 32, ctypes.byref(kv), None, 4096, 0, p, p, ws, None) == 2  # NEST_EALIGN
     assert b"q must be 16-byte aligned" in lib.nest_last_error()
-    assert f(p, 1, 30, ctypes.byref(kv), 4096, 0, p, p, ws, None) == 3  # NEST_ESHAPE: 8 does not divide 30
-    assert f(p, 1, 32, ctypes.byref(kv), 4096, 2, p, p, ws, None) == 1  # NEST_EINVAL: view
-    assert f(p, 1, 32, ctypes.byref(kv), 40000, 0, p, p, ws, None) == 1  # ctx_len > capacity
-    assert f(p, 17, 32, ctypes.byref(kv), 4096, 1, p, p, ws, None) == 5  # NEST_EUNSUPPORTED: 68 rows
-    assert f(p, 1, 32, ctypes.byref(kv), 4096, 0, p, p, 16, None) == 4  # NEST_EWORKSPACE
+    assert f(p, 1, 30, ctypes.byref(kv), None, 4096, 0, p, p, ws, None) == 3  # NEST_ESHAPE: 8 does not divide 30
+    assert f(p, 1, 32, ctypes.byref(kv), None, 4096, 2, p, p, ws, None) == 1  # NEST_EINVAL: view
+    assert f(p, 1, 32, ctypes.byref(kv), None, 40000, 0, p, p, ws, None) == 1  # ctx_len > capacity
+    assert f(p, 17, 32, ctypes.byref(kv), None, 4096, 1, p, p, ws, None) == 5  # NEST_EUNSUPPORTED: 68 rows
+    assert f(p, 1, 32, ctypes.byref(kv), None, 4096, 0, p, p, 16, None) == 4  # NEST_EWORKSPACE
+    # with the length on the device the host value is an offset, and the
+    # workspace must cover the whole capacity
+    sz = lib.kv_nest_attend_workspace_size
+    sz.restype = ctypes.c_size_t
+    sz.argtypes = [ctypes.c_int64] * 5
+    small, full = sz(1, 32, 8, 128, 4096), sz(1, 32, 8, 128, 32768)
+    assert 0 < small < full
+    assert f(p, 1, 32, ctypes.byref(kv), p, 0, 0, p, p, small, None) == 4
+    assert f(p, 1, 32, ctypes.byref(kv), p, -1, 0, p, p, full, None) == 1  # negative offset
+
+
+def test_workspaces_are_checked_without_a_gpu(lib):
+    # the fp32-activation GEMVs need the caller's workspace (block counter,
+    # argmax keys, quantize-first codes), 256-byte aligned; nothing runs
+    # before these checks
+    lib.nest_last_error.restype = ctypes.c_char_p
+    sz = lib.nest_gemv_x_workspace_size
+    sz.restype = ctypes.c_size_t
+    sz.argtypes = [ctypes.c_int64] * 3
+    need = sz(5, 3584, 37888)
+    assert need >= 256 + 5 * 3584 and sz(0, 1, 1) == 0
+    g = lib.verify_gemm_x
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 3 + \
+        [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 2 + [ctypes.c_size_t, ctypes.c_void_p]
+    p = ctypes.c_void_p(256)
+    assert g(p, 5, 3584, p, p, p, 37888, 128, p, None, 0, None) == 4  # NEST_EWORKSPACE
+    assert b"workspace needs" in lib.nest_last_error()
+    assert g(p, 5, 3584, p, p, p, 37888, 128, p, ctypes.c_void_p(272), need, None) == 2  # not 256-aligned
+    a = lib.kv_nest_append
+    a.restype = ctypes.c_int
+    a.argtypes = [ctypes.POINTER(_KV)] + [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]
+    kv = _KV(256, 256, 256, 256, 256, 256, 8, 128, 32768, 128)
+    assert a(ctypes.byref(kv), p, p, p, p, None, 32700, 129, None) == 1  # n > block
+    assert a(ctypes.byref(kv), p, p, p, p, None, 32700, 100, None) == 1  # past capacity

@@ -12,19 +12,26 @@ the large model alone").
   * The claim: speculative rounds with position-by-position attention in the
     target pass emit exactly the tokens of target-only decoding, and the
     target logits of every emitted position are bit-identical.
-  * Against the oracle's own decode: the token sequences agree; a
-    divergence is allowed only where the oracle's top two logits are within
-    the envelope of the GPU-oracle logit differences seen up to that point.
-    Stage by stage the two decoders agree closely (linears bit-identical,
-    attention within the KV tolerance, glue within fp32 rounding), but the
-    per-token int8 activations are a step function: a 1e-4 difference in a
-    layer's input moves about 2 % of its codes by one step (1/127 of the
-    row's max), and the layers after it carry that, so the logits differ by
-    about 2 % of their largest value. The envelope is checked against 5 %.
-  * The batched target pass (one append + one k+1-query attention) is run
-    and its first divergence from target-only decoding reported: there the
-    open block is quantized with later positions, so agreement is measured,
-    not guaranteed.
+  * Rounds chained on the device (committed length and next input kept by
+    verify_accept, no host read between rounds) emit the same tokens and
+    bit-identical logits as the host-driven loop, and as target-only
+    decoding.
+  * Against the oracle, position by position: the oracle scores every
+    generated position from the GPU's own prefix (teacher forcing, which is
+    what target-only decoding computes there). The GPU's logits must lie
+    within eps of the oracle's, and its token must be the oracle's top
+    choice unless the oracle's top two are within 2 eps (a near-tie). eps
+    comes from the attention tolerance itself: twice the largest logit
+    change of the oracle when every attention output is moved by a random
+    2e-3 of its norm (two draws). Stage by stage the decoders agree closely
+    (linears bit-identical, attention well inside the tolerance, glue
+    within fp32 rounding), but the per-token int8 activations are a step
+    function that turns such differences into whole code steps.
+  * The batched target pass (one append + one k+1-query attention) is run;
+    its rounds obey the accept rule on their own logits, and its first
+    divergence from target-only decoding is reported (there the open block
+    is quantized with later positions, so agreement is measured, not
+    guaranteed).
 """
 import numpy as np
 import pytest
@@ -142,26 +149,46 @@ def test_speculative_rounds_emit_the_target_only_tokens(gpu_dec, k):
     assert tpr > 1.5
 
 
-def test_decode_matches_the_oracle(gpu_dec, weights, D):
+def test_chained_rounds_match_the_host_loop(gpu_dec):
     prompt = synth.tokens(40, CFG["vocab"], (801,))
-    ar, r_ar = gpu_dec.generate(prompt, 48, 0)
-    odec = D.Decoder(CFG, weights)
-    oar, r_oar = odec.generate(prompt, 48, 0)
-    envelope = 0.0
-    for j, (a, b) in enumerate(zip(ar, oar)):
-        yg = r_ar[j][1][0].cpu().numpy().astype(np.float64)
-        yo = r_oar[j][1][0].astype(np.float64)
-        if a != b:
-            # a divergence only where the oracle's choice and the GPU's are
-            # within the logit differences seen so far
-            assert yo[b] - yo[a] <= 4.0 * envelope, (j, yo[b] - yo[a], envelope)
-            assert j >= 8  # the first tokens must agree
-            print(f"diverged at token {j} (oracle gap {yo[b] - yo[a]:.3g}, envelope {envelope:.3g})")
-            return
-        envelope = max(envelope, float(np.abs(yg - yo).max()))
-    scale = max(float(np.abs(y[0].cpu().numpy()).max()) for _, y in r_ar)
-    print(f"all {len(ar)} tokens agree; max logit difference {envelope:.3g} (largest logit {scale:.3g})")
-    assert envelope < 0.05 * scale
+    for k in (0, 4):
+        toks, per = gpu_dec.run_rounds(prompt, 50, k, exact=True)
+        ref, per_ref = gpu_dec.generate(prompt, len(toks), k, exact=True)
+        assert toks == ref
+        assert [n for n, _ in per] == [n for n, _ in per_ref][:len(per)]
+        y = torch.cat([y for _, y in per]).cpu().numpy()
+        y_ref = torch.cat([y for _, y in per_ref]).cpu().numpy()[:len(y)]
+        assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+        assert len(toks) >= 50 and all(1 <= n <= k + 1 for n, _ in per)
+
+
+def test_chained_decode_matches_the_oracle(gpu_dec, weights, D):
+    prompt = synth.tokens(40, CFG["vocab"], (801,))
+    k = 4
+    toks, per = gpu_dec.run_rounds(prompt, 50, k, exact=True)
+    ar, per_ar = gpu_dec.run_rounds(prompt, len(toks), 0, exact=True)
+    assert toks == ar[:len(toks)]
+    y_g = torch.cat([y for _, y in per]).cpu().numpy().astype(np.float64)
+    seq = list(prompt) + toks
+    start = len(prompt) - 1
+    y_o = D.Decoder(CFG, weights).teacher_forced_logits(seq, start).astype(np.float64)
+    assert y_o.shape == y_g.shape
+    sens = 0.0
+    for seed in (1, 2):
+        y_n = D.Decoder(CFG, weights, att_noise=2e-3, noise_seed=seed).teacher_forced_logits(seq, start)
+        sens = max(sens, float(np.abs(y_n.astype(np.float64) - y_o).max()))
+    eps = 2.0 * sens
+    diff = np.abs(y_g - y_o).max(axis=1)
+    print(f"{len(toks)} tokens; GPU-oracle logit difference max {diff.max():.3g}, "
+          f"eps {eps:.3g} (largest logit {np.abs(y_o).max():.3g})")
+    assert float(diff.max()) <= eps
+    near = 0
+    for j, t in enumerate(toks):
+        top = int(np.argmax(y_o[j]))
+        gap = y_o[j][top] - y_o[j][t]
+        assert gap <= 2.0 * eps, (j, t, top, gap, eps)
+        near += int(t != top)
+    print(f"tokens that are not the oracle's top choice (near-ties): {near}")
 
 
 def test_batched_target_pass_is_measured(gpu_dec):
@@ -171,4 +198,11 @@ def test_batched_target_pass_is_measured(gpu_dec):
         sp, r = gpu_dec.generate(prompt, 48, k, exact=False)
         first = next((i for i, (a, b) in enumerate(zip(sp, ar)) if a != b), None)
         print(f"batched k={k}: {np.mean([n for n, _ in r]):.3f} tokens/round, first divergence {first}")
-        assert all(0 <= t < CFG["vocab"] for t in sp)
+        # each round emits its own target choices: the argmax of the pass's
+        # logits at every emitted position, 1..k+1 of them
+        pos = 0
+        for n, y in r:
+            assert 1 <= n <= k + 1
+            assert sp[pos:pos + n] == y.argmax(dim=1).tolist()[:len(sp[pos:pos + n])]
+            pos += n
+        assert sp[:first] == ar[:first] if first is not None else sp == ar

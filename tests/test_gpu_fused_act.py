@@ -202,32 +202,34 @@ def test_batched_verify_quantizes_near_ties(ns, oracle, M, K):
     assert np.array_equal(y.view(np.uint32), y8.view(np.uint32))
 
 
-def test_two_streams_keep_their_own_counters_and_scratch(ns, oracle):
-    # the argmax GEMV's block counter and the quantize-first scratch are per
-    # stream: calls interleaved on two streams must each match the oracle
-    N, K, M = 4096, 3584, 5
+def test_two_streams_use_their_own_workspaces(ns, oracle):
+    # The argmax GEMV's block counter and the quantize-first activation codes
+    # live in the caller's workspace; the binding keeps one per stream. Calls
+    # interleaved on two streams must each match the oracle. 37888 x 3584
+    # with 5 rows has N*M*K >= 1.2e8, so verify_gemm_x quantizes into the
+    # workspace first; every result is held to the exact int32 sums (R9).
+    N, K, M = 37888, 3584, 5
     w = synth.weights(N, K, (311,))
     base, refine, scales = oracle.nest_pack(w)
     W = tiled(ns, base, refine, scales)
-    xs = [synth.activations(M, K, (312, i)) for i in range(6)]
+    xs = [synth.activations(M, K, (312, i)) for i in range(4)]
     refs = []
     for x in xs:
         qa, sa = oracle.act_quant(x)
-        refs.append((oracle.verify_gemm(qa, sa, base, refine, scales),
-                     oracle.argmax(oracle.draft_gemv(qa[:1], sa[:1], base, scales)[0])))
+        _, acc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
+        refs.append((sa, acc, oracle.argmax(oracle.draft_gemv(qa[:1], sa[:1], base, scales)[0])))
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = []
-    for rep in range(3):
+    for rep in range(2):
         for i, x in enumerate(xs):
             s = streams[i % 2]
             with torch.cuda.stream(s):
                 xd = dev(x)
-                y = ns.verify_gemm_x(xd, W)  # N*M*K >= 1.2e8: quantized first into the stream's scratch
-                _, am = ns.draft_gemv_x(xd[:1].contiguous(), W, argmax=True)  # the stream's block counter
+                y = ns.verify_gemm_x(xd, W)  # quantized first into this stream's workspace
+                _, am = ns.draft_gemv_x(xd[:1].contiguous(), W, argmax=True)  # this stream's counter
                 outs.append((i, y, am))
     torch.cuda.synchronize()
     for i, y, am in outs:
-        ref_y, ref_am = refs[i]
+        sa, acc, ref_am = refs[i]
         assert int(am.item()) == ref_am
-        err = np.abs(host(y).astype(np.float64) - ref_y.astype(np.float64)).max()
-        assert err <= 1e-3 * np.abs(ref_y).max()
+        assert bound_ok(host(y), sa, scales, acc, 1.0 / 16)

@@ -178,9 +178,8 @@ def test_verify_gemm(ns, oracle, N, K, M):
 
 
 def test_batched_verify_repeats(ns, oracle):
-    # blocks that split a row block's groups count themselves done on
-    # per-stream counters and leave them at zero: calls in a row agree bit
-    # for bit, also after a call with other shapes on the same stream
+    # the batched kernel keeps no state between calls: calls in a row agree
+    # bit for bit, also after a call with other shapes on the same stream
     base, refine, scales, qa, sa = _layer(oracle, 300, 4096, 144, (11,))
     W = tiled(ns, base, refine, scales)
     y1 = host(ns.verify_gemm(dev(qa), dev(sa), W))

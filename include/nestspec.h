@@ -310,6 +310,24 @@ int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K,
                     int32_t* emitted, float* y, int32_t* len, int32_t* next,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* verify_accept_x_static -- verify_accept_x with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The workspace is a
+ * device array inside the library, 1 MiB per device, held from the first
+ * call on a device until the process ends. It allocates and frees nothing. The call needs
+ * nest_gemv_x_workspace_size(B*(k+1), K, V) <= 1 MiB (the 152064-row LM
+ * head with up to 16 rows of K = 3584 needs 362 KB); a larger one returns
+ * NEST_EUNSUPPORTED before anything runs. All calls on one device share the array, so calls
+ * that overlap in time on one device (different streams, or threads
+ * without ordering) race; calls on one stream are ordered and safe.
+ * Arguments and errors otherwise as verify_accept_x. */
+int verify_accept_x_static(const float* x, int64_t B, int64_t k, int64_t K,
+                           const uint8_t* base, const uint8_t* refine,
+                           const float* scales, int64_t V, int64_t group,
+                           const int32_t* draft, int32_t* target,
+                           int32_t* n_emitted, int32_t* emitted, float* y,
+                           int32_t* len, int32_t* next, void* stream);
+
 /* Nested KV cache: a host struct holding device pointers (layouts above). */
 typedef struct nest_kv {
   const uint8_t* k_base;   /* [Hkv][capacity][d/2] bytes             */

@@ -999,3 +999,66 @@ extern "C" int verify_accept_x(const float* x, int64_t B, int64_t k, int64_t K, 
   return accept_impl("verify_accept_x", Act{nullptr, nullptr, x}, B, k, K, base, refine, scales, V,
                      group, draft, target, n_emitted, emitted, y, len, next, ws, ws_bytes, stream);
 }
+
+// ---------------------------------------------------------------------------
+// verify_accept_x without a caller workspace, for callers that cannot
+// allocate: the workspace is a file-scope device array of kStaticScratch
+// bytes, one copy per device, held until the process ends.
+// ---------------------------------------------------------------------------
+
+#include <mutex>
+
+namespace {
+
+constexpr size_t kStaticScratch = size_t{1} << 20;
+constexpr int kMaxDevices = 64;
+
+// Zero when the library loads; the only part that must be zero before a
+// call (the block counter in its first 256 bytes) is returned to zero by
+// every call, and the rest needs no initial contents.
+__device__ __align__(256) unsigned char scratch[kStaticScratch];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current); the host-side name of the array is not
+// a device address and is never passed to a kernel.
+int static_scratch(const char* what, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return nest::fail(NEST_EHIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return nest::fail(NEST_EUNSUPPORTED, "%s: device %d", what, dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return nest::fail(NEST_EHIP, "%s: hipGetSymbolAddress: %s", what, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NEST_OK;
+}
+
+}  // namespace
+
+extern "C" int verify_accept_x_static(const float* x, int64_t B, int64_t k, int64_t K, const uint8_t* base,
+                                      const uint8_t* refine, const float* scales, int64_t V, int64_t group,
+                                      const int32_t* draft, int32_t* target, int32_t* n_emitted,
+                                      int32_t* emitted, float* y, int32_t* len, int32_t* next, void* stream) {
+  const char* what = "verify_accept_x_static";
+  if (!x) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (B < 1 || k < 0 || K < 1 || V < 1 || B * (k + 1) > 16 || K > (1LL << 24) || V > (1LL << 30))
+    return nest::fail(NEST_EINVAL, "%s: B=%lld k=%lld K=%lld V=%lld", what, (long long)B, (long long)k,
+                      (long long)K, (long long)V);
+  const size_t need = gemv_ws_bytes(B * (k + 1), K, V, true);
+  if (need > kStaticScratch)
+    return nest::fail(NEST_EUNSUPPORTED, "%s: needs %zu bytes of scratch, more than its %zu", what, need,
+                      kStaticScratch);
+  void* ws = nullptr;
+  const int rc = static_scratch(what, &ws);
+  if (rc) return rc;
+  return accept_impl(what, Act{nullptr, nullptr, x}, B, k, K, base, refine, scales, V, group, draft, target,
+                     n_emitted, emitted, y, len, next, ws, kStaticScratch, stream);
+}

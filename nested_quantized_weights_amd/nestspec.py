@@ -66,6 +66,8 @@ _SIGS = {
     "verify_accept_x": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
                                        _p, _p, _p, _p, _p, _sz, _p]),
     "nest_gemv_x_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "verify_accept_x_static": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
+                                              _p, _p, _p, _p, _p]),
     "kv_nest_pack": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
     "nest_expected_tokens": (_d, [_d, _i64]),
     "nest_token_time": (_d, [_d, _i64, _d, _d]),
@@ -381,6 +383,25 @@ def verify_accept_x(x, B: int, k: int, W, draft, group: int = 128, want_y: bool 
                                  _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
                                  _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(length), _ptr(next_token),
                                  _ptr(ws), ws.numel(), _stream(dev)), what)
+    return out
+
+
+def verify_accept_x_static(x, B: int, k: int, W, draft, group: int = 128, want_y: bool = False, out=None,
+                           length=None, next_token=None):
+    """verify_accept_x on the library's own per-device scratch (no workspace)."""
+    what = "verify_accept_x_static"
+    _dev(x, torch.float32, what, "x")
+    _dev(draft, torch.int32, what, "draft")
+    W = _tiled(W, what, 2)
+    K = x.shape[1]
+    V = W.rows
+    dev = x.device
+    if out is None:
+        out = _accept_out(B, k, V, dev, want_y)
+    _check(lib().verify_accept_x_static(_ptr(x), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), V,
+                                        group, _ptr(draft), _ptr(out["target"]), _ptr(out["n_emitted"]),
+                                        _ptr(out["emitted"]), _ptr(out.get("y")), _ptr(length),
+                                        _ptr(next_token), _stream(dev)), what)
     return out
 
 

@@ -12,8 +12,11 @@ head and nested KV cache. A step is one full round at k = 4:
                         gives the draft token;
   one verify pass:      verify_gemm over both planes for the k+1 rows;
                         kv_nest_append of the target's K/V for the k+1
-                        positions (over the draft's); kv_nest_attend over
-                        the full view with k+1 queries; verify_accept on the
+                        positions (over the draft's); kv_nest_attend_exact
+                        over the full view: each of the k+1 queries sees the
+                        cache as a one-token pass at its position would, in
+                        one launch (so the round keeps target-only decoding's
+                        tokens exactly); verify_accept on the
                         LM head (exact fold, fused argmax, greedy accept of
                         the draft tokens).
 The per-token int8 quantization of each linear's fp32 input is part of the
@@ -108,6 +111,17 @@ def attend_bytes(view, Hkv, Hq, nq, ctx, d=128):
             + nq * Hq * d * 2 + nq * Hq * d * 4)
 
 
+def attend_exact_bytes(Hkv, Hq, nq, ctx, d=128, blk=128):
+    """The full view's planes and scales once, q in and o out, and for every
+    query the fp32 values of its open block up to its position (K and V),
+    which it quantizes over its own prefix."""
+    b = attend_bytes(1, Hkv, Hq, nq, ctx, d)
+    for i in range(nq):
+        p = ctx - nq + i
+        b += Hkv * 2 * (p - (p // blk) * blk + 1) * d * 4
+    return b
+
+
 def append_bytes(Hkv, pos, n, d=128, blk=128):
     """New K/V values in, the touched blocks' valid fp32 values read back from
     the shadow, both planes of every touched K and V block written, scales."""
@@ -144,7 +158,7 @@ def round_bytes(k):
         tot += linear_bytes(V, H, 1, 1, y=False, argmax=True)
     for _, N, K in LINEARS:
         tot += linear_bytes(N, K, k + 1, 2)
-    tot += append_bytes(hkv, CONTEXT, k + 1) + attend_bytes(1, hkv, hq, k + 1, CONTEXT + k + 1)
+    tot += append_bytes(hkv, CONTEXT, k + 1) + attend_exact_bytes(hkv, hq, k + 1, CONTEXT + k + 1)
     tot += accept_bytes(V, H, k, x_fp32=True)
     return tot
 
@@ -289,9 +303,9 @@ class Round:
                 calls.append((L.kv_nest_append, (ctypes.byref(self.kvs), p(sh[0]), p(sh[1]), p(vk),
                                                  p(vvv), lp, base_pos, k + 1, st), "append_verify"))
                 q = d["qv"][:k + 1]
-                calls.append((L.kv_nest_attend, (p(q), k + 1, hq, ctypes.byref(self.kvs), lp,
-                                                 base_pos + k + 1, 1, p(att_out), p(ws_att), ws_att_n,
-                                                 st), "attend_verify"))
+                calls.append((L.kv_nest_attend_exact, (p(q), k + 1, hq, ctypes.byref(self.kvs), p(sh[0]),
+                                                       p(sh[1]), lp, base_pos + k + 1, 1, p(att_out), p(ws_att),
+                                                       ws_att_n, st), "attend_verify"))
         xh = d["xv"]["head"][:k + 1]
         if sampled:
             calls.append((L.verify_gemm_x, (p(xh), k + 1, H, p(d["base"]["head"]), p(d["refine"]["head"]),
@@ -391,24 +405,25 @@ def tiny_decoder(torch, n_new=48, prompt_len=40):
     dec = Decoder(cfg, synth.decoder_weights(cfg, (800,)))
     prompt = synth.tokens(prompt_len, cfg["vocab"], (801,))
 
-    def run(k, exact):
-        dec.generate(prompt, 8, k, exact)  # warm-up
+    def run(k, mode):
+        dec.generate(prompt, 8, k, mode)  # warm-up
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        toks, rounds = dec.generate(prompt, n_new, k, exact)
+        toks, rounds = dec.generate(prompt, n_new, k, mode)
         torch.cuda.synchronize()
         return toks, rounds, time.perf_counter() - t0
 
-    ar, _, t_ar = run(0, True)
+    ar, _, t_ar = run(0, "exact")
     out = {"workload": f"{cfg['layers']}-layer synthetic pre-norm decoder, hidden {cfg['hidden']}, "
                        f"{cfg['q_heads']}/{cfg['kv_heads']} heads of {cfg['head_dim']}, SwiGLU {cfg['inter']}, "
                        f"vocab {cfg['vocab']}; {prompt_len}-token prompt, {n_new} new tokens",
            "tokens_per_round": {}, "equal_to_target_only": {}, "batched_first_divergence": {},
            "host_loop_tokens_per_s": {"target_only": round(n_new / t_ar, 1)}}
     for k in (1, 4):
-        for exact in (True, False):
-            toks, rounds, t = run(k, exact)
-            tag = f"k{k}_{'exact' if exact else 'batched'}"
+        for mode in ("exact", "batched"):
+            exact = mode == "exact"
+            toks, rounds, t = run(k, mode)
+            tag = f"k{k}_{mode}"
             out["tokens_per_round"][tag] = round(float(np.mean([n for n, _ in rounds])), 3)
             out["host_loop_tokens_per_s"][tag] = round(n_new / t, 1)
             if exact:
@@ -722,8 +737,12 @@ def oracle_round(O, inp, packed, k):
         qa, sa = O.act_quant(inp["xv"][n][:k + 1])
         O.verify_gemm(qa, sa, *packed[n])
         if n == "qkv":
-            O.kv_append(okv, kf, vf, inp["vk"][:, :k + 1], inp["vv"][:, :k + 1], CONTEXT)
-            att = O.kv_attend(inp["qv"][:k + 1], okv, CONTEXT + k + 1, 1)
+            # the target's k+1 positions, each attending the cache a
+            # one-token pass at that position sees
+            att = np.empty((k + 1, QWEN["q_heads"], 128))
+            for i in range(k + 1):
+                O.kv_append(okv, kf, vf, inp["vk"][:, i:i + 1], inp["vv"][:, i:i + 1], CONTEXT + i)
+                att[i] = O.kv_attend(inp["qv"][i:i + 1], okv, CONTEXT + i + 1, 1)[0]
     qa, sa = O.act_quant(inp["xv"]["head"][:k + 1])
     acc = O.verify_accept(qa, sa, 1, k, *packed["head"], np.array(drafts, np.int32))
     dt = time.perf_counter() - t0

@@ -420,6 +420,31 @@ int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
                    const nest_kv* kv, const int32_t* ctx_dev, int64_t ctx_len,
                    int view, float* out, void* ws, size_t ws_bytes,
                    void* stream);
+/* kv_nest_attend_exact -- the k+1 queries of one verify pass, each seeing
+ * the cache exactly as a one-token pass at its own position would ("How
+ * Speculative Decoding Speeds Up Inference", section "Drafting and checking
+ * tokens", step 2: one pass checks every position; section "The same
+ * output as the large model alone"), in one launch.
+ * Query i (position p_i = L - nq + i, L the visible length) sees tokens
+ * 0..p_i. The block holding p_i is taken as kv_nest_append would have
+ * quantized it after a one-token append at p_i: from its fp32 values in
+ * the shadows, over its tokens up to p_i only; every earlier block comes
+ * from the planes. Each query's output is bit-identical to kv_nest_attend
+ * with that one query at length p_i + 1 (same view, same ctx_dev use) when
+ * both split the context alike, which they always do when the length is on
+ * the device. Call it after kv_nest_append of the nq new tokens: the
+ * append leaves every token of the (at most two) blocks they touch in the
+ * shadows and seals a block they fill.
+ *   shadow_k, shadow_v  the kv_nest_append shadows of this cache
+ *   the rest as for kv_nest_attend; the workspace of kv_nest_attend with
+ *   the same arguments is enough.
+ * Requires Hq/Hkv <= 16 and nq <= block. Errors: as kv_nest_attend. */
+int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,
+                         const nest_kv* kv, const float* shadow_k,
+                         const float* shadow_v, const int32_t* ctx_dev,
+                         int64_t ctx_len, int view, float* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
 size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
                                      int64_t n_kv_heads, int64_t head_dim,
                                      int64_t ctx_len);

@@ -43,7 +43,7 @@
 //     running maximum multiply the block's fp32 product.
 // The result then does not depend on the magnitude of q, K or V beyond
 // fp32's range.
-#include "common.h"
+#include "quant.h"
 
 namespace {
 
@@ -62,6 +62,7 @@ struct AttArgs {
   const uint8_t *kb, *kr, *vb, *vr;
   const float *ks, *vs;
   int cap, nb;         // capacity and blocks per head in the planes
+  const float *shk, *shv;  // exact mode: fp32 shadows [Hkv][2][block][d] of the two newest blocks
   int bpw, nchunk;     // blocks per workgroup, chunks (workgroups) per head
   float* part_ml;      // [Hkv][nchunk][R][2]  (max in log2 domain, sum)
   float* part_o;       // [Hkv][nchunk][R][128]
@@ -430,6 +431,75 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   }
 }
 
+// Exact mode (kv_nest_attend_exact): the block holding query position pos,
+// rebuilt from its fp32 values in the shadow and quantized over its tokens
+// up to pos alone, with the rule and the layouts kv_nest_append uses, so
+// the codes and scales are those a one-token append at pos would have
+// written. Planes go to LDS (K [token][64 B], V [dim][64 B], base then
+// refine), the scales to osc[0] (K) and osc[1] (V). All 256 threads take
+// part; ends with a barrier.
+constexpr int kOpenPlane = kBlk * kD / 2;  // bytes of one plane of one block
+
+// One plane pair of the open block. Thread t holds 64 values: K elements
+// 64t .. 64t + 63 (token t/2, half of its dims: 32 bytes of each K plane),
+// or V dim t/2 over tokens 64(t&1) .. + 63 (32 bytes of each dim-major V
+// plane). All loads are issued at once (values past the valid tokens are
+// taken as 0), so each plane pair waits for one round trip.
+template <bool IS_V>
+__device__ __forceinline__ void quantize_open_plane(const float* src, int valid, uint8_t* pb, uint8_t* pr,
+                                                    float* osc, float* red) {
+  const int t = threadIdx.x, row = t >> 1, c0 = 64 * (t & 1);
+  float x[64];
+  if (IS_V) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = src[(c0 + i) * kD + row];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(src + row * kD + c0)[i];
+      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if ((IS_V ? c0 + i : row) >= valid) x[i] = 0.0f;
+    m = fmaxf(m, fabsf(x[i]));
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m / 7.0f, s16 = s * 0.0625f, r = 1.0f / s, r16 = 1.0f / s16;
+  if (t == 0) osc[IS_V ? 1 : 0] = s;
+  // element pair (2m, 2m+1) -> one byte of each plane (low nibble first),
+  // as kv_nest_append writes them
+  uint32_t* b32 = reinterpret_cast<uint32_t*>(pb + row * 64 + c0 / 2);
+  uint32_t* r32 = reinterpret_cast<uint32_t*>(pr + row * 64 + c0 / 2);
+#pragma unroll
+  for (int i = 0; i < 64; i += 8) {
+    uint32_t wb = 0, wr = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int qb, qr;
+      nest::nest_codes_fast(x[i + j], s, s16, r, r16, qb, qr);
+      wb |= static_cast<uint32_t>(qb & 15) << (4 * j);
+      wr |= static_cast<uint32_t>(qr & 15) << (4 * j);
+    }
+    b32[i / 8] = wb;
+    r32[i / 8] = wr;
+  }
+  __syncthreads();  // red is reused by the next plane pair
+}
+
+__device__ void quantize_open_block(const AttArgs& a, int h, int blk, int pos, uint8_t* ob, float* osc,
+                                    float* red) {
+  const int valid = pos - blk * kBlk + 1;
+  const size_t off = (static_cast<size_t>(h) * 2 + (blk & 1)) * kBlk * kD;
+  quantize_open_plane<false>(a.shk + off, valid, ob, ob + kOpenPlane, osc, red);
+  quantize_open_plane<true>(a.shv + off, valid, ob + 2 * kOpenPlane, ob + 3 * kOpenPlane, osc, red);
+}
+
 // Few query rows (R <= 16, e.g. one draft query over a GQA group): every
 // wave owns whole 128-token blocks. Lane (q4, c16) loads exactly the 16-byte
 // code slices its MFMA operands need (K: token tau(tt, c16), dims
@@ -442,41 +512,93 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
 // (one block per wave, kTargetWaves), so the register budget of two waves
 // per SIMD is free: the MFMA accumulators then stay in VGPRs (no AGPR round
 // trips per block).
-template <int VIEW>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) attend_wave_kernel(AttArgs a) {
+//
+// EXACT (kv_nest_attend_exact): each query of a verify pass is computed as
+// the one-query call at its own position would compute it, in one launch.
+// A workgroup serves one (chunk, kv head, query); its rows are that
+// query's GQA group, its visible blocks end at the query's position, and
+// the block holding that position is rebuilt by quantize_open_block (the
+// others are read from the planes). The per-row arithmetic, the split into
+// chunks and the merge are those of the one-query call, so the outputs are
+// bit-identical to it. Workgroups are numbered so that the queries of one
+// (chunk, head) run one after another on one XCD and share its L2.
+template <int VIEW, bool EXACT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+attend_wave_kernel(AttArgs a) {
   __shared__ float ml[4][16][2];
-  __shared__ float buf[4][16][kD + 4];  // each wave's rescaled O
+  __shared__ __align__(16) float buf[4][16][kD + 4];  // each wave's rescaled O
+  // exact mode: the rebuilt open block's planes share buf's space (read
+  // only in the block loop; buf is written after the barrier that follows
+  // every wave's loop)
+  static_assert(sizeof(buf) >= 4 * kOpenPlane, "open block planes fit in buf");
+  uint8_t* ob = reinterpret_cast<uint8_t*>(&buf[0][0][0]);
+  __shared__ float osc[2], ored[8];
   // the wave index is uniform: block numbers, scale loads and branches on
   // them stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
-  const int h = blockIdx.y, chunk = blockIdx.x;
-  const int ctx = live_ctx(a), nbv = (ctx + kBlk - 1) / kBlk;
+  int h = blockIdx.y, chunk = blockIdx.x, z = 0;
+  if (EXACT) {
+    // item = (chunk, head, query) with the query fastest; XCD x (= block id
+    // mod 8) takes the contiguous items [x * per, (x + 1) * per), so the
+    // queries of one (chunk, head) run together on one XCD and share its L2
+    const int n_items = a.nchunk * (a.Hq / a.grp) * a.nq;
+    const int per = (n_items + 7) / 8;
+    const int item = (static_cast<int>(blockIdx.x) & 7) * per + (static_cast<int>(blockIdx.x) >> 3);
+    if (item >= n_items) return;
+    z = item % a.nq;
+    chunk = (item / a.nq) % a.nchunk;
+    h = item / a.nq / a.nchunk;
+  }
+  const int ctx = live_ctx(a);
+  // exact: this query's position and the blocks it sees
+  const int pos_z = ctx - a.nq + z;
+  const int nbv = EXACT ? pos_z / kBlk + 1 : (ctx + kBlk - 1) / kBlk;
+  const int b_open = EXACT ? pos_z / kBlk : -1;
 
   const int b_first = chunk * a.bpw;
   const int b_last = min(b_first + a.bpw, nbv);
   const int b0 = b_first + wave;  // the wave's blocks are b0, b0 + 4, ...
+  if (EXACT && b_open >= b_first && b_open < b_last) quantize_open_block(a, h, b_open, pos_z, ob, osc, ored);
 
   uint4 kb[8], kr[8], vb[8], vr[8];
   float ks, vs;
   // K codes first, then V: loads return in issue order, so the scores and
   // the softmax of a block start while its V codes are still on the way
   auto load = [&](int blk) {
+    if (EXACT && blk == b_open) {  // the rebuilt open block, from LDS
+      ks = osc[0];
+      vs = osc[1];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
+        kb[tt] = ld16(ob + tok * (kD / 2) + 16 * q4);
+        kr[tt] = VIEW ? ld16(ob + kOpenPlane + tok * (kD / 2) + 16 * q4) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int o = (tt * 16 + c16) * (kBlk / 2) + 16 * q4;
+        vb[tt] = ld16(ob + 2 * kOpenPlane + o);
+        vr[tt] = VIEW ? ld16(ob + 3 * kOpenPlane + o) : make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
     const size_t hb = static_cast<size_t>(h) * a.nb + blk;
     ks = a.ks[hb];
     vs = a.vs[hb];
+    auto ld = [](const uint8_t* p) { return nest::ldnt16(p); };
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
       const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
-      kb[tt] = nest::ldnt16(a.kb + koff);
-      kr[tt] = VIEW ? nest::ldnt16(a.kr + koff) : make_uint4(0, 0, 0, 0);
+      kb[tt] = ld(a.kb + koff);
+      kr[tt] = VIEW ? ld(a.kr + koff) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
-      vb[tt] = nest::ldnt16(a.vb + voff);
-      vr[tt] = VIEW ? nest::ldnt16(a.vr + voff) : make_uint4(0, 0, 0, 0);
+      vb[tt] = ld(a.vb + voff);
+      vr[tt] = VIEW ? ld(a.vr + voff) : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -485,8 +607,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   // the bias product are formed while the codes are on the way.
   uint4 qraw[4];
   int pos = -1;
-  if (c16 < a.R) {
-    const int i = c16 / a.grp, g = c16 % a.grp;
+  // rows of this workgroup: its query's GQA group (exact), or all R rows
+  const int nrow = EXACT ? a.grp : a.R;
+  if (c16 < nrow) {
+    const int i = EXACT ? z : c16 / a.grp, g = EXACT ? c16 : c16 % a.grp;
     pos = ctx - a.nq + i;
     const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
@@ -527,7 +651,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   // Rows whose position is at least pos_min see every token of a block that
   // ends at or before pos_min; only later blocks need the causal mask.
-  const int pos_min = ctx - a.nq;
+  const int pos_min = EXACT ? pos_z : ctx - a.nq;
   auto block = [&](int blk, bool first) {
     const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
     const int t0 = blk * kBlk;
@@ -659,9 +783,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
     for (int i = 0; i < 4; ++i) buf[wave][c16][dt * 16 + 4 * q4 + i] = O[dt][i] * f;
   __syncthreads();
-  // the four waves' parts added in the fixed order w = 3 .. 0
-  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R;
-  for (int idx = threadIdx.x; idx < a.R * (kD / 4); idx += 256) {
+  // the four waves' parts added in the fixed order w = 3 .. 0; in exact
+  // mode this workgroup's rows are rows z * grp .. of the call
+  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R + (EXACT ? z * a.grp : 0);
+  for (int idx = threadIdx.x; idx < nrow * (kD / 4); idx += 256) {
     const int row = idx / (kD / 4), d4 = idx % (kD / 4);
     float4 v = *reinterpret_cast<const float4*>(&buf[3][row][4 * d4]);
 #pragma unroll
@@ -671,7 +796,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
     *reinterpret_cast<float4*>(&a.part_o[(pbase + row) * kD + 4 * d4]) = v;
   }
-  if (threadIdx.x < a.R) {
+  if (static_cast<int>(threadIdx.x) < nrow) {
     const int row = threadIdx.x;
     float Mr = -INFINITY;
 #pragma unroll
@@ -793,7 +918,7 @@ template <int VIEW>
 int launch_att(const AttArgs& a, const Plan& p, int Hkv, hipStream_t st) {
   dim3 grid(p.nchunk, Hkv);
   switch (p.RT) {
-    case 1: attend_wave_kernel<VIEW><<<grid, 256, 0, st>>>(a); break;
+    case 1: attend_wave_kernel<VIEW, false><<<grid, 256, 0, st>>>(a); break;
     case 2: attend_kernel<2, VIEW><<<grid, 256, 0, st>>>(a); break;
     case 3: attend_kernel<3, VIEW><<<grid, 256, 0, st>>>(a); break;
     default: attend_kernel<4, VIEW><<<grid, 256, 0, st>>>(a); break;
@@ -812,10 +937,12 @@ extern "C" size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads, i
   return make_plan(nq, n_q_heads, n_kv_heads, ctx_len).ws;
 }
 
-extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
-                              const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, void* ws,
-                              size_t ws_bytes, void* stream) {
-  const char* what = "kv_nest_attend";
+namespace {
+
+// Host checks shared by both attention entry points; fills the kernel
+// arguments except the plan-dependent ones.
+int prepare_attend(const char* what, const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
+                   const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, AttArgs& a) {
   if (!q || !kv || !out) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (!kv->k_base || !kv->v_base || !kv->k_scale || !kv->v_scale)
     return nest::fail(NEST_EINVAL, "%s: null cache pointer", what);
@@ -841,24 +968,87 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
       (view == 1 && (!nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))))
     return nest::fail(NEST_EALIGN, "%s: planes must be 16-byte aligned", what);
   if (!nest::aligned16(q)) return nest::fail(NEST_EALIGN, "%s: q must be 16-byte aligned", what);
-  // with the length on the device, the grid covers the whole capacity and
-  // the workgroups past the live length write empty partials
-  const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
-  if (p.nchunk > kMaxChunks) return nest::fail(NEST_EUNSUPPORTED, "%s: too many chunks", what);
-  if (!ws || ws_bytes < p.ws) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, p.ws);
-  if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
-  AttArgs a{};
+  a = AttArgs{};
   a.q = q; a.nq = (int)nq; a.Hq = (int)n_q_heads; a.grp = (int)(n_q_heads / Hkv); a.R = (int)R;
   a.ctx = (int)ctx_len; a.ctx_dev = ctx_dev;
   a.kb = kv->k_base; a.kr = kv->k_refine; a.vb = kv->v_base; a.vr = kv->v_refine;
   a.ks = kv->k_scale; a.vs = kv->v_scale;
   a.cap = (int)kv->capacity; a.nb = (int)(kv->capacity / kBlk);
+  a.out = out;
+  return NEST_OK;
+}
+
+int attach_workspace(const char* what, AttArgs& a, const Plan& p, int64_t Hkv, void* ws, size_t ws_bytes,
+                     size_t need) {
+  if (p.nchunk > kMaxChunks) return nest::fail(NEST_EUNSUPPORTED, "%s: too many chunks", what);
+  if (!ws || ws_bytes < need) return nest::fail(NEST_EWORKSPACE, "%s: workspace needs %zu bytes", what, need);
+  if (!nest::aligned16(ws)) return nest::fail(NEST_EALIGN, "%s: workspace must be 16-byte aligned", what);
   a.bpw = p.bpw; a.nchunk = p.nchunk;
   a.part_ml = static_cast<float*>(ws);
   // part_o starts 16-byte aligned after the (max, sum) pairs
-  const size_t ml_floats = (static_cast<size_t>(Hkv) * p.nchunk * R * 2 + 3) & ~static_cast<size_t>(3);
+  const size_t ml_floats = (static_cast<size_t>(Hkv) * p.nchunk * a.R * 2 + 3) & ~static_cast<size_t>(3);
   a.part_o = a.part_ml + ml_floats;
-  a.out = out;
+  return NEST_OK;
+}
+
+}  // namespace
+
+extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
+                              const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  const char* what = "kv_nest_attend";
+  AttArgs a;
+  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, a);
+  if (rc) return rc;
+  const int64_t Hkv = kv->n_kv_heads;
+  // with the length on the device, the grid covers the whole capacity and
+  // the workgroups past the live length write empty partials
+  const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
+  rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, p.ws);
+  if (rc) return rc;
   hipStream_t st = nest::as_stream(stream);
   return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);
+}
+
+extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
+                                    const float* shadow_k, const float* shadow_v, const int32_t* ctx_dev,
+                                    int64_t ctx_len, int view, float* out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  const char* what = "kv_nest_attend_exact";
+  AttArgs a;
+  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, a);
+  if (rc) return rc;
+  if (!shadow_k || !shadow_v) return nest::fail(NEST_EINVAL, "%s: null shadow", what);
+  if (a.grp > 16) return nest::fail(NEST_EUNSUPPORTED, "%s: Hq/Hkv=%d > 16", what, a.grp);
+  if (nq > kBlk) return nest::fail(NEST_EUNSUPPORTED, "%s: nq=%lld > block", what, (long long)nq);
+  a.shk = shadow_k;
+  a.shv = shadow_v;
+  const int64_t Hkv = kv->n_kv_heads;
+  if (nq == 1) {
+    // one query: the append of its token left its block quantized over
+    // exactly the tokens up to it, so the planes are what it must see
+    const Plan p = make_plan(1, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
+    rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, p.ws);
+    if (rc) return rc;
+    hipStream_t st = nest::as_stream(stream);
+    return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);
+  }
+  // every query takes the split of a one-query call (its workgroups write
+  // rows z * grp .. of the partials)
+  const Plan p = make_plan(1, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
+  const size_t rows = static_cast<size_t>(Hkv) * p.nchunk * a.R;
+  const size_t need = (((rows * 2 + 3) & ~static_cast<size_t>(3)) + rows * kD) * sizeof(float);
+  rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, need);
+  if (rc) return rc;
+  const int64_t items = static_cast<int64_t>(p.nchunk) * Hkv * nq;
+  const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
+  hipStream_t st = nest::as_stream(stream);
+  if (view == 0)
+    attend_wave_kernel<0, true><<<grid, 256, 0, st>>>(a);
+  else
+    attend_wave_kernel<1, true><<<grid, 256, 0, st>>>(a);
+  rc = nest::check_launch(what);
+  if (rc) return rc;
+  combine_kernel<<<dim3(a.R, Hkv), 1024, 0, st>>>(a);
+  return nest::check_launch("kv_nest_attend_exact(combine)");
 }

@@ -7,7 +7,7 @@
 // one byte in each plane. Every division is IEEE fp32 (correctly rounded,
 // HIP's default), rintf rounds ties to even, and the residual is one fmaf,
 // so the codes are those of the rule in nestspec.h bit for bit.
-#include "common.h"
+#include "quant.h"
 
 namespace {
 
@@ -161,38 +161,6 @@ __global__ void __launch_bounds__(256) tile_scales_kernel(const float* __restric
   dst[f] = (n < rows && g < G) ? src[n * G + g] : 0.0f;
 }
 
-// Round to the nearest integer of x / s by x * r (r = 1/s), taking the IEEE
-// quotient only when x * r is within 1e-5 of a half-integer. For |x/s| <= 8
-// both x * r and fl(x/s) are within 1e-6 of x/s, so away from a tie all
-// three round alike.
-__device__ __forceinline__ float rint_div(float x, float s, float r) {
-  const float t = x * r;
-  return (fabsf(t - floorf(t) - 0.5f) > 1.0e-5f && r < INFINITY) ? rintf(t) : rintf(x / s);
-}
-
-// nest_codes with the two quotients formed by rint_div; |w/s| <= 7 and
-// |e/s16| <= 8 + 2^-20 hold by construction of s, so the codes are those of
-// nest_codes bit for bit.
-__device__ __forceinline__ void nest_codes_fast(float w, float s, float s16, float rs, float rs16, int& qb,
-                                                int& qr) {
-  if (s == 0.0f) {
-    qb = 0;
-    qr = 0;
-    return;
-  }
-  int b = static_cast<int>(rint_div(w, s, rs));
-  b = b < -7 ? -7 : (b > 7 ? 7 : b);
-  const float e = fmaf(-s, static_cast<float>(b), w);
-  int r = 0;
-  if (s16 != 0.0f) {
-    float u = rint_div(e, s16, rs16);
-    u = u < -8.0f ? -8.0f : (u > 7.0f ? 7.0f : u);
-    r = static_cast<int>(u);
-  }
-  qb = b;
-  qr = r;
-}
-
 // KV append. Block b of kv head h, K or V, is coded by kAppendSplit
 // workgroups, each over its own share of the element pairs. Every one of
 // them takes the block's max |v| itself (tokens before pos from the shadow
@@ -279,8 +247,8 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
       w1 = value(t, j + 1);
     }
     int b0, r0, b1, r1;
-    nest_codes_fast(w0, s, s16, rs, rs16, b0, r0);
-    nest_codes_fast(w1, s, s16, rs, rs16, b1, r1);
+    nest::nest_codes_fast(w0, s, s16, rs, rs16, b0, r0);
+    nest::nest_codes_fast(w1, s, s16, rs, rs16, b1, r1);
     pb[p] = static_cast<uint8_t>((b0 & 15) | ((b1 & 15) << 4));
     pr[p] = static_cast<uint8_t>((r0 & 15) | ((r1 & 15) << 4));
   }

@@ -15,15 +15,17 @@ position and context length is that device length plus a host offset, so
 rounds can be issued back to back without the host reading anything
 (run_rounds); generate() reads each round's count only to know when to stop.
 
-A target pass over the k+1 positions of a round attends either
-  exact    position by position (append one token, attend with its query),
-           so each query sees the cache a one-token pass would see; with
-           row-independent layers the round then emits exactly the tokens
-           and logits of target-only decoding ("The same output as the
-           large model alone"), or
-  batched  with one append of all k+1 tokens and one attention of all k+1
-           queries, where the open block is quantized with the later
-           positions of the pass included.
+A target pass over the k+1 positions of a round attends in one of three ways:
+  exact     one append of the k+1 tokens, then kv_nest_attend_exact: one
+            launch in which each query sees the cache a one-token pass at
+            its position would see (its open block quantized over its own
+            prefix); with row-independent layers the round then emits
+            exactly the tokens and logits of target-only decoding ("The
+            same output as the large model alone");
+  stepwise  position by position (append one token, attend with its
+            query): the same result with k+1 launches of each;
+  batched   one append and one attention of all k+1 queries, where the open
+            block is quantized with the later positions of the pass included.
 """
 from __future__ import annotations
 
@@ -67,10 +69,13 @@ class Decoder:
     def _linear(self, x, W, draft):
         return ns.draft_gemv_x(x, W) if draft else ns.verify_gemm_x(x, W)
 
-    def forward(self, tokens: torch.Tensor, off: int, draft: bool, exact: bool = True) -> torch.Tensor:
+    def forward(self, tokens: torch.Tensor, off: int, draft: bool, mode: str = "exact") -> torch.Tensor:
         """Hidden states after the final norm for int32 tokens [M] at
         positions length + off.. (length on the device), with their K/V
-        appended to every layer's cache."""
+        appended to every layer's cache; mode is how a multi-token pass
+        attends (module docstring)."""
+        if mode not in ("exact", "stepwise", "batched"):
+            raise ValueError(f"mode {mode!r}")
         c = self.cfg
         M = tokens.numel()
         Hq, Hkv, d, eps = c["q_heads"], c["kv_heads"], c["head_dim"], c["eps"]
@@ -82,15 +87,21 @@ class Decoder:
         for lw, (kv, sh) in zip(self.layers, self.kv):
             ns.add_rmsnorm(x, dn, lw["norm_attn"], eps, out=h)
             qkv = self._linear(h, lw["qkv"], draft)
-            q, k, v = ns.rope_split(qkv, off, Hq, Hkv, d, c["theta"], token_major=exact, pos_dev=L)
-            if exact:
+            stepwise = mode == "stepwise"
+            q, k, v = ns.rope_split(qkv, off, Hq, Hkv, d, c["theta"], token_major=stepwise, pos_dev=L)
+            if stepwise:
                 att = torch.empty((M, Hq, d), dtype=torch.float32, device=self.dev)
                 for i in range(M):
                     ns.kv_nest_append(kv, sh, k[i].unsqueeze(1), v[i].unsqueeze(1), off + i, pos_dev=L)
                     ns.kv_nest_attend(q[i:i + 1], kv, off + i + 1, view, out=att[i:i + 1], ctx_dev=L)
             else:
                 ns.kv_nest_append(kv, sh, k, v, off, pos_dev=L)
-                att = ns.kv_nest_attend(q, kv, off + M, view, ctx_dev=L)
+                # one position: the append quantized its block over exactly
+                # the tokens up to it, so every mode is the plain attention
+                if mode == "exact" and M > 1:
+                    att = ns.kv_nest_attend_exact(q, kv, sh, off + M, view, ctx_dev=L)
+                else:
+                    att = ns.kv_nest_attend(q, kv, off + M, view, ctx_dev=L)
             o = self._linear(att.view(M, Hq * d), lw["o"], draft)
             ns.add_rmsnorm(x, o, lw["norm_mlp"], eps, out=h)
             dn = self._linear(ns.swiglu(self._linear(h, lw["gate_up"], draft)), lw["down"], draft)
@@ -105,7 +116,7 @@ class Decoder:
         p = torch.from_numpy(np.ascontiguousarray(prompt, np.int32)).to(self.dev)
         n = p.numel() - 1
         for s in range(0, n, 16):
-            self.forward(p[s:min(n, s + 16)], s, draft=False, exact=True)
+            self.forward(p[s:min(n, s + 16)], s, draft=False, mode="exact")
         self.length.fill_(n)
         return p[n:n + 1]
 
@@ -118,22 +129,22 @@ class Decoder:
                 "emitted": E((rounds, k + 1), dtype=torch.int32, device=self.dev),
                 "y": E((rounds, k + 1, V), dtype=torch.float32, device=self.dev) if want_y else None}
 
-    def _round(self, r: int, k: int, exact: bool, b: dict):
+    def _round(self, r: int, k: int, mode: str, b: dict):
         """Issue round r: k draft steps and one target pass. Slot 0 of
         b["toks"][r] holds the round's input; verify_accept advances the
         committed length and writes the next round's input."""
         toks = b["toks"][r]
         for j in range(k):
-            h = self.forward(toks[j:j + 1], j, draft=True, exact=True)
+            h = self.forward(toks[j:j + 1], j, draft=True, mode="exact")
             ns.draft_gemv_x(h, self.head, want_y=False, argmax=True, argmax_out=toks[j + 1:j + 2])
-        h = self.forward(toks, 0, draft=False, exact=exact)
+        h = self.forward(toks, 0, draft=False, mode=mode)
         out = {"target": b["target"][r], "n_emitted": b["n_emitted"][r], "emitted": b["emitted"][r]}
         if b["y"] is not None:
             out["y"] = b["y"][r]
         ns.verify_accept_x(h, 1, k, self.head, toks[1:] if k else self.no_draft, out=out,
                            length=self.length, next_token=b["toks"][r + 1][0:1])
 
-    def run_rounds(self, prompt, rounds: int, k: int, exact: bool = True, want_y: bool = True):
+    def run_rounds(self, prompt, rounds: int, k: int, mode: str = "exact", want_y: bool = True):
         """A fixed number of rounds issued back to back with no host read
         between them (positions, lengths and inputs advance on the device).
         Returns (tokens, per round (emitted count, logits of the emitted
@@ -141,7 +152,7 @@ class Decoder:
         b = self._buffers(rounds, k, want_y)
         b["toks"][0, 0:1].copy_(self.prefill(prompt))
         for r in range(rounds):
-            self._round(r, k, exact, b)
+            self._round(r, k, mode, b)
         n = b["n_emitted"][:, 0].cpu().numpy()
         em = b["emitted"].cpu().numpy()
         toks, per = [], []
@@ -150,7 +161,7 @@ class Decoder:
             per.append((int(n[r]), b["y"][r, :n[r]] if want_y else None))
         return toks, per
 
-    def generate(self, prompt, n_new: int, k: int, exact: bool = True):
+    def generate(self, prompt, n_new: int, k: int, mode: str = "exact"):
         """Greedy decoding of n_new tokens after the prompt: one target pass
         per token when k = 0, else rounds of k draft steps and one target
         pass; each round's emitted count is read back to know when to stop.
@@ -160,7 +171,7 @@ class Decoder:
         b["toks"][0, 0:1].copy_(self.prefill(prompt))
         out, rounds, r = [], [], 0
         while len(out) < n_new:
-            self._round(r, k, exact, b)
+            self._round(r, k, mode, b)
             n = int(b["n_emitted"][r, 0].item())
             out += b["emitted"][r, :n].tolist()
             rounds.append((n, b["y"][r, :n]))

@@ -81,6 +81,8 @@ _SIGS = {
     "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _i64, ctypes.c_int, _p,
                                       _p, _sz, _p]),
     "kv_nest_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "kv_nest_attend_exact": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _p, _p, _i64, ctypes.c_int,
+                                            _p, _p, _sz, _p]),
     "nest_sample": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_float, _p, _p, _p, _sz, _p]),
     "nest_sample_workspace_size": (_sz, [_i64, _i64]),
     "verify_sample": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p, _p,
@@ -491,6 +493,33 @@ def kv_nest_attend(q: torch.Tensor, kv: NestKV, ctx_len: int, view: int, out=Non
     s = kv.struct()
     _check(lib().kv_nest_attend(_ptr(q), nq, Hq, ctypes.byref(s), _ptr(ctx_dev), int(ctx_len), int(view),
                                 _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), what)
+    return out
+
+
+def kv_nest_attend_exact(q: torch.Tensor, kv: NestKV, shadow, ctx_len: int, view: int, out=None, ws=None,
+                         ctx_dev=None):
+    """The nq queries of one verify pass, each exactly as a one-query call at
+    its own position (after kv_nest_append of the nq tokens). q: bf16 bits
+    [nq][Hq][d]. Returns fp32 [nq][Hq][d]."""
+    what = "kv_nest_attend_exact"
+    if not isinstance(q, torch.Tensor) or not q.is_cuda or not q.is_contiguous():
+        raise NestError(f"{what}: q must be a contiguous CUDA tensor")
+    if q.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise NestError(f"{what}: q must hold bf16 bit patterns")
+    if ctx_dev is not None:
+        _dev(ctx_dev, torch.int32, what, "ctx_dev")
+    nq, Hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((nq, Hq, d), dtype=torch.float32, device=dev)
+    plan_len = kv.capacity if ctx_dev is not None else int(ctx_len)
+    wsn = lib().kv_nest_attend_workspace_size(nq, Hq, kv.n_kv_heads, d, plan_len)
+    if ws is None or ws.numel() < wsn:
+        ws = workspace(max(wsn, 256), dev, "attend")
+    s = kv.struct()
+    _check(lib().kv_nest_attend_exact(_ptr(q), nq, Hq, ctypes.byref(s), _ptr(shadow[0]), _ptr(shadow[1]),
+                                      _ptr(ctx_dev), int(ctx_len), int(view), _ptr(out), _ptr(ws), ws.numel(),
+                                      _stream(dev)), what)
     return out
 
 

@@ -1,0 +1,104 @@
+"""kv_nest_attend_exact: the k+1 queries of a verify pass in one launch, each
+seeing the cache as a one-token pass at its own position would (GPU).
+
+After one kv_nest_append of the nq new tokens, query i's output must be
+bit-identical to the one-query kv_nest_attend a position-by-position pass
+makes (append token i, attend with query i), and within the 2e-3 normwise
+tolerance of the oracle's position-by-position attention ("How Speculative
+Decoding Speeds Up Inference", section "Drafting and checking tokens",
+step 2; BitNest, Figure 4). Cases cross a block boundary inside the pass,
+start at an empty cache, use every GQA width the configurations have, both
+views, and device-held lengths; one runs at the 32K context.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nested_quantized_weights_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ns():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nested_quantized_weights_amd import nestspec
+
+    nestspec.lib()
+    return nestspec
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def prefilled(ns, kf, vf, ctx0):
+    kd, vd = dev(kf), dev(vf)
+    kv = ns.kv_nest_pack(kd, vd)
+    sh = ns.kv_shadow(kv)
+    ns.kv_nest_shadow_fill(kv, kd, vd, ctx0, sh)
+    return kv, sh
+
+
+def inputs(Hq, Hkv, cap, ctx0, nq, key):
+    kf, vf = synth.kv(Hkv, cap, 128, (key, 0))
+    kf[:, ctx0:] = 0.0
+    vf[:, ctx0:] = 0.0
+    kn, vn = synth.kv(Hkv, nq, 128, (key, 1))
+    q = synth.queries_bf16(nq, Hq, 128, (key, 2))
+    return kf, vf, kn, vn, q
+
+
+CASES = [(28, 4, 1024, 300, 5), (8, 2, 512, 126, 5), (32, 8, 384, 250, 9), (4, 1, 256, 0, 3),
+         (16, 16, 640, 511, 2), (28, 4, 512, 123, 9)]
+
+
+@pytest.mark.parametrize("view", [0, 1])
+@pytest.mark.parametrize("on_device", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,cap,ctx0,nq", CASES)
+def test_exact_equals_position_by_position(ns, oracle, Hq, Hkv, cap, ctx0, nq, on_device, view):
+    kf, vf, kn, vn, q = inputs(Hq, Hkv, cap, ctx0, nq, 250 + ctx0)
+    qd = dev(q.view(np.int16))
+    length = torch.full((1,), ctx0, dtype=torch.int32, device="cuda") if on_device else None
+    base = 0 if on_device else ctx0
+    # one append of all nq tokens, then one exact launch
+    kv, sh = prefilled(ns, kf, vf, ctx0)
+    ns.kv_nest_append(kv, sh, dev(kn), dev(vn), base, pos_dev=length)
+    got = host(ns.kv_nest_attend_exact(qd, kv, sh, base + nq, view, ctx_dev=length))
+    # position by position: append token i, attend with query i
+    kv2, sh2 = prefilled(ns, kf, vf, ctx0)
+    ref = np.empty_like(got)
+    for i in range(nq):
+        ns.kv_nest_append(kv2, sh2, dev(kn[:, i:i + 1]), dev(vn[:, i:i + 1]), base + i, pos_dev=length)
+        ref[i] = host(ns.kv_nest_attend(qd[i:i + 1], kv2, base + i + 1, view, ctx_dev=length))[0]
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # the oracle, position by position
+    okv = oracle.kv_nest_pack(kf, vf)
+    ok, ov = kf.copy(), vf.copy()
+    for i in range(nq):
+        oracle.kv_append(okv, ok, ov, kn[:, i:i + 1], vn[:, i:i + 1], ctx0 + i)
+        o = oracle.kv_attend(np.ascontiguousarray(q[i:i + 1]), okv, ctx0 + i + 1, view)[0]
+        rel = np.linalg.norm(got[i] - o, axis=-1) / np.linalg.norm(o, axis=-1)
+        assert float(rel.max()) <= 2e-3, (i, float(rel.max()))
+
+
+def test_exact_at_32k_crossing_a_block(ns):
+    Hq, Hkv, nq = 28, 4, 5
+    ctx0 = 32768 - 2
+    cap = 32768 + 256
+    kf, vf, kn, vn, q = inputs(Hq, Hkv, cap, ctx0, nq, 260)
+    qd = dev(q.view(np.int16))
+    kv, sh = prefilled(ns, kf, vf, ctx0)
+    ns.kv_nest_append(kv, sh, dev(kn), dev(vn), ctx0)
+    got = host(ns.kv_nest_attend_exact(qd, kv, sh, ctx0 + nq, 1))
+    kv2, sh2 = prefilled(ns, kf, vf, ctx0)
+    for i in range(nq):
+        ns.kv_nest_append(kv2, sh2, dev(kn[:, i:i + 1]), dev(vn[:, i:i + 1]), ctx0 + i)
+        ref = host(ns.kv_nest_attend(qd[i:i + 1], kv2, ctx0 + i + 1, 1))[0]
+        assert np.array_equal(got[i].view(np.uint32), ref.view(np.uint32)), i

@@ -9,9 +9,11 @@ the large model alone").
     bf16 step.
   * Row independence: every glue kernel and linear gives a row the same bits
     alone as inside a batch of 5 (what makes the claim below exact).
-  * The claim: speculative rounds with position-by-position attention in the
-    target pass emit exactly the tokens of target-only decoding, and the
-    target logits of every emitted position are bit-identical.
+  * The claim: speculative rounds whose target pass attends exactly (one
+    kv_nest_attend_exact launch for the k+1 queries) emit exactly the tokens
+    of target-only decoding, and the target logits of every emitted
+    position are bit-identical; so do rounds that attend position by
+    position (k+1 launches).
   * Rounds chained on the device (committed length and next input kept by
     verify_accept, no host read between rounds) emit the same tokens and
     bit-identical logits as the host-driven loop, and as target-only
@@ -139,7 +141,7 @@ def test_rows_do_not_depend_on_the_batch(ns, gpu_dec):
 def test_speculative_rounds_emit_the_target_only_tokens(gpu_dec, k):
     prompt = synth.tokens(40, CFG["vocab"], (801,))
     ar, r_ar = gpu_dec.generate(prompt, 48, 0)
-    sp, r_sp = gpu_dec.generate(prompt, 48, k, exact=True)
+    sp, r_sp = gpu_dec.generate(prompt, 48, k, mode="exact")
     assert sp == ar
     y_ar = torch.cat([y for _, y in r_ar]).cpu().numpy()
     y_sp = torch.cat([y for _, y in r_sp]).cpu().numpy()[:len(y_ar)]
@@ -149,11 +151,24 @@ def test_speculative_rounds_emit_the_target_only_tokens(gpu_dec, k):
     assert tpr > 1.5
 
 
+@pytest.mark.parametrize("k", [1, 4])
+def test_one_pass_exact_equals_position_by_position(gpu_dec, k):
+    # the one-launch exact target pass and k+1 launches of one-token appends
+    # and attentions give the same bits
+    prompt = synth.tokens(40, CFG["vocab"], (801,))
+    a, ra = gpu_dec.run_rounds(prompt, 20, k, mode="exact")
+    b, rb = gpu_dec.run_rounds(prompt, 20, k, mode="stepwise")
+    assert a == b
+    ya = torch.cat([y for _, y in ra]).cpu().numpy()
+    yb = torch.cat([y for _, y in rb]).cpu().numpy()
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+
+
 def test_chained_rounds_match_the_host_loop(gpu_dec):
     prompt = synth.tokens(40, CFG["vocab"], (801,))
     for k in (0, 4):
-        toks, per = gpu_dec.run_rounds(prompt, 50, k, exact=True)
-        ref, per_ref = gpu_dec.generate(prompt, len(toks), k, exact=True)
+        toks, per = gpu_dec.run_rounds(prompt, 50, k)
+        ref, per_ref = gpu_dec.generate(prompt, len(toks), k)
         assert toks == ref
         assert [n for n, _ in per] == [n for n, _ in per_ref][:len(per)]
         y = torch.cat([y for _, y in per]).cpu().numpy()
@@ -165,8 +180,8 @@ def test_chained_rounds_match_the_host_loop(gpu_dec):
 def test_chained_decode_matches_the_oracle(gpu_dec, weights, D):
     prompt = synth.tokens(40, CFG["vocab"], (801,))
     k = 4
-    toks, per = gpu_dec.run_rounds(prompt, 50, k, exact=True)
-    ar, per_ar = gpu_dec.run_rounds(prompt, len(toks), 0, exact=True)
+    toks, per = gpu_dec.run_rounds(prompt, 50, k)
+    ar, per_ar = gpu_dec.run_rounds(prompt, len(toks), 0)
     assert toks == ar[:len(toks)]
     y_g = torch.cat([y for _, y in per]).cpu().numpy().astype(np.float64)
     seq = list(prompt) + toks
@@ -195,7 +210,7 @@ def test_batched_target_pass_is_measured(gpu_dec):
     prompt = synth.tokens(40, CFG["vocab"], (801,))
     ar, _ = gpu_dec.generate(prompt, 48, 0)
     for k in (1, 4):
-        sp, r = gpu_dec.generate(prompt, 48, k, exact=False)
+        sp, r = gpu_dec.generate(prompt, 48, k, mode="batched")
         first = next((i for i, (a, b) in enumerate(zip(sp, ar)) if a != b), None)
         print(f"batched k={k}: {np.mean([n for n, _ in r]):.3f} tokens/round, first divergence {first}")
         # each round emits its own target choices: the argmax of the pass's

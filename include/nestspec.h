@@ -587,10 +587,11 @@ double nest_alpha_value(const nest_alpha* st);
  * --------------------------------------------------------------------------- */
 
 /* nest_read_stream -- read `bytes` of device memory once as a plain stream
- * (16-byte nontemporal loads, as the weight and cache streams use), folding
- * them into one word xored into *sink. Its rate is what a kernel that reads
- * each byte once can reach on the device: the "achievable" bandwidth the
- * kernels' roofline fractions are also quoted against.
+ * (16-byte nontemporal loads, as the weight and cache streams use). *sink
+ * is written only if a thread's folded word equals a fixed constant, which
+ * keeps the loads live without contended writes. Its rate is what a kernel
+ * that reads each byte once can reach on the device: the "achievable"
+ * bandwidth the kernels' roofline fractions are also quoted against.
  *   src   device, 16-byte aligned;  bytes  a positive multiple of 16
  *   sink  uint32 (device)
  * Errors: NEST_EINVAL, NEST_ESHAPE, NEST_EALIGN, NEST_EHIP. */

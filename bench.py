@@ -243,7 +243,8 @@ class Round:
         ws_g = torch.zeros(ws_g_n, dtype=torch.uint8, device=cuda)
         plan_len = CAPACITY if chained else CONTEXT + k + 1
         ws_att_n = max(L.kv_nest_attend_workspace_size(1, hq, hkv, 128, plan_len),
-                       L.kv_nest_attend_workspace_size(k + 1, hq, hkv, 128, plan_len))
+                       L.kv_nest_attend_workspace_size(k + 1, hq, hkv, 128, plan_len),
+                       L.kv_nest_attend_exact_workspace_size(k + 1, hq, hkv, 128, plan_len))
         ws_att = E(ws_att_n, dtype=torch.uint8, device=cuda)
         length = torch.full((1,), CONTEXT, dtype=torch.int32, device=cuda)
         keep += [y, att_out, draft_tok, acc_out, ws_g, ws_att, length]

@@ -436,8 +436,13 @@ int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
  * append leaves every token of the (at most two) blocks they touch in the
  * shadows and seals a block they fill.
  *   shadow_k, shadow_v  the kv_nest_append shadows of this cache
- *   the rest as for kv_nest_attend; the workspace of kv_nest_attend with
- *   the same arguments is enough.
+ *   ws       kv_nest_attend_exact_workspace_size(nq, Hq, Hkv, d, L) bytes
+ *            (L as for kv_nest_attend): the chunk partials, then one
+ *            rebuilt open block (both planes of K and V, 32 KB) and its two
+ *            scales per (query, kv head); no zero-fill needed
+ *   the rest as for kv_nest_attend.
+ * Two kernels and the merge run: the first rebuilds every query's open
+ * block into the workspace, the second attends.
  * Requires Hq/Hkv <= 16 and nq <= block. Errors: as kv_nest_attend. */
 int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,
                          const nest_kv* kv, const float* shadow_k,
@@ -448,6 +453,10 @@ int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,
 size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
                                      int64_t n_kv_heads, int64_t head_dim,
                                      int64_t ctx_len);
+/* Bytes of kv_nest_attend_exact's workspace; 0 for an unsupported shape. */
+size_t kv_nest_attend_exact_workspace_size(int64_t nq, int64_t n_q_heads,
+                                           int64_t n_kv_heads,
+                                           int64_t head_dim, int64_t ctx_len);
 
 /* ---------------------------------------------------------------------------
  * Speculative sampling ("How Speculative Decoding Speeds Up Inference",

@@ -63,6 +63,8 @@ struct AttArgs {
   const float *ks, *vs;
   int cap, nb;         // capacity and blocks per head in the planes
   const float *shk, *shv;  // exact mode: fp32 shadows [Hkv][2][block][d] of the two newest blocks
+  uint8_t* open;           // exact mode: [nq][Hkv] rebuilt open blocks, 4 planes each
+  float* open_sc;          // exact mode: [nq][Hkv][2] their scales (K, V)
   int bpw, nchunk;     // blocks per workgroup, chunks (workgroups) per head
   float* part_ml;      // [Hkv][nchunk][R][2]  (max in log2 domain, sum)
   float* part_o;       // [Hkv][nchunk][R][128]
@@ -431,73 +433,77 @@ __global__ void __launch_bounds__(256) attend_kernel(AttArgs a) {
   }
 }
 
-// Exact mode (kv_nest_attend_exact): the block holding query position pos,
-// rebuilt from its fp32 values in the shadow and quantized over its tokens
-// up to pos alone, with the rule and the layouts kv_nest_append uses, so
-// the codes and scales are those a one-token append at pos would have
-// written. Planes go to LDS (K [token][64 B], V [dim][64 B], base then
-// refine), the scales to osc[0] (K) and osc[1] (V). All 256 threads take
-// part; ends with a barrier.
+// Exact mode (kv_nest_attend_exact), first kernel: for every query z of the
+// pass and kv head h, the block holding the query's position, rebuilt from
+// its fp32 values in the shadow and quantized over its tokens up to that
+// position alone, with the rule and the layouts kv_nest_append uses: the
+// codes and scales a one-token append at that position would have
+// written. Each goes to its own slot of the workspace, laid out as a block
+// of the planes (K base, K refine: [token][64 B]; V base, V refine:
+// [dim][64 B]), and its two scales (K, V) to open_sc.
+//
+// Grid (kOpenSplit, Hkv, 2 nq): workgroup (part, h, 2z + is_v) reduces the
+// plane's max |x| over the valid tokens (every part reads the whole valid
+// region, from L2 after the first) and writes part's eighth of the codes,
+// one 32-bit word of each plane per thread (8 elements, element 2m in the
+// low nibble of byte m).
 constexpr int kOpenPlane = kBlk * kD / 2;  // bytes of one plane of one block
+constexpr int kOpenSplit = 8;              // workgroups per (query, kv head, K or V)
+static_assert(kOpenSplit * 256 * 8 == kBlk * kD, "one word of each plane per thread");
 
-// One plane pair of the open block. Thread t holds 64 values: K elements
-// 64t .. 64t + 63 (token t/2, half of its dims: 32 bytes of each K plane),
-// or V dim t/2 over tokens 64(t&1) .. + 63 (32 bytes of each dim-major V
-// plane). All loads are issued at once (values past the valid tokens are
-// taken as 0), so each plane pair waits for one round trip.
-template <bool IS_V>
-__device__ __forceinline__ void quantize_open_plane(const float* src, int valid, uint8_t* pb, uint8_t* pr,
-                                                    float* osc, float* red) {
-  const int t = threadIdx.x, row = t >> 1, c0 = 64 * (t & 1);
-  float x[64];
-  if (IS_V) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = src[(c0 + i) * kD + row];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4 v = reinterpret_cast<const float4*>(src + row * kD + c0)[i];
-      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-    }
-  }
+__global__ void __launch_bounds__(256) open_block_kernel(AttArgs a) {
+  __shared__ float red[4];
+  const int part = blockIdx.x, h = blockIdx.y, z = blockIdx.z >> 1;
+  const bool is_v = (blockIdx.z & 1) != 0;
+  const int Hkv = a.Hq / a.grp;
+  const int pos = live_ctx(a) - a.nq + z;
+  const int blk = pos / kBlk, valid = pos - blk * kBlk + 1;
+  const float* src = (is_v ? a.shv : a.shk) + (static_cast<size_t>(h) * 2 + (blk & 1)) * kBlk * kD;
+  // 1. max |x| over tokens [0, valid) (token-major, contiguous); all loads
+  // are issued together
+  const int n4 = valid * (kD / 4);
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    if ((IS_V ? c0 + i : row) >= valid) x[i] = 0.0f;
-    m = fmaxf(m, fabsf(x[i]));
+  for (int u = 0; u < kBlk * kD / 4 / 256; ++u) {
+    const int i = static_cast<int>(threadIdx.x) + 256 * u;
+    if (i < n4) {
+      const float4 v = reinterpret_cast<const float4*>(src)[i];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
   }
   m = wave_max(m);
-  if ((t & 63) == 0) red[t >> 6] = m;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = m / 7.0f, s16 = s * 0.0625f, r = 1.0f / s, r16 = 1.0f / s16;
-  if (t == 0) osc[IS_V ? 1 : 0] = s;
-  // element pair (2m, 2m+1) -> one byte of each plane (low nibble first),
-  // as kv_nest_append writes them
-  uint32_t* b32 = reinterpret_cast<uint32_t*>(pb + row * 64 + c0 / 2);
-  uint32_t* r32 = reinterpret_cast<uint32_t*>(pr + row * 64 + c0 / 2);
+  const float s = m / 7.0f, s16 = s * 0.0625f, rs = 1.0f / s, rs16 = 1.0f / s16;
+  const size_t slot = static_cast<size_t>(z) * Hkv + h;
+  if (part == 0 && threadIdx.x == 0) a.open_sc[slot * 2 + (is_v ? 1 : 0)] = s;
+  // 2. word w of each plane: elements 8w .. 8w + 7 in plane order (K: token
+  // 8w / 128, dims 8w % 128 ..; V: dim 8w / 128, tokens 8w % 128 ..)
+  const int w = part * 256 + static_cast<int>(threadIdx.x);
+  const int row = (8 * w) / kD, c0 = (8 * w) % kD;
+  float x[8];
+  if (is_v) {
 #pragma unroll
-  for (int i = 0; i < 64; i += 8) {
-    uint32_t wb = 0, wr = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int qb, qr;
-      nest::nest_codes_fast(x[i + j], s, s16, r, r16, qb, qr);
-      wb |= static_cast<uint32_t>(qb & 15) << (4 * j);
-      wr |= static_cast<uint32_t>(qr & 15) << (4 * j);
-    }
-    b32[i / 8] = wb;
-    r32[i / 8] = wr;
+    for (int j = 0; j < 8; ++j) x[j] = c0 + j < valid ? src[(c0 + j) * kD + row] : 0.0f;
+  } else {
+    const float4 lo = reinterpret_cast<const float4*>(src + row * kD + c0)[0];
+    const float4 hi = reinterpret_cast<const float4*>(src + row * kD + c0)[1];
+    const bool in = row < valid;
+    x[0] = in ? lo.x : 0.0f; x[1] = in ? lo.y : 0.0f; x[2] = in ? lo.z : 0.0f; x[3] = in ? lo.w : 0.0f;
+    x[4] = in ? hi.x : 0.0f; x[5] = in ? hi.y : 0.0f; x[6] = in ? hi.z : 0.0f; x[7] = in ? hi.w : 0.0f;
   }
-  __syncthreads();  // red is reused by the next plane pair
-}
-
-__device__ void quantize_open_block(const AttArgs& a, int h, int blk, int pos, uint8_t* ob, float* osc,
-                                    float* red) {
-  const int valid = pos - blk * kBlk + 1;
-  const size_t off = (static_cast<size_t>(h) * 2 + (blk & 1)) * kBlk * kD;
-  quantize_open_plane<false>(a.shk + off, valid, ob, ob + kOpenPlane, osc, red);
-  quantize_open_plane<true>(a.shv + off, valid, ob + 2 * kOpenPlane, ob + 3 * kOpenPlane, osc, red);
+  uint32_t wb = 0, wr = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int qb, qr;
+    nest::nest_codes_fast(x[j], s, s16, rs, rs16, qb, qr);
+    wb |= static_cast<uint32_t>(qb & 15) << (4 * j);
+    wr |= static_cast<uint32_t>(qr & 15) << (4 * j);
+  }
+  uint8_t* base = a.open + (slot * 4 + (is_v ? 2 : 0)) * kOpenPlane;
+  reinterpret_cast<uint32_t*>(base)[w] = wb;
+  reinterpret_cast<uint32_t*>(base + kOpenPlane)[w] = wr;
 }
 
 // Few query rows (R <= 16, e.g. one draft query over a GQA group): every
@@ -517,22 +523,17 @@ __device__ void quantize_open_block(const AttArgs& a, int h, int blk, int pos, u
 // the one-query call at its own position would compute it, in one launch.
 // A workgroup serves one (chunk, kv head, query); its rows are that
 // query's GQA group, its visible blocks end at the query's position, and
-// the block holding that position is rebuilt by quantize_open_block (the
-// others are read from the planes). The per-row arithmetic, the split into
-// chunks and the merge are those of the one-query call, so the outputs are
-// bit-identical to it. Workgroups are numbered so that the queries of one
-// (chunk, head) run one after another on one XCD and share its L2.
+// the block holding that position is read from the query's slot that
+// open_block_kernel wrote (the others from the planes, same layout). The
+// per-row arithmetic, the split into chunks and the merge are those of the
+// one-query call, so the outputs are bit-identical to it. Workgroups are
+// numbered so that the queries of one (chunk, head) run one after another
+// on one XCD and share its L2.
 template <int VIEW, bool EXACT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 attend_wave_kernel(AttArgs a) {
   __shared__ float ml[4][16][2];
   __shared__ __align__(16) float buf[4][16][kD + 4];  // each wave's rescaled O
-  // exact mode: the rebuilt open block's planes share buf's space (read
-  // only in the block loop; buf is written after the barrier that follows
-  // every wave's loop)
-  static_assert(sizeof(buf) >= 4 * kOpenPlane, "open block planes fit in buf");
-  uint8_t* ob = reinterpret_cast<uint8_t*>(&buf[0][0][0]);
-  __shared__ float osc[2], ored[8];
   // the wave index is uniform: block numbers, scale loads and branches on
   // them stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -559,46 +560,47 @@ attend_wave_kernel(AttArgs a) {
   const int b_first = chunk * a.bpw;
   const int b_last = min(b_first + a.bpw, nbv);
   const int b0 = b_first + wave;  // the wave's blocks are b0, b0 + 4, ...
-  if (EXACT && b_open >= b_first && b_open < b_last) quantize_open_block(a, h, b_open, pos_z, ob, osc, ored);
 
   uint4 kb[8], kr[8], vb[8], vr[8];
   float ks, vs;
   // K codes first, then V: loads return in issue order, so the scores and
   // the softmax of a block start while its V codes are still on the way
   auto load = [&](int blk) {
-    if (EXACT && blk == b_open) {  // the rebuilt open block, from LDS
-      ks = osc[0];
-      vs = osc[1];
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
-        kb[tt] = ld16(ob + tok * (kD / 2) + 16 * q4);
-        kr[tt] = VIEW ? ld16(ob + kOpenPlane + tok * (kD / 2) + 16 * q4) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int o = (tt * 16 + c16) * (kBlk / 2) + 16 * q4;
-        vb[tt] = ld16(ob + 2 * kOpenPlane + o);
-        vr[tt] = VIEW ? ld16(ob + 3 * kOpenPlane + o) : make_uint4(0, 0, 0, 0);
-      }
-      return;
+    // the block's four planes (K [token][64 B], V [dim][64 B]) and scales:
+    // from the cache, or, for the query's open block in exact mode, from its
+    // rebuilt slot (the same layout)
+    const uint8_t *pkb, *pkr, *pvb, *pvr;
+    if (EXACT && blk == b_open) {
+      const size_t slot = static_cast<size_t>(z) * (a.Hq / a.grp) + h;
+      pkb = a.open + slot * 4 * kOpenPlane;
+      pkr = pkb + kOpenPlane;
+      pvb = pkb + 2 * kOpenPlane;
+      pvr = pkb + 3 * kOpenPlane;
+      ks = a.open_sc[slot * 2];
+      vs = a.open_sc[slot * 2 + 1];
+    } else {
+      const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+      const size_t kblk = (static_cast<size_t>(h) * a.cap + static_cast<size_t>(blk) * kBlk) * (kD / 2);
+      pkb = a.kb + kblk;
+      pkr = a.kr + kblk;
+      pvb = a.vb + hb * kD * (kBlk / 2);
+      pvr = a.vr + hb * kD * (kBlk / 2);
+      ks = a.ks[hb];
+      vs = a.vs[hb];
     }
-    const size_t hb = static_cast<size_t>(h) * a.nb + blk;
-    ks = a.ks[hb];
-    vs = a.vs[hb];
     auto ld = [](const uint8_t* p) { return nest::ldnt16(p); };
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int tok = 32 * (c16 >> 2) + 8 * (tt >> 1) + 4 * (tt & 1) + (c16 & 3);
-      const size_t koff = (static_cast<size_t>(h) * a.cap + blk * kBlk + tok) * (kD / 2) + 16 * q4;
-      kb[tt] = ld(a.kb + koff);
-      kr[tt] = VIEW ? ld(a.kr + koff) : make_uint4(0, 0, 0, 0);
+      const int koff = tok * (kD / 2) + 16 * q4;
+      kb[tt] = ld(pkb + koff);
+      kr[tt] = VIEW ? ld(pkr + koff) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const size_t voff = (hb * kD + tt * 16 + c16) * (kBlk / 2) + 16 * q4;
-      vb[tt] = ld(a.vb + voff);
-      vr[tt] = VIEW ? ld(a.vr + voff) : make_uint4(0, 0, 0, 0);
+      const int voff = (tt * 16 + c16) * (kBlk / 2) + 16 * q4;
+      vb[tt] = ld(pvb + voff);
+      vr[tt] = VIEW ? ld(pvr + voff) : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -929,12 +931,41 @@ int launch_att(const AttArgs& a, const Plan& p, int Hkv, hipStream_t st) {
   return nest::check_launch("kv_nest_attend(combine)");
 }
 
+// Exact mode's workspace: the partials of nq queries (R = nq * grp rows)
+// under the one-query split, then, from a 256-byte boundary, the rebuilt
+// open blocks [nq][Hkv][4 planes] and their scales [nq][Hkv][2].
+struct ExactLayout {
+  Plan p;
+  size_t open_off, sc_off, bytes;
+};
+
+ExactLayout exact_layout(int64_t nq, int64_t Hq, int64_t Hkv, int64_t plan_len) {
+  ExactLayout e{};
+  e.p = make_plan(1, Hq, Hkv, plan_len);
+  const size_t rows = static_cast<size_t>(Hkv) * e.p.nchunk * nq * (Hq / Hkv);
+  const size_t part = (((rows * 2 + 3) & ~static_cast<size_t>(3)) + rows * kD) * sizeof(float);
+  const size_t slots = static_cast<size_t>(nq) * Hkv;
+  e.open_off = (part + 255) & ~static_cast<size_t>(255);
+  e.sc_off = e.open_off + slots * 4 * kOpenPlane;
+  e.bytes = e.sc_off + slots * 2 * sizeof(float);
+  return e;
+}
+
 }  // namespace
 
 extern "C" size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads, int64_t n_kv_heads,
                                                 int64_t head_dim, int64_t ctx_len) {
   if (nq < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || head_dim != kD || ctx_len < 1) return 0;
   return make_plan(nq, n_q_heads, n_kv_heads, ctx_len).ws;
+}
+
+extern "C" size_t kv_nest_attend_exact_workspace_size(int64_t nq, int64_t n_q_heads, int64_t n_kv_heads,
+                                                      int64_t head_dim, int64_t ctx_len) {
+  if (nq < 1 || nq > kBlk || n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads ||
+      head_dim != kD || ctx_len < 1)
+    return 0;
+  if (nq == 1) return make_plan(1, n_q_heads, n_kv_heads, ctx_len).ws;
+  return exact_layout(nq, n_q_heads, n_kv_heads, ctx_len).bytes;
 }
 
 namespace {
@@ -1034,15 +1065,20 @@ extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_h
     return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);
   }
   // every query takes the split of a one-query call (its workgroups write
-  // rows z * grp .. of the partials)
-  const Plan p = make_plan(1, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
-  const size_t rows = static_cast<size_t>(Hkv) * p.nchunk * a.R;
-  const size_t need = (((rows * 2 + 3) & ~static_cast<size_t>(3)) + rows * kD) * sizeof(float);
-  rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, need);
+  // rows z * grp .. of the partials); first the open blocks, one slot per
+  // (query, kv head)
+  const ExactLayout e = exact_layout(nq, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
+  const Plan& p = e.p;
+  rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, e.bytes);
+  if (rc) return rc;
+  a.open = static_cast<uint8_t*>(ws) + e.open_off;
+  a.open_sc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + e.sc_off);
+  hipStream_t st = nest::as_stream(stream);
+  open_block_kernel<<<dim3(kOpenSplit, static_cast<unsigned>(Hkv), static_cast<unsigned>(2 * nq)), 256, 0, st>>>(a);
+  rc = nest::check_launch("kv_nest_attend_exact(open blocks)");
   if (rc) return rc;
   const int64_t items = static_cast<int64_t>(p.nchunk) * Hkv * nq;
   const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
-  hipStream_t st = nest::as_stream(stream);
   if (view == 0)
     attend_wave_kernel<0, true><<<grid, 256, 0, st>>>(a);
   else

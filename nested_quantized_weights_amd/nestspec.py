@@ -81,6 +81,7 @@ _SIGS = {
     "kv_nest_attend": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _i64, ctypes.c_int, _p,
                                       _p, _sz, _p]),
     "kv_nest_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "kv_nest_attend_exact_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "kv_nest_attend_exact": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _p, _p, _i64, ctypes.c_int,
                                             _p, _p, _sz, _p]),
     "nest_sample": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_float, _p, _p, _p, _sz, _p]),
@@ -513,7 +514,7 @@ def kv_nest_attend_exact(q: torch.Tensor, kv: NestKV, shadow, ctx_len: int, view
     if out is None:
         out = torch.empty((nq, Hq, d), dtype=torch.float32, device=dev)
     plan_len = kv.capacity if ctx_dev is not None else int(ctx_len)
-    wsn = lib().kv_nest_attend_workspace_size(nq, Hq, kv.n_kv_heads, d, plan_len)
+    wsn = lib().kv_nest_attend_exact_workspace_size(nq, Hq, kv.n_kv_heads, d, plan_len)
     if ws is None or ws.numel() < wsn:
         ws = workspace(max(wsn, 256), dev, "attend")
     s = kv.struct()

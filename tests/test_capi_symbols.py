@@ -108,6 +108,14 @@ def test_attend_host_validation_without_a_gpu(lib):
     assert 0 < small < full
     assert f(p, 1, 32, ctypes.byref(kv), p, 0, 0, p, p, small, None) == 4
     assert f(p, 1, 32, ctypes.byref(kv), p, -1, 0, p, p, full, None) == 1  # negative offset
+    # the exact entry's workspace adds one rebuilt open block (32 KB) and
+    # two scales per (query, kv head) to the partials of the one-query split
+    ex = lib.kv_nest_attend_exact_workspace_size
+    ex.restype = ctypes.c_size_t
+    ex.argtypes = [ctypes.c_int64] * 5
+    assert ex(1, 32, 8, 128, 32768) == full
+    assert ex(5, 32, 8, 128, 32768) >= 5 * full + 5 * 8 * (32768 + 8)
+    assert ex(129, 32, 8, 128, 32768) == 0 and ex(5, 30, 8, 128, 32768) == 0
 
 
 def test_workspaces_are_checked_without_a_gpu(lib):

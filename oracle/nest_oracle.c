@@ -263,11 +263,12 @@ int64_t oracle_argmax(const float* y, int64_t n) {
   return best;
 }
 
-/* One round [Blog, "Drafting and checking tokens"]. Matching draft tokens
- * are kept from the start. At the first mismatch the target's token
- * replaces the draft and the rest is discarded. If every draft matches,
- * the target's choice after the last draft is added as well, so a pass
- * yields between 1 and k+1 tokens ([Blog] ibid.; [SpecKV] tokens = k+1).
+/* One round [Blog, "Drafting and checking tokens"]. The drafts are walked
+ * in order while each equals the target's choice for its slot; the first
+ * one that differs gives way to the target's choice, and nothing after it
+ * survives. When none differs, one more token, the target's choice after
+ * the last draft, follows, so a round emits 1 to k+1 tokens ([Blog]
+ * ibid.; [SpecKV] tokens = k+1).
  * draft[i-1] is d_i and target[i] is t_i, the target's choice after slot
  * i. d_i is checked against t_{i-1}. Writes t_0..t_a to emitted, -1
  * after them, and returns a+1. */

@@ -72,7 +72,8 @@ def test_choice_limits_and_monotonicity(oracle):
     assert oracle.choose_k(1.0, 0.5, t_pass) == kmax  # always accepted, drafting cheaper than a pass
     ks = [oracle.choose_k(a, 0.05, t_pass) for a in np.linspace(0, 0.99, 50)]
     assert all(a <= b for a, b in zip(ks, ks[1:]))
-    # "Longer drafts pay off only when the draft is usually right"
+    # long drafts are worth it only at a high acceptance rate (blog, "Tokens per
+    # pass and time per token")
     assert oracle.choose_k(0.5, 0.05, t_pass) <= 4 < 8 <= oracle.choose_k(0.9, 0.05, t_pass)
     # a pass that grows with k moves the choice down
     growing = 1.0 + 0.05 * np.arange(kmax + 1)

@@ -113,12 +113,15 @@ __device__ __forceinline__ void build_ops(const WLoad (&w)[kRT], WOps& o) {
 }
 
 // LDS slot of one group: per column tile ct, 16 rows of 128 bytes, the
-// 16-byte piece q of row r stored at position q ^ ((r >> 1) & 7) of that
-// row. A copy instruction then reads eight whole rows (full cache lines),
-// and a 16-lane read of one piece from rows 0..15 covers each of the 64
-// four-byte banks once (rows of one parity share half the banks; the
-// swizzle spreads the eight of each parity over that half).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// 16-byte piece q of row r stored at position q ^ swz(r) of that row, with
+// swz(r) = (r & 7) ^ (r >> 3). A copy instruction then reads eight whole
+// rows (full cache lines). A ds_read_b128 is served eight lanes at a time
+// over 128 bytes of banks; lanes 0..7 (and 8..15) read one piece from eight
+// consecutive rows, and swz gives those rows eight different positions, so
+// no read has a bank conflict (measured: SQ_LDS_BANK_CONFLICT 0, against
+// 3.7 cycles per read with the swizzle (r >> 1) & 7, which assumed
+// 16-lane phases over 256 bytes).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int act_lds_off(int ct, int r, int q) { return ct * 2048 + r * 128 + ((q ^ swz(r)) << 4); }
 
 // One group for the wave's weight tile(s) and the block's CTP column tiles:

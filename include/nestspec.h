@@ -443,7 +443,8 @@ int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
  *   the rest as for kv_nest_attend.
  * Two kernels and the merge run: the first rebuilds every query's open
  * block into the workspace, the second attends.
- * Requires Hq/Hkv <= 16 and nq <= block. Errors: as kv_nest_attend. */
+ * Requires Hq/Hkv <= 16 and nq <= block; nq*(Hq/Hkv) may exceed
+ * kv_nest_attend's 64. Errors: as kv_nest_attend. */
 int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,
                          const nest_kv* kv, const float* shadow_k,
                          const float* shadow_v, const int32_t* ctx_dev,

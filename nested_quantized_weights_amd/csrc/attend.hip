@@ -971,9 +971,12 @@ extern "C" size_t kv_nest_attend_exact_workspace_size(int64_t nq, int64_t n_q_he
 namespace {
 
 // Host checks shared by both attention entry points; fills the kernel
-// arguments except the plan-dependent ones.
+// arguments except the plan-dependent ones. max_rows bounds nq * (Hq/Hkv):
+// 64 for kv_nest_attend (the LDS-table kernel's four row tiles); the exact
+// pass attends one query's GQA group per workgroup and has no such bound.
 int prepare_attend(const char* what, const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
-                   const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, AttArgs& a) {
+                   const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, int64_t max_rows,
+                   AttArgs& a) {
   if (!q || !kv || !out) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
   if (!kv->k_base || !kv->v_base || !kv->k_scale || !kv->v_scale)
     return nest::fail(NEST_EINVAL, "%s: null cache pointer", what);
@@ -992,7 +995,8 @@ int prepare_attend(const char* what, const uint16_t* q, int64_t nq, int64_t n_q_
     return nest::fail(NEST_EINVAL, "%s: need nq <= ctx_len <= capacity (ctx_len=%lld)", what,
                       (long long)ctx_len);
   const int64_t R = nq * (n_q_heads / Hkv);
-  if (R > 64) return nest::fail(NEST_EUNSUPPORTED, "%s: nq*(Hq/Hkv)=%lld > 64", what, (long long)R);
+  if (R > max_rows)
+    return nest::fail(NEST_EUNSUPPORTED, "%s: nq*(Hq/Hkv)=%lld > %lld", what, (long long)R, (long long)max_rows);
   if (kv->capacity > (1LL << 30) || Hkv > 65535)
     return nest::fail(NEST_EUNSUPPORTED, "%s: cache too large", what);
   if (!nest::aligned16(kv->k_base) || !nest::aligned16(kv->v_base) ||
@@ -1029,7 +1033,7 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
                               size_t ws_bytes, void* stream) {
   const char* what = "kv_nest_attend";
   AttArgs a;
-  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, a);
+  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, 64, a);
   if (rc) return rc;
   const int64_t Hkv = kv->n_kv_heads;
   // with the length on the device, the grid covers the whole capacity and
@@ -1047,7 +1051,7 @@ extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_h
                                     void* stream) {
   const char* what = "kv_nest_attend_exact";
   AttArgs a;
-  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, a);
+  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, kBlk * 16, a);
   if (rc) return rc;
   if (!shadow_k || !shadow_v) return nest::fail(NEST_EINVAL, "%s: null shadow", what);
   if (a.grp > 16) return nest::fail(NEST_EUNSUPPORTED, "%s: Hq/Hkv=%d > 16", what, a.grp);

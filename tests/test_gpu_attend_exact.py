@@ -55,8 +55,11 @@ def inputs(Hq, Hkv, cap, ctx0, nq, key):
     return kf, vf, kn, vn, q
 
 
+# (Hq, Hkv, capacity, ctx0, nq); the last two: one query (the entry point's
+# one-query path) and 9 queries of a GQA group of 8 (72 rows, more than
+# kv_nest_attend's 64)
 CASES = [(28, 4, 1024, 300, 5), (8, 2, 512, 126, 5), (32, 8, 384, 250, 9), (4, 1, 256, 0, 3),
-         (16, 16, 640, 511, 2), (28, 4, 512, 123, 9)]
+         (16, 16, 640, 511, 2), (28, 4, 512, 123, 9), (28, 4, 512, 200, 1), (64, 8, 512, 380, 9)]
 
 
 @pytest.mark.parametrize("view", [0, 1])

@@ -597,7 +597,8 @@ double nest_alpha_value(const nest_alpha* st);
  * --------------------------------------------------------------------------- */
 
 /* nest_read_stream -- read `bytes` of device memory once as a plain stream
- * (16-byte nontemporal loads, as the weight and cache streams use). *sink
+ * (16-byte nontemporal loads, as the weight and cache streams use; each
+ * wave reads whole 16 KB chunks, the fastest pattern measured). *sink
  * is written only if a thread's folded word equals a fixed constant, which
  * keeps the loads live without contended writes. Its rate is what a kernel
  * that reads each byte once can reach on the device: the "achievable"

@@ -65,6 +65,7 @@ struct AttArgs {
   const float *shk, *shv;  // exact mode: fp32 shadows [Hkv][2][block][d] of the two newest blocks
   uint8_t* open;           // exact mode: [nq][Hkv] rebuilt open blocks, 4 planes each
   float* open_sc;          // exact mode: [nq][Hkv][2] their scales (K, V)
+  int qpack;               // exact mode: queries per workgroup (qpack * grp <= 16)
   int bpw, nchunk;     // blocks per workgroup, chunks (workgroups) per head
   float* part_ml;      // [Hkv][nchunk][R][2]  (max in log2 domain, sum)
   float* part_o;       // [Hkv][nchunk][R][128]
@@ -521,14 +522,22 @@ __global__ void __launch_bounds__(256) open_block_kernel(AttArgs a) {
 //
 // EXACT (kv_nest_attend_exact): each query of a verify pass is computed as
 // the one-query call at its own position would compute it, in one launch.
-// A workgroup serves one (chunk, kv head, query); its rows are that
-// query's GQA group, its visible blocks end at the query's position, and
-// the block holding that position is read from the query's slot that
-// open_block_kernel wrote (the others from the planes, same layout). The
-// per-row arithmetic, the split into chunks and the merge are those of the
-// one-query call, so the outputs are bit-identical to it. Workgroups are
-// numbered so that the queries of one (chunk, head) run one after another
-// on one XCD and share its L2.
+// A workgroup serves one (chunk, kv head, group of qpack consecutive
+// queries); its rows are those queries' GQA groups side by side (query
+// z_lo + r / grp, head r % grp in row r; qpack * grp <= 16). A block that
+// comes before every row's own block is processed once for all rows from
+// the planes. A block that holds some rows' positions is processed once
+// from the planes for the rows it is sealed for (their position lies in a
+// later block), then once per query it holds, from that query's slot (the
+// open block open_block_kernel rebuilt), each time with every other row
+// masked. Every row therefore sees exactly the blocks, codes and order of
+// the one-query call at its position, with the same split into chunks and
+// the same merge; a call in which a row is masked leaves its running
+// maximum, sum and output unchanged (or, as the wave's first call, at the
+// state of an empty wave, from which the next call yields what a first
+// call would), so the outputs are bit-identical to the one-query call.
+// Workgroups are numbered so that the query groups of one (chunk, head)
+// run one after another on one XCD and share its L2.
 template <int VIEW, bool EXACT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 attend_wave_kernel(AttArgs a) {
@@ -538,24 +547,29 @@ attend_wave_kernel(AttArgs a) {
   // them stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c16 = lane & 15;
-  int h = blockIdx.y, chunk = blockIdx.x, z = 0;
+  int h = blockIdx.y, chunk = blockIdx.x, z_lo = 0, nz = 1;
   if (EXACT) {
-    // item = (chunk, head, query) with the query fastest; XCD x (= block id
-    // mod 8) takes the contiguous items [x * per, (x + 1) * per), so the
-    // queries of one (chunk, head) run together on one XCD and share its L2
-    const int n_items = a.nchunk * (a.Hq / a.grp) * a.nq;
+    // item = (chunk, head, query group) with the group fastest; XCD x (=
+    // block id mod 8) takes the contiguous items [x * per, (x + 1) * per),
+    // so the groups of one (chunk, head) run together on one XCD and share
+    // its L2
+    const int ngrp = (a.nq + a.qpack - 1) / a.qpack;
+    const int n_items = a.nchunk * (a.Hq / a.grp) * ngrp;
     const int per = (n_items + 7) / 8;
     const int item = (static_cast<int>(blockIdx.x) & 7) * per + (static_cast<int>(blockIdx.x) >> 3);
     if (item >= n_items) return;
-    z = item % a.nq;
-    chunk = (item / a.nq) % a.nchunk;
-    h = item / a.nq / a.nchunk;
+    z_lo = (item % ngrp) * a.qpack;
+    nz = min(a.qpack, a.nq - z_lo);
+    chunk = (item / ngrp) % a.nchunk;
+    h = item / ngrp / a.nchunk;
   }
   const int ctx = live_ctx(a);
-  // exact: this query's position and the blocks it sees
-  const int pos_z = ctx - a.nq + z;
-  const int nbv = EXACT ? pos_z / kBlk + 1 : (ctx + kBlk - 1) / kBlk;
-  const int b_open = EXACT ? pos_z / kBlk : -1;
+  // exact: the group's first and last positions and the blocks holding them
+  // (the group sees blocks up to the last one)
+  const int pos_lo = ctx - a.nq + z_lo;
+  const int b_open_lo = EXACT ? pos_lo / kBlk : -1;
+  const int b_open_hi = EXACT ? (pos_lo + nz - 1) / kBlk : -1;
+  const int nbv = EXACT ? b_open_hi + 1 : (ctx + kBlk - 1) / kBlk;
 
   const int b_first = chunk * a.bpw;
   const int b_last = min(b_first + a.bpw, nbv);
@@ -565,13 +579,13 @@ attend_wave_kernel(AttArgs a) {
   float ks, vs;
   // K codes first, then V: loads return in issue order, so the scores and
   // the softmax of a block start while its V codes are still on the way
-  auto load = [&](int blk) {
+  auto load = [&](int blk, int zs) {
     // the block's four planes (K [token][64 B], V [dim][64 B]) and scales:
-    // from the cache, or, for the query's open block in exact mode, from its
-    // rebuilt slot (the same layout)
+    // from the cache, or, in exact mode with zs >= 0, query zs's rebuilt
+    // open block (the same layout)
     const uint8_t *pkb, *pkr, *pvb, *pvr;
-    if (EXACT && blk == b_open) {
-      const size_t slot = static_cast<size_t>(z) * (a.Hq / a.grp) + h;
+    if (EXACT && zs >= 0) {
+      const size_t slot = static_cast<size_t>(zs) * (a.Hq / a.grp) + h;
       pkb = a.open + slot * 4 * kOpenPlane;
       pkr = pkb + kOpenPlane;
       pvb = pkb + 2 * kOpenPlane;
@@ -608,11 +622,13 @@ attend_wave_kernel(AttArgs a) {
   // the first block's codes are requested together; the query operand and
   // the bias product are formed while the codes are on the way.
   uint4 qraw[4];
-  int pos = -1;
-  // rows of this workgroup: its query's GQA group (exact), or all R rows
-  const int nrow = EXACT ? a.grp : a.R;
+  int pos = -1, zr = -1;
+  // rows of this workgroup: its query group's GQA groups (exact), or all R
+  // rows; row c16 is query c16 / grp (of the group) and head c16 % grp
+  const int nrow = EXACT ? nz * a.grp : a.R;
   if (c16 < nrow) {
-    const int i = EXACT ? z : c16 / a.grp, g = EXACT ? c16 : c16 % a.grp;
+    const int i = (EXACT ? z_lo : 0) + c16 / a.grp, g = c16 % a.grp;
+    zr = i;
     pos = ctx - a.nq + i;
     const uint16_t* qr = a.q + (static_cast<size_t>(i) * a.Hq + h * a.grp + g) * kD + 32 * q4;
 #pragma unroll
@@ -621,10 +637,29 @@ attend_wave_kernel(AttArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qraw[s] = make_uint4(0, 0, 0, 0);
   }
+  // exact: the wave's calls (blk, zc) in order: per block, first the
+  // planes (zc = z_lo - 1) when the block is sealed for some row, then each
+  // query zc of the group whose position the block holds
+  auto call_ok = [&](int blk, int zc) {
+    return zc < z_lo ? blk < b_open_hi : (ctx - a.nq + zc) / kBlk == blk;
+  };
+  auto next_call = [&](int& blk, int& zc) {
+    for (;;) {
+      if (++zc >= z_lo + nz) {
+        blk += 4;
+        zc = z_lo - 1;
+      }
+      if (blk >= b_last) return false;
+      if (call_ok(blk, zc)) return true;
+    }
+  };
+  int cblk = b0, czc = z_lo - 1;
+  bool have = b0 < b_last;
+  if (EXACT && have && !call_ok(cblk, czc)) have = next_call(cblk, czc);
   // unconditional (a wave without a block of its own reads the chunk's first
   // block and discards it): a load under a branch makes the compiler copy
   // the codes at the join, which waits for all of them
-  load(b0 < b_last ? b0 : b_first);
+  load(have ? cblk : b_first, (EXACT && have && czc >= z_lo) ? czc : -1);
   __builtin_amdgcn_sched_barrier(0);
   // the query operand of this lane's row, times the row's power of two
   const int qe = q_row_exp(qraw);
@@ -652,9 +687,11 @@ attend_wave_kernel(AttArgs a) {
   const float sm_scale = __builtin_amdgcn_ldexpf(0.0625f * 0.08838834764831845f * kLog2e, -qe);
 
   // Rows whose position is at least pos_min see every token of a block that
-  // ends at or before pos_min; only later blocks need the causal mask.
-  const int pos_min = EXACT ? pos_z : ctx - a.nq;
-  auto block = [&](int blk, bool first) {
+  // ends at or before pos_min; only later blocks need the causal mask (and,
+  // in exact mode, every call with masked rows: force). pc is this row's
+  // position for the call, -1 for a masked row.
+  const int pos_min = pos_lo;
+  auto block = [&](int blk, bool first, int pc, bool force) {
     const uint4 *ck = kb, *cr = kr, *dk = vb, *dr = vr;
     const int t0 = blk * kBlk;
     const float sk = ks * sm_scale;
@@ -670,7 +707,7 @@ attend_wave_kernel(AttArgs a) {
     }
     // block maximum of the biased scores (the bias and the scale sk >= 0
     // are applied after)
-    const bool masked = t0 + kBlk - 1 > pos_min;
+    const bool masked = force || t0 + kBlk - 1 > pos_min;
     float mb = -INFINITY;
     if (masked) {
 #pragma unroll
@@ -678,7 +715,7 @@ attend_wave_kernel(AttArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = t0 + 32 * q4 + 8 * (tt >> 1) + 4 * (tt & 1) + i;
-          if (tok > pos) S[tt][i] = -INFINITY;
+          if (tok > pc) S[tt][i] = -INFINITY;
           mb = fmaxf(mb, S[tt][i]);
         }
     } else {
@@ -757,12 +794,26 @@ attend_wave_kernel(AttArgs a) {
   };
   // the first block (already requested) starts the running max and sum, so
   // O needs no rescaling there; most waves own a single block
-  if (b0 < b_last) {
-    block(b0, true);
+  if constexpr (EXACT) {
+    const int b_row = pos >= 0 ? pos / kBlk : -1;  // the block holding this row's position
+    bool first = true;
+    while (have) {
+      // planes: the rows for which the block is sealed; a query's slot: its rows
+      const bool act = czc < z_lo ? (zr >= 0 && b_row > cblk) : zr == czc;
+      block(cblk, first, act ? pos : -1, cblk >= b_open_lo);
+      first = false;
+      have = next_call(cblk, czc);
+      if (have) {
+        load(cblk, czc >= z_lo ? czc : -1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if (b0 < b_last) {
+    block(b0, true, pos, false);
     for (int blk = b0 + 4; blk < b_last; blk += 4) {
-      load(blk);
+      load(blk, -1);
       __builtin_amdgcn_sched_barrier(0);
-      block(blk, false);
+      block(blk, false, pos, false);
     }
   }
   // take the V bias off (every dim of a row has the same bias sum)
@@ -786,8 +837,8 @@ attend_wave_kernel(AttArgs a) {
     for (int i = 0; i < 4; ++i) buf[wave][c16][dt * 16 + 4 * q4 + i] = O[dt][i] * f;
   __syncthreads();
   // the four waves' parts added in the fixed order w = 3 .. 0; in exact
-  // mode this workgroup's rows are rows z * grp .. of the call
-  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R + (EXACT ? z * a.grp : 0);
+  // mode this workgroup's rows are rows z_lo * grp .. of the call
+  const size_t pbase = (static_cast<size_t>(h) * a.nchunk + chunk) * a.R + (EXACT ? z_lo * a.grp : 0);
   for (int idx = threadIdx.x; idx < nrow * (kD / 4); idx += 256) {
     const int row = idx / (kD / 4), d4 = idx % (kD / 4);
     float4 v = *reinterpret_cast<const float4*>(&buf[3][row][4 * d4]);
@@ -1081,7 +1132,10 @@ extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_h
   open_block_kernel<<<dim3(kOpenSplit, static_cast<unsigned>(Hkv), static_cast<unsigned>(2 * nq)), 256, 0, st>>>(a);
   rc = nest::check_launch("kv_nest_attend_exact(open blocks)");
   if (rc) return rc;
-  const int64_t items = static_cast<int64_t>(p.nchunk) * Hkv * nq;
+  // as many queries per workgroup as their GQA groups fit in 16 rows
+  a.qpack = static_cast<int>(16 / a.grp < nq ? 16 / a.grp : nq);
+  if (a.qpack < 1) a.qpack = 1;
+  const int64_t items = static_cast<int64_t>(p.nchunk) * Hkv * ((nq + a.qpack - 1) / a.qpack);
   const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
   if (view == 0)
     attend_wave_kernel<0, true><<<grid, 256, 0, st>>>(a);

@@ -422,13 +422,15 @@ __device__ __forceinline__ void gemv_segment_d(const GemvArgs& a, const uint4* l
 // SIMD, measured no faster), and three for one plane was slower.
 constexpr int prefetch_depth(int planes) { return planes == 1 ? 2 : 1; }
 
-constexpr int occupancy_target(int planes, int mr, bool dbg) {
-  return dbg ? 1 : planes == 2 ? 3 : mr == 1 ? 3 : 4;
+constexpr int occupancy_target(int planes, int mr, bool dbg, bool unstaged_depth2 = false) {
+  // the two-plane fold with two quads in flight (unstaged activations)
+  // needs the register budget of two waves per SIMD
+  return dbg ? 1 : planes == 2 ? (unstaged_depth2 ? 2 : 3) : mr == 1 ? 3 : 4;
 }
 
 template <int PLANES, int MR, int WAVES, bool ARGMAX, bool DBG, bool A4, bool LDSACT, bool XQ>
 __global__ void __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(occupancy_target(PLANES, MR, DBG))))
+__attribute__((amdgpu_waves_per_eu(occupancy_target(PLANES, MR, DBG, !ARGMAX && A4 && !LDSACT))))
 gemv_kernel(GemvArgs a) {
   static_assert(!XQ || LDSACT, "fp32 activations are quantized into LDS");
   extern __shared__ uint4 lds_act[];
@@ -466,7 +468,11 @@ gemv_kernel(GemvArgs a) {
 
   // branch-free first quad: tile and group clamped into range; it is only
   // used when this wave's first tile exists and its segment is not empty
-  constexpr int kDepth = (ARGMAX && A4 && !DBG) ? prefetch_depth(PLANES) : 1;
+  // quads in flight per wave: the argmax GEMVs as prefetch_depth says; the
+  // two-plane products whose activations are not staged (long rows, e.g.
+  // the 5-row down projection) keep two (their waves walk a chain of quads,
+  // each a round trip; 19.9 -> 17.8 us for 5 x 18944 x 3584), the rest one
+  constexpr int kDepth = (A4 && !DBG) ? (ARGMAX ? prefetch_depth(PLANES) : (PLANES == 2 && !LDSACT ? 2 : 1)) : 1;
   Quad qs[kDepth];
   Quad& cur = qs[0];
   if (A4) {

@@ -55,11 +55,14 @@ def inputs(Hq, Hkv, cap, ctx0, nq, key):
     return kf, vf, kn, vn, q
 
 
-# (Hq, Hkv, capacity, ctx0, nq); the last two: one query (the entry point's
-# one-query path) and 9 queries of a GQA group of 8 (72 rows, more than
-# kv_nest_attend's 64)
+# (Hq, Hkv, capacity, ctx0, nq). A workgroup packs floor(16 / (Hq/Hkv))
+# queries (2 for GQA 7 or 8, 4 for GQA 4, 16 for GQA 1). The last three: one
+# query (the entry point's one-query path), 9 queries of a GQA group of 8
+# (72 rows, more than kv_nest_attend's 64), and 17 queries of GQA 1 (a full
+# group of 16 and one more) crossing a block boundary
 CASES = [(28, 4, 1024, 300, 5), (8, 2, 512, 126, 5), (32, 8, 384, 250, 9), (4, 1, 256, 0, 3),
-         (16, 16, 640, 511, 2), (28, 4, 512, 123, 9), (28, 4, 512, 200, 1), (64, 8, 512, 380, 9)]
+         (16, 16, 640, 511, 2), (28, 4, 512, 123, 9), (28, 4, 512, 200, 1), (64, 8, 512, 380, 9),
+         (16, 16, 640, 370, 17)]
 
 
 @pytest.mark.parametrize("view", [0, 1])

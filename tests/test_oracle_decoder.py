@@ -114,3 +114,47 @@ def test_round_bookkeeping_mistakes_break_the_claim(tiny, D):
     bad.__dict__.update(tiny.__dict__)
     sp, _ = bad.generate(prompt, 48, 4)
     assert sp != ar
+
+
+def test_teacher_forced_logits_are_those_of_target_only_decoding(tiny):
+    # scoring a sequence position by position from its own prefix (16
+    # positions per exact target pass) must give, bit for bit, the logits
+    # that target-only decoding computed when it produced that sequence: an
+    # off-by-one in the start row or in the positions would shift them
+    prompt = synth.tokens(40, tiny.cfg["vocab"], (801,))
+    ar, r_ar = tiny.generate(prompt, 20, 0)
+    y_ar = np.concatenate([y for _, y in r_ar])[:len(ar)]
+    y_tf = tiny.teacher_forced_logits(list(prompt) + list(ar), len(prompt) - 1)
+    assert y_tf.shape == y_ar.shape
+    assert np.array_equal(y_tf.view(np.uint32), y_ar.view(np.uint32))
+
+
+def test_attention_noise_has_its_stated_relative_norm(D):
+    # the noise the decoder-vs-oracle tolerance is derived from: every
+    # attention output vector (per position and head) moves by exactly
+    # att_noise times its norm, the same seed gives the same draw, and
+    # att_noise = 0 leaves the computation untouched
+    cfg = synth.TINY_DECODER
+    w = synth.decoder_weights(cfg, (800,))
+    d, Hq = cfg["head_dim"], cfg["q_heads"]
+
+    class Capture(D.Decoder):
+        def linear(self, x, packed, draft):
+            if any(packed is lw["o"] for lw in self.layers):
+                self.seen.append(np.array(x, np.float64).reshape(len(x), Hq, d))
+            return D.Decoder.linear(x, packed, draft)
+
+    toks = synth.tokens(12, cfg["vocab"], (802,))
+    outs = {}
+    for key, noise, seed in (("plain", 0.0, 0), ("zero", 0.0, 5), ("a", 2e-3, 1), ("b", 2e-3, 1)):
+        dec = Capture(cfg, w, att_noise=noise, noise_seed=seed)
+        dec.seen = []
+        h = dec.forward(list(toks), 0, draft=False, exact=True)
+        outs[key] = (dec.seen, h)
+    assert np.array_equal(outs["plain"][1], outs["zero"][1])
+    assert np.array_equal(outs["a"][1], outs["b"][1])
+    assert not np.array_equal(outs["a"][1], outs["plain"][1])
+    # first layer: same inputs, so the attention outputs differ by the noise alone
+    att0, att1 = outs["plain"][0][0], outs["a"][0][0]
+    rel = np.linalg.norm(att1 - att0, axis=-1) / np.linalg.norm(att0, axis=-1)
+    assert np.allclose(rel, 2e-3, rtol=1e-3), (rel.min(), rel.max())

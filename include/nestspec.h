@@ -424,7 +424,7 @@ int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
  * the cache exactly as a one-token pass at its own position would ("How
  * Speculative Decoding Speeds Up Inference", section "Drafting and checking
  * tokens", step 2: one pass checks every position; section "The same
- * output as the large model alone"), in one launch.
+ * output as the large model alone"), in one call.
  * Query i (position p_i = L - nq + i, L the visible length) sees tokens
  * 0..p_i. The block holding p_i is taken as kv_nest_append would have
  * quantized it after a one-token append at p_i: from its fp32 values in
@@ -441,8 +441,11 @@ int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
  *            rebuilt open block (both planes of K and V, 32 KB) and its two
  *            scales per (query, kv head); no zero-fill needed
  *   the rest as for kv_nest_attend.
- * Two kernels and the merge run: the first rebuilds every query's open
- * block into the workspace, the second attends.
+ * Three launches: the open blocks are rebuilt into the workspace, then
+ * one attention kernel serves all queries (as many queries per workgroup
+ * as their GQA groups fit in 16 rows), then the chunk partials are merged.
+ * With nq == 1 the call is kv_nest_attend's (the append already quantized
+ * the block over the tokens up to the query).
  * Requires Hq/Hkv <= 16 and nq <= block; nq*(Hq/Hkv) may exceed
  * kv_nest_attend's 64. Errors: as kv_nest_attend. */
 int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,

@@ -46,12 +46,12 @@ def prefilled(ns, kf, vf, ctx0):
     return kv, sh
 
 
-def inputs(Hq, Hkv, cap, ctx0, nq, key):
-    kf, vf = synth.kv(Hkv, cap, 128, (key, 0))
+def inputs(Hq, Hkv, cap, ctx0, nq, key, k_std=1.0, v_std=1.0, q_std=1.0):
+    kf, vf = synth.kv(Hkv, cap, 128, (key, 0), k_std, v_std)
     kf[:, ctx0:] = 0.0
     vf[:, ctx0:] = 0.0
-    kn, vn = synth.kv(Hkv, nq, 128, (key, 1))
-    q = synth.queries_bf16(nq, Hq, 128, (key, 2))
+    kn, vn = synth.kv(Hkv, nq, 128, (key, 1), k_std, v_std)
+    q = synth.queries_bf16(nq, Hq, 128, (key, 2), q_std)
     return kf, vf, kn, vn, q
 
 
@@ -108,3 +108,27 @@ def test_exact_at_32k_crossing_a_block(ns):
         ns.kv_nest_append(kv2, sh2, dev(kn[:, i:i + 1]), dev(vn[:, i:i + 1]), ctx0 + i)
         ref = host(ns.kv_nest_attend(qd[i:i + 1], kv2, ctx0 + i + 1, 1))[0]
         assert np.array_equal(got[i].view(np.uint32), ref.view(np.uint32)), i
+
+
+# (k_std, v_std, q_std): the magnitudes of the kv_nest_attend scale tests, here
+# through the open-block rebuild of the exact pass
+SCALES = [(1.0, 1e-4, 1.0), (1.0, 1e-3, 1.0), (30.0, 30.0, 1.0), (1.0, 1.0, 100.0), (1.0, 1.0, 1e-3),
+          (1e-4, 1.0, 1.0)]
+
+
+@pytest.mark.parametrize("view", [0, 1])
+@pytest.mark.parametrize("k_std,v_std,q_std", SCALES)
+def test_exact_at_extreme_scales(ns, oracle, k_std, v_std, q_std, view):
+    Hq, Hkv, cap, ctx0, nq = 28, 4, 512, 250, 9
+    kf, vf, kn, vn, q = inputs(Hq, Hkv, cap, ctx0, nq, 270, k_std, v_std, q_std)
+    qd = dev(q.view(np.int16))
+    kv, sh = prefilled(ns, kf, vf, ctx0)
+    ns.kv_nest_append(kv, sh, dev(kn), dev(vn), ctx0)
+    got = host(ns.kv_nest_attend_exact(qd, kv, sh, ctx0 + nq, view))
+    okv = oracle.kv_nest_pack(kf, vf)
+    ok, ov = kf.copy(), vf.copy()
+    for i in range(nq):
+        oracle.kv_append(okv, ok, ov, kn[:, i:i + 1], vn[:, i:i + 1], ctx0 + i)
+        o = oracle.kv_attend(np.ascontiguousarray(q[i:i + 1]), okv, ctx0 + i + 1, view)[0]
+        rel = np.linalg.norm(got[i] - o, axis=-1) / np.linalg.norm(o, axis=-1)
+        assert float(rel.max()) <= 2e-3, (i, float(rel.max()))

@@ -398,7 +398,8 @@ def k_choice(ns, torch, dv, kmax=8):
 def tiny_decoder(torch, n_new=48, prompt_len=40):
     """Greedy rounds end to end through the small synthetic decoder: emitted
     tokens per round, equality with target-only decoding, and wall-clock
-    tokens/s of the host-driven loop (one host sync per round)."""
+    tokens/s of the host-driven loop (one host sync per round), of rounds
+    chained on the device and of rounds replayed from a HIP graph."""
     from nested_quantized_weights_amd import synth
     from nested_quantized_weights_amd.decoder import Decoder
 
@@ -432,6 +433,19 @@ def tiny_decoder(torch, n_new=48, prompt_len=40):
             else:
                 out["batched_first_divergence"][tag] = next(
                     (i for i, (a, b) in enumerate(zip(toks, ar)) if a != b), None)
+    # k=4 exact rounds with no host read between them: issued eagerly one
+    # launch at a time, and replayed from one captured HIP graph of a round
+    rounds, k = 60, 4
+    dec.run_rounds(prompt, 4, k, want_y=False)  # warm-up
+    tm = {}
+    toks_e, per = dec.run_rounds(prompt, rounds, k, want_y=False, timing=tm)
+    tg = {}
+    toks_g, counts = dec.graph_rounds(prompt, rounds, k, timing=tg)
+    out["chained_k4_exact"] = {
+        "rounds": rounds, "tokens": len(toks_e),
+        "eager_tokens_per_s": round(len(toks_e) / tm["rounds_s"], 1),
+        "graph_replay_tokens_per_s": round(sum(counts[1:]) / tg["replay_s"], 1),
+        "graph_equal_to_eager": toks_g == toks_e and counts == [n for n, _ in per]}
     return out
 
 

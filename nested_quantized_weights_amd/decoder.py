@@ -29,6 +29,8 @@ A target pass over the k+1 positions of a round attends in one of three ways:
 """
 from __future__ import annotations
 
+import time
+
 import numpy as np
 import torch
 
@@ -144,15 +146,21 @@ class Decoder:
         ns.verify_accept_x(h, 1, k, self.head, toks[1:] if k else self.no_draft, out=out,
                            length=self.length, next_token=b["toks"][r + 1][0:1])
 
-    def run_rounds(self, prompt, rounds: int, k: int, mode: str = "exact", want_y: bool = True):
+    def run_rounds(self, prompt, rounds: int, k: int, mode: str = "exact", want_y: bool = True, timing=None):
         """A fixed number of rounds issued back to back with no host read
         between them (positions, lengths and inputs advance on the device).
         Returns (tokens, per round (emitted count, logits of the emitted
-        positions [n][V] or None)) after one synchronisation at the end."""
+        positions [n][V] or None)) after one synchronisation at the end;
+        timing, a dict, receives the rounds' wall-clock seconds."""
         b = self._buffers(rounds, k, want_y)
         b["toks"][0, 0:1].copy_(self.prefill(prompt))
+        torch.cuda.synchronize(self.dev)
+        t0 = time.perf_counter()
         for r in range(rounds):
             self._round(r, k, mode, b)
+        torch.cuda.synchronize(self.dev)
+        if timing is not None:
+            timing["rounds_s"] = time.perf_counter() - t0
         n = b["n_emitted"][:, 0].cpu().numpy()
         em = b["emitted"].cpu().numpy()
         toks, per = [], []
@@ -160,6 +168,65 @@ class Decoder:
             toks += em[r, :n[r]].tolist()
             per.append((int(n[r]), b["y"][r, :n[r]] if want_y else None))
         return toks, per
+
+    def graph_rounds(self, prompt, rounds: int, k: int, mode: str = "exact", sync_each: bool = False,
+                     timing=None):
+        """The same rounds as run_rounds, with round 0 issued eagerly and every
+        later round a replay of one HIP graph of a round (captured after
+        round 0, on a stream of its own). A round reads its input token from
+        and writes the next one to one device buffer, and appends its emitted
+        tokens and count to a device ring at a device-held index, so a replay
+        needs no host work at all. sync_each synchronizes after every replay
+        and reads the ring index (eager work between replays); timing, a
+        dict, receives the replays' wall-clock seconds. Returns (tokens,
+        emitted counts)."""
+        dev = self.dev
+        k1 = k + 1
+        toks = torch.empty(k1, dtype=torch.int32, device=dev)  # [0]: the round's input
+        out = {"target": torch.empty(k1, dtype=torch.int32, device=dev),
+               "n_emitted": torch.empty(1, dtype=torch.int32, device=dev),
+               "emitted": torch.empty(k1, dtype=torch.int32, device=dev)}
+        ring_t = torch.full((rounds, k1), -1, dtype=torch.int32, device=dev)
+        ring_n = torch.zeros(rounds, dtype=torch.int32, device=dev)
+        ring_i = torch.zeros(1, dtype=torch.int64, device=dev)
+
+        def one_round():
+            for j in range(k):
+                h = self.forward(toks[j:j + 1], j, draft=True, mode="exact")
+                ns.draft_gemv_x(h, self.head, want_y=False, argmax=True, argmax_out=toks[j + 1:j + 2])
+            h = self.forward(toks, 0, draft=False, mode=mode)
+            ns.verify_accept_x(h, 1, k, self.head, toks[1:] if k else self.no_draft, out=dict(out),
+                               length=self.length, next_token=toks[0:1])
+            ring_t.index_copy_(0, ring_i, out["emitted"].view(1, k1))
+            ring_n.index_copy_(0, ring_i, out["n_emitted"])
+            ring_i.add_(1)
+
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            toks[0:1].copy_(self.prefill(prompt))
+            one_round()  # round 0, eager: also sets up every workspace on this stream
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                one_round()
+            side.synchronize()
+            t0 = time.perf_counter()
+            for r in range(rounds - 1):
+                graph.replay()
+                if sync_each:
+                    side.synchronize()
+                    if int(ring_i.item()) != r + 2:
+                        raise RuntimeError(f"replay {r}: ring index {int(ring_i.item())}")
+            side.synchronize()
+            if timing is not None:
+                timing["replay_s"] = time.perf_counter() - t0
+        torch.cuda.current_stream(dev).wait_stream(side)
+        n = ring_n.cpu().numpy()
+        t = ring_t.cpu().numpy()
+        tokens = []
+        for r in range(rounds):
+            tokens += t[r, :n[r]].tolist()
+        return tokens, n.tolist()
 
     def generate(self, prompt, n_new: int, k: int, mode: str = "exact"):
         """Greedy decoding of n_new tokens after the prompt: one target pass

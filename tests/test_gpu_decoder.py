@@ -17,7 +17,7 @@ the large model alone").
   * Rounds chained on the device (committed length and next input kept by
     verify_accept, no host read between rounds) emit the same tokens and
     bit-identical logits as the host-driven loop, and as target-only
-    decoding.
+    decoding; so do rounds replayed from one captured HIP graph.
   * Against the oracle, position by position: the oracle scores every
     generated position from the GPU's own prefix (teacher forcing, which is
     what target-only decoding computes there). The GPU's logits must lie
@@ -175,6 +175,20 @@ def test_chained_rounds_match_the_host_loop(gpu_dec):
         y_ref = torch.cat([y for _, y in per_ref]).cpu().numpy()[:len(y)]
         assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
         assert len(toks) >= 50 and all(1 <= n <= k + 1 for n, _ in per)
+
+
+@pytest.mark.parametrize("k", [0, 4])
+def test_graph_replayed_rounds_match_the_eager_rounds(gpu_dec, k):
+    """Round 0 eager, then every round a replay of one captured round: the
+    same tokens and emitted counts as the eager chained rounds, both when
+    the replays run back to back and when the host synchronizes and reads
+    the device's ring index between them."""
+    prompt = synth.tokens(40, CFG["vocab"], (801,))
+    ref, per = gpu_dec.run_rounds(prompt, 40, k, want_y=False)
+    for sync_each in (False, True):
+        toks, counts = gpu_dec.graph_rounds(prompt, 40, k, sync_each=sync_each)
+        assert counts == [n for n, _ in per]
+        assert toks == ref
 
 
 def test_chained_decode_matches_the_oracle(gpu_dec, weights, D):

@@ -662,6 +662,9 @@ def workloads(ns, torch, dv):
     xs = {K: ns.nest_act_quant(torch.from_numpy(synth.activations(M, K, (key, 1, 0, K))).cuda())
           for _, (_, K) in wl["linears"].items()}
     ys = {n: torch.empty((M, N), dtype=torch.float32, device=cuda) for n, (N, _) in wl["linears"].items()}
+    # one workspace for every linear (calls on one stream run in order)
+    wsn = max(L.verify_gemm_workspace_size(M, K, N) for N, K in wl["linears"].values())
+    wsv = torch.zeros(max(wsn, 256), dtype=torch.uint8, device=cuda)
     calls = []
     for lay in layers:
         for name, (N, K) in wl["linears"].items():
@@ -671,11 +674,13 @@ def workloads(ns, torch, dv):
 
     def verify_pass():
         for N, K, pq, psa, pb, pr, ps, py in calls:
-            _check_rc(ns, L.verify_gemm(pq, psa, M, K, pb, pr, ps, N, 128, py, None, st), "verify_gemm")
+            _check_rc(ns, L.verify_gemm(pq, psa, M, K, pb, pr, ps, N, 128, py, None, ptr(wsv), wsv.numel(), st),
+                      "verify_gemm")
 
     per_layer = {n: _timed_us(torch, lambda n=n, N=N, K=K: _check_rc(
         ns, L.verify_gemm(ptr(xs[K][0]), ptr(xs[K][1]), M, K, ptr(layers[1][n].base), ptr(layers[1][n].refine),
-                          ptr(layers[1][n].scales), N, 128, ptr(ys[n]), None, st), "verify_gemm"), 20)
+                          ptr(layers[1][n].scales), N, 128, ptr(ys[n]), None, ptr(wsv), wsv.numel(), st),
+        "verify_gemm"), 20)
                  for n, (N, K) in wl["linears"].items()}
     us = _timed_us(torch, verify_pass, 5, warmup=1)
     nbytes = wl["layers"] * sum(gemv_bytes(N, K, M, 2) for N, K in wl["linears"].values())
@@ -683,7 +688,7 @@ def workloads(ns, torch, dv):
     out["llama3-8b_batched_verify"] = dict(_rate(nbytes, us, ops), rows=M, layers=wl["layers"],
                                            ms_per_pass=round(us / 1e3, 4),
                                            per_linear_us={n: round(v, 2) for n, v in per_layer.items()})
-    del layers, layer0, xs, ys, calls
+    del layers, layer0, xs, ys, calls, wsv
 
     # -- nested KV attention at 32K: draft (1 query, base view), verify (9
     # queries, full view), rotating over 8 caches

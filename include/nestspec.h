@@ -33,11 +33,11 @@
  *    Every call enqueues its kernels on that stream and returns without
  *    synchronising.
  *  - Workspaces: sizes come from the *_workspace_size functions. The GEMV
- *    workspaces (draft_gemv, draft_gemv_x, verify_gemm_x, verify_accept,
- *    verify_accept_x) are 256-byte aligned and must be all zero before
- *    their first use; every call leaves the part that must stay zero (a
- *    block counter in the first 256 bytes) at zero, so one workspace serves
- *    any number of calls. Calls that share a workspace must not overlap in
+ *    workspaces (draft_gemv, draft_gemv_x, verify_gemm, verify_gemm_x,
+ *    verify_accept, verify_accept_x) are 256-byte aligned and must be all
+ *    zero before their first use; every call leaves the parts that must
+ *    stay zero (block counters) at zero, so one workspace serves any number
+ *    of calls. Calls that share a workspace must not overlap in
  *    time (same stream, or ordered by events).
  *  - Lengths that change from round to round can live on the device: the
  *    calls that take a position or a context length also take an optional
@@ -240,14 +240,24 @@ int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
  *   qa int8 [M][K] (16-byte aligned); sa fp32 [M]
  *   base, refine, scales: the tile layout (nest_tile), 16-byte aligned
  *   y fp32 [M][N] (out); acc_dbg int32 [M][N][K/group] (out, nullable): Av
+ *   ws       verify_gemm_workspace_size(M, K, N) bytes, zeroed before first
+ *            use; may be NULL (ws_bytes 0) when that size is 0
  * Requires M >= 1, group == 128, K % 128 == 0, N >= 1. M <= 16 runs the
- * one-tile kernel. Larger M runs the batched MFMA kernel.
+ * one-tile kernel. Larger M runs the batched MFMA kernel in launches of up
+ * to 144 rows; with few weight rows over long rows (e.g. 4096 x 14336) it
+ * splits the groups over several blocks per row block, whose sums meet in
+ * the workspace.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
- * NEST_EHIP. */
+ * NEST_EWORKSPACE, NEST_EHIP. */
 int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                 const uint8_t* base, const uint8_t* refine, const float* scales,
-                int64_t N, int64_t group, float* y, int32_t* acc_dbg,
-                void* stream);
+                int64_t N, int64_t group, float* y, int32_t* acc_dbg, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Workspace of verify_gemm over M rows, reduction length K and N output
+ * rows: 0 when the call needs none (M <= 16, or no group split) or the
+ * sizes are invalid. It depends on the current device's CU count. */
+size_t verify_gemm_workspace_size(int64_t M, int64_t K, int64_t N);
 
 /* verify_gemm_x -- verify_gemm on fp32 activations, quantized in the kernel
  * as for draft_gemv_x (bit-identical to nest_act_quant + verify_gemm), or

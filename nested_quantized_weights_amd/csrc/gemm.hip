@@ -19,6 +19,11 @@
 // of q_a c; the activation operand is 16 contiguous bytes of one row. The
 // fp32 fold runs in registers in ascending group order within each half,
 // and the halves are added in group order. Matrices with few rows split
+// either the groups over S blocks (long rows: each block folds a
+// contiguous slice of the groups for all activation rows, and the last of
+// the S blocks to finish adds the slices' sums in slice order; it sees them
+// by the same ordering argument as the argmax handoff in gemv.hip, agent-
+// scope stores acknowledged before an agent-scope counter increment) or
 // the activation rows over several blocks (each reads the same weights, on
 // the same XCD, so the repeats come from its L2).
 #include <algorithm>
@@ -41,9 +46,13 @@ constexpr int ring_slots(int ctp, int wk) { return 3 * wk * ctp * 2048 <= kLdsBy
 constexpr int kSlots = 3;                // weight groups in flight per compute wave
 constexpr int kMaxCT = 9;                // 144 activation rows per launch
 constexpr int kXcds = 8;                 // blocks are dealt to the XCDs in turn
+constexpr int kMaxSplit = 4;             // most slices of the groups (blocks per row block)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit data, bounds = num_records bytes
+constexpr int kSC1 = 16;                // cache-policy bit sc1 of a buffer load / store
 
 struct GemmArgs {
   const int8_t* qa;   // [M][K]
@@ -53,8 +62,10 @@ struct GemmArgs {
   const float* scales;
   float* y;           // [M][N]
   int32_t* acc_dbg;   // [M][N][G] (DBG)
+  unsigned* done;     // split: [row_blocks] finished-slice counters (zero between launches)
+  float* part;        // split: [row_blocks][S] per-block sums, lane-major
   int M, K, N, G, T;
-  int row_blocks, parts;
+  int row_blocks, parts, split;
 };
 
 struct WLoad {
@@ -201,18 +212,21 @@ __global__ void __launch_bounds__(threads_for(WK, WR)) gemm_kernel(GemmArgs a) {
   static_assert((kAhead - 1) * kCopies <= 63, "copies in flight exceed the vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kNBuf * kWK * SB];
 
-  // blocks of one row block sit kXcds apart, i.e. on one XCD
-  const int b = static_cast<int>(blockIdx.x), P = a.parts;
-  const int rb = (b / (kXcds * P)) * kXcds + b % kXcds;
-  const int part = (b / kXcds) % P;
+  // blocks of one row block (its P activation-row parts or its S slices
+  // of the groups) sit kXcds apart, i.e. on one XCD
+  const int b = static_cast<int>(blockIdx.x), P = a.parts, S = a.split;
+  const int rb = (b / (kXcds * P * S)) * kXcds + b % kXcds;
+  const int ps = (b / kXcds) % (P * S);
+  const int part = ps % P, slice = ps / P;
   if (rb >= a.row_blocks) return;
   const int ct0 = part * CTP;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int kq = lane >> 4, idx = lane & 15;
-  const int G = a.G;
-  const int steps = (G + kWK - 1) / kWK;
-  auto h0 = [&](int wk) { return wk * G / kWK; };  // half wk: groups [h0(wk), h0(wk + 1))
+  // this block's groups: slice `slice` of S, [gs0, gs0 + Gs)
+  const int gs0 = slice * a.G / S, Gs = (slice + 1) * a.G / S - gs0;
+  const int steps = (Gs + kWK - 1) / kWK;
+  auto h0 = [&](int wk) { return gs0 + wk * Gs / kWK; };  // half wk: groups [h0(wk), h0(wk + 1))
 
   if (wave == kCW) {
     // copy wave: group j of each half into slot j % kNBuf. Copy (ct, e)
@@ -257,6 +271,10 @@ __global__ void __launch_bounds__(threads_for(WK, WR)) gemm_kernel(GemmArgs a) {
     wait_vm<0>();
     copy_barrier();  // the ring is free: the parts' sums go through it
     copy_barrier();
+    if (S > 1) {     // the compute waves' slice handoff
+      copy_barrier();
+      copy_barrier();
+    }
     return;
   }
 
@@ -325,23 +343,97 @@ __global__ void __launch_bounds__(threads_for(WK, WR)) gemm_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) comb[cidx(wk, rt, ct, i)] = run[rt][ct][i];
   }
   lds_barrier();
-  if (wk > 0) return;
+  if (wk == 0) {
 #pragma unroll
-  for (int ct = 0; ct < CTP; ++ct)
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTP; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int w = 1; w < kWK; ++w) run[rt][ct][i] += comb[cidx(w, rt, ct, i)];
+  }
+  if (S == 1) {
+    if (wk > 0) return;
+#pragma unroll
+    for (int ct = 0; ct < CTP; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = (ct0 + ct) * 16 + 4 * kq + i;
+        if (m >= a.M) continue;
+        const float sm = a.sa[m];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          const int n = t[rt] * 16 + idx;
+          if (t_ok[rt] && n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = run[rt][ct][i] * sm;
+        }
+      }
+    return;
+  }
+
+  // Groups split over S blocks: this block's sums go to its slot, one
+  // 16-byte piece per (tile, column tile, lane) holding its four rows i,
+  // stored with the sc1 policy (what an agent-scope atomic store uses:
+  // written through to the device's coherence point); once every store is
+  // acknowledged the block counts itself in, and the last of the row
+  // block's S blocks reads the S slots with the same policy (what an
+  // agent-scope atomic load uses) and adds them in slice order.
+  constexpr int kSlot = kWR * kRT * CTP * 4 * 64;  // floats per block slot
+  const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+      a.part + static_cast<size_t>(rb) * S * kSlot, 0, S * kSlot * static_cast<int>(sizeof(float)), kRsrcWord3);
+  if (wk == 0) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTP; ++ct) {
+        const v4u v = {__float_as_uint(run[rt][ct][0]), __float_as_uint(run[rt][ct][1]),
+                       __float_as_uint(run[rt][ct][2]), __float_as_uint(run[rt][ct][3])};
+        const int piece = ((wr * kRT + rt) * CTP + ct) * 64 + lane;
+        __builtin_amdgcn_raw_buffer_store_b128(v, slots, (slice * kSlot + 4 * piece) * 4, 0, kSC1);
+      }
+  }
+  __shared__ int last_sh;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) last_sh = atomicAdd(a.done + rb, 1u) == static_cast<unsigned>(S - 1);
+  __syncthreads();
+  if (!last_sh) return;
+  // the compute waves' threads take the pieces in turn; every load is
+  // issued before the sums
+  constexpr int kPieces = kSlot / 4, kNT = kCW * 64, kIter = (kPieces + kNT - 1) / kNT;
+  const int tid = static_cast<int>(threadIdx.x);
+  v4u v[kIter][kMaxSplit];
+#pragma unroll
+  for (int it = 0; it < kIter; ++it)
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      const int q = min(tid + it * kNT, kPieces - 1);
+      v[it][s] = __builtin_amdgcn_raw_buffer_load_b128(slots, ((s < S ? s : 0) * kSlot + 4 * q) * 4, 0, kSC1);
+    }
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int q = tid + it * kNT;
+    if (q >= kPieces) continue;
+    float tot[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] = __uint_as_float(v[it][0][i]);
+#pragma unroll
+    for (int s = 1; s < kMaxSplit; ++s)
+      if (s < S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] += __uint_as_float(v[it][s][i]);
+      }
+    // piece q: lane q % 64, column tile and tile from q / 64
+    const int l = q & 63, ct = (q >> 6) % CTP, tr = (q >> 6) / CTP;  // tr = wr * kRT + rt
+    const int tt = rb * kWR * kRT + tr, n = tt * 16 + (l & 15);
+    if (tt >= a.T || n >= a.N) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = (ct0 + ct) * 16 + 4 * kq + i;
-      if (m >= a.M) continue;
-      const float sm = a.sa[m];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        const int n = t[rt] * 16 + idx;
-        float v = run[rt][ct][i];
-#pragma unroll
-        for (int w = 1; w < kWK; ++w) v += comb[cidx(w, rt, ct, i)];
-        if (t_ok[rt] && n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = v * sm;
-      }
+      const int m = (ct0 + ct) * 16 + 4 * (l >> 4) + i;
+      if (m < a.M) a.y[static_cast<size_t>(m) * a.N + n] = tot[i] * a.sa[m];
     }
+  }
+  if (threadIdx.x == 0) atomicExch(a.done + rb, 0u);
 }
 
 template <int CTP, int WK, int WR, bool DBG>
@@ -386,48 +478,88 @@ int device_cus() {
   return cus;
 }
 
-// Work split: four weight tiles per block, the activation rows split evenly
-// over P blocks per row block when the matrix alone would leave CUs idle
-// (P divides the column tiles). When that needs more blocks than CUs (a
-// partial second round of blocks on some CUs) and two-tile blocks over all
-// activation rows fit in one round, those are taken: LLaMA-3-8B qkv
-// (6144 x 4096, 144 rows) 23.9 -> 19.4 us, with the other linears' splits
-// measured best as they were.
-void plan_batched(int T, int CT, int cus, int& WR, int& P) {
-  WR = 4;
-  const int row_blocks = (T + 3) / 4;
-  P = 1;
-  for (int p = 1; p <= CT; ++p) {
-    if (CT % p) continue;
-    P = p;
-    if (4 * row_blocks * p >= 3 * cus) break;
+// Work split: four weight tiles per block. Few row blocks (under half the
+// CUs) over long rows (64 groups or more) split the groups over S blocks
+// per row block, each with all activation rows: every block stages a
+// quarter (S = 4) of the activation bytes and streams a quarter of the
+// row block's weights, where splitting the activation rows instead has each
+// block read all the weights (LLaMA-3-8B down, 4096 x 14336 at 144 rows:
+// 38.5 us as P = 3 against ~25 us for the same bytes in 256 one-slice
+// blocks). Otherwise the activation rows are split evenly over P blocks per
+// row block when the matrix alone would leave CUs idle (P divides the
+// column tiles). When that needs more blocks than CUs (a partial second
+// round of blocks on some CUs) and two-tile blocks over all activation rows
+// fit in one round, those are taken: LLaMA-3-8B qkv (6144 x 4096, 144 rows)
+// 23.9 -> 19.4 us, with the other linears' splits measured best as they
+// were.
+struct Plan {
+  int WR, P, S, row_blocks, CTP, blocks;
+  size_t ws_bytes;  // workspace of the group split (0 when S == 1)
+};
+
+size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+Plan plan_batched(int M, int K, int N, int cus) {
+  Plan p{};
+  const int T = (N + 15) / 16, CT = (M + 15) / 16, G = K / kGroup;
+  p.WR = 4;
+  p.P = 1;
+  p.S = 1;
+  int row_blocks = (T + 3) / 4;
+  if (2 * row_blocks <= cus && G >= 64) {
+    p.S = std::min(std::min(cus / row_blocks, G / 16), kMaxSplit);
+  } else {
+    for (int q = 1; q <= CT; ++q) {
+      if (CT % q) continue;
+      p.P = q;
+      if (4 * row_blocks * q >= 3 * cus) break;
+    }
+    if (row_blocks * p.P > cus && (T + 1) / 2 <= cus) {
+      p.WR = 2;
+      p.P = 1;
+    }
   }
-  if (row_blocks * P > cus && (T + 1) / 2 <= cus) {
-    WR = 2;
-    P = 1;
+  p.row_blocks = (T + p.WR - 1) / p.WR;
+  p.CTP = CT / p.P;
+  p.blocks = ((p.row_blocks + kXcds - 1) / kXcds) * kXcds * p.P * p.S;
+  if (p.S > 1) {
+    const size_t slot = static_cast<size_t>(p.WR) * kRT * p.CTP * 4 * 64 * sizeof(float);
+    p.ws_bytes = round256(static_cast<size_t>(p.row_blocks) * sizeof(unsigned)) +
+                 static_cast<size_t>(p.row_blocks) * p.S * slot;
   }
+  return p;
 }
 
 }  // namespace
 
 namespace nest {
 
+size_t verify_batched_ws_bytes(int M, int K, int N) {
+  if (M < 1 || M > 16 * kMaxCT || K < kGroup || N < 1) return 0;
+  return plan_batched(M, K, N, device_cus()).ws_bytes;
+}
+
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
                           const uint8_t* refine, const float* scales, int N, float* y, int32_t* acc_dbg,
-                          hipStream_t st) {
+                          void* ws, size_t ws_bytes, hipStream_t st) {
   if (M < 1 || M > 16 * kMaxCT)
     return fail(NEST_EINVAL, "verify_gemm(batched): %d rows per launch (1..%d)", M, 16 * kMaxCT);
   GemmArgs a{};
   a.qa = qa; a.sa = sa; a.base = base; a.refine = refine; a.scales = scales;
   a.y = y; a.acc_dbg = acc_dbg;
   a.M = M; a.K = K; a.N = N; a.G = K / kGroup; a.T = (N + 15) / 16;
-  const int CT = (M + 15) / 16;
-  int WR = 4, P = 1;
-  plan_batched(a.T, CT, device_cus(), WR, P);
-  a.row_blocks = (a.T + WR - 1) / WR;
-  a.parts = P;
-  const int blocks = ((a.row_blocks + kXcds - 1) / kXcds) * kXcds * P;
-  return acc_dbg ? launch_wr<true>(a, WR, CT / P, blocks, st) : launch_wr<false>(a, WR, CT / P, blocks, st);
+  const Plan p = plan_batched(M, K, N, device_cus());
+  if (p.S > 1) {
+    if (!ws || ws_bytes < p.ws_bytes)
+      return fail(NEST_EWORKSPACE, "verify_gemm: workspace needs %zu bytes", p.ws_bytes);
+    if (!aligned16(ws)) return fail(NEST_EALIGN, "verify_gemm: workspace not 16-byte aligned");
+    a.done = static_cast<unsigned*>(ws);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(static_cast<size_t>(p.row_blocks) * sizeof(unsigned)));
+  }
+  a.row_blocks = p.row_blocks;
+  a.parts = p.P;
+  a.split = p.S;
+  return acc_dbg ? launch_wr<true>(a, p.WR, p.CTP, p.blocks, st) : launch_wr<false>(a, p.WR, p.CTP, p.blocks, st);
 }
 
 }  // namespace nest

@@ -746,9 +746,18 @@ size_t argmax_ws_bytes(int N) {
 constexpr size_t kCounterBytes = 256;
 constexpr size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
+// The batched verify's own workspace (its groups split over blocks), for the
+// launches of up to 144 rows that an M-row call makes.
+size_t batched_ws_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M <= 16 || N > (1LL << 30) || K > (1LL << 24)) return 0;
+  return round256(nest::verify_batched_ws_bytes(static_cast<int>(M < 144 ? M : 144), static_cast<int>(K),
+                                                static_cast<int>(N)));
+}
+
 size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N, bool x) {
   size_t n = kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
-  if (x) n += round256(static_cast<size_t>(M) * K) + round256(static_cast<size_t>(M) * sizeof(float));
+  if (x) n += round256(static_cast<size_t>(M) * K) + round256(static_cast<size_t>(M) * sizeof(float)) +
+              batched_ws_bytes(M, K, N);
   return n;
 }
 
@@ -757,6 +766,7 @@ struct Workspace {
   unsigned long long* partials;
   int8_t* codes;  // fp32-activation paths only
   float* code_scales;
+  void* batched;  // fp32-activation verify of more than 16 rows: the batched kernel's workspace
 };
 
 Workspace carve(void* ws, int64_t M, int64_t K, int64_t N) {
@@ -767,6 +777,7 @@ Workspace carve(void* ws, int64_t M, int64_t K, int64_t N) {
   char* c = p + kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
   w.codes = reinterpret_cast<int8_t*>(c);
   w.code_scales = reinterpret_cast<float*>(c + round256(static_cast<size_t>(M) * K));
+  w.batched = reinterpret_cast<char*>(w.code_scales) + round256(static_cast<size_t>(M) * sizeof(float));
   return w;
 }
 
@@ -890,8 +901,16 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
   }
   hipStream_t st = nest::as_stream(stream);
   Act act2 = act;
+  void* bws = ws;  // the batched kernel's workspace
+  size_t bws_bytes = ws_bytes;
   if (act.x) {
-    rc = quantize_first(act2, M, K, N, carve(ws, M, K, N), st, true);
+    const Workspace w = carve(ws, M, K, N);
+    rc = quantize_first(act2, M, K, N, w, st, true);
+    if (rc) return rc;
+    bws = w.batched;
+    bws_bytes = batched_ws_bytes(M, K, N);
+  } else if (M > 16) {
+    rc = batched_ws_bytes(M, K, N) ? check_ws(what, ws, ws_bytes, batched_ws_bytes(M, K, N)) : NEST_OK;
     if (rc) return rc;
   }
   if (M <= 16) {
@@ -905,7 +924,7 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
     const int64_t mc = M - m0 < 144 ? M - m0 : 144;
     rc = nest::launch_verify_batched(act2.qa + m0 * K, act2.sa + m0, (int)mc, (int)K, base, refine, scales,
                                      (int)N, y + m0 * N,
-                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, st);
+                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, bws, bws_bytes, st);
     if (rc) return rc;
   }
   return NEST_OK;
@@ -972,11 +991,17 @@ extern "C" int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t*
                     nullptr, ws, ws_bytes, stream);
 }
 
+extern "C" size_t verify_gemm_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M < 1 || K < 1 || N < 1) return 0;
+  return batched_ws_bytes(M, K, N);
+}
+
 extern "C" int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                            const uint8_t* base, const uint8_t* refine, const float* scales,
-                           int64_t N, int64_t group, float* y, int32_t* acc_dbg, void* stream) {
+                           int64_t N, int64_t group, float* y, int32_t* acc_dbg, void* ws,
+                           size_t ws_bytes, void* stream) {
   return verify_impl("verify_gemm", Act{qa, sa, nullptr}, M, K, base, refine, scales, N, group, y,
-                     acc_dbg, nullptr, 0, stream);
+                     acc_dbg, ws, ws_bytes, stream);
 }
 
 extern "C" int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,

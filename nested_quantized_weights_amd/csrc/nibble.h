@@ -56,9 +56,12 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 // dynamic LDS size).
 int resident_blocks(const void* kernel, int threads, size_t dyn_lds);
 
-// Batched verify (M > 16 rows): one launch for up to 144 rows.
+// Batched verify (M > 16 rows): one launch for up to 144 rows. Shapes whose
+// groups are split over several blocks need verify_batched_ws_bytes(M, K, N)
+// bytes of workspace (counters zero before first use), else none (0).
+size_t verify_batched_ws_bytes(int M, int K, int N);
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
                           const uint8_t* refine, const float* scales, int N, float* y,
-                          int32_t* acc_dbg, hipStream_t st);
+                          int32_t* acc_dbg, void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace nest

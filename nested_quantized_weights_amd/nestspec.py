@@ -54,7 +54,8 @@ _SIGS = {
     "nest_act_quant": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
     "draft_gemv": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "draft_gemv_workspace_size": (_sz, [_i64, _i64]),
-    "verify_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p]),
+    "verify_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "verify_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "verify_accept": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p,
                                      _p, _p, _p, _p, _p, _sz, _p]),
     "verify_accept_workspace_size": (_sz, [_i64, _i64, _i64]),
@@ -274,7 +275,7 @@ def draft_gemv(qa, sa, W, group: int = 128, y=None, want_y: bool = True, argmax:
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def verify_gemm(qa, sa, W, group: int = 128, y=None, acc_dbg: bool = False):
+def verify_gemm(qa, sa, W, group: int = 128, y=None, acc_dbg: bool = False, ws=None):
     """W8A8 over both planes of W (Tiled). Returns y [M][N] (and the int32
     group sums when acc_dbg)."""
     what = "verify_gemm"
@@ -287,8 +288,12 @@ def verify_gemm(qa, sa, W, group: int = 128, y=None, acc_dbg: bool = False):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
+    wsn = lib().verify_gemm_workspace_size(M, K, N)
+    if wsn and (ws is None or ws.numel() < wsn):
+        ws = workspace(wsn, dev, "verify_gemm")
     _check(lib().verify_gemm(_ptr(qa), _ptr(sa), M, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), N,
-                             group, _ptr(y), _ptr(acc), _stream(dev)), what)
+                             group, _ptr(y), _ptr(acc), _ptr(ws) if wsn else None, ws.numel() if wsn else 0,
+                             _stream(dev)), what)
     return (y, acc) if acc_dbg else y
 
 

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for required in ("nest_pack", "nest_act_quant", "draft_gemv", "verify_gemm", "verify_accept",
                      "kv_nest_pack", "kv_nest_attend", "nest_last_error",
                      "draft_gemv_workspace_size", "verify_accept_workspace_size",
-                     "kv_nest_attend_workspace_size"):
+                     "verify_gemm_workspace_size", "kv_nest_attend_workspace_size"):
         assert required in names
 
 
@@ -136,6 +136,24 @@ def test_workspaces_are_checked_without_a_gpu(lib):
     assert g(p, 5, 3584, p, p, p, 37888, 128, p, None, 0, None) == 4  # NEST_EWORKSPACE
     assert b"workspace needs" in lib.nest_last_error()
     assert g(p, 5, 3584, p, p, p, 37888, 128, p, ctypes.c_void_p(272), need, None) == 2  # not 256-aligned
+    # the batched verify splits the groups of few, long weight rows over
+    # several blocks and needs a workspace for their sums (counters + one
+    # 64 x 144 fp32 slot per block); other shapes need none
+    vs = lib.verify_gemm_workspace_size
+    vs.restype = ctypes.c_size_t
+    vs.argtypes = [ctypes.c_int64] * 3
+    down = vs(144, 14336, 4096)
+    assert down >= 64 * 2 * 64 * 144 * 4
+    assert vs(5, 14336, 4096) == 0 and vs(144, 4096, 14336) == 0 and vs(144, 4096, 4096) == 0
+    assert vs(300, 14336, 4096) == down  # launches of up to 144 rows share it
+    assert sz(144, 14336, 4096) >= down + 144 * 14336  # the fp32 path: codes + the same workspace
+    v = lib.verify_gemm
+    v.restype = ctypes.c_int
+    v.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 3 + \
+        [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert v(p, p, 144, 14336, p, p, p, 4096, 128, p, None, None, 0, None) == 4  # NEST_EWORKSPACE
+    assert b"workspace needs" in lib.nest_last_error()
+    assert v(p, p, 144, 14336, p, p, p, 4096, 128, p, None, p, down - 1, None) == 4
     a = lib.kv_nest_append
     a.restype = ctypes.c_int
     a.argtypes = [ctypes.POINTER(_KV)] + [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]

@@ -159,9 +159,15 @@ def test_draft_gemv(ns, oracle, N, K, M):
 # each); K = 128 leaves one part of a block's groups empty; (130, 384, 100)
 # has an odd group count and ragged row and activation tiles; (5511, 256,
 # 144) has more row blocks than three parts of them fit in one round, so it
-# takes two-tile blocks (345 tiles, the last one partial).
+# takes two-tile blocks (345 tiles, the last one partial). Few row blocks
+# over 64 groups or more split the groups over four blocks per row block
+# (the workspace path): (640, 8192, 144) with whole tiles; (300, 9216, 37)
+# with a ragged last tile and three-part blocks; (200, 8320, 100) with 65
+# groups (slices of 16, 16, 16 and 17); (130, 16384, 150) in two launches
+# (144 + 6 rows) that share the workspace.
 BATCHED_SHAPES = [(50, 512, 17), (200, 256, 144), (64, 384, 150), (200, 2048, 144), (1000, 1024, 144),
-                  (64, 128, 33), (130, 384, 100), (5511, 256, 144)]
+                  (64, 128, 33), (130, 384, 100), (5511, 256, 144),
+                  (640, 8192, 144), (300, 9216, 37), (200, 8320, 100), (130, 16384, 150)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMV_SHAPES + BATCHED_SHAPES)
@@ -177,15 +183,19 @@ def test_verify_gemm(ns, oracle, N, K, M):
     assert np.array_equal(host(y_nodbg).view(np.uint32), host(y).view(np.uint32))
 
 
-def test_batched_verify_repeats(ns, oracle):
-    # the batched kernel keeps no state between calls: calls in a row agree
-    # bit for bit, also after a call with other shapes on the same stream
-    base, refine, scales, qa, sa = _layer(oracle, 300, 4096, 144, (11,))
+@pytest.mark.parametrize("N,K", [(300, 4096), (300, 9216)])
+def test_batched_verify_repeats(ns, oracle, N, K):
+    # the batched kernel keeps no state between calls (the group split's
+    # counters return to zero): calls in a row agree bit for bit, also after
+    # calls with other shapes on the same stream and workspace
+    base, refine, scales, qa, sa = _layer(oracle, N, K, 144, (11,))
     W = tiled(ns, base, refine, scales)
     y1 = host(ns.verify_gemm(dev(qa), dev(sa), W))
     b2, r2, s2, qa2, sa2 = _layer(oracle, 70, 1024, 40, (12,))
+    b3, r3, s3, qa3, sa3 = _layer(oracle, 900, 8192, 20, (13,))
     ns.verify_gemm(dev(qa2), dev(sa2), tiled(ns, b2, r2, s2))
     for _ in range(3):
+        ns.verify_gemm(dev(qa3), dev(sa3), tiled(ns, b3, r3, s3))
         y2 = host(ns.verify_gemm(dev(qa), dev(sa), W))
         assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)

@@ -2,8 +2,8 @@
 // base and the refinement plane) for more than 16 activation rows, e.g. 16
 // sequences x (k+1) = 144 rows: y = sa * fold_g s/16 * (sum q_a (16 q_b + q_r)).
 //
-// A block owns WR 16-row weight tiles (four, i.e. 64 rows; two for some
-// shapes), a range of the activation rows (CTP column tiles of 16) and all
+// A block owns WR 16-row weight tiles (four, i.e. 64 rows; two to seven for
+// some shapes), a range of the activation rows (CTP column tiles of 16) and all
 // groups. Its last wave only copies int8 activation rows from HBM/L2 into an
 // LDS ring (direct 16-byte loads to LDS, whole 128-byte rows of a group, two
 // groups ahead). The WR WK compute waves (which hide each other's MFMA and
@@ -35,7 +35,7 @@ namespace {
 using nest::kGroup;
 
 constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
-// WR 16-row weight tiles per block (a template parameter, 4 or 2) and WK
+// WR 16-row weight tiles per block (a template parameter, 2 and 4 to 7) and WK
 // parts of the groups: WR WK compute waves, one per (tile, part), plus the
 // copy wave
 constexpr int threads_for(int wk, int wr) { return (wr * wk + 1) * 64; }
@@ -464,9 +464,29 @@ int launch_ctp(const GemmArgs& a, int ctp, int blocks, hipStream_t st) {
   }
 }
 
+// Wide blocks (five to seven tiles) always carry four or more column tiles,
+// so two parts of the groups: 11 to 15 waves.
+template <int WR, bool DBG>
+int launch_ctp_wide(const GemmArgs& a, int ctp, int blocks, hipStream_t st) {
+  switch (ctp) {
+    case 4: return launch_gemm<4, 2, WR, DBG>(a, blocks, st);
+    case 5: return launch_gemm<5, 2, WR, DBG>(a, blocks, st);
+    case 6: return launch_gemm<6, 2, WR, DBG>(a, blocks, st);
+    case 7: return launch_gemm<7, 2, WR, DBG>(a, blocks, st);
+    case 8: return launch_gemm<8, 2, WR, DBG>(a, blocks, st);
+    default: return launch_gemm<9, 2, WR, DBG>(a, blocks, st);
+  }
+}
+
 template <bool DBG>
 int launch_wr(const GemmArgs& a, int wr, int ctp, int blocks, hipStream_t st) {
-  return wr == 2 ? launch_ctp<2, DBG>(a, ctp, blocks, st) : launch_ctp<4, DBG>(a, ctp, blocks, st);
+  switch (wr) {
+    case 2: return launch_ctp<2, DBG>(a, ctp, blocks, st);
+    case 5: return launch_ctp_wide<5, DBG>(a, ctp, blocks, st);
+    case 6: return launch_ctp_wide<6, DBG>(a, ctp, blocks, st);
+    case 7: return launch_ctp_wide<7, DBG>(a, ctp, blocks, st);
+    default: return launch_ctp<4, DBG>(a, ctp, blocks, st);
+  }
 }
 
 int device_cus() {
@@ -482,7 +502,10 @@ int device_cus() {
   return cus;
 }
 
-// Work split: four weight tiles per block. Few row blocks (under half the
+// Work split: four weight tiles per block (five to seven when more tiles
+// than four rounds' worth of CUs would need a second round: LLaMA-3-8B
+// gate|up as one 28672 x 4096 matrix at 144 rows, 51.5 -> 39.9 us with
+// seven-tile blocks in one round). Few row blocks (under half the
 // CUs) over long rows (64 groups or more) split the groups over S blocks
 // per row block, each with all activation rows: every block stages a
 // quarter (S = 4) of the activation bytes and streams a quarter of the
@@ -521,6 +544,11 @@ Plan plan_batched(int M, int K, int N, int cus) {
     if (row_blocks * p.P > cus && (T + 1) / 2 <= cus) {
       p.WR = 2;
       p.P = 1;
+    } else if (p.P == 1 && CT >= 4 && T > 4 * cus && T <= 7 * cus) {
+      // more than one round of four-tile blocks: the fewest tiles per block
+      // (five to seven) that fit one round, which also stages the
+      // activations once per 80 to 112 weight rows instead of 64
+      p.WR = (T + cus - 1) / cus;
     }
   }
   p.row_blocks = (T + p.WR - 1) / p.WR;

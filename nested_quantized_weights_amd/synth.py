@@ -17,7 +17,8 @@ Workloads (names give what they are):
     rates that SpecQuant's Table II and BitNest's abstract report.
   * ``llama3-8b_batched_verify``: 16 sequences x 9 rows = 144-row verify over
     the LLaMA-3-8B-shaped linears (hidden 4096, QKV 4096->6144, O
-    4096->4096, gate and up 4096->14336, down 14336->4096), 32 layers.
+    4096->4096, gate and up 4096->14336 each, stored as one 28672 x 4096
+    matrix since both read the same rows, down 14336->4096), 32 layers.
   * ``kv_32k``: nested KV cache with 32 q heads / 8 kv heads, d=128 and a
     32768-token context. bf16 queries; 1 draft query; 9 verify queries.
 
@@ -47,8 +48,8 @@ WORKLOADS = {
                            "alphas": (0.58, 0.66, 0.95), "rounds": 10000, "pool": 16},
     "llama3-8b_batched_verify": {
         "hidden": 4096, "group": 128, "layers": 32, "sequences": 16, "rows_per_seq": 9,
-        "linears": {"qkv": (6144, 4096), "o": (4096, 4096), "gate": (14336, 4096),
-                    "up": (14336, 4096), "down": (4096, 14336)},
+        "linears": {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096),
+                    "down": (4096, 14336)},
     },
     "kv_32k": {"q_heads": 32, "kv_heads": 8, "head_dim": 128, "context": 32768,
                "block": 128, "draft_queries": 1, "verify_queries": 9},

@@ -11,12 +11,12 @@ head and nested KV cache. A step is one full round at k = 4:
                         LM head (152064x3584) with the fused argmax that
                         gives the draft token;
   one verify pass:      verify_gemm over both planes for the k+1 rows;
-                        kv_nest_append of the target's K/V for the k+1
-                        positions (over the draft's); kv_nest_attend_exact
-                        over the full view: each of the k+1 queries sees the
-                        cache as a one-token pass at its position would, in
-                        one launch (so the round keeps target-only decoding's
-                        tokens exactly); verify_accept on the
+                        kv_nest_append_attend_exact: the target's K/V for
+                        the k+1 positions (over the draft's) appended, and
+                        the exact attention over the full view, where each
+                        of the k+1 queries sees the cache as a one-token pass
+                        at its position would (so the round keeps
+                        target-only decoding's tokens exactly); verify_accept on the
                         LM head (exact fold, fused argmax, greedy accept of
                         the draft tokens).
 The per-token int8 quantization of each linear's fp32 input is part of the
@@ -298,15 +298,14 @@ class Round:
             calls.append((L.verify_gemm_x, (p(xv), k + 1, K, p(d["base"][n]), p(d["refine"][n]),
                                             p(d["scales"][n]), N, 128, p(y[n]), *gw, st), "verify_" + n))
             if n == "qkv":
-                # the target's K/V for all k+1 positions overwrite the draft's, then attend (full view)
+                # the target's K/V for all k+1 positions overwrite the draft's, and the k+1 queries
+                # attend (full view): one call, the append folded into the open-block kernel
                 vk, vvv = d["vk"][:, :k + 1].contiguous(), d["vv"][:, :k + 1].contiguous()
                 keep += [vk, vvv]
-                calls.append((L.kv_nest_append, (ctypes.byref(self.kvs), p(sh[0]), p(sh[1]), p(vk),
-                                                 p(vvv), lp, base_pos, k + 1, st), "append_verify"))
                 q = d["qv"][:k + 1]
-                calls.append((L.kv_nest_attend_exact, (p(q), k + 1, hq, ctypes.byref(self.kvs), p(sh[0]),
-                                                       p(sh[1]), lp, base_pos + k + 1, 1, p(att_out), p(ws_att),
-                                                       ws_att_n, st), "attend_verify"))
+                calls.append((L.kv_nest_append_attend_exact, (p(q), k + 1, hq, ctypes.byref(self.kvs), p(sh[0]),
+                                                              p(sh[1]), p(vk), p(vvv), lp, base_pos, 1, p(att_out),
+                                                              p(ws_att), ws_att_n, st), "attend_verify"))
         xh = d["xv"]["head"][:k + 1]
         if sampled:
             calls.append((L.verify_gemm_x, (p(xh), k + 1, H, p(d["base"]["head"]), p(d["refine"]["head"]),

@@ -464,6 +464,34 @@ int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,
                          int64_t ctx_len, int view, float* out, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* kv_nest_append_attend_exact -- a verify pass's append and exact attention
+ * in one call (the same two steps of "How Speculative Decoding Speeds Up
+ * Inference", "Drafting and checking tokens", step 2): the result, the
+ * planes, scales and shadows afterwards are bit-identical to
+ *   kv_nest_append(kv, shadow_k, shadow_v, k_new, v_new, pos_dev, pos, n)
+ *   kv_nest_attend_exact(q, n, Hq, kv, shadow_k, shadow_v, pos_dev, pos + n, ...)
+ * on the same stream, with one launch fewer: the append's codes, scales and
+ * shadow rows are written by the kernel that rebuilds the queries' open
+ * blocks, which reads the new tokens from k_new / v_new.
+ *   k_new, v_new  fp32 [Hkv][n][d], 16-byte aligned: the n new tokens at
+ *                 positions pos .. pos + n - 1 (plus *pos_dev when given)
+ *   q             bf16 bits [n][Hq][d]: query i at position pos + i
+ *   the rest as for kv_nest_attend_exact with nq = n and ctx_len = pos + n;
+ *   ws is kv_nest_attend_exact_workspace_size(n, Hq, Hkv, d, L).
+ * With a device position whose append would not fit in the capacity,
+ * nothing is appended (as kv_nest_append) and the queries attend as
+ * kv_nest_attend_exact would after it. With n == 1: the append, then
+ * kv_nest_attend's one-query launch (no launch is saved).
+ * Requires 1 <= n <= block, pos + n <= capacity without pos_dev and
+ * -capacity <= pos <= capacity, pos + n >= 0 with it; both refinement
+ * planes. Errors: as kv_nest_attend_exact. */
+int kv_nest_append_attend_exact(const uint16_t* q, int64_t n, int64_t n_q_heads,
+                                const nest_kv* kv, float* shadow_k,
+                                float* shadow_v, const float* k_new,
+                                const float* v_new, const int32_t* pos_dev,
+                                int64_t pos, int view, float* out, void* ws,
+                                size_t ws_bytes, void* stream);
+
 size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads,
                                      int64_t n_kv_heads, int64_t head_dim,
                                      int64_t ctx_len);

@@ -65,6 +65,16 @@ struct AttArgs {
   const float *shk, *shv;  // exact mode: fp32 shadows [Hkv][2][block][d] of the two newest blocks
   uint8_t* open;           // exact mode: [nq][Hkv] rebuilt open blocks, 4 planes each
   float* open_sc;          // exact mode: [nq][Hkv][2] their scales (K, V)
+  // exact mode with the append folded in (kv_nest_append_attend_exact): the
+  // pass's nq new tokens [Hkv][nq][d] (null otherwise), and what the append
+  // writes: the touched blocks' planes and scales and the new tokens' shadow
+  // rows. The first new position is ctx - nq; an append that would not fit
+  // in the cache writes nothing (the pass then sees the planes and shadow as
+  // they were), as kv_nest_append does.
+  const float *knew, *vnew;
+  uint8_t *w_kb, *w_kr, *w_vb, *w_vr;
+  float *w_ks, *w_vs, *w_shk, *w_shv;
+  int zbase;               // open_block_kernel: layer index of blockIdx.z = 0 (the append alone: nq)
   int qpack;               // exact mode: queries per workgroup (qpack * grp <= 16)
   int bpw, nchunk;     // blocks per workgroup, chunks (workgroups) per head
   float* part_ml;      // [Hkv][nchunk][R][2]  (max in log2 domain, sum)
@@ -452,23 +462,55 @@ constexpr int kOpenPlane = kBlk * kD / 2;  // bytes of one plane of one block
 constexpr int kOpenSplit = 8;              // workgroups per (query, kv head, K or V)
 static_assert(kOpenSplit * 256 * 8 == kBlk * kD, "one word of each plane per thread");
 
+// With the append folded in (a.knew set), tokens at or past the first new
+// position come from the new values rather than the shadow, and the grid
+// carries four more workgroup layers (z = 2 nq .. 2 nq + 3): the append of
+// the pass's tokens to the (at most two) blocks they touch, K or V, each
+// workgroup the same eighth of the codes as above, quantized over the
+// block's tokens up to the pass's last one, with the scale and its share of
+// the new tokens' shadow rows. The rebuilds read only older tokens from the
+// shadow, and no workgroup here reads the planes, so the layers are
+// independent of one another.
 __global__ void __launch_bounds__(256) open_block_kernel(AttArgs a) {
   __shared__ float red[4];
-  const int part = blockIdx.x, h = blockIdx.y, z = blockIdx.z >> 1;
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int zz = a.zbase + (static_cast<int>(blockIdx.z) >> 1);
   const bool is_v = (blockIdx.z & 1) != 0;
+  const bool append = zz >= a.nq;  // an append layer (only when a.knew is set)
   const int Hkv = a.Hq / a.grp;
-  const int pos = live_ctx(a) - a.nq + z;
-  const int blk = pos / kBlk, valid = pos - blk * kBlk + 1;
-  const float* src = (is_v ? a.shv : a.shk) + (static_cast<size_t>(h) * 2 + (blk & 1)) * kBlk * kD;
-  // 1. max |x| over tokens [0, valid) (token-major, contiguous); all loads
-  // are issued together
+  const int ctx = live_ctx(a), pos0 = ctx - a.nq;  // the pass's first position
+  // the append happened (or happens here) only if the tokens fit
+  const bool fits = a.knew && (!a.ctx_dev || static_cast<long long>(a.ctx) + *a.ctx_dev == ctx);
+  if (append && !fits) return;
+  // the block and its last token: query zz's own position, or for an append
+  // layer the pass's last token in the first or second block it touches
+  int blk, pos;
+  if (append) {
+    blk = pos0 / kBlk + (zz - a.nq);
+    if (blk * kBlk > ctx - 1) return;  // the second block, not touched
+    pos = min(ctx - 1, blk * kBlk + kBlk - 1);
+  } else {
+    pos = pos0 + zz;
+    blk = pos / kBlk;
+  }
+  const int t0 = blk * kBlk, valid = pos - t0 + 1;
+  const float* sh = (is_v ? a.shv : a.shk) + (static_cast<size_t>(h) * 2 + (blk & 1)) * kBlk * kD;
+  // tokens [0, old) of the block from the shadow, [old, valid) new (new
+  // token t0 + t - pos0 of the pass)
+  const int old = fits ? max(0, min(valid, pos0 - t0)) : valid;
+  const float* nwh = fits ? (is_v ? a.vnew : a.knew) + static_cast<size_t>(h) * a.nq * kD : nullptr;
+  auto row_ptr = [&](int t) {  // token t of the block
+    return t < old ? sh + t * kD : nwh + static_cast<ptrdiff_t>(t0 + t - pos0) * kD;
+  };
+  // 1. max |x| over tokens [0, valid) (token-major); all loads are issued
+  // together
   const int n4 = valid * (kD / 4);
   float m = 0.0f;
 #pragma unroll
   for (int u = 0; u < kBlk * kD / 4 / 256; ++u) {
     const int i = static_cast<int>(threadIdx.x) + 256 * u;
     if (i < n4) {
-      const float4 v = reinterpret_cast<const float4*>(src)[i];
+      const float4 v = reinterpret_cast<const float4*>(row_ptr(i / (kD / 4)))[i % (kD / 4)];
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
   }
@@ -477,8 +519,14 @@ __global__ void __launch_bounds__(256) open_block_kernel(AttArgs a) {
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = m / 7.0f, s16 = s * 0.0625f, rs = 1.0f / s, rs16 = 1.0f / s16;
-  const size_t slot = static_cast<size_t>(z) * Hkv + h;
-  if (part == 0 && threadIdx.x == 0) a.open_sc[slot * 2 + (is_v ? 1 : 0)] = s;
+  const size_t slot = static_cast<size_t>(zz) * Hkv + h;
+  const size_t hb = static_cast<size_t>(h) * a.nb + blk;
+  if (part == 0 && threadIdx.x == 0) {
+    if (append)
+      (is_v ? a.w_vs : a.w_ks)[hb] = s;
+    else
+      a.open_sc[slot * 2 + (is_v ? 1 : 0)] = s;
+  }
   // 2. word w of each plane: elements 8w .. 8w + 7 in plane order (K: token
   // 8w / 128, dims 8w % 128 ..; V: dim 8w / 128, tokens 8w % 128 ..)
   const int w = part * 256 + static_cast<int>(threadIdx.x);
@@ -486,11 +534,12 @@ __global__ void __launch_bounds__(256) open_block_kernel(AttArgs a) {
   float x[8];
   if (is_v) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = c0 + j < valid ? src[(c0 + j) * kD + row] : 0.0f;
+    for (int j = 0; j < 8; ++j) x[j] = c0 + j < valid ? row_ptr(c0 + j)[row] : 0.0f;
   } else {
-    const float4 lo = reinterpret_cast<const float4*>(src + row * kD + c0)[0];
-    const float4 hi = reinterpret_cast<const float4*>(src + row * kD + c0)[1];
     const bool in = row < valid;
+    const float* src = row_ptr(in ? row : 0) + c0;
+    const float4 lo = reinterpret_cast<const float4*>(src)[0];
+    const float4 hi = reinterpret_cast<const float4*>(src)[1];
     x[0] = in ? lo.x : 0.0f; x[1] = in ? lo.y : 0.0f; x[2] = in ? lo.z : 0.0f; x[3] = in ? lo.w : 0.0f;
     x[4] = in ? hi.x : 0.0f; x[5] = in ? hi.y : 0.0f; x[6] = in ? hi.z : 0.0f; x[7] = in ? hi.w : 0.0f;
   }
@@ -501,6 +550,18 @@ __global__ void __launch_bounds__(256) open_block_kernel(AttArgs a) {
     nest::nest_codes_fast(x[j], s, s16, rs, rs16, qb, qr);
     wb |= static_cast<uint32_t>(qb & 15) << (4 * j);
     wr |= static_cast<uint32_t>(qr & 15) << (4 * j);
+  }
+  if (append) {
+    // the cache's block: K planes [token][64 B] from (h cap + t0) * 64, V
+    // planes [dim][64 B] from hb * 128 * 64 (the slot layout)
+    const size_t off = is_v ? hb * kD * (kBlk / 2) : (static_cast<size_t>(h) * a.cap + t0) * (kD / 2);
+    reinterpret_cast<uint32_t*>((is_v ? a.w_vb : a.w_kb) + off)[w] = wb;
+    reinterpret_cast<uint32_t*>((is_v ? a.w_vr : a.w_kr) + off)[w] = wr;
+    // this workgroup's share of the new tokens' shadow rows [old, valid)
+    float* shw = (is_v ? a.w_shv : a.w_shk) + (static_cast<size_t>(h) * 2 + (blk & 1)) * kBlk * kD;
+    for (int i = (old * kD) / 4 + w; i < (valid * kD) / 4; i += kOpenSplit * 256)
+      reinterpret_cast<float4*>(shw)[i] = reinterpret_cast<const float4*>(row_ptr(i / (kD / 4)))[i % (kD / 4)];
+    return;
   }
   uint8_t* base = a.open + (slot * 4 + (is_v ? 2 : 0)) * kOpenPlane;
   reinterpret_cast<uint32_t*>(base)[w] = wb;
@@ -1096,11 +1157,14 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
   return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);
 }
 
-extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
-                                    const float* shadow_k, const float* shadow_v, const int32_t* ctx_dev,
-                                    int64_t ctx_len, int view, float* out, void* ws, size_t ws_bytes,
-                                    void* stream) {
-  const char* what = "kv_nest_attend_exact";
+namespace {
+
+// kv_nest_attend_exact, and with k_new set kv_nest_append_attend_exact: the
+// append of the nq new tokens folded into the open-block kernel.
+int attend_exact_impl(const char* what, const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
+                      float* shadow_k, float* shadow_v, const float* k_new, const float* v_new,
+                      const int32_t* ctx_dev, int64_t ctx_len, int view, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
   AttArgs a;
   int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, kBlk * 16, a);
   if (rc) return rc;
@@ -1110,13 +1174,35 @@ extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_h
   a.shk = shadow_k;
   a.shv = shadow_v;
   const int64_t Hkv = kv->n_kv_heads;
+  hipStream_t st = nest::as_stream(stream);
+  if (k_new) {
+    if (!kv->k_refine || !kv->v_refine)
+      return nest::fail(NEST_EINVAL, "%s: the append writes both refinement planes", what);
+    if (!nest::aligned16(k_new) || !nest::aligned16(v_new) || !nest::aligned16(shadow_k) ||
+        !nest::aligned16(shadow_v) || !nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))
+      return nest::fail(NEST_EALIGN, "%s: new tokens, shadows and planes must be 16-byte aligned", what);
+    a.knew = k_new;
+    a.vnew = v_new;
+    a.w_kb = const_cast<uint8_t*>(kv->k_base); a.w_kr = const_cast<uint8_t*>(kv->k_refine);
+    a.w_vb = const_cast<uint8_t*>(kv->v_base); a.w_vr = const_cast<uint8_t*>(kv->v_refine);
+    a.w_ks = const_cast<float*>(kv->k_scale); a.w_vs = const_cast<float*>(kv->v_scale);
+    a.w_shk = shadow_k;
+    a.w_shv = shadow_v;
+  }
   if (nq == 1) {
-    // one query: the append of its token left its block quantized over
-    // exactly the tokens up to it, so the planes are what it must see
+    // one query: the append of its token leaves its block quantized over
+    // exactly the tokens up to it, so the planes are what it must see (the
+    // folded append runs alone first: the append layers of the open-block
+    // kernel)
+    if (k_new) {
+      a.zbase = 1;
+      open_block_kernel<<<dim3(kOpenSplit, static_cast<unsigned>(Hkv), 4), 256, 0, st>>>(a);
+      rc = nest::check_launch("kv_nest_append_attend_exact(append)");
+      if (rc) return rc;
+    }
     const Plan p = make_plan(1, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
     rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, p.ws);
     if (rc) return rc;
-    hipStream_t st = nest::as_stream(stream);
     return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);
   }
   // every query takes the split of a one-query call (its workgroups write
@@ -1128,8 +1214,8 @@ extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_h
   if (rc) return rc;
   a.open = static_cast<uint8_t*>(ws) + e.open_off;
   a.open_sc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + e.sc_off);
-  hipStream_t st = nest::as_stream(stream);
-  open_block_kernel<<<dim3(kOpenSplit, static_cast<unsigned>(Hkv), static_cast<unsigned>(2 * nq)), 256, 0, st>>>(a);
+  const unsigned layers = static_cast<unsigned>(2 * nq + (k_new ? 4 : 0));
+  open_block_kernel<<<dim3(kOpenSplit, static_cast<unsigned>(Hkv), layers), 256, 0, st>>>(a);
   rc = nest::check_launch("kv_nest_attend_exact(open blocks)");
   if (rc) return rc;
   // as many queries per workgroup as their GQA groups fit in 16 rows
@@ -1145,4 +1231,30 @@ extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_h
   if (rc) return rc;
   combine_kernel<<<dim3(a.R, Hkv), 1024, 0, st>>>(a);
   return nest::check_launch("kv_nest_attend_exact(combine)");
+}
+
+}  // namespace
+
+extern "C" int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
+                                    const float* shadow_k, const float* shadow_v, const int32_t* ctx_dev,
+                                    int64_t ctx_len, int view, float* out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return attend_exact_impl("kv_nest_attend_exact", q, nq, n_q_heads, kv, const_cast<float*>(shadow_k),
+                           const_cast<float*>(shadow_v), nullptr, nullptr, ctx_dev, ctx_len, view, out, ws,
+                           ws_bytes, stream);
+}
+
+extern "C" int kv_nest_append_attend_exact(const uint16_t* q, int64_t n, int64_t n_q_heads, const nest_kv* kv,
+                                           float* shadow_k, float* shadow_v, const float* k_new,
+                                           const float* v_new, const int32_t* pos_dev, int64_t pos, int view,
+                                           float* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* what = "kv_nest_append_attend_exact";
+  if (!k_new || !v_new) return nest::fail(NEST_EINVAL, "%s: null new tokens", what);
+  if (!kv) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (n < 1 || n > kBlk || (!pos_dev && (pos < 0 || pos + n > kv->capacity)) ||
+      (pos_dev && (pos < -kv->capacity || pos > kv->capacity)))
+    return nest::fail(NEST_EINVAL, "%s: need pos >= 0, 1 <= n <= block, pos + n <= capacity (pos=%lld n=%lld)",
+                      what, (long long)pos, (long long)n);
+  return attend_exact_impl(what, q, n, n_q_heads, kv, shadow_k, shadow_v, k_new, v_new, pos_dev, pos + n, view,
+                           out, ws, ws_bytes, stream);
 }

@@ -16,12 +16,12 @@ rounds can be issued back to back without the host reading anything
 (run_rounds); generate() reads each round's count only to know when to stop.
 
 A target pass over the k+1 positions of a round attends in one of three ways:
-  exact     one append of the k+1 tokens, then kv_nest_attend_exact: one
-            launch in which each query sees the cache a one-token pass at
-            its position would see (its open block quantized over its own
-            prefix); with row-independent layers the round then emits
-            exactly the tokens and logits of target-only decoding ("The
-            same output as the large model alone");
+  exact     kv_nest_append_attend_exact: the append of the k+1 tokens and
+            one attention launch in which each query sees the cache a
+            one-token pass at its position would see (its open block
+            quantized over its own prefix); with row-independent layers the
+            round then emits exactly the tokens and logits of target-only
+            decoding ("The same output as the large model alone");
   stepwise  position by position (append one token, attend with its
             query): the same result with k+1 launches of each;
   batched   one append and one attention of all k+1 queries, where the open
@@ -96,14 +96,14 @@ class Decoder:
                 for i in range(M):
                     ns.kv_nest_append(kv, sh, k[i].unsqueeze(1), v[i].unsqueeze(1), off + i, pos_dev=L)
                     ns.kv_nest_attend(q[i:i + 1], kv, off + i + 1, view, out=att[i:i + 1], ctx_dev=L)
+            elif mode == "exact" and M > 1:
+                # the append and the exact attention in one call
+                att = ns.kv_nest_append_attend_exact(q, kv, sh, k, v, off, view, pos_dev=L)
             else:
                 ns.kv_nest_append(kv, sh, k, v, off, pos_dev=L)
                 # one position: the append quantized its block over exactly
                 # the tokens up to it, so every mode is the plain attention
-                if mode == "exact" and M > 1:
-                    att = ns.kv_nest_attend_exact(q, kv, sh, off + M, view, ctx_dev=L)
-                else:
-                    att = ns.kv_nest_attend(q, kv, off + M, view, ctx_dev=L)
+                att = ns.kv_nest_attend(q, kv, off + M, view, ctx_dev=L)
             o = self._linear(att.view(M, Hq * d), lw["o"], draft)
             ns.add_rmsnorm(x, o, lw["norm_mlp"], eps, out=h)
             dn = self._linear(ns.swiglu(self._linear(h, lw["gate_up"], draft)), lw["down"], draft)

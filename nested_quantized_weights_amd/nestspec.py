@@ -85,6 +85,8 @@ _SIGS = {
     "kv_nest_attend_exact_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "kv_nest_attend_exact": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _p, _p, _i64, ctypes.c_int,
                                             _p, _p, _sz, _p]),
+    "kv_nest_append_attend_exact": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_KV), _p, _p, _p, _p, _p,
+                                                   _i64, ctypes.c_int, _p, _p, _sz, _p]),
     "nest_sample": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_float, _p, _p, _p, _sz, _p]),
     "nest_sample_workspace_size": (_sz, [_i64, _i64]),
     "verify_sample": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p, _p,
@@ -526,6 +528,36 @@ def kv_nest_attend_exact(q: torch.Tensor, kv: NestKV, shadow, ctx_len: int, view
     _check(lib().kv_nest_attend_exact(_ptr(q), nq, Hq, ctypes.byref(s), _ptr(shadow[0]), _ptr(shadow[1]),
                                       _ptr(ctx_dev), int(ctx_len), int(view), _ptr(out), _ptr(ws), ws.numel(),
                                       _stream(dev)), what)
+    return out
+
+
+def kv_nest_append_attend_exact(q: torch.Tensor, kv: NestKV, shadow, k_new: torch.Tensor, v_new: torch.Tensor,
+                                pos: int, view: int, out=None, ws=None, pos_dev=None):
+    """kv_nest_append of the n new tokens k_new, v_new [Hkv][n][d] at
+    positions pos.. (plus the device int32 pos_dev when given), then
+    kv_nest_attend_exact of q [n][Hq][d] (bf16 bits) at length pos + n, in
+    one call with one launch fewer. Returns fp32 [n][Hq][d]."""
+    what = "kv_nest_append_attend_exact"
+    if not isinstance(q, torch.Tensor) or not q.is_cuda or not q.is_contiguous():
+        raise NestError(f"{what}: q must be a contiguous CUDA tensor")
+    if q.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise NestError(f"{what}: q must hold bf16 bit patterns")
+    _dev(k_new, torch.float32, what, "k_new")
+    _dev(v_new, torch.float32, what, "v_new")
+    if pos_dev is not None:
+        _dev(pos_dev, torch.int32, what, "pos_dev")
+    n, Hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((n, Hq, d), dtype=torch.float32, device=dev)
+    plan_len = kv.capacity if pos_dev is not None else int(pos) + n
+    wsn = lib().kv_nest_attend_exact_workspace_size(n, Hq, kv.n_kv_heads, d, plan_len)
+    if ws is None or ws.numel() < wsn:
+        ws = workspace(max(wsn, 256), dev, "attend")
+    s = kv.struct()
+    _check(lib().kv_nest_append_attend_exact(_ptr(q), n, Hq, ctypes.byref(s), _ptr(shadow[0]), _ptr(shadow[1]),
+                                             _ptr(k_new), _ptr(v_new), _ptr(pos_dev), int(pos), int(view),
+                                             _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), what)
     return out
 
 

@@ -1159,6 +1159,34 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
 
 namespace {
 
+// Shared checks and arguments of the appends folded into an attention call.
+int attach_append(const char* what, AttArgs& a, const nest_kv* kv, float* shadow_k, float* shadow_v,
+                  const float* k_new, const float* v_new) {
+  if (!shadow_k || !shadow_v || !k_new || !v_new) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (!kv->k_refine || !kv->v_refine)
+    return nest::fail(NEST_EINVAL, "%s: the append writes both refinement planes", what);
+  if (!nest::aligned16(k_new) || !nest::aligned16(v_new) || !nest::aligned16(shadow_k) ||
+      !nest::aligned16(shadow_v) || !nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))
+    return nest::fail(NEST_EALIGN, "%s: new tokens, shadows and planes must be 16-byte aligned", what);
+  a.knew = k_new;
+  a.vnew = v_new;
+  a.w_kb = const_cast<uint8_t*>(kv->k_base); a.w_kr = const_cast<uint8_t*>(kv->k_refine);
+  a.w_vb = const_cast<uint8_t*>(kv->v_base); a.w_vr = const_cast<uint8_t*>(kv->v_refine);
+  a.w_ks = const_cast<float*>(kv->k_scale); a.w_vs = const_cast<float*>(kv->v_scale);
+  a.w_shk = shadow_k;
+  a.w_shv = shadow_v;
+  return NEST_OK;
+}
+
+int check_append_pos(const char* what, const nest_kv* kv, const int32_t* pos_dev, int64_t pos, int64_t n) {
+  if (!kv) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (n < 1 || n > kBlk || (!pos_dev && (pos < 0 || pos + n > kv->capacity)) ||
+      (pos_dev && (pos < -kv->capacity || pos > kv->capacity || pos + n < 0)))
+    return nest::fail(NEST_EINVAL, "%s: need pos >= 0, 1 <= n <= block, pos + n <= capacity (pos=%lld n=%lld)",
+                      what, (long long)pos, (long long)n);
+  return NEST_OK;
+}
+
 // kv_nest_attend_exact, and with k_new set kv_nest_append_attend_exact: the
 // append of the nq new tokens folded into the open-block kernel.
 int attend_exact_impl(const char* what, const uint16_t* q, int64_t nq, int64_t n_q_heads, const nest_kv* kv,
@@ -1176,18 +1204,8 @@ int attend_exact_impl(const char* what, const uint16_t* q, int64_t nq, int64_t n
   const int64_t Hkv = kv->n_kv_heads;
   hipStream_t st = nest::as_stream(stream);
   if (k_new) {
-    if (!kv->k_refine || !kv->v_refine)
-      return nest::fail(NEST_EINVAL, "%s: the append writes both refinement planes", what);
-    if (!nest::aligned16(k_new) || !nest::aligned16(v_new) || !nest::aligned16(shadow_k) ||
-        !nest::aligned16(shadow_v) || !nest::aligned16(kv->k_refine) || !nest::aligned16(kv->v_refine))
-      return nest::fail(NEST_EALIGN, "%s: new tokens, shadows and planes must be 16-byte aligned", what);
-    a.knew = k_new;
-    a.vnew = v_new;
-    a.w_kb = const_cast<uint8_t*>(kv->k_base); a.w_kr = const_cast<uint8_t*>(kv->k_refine);
-    a.w_vb = const_cast<uint8_t*>(kv->v_base); a.w_vr = const_cast<uint8_t*>(kv->v_refine);
-    a.w_ks = const_cast<float*>(kv->k_scale); a.w_vs = const_cast<float*>(kv->v_scale);
-    a.w_shk = shadow_k;
-    a.w_shv = shadow_v;
+    rc = attach_append(what, a, kv, shadow_k, shadow_v, k_new, v_new);
+    if (rc) return rc;
   }
   if (nq == 1) {
     // one query: the append of its token leaves its block quantized over
@@ -1250,11 +1268,8 @@ extern "C" int kv_nest_append_attend_exact(const uint16_t* q, int64_t n, int64_t
                                            float* out, void* ws, size_t ws_bytes, void* stream) {
   const char* what = "kv_nest_append_attend_exact";
   if (!k_new || !v_new) return nest::fail(NEST_EINVAL, "%s: null new tokens", what);
-  if (!kv) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
-  if (n < 1 || n > kBlk || (!pos_dev && (pos < 0 || pos + n > kv->capacity)) ||
-      (pos_dev && (pos < -kv->capacity || pos > kv->capacity)))
-    return nest::fail(NEST_EINVAL, "%s: need pos >= 0, 1 <= n <= block, pos + n <= capacity (pos=%lld n=%lld)",
-                      what, (long long)pos, (long long)n);
+  const int rc = check_append_pos(what, kv, pos_dev, pos, n);
+  if (rc) return rc;
   return attend_exact_impl(what, q, n, n_q_heads, kv, shadow_k, shadow_v, k_new, v_new, pos_dev, pos + n, view,
                            out, ws, ws_bytes, stream);
 }

@@ -3,9 +3,10 @@
 Every computation is a call into the HIP library (nestspec): nest_embed,
 nest_add_rmsnorm, nest_rope_split and nest_swiglu for the layers around the
 nested linears (draft_gemv_x over the base planes, verify_gemm_x over both),
-kv_nest_append / kv_nest_attend on one nested KV cache per layer (base view
-for the draft, full view for the target), and draft_gemv_x / verify_accept_x
-with the fused argmax on the nested LM head. This module only sequences the
+kv_nest_append / kv_nest_attend (one position) and
+kv_nest_append_attend_exact (a verify pass) on one nested KV cache per layer
+(base view for the draft, full view for the target), and draft_gemv_x /
+verify_accept_x with the fused argmax on the nested LM head. This module only sequences the
 calls (the round of "How Speculative Decoding Speeds Up Inference", Table 1).
 
 Round state lives on the device: the committed cache length (one int32,

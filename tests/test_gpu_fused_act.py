@@ -187,11 +187,13 @@ def test_quantization_near_ties(ns, oracle, M, K):
         assert np.array_equal(host(y).view(np.uint32), host(y8).view(np.uint32))
 
 
-@pytest.mark.parametrize("M,K", [(40, 1024), (144, 4096)])
+@pytest.mark.parametrize("M,K", [(40, 1024), (144, 4096), (144, 8192)])
 def test_batched_verify_quantizes_near_ties(ns, oracle, M, K):
     # M > 16: the batched kernel's staging pass quantizes fp32 rows; on rows
     # built on and around ties its result equals the int8 path fed with the
-    # oracle's codes and scales, bit for bit
+    # oracle's codes and scales, bit for bit (at K = 8192 the 200 weight rows
+    # split their 64 groups over four blocks, whose sums meet in the fp32
+    # entry point's workspace)
     x = near_tie_rows(M, K, (313, M, K))
     qa, sa = oracle.act_quant(x)
     w = synth.weights(200, K, (314, M, K))

@@ -35,7 +35,7 @@ namespace {
 using nest::kGroup;
 
 constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
-// WR 16-row weight tiles per block (a template parameter, 2 and 4 to 7) and WK
+// WR 16-row weight tiles per block (a template parameter, 2 to 7) and WK
 // parts of the groups: WR WK compute waves, one per (tile, part), plus the
 // copy wave
 constexpr int threads_for(int wk, int wr) { return (wr * wk + 1) * 64; }
@@ -482,6 +482,7 @@ template <bool DBG>
 int launch_wr(const GemmArgs& a, int wr, int ctp, int blocks, hipStream_t st) {
   switch (wr) {
     case 2: return launch_ctp<2, DBG>(a, ctp, blocks, st);
+    case 3: return launch_ctp<3, DBG>(a, ctp, blocks, st);
     case 5: return launch_ctp_wide<5, DBG>(a, ctp, blocks, st);
     case 6: return launch_ctp_wide<6, DBG>(a, ctp, blocks, st);
     case 7: return launch_ctp_wide<7, DBG>(a, ctp, blocks, st);
@@ -515,10 +516,12 @@ int device_cus() {
 // blocks). Otherwise the activation rows are split evenly over P blocks per
 // row block when the matrix alone would leave CUs idle (P divides the
 // column tiles). When that needs more blocks than CUs (a partial second
-// round of blocks on some CUs) and two-tile blocks over all activation rows
-// fit in one round, those are taken: LLaMA-3-8B qkv (6144 x 4096, 144 rows)
-// 23.9 -> 19.4 us, with the other linears' splits measured best as they
-// were.
+// round of blocks on some CUs) and narrower blocks over all activation rows
+// fit in one round, those are taken: three-tile blocks over half the groups
+// each when there are 32 groups or more, else two-tile blocks (LLaMA-3-8B
+// qkv, 6144 x 4096 at 144 rows: 23.9 us as P = 3, 19.4-20.1 with two-tile
+// blocks, 18.4 with three-tile half-group blocks), with the other linears'
+// splits measured best as they were.
 struct Plan {
   int WR, P, S, row_blocks, CTP, blocks;
   size_t ws_bytes;  // workspace of the group split (0 when S == 1)
@@ -542,8 +545,17 @@ Plan plan_batched(int M, int K, int N, int cus) {
       if (4 * row_blocks * q >= 3 * cus) break;
     }
     if (row_blocks * p.P > cus && (T + 1) / 2 <= cus) {
-      p.WR = 2;
+      // more blocks than CUs: narrower blocks over all activation rows in
+      // one round; with 32 groups or more, three-tile blocks over half the
+      // groups each (two per row block), which stage half the activation
+      // bytes per block (LLaMA-3-8B qkv 6144 x 4096: 19.8-20.1 -> 18.4 us)
       p.P = 1;
+      if (G >= 32 && 2 * ((T + 2) / 3) <= cus) {
+        p.WR = 3;
+        p.S = 2;
+      } else {
+        p.WR = 2;
+      }
     } else if (p.P == 1 && CT >= 4 && T > 4 * cus && T <= 7 * cus) {
       // more than one round of four-tile blocks: the fewest tiles per block
       // (five to seven) that fit one round, which also stages the

@@ -166,11 +166,13 @@ def test_draft_gemv(ns, oracle, N, K, M):
 # groups (slices of 16, 16, 16 and 17); (130, 16384, 150) in two launches
 # (144 + 6 rows) that share the workspace. More tiles than four per CU take
 # five- to seven-tile blocks in one round: (17000, 256, 64) five (ragged
-# last tile), (24000, 128, 50) six, (28672, 128, 144) seven.
+# last tile), (24000, 128, 50) six, (28672, 128, 144) seven. (5515, 4096,
+# 144) needs more blocks than CUs with P = 3 and has 32 groups: three-tile
+# blocks over half the groups each (ragged last tile).
 BATCHED_SHAPES = [(50, 512, 17), (200, 256, 144), (64, 384, 150), (200, 2048, 144), (1000, 1024, 144),
                   (64, 128, 33), (130, 384, 100), (5511, 256, 144),
                   (640, 8192, 144), (300, 9216, 37), (200, 8320, 100), (130, 16384, 150),
-                  (17000, 256, 64), (24000, 128, 50), (28672, 128, 144)]
+                  (17000, 256, 64), (24000, 128, 50), (28672, 128, 144), (5515, 4096, 144)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMV_SHAPES + BATCHED_SHAPES)

@@ -682,11 +682,29 @@ def workloads(ns, torch, dv):
         "verify_gemm"), 20)
                  for n, (N, K) in wl["linears"].items()}
     us = _timed_us(torch, verify_pass, 5, warmup=1)
+    # the last layer's outputs of the timed passes (one workspace shared by
+    # every linear) against one call per linear on a fresh workspace, bit for
+    # bit; each linear's products are checked against the oracle on sampled
+    # rows by the full-size tests
+    torch.cuda.synchronize()
+    same = {}
+    for name, (N, K) in wl["linears"].items():
+        W, y_pass = layers[-1][name], ys[name].clone()
+        fresh = torch.zeros(max(wsn, 256), dtype=torch.uint8, device=cuda)
+        _check_rc(ns, L.verify_gemm(ptr(xs[K][0]), ptr(xs[K][1]), M, K, ptr(W.base), ptr(W.refine),
+                                    ptr(W.scales), N, 128, ptr(ys[name]), None, ptr(fresh), fresh.numel(), st),
+                  "verify_gemm")
+        torch.cuda.synchronize()
+        same[name] = bool(torch.equal(y_pass.view(torch.int32), ys[name].view(torch.int32)))
+        del fresh
+    if not all(same.values()):
+        raise SystemExit(f"batched verify: the timed pass's outputs differ from fresh-workspace calls: {same}")
     nbytes = wl["layers"] * sum(gemv_bytes(N, K, M, 2) for N, K in wl["linears"].values())
     ops = wl["layers"] * sum(2 * M * N * K for N, K in wl["linears"].values())
     out["llama3-8b_batched_verify"] = dict(_rate(nbytes, us, ops), rows=M, layers=wl["layers"],
                                            ms_per_pass=round(us / 1e3, 4),
-                                           per_linear_us={n: round(v, 2) for n, v in per_layer.items()})
+                                           per_linear_us={n: round(v, 2) for n, v in per_layer.items()},
+                                           pass_equals_fresh_workspace_calls=same)
     del layers, layer0, xs, ys, calls, wsv
 
     # -- nested KV attention at 32K: draft (1 query, base view), verify (9

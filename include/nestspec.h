@@ -35,10 +35,12 @@
  *  - Workspaces: sizes come from the *_workspace_size functions. The GEMV
  *    workspaces (draft_gemv, draft_gemv_x, verify_gemm, verify_gemm_x,
  *    verify_accept, verify_accept_x) are 256-byte aligned and must be all
- *    zero before their first use; every call leaves the parts that must
- *    stay zero (block counters) at zero, so one workspace serves any number
- *    of calls. Calls that share a workspace must not overlap in
- *    time (same stream, or ordered by events).
+ *    zero before their first use. Their first 4352 bytes are a counter zone
+ *    (block counters, laid out alike for all six entry points and every
+ *    shape) that every call leaves at zero and no call stores data in, so
+ *    one workspace, sized for the largest call, serves any number of calls
+ *    of these entry points and shapes. Calls that share a workspace must
+ *    not overlap in time (same stream, or ordered by events).
  *  - Lengths that change from round to round can live on the device: the
  *    calls that take a position or a context length also take an optional
  *    device int32 pointer whose value is added to the host value, so a
@@ -240,8 +242,9 @@ int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
  *   qa int8 [M][K] (16-byte aligned); sa fp32 [M]
  *   base, refine, scales: the tile layout (nest_tile), 16-byte aligned
  *   y fp32 [M][N] (out); acc_dbg int32 [M][N][K/group] (out, nullable): Av
- *   ws       verify_gemm_workspace_size(M, K, N) bytes, zeroed before first
- *            use; may be NULL (ws_bytes 0) when that size is 0
+ *   ws       verify_gemm_workspace_size(M, K, N) bytes (256-byte aligned),
+ *            zeroed before first use; may be NULL (ws_bytes 0) when that
+ *            size is 0
  * Requires M >= 1, group == 128, K % 128 == 0, N >= 1. M <= 16 runs the
  * one-tile kernel. Larger M runs the batched MFMA kernel in launches of up
  * to 144 rows; with few weight rows over long rows (e.g. 4096 x 14336) it

@@ -33,9 +33,10 @@
 namespace {
 
 using nest::kGroup;
+using nest::kMaxSplitRowBlocks;
 
 constexpr int kRT = 1;                   // 16-row weight tiles per compute wave
-// WR 16-row weight tiles per block (a template parameter, 2 to 7) and WK
+// WR 16-row weight tiles per block (a template parameter, 2 and 4 to 7) and WK
 // parts of the groups: WR WK compute waves, one per (tile, part), plus the
 // copy wave
 constexpr int threads_for(int wk, int wr) { return (wr * wk + 1) * 64; }
@@ -482,7 +483,6 @@ template <bool DBG>
 int launch_wr(const GemmArgs& a, int wr, int ctp, int blocks, hipStream_t st) {
   switch (wr) {
     case 2: return launch_ctp<2, DBG>(a, ctp, blocks, st);
-    case 3: return launch_ctp<3, DBG>(a, ctp, blocks, st);
     case 5: return launch_ctp_wide<5, DBG>(a, ctp, blocks, st);
     case 6: return launch_ctp_wide<6, DBG>(a, ctp, blocks, st);
     case 7: return launch_ctp_wide<7, DBG>(a, ctp, blocks, st);
@@ -516,15 +516,16 @@ int device_cus() {
 // blocks). Otherwise the activation rows are split evenly over P blocks per
 // row block when the matrix alone would leave CUs idle (P divides the
 // column tiles). When that needs more blocks than CUs (a partial second
-// round of blocks on some CUs) and narrower blocks over all activation rows
-// fit in one round, those are taken: three-tile blocks over half the groups
-// each when there are 32 groups or more, else two-tile blocks (LLaMA-3-8B
-// qkv, 6144 x 4096 at 144 rows: 23.9 us as P = 3, 19.4-20.1 with two-tile
-// blocks, 18.4 with three-tile half-group blocks), with the other linears'
-// splits measured best as they were.
+// round of blocks on some CUs) and two-tile blocks over all activation rows
+// fit in one round, those are taken (LLaMA-3-8B qkv, 6144 x 4096 at 144
+// rows: 23.9 us as P = 3, 19.4-20.1 with two-tile blocks), with the other
+// linears' splits measured best as they were. A group split needs one
+// counter per row block in the workspace's counter zone, so it is taken
+// only for at most kMaxSplitRowBlocks row blocks (with 256 CUs it never
+// has more than 128).
 struct Plan {
   int WR, P, S, row_blocks, CTP, blocks;
-  size_t ws_bytes;  // workspace of the group split (0 when S == 1)
+  size_t slot_bytes;  // the group split's partial sums (0 when S == 1)
 };
 
 size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -536,7 +537,7 @@ Plan plan_batched(int M, int K, int N, int cus) {
   p.P = 1;
   p.S = 1;
   int row_blocks = (T + 3) / 4;
-  if (2 * row_blocks <= cus && G >= 64) {
+  if (2 * row_blocks <= cus && G >= 64 && row_blocks <= kMaxSplitRowBlocks) {
     p.S = std::min(std::min(cus / row_blocks, G / 16), kMaxSplit);
   } else {
     for (int q = 1; q <= CT; ++q) {
@@ -545,17 +546,8 @@ Plan plan_batched(int M, int K, int N, int cus) {
       if (4 * row_blocks * q >= 3 * cus) break;
     }
     if (row_blocks * p.P > cus && (T + 1) / 2 <= cus) {
-      // more blocks than CUs: narrower blocks over all activation rows in
-      // one round; with 32 groups or more, three-tile blocks over half the
-      // groups each (two per row block), which stage half the activation
-      // bytes per block (LLaMA-3-8B qkv 6144 x 4096: 19.8-20.1 -> 18.4 us)
+      p.WR = 2;
       p.P = 1;
-      if (G >= 32 && 2 * ((T + 2) / 3) <= cus) {
-        p.WR = 3;
-        p.S = 2;
-      } else {
-        p.WR = 2;
-      }
     } else if (p.P == 1 && CT >= 4 && T > 4 * cus && T <= 7 * cus) {
       // more than one round of four-tile blocks: the fewest tiles per block
       // (five to seven) that fit one round, which also stages the
@@ -568,8 +560,7 @@ Plan plan_batched(int M, int K, int N, int cus) {
   p.blocks = ((p.row_blocks + kXcds - 1) / kXcds) * kXcds * p.P * p.S;
   if (p.S > 1) {
     const size_t slot = static_cast<size_t>(p.WR) * kRT * p.CTP * 4 * 64 * sizeof(float);
-    p.ws_bytes = round256(static_cast<size_t>(p.row_blocks) * sizeof(unsigned)) +
-                 static_cast<size_t>(p.row_blocks) * p.S * slot;
+    p.slot_bytes = static_cast<size_t>(p.row_blocks) * p.S * slot;
   }
   return p;
 }
@@ -578,14 +569,14 @@ Plan plan_batched(int M, int K, int N, int cus) {
 
 namespace nest {
 
-size_t verify_batched_ws_bytes(int M, int K, int N) {
+size_t verify_batched_slot_bytes(int M, int K, int N) {
   if (M < 1 || M > 16 * kMaxCT || K < kGroup || N < 1) return 0;
-  return plan_batched(M, K, N, device_cus()).ws_bytes;
+  return plan_batched(M, K, N, device_cus()).slot_bytes;
 }
 
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
                           const uint8_t* refine, const float* scales, int N, float* y, int32_t* acc_dbg,
-                          void* ws, size_t ws_bytes, hipStream_t st) {
+                          unsigned* counters, void* slots, size_t slot_bytes, hipStream_t st) {
   if (M < 1 || M > 16 * kMaxCT)
     return fail(NEST_EINVAL, "verify_gemm(batched): %d rows per launch (1..%d)", M, 16 * kMaxCT);
   GemmArgs a{};
@@ -594,11 +585,12 @@ int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const
   a.M = M; a.K = K; a.N = N; a.G = K / kGroup; a.T = (N + 15) / 16;
   const Plan p = plan_batched(M, K, N, device_cus());
   if (p.S > 1) {
-    if (!ws || ws_bytes < p.ws_bytes)
-      return fail(NEST_EWORKSPACE, "verify_gemm: workspace needs %zu bytes", p.ws_bytes);
-    if (!aligned16(ws)) return fail(NEST_EALIGN, "verify_gemm: workspace not 16-byte aligned");
-    a.done = static_cast<unsigned*>(ws);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(static_cast<size_t>(p.row_blocks) * sizeof(unsigned)));
+    if (!counters || !slots || slot_bytes < p.slot_bytes)
+      return fail(NEST_EWORKSPACE, "verify_gemm: the group split needs %zu bytes of partial sums", p.slot_bytes);
+    if (!aligned16(slots) || !aligned16(counters))
+      return fail(NEST_EALIGN, "verify_gemm: workspace not 16-byte aligned");
+    a.done = counters;
+    a.part = static_cast<float*>(slots);
   }
   a.row_blocks = p.row_blocks;
   a.parts = p.P;

@@ -737,21 +737,37 @@ size_t argmax_ws_bytes(int N) {
 }
 
 // Workspace of the GEMV entry points (all offsets 256-byte aligned):
-//   [0, 256)             the argmax kernels' finished-block counter; zero
+//   [0, C)               the counter zone (C = nest::kCounterZoneBytes): the
+//                        argmax kernels' finished-block counter and the
+//                        batched verify's finished-slice counters; zero
 //                        before the first call, and every call leaves it zero
-//   [256, 256 + P)       per-block argmax keys, P = argmax_ws_bytes(N)
+//   [C, C + P)           per-block argmax keys, P = argmax_ws_bytes(N)
 //   then, for fp32 activations (the *_x entry points), M*K int8 codes and M
 //   fp32 row scales, used when the codes are made by a separate
-//   nest_act_quant launch rather than inside the GEMV.
-constexpr size_t kCounterBytes = 256;
+//   nest_act_quant launch rather than inside the GEMV, and the batched
+//   verify's partial sums when it splits the groups.
+// verify_gemm with int8 rows over more than 16 rows uses the counter zone
+// and then the partial sums. Only counters ever live in the zone, at the
+// same offsets for every entry point and shape, so calls of different
+// shapes and entry points can take turns on one workspace.
+constexpr size_t kCounterBytes = nest::kCounterZoneBytes;
+static_assert(kCounterBytes % 256 == 0, "the counter zone keeps the 256-byte alignment");
 constexpr size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
-// The batched verify's own workspace (its groups split over blocks), for the
-// launches of up to 144 rows that an M-row call makes.
+// The batched verify's partial sums (its groups split over blocks), for the
+// launches of up to 144 rows that an M-row call makes (the largest is the
+// first, of min(M, 144) rows).
 size_t batched_ws_bytes(int64_t M, int64_t K, int64_t N) {
   if (M <= 16 || N > (1LL << 30) || K > (1LL << 24)) return 0;
-  return round256(nest::verify_batched_ws_bytes(static_cast<int>(M < 144 ? M : 144), static_cast<int>(K),
-                                                static_cast<int>(N)));
+  return round256(nest::verify_batched_slot_bytes(static_cast<int>(M < 144 ? M : 144), static_cast<int>(K),
+                                                  static_cast<int>(N)));
+}
+
+// verify_gemm's workspace with int8 rows: the counter zone and the partial
+// sums, or nothing when no launch splits the groups.
+size_t verify_int8_ws_bytes(int64_t M, int64_t K, int64_t N) {
+  const size_t slots = batched_ws_bytes(M, K, N);
+  return slots ? kCounterBytes + slots : 0;
 }
 
 size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N, bool x) {
@@ -763,6 +779,7 @@ size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N, bool x) {
 
 struct Workspace {
   unsigned* counter;
+  unsigned* split_counters;  // the batched verify's, in the counter zone
   unsigned long long* partials;
   int8_t* codes;  // fp32-activation paths only
   float* code_scales;
@@ -773,6 +790,7 @@ Workspace carve(void* ws, int64_t M, int64_t K, int64_t N) {
   char* p = static_cast<char*>(ws);
   Workspace w{};
   w.counter = reinterpret_cast<unsigned*>(p);
+  w.split_counters = reinterpret_cast<unsigned*>(p + nest::kSplitCounterOff);
   w.partials = reinterpret_cast<unsigned long long*>(p + kCounterBytes);
   char* c = p + kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
   w.codes = reinterpret_cast<int8_t*>(c);
@@ -901,17 +919,21 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
   }
   hipStream_t st = nest::as_stream(stream);
   Act act2 = act;
-  void* bws = ws;  // the batched kernel's workspace
-  size_t bws_bytes = ws_bytes;
+  // the batched kernel's counters (in the counter zone) and partial sums
+  unsigned* bcnt = nullptr;
+  void* bslots = nullptr;
+  const size_t bslot_bytes = batched_ws_bytes(M, K, N);
   if (act.x) {
     const Workspace w = carve(ws, M, K, N);
     rc = quantize_first(act2, M, K, N, w, st, true);
     if (rc) return rc;
-    bws = w.batched;
-    bws_bytes = batched_ws_bytes(M, K, N);
-  } else if (M > 16) {
-    rc = batched_ws_bytes(M, K, N) ? check_ws(what, ws, ws_bytes, batched_ws_bytes(M, K, N)) : NEST_OK;
+    bcnt = w.split_counters;
+    bslots = w.batched;
+  } else if (bslot_bytes) {
+    rc = check_ws(what, ws, ws_bytes, verify_int8_ws_bytes(M, K, N));
     if (rc) return rc;
+    bcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + nest::kSplitCounterOff);
+    bslots = static_cast<char*>(ws) + kCounterBytes;
   }
   if (M <= 16) {
     GemvArgs a = make_args(act2, M, K, base, refine, scales, N, y, acc_dbg);
@@ -924,7 +946,8 @@ int verify_impl(const char* what, const Act& act, int64_t M, int64_t K, const ui
     const int64_t mc = M - m0 < 144 ? M - m0 : 144;
     rc = nest::launch_verify_batched(act2.qa + m0 * K, act2.sa + m0, (int)mc, (int)K, base, refine, scales,
                                      (int)N, y + m0 * N,
-                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, bws, bws_bytes, st);
+                                     acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr, bcnt, bslots,
+                                     bslot_bytes, st);
     if (rc) return rc;
   }
   return NEST_OK;
@@ -993,7 +1016,7 @@ extern "C" int draft_gemv_x(const float* x, int64_t M, int64_t K, const uint8_t*
 
 extern "C" size_t verify_gemm_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (M < 1 || K < 1 || N < 1) return 0;
-  return batched_ws_bytes(M, K, N);
+  return verify_int8_ws_bytes(M, K, N);
 }
 
 extern "C" int verify_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K,

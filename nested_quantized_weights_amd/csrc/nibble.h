@@ -56,12 +56,26 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 // dynamic LDS size).
 int resident_blocks(const void* kernel, int threads, size_t dyn_lds);
 
+// Counter zone at the start of every workspace of the GEMV entry points
+// (draft_gemv*, verify_gemm*, verify_accept*), the same for every entry point
+// and shape: [0, 256) the argmax kernels' finished-block counter, then one
+// finished-slice counter per row block of the batched verify (at most
+// kMaxSplitRowBlocks). Counters are zero at rest, every call returns the
+// ones it used to zero, and no call stores data in the zone, so one
+// workspace serves calls of any of these entry points and shapes in turn.
+constexpr size_t kSplitCounterOff = 256;
+constexpr int kMaxSplitRowBlocks = 1024;
+constexpr size_t kCounterZoneBytes = kSplitCounterOff + 4 * kMaxSplitRowBlocks;
+
 // Batched verify (M > 16 rows): one launch for up to 144 rows. Shapes whose
-// groups are split over several blocks need verify_batched_ws_bytes(M, K, N)
-// bytes of workspace (counters zero before first use), else none (0).
-size_t verify_batched_ws_bytes(int M, int K, int N);
+// groups are split over several blocks need the row blocks' counters (zero
+// before the launch; the launch leaves them zero) and
+// verify_batched_slot_bytes(M, K, N) bytes of partial sums (16-byte
+// aligned, no initial contents); other shapes need neither (0 bytes).
+size_t verify_batched_slot_bytes(int M, int K, int N);
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
                           const uint8_t* refine, const float* scales, int N, float* y,
-                          int32_t* acc_dbg, void* ws, size_t ws_bytes, hipStream_t st);
+                          int32_t* acc_dbg, unsigned* counters, void* slots, size_t slot_bytes,
+                          hipStream_t st);
 
 }  // namespace nest

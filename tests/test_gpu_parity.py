@@ -166,13 +166,13 @@ def test_draft_gemv(ns, oracle, N, K, M):
 # groups (slices of 16, 16, 16 and 17); (130, 16384, 150) in two launches
 # (144 + 6 rows) that share the workspace. More tiles than four per CU take
 # five- to seven-tile blocks in one round: (17000, 256, 64) five (ragged
-# last tile), (24000, 128, 50) six, (28672, 128, 144) seven. (5515, 4096,
-# 144) needs more blocks than CUs with P = 3 and has 32 groups: three-tile
-# blocks over half the groups each (ragged last tile).
+# last tile), (24000, 128, 50) six, (28672, 128, 144) seven. (4400, 8192,
+# 20) splits the groups over three blocks for each of 69 row blocks (more
+# counters than a 256-byte area holds; ragged last tile).
 BATCHED_SHAPES = [(50, 512, 17), (200, 256, 144), (64, 384, 150), (200, 2048, 144), (1000, 1024, 144),
                   (64, 128, 33), (130, 384, 100), (5511, 256, 144),
                   (640, 8192, 144), (300, 9216, 37), (200, 8320, 100), (130, 16384, 150),
-                  (17000, 256, 64), (24000, 128, 50), (28672, 128, 144), (5515, 4096, 144)]
+                  (17000, 256, 64), (24000, 128, 50), (28672, 128, 144), (4400, 8192, 20)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMV_SHAPES + BATCHED_SHAPES)
@@ -206,6 +206,44 @@ def test_batched_verify_repeats(ns, oracle, N, K):
     oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
     ok, worst = bound_ok(y1, sa, scales, oacc, 1.0 / 16)
     assert ok, worst
+
+
+def test_shapes_and_entry_points_share_one_workspace(ns, oracle):
+    # The workspace starts with a counter zone that holds only block
+    # counters, at the same offsets for every entry point and shape. A group
+    # split over 69 row blocks (4400 x 8192, three slices), one over 10 row
+    # blocks and four slices (640 x 8192), the fp32-input path of the first
+    # shape and an argmax GEMV take turns on one workspace, and each gives
+    # bit for bit what it gives on a fresh one; the zone is zero afterwards.
+    # (With the counters placed before the partial sums at a shape-dependent
+    # offset, the 4-slice call's sums landed on the 69-row-block call's
+    # counters.)
+    la = _layer(oracle, 4400, 8192, 144, (14,))
+    lb = _layer(oracle, 640, 8192, 144, (15,))
+    Wa, Wb = tiled(ns, *la[:3]), tiled(ns, *lb[:3])
+    x = dev(synth.activations(144, 8192, (16,)))
+    L = ns.lib()
+    zone = 4352
+    assert L.verify_gemm_workspace_size(144, 8192, 4400) > zone
+    assert L.verify_gemm_workspace_size(144, 8192, 640) > zone
+    n = max(L.verify_gemm_workspace_size(144, 8192, 4400), L.verify_gemm_workspace_size(144, 8192, 640),
+            L.nest_gemv_x_workspace_size(144, 8192, 4400), L.nest_gemv_x_workspace_size(1, 8192, 4400))
+
+    def fresh():
+        return torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+    calls = {
+        "split3": lambda ws: ns.verify_gemm(dev(la[3]), dev(la[4]), Wa, ws=ws),
+        "split4": lambda ws: ns.verify_gemm(dev(lb[3]), dev(lb[4]), Wb, ws=ws),
+        "x": lambda ws: ns.verify_gemm_x(x, Wa, ws=ws),
+        "argmax": lambda ws: ns.draft_gemv_x(x[:1], Wa, argmax=True, want_y=False, ws=ws),
+    }
+    ref = {k: host(f(fresh())) for k, f in calls.items()}
+    ws = fresh()
+    for k in ["split4", "split3", "split4", "x", "split3", "argmax", "split4", "x", "split3"]:
+        got = host(calls[k](ws))
+        assert np.array_equal(got.view(np.uint32), ref[k].view(np.uint32)), k
+    assert not host(ws[:zone]).any()
 
 
 def test_gemv_deterministic(ns, oracle):

@@ -154,6 +154,12 @@ def test_workspaces_are_checked_without_a_gpu(lib):
     assert v(p, p, 144, 14336, p, p, p, 4096, 128, p, None, None, 0, None) == 4  # NEST_EWORKSPACE
     assert b"workspace needs" in lib.nest_last_error()
     assert v(p, p, 144, 14336, p, p, p, 4096, 128, p, None, p, down - 1, None) == 4
+    assert v(p, p, 144, 14336, p, p, p, 4096, 128, p, None, ctypes.c_void_p(272), down, None) == 2
+    # layout: the 4352-byte counter zone every GEMV workspace starts with
+    # (256 B for the argmax counter, 1024 row-block counters), then one slot
+    # of 4 tiles x 9 column tiles x 64 lanes x 16 B per (row block, slice):
+    # 64 row blocks x 4 slices on a 256-CU device (the count without a GPU)
+    assert down == 4352 + 64 * 4 * (4 * 9 * 64 * 16)
     a = lib.kv_nest_append
     a.restype = ctypes.c_int
     a.argtypes = [ctypes.POINTER(_KV)] + [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]

@@ -44,6 +44,8 @@
 // (sc1, served from that point). This is the ordering a release/acquire
 // pair would give, without the release's write-back of the whole L2, which
 // nothing here needs because no plain store carries data between blocks.
+#include <type_traits>
+
 #include "nibble.h"
 
 namespace {
@@ -493,7 +495,13 @@ gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int r = 0; r < MR; ++r) s_a[r] = XQ ? sa_sh[min(4 * kq + r, a.M - 1)] : a.sa[min(4 * kq + r, a.M - 1)];
 
-  for (int j = 0; j < J; ++j) {
+  // One tile of this wave's range. The first tile (its first quads already
+  // in flight) is an instance of its own: as one loop with a first-iteration
+  // test, the compiler kept more registers live and spilled some (the
+  // one-plane argmax kernels over several rows).
+  __shared__ float part[WAVES][MR][64];  // segment sums (S > 1)
+  auto tile = [&](int j, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
     const int n0 = (t_lo + j) * 16;
     const bool tile_ok = t_lo + j < t_hi;
     const int n = n0 + c;  // this lane's output column (weight row)
@@ -502,16 +510,17 @@ gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < MR; ++r) run[r] = 0.0f;
     // the first tile's first quad was requested before staging
-    if (A4 && tile_ok && j != 0 && g_begin < g_end) {
+    if (A4 && tile_ok && !kFirst && g_begin < g_end) {
 #pragma unroll
       for (int i = 0; i < kDepth; ++i)
         if (g_begin + 4 * i < g_end) load_quad<PLANES>(tp, g_begin + 4 * i, qs[i]);
     }
     if (tile_ok) {
-      if constexpr (kDepth > 1)
+      if constexpr (kDepth > 1) {
         gemv_segment_d<PLANES, MR, DBG, LDSACT, kDepth>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, qs);
-      else
+      } else {
         gemv_segment<PLANES, MR, DBG, A4, LDSACT>(a, lds_act, tp, pa, kq, mrow, n, g_begin, g_end, run, cur);
+      }
     }
 
     if (ARGMAX) {
@@ -525,12 +534,11 @@ gemv_kernel(GemvArgs a) {
           }
         }
       }
-      continue;
+      return;
     }
 
     float tot[MR];
     if (S > 1) {
-      __shared__ float part[WAVES][MR][64];
 #pragma unroll
       for (int r = 0; r < MR; ++r) part[wave][r][lane] = run[r];
       __syncthreads();
@@ -547,13 +555,15 @@ gemv_kernel(GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < MR; ++r) tot[r] = run[r];
     }
-    if (seg != 0 || !tile_ok || n >= a.N) continue;
+    if (seg != 0 || !tile_ok || n >= a.N) return;
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       const int m = 4 * kq + r;
       if (m < a.M) a.y[static_cast<size_t>(m) * a.N + n] = tot[r] * s_a[r];
     }
-  }
+  };
+  if (J > 0) tile(0, std::true_type{});
+  for (int j = 1; j < J; ++j) tile(j, std::false_type{});
 
   if (ARGMAX) {
     // best over the 16 lanes of each k-quarter group, then over the waves

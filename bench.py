@@ -523,9 +523,40 @@ def _timed_us(torch, fn, reps, warmup=3):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def _timed_stats(torch, fn, reps, batch, warmup=3):
+    """Microseconds per call of fn over `reps` calls in batches of `batch`
+    back-to-back calls, each batch between two HIP events (an event between
+    every two calls would add its own gap): the mean over all calls, and the
+    median and minimum of the batch means."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    nb = max(1, reps // batch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    ev[0].record()
+    for i in range(nb):
+        for _ in range(batch):
+            fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / batch for i in range(nb)])
+    return {"mean": float(per.mean()), "median": float(np.median(per)), "min": float(per.min()),
+            "calls": nb * batch, "batch": batch}
+
+
 def _rate(nbytes, us, ops=None):
+    """Rates of one call; us is a number (the mean) or _timed_stats' dict,
+    whose mean gives the rates and whose median and minimum are reported
+    beside them."""
+    st = us if isinstance(us, dict) else None
+    if st is not None:
+        us = st["mean"]
     r = {"us": round(us, 2), "GB_per_s": round(nbytes / us / 1e3, 1),
          "frac_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "bytes": int(nbytes)}
+    if st is not None:
+        r["us_median"] = round(st["median"], 2)
+        r["us_min"] = round(st["min"], 2)
+        r["timing"] = f"{st['calls']} calls in batches of {st['batch']}; median and minimum of the batch means"
     if ops is not None:
         r["int8_TOPS"] = round(ops / us / 1e6, 1)
         r["frac_int8_mfma_peak"] = round(ops / us / 1e6 / PEAK_INT8_TOPS, 4)
@@ -576,13 +607,13 @@ def workloads(ns, torch, dv):
                                       N, 128, ptr(y), ptr(wsg), wsn, st), "verify_gemm_x")
 
     out["linear_4096"] = {
-        "draft_gemv_x_1row": _rate(gemv_bytes(N, K, 1, 1, x_fp32=True), _timed_us(torch, draft, 200)),
-        "verify_gemm_x_5rows": _rate(gemv_bytes(N, K, 5, 2, x_fp32=True), _timed_us(torch, verify, 200))}
+        "draft_gemv_x_1row": _rate(gemv_bytes(N, K, 1, 1, x_fp32=True), _timed_stats(torch, draft, 400, 20)),
+        "verify_gemm_x_5rows": _rate(gemv_bytes(N, K, 5, 2, x_fp32=True), _timed_stats(torch, verify, 400, 20))}
     # the same calls on one copy, which stays in the 256 MB last-level cache
     rot[0] = 1
     out["linear_4096"]["cache_hot"] = {
-        "draft_gemv_x_1row": _rate(gemv_bytes(N, K, 1, 1, x_fp32=True), _timed_us(torch, draft, 200)),
-        "verify_gemm_x_5rows": _rate(gemv_bytes(N, K, 5, 2, x_fp32=True), _timed_us(torch, verify, 200)),
+        "draft_gemv_x_1row": _rate(gemv_bytes(N, K, 1, 1, x_fp32=True), _timed_stats(torch, draft, 400, 20)),
+        "verify_gemm_x_5rows": _rate(gemv_bytes(N, K, 5, 2, x_fp32=True), _timed_stats(torch, verify, 400, 20)),
         "note": "one weight copy re-read every call (last-level-cache hits); not HBM figures"}
     del Ws, x, y, wsg
 
@@ -615,7 +646,7 @@ def workloads(ns, torch, dv):
                                         None, None, ptr(ws), wsn, st), "verify_accept_x")
 
     head = {"draft_gemv_x_argmax_1row": _rate(gemv_bytes(V, H, 1, 1, y=False, argmax=True, x_fp32=True),
-                                               _timed_us(torch, head_draft, 100))}
+                                               _timed_stats(torch, head_draft, 200, 10))}
     zd = zero_draft.repeat(len(pool), 1).contiguous()
     for r in range(len(pool)):
         accept(r, zd)
@@ -627,7 +658,7 @@ def workloads(ns, torch, dv):
         accept(cnt[0] % len(pool), zd)
         cnt[0] += 1
 
-    head["verify_accept_x_9rows"] = _rate(accept_bytes(V, H, k, x_fp32=True), _timed_us(torch, accept_one, 100))
+    head["verify_accept_x_9rows"] = _rate(accept_bytes(V, H, k, x_fp32=True), _timed_stats(torch, accept_one, 200, 10))
     head["planted_rounds"] = {}
     for a in wl["alphas"]:
         t_r = targets[np.arange(R) % len(pool)]
@@ -681,7 +712,8 @@ def workloads(ns, torch, dv):
                           ptr(layers[1][n].scales), N, 128, ptr(ys[n]), None, ptr(wsv), wsv.numel(), st),
         "verify_gemm"), 20)
                  for n, (N, K) in wl["linears"].items()}
-    us = _timed_us(torch, verify_pass, 5, warmup=1)
+    pass_stats = _timed_stats(torch, verify_pass, 8, 1, warmup=1)  # 8 passes = 1024 launches
+    us = pass_stats["mean"]
     # the last layer's outputs of the timed passes (one workspace shared by
     # every linear) against one call per linear on a fresh workspace, bit for
     # bit; each linear's products are checked against the oracle on sampled
@@ -701,7 +733,7 @@ def workloads(ns, torch, dv):
         raise SystemExit(f"batched verify: the timed pass's outputs differ from fresh-workspace calls: {same}")
     nbytes = wl["layers"] * sum(gemv_bytes(N, K, M, 2) for N, K in wl["linears"].values())
     ops = wl["layers"] * sum(2 * M * N * K for N, K in wl["linears"].values())
-    out["llama3-8b_batched_verify"] = dict(_rate(nbytes, us, ops), rows=M, layers=wl["layers"],
+    out["llama3-8b_batched_verify"] = dict(_rate(nbytes, pass_stats, ops), rows=M, layers=wl["layers"],
                                            ms_per_pass=round(us / 1e3, 4),
                                            per_linear_us={n: round(v, 2) for n, v in per_layer.items()},
                                            pass_equals_fresh_workspace_calls=same)
@@ -736,11 +768,11 @@ def workloads(ns, torch, dv):
 
         tag = "draft_base_view_1q" if view == 0 else f"verify_full_view_{nq}q"
         rot[0] = len(kvs)
-        att[tag] = _rate(attend_bytes(view, Hkv, Hq, nq, ctx), _timed_us(torch, attend, 200))
+        att[tag] = _rate(attend_bytes(view, Hkv, Hq, nq, ctx), _timed_stats(torch, attend, 400, 20))
         rot[0] = 1
         att.setdefault("cache_hot", {"note": "one cache re-read every call (last-level-cache hits); "
                                              "not HBM figures"})[tag] = _rate(attend_bytes(view, Hkv, Hq, nq, ctx),
-                                                                            _timed_us(torch, attend, 200))
+                                                                            _timed_stats(torch, attend, 400, 20))
     out["kv_32k"] = att
     del caches, kvs
     torch.cuda.empty_cache()

@@ -1078,8 +1078,8 @@ constexpr size_t kStaticScratch = size_t{1} << 20;
 constexpr int kMaxDevices = 64;
 
 // Zero when the library loads; the only part that must be zero before a
-// call (the block counter in its first 256 bytes) is returned to zero by
-// every call, and the rest needs no initial contents.
+// call (the counter zone at its start) is returned to zero by every call,
+// and the rest needs no initial contents.
 __device__ __align__(256) unsigned char scratch[kStaticScratch];
 
 std::mutex g_scratch_mu;

@@ -268,7 +268,8 @@ class Round:
         for j in range(k):
             for n, N, K in LINEARS:
                 x = d["x"][n][j:j + 1]
-                calls.append((L.draft_gemv_x, (p(x), 1, K, p(d["base"][n]), p(d["scales"][n]), N,
+                Wj = d["steps"][n][j]  # this step's copy of the weights
+                calls.append((L.draft_gemv_x, (p(x), 1, K, p(Wj.base), p(Wj.scales), N,
                                                128, p(y[n]), None, *gw, st), "draft_" + n))
                 if n == "qkv":
                     # the step's own token enters the cache, then the draft attends (base view)
@@ -295,8 +296,9 @@ class Round:
             phases += [j] * (len(calls) - len(phases))
         for n, N, K in LINEARS:
             xv = d["xv"][n][:k + 1]
-            calls.append((L.verify_gemm_x, (p(xv), k + 1, K, p(d["base"][n]), p(d["refine"][n]),
-                                            p(d["scales"][n]), N, 128, p(y[n]), *gw, st), "verify_" + n))
+            Wv = d["steps"][n][k]  # the verify pass's copy
+            calls.append((L.verify_gemm_x, (p(xv), k + 1, K, p(Wv.base), p(Wv.refine),
+                                            p(Wv.scales), N, 128, p(y[n]), *gw, st), "verify_" + n))
             if n == "qkv":
                 # the target's K/V for all k+1 positions overwrite the draft's, and the k+1 queries
                 # attend (full view): one call, the append folded into the open-block kernel
@@ -448,12 +450,22 @@ def tiny_decoder(torch, n_new=48, prompt_len=40):
     return out
 
 
+# Copies of the layer's linears: draft step j of a round reads copy j and
+# the verify pass copy k, so that no step finds the previous step's weights
+# in the 256 MB last-level cache, as no layer would in a model of many
+# layers (9 copies, 2.2 GB, cover k <= 8). The LM head is one copy, as in a
+# model: at 545 MB it does not fit that cache.
+STEP_COPIES = 9
+
+
 def upload(ns, torch, inp):
-    dv = {"base": {}, "refine": {}, "scales": {}, "x": {}, "xv": {}}
+    dv = {"base": {}, "refine": {}, "scales": {}, "x": {}, "xv": {}, "steps": {}}
     for name, w in inp["w"].items():
         wt = torch.from_numpy(w).cuda()
         t = ns.nest_pack_tiled(wt)  # storage format, then the kernels' tile layout
         dv["base"][name], dv["refine"][name], dv["scales"][name] = t.base, t.refine, t.scales
+        if name != "head":
+            dv["steps"][name] = _copies(torch, t, STEP_COPIES)
         del wt, t
     for key in ("x", "xv"):
         for name, x in inp[key].items():

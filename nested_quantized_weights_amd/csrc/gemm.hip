@@ -528,8 +528,6 @@ struct Plan {
   size_t slot_bytes;  // the group split's partial sums (0 when S == 1)
 };
 
-size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
-
 Plan plan_batched(int M, int K, int N, int cus) {
   Plan p{};
   const int T = (N + 15) / 16, CT = (M + 15) / 16, G = K / kGroup;

@@ -671,6 +671,27 @@ def workloads(ns, torch, dv):
         cnt[0] += 1
 
     head["verify_accept_x_9rows"] = _rate(accept_bytes(V, H, k, x_fp32=True), _timed_stats(torch, accept_one, 200, 10))
+    # a batched decode: 16 sequences' verify passes (k = 8, 144 rows) through
+    # the LM head in one call (the batched kernel writes the logits, then the
+    # row argmaxes and the rule), against 16 calls of 9 rows
+    B16 = 16
+    x144 = torch.from_numpy(synth.activations(B16 * (k + 1), H, (key, 4))).cuda()
+    d144 = torch.zeros(B16 * k, dtype=torch.int32, device=cuda)
+    y144 = torch.empty((B16 * (k + 1), V), dtype=torch.float32, device=cuda)
+    o144 = [torch.empty(n, dtype=torch.int32, device=cuda) for n in (B16 * (k + 1), B16, B16 * (k + 1))]
+    wsn144 = L.nest_gemv_x_workspace_size(B16 * (k + 1), H, V)
+    ws144 = torch.zeros(wsn144, dtype=torch.uint8, device=cuda)
+
+    def accept_batch():
+        _check_rc(ns, L.verify_accept_x(ptr(x144), B16, k, H, ptr(base), ptr(refine), ptr(scales), V, 128,
+                                        ptr(d144), ptr(o144[0]), ptr(o144[1]), ptr(o144[2]), ptr(y144),
+                                        None, None, ptr(ws144), wsn144, st), "verify_accept_x")
+
+    head["verify_accept_x_16seq_9rows"] = dict(
+        _rate(gemv_bytes(V, H, B16 * (k + 1), 2, y=True, x_fp32=True), _timed_stats(torch, accept_batch, 40, 4)),
+        note="16 sequences at k = 8 in one call; bytes count the logits written once (the row argmax "
+             "re-reads them)")
+    del x144, d144, y144, o144, ws144
     head["planted_rounds"] = {}
     for a in wl["alphas"]:
         t_r = targets[np.arange(R) % len(pool)]

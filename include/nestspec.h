@@ -286,7 +286,8 @@ int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
  *   n_emitted int32 [B] (out): a+1, where a is the largest j <= k with
  *             d_i == t_{i-1} for all 1 <= i <= j
  *   emitted   int32 [B][k+1] (out): t_0..t_a, then -1 in the unused slots
- *   y         fp32 [B*(k+1)][V] (out, nullable): the verify logits
+ *   y         fp32 [B*(k+1)][V] (out; nullable up to 16 rows): the verify
+ *             logits
  *   len       int32 [B] (in/out, nullable): each sequence's committed
  *             length, advanced by n_emitted (BitNest, Figure 4: the
  *             accepted entries stay; the blog's round step 3: the next pass
@@ -298,7 +299,15 @@ int verify_gemm_x(const float* x, int64_t M, int64_t K, const uint8_t* base,
  *   ws        verify_accept_workspace_size(B, k, V) bytes, zeroed before
  *             first use (per-block partial maxima and the last-block
  *             counter).
- * Requires B >= 1, k >= 0, B*(k+1) <= 16, group == 128, K % 128 == 0.
+ * Up to 16 rows, one launch: the argmax is fused into the GEMV and its
+ * last block applies the rule. More rows (several sequences, or k >= 16):
+ * the batched verify kernel writes y (required then), one block per row
+ * takes its argmax with the same tie rule (the lowest index), and one
+ * thread per sequence applies the rule; the fp32 fold then adds the group
+ * sums in the batched kernel's order, so a target can differ from the
+ * fused path's only where a row's two largest logits are within the
+ * fold's rounding of each other.
+ * Requires B >= 1, k >= 0, B*(k+1) <= 65535, group == 128, K % 128 == 0.
  * Draft ids are not read on the host, so an id outside [0, V) simply
  * never matches. Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE,
  * NEST_EUNSUPPORTED, NEST_EWORKSPACE, NEST_EHIP. */

@@ -528,14 +528,14 @@ struct Plan {
   size_t slot_bytes;  // the group split's partial sums (0 when S == 1)
 };
 
-Plan plan_batched(int M, int K, int N, int cus) {
+Plan plan_batched(int M, int K, int N, int cus, bool split_ok = true) {
   Plan p{};
   const int T = (N + 15) / 16, CT = (M + 15) / 16, G = K / kGroup;
   p.WR = 4;
   p.P = 1;
   p.S = 1;
   int row_blocks = (T + 3) / 4;
-  if (2 * row_blocks <= cus && G >= 64 && row_blocks <= kMaxSplitRowBlocks) {
+  if (split_ok && 2 * row_blocks <= cus && G >= 64 && row_blocks <= kMaxSplitRowBlocks) {
     p.S = std::min(std::min(cus / row_blocks, G / 16), kMaxSplit);
   } else {
     for (int q = 1; q <= CT; ++q) {
@@ -581,7 +581,9 @@ int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const
   a.qa = qa; a.sa = sa; a.base = base; a.refine = refine; a.scales = scales;
   a.y = y; a.acc_dbg = acc_dbg;
   a.M = M; a.K = K; a.N = N; a.G = K / kGroup; a.T = (N + 15) / 16;
-  const Plan p = plan_batched(M, K, N, device_cus());
+  // without counters (a caller with no room for the partial sums) the
+  // groups are not split
+  const Plan p = plan_batched(M, K, N, device_cus(), counters != nullptr);
   if (p.S > 1) {
     if (!counters || !slots || slot_bytes < p.slot_bytes)
       return fail(NEST_EWORKSPACE, "verify_gemm: the group split needs %zu bytes of partial sums", p.slot_bytes);

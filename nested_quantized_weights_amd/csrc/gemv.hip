@@ -608,6 +608,25 @@ gemv_kernel(GemvArgs a) {
 // memory. Rows are then reduced per wave (shuffles) and across the waves
 // (LDS). The keys were written by other blocks of the running kernel with
 // agent-scope stores and are read with agent-scope loads.
+// The greedy accept rule for sequence b, given the target (argmax) of each
+// of its k+1 rows, tgt(b*(k+1) + j): slot i's draft d_i is checked against
+// the target of row i-1, and the first mismatch ends the round. Writes the
+// targets, the emitted count and tokens, and advances the lengths.
+template <typename Tgt>
+__device__ void accept_sequence(const FinishArgs& f, int b, Tgt tgt) {
+  const int k1 = f.k + 1;
+  int acc = 0;
+  while (acc < f.k && f.draft[b * f.k + acc] == tgt(b * k1 + acc)) ++acc;
+  f.n_emitted[b] = acc + 1;
+  for (int j = 0; j < k1; ++j) {
+    const int32_t tj = tgt(b * k1 + j);
+    f.target[b * k1 + j] = tj;
+    f.emitted[b * k1 + j] = j <= acc ? tj : -1;
+  }
+  if (f.len) f.len[b] += acc + 1;
+  if (f.next) f.next[b] = tgt(b * k1 + acc);
+}
+
 template <int NT>
 __device__ void finish_reduce(const FinishArgs& f) {
   constexpr int kPer = kMaxArgmaxBlocks / NT, kW = NT / 64;
@@ -645,20 +664,32 @@ __device__ void finish_reduce(const FinishArgs& f) {
     if (!f.accept) f.argmax_out[t] = tgt[t];
   }
   __syncthreads();
-  if (f.accept && t < f.B) {
-    // One thread per sequence: slot i's draft d_i is checked against
-    // t_{i-1}; the first mismatch ends the round.
-    const int b = t, k1 = f.k + 1;
-    int acc = 0;
-    while (acc < f.k && f.draft[b * f.k + acc] == tgt[b * k1 + acc]) ++acc;
-    f.n_emitted[b] = acc + 1;
-    for (int j = 0; j < k1; ++j) {
-      f.target[b * k1 + j] = tgt[b * k1 + j];
-      f.emitted[b * k1 + j] = j <= acc ? tgt[b * k1 + j] : -1;
-    }
-    if (f.len) f.len[b] += acc + 1;
-    if (f.next) f.next[b] = tgt[b * k1 + acc];
-  }
+  if (f.accept && t < f.B) accept_sequence(f, t, [&](int r) { return tgt[r]; });
+}
+
+// verify_accept over more than 16 rows (several sequences, or k >= 16): the
+// batched verify writes the logits to y, then one block per row takes the
+// row's argmax with the same keys as the fused path (the largest value, the
+// lowest index among equal ones), then one thread per sequence applies the
+// accept rule.
+__global__ void __launch_bounds__(256) row_argmax_kernel(const float* __restrict__ y, int V,
+                                                         unsigned long long* keys) {
+  __shared__ unsigned long long red[4];
+  const int t = threadIdx.x;
+  const float* yr = y + static_cast<size_t>(blockIdx.x) * V;
+  unsigned long long k = 0;
+#pragma unroll 8
+  for (int n = t; n < V; n += 256) k = umax64(k, argmax_key(yr[n], static_cast<uint32_t>(n)));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) k = umax64(k, shfl_xor_u64(k, o));
+  if ((t & 63) == 0) red[t >> 6] = k;
+  __syncthreads();
+  if (t == 0) keys[blockIdx.x] = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+}
+
+__global__ void __launch_bounds__(64) accept_rows_kernel(const unsigned long long* keys, FinishArgs f) {
+  for (int b = threadIdx.x; b < f.B; b += 64)
+    accept_sequence(f, b, [&](int r) { return static_cast<int32_t>(argmax_key_index(keys[r])); });
 }
 
 // ---------------------------------------------------------------------------
@@ -780,8 +811,16 @@ size_t verify_int8_ws_bytes(int64_t M, int64_t K, int64_t N) {
   return slots ? kCounterBytes + slots : 0;
 }
 
+// The keys region: per-block argmax keys, or one key per row for
+// verify_accept over more than 16 rows.
+size_t keys_bytes(int64_t M, int64_t N) {
+  const size_t blocks = argmax_ws_bytes(static_cast<int>(N));
+  const size_t rows = M > 16 ? static_cast<size_t>(M) * sizeof(unsigned long long) : 0;
+  return round256(blocks > rows ? blocks : rows);
+}
+
 size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N, bool x) {
-  size_t n = kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
+  size_t n = kCounterBytes + keys_bytes(M, N);
   if (x) n += round256(static_cast<size_t>(M) * K) + round256(static_cast<size_t>(M) * sizeof(float)) +
               batched_ws_bytes(M, K, N);
   return n;
@@ -802,7 +841,7 @@ Workspace carve(void* ws, int64_t M, int64_t K, int64_t N) {
   w.counter = reinterpret_cast<unsigned*>(p);
   w.split_counters = reinterpret_cast<unsigned*>(p + nest::kSplitCounterOff);
   w.partials = reinterpret_cast<unsigned long long*>(p + kCounterBytes);
-  char* c = p + kCounterBytes + round256(argmax_ws_bytes(static_cast<int>(N)));
+  char* c = p + kCounterBytes + keys_bytes(M, N);
   w.codes = reinterpret_cast<int8_t*>(c);
   w.code_scales = reinterpret_cast<float*>(c + round256(static_cast<size_t>(M) * K));
   w.batched = reinterpret_cast<char*>(w.code_scales) + round256(static_cast<size_t>(M) * sizeof(float));
@@ -968,9 +1007,10 @@ int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t 
                 const int32_t* draft, int32_t* target, int32_t* n_emitted, int32_t* emitted, float* y,
                 int32_t* len, int32_t* next, void* ws, size_t ws_bytes, void* stream) {
   if (B < 1 || k < 0) return nest::fail(NEST_EINVAL, "%s: B=%lld k=%lld", what, (long long)B, (long long)k);
-  if (B * (k + 1) > 16)
-    return nest::fail(NEST_EUNSUPPORTED, "%s: B*(k+1)=%lld > 16", what, (long long)(B * (k + 1)));
+  if (B * (k + 1) > 65535)
+    return nest::fail(NEST_EUNSUPPORTED, "%s: B*(k+1)=%lld > 65535", what, (long long)(B * (k + 1)));
   const int64_t M = B * (k + 1);
+  if (M > 16 && !y) return nest::fail(NEST_EINVAL, "%s: more than 16 rows need y for the logits", what);
   int rc = check_common(what, act, M, K, base, scales, V, group);
   if (rc) return rc;
   if (!refine || !target || !n_emitted || !emitted || (k > 0 && !draft))
@@ -984,10 +1024,25 @@ int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t 
   Act act2 = act;  // the LM head stays with in-kernel quantization whenever it fits
   rc = quantize_first(act2, M, K, V, w, st, false);
   if (rc) return rc;
-  GemvArgs a = make_args(act2, M, K, base, refine, scales, V, y, nullptr);
   FinishArgs f{};
   f.B = (int)B; f.k = (int)k; f.draft = draft; f.target = target; f.n_emitted = n_emitted;
   f.emitted = emitted; f.len = len; f.next = next;
+  if (M > 16) {
+    // the batched kernel (groups never split: no room for partial sums is
+    // asked of the caller) writes y, then the row argmaxes and the rule
+    for (int64_t m0 = 0; m0 < M; m0 += 144) {
+      const int64_t mc = M - m0 < 144 ? M - m0 : 144;
+      rc = nest::launch_verify_batched(act2.qa + m0 * K, act2.sa + m0, (int)mc, (int)K, base, refine, scales,
+                                       (int)V, y + m0 * V, nullptr, nullptr, nullptr, 0, st);
+      if (rc) return rc;
+    }
+    row_argmax_kernel<<<static_cast<unsigned>(M), 256, 0, st>>>(y, (int)V, w.partials);
+    rc = nest::check_launch(what);
+    if (rc) return rc;
+    accept_rows_kernel<<<1, 64, 0, st>>>(w.partials, f);
+    return nest::check_launch(what);
+  }
+  GemvArgs a = make_args(act2, M, K, base, refine, scales, V, y, nullptr);
   return launch_argmax<2, false>(a, f, true, w, st, what);
 }
 

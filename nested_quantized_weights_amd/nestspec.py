@@ -324,7 +324,7 @@ def verify_accept(qa, sa, B: int, k: int, W, draft, group: int = 128, want_y: bo
     V = W.rows
     dev = qa.device
     if out is None:
-        out = _accept_out(B, k, V, dev, want_y)
+        out = _accept_out(B, k, V, dev, want_y or B * (k + 1) > 16)  # more rows: y holds the logits
     if ws is None:
         ws = workspace(lib().verify_accept_workspace_size(B, k, V), dev, "gemv")
     _check(lib().verify_accept(_ptr(qa), _ptr(sa), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales),
@@ -386,7 +386,7 @@ def verify_accept_x(x, B: int, k: int, W, draft, group: int = 128, want_y: bool 
     V = W.rows
     dev = x.device
     if out is None:
-        out = _accept_out(B, k, V, dev, want_y)
+        out = _accept_out(B, k, V, dev, want_y or B * (k + 1) > 16)  # more rows: y holds the logits
     if ws is None:
         ws = gemv_x_workspace(B * (k + 1), K, V, dev)
     _check(lib().verify_accept_x(_ptr(x), B, k, K, _ptr(W.base), _ptr(W.refine), _ptr(W.scales), V, group,

@@ -311,6 +311,59 @@ def test_verify_accept(ns, oracle, V, K, B, k, alpha):
         assert np.array_equal(host(g["y"]).view(np.uint32), o["y"].view(np.uint32))
 
 
+@pytest.mark.parametrize("V,K,B,k", [(5000, 512, 2, 8), (3000, 384, 1, 16), (20000, 1024, 16, 8),
+                                     (1200, 256, 1, 150)])
+def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
+    # More than 16 rows (several sequences, or k >= 16): the batched kernel
+    # writes y (int32 group sums exact, the fp32 fold within its rounding
+    # bound, in the batched kernel's order), then a per-row argmax and the
+    # accept rule. A row's target is the exact argmax wherever the exact
+    # logits' two largest are further apart than twice the bound, and
+    # within that of the largest elsewhere; the rule's outputs follow
+    # exactly from the targets, and the lengths advance by the emitted
+    # counts. 151 rows take two batched launches (144 + 7).
+    M = B * (k + 1)
+    w = synth.weights(V, K, (224, V, K))
+    x = synth.activations(M, K, (225, V, K))
+    base, refine, scales = oracle.nest_pack(w)
+    qa, sa = oracle.act_quant(x)
+    oy, oacc = oracle.verify_gemm(qa, sa, base, refine, scales, want_acc=True)
+    draft = synth.plant_drafts(oy.argmax(axis=1).reshape(B, k + 1), 0.8, V, (226, V))
+    W = tiled(ns, base, refine, scales)
+    length = torch.full((B,), 100, dtype=torch.int32, device="cuda")
+    g = ns.verify_accept(dev(qa), dev(sa), B, k, W, dev(draft.reshape(-1)), length=length)
+    y = host(g["y"])
+    ok, worst = bound_ok(y, sa, scales, oacc, 1.0 / 16)
+    assert ok, worst
+    terms = (scales.astype(np.float64) / 16)[None] * oacc.astype(np.float64)
+    exact = sa.astype(np.float64)[:, None] * terms.sum(axis=2)
+    tol = (scales.shape[1] + 2) * U32 * sa.astype(np.float64)[:, None] * np.abs(terms).sum(axis=2)
+    tg = host(g["target"]).reshape(-1)
+    unique = 0
+    for r in range(M):
+        order = np.argsort(-exact[r], kind="stable")
+        top, second = order[0], order[1]
+        margin = 2 * tol[r].max()
+        assert exact[r, tg[r]] >= exact[r, top] - margin, r
+        if exact[r, top] - exact[r, second] > margin:
+            assert tg[r] == top, r
+            unique += 1
+    assert unique >= M - 2
+    n_got, em_got = host(g["n_emitted"]), host(g["emitted"])
+    t2 = tg.reshape(B, k + 1)
+    for b in range(B):
+        a = 0
+        while a < k and draft[b, a] == t2[b, a]:
+            a += 1
+        assert n_got[b] == a + 1
+        assert list(em_got[b]) == list(t2[b, :a + 1]) + [-1] * (k - a)
+    assert np.array_equal(host(length), 100 + n_got)
+    if M <= 18:  # the fp32-input path quantizes first: the same codes, the same logits
+        gx = ns.verify_accept_x(dev(x), B, k, W, dev(draft.reshape(-1)))
+        assert np.array_equal(host(gx["y"]).view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(host(gx["target"]).reshape(-1), tg)
+
+
 def test_argmax_ties_take_lowest_index(ns, oracle):
     # Two identical LM-head rows tie on every logit: the lower index wins.
     V, K = 500, 256

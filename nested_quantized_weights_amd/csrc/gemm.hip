@@ -506,7 +506,7 @@ int device_cus() {
 // Work split: four weight tiles per block (five to seven when more tiles
 // than four rounds' worth of CUs would need a second round: LLaMA-3-8B
 // gate|up as one 28672 x 4096 matrix at 144 rows, 51.5 -> 39.9 us with
-// seven-tile blocks in one round). Few row blocks (under half the
+// seven-tile blocks in one round; seven for still more tiles). Few row blocks (under half the
 // CUs) over long rows (64 groups or more) split the groups over S blocks
 // per row block, each with all activation rows: every block stages a
 // quarter (S = 4) of the activation bytes and streams a quarter of the
@@ -546,11 +546,13 @@ Plan plan_batched(int M, int K, int N, int cus, bool split_ok = true) {
     if (row_blocks * p.P > cus && (T + 1) / 2 <= cus) {
       p.WR = 2;
       p.P = 1;
-    } else if (p.P == 1 && CT >= 4 && T > 4 * cus && T <= 7 * cus) {
+    } else if (p.P == 1 && CT >= 4 && T > 4 * cus) {
       // more than one round of four-tile blocks: the fewest tiles per block
       // (five to seven) that fit one round, which also stages the
-      // activations once per 80 to 112 weight rows instead of 64
-      p.WR = (T + cus - 1) / cus;
+      // activations once per 80 to 112 weight rows instead of 64; seven
+      // when even those need several rounds (the 152064-row LM head at 144
+      // rows: 290-297 -> 248-261 us per verify_accept of 16 sequences)
+      p.WR = std::min((T + cus - 1) / cus, 7);
     }
   }
   p.row_blocks = (T + p.WR - 1) / p.WR;

@@ -333,7 +333,8 @@ def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
     draft = synth.plant_drafts(oy.argmax(axis=1).reshape(B, k + 1), 0.8, V, (226, V))
     W = tiled(ns, base, refine, scales)
     length = torch.full((B,), 100, dtype=torch.int32, device="cuda")
-    g = ns.verify_accept(dev(qa), dev(sa), B, k, W, dev(draft.reshape(-1)), length=length)
+    nxt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    g = ns.verify_accept(dev(qa), dev(sa), B, k, W, dev(draft.reshape(-1)), length=length, next_token=nxt)
     y = host(g["y"])
     ok, worst = bound_ok(y, sa, scales, oacc, 1.0 / 16)
     assert ok, worst
@@ -359,6 +360,7 @@ def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
             a += 1
         assert n_got[b] == a + 1
         assert list(em_got[b]) == list(t2[b, :a + 1]) + [-1] * (k - a)
+        assert host(nxt)[b] == t2[b, a]  # the next round's input: the last emitted token
     assert np.array_equal(host(length), 100 + n_got)
     if M <= 18:  # the fp32-input path quantizes first: the same codes, the same logits
         gx = ns.verify_accept_x(dev(x), B, k, W, dev(draft.reshape(-1)))

@@ -205,7 +205,13 @@ int nest_act_quant(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa,
  *            before first use, see the conventions), needed only when
  *            argmax is given (else it may be NULL). It holds the per-block
  *            partial maxima and the counter that finds the last block.
- * Requires 1 <= M <= 16, group == 128, K % 128 == 0, N >= 1.
+ * Up to 16 rows: one GEMV launch, the argmax fused in it (its fold then
+ * bit-identical to the sequential one). More rows (the drafts of more than
+ * 16 sequences): the batched MFMA kernel over the base plane alone writes
+ * y (required then), and one block per row takes the argmax of those
+ * values with the same tie rule; the fold adds the group sums in that
+ * kernel's order, within the same rounding bound.
+ * Requires 1 <= M <= 65535, group == 128, K % 128 == 0, N >= 1.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
 int draft_gemv(const int8_t* qa, const float* sa, int64_t M, int64_t K,
@@ -227,8 +233,9 @@ size_t nest_gemv_x_workspace_size(int64_t M, int64_t K, int64_t N);
  *   the rest as for draft_gemv (no debug accumulators)
  *   ws       nest_gemv_x_workspace_size(M, K, N) bytes, zeroed before first
  *            use (always required)
- * Requires 1 <= M <= 16. Activations with M*K > 131072 (beyond the LDS
- * budget for codes), and several rows that many blocks would each quantize
+ * Requires 1 <= M <= 65535 (more than 16 rows as for draft_gemv).
+ * Activations with M*K > 131072 (beyond the LDS budget for codes), more
+ * than 16 rows, and several rows that many blocks would each quantize
  * again (N*M*K >= 1.2e8, M >= 2), are quantized once by a nest_act_quant
  * launch into the workspace; the codes are the same either way.
  * Errors: as draft_gemv. */

@@ -1,6 +1,8 @@
 // Batched verify over both planes (BitNest, Figure 3: the target reads the
 // base and the refinement plane) for more than 16 activation rows, e.g. 16
 // sequences x (k+1) = 144 rows: y = sa * fold_g s/16 * (sum q_a (16 q_b + q_r)).
+// Given no refinement plane it computes the draft's base-plane product the
+// same way (q_r = 0), for drafts of more than 16 rows.
 //
 // A block owns WR 16-row weight tiles (four, i.e. 64 rows; two to seven for
 // some shapes), a range of the activation rows (CTP column tiles of 16) and all
@@ -80,7 +82,10 @@ __device__ __forceinline__ void load_w(const GemmArgs& a, int t, int g, int kq, 
   // ((t Gq + g/4) 16 + idx) 4 + g%4
   const size_t off = (static_cast<size_t>(t * a.G + g) * 4 + kq) * 256 + idx * 16;
   w.b = nest::ldnt16(a.base + off);
-  w.r = nest::ldnt16(a.refine + off);
+  // without a refinement plane (the draft over more than 16 rows) the codes
+  // merge to 16 q_b: the product is 16 times the base plane's, folded at
+  // s/16 as the verify's is
+  w.r = a.refine ? nest::ldnt16(a.refine + off) : make_uint4(0, 0, 0, 0);
   const int Gq = (a.G + 3) >> 2;
   w.s = __builtin_nontemporal_load(a.scales + (static_cast<size_t>(t * Gq + (g >> 2)) * 16 + idx) * 4 + (g & 3));
 }
@@ -178,7 +183,8 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& a, const uint8_t* slo
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = (ct0 + ct) * 16 + 4 * kq + i;
-          if (m < a.M && n < a.N) a.acc_dbg[(static_cast<size_t>(m) * a.N + n) * a.G + g] = d[ct % 2][rt][i];
+          if (m < a.M && n < a.N)  // the base plane's exact sum is the product / 16
+            a.acc_dbg[(static_cast<size_t>(m) * a.N + n) * a.G + g] = a.refine ? d[ct % 2][rt][i] : d[ct % 2][rt][i] >> 4;
         }
       }
     }

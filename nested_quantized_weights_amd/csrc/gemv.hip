@@ -673,7 +673,7 @@ __device__ void finish_reduce(const FinishArgs& f) {
 // lowest index among equal ones), then one thread per sequence applies the
 // accept rule.
 __global__ void __launch_bounds__(256) row_argmax_kernel(const float* __restrict__ y, int V,
-                                                         unsigned long long* keys) {
+                                                         unsigned long long* keys, int32_t* index) {
   __shared__ unsigned long long red[4];
   const int t = threadIdx.x;
   const float* yr = y + static_cast<size_t>(blockIdx.x) * V;
@@ -684,7 +684,11 @@ __global__ void __launch_bounds__(256) row_argmax_kernel(const float* __restrict
   for (int o = 32; o >= 1; o >>= 1) k = umax64(k, shfl_xor_u64(k, o));
   if ((t & 63) == 0) red[t >> 6] = k;
   __syncthreads();
-  if (t == 0) keys[blockIdx.x] = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+  if (t == 0) {
+    const unsigned long long best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+    keys[blockIdx.x] = best;
+    if (index) index[blockIdx.x] = static_cast<int32_t>(argmax_key_index(best));
+  }
 }
 
 __global__ void __launch_bounds__(64) accept_rows_kernel(const unsigned long long* keys, FinishArgs f) {
@@ -932,8 +936,9 @@ int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uin
                int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(what, act, M, K, base, scales, N, group);
   if (rc) return rc;
-  if (M > 16) return nest::fail(NEST_EUNSUPPORTED, "%s: M=%lld > 16", what, (long long)M);
   if (!y && !argmax) return nest::fail(NEST_EINVAL, "%s: need y or argmax", what);
+  if (M > 16 && !y) return nest::fail(NEST_EINVAL, "%s: more than 16 rows need y for the products", what);
+  if (M > 65535) return nest::fail(NEST_EUNSUPPORTED, "%s: M=%lld > 65535", what, (long long)M);
   if (act.x || argmax) {
     rc = check_ws(what, ws, ws_bytes, gemv_ws_bytes(M, K, N, act.x != nullptr));
     if (rc) return rc;
@@ -943,6 +948,21 @@ int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uin
   Act act2 = act;
   rc = quantize_first(act2, M, K, N, w, st, true);
   if (rc) return rc;
+  if (M > 16) {
+    // more rows (the drafts of more than 16 sequences): the batched kernel
+    // over the base plane alone (no refinement plane, groups not split),
+    // then the row argmaxes with the fused path's keys
+    for (int64_t m0 = 0; m0 < M; m0 += 144) {
+      const int64_t mc = M - m0 < 144 ? M - m0 : 144;
+      rc = nest::launch_verify_batched(act2.qa + m0 * K, act2.sa + m0, (int)mc, (int)K, base, nullptr, scales,
+                                       (int)N, y + m0 * N, acc_dbg ? acc_dbg + m0 * N * (K / kGroup) : nullptr,
+                                       nullptr, nullptr, 0, st);
+      if (rc) return rc;
+    }
+    if (!argmax) return NEST_OK;
+    row_argmax_kernel<<<static_cast<unsigned>(M), 256, 0, st>>>(y, (int)N, w.partials, argmax);
+    return nest::check_launch(what);
+  }
   GemvArgs a = make_args(act2, M, K, base, nullptr, scales, N, y, acc_dbg);
   if (argmax) {
     FinishArgs f{};
@@ -1036,7 +1056,7 @@ int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t 
                                        (int)V, y + m0 * V, nullptr, nullptr, nullptr, 0, st);
       if (rc) return rc;
     }
-    row_argmax_kernel<<<static_cast<unsigned>(M), 256, 0, st>>>(y, (int)V, w.partials);
+    row_argmax_kernel<<<static_cast<unsigned>(M), 256, 0, st>>>(y, (int)V, w.partials, nullptr);
     rc = nest::check_launch(what);
     if (rc) return rc;
     accept_rows_kernel<<<1, 64, 0, st>>>(w.partials, f);

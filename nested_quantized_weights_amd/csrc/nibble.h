@@ -72,7 +72,9 @@ constexpr size_t kCounterZoneBytes = kSplitCounterOff + 4 * kMaxSplitRowBlocks;
 // before the launch; the launch leaves them zero) and
 // verify_batched_slot_bytes(M, K, N) bytes of partial sums (16-byte
 // aligned, no initial contents); other shapes need neither (0 bytes).
-// Without counters (null) the groups are never split.
+// Without counters (null) the groups are never split. With refine null the
+// launch computes the draft's product over the base plane alone (acc_dbg
+// then holds the base plane's exact group sums).
 size_t verify_batched_slot_bytes(int M, int K, int N);
 int launch_verify_batched(const int8_t* qa, const float* sa, int M, int K, const uint8_t* base,
                           const uint8_t* refine, const float* scales, int N, float* y,

@@ -257,7 +257,8 @@ def draft_gemv(qa, sa, W, group: int = 128, y=None, want_y: bool = True, argmax:
     M, K = qa.shape
     N = W.rows
     dev = qa.device
-    if y is None and (want_y or not argmax):
+    ret_y = y is not None or want_y or not argmax
+    if y is None and (ret_y or M > 16):  # more than 16 rows: the library writes y on the way
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     am = None
     wsp, wsn = None, 0
@@ -269,7 +270,7 @@ def draft_gemv(qa, sa, W, group: int = 128, y=None, want_y: bool = True, argmax:
     acc = torch.empty((M, N, K // group), dtype=torch.int32, device=dev) if acc_dbg else None
     _check(lib().draft_gemv(_ptr(qa), _ptr(sa), M, K, _ptr(W.base), _ptr(W.scales), N, group, _ptr(y),
                             _ptr(am), _ptr(acc), wsp, wsn, _stream(dev)), what)
-    out = [y]
+    out = [y if ret_y else None]
     if argmax:
         out.append(am)
     if acc_dbg:
@@ -344,7 +345,8 @@ def draft_gemv_x(x, W, group: int = 128, y=None, want_y: bool = True, argmax: bo
     M, K = x.shape
     N = W.rows
     dev = x.device
-    if y is None and (want_y or not argmax):
+    ret_y = y is not None or want_y or not argmax
+    if y is None and (ret_y or M > 16):  # more than 16 rows: the library writes y on the way
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     am = None
     if argmax:
@@ -354,7 +356,7 @@ def draft_gemv_x(x, W, group: int = 128, y=None, want_y: bool = True, argmax: bo
     _check(lib().draft_gemv_x(_ptr(x), M, K, _ptr(W.base), _ptr(W.scales), N, group, _ptr(y), _ptr(am),
                               _ptr(ws), ws.numel(), _stream(dev)), what)
     if argmax:
-        return (y, am) if y is not None else am
+        return (y, am) if ret_y else am
     return y
 
 

@@ -154,6 +154,40 @@ def test_draft_gemv(ns, oracle, N, K, M):
     assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
 
 
+@pytest.mark.parametrize("N,K,M", [(3000, 512, 20), (5000, 384, 144), (1500, 256, 150), (20000, 128, 33)])
+def test_draft_gemv_over_16_rows(ns, oracle, N, K, M):
+    # More than 16 rows (the drafts of more than 16 sequences): the batched
+    # kernel over the base plane alone (its codes merge to 16 q_b, folded at
+    # s/16), in launches of up to 144 rows, then the row argmaxes. The group
+    # sums are exact, y within the fold's bound, each argmax the exact one
+    # wherever the row's top two are apart by more than twice the bound, and
+    # the fp32-input path gives the same products.
+    base, _, scales, qa, sa = _layer(oracle, N, K, M, (N, K, M, 2))
+    oy, oacc = oracle.draft_gemv(qa, sa, base, scales, want_acc=True)
+    W = tiled(ns, base, None, scales)
+    y, acc = ns.draft_gemv(dev(qa), dev(sa), W, acc_dbg=True)
+    assert np.array_equal(host(acc), oacc)
+    ok, worst = bound_ok(host(y), sa, scales, oacc, 1.0)
+    assert ok, worst
+    y2, am = ns.draft_gemv(dev(qa), dev(sa), W, argmax=True)
+    y2 = host(y2)
+    assert np.array_equal(y2.view(np.uint32), host(y).view(np.uint32))
+    terms = scales.astype(np.float64)[None] * oacc.astype(np.float64)
+    exact = sa.astype(np.float64)[:, None] * terms.sum(axis=2)
+    tol = (scales.shape[1] + 2) * U32 * sa.astype(np.float64)[:, None] * np.abs(terms).sum(axis=2)
+    am = host(am)
+    for r in range(M):
+        order = np.argsort(-exact[r], kind="stable")
+        margin = 2 * tol[r].max()
+        assert exact[r, am[r]] >= exact[r, order[0]] - margin, r
+        if exact[r, order[0]] - exact[r, order[1]] > margin:
+            assert am[r] == order[0], r
+        assert am[r] == int(np.argmax(y2[r]))  # the argmax of the kernel's own logits, lowest index first
+    x = synth.activations(M, K, (211, N, K, M, 2))  # the activations _layer quantized
+    yx = ns.draft_gemv_x(dev(x), W)
+    assert np.array_equal(host(yx).view(np.uint32), host(y).view(np.uint32))
+
+
 # M > 16 runs the batched kernel: (200, 2048, 144) and (1000, 1024, 144)
 # split each row block's activation rows over 9 blocks (one column tile
 # each); K = 128 leaves one part of a block's groups empty; (130, 384, 100)
@@ -460,8 +494,15 @@ def test_errors_are_reported(ns):
     qa = torch.zeros((17, 128), dtype=torch.int8, device="cuda")
     W = ns.nest_tile(torch.zeros((16, 64), dtype=torch.uint8, device="cuda"), None,
                      torch.zeros((16, 1), dtype=torch.float32, device="cuda"))
-    with pytest.raises(ns.NestError, match="M=17"):
-        ns.draft_gemv(qa, torch.zeros(17, dtype=torch.float32, device="cuda"), W)
+    # more than 16 rows go through the batched kernel, which writes y: a
+    # call that gives only the argmax output is refused on the host
+    L = ns.lib()
+    am = torch.zeros(17, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(L.draft_gemv_workspace_size(17, 16), dtype=torch.uint8, device="cuda")
+    rc = L.draft_gemv(qa.data_ptr(), torch.zeros(17, dtype=torch.float32, device="cuda").data_ptr(), 17, 128,
+                      W.base.data_ptr(), W.scales.data_ptr(), 16, 128, None, am.data_ptr(), None,
+                      ws.data_ptr(), ws.numel(), None)
+    assert rc == 1 and b"need y" in L.nest_last_error()
     with pytest.raises(ns.NestError, match="Tiled"):
         ns.draft_gemv(qa[:1], sa, torch.zeros((16, 64), dtype=torch.uint8, device="cuda"))
     with pytest.raises(ns.NestError, match="multiple of 128"):

@@ -442,7 +442,11 @@ int kv_nest_shadow_fill(const nest_kv* kv, const float* k, const float* v,
  *            L = ctx_len, or L = capacity when ctx_dev is given (no
  *            zero-fill needed)
  * Requires head_dim == 128, block == 128, Hq % Hkv == 0,
- * 1 <= nq*(Hq/Hkv) <= 64, and 16-byte aligned planes and q.
+ * 1 <= Hq/Hkv <= 64, and 16-byte aligned planes and q. Up to 64 query
+ * rows per kv head (nq*(Hq/Hkv)) run in one launch of the attention and
+ * one of the merge; more are taken in chunks of 64/(Hq/Hkv) queries, each
+ * chunk launched as the call of those queries alone (the same positions,
+ * hence the same results), the chunks sharing the workspace in turn.
  * Errors: NEST_EINVAL, NEST_EALIGN, NEST_ESHAPE, NEST_EUNSUPPORTED,
  * NEST_EWORKSPACE, NEST_EHIP. */
 int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
@@ -475,8 +479,8 @@ int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads,
  * as their GQA groups fit in 16 rows), then the chunk partials are merged.
  * With nq == 1 the call is kv_nest_attend's (the append already quantized
  * the block over the tokens up to the query).
- * Requires Hq/Hkv <= 16 and nq <= block; nq*(Hq/Hkv) may exceed
- * kv_nest_attend's 64. Errors: as kv_nest_attend. */
+ * Requires Hq/Hkv <= 16 and nq <= block; all nq queries go through one
+ * attention launch, whatever nq*(Hq/Hkv). Errors: as kv_nest_attend. */
 int kv_nest_attend_exact(const uint16_t* q, int64_t nq, int64_t n_q_heads,
                          const nest_kv* kv, const float* shadow_k,
                          const float* shadow_v, const int32_t* ctx_dev,

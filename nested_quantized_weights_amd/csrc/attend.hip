@@ -1006,6 +1006,14 @@ struct Plan {
   size_t ws;
 };
 
+// Query rows per kv head one launch of kv_nest_attend holds (four 16-row
+// tiles), and the queries per launch of a call that has more.
+constexpr int kMaxRowsPerLaunch = 64;
+int64_t chunk_queries(int64_t nq, int64_t grp) {
+  const int64_t per = kMaxRowsPerLaunch / (grp > 0 ? grp : 1);
+  return nq < per ? nq : (per > 0 ? per : 1);
+}
+
 // Work split. Up to 16 query rows: one 128-token block per wave while the
 // chip has wave slots to spare (about kTargetWaves), 4 waves per workgroup.
 // More rows: the LDS-table kernel with about kTargetBlocks workgroups.
@@ -1068,7 +1076,9 @@ ExactLayout exact_layout(int64_t nq, int64_t Hq, int64_t Hkv, int64_t plan_len) 
 extern "C" size_t kv_nest_attend_workspace_size(int64_t nq, int64_t n_q_heads, int64_t n_kv_heads,
                                                 int64_t head_dim, int64_t ctx_len) {
   if (nq < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || head_dim != kD || ctx_len < 1) return 0;
-  return make_plan(nq, n_q_heads, n_kv_heads, ctx_len).ws;
+  if (n_q_heads / n_kv_heads > kMaxRowsPerLaunch) return 0;
+  // the largest launch: a full chunk of queries at the full length
+  return make_plan(chunk_queries(nq, n_q_heads / n_kv_heads), n_q_heads, n_kv_heads, ctx_len).ws;
 }
 
 extern "C" size_t kv_nest_attend_exact_workspace_size(int64_t nq, int64_t n_q_heads, int64_t n_kv_heads,
@@ -1145,16 +1155,36 @@ extern "C" int kv_nest_attend(const uint16_t* q, int64_t nq, int64_t n_q_heads, 
                               size_t ws_bytes, void* stream) {
   const char* what = "kv_nest_attend";
   AttArgs a;
-  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, 64, a);
+  if (!kv) return nest::fail(NEST_EINVAL, "%s: null pointer", what);
+  if (kv->n_kv_heads >= 1 && n_q_heads / kv->n_kv_heads > kMaxRowsPerLaunch)
+    return nest::fail(NEST_EUNSUPPORTED, "%s: Hq/Hkv > %d", what, kMaxRowsPerLaunch);
+  int rc = prepare_attend(what, q, nq, n_q_heads, kv, ctx_dev, ctx_len, view, out, 1LL << 40, a);
   if (rc) return rc;
   const int64_t Hkv = kv->n_kv_heads;
-  // with the length on the device, the grid covers the whole capacity and
-  // the workgroups past the live length write empty partials
-  const Plan p = make_plan(nq, n_q_heads, Hkv, ctx_dev ? kv->capacity : ctx_len);
-  rc = attach_workspace(what, a, p, Hkv, ws, ws_bytes, p.ws);
-  if (rc) return rc;
+  // More query rows than one launch holds: the queries in chunks of
+  // kMaxRowsPerLaunch / grp, each launched as the call of its queries alone
+  // (its last query's position as the length), which is what each query
+  // sees in any case; the chunks share the workspace in turn.
+  const int64_t per = chunk_queries(nq, a.grp);
   hipStream_t st = nest::as_stream(stream);
-  return view == 0 ? launch_att<0>(a, p, (int)Hkv, st) : launch_att<1>(a, p, (int)Hkv, st);
+  for (int64_t i0 = 0; i0 < nq; i0 += per) {
+    const int64_t n = nq - i0 < per ? nq - i0 : per;
+    const int64_t len = ctx_len - (nq - i0 - n);
+    AttArgs c = a;
+    c.q = q + static_cast<size_t>(i0) * n_q_heads * kD;
+    c.out = out + static_cast<size_t>(i0) * n_q_heads * kD;
+    c.nq = static_cast<int>(n);
+    c.R = static_cast<int>(n * a.grp);
+    c.ctx = static_cast<int>(len);
+    // with the length on the device, the grid covers the whole capacity and
+    // the workgroups past the live length write empty partials
+    const Plan p = make_plan(n, n_q_heads, Hkv, ctx_dev ? kv->capacity : len);
+    rc = attach_workspace(what, c, p, Hkv, ws, ws_bytes, p.ws);
+    if (rc) return rc;
+    rc = view == 0 ? launch_att<0>(c, p, (int)Hkv, st) : launch_att<1>(c, p, (int)Hkv, st);
+    if (rc) return rc;
+  }
+  return NEST_OK;
 }
 
 namespace {

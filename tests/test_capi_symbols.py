@@ -97,7 +97,9 @@ def test_attend_host_validation_without_a_gpu(lib):
     assert f(p, 1, 30, ctypes.byref(kv), None, 4096, 0, p, p, ws, None) == 3  # NEST_ESHAPE: 8 does not divide 30
     assert f(p, 1, 32, ctypes.byref(kv), None, 4096, 2, p, p, ws, None) == 1  # NEST_EINVAL: view
     assert f(p, 1, 32, ctypes.byref(kv), None, 40000, 0, p, p, ws, None) == 1  # ctx_len > capacity
-    assert f(p, 17, 32, ctypes.byref(kv), None, 4096, 1, p, p, ws, None) == 5  # NEST_EUNSUPPORTED: 68 rows
+    # more query rows than one launch holds are taken in chunks of queries,
+    # but one query's GQA group must fit a launch (64 rows)
+    assert f(p, 1, 8 * 65, ctypes.byref(kv), None, 4096, 1, p, p, ws, None) == 5  # NEST_EUNSUPPORTED
     assert f(p, 1, 32, ctypes.byref(kv), None, 4096, 0, p, p, 16, None) == 4  # NEST_EWORKSPACE
     # with the length on the device the host value is an offset, and the
     # workspace must cover the whole capacity

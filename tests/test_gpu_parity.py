@@ -434,8 +434,11 @@ def _rel_err(o, ref):
 @pytest.mark.parametrize("Hq,Hkv,cap,ctx,nq", [(32, 8, 256, 256, 1), (32, 8, 384, 300, 9),
                                                (28, 4, 512, 389, 5), (4, 1, 128, 1, 1),
                                                (8, 8, 1024, 1000, 8), (16, 2, 2048, 2048, 8),
-                                               (32, 8, 20096, 20000, 1), (8, 8, 40960, 40000, 1)])
+                                               (32, 8, 20096, 20000, 1), (8, 8, 40960, 40000, 1),
+                                               (28, 4, 512, 389, 12), (32, 8, 384, 300, 20)])
 def test_kv_attend(ns, oracle, view, Hq, Hkv, cap, ctx, nq):
+    # the last two have more than 64 query rows per kv head (84, 80): they
+    # run in chunks of 9 and 16 queries
     d = 128
     kf, vf = synth.kv(Hkv, cap, d, (230, Hq, cap))
     q = synth.queries_bf16(nq, Hq, d, (231, Hq, nq))
@@ -444,6 +447,10 @@ def test_kv_attend(ns, oracle, view, Hq, Hkv, cap, ctx, nq):
     kv = ns.kv_nest_pack(dev(kf), dev(vf))
     out = host(ns.kv_nest_attend(dev(q.view(np.int16)), kv, ctx, view))
     assert _rel_err(out, ref) <= 2e-3
+    if nq * (Hq // Hkv) > 64:  # the chunks with the length on the device (offset 5 on the host)
+        length = torch.tensor([ctx - 5], dtype=torch.int32, device="cuda")
+        out_d = host(ns.kv_nest_attend(dev(q.view(np.int16)), kv, 5, view, ctx_dev=length))
+        assert _rel_err(out_d, ref) <= 2e-3
 
 
 @pytest.mark.parametrize("view", [0, 1])

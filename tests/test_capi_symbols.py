@@ -72,6 +72,19 @@ def test_host_validation_reports_errors_without_a_gpu(lib):
     ws.restype = ctypes.c_size_t
     ws.argtypes = [ctypes.c_int64] * 3
     assert ws(1, 8, 152064) > 0
+    # more than 16 rows go through the batched kernel, which writes y: a
+    # call without y is refused before anything runs; the accept workspace
+    # holds one argmax key per row
+    p = ctypes.c_void_p(256)
+    assert g(p, p, 17, 256, p, p, 16, 128, None, p, None, p, 1 << 20, None) == 1  # NEST_EINVAL
+    assert b"need y" in lib.nest_last_error()
+    va = lib.verify_accept
+    va.restype = ctypes.c_int
+    va.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 3 + \
+        [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert va(p, p, 2, 8, 256, p, p, p, 1000, 128, p, p, p, p, None, None, None, p, 1 << 20, None) == 1
+    assert b"need y" in lib.nest_last_error()
+    assert ws(16, 8, 152064) >= 4352 + 144 * 8 and ws(16, 8, 1000) >= 4352 + 144 * 8
 
 
 class _KV(ctypes.Structure):

@@ -678,8 +678,19 @@ __global__ void __launch_bounds__(256) row_argmax_kernel(const float* __restrict
   const int t = threadIdx.x;
   const float* yr = y + static_cast<size_t>(blockIdx.x) * V;
   unsigned long long k = 0;
+  // the largest key does not depend on the order the values are visited
+  // in: 16-byte loads where the rows allow them, the remainder one by one
+  const int V4 = ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? V / 4 : 0;
+  const float4* y4 = reinterpret_cast<const float4*>(yr);
+#pragma unroll 4
+  for (int i = t; i < V4; i += 256) {
+    const float4 v = y4[i];
+    const uint32_t n = 4 * static_cast<uint32_t>(i);
+    k = umax64(umax64(k, umax64(argmax_key(v.x, n), argmax_key(v.y, n + 1))),
+               umax64(argmax_key(v.z, n + 2), argmax_key(v.w, n + 3)));
+  }
 #pragma unroll 8
-  for (int n = t; n < V; n += 256) k = umax64(k, argmax_key(yr[n], static_cast<uint32_t>(n)));
+  for (int n = 4 * V4 + t; n < V; n += 256) k = umax64(k, argmax_key(yr[n], static_cast<uint32_t>(n)));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) k = umax64(k, shfl_xor_u64(k, o));
   if ((t & 63) == 0) red[t >> 6] = k;

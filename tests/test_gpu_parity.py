@@ -154,7 +154,8 @@ def test_draft_gemv(ns, oracle, N, K, M):
     assert host(am).tolist() == [oracle.argmax(oy[m]) for m in range(M)]
 
 
-@pytest.mark.parametrize("N,K,M", [(3000, 512, 20), (5000, 384, 144), (1500, 256, 150), (20000, 128, 33)])
+@pytest.mark.parametrize("N,K,M", [(3000, 512, 20), (5000, 384, 144), (1500, 256, 150), (20000, 128, 33),
+                                   (1499, 256, 40)])
 def test_draft_gemv_over_16_rows(ns, oracle, N, K, M):
     # More than 16 rows (the drafts of more than 16 sequences): the batched
     # kernel over the base plane alone (its codes merge to 16 q_b, folded at
@@ -186,6 +187,14 @@ def test_draft_gemv_over_16_rows(ns, oracle, N, K, M):
     x = synth.activations(M, K, (211, N, K, M, 2))  # the activations _layer quantized
     yx = ns.draft_gemv_x(dev(x), W)
     assert np.array_equal(host(yx).view(np.uint32), host(y).view(np.uint32))
+    # the row argmax reads 16 bytes at a time only where the rows allow it:
+    # N = 1499 and a caller's y 4 bytes off a 16-byte boundary take the
+    # scalar loads, with the same results
+    yo = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")[1:].view(M, N)
+    assert yo.data_ptr() % 16 != 0
+    y3, am3 = ns.draft_gemv(dev(qa), dev(sa), W, y=yo, argmax=True)
+    assert np.array_equal(host(y3).view(np.uint32), y2.view(np.uint32))
+    assert np.array_equal(host(am3), am)
 
 
 # M > 16 runs the batched kernel: (200, 2048, 144) and (1000, 1024, 144)
@@ -348,7 +357,7 @@ def test_verify_accept(ns, oracle, V, K, B, k, alpha):
 
 
 @pytest.mark.parametrize("V,K,B,k", [(5000, 512, 2, 8), (3000, 384, 1, 16), (20000, 1024, 16, 8),
-                                     (1200, 256, 1, 150)])
+                                     (1200, 256, 1, 150), (3001, 384, 3, 8)])
 def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
     # More than 16 rows (several sequences, or k >= 16): the batched kernel
     # writes y (int32 group sums exact, the fp32 fold within its rounding
@@ -357,7 +366,8 @@ def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
     # logits' two largest are further apart than twice the bound, and
     # within that of the largest elsewhere; the rule's outputs follow
     # exactly from the targets, and the lengths advance by the emitted
-    # counts. 151 rows take two batched launches (144 + 7).
+    # counts. 151 rows take two batched launches (144 + 7); rows of 3001
+    # logits take the row argmax's scalar loads.
     M = B * (k + 1)
     w = synth.weights(V, K, (224, V, K))
     x = synth.activations(M, K, (225, V, K))

@@ -667,44 +667,72 @@ __device__ void finish_reduce(const FinishArgs& f) {
   if (f.accept && t < f.B) accept_sequence(f, t, [&](int r) { return tgt[r]; });
 }
 
-// verify_accept over more than 16 rows (several sequences, or k >= 16): the
-// batched verify writes the logits to y, then one block per row takes the
-// row's argmax with the same keys as the fused path (the largest value, the
-// lowest index among equal ones), then one thread per sequence applies the
-// accept rule.
-__global__ void __launch_bounds__(256) row_argmax_kernel(const float* __restrict__ y, int V,
-                                                         unsigned long long* keys, int32_t* index) {
+// More than 16 rows (the drafts of several sequences, or verify_accept over
+// several sequences or k >= 16): the batched kernel writes the logits to y,
+// then each row's argmax is taken with the same keys as the fused path (the
+// largest value, the lowest index among equal ones) by C workgroups per row,
+// one per chunk of L values (L a multiple of 4). With C > 1 the chunks'
+// keys meet through the handoff of the file header: each workgroup
+// publishes its key with an agent-scope store, waits for it, and counts in
+// on its row's counter; the row's last workgroup reduces the C keys, writes
+// the row's index and returns the counter to zero.
+__global__ void __launch_bounds__(256) row_argmax_kernel(const float* __restrict__ y, int V, int C, int L,
+                                                         unsigned long long* keys, unsigned* counters,
+                                                         int32_t* index) {
   __shared__ unsigned long long red[4];
+  __shared__ int last_sh;
   const int t = threadIdx.x;
-  const float* yr = y + static_cast<size_t>(blockIdx.x) * V;
+  const int row = static_cast<int>(blockIdx.x) / C, c = static_cast<int>(blockIdx.x) - row * C;
+  const int lo = c * L, hi = min(lo + L, V);
+  const float* yr = y + static_cast<size_t>(row) * V;
   unsigned long long k = 0;
   // the largest key does not depend on the order the values are visited
-  // in: 16-byte loads where the rows allow them, the remainder one by one
-  const int V4 = ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? V / 4 : 0;
-  const float4* y4 = reinterpret_cast<const float4*>(yr);
+  // in: 16-byte loads where the rows allow them, else one value at a time
+  int n0 = lo;
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+    const float4* y4 = reinterpret_cast<const float4*>(yr);
 #pragma unroll 4
-  for (int i = t; i < V4; i += 256) {
-    const float4 v = y4[i];
-    const uint32_t n = 4 * static_cast<uint32_t>(i);
-    k = umax64(umax64(k, umax64(argmax_key(v.x, n), argmax_key(v.y, n + 1))),
-               umax64(argmax_key(v.z, n + 2), argmax_key(v.w, n + 3)));
+    for (int i = (lo >> 2) + t; i < (hi >> 2); i += 256) {
+      const float4 v = y4[i];
+      const uint32_t n = 4 * static_cast<uint32_t>(i);
+      k = umax64(umax64(k, umax64(argmax_key(v.x, n), argmax_key(v.y, n + 1))),
+                 umax64(argmax_key(v.z, n + 2), argmax_key(v.w, n + 3)));
+    }
+    n0 = hi;
   }
 #pragma unroll 8
-  for (int n = 4 * V4 + t; n < V; n += 256) k = umax64(k, argmax_key(yr[n], static_cast<uint32_t>(n)));
+  for (int n = n0 + t; n < hi; n += 256) k = umax64(k, argmax_key(yr[n], static_cast<uint32_t>(n)));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) k = umax64(k, shfl_xor_u64(k, o));
   if ((t & 63) == 0) red[t >> 6] = k;
   __syncthreads();
-  if (t == 0) {
-    const unsigned long long best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
-    keys[blockIdx.x] = best;
-    if (index) index[blockIdx.x] = static_cast<int32_t>(argmax_key_index(best));
+  const unsigned long long best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+  if (C == 1) {
+    if (t == 0) index[row] = static_cast<int32_t>(argmax_key_index(best));
+    return;
+  }
+  if (t == 0) __hip_atomic_store(keys + static_cast<size_t>(row) * C + c, best, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t == 0) last_sh = atomicAdd(counters + row, 1u) == static_cast<unsigned>(C - 1);
+  __syncthreads();
+  if (last_sh && t < 64) {
+    unsigned long long b = 0;
+    for (int j = t; j < C; j += 64)
+      b = umax64(b, __hip_atomic_load(keys + static_cast<size_t>(row) * C + j, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) b = umax64(b, shfl_xor_u64(b, o));
+    if (t == 0) {
+      index[row] = static_cast<int32_t>(argmax_key_index(b));
+      atomicExch(counters + row, 0u);
+    }
   }
 }
 
-__global__ void __launch_bounds__(64) accept_rows_kernel(const unsigned long long* keys, FinishArgs f) {
-  for (int b = threadIdx.x; b < f.B; b += 64)
-    accept_sequence(f, b, [&](int r) { return static_cast<int32_t>(argmax_key_index(keys[r])); });
+__global__ void __launch_bounds__(64) accept_rows_kernel(const int32_t* index, FinishArgs f) {
+  for (int b = threadIdx.x; b < f.B; b += 64) accept_sequence(f, b, [&](int r) { return index[r]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -826,13 +854,32 @@ size_t verify_int8_ws_bytes(int64_t M, int64_t K, int64_t N) {
   return slots ? kCounterBytes + slots : 0;
 }
 
-// The keys region: per-block argmax keys, or one key per row for
-// verify_accept over more than 16 rows.
+// Chunks per row of the row argmax (more than 16 rows): about 1024
+// workgroups over all rows, each chunk at least 2048 values, at most one
+// row counter per row of the counter zone.
+int row_chunks(int64_t M, int64_t V) {
+  if (M >= nest::kMaxSplitRowBlocks) return 1;
+  int64_t c = (1024 + M - 1) / M;
+  const int64_t cap = V / 2048;
+  if (c > cap) c = cap;
+  if (c > 64) c = 64;
+  return c < 1 ? 1 : static_cast<int>(c);
+}
+
+// The row argmax's chunk keys [M][C] and row indices [M] (int32, after the
+// keys) over more than 16 rows.
+size_t row_keys_bytes(int64_t M, int64_t V) {
+  return static_cast<size_t>(M) * row_chunks(M, V) * sizeof(unsigned long long);
+}
+
+// The keys region: per-block argmax keys, or the row argmax's keys and
+// indices over more than 16 rows.
 size_t keys_bytes(int64_t M, int64_t N) {
   const size_t blocks = argmax_ws_bytes(static_cast<int>(N));
-  const size_t rows = M > 16 ? static_cast<size_t>(M) * sizeof(unsigned long long) : 0;
+  const size_t rows = M > 16 ? row_keys_bytes(M, N) + static_cast<size_t>(M) * sizeof(int32_t) : 0;
   return round256(blocks > rows ? blocks : rows);
 }
+
 
 size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N, bool x) {
   size_t n = kCounterBytes + keys_bytes(M, N);
@@ -861,6 +908,17 @@ Workspace carve(void* ws, int64_t M, int64_t K, int64_t N) {
   w.code_scales = reinterpret_cast<float*>(c + round256(static_cast<size_t>(M) * K));
   w.batched = reinterpret_cast<char*>(w.code_scales) + round256(static_cast<size_t>(M) * sizeof(float));
   return w;
+}
+
+// Launch the row argmax over M rows of V logits; index gets each row's
+// argmax. Keys and row counters come from the workspace.
+int launch_row_argmax(const float* y, int64_t M, int64_t V, const Workspace& w, int32_t* index,
+                      hipStream_t st, const char* what) {
+  const int C = row_chunks(M, V);
+  const int64_t L = (((V + C - 1) / C) + 3) & ~static_cast<int64_t>(3);
+  row_argmax_kernel<<<static_cast<unsigned>(M * C), 256, 0, st>>>(y, (int)V, C, (int)L, w.partials,
+                                                                    w.split_counters, index);
+  return nest::check_launch(what);
 }
 
 // The exact-fold argmax GEMV; its last block reduces the keys.
@@ -971,8 +1029,7 @@ int draft_impl(const char* what, const Act& act, int64_t M, int64_t K, const uin
       if (rc) return rc;
     }
     if (!argmax) return NEST_OK;
-    row_argmax_kernel<<<static_cast<unsigned>(M), 256, 0, st>>>(y, (int)N, w.partials, argmax);
-    return nest::check_launch(what);
+    return launch_row_argmax(y, M, N, w, argmax, st, what);
   }
   GemvArgs a = make_args(act2, M, K, base, nullptr, scales, N, y, acc_dbg);
   if (argmax) {
@@ -1067,10 +1124,10 @@ int accept_impl(const char* what, const Act& act, int64_t B, int64_t k, int64_t 
                                        (int)V, y + m0 * V, nullptr, nullptr, nullptr, 0, st);
       if (rc) return rc;
     }
-    row_argmax_kernel<<<static_cast<unsigned>(M), 256, 0, st>>>(y, (int)V, w.partials, nullptr);
-    rc = nest::check_launch(what);
+    int32_t* rows = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(w.partials) + row_keys_bytes(M, V));
+    rc = launch_row_argmax(y, M, V, w, rows, st, what);
     if (rc) return rc;
-    accept_rows_kernel<<<1, 64, 0, st>>>(w.partials, f);
+    accept_rows_kernel<<<1, 64, 0, st>>>(rows, f);
     return nest::check_launch(what);
   }
   GemvArgs a = make_args(act2, M, K, base, refine, scales, V, y, nullptr);

@@ -84,7 +84,9 @@ def test_host_validation_reports_errors_without_a_gpu(lib):
         [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     assert va(p, p, 2, 8, 256, p, p, p, 1000, 128, p, p, p, p, None, None, None, p, 1 << 20, None) == 1
     assert b"need y" in lib.nest_last_error()
-    assert ws(16, 8, 152064) >= 4352 + 144 * 8 and ws(16, 8, 1000) >= 4352 + 144 * 8
+    # over 16 rows: the row argmax's chunk keys (8 chunks of each of the 144 rows of
+    # 152064 logits; one chunk of 1000) and the row indices after the counter zone
+    assert ws(16, 8, 152064) >= 4352 + 144 * 8 * 8 + 144 * 4 and ws(16, 8, 1000) >= 4352 + 144 * (8 + 4)
 
 
 class _KV(ctypes.Structure):

@@ -155,7 +155,7 @@ def test_draft_gemv(ns, oracle, N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(3000, 512, 20), (5000, 384, 144), (1500, 256, 150), (20000, 128, 33),
-                                   (1499, 256, 40)])
+                                   (1499, 256, 40), (9001, 256, 40)])
 def test_draft_gemv_over_16_rows(ns, oracle, N, K, M):
     # More than 16 rows (the drafts of more than 16 sequences): the batched
     # kernel over the base plane alone (its codes merge to 16 q_b, folded at
@@ -188,8 +188,10 @@ def test_draft_gemv_over_16_rows(ns, oracle, N, K, M):
     yx = ns.draft_gemv_x(dev(x), W)
     assert np.array_equal(host(yx).view(np.uint32), host(y).view(np.uint32))
     # the row argmax reads 16 bytes at a time only where the rows allow it:
-    # N = 1499 and a caller's y 4 bytes off a 16-byte boundary take the
-    # scalar loads, with the same results
+    # N = 1499 or 9001 and a caller's y 4 bytes off a 16-byte boundary take
+    # the scalar loads, with the same results; rows are split into chunks
+    # where there are few rows of many logits (20000 x 33 rows: 9 chunks,
+    # 9001 x 40: 4, 5000 x 144: 2)
     yo = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")[1:].view(M, N)
     assert yo.data_ptr() % 16 != 0
     y3, am3 = ns.draft_gemv(dev(qa), dev(sa), W, y=yo, argmax=True)
@@ -260,7 +262,9 @@ def test_shapes_and_entry_points_share_one_workspace(ns, oracle):
     # counters, at the same offsets for every entry point and shape. A group
     # split over 69 row blocks (4400 x 8192, three slices), one over 10 row
     # blocks and four slices (640 x 8192), the fp32-input path of the first
-    # shape and an argmax GEMV take turns on one workspace, and each gives
+    # shape, an argmax GEMV and the argmaxes of a 144-row draft (two chunks
+    # per row, meeting through the zone's row counters) take turns on one
+    # workspace, and each gives
     # bit for bit what it gives on a fresh one; the zone is zero afterwards.
     # (With the counters placed before the partial sums at a shape-dependent
     # offset, the 4-slice call's sums landed on the 69-row-block call's
@@ -274,7 +278,8 @@ def test_shapes_and_entry_points_share_one_workspace(ns, oracle):
     assert L.verify_gemm_workspace_size(144, 8192, 4400) > zone
     assert L.verify_gemm_workspace_size(144, 8192, 640) > zone
     n = max(L.verify_gemm_workspace_size(144, 8192, 4400), L.verify_gemm_workspace_size(144, 8192, 640),
-            L.nest_gemv_x_workspace_size(144, 8192, 4400), L.nest_gemv_x_workspace_size(1, 8192, 4400))
+            L.nest_gemv_x_workspace_size(144, 8192, 4400), L.nest_gemv_x_workspace_size(1, 8192, 4400),
+            L.draft_gemv_workspace_size(144, 4400))
 
     def fresh():
         return torch.zeros(n, dtype=torch.uint8, device="cuda")
@@ -284,10 +289,12 @@ def test_shapes_and_entry_points_share_one_workspace(ns, oracle):
         "split4": lambda ws: ns.verify_gemm(dev(lb[3]), dev(lb[4]), Wb, ws=ws),
         "x": lambda ws: ns.verify_gemm_x(x, Wa, ws=ws),
         "argmax": lambda ws: ns.draft_gemv_x(x[:1], Wa, argmax=True, want_y=False, ws=ws),
+        "rows": lambda ws: ns.draft_gemv(dev(la[3]), dev(la[4]), Wa, argmax=True, want_y=False, ws=ws)[1],
     }
     ref = {k: host(f(fresh())) for k, f in calls.items()}
     ws = fresh()
-    for k in ["split4", "split3", "split4", "x", "split3", "argmax", "split4", "x", "split3"]:
+    for k in ["split4", "split3", "rows", "split4", "x", "split3", "argmax", "rows", "split4", "x", "split3",
+              "rows"]:
         got = host(calls[k](ws))
         assert np.array_equal(got.view(np.uint32), ref[k].view(np.uint32)), k
     assert not host(ws[:zone]).any()
@@ -357,7 +364,8 @@ def test_verify_accept(ns, oracle, V, K, B, k, alpha):
 
 
 @pytest.mark.parametrize("V,K,B,k", [(5000, 512, 2, 8), (3000, 384, 1, 16), (20000, 1024, 16, 8),
-                                     (1200, 256, 1, 150), (3001, 384, 3, 8)])
+                                     (1200, 256, 1, 150), (3001, 384, 3, 8),
+                                     (20001, 384, 3, 8)])
 def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
     # More than 16 rows (several sequences, or k >= 16): the batched kernel
     # writes y (int32 group sums exact, the fp32 fold within its rounding
@@ -366,8 +374,11 @@ def test_verify_accept_over_16_rows(ns, oracle, V, K, B, k):
     # logits' two largest are further apart than twice the bound, and
     # within that of the largest elsewhere; the rule's outputs follow
     # exactly from the targets, and the lengths advance by the emitted
-    # counts. 151 rows take two batched launches (144 + 7); rows of 3001
-    # logits take the row argmax's scalar loads.
+    # counts. 151 rows take two batched launches (144 + 7). The row argmax
+    # splits a row into chunks where there are few rows of many logits
+    # (5000 x 18 rows: 2, 20000 x 144 rows: 8, 20001 x 27 rows: 9 chunks,
+    # whose keys meet through a row counter); rows of 3001 and 20001
+    # logits take its scalar loads.
     M = B * (k + 1)
     w = synth.weights(V, K, (224, V, K))
     x = synth.activations(M, K, (225, V, K))

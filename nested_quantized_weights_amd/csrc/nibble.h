@@ -60,7 +60,8 @@ int resident_blocks(const void* kernel, int threads, size_t dyn_lds);
 // (draft_gemv*, verify_gemm*, verify_accept*), the same for every entry point
 // and shape: [0, 256) the argmax kernels' finished-block counter, then one
 // finished-slice counter per row block of the batched verify (at most
-// kMaxSplitRowBlocks). Counters are zero at rest, every call returns the
+// kMaxSplitRowBlocks), which the row argmax of more than 16 rows takes in
+// turn as one finished-chunk counter per row. Counters are zero at rest, every call returns the
 // ones it used to zero, and no call stores data in the zone, so one
 // workspace serves calls of any of these entry points and shapes in turn.
 constexpr size_t kSplitCounterOff = 256;

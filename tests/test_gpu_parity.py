@@ -216,12 +216,13 @@ def test_draft_gemv_over_16_rows(ns, oracle, N, K, M):
 # counters than a 256-byte area holds; ragged last tile). A single weight
 # row: (1, 256, 20) in one block, (1, 8192, 144) split over four slices.
 # (30000, 256, 144): more tiles than seven rounds' worth of CUs, seven-tile
-# blocks in two rounds.
+# blocks in two rounds; (28705, 128, 70) the same with a one-row last tile
+# and ragged rows.
 BATCHED_SHAPES = [(50, 512, 17), (200, 256, 144), (64, 384, 150), (200, 2048, 144), (1000, 1024, 144),
                   (64, 128, 33), (130, 384, 100), (5511, 256, 144),
                   (640, 8192, 144), (300, 9216, 37), (200, 8320, 100), (130, 16384, 150),
                   (17000, 256, 64), (24000, 128, 50), (28672, 128, 144), (4400, 8192, 20), (1, 256, 20),
-                  (1, 8192, 144), (30000, 256, 144)]
+                  (1, 8192, 144), (30000, 256, 144), (28705, 128, 70)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMV_SHAPES + BATCHED_SHAPES)
